@@ -1,0 +1,89 @@
+"""Encoders from fp32 values to the cache byte formats (input preparation).
+
+Formats (CSA2 deep-dive page, "attention calc" and "SGLang" sections; V4.1-Flash
+report reading, section 6 on the FP4 main KV; DSA page, "two KV caches"):
+
+* Index K / indexer query: OCP FP8 E4M3FN codes, one fp32 scale per 128-wide
+  row (per key, or per (query, head)).  scale = amax / 448, so every scaled
+  value is inside the E4M3 range.  Keys and scales live in separate arrays so
+  the keys form a dense [n, 128] byte matrix.
+* Main KV: FP4 E2M1 codes, two per byte (element 2i in the low nibble of byte
+  i), one fp32 scale per 32 elements, packed as a 320-byte record
+  [256 B codes | 16 x fp32 scales].  scale = amax / 6.
+* SWA KV: FP8 E4M3FN codes with one fp32 scale per 128 elements, packed as a
+  528-byte record [512 B codes | 4 x fp32 scales].
+* bf16: round-to-nearest-even truncation of fp32.
+
+Every encoder rounds to nearest, ties to even, and saturates at the format's
+largest finite magnitude.  The encoders run on whatever device the input
+tensor lives on.
+"""
+import torch
+
+E4M3_MAX = 448.0
+E2M1_MAX = 6.0
+FP4_RECORD_BYTES = 320      # 256 B of E2M1 pairs + 16 fp32 scales
+SWA_RECORD_BYTES = 528      # 512 B of E4M3 + 4 fp32 scales
+
+
+def _group_scale(x, group, fmax):
+    n, d = x.shape
+    g = x.reshape(n, d // group, group)
+    amax = g.abs().amax(dim=2)
+    scale = amax / fmax
+    scale = torch.where(amax > 0, scale, torch.ones_like(scale))
+    return g, scale.to(torch.float32)
+
+
+def encode_e4m3_rows(x, group=None):
+    """fp32 [n, d] -> (u8 codes [n, d], fp32 scales [n, d // group])."""
+    x = x.to(torch.float32)
+    n, d = x.shape
+    group = d if group is None else group
+    g, scale = _group_scale(x, group, E4M3_MAX)
+    y = (g / scale.unsqueeze(2)).clamp_(-E4M3_MAX, E4M3_MAX)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).reshape(n, d)
+    return codes.contiguous(), scale.contiguous()
+
+
+def _e2m1_codes(y):
+    """Round |y| <= 6 onto the E2M1 grid {0,.5,1,1.5,2,3,4,6}, ties to the
+    code with an even mantissa bit, and return 4-bit codes (sign in bit 3)."""
+    a = y.abs()
+    code = ((a > 0.25).to(torch.uint8) + (a >= 0.75).to(torch.uint8)
+            + (a > 1.25).to(torch.uint8) + (a >= 1.75).to(torch.uint8)
+            + (a > 2.5).to(torch.uint8) + (a >= 3.5).to(torch.uint8)
+            + (a > 5.0).to(torch.uint8))
+    sign = (y < 0).to(torch.uint8) << 3
+    return code | sign
+
+
+def encode_fp4_records(x):
+    """fp32 [n, 512] -> u8 records [n, 320]."""
+    x = x.to(torch.float32)
+    n, d = x.shape
+    assert d == 512
+    g, scale = _group_scale(x, 32, E2M1_MAX)
+    y = (g / scale.unsqueeze(2)).clamp_(-E2M1_MAX, E2M1_MAX).reshape(n, d)
+    c = _e2m1_codes(y)
+    packed = c[:, 0::2] | (c[:, 1::2] << 4)
+    rec = torch.empty((n, FP4_RECORD_BYTES), dtype=torch.uint8, device=x.device)
+    rec[:, :256] = packed
+    rec[:, 256:] = scale.contiguous().view(torch.uint8).reshape(n, 64)
+    return rec
+
+
+def encode_swa_records(x):
+    """fp32 [n, 512] -> u8 records [n, 528]."""
+    n, d = x.shape
+    assert d == 512
+    codes, scale = encode_e4m3_rows(x, 128)
+    rec = torch.empty((n, SWA_RECORD_BYTES), dtype=torch.uint8, device=x.device)
+    rec[:, :512] = codes
+    rec[:, 512:] = scale.view(torch.uint8).reshape(n, 16)
+    return rec
+
+
+def encode_bf16(x):
+    """fp32 -> bf16 bit patterns as int16 (round to nearest even)."""
+    return x.to(torch.float32).to(torch.bfloat16).view(torch.int16)

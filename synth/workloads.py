@@ -1,0 +1,275 @@
+"""Seeded synthetic workloads shaped like the pages' CSA2 configurations.
+
+Each workload is a set of device-resident tensors plus the metadata the four
+library calls need.  Nothing here scores, selects or attends: the tensors are
+random draws, encoded into the cache formats by :mod:`synth.formats`.
+
+The shapes follow the V4.1-Flash description (CSA2 deep-dive page, sections on
+the per-layer attention computation, the hierarchical sparse indexer and the
+V4.1-Flash layout; V4.1-Flash report reading, sections 4 and 5):
+
+* indexer 32 heads x 128 dims, top-512, 8-position blocks, 2048 kept blocks;
+* attention 64 heads x 512 dims, MQA with K = V, 128 sliding-window entries;
+* decoder ratio m = 1, encoder ratio m = 2 (per-channel softmax pooling of
+  non-overlapping token pairs, no positional bias).
+
+Random streams: every tensor draws from its own torch.Generator seeded with a
+64-bit value derived by numpy's SeedSequence from (seed, tensor id, chunk), so
+a tensor never depends on which other tensors were drawn.  Large tensors are
+drawn in fixed chunks of 2^20 rows so the values do not depend on the memory
+available.  The same seed gives the same bytes on the same device type; CPU
+and GPU draws differ (different generators), and each test uses one device's
+draw for both sides of a comparison.
+"""
+from dataclasses import dataclass, field
+import math
+
+import numpy as np
+import torch
+
+from .formats import (encode_e4m3_rows, encode_fp4_records, encode_swa_records,
+                      encode_bf16)
+
+CONFIG_NAMES = ("tiny_full_fp32", "decode_128k", "prefill_m2_chunk",
+                "reindex_1m", "decoder_group_256k")
+
+H_IDX, D_IDX = 32, 128
+H_ATT, D_ATT = 64, 512
+TOPK, BLOCK, N_BLOCKS, WINDOW = 512, 8, 2048, 128
+CHUNK_ROWS = 1 << 20
+
+# tensor ids for the seed derivation
+_T_KIDX, _T_MAIN, _T_C, _T_Z = 1, 2, 3, 4
+_T_QIDX, _T_W, _T_Q, _T_SWA, _T_SINK = 10, 11, 12, 13, 14
+
+
+def _gen(seed, tid, sub, device):
+    s = np.random.SeedSequence([int(seed), int(tid), int(sub)])
+    v = int(s.generate_state(1, np.uint64)[0]) & ((1 << 63) - 1)
+    g = torch.Generator(device=device)
+    g.manual_seed(v)
+    return g
+
+
+def _randn(shape, seed, tid, sub, device):
+    return torch.randn(shape, generator=_gen(seed, tid, sub, device),
+                       device=device, dtype=torch.float32)
+
+
+def _randint(lo, hi, shape, seed, tid, sub, device):
+    """Integers uniform in [lo, hi], as fp32."""
+    return torch.randint(lo, hi + 1, shape, generator=_gen(seed, tid, sub, device),
+                         device=device).to(torch.float32)
+
+
+@dataclass
+class Layer:
+    mode: str                      # "full", "reindex" or "reuse"
+    q: torch.Tensor                # [Q, H, D] bf16 bits (int16) or fp32
+    swa: torch.Tensor              # [rows, 528] u8 records, or [rows, 512] fp32
+    sink: torch.Tensor             # [H] fp32
+    q_idx: torch.Tensor = None     # [Q, 32, 128] u8 E4M3 codes, or fp32
+    q_scale: torch.Tensor = None   # [Q, 32] fp32 (None for fp32 q_idx)
+    w: torch.Tensor = None         # [Q, 32] bf16 bits (int16), or fp32
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    quantized: bool
+    ratio: int
+    n_entries: list                # main-KV / index-K entries per sequence
+    seq_base: torch.Tensor         # [B] int64 first row of each sequence
+    q_seq: torch.Tensor            # [Q] int32
+    q_pos: torch.Tensor            # [Q] int32 token position of each query
+    k_idx: torch.Tensor            # [sum N, 128] u8 E4M3 codes, or fp32
+    k_scale: torch.Tensor          # [sum N] fp32 or None
+    main_kv: torch.Tensor          # [sum N, 320] u8 records, or [sum N, 512] fp32
+    swa_base: torch.Tensor         # [B] int64 first SWA row of each sequence
+    swa_pos0: torch.Tensor         # [B] int32 token position of that row
+    layers: list = field(default_factory=list)
+    topk: int = TOPK
+    block_size: int = BLOCK
+    n_blocks: int = N_BLOCKS
+    window: int = WINDOW
+    softmax_scale: float = 1.0 / math.sqrt(D_ATT)
+
+    @property
+    def Q(self):
+        return int(self.q_pos.shape[0])
+
+    @property
+    def B(self):
+        return len(self.n_entries)
+
+    def n_vis(self):
+        """Visible main entries per query: (pos + 1) // ratio."""
+        return (self.q_pos.to(torch.int64) + 1) // self.ratio
+
+    def max_cols(self):
+        return int(self.n_vis().max().item())
+
+
+def _chunked(total, fn):
+    parts = []
+    for c, r0 in enumerate(range(0, total, CHUNK_ROWS)):
+        parts.append(fn(c, min(CHUNK_ROWS, total - r0)))
+    return torch.cat(parts, 0) if len(parts) > 1 else parts[0]
+
+
+def _index_keys(seed, total, quantized, device):
+    if not quantized:
+        return _randint(-4, 4, (total, D_IDX), seed, _T_KIDX, 0, device), None
+
+    def one(c, n):
+        return encode_e4m3_rows(_randn((n, D_IDX), seed, _T_KIDX, c, device))
+    parts = []
+    for c, r0 in enumerate(range(0, total, CHUNK_ROWS)):
+        parts.append(one(c, min(CHUNK_ROWS, total - r0)))
+    codes = torch.cat([p[0] for p in parts], 0)
+    scale = torch.cat([p[1] for p in parts], 0).reshape(total)
+    return codes, scale
+
+
+def _main_kv_gauss(seed, total, quantized, device):
+    if not quantized:
+        return _randn((total, D_ATT), seed, _T_MAIN, 0, device)
+    return _chunked(total, lambda c, n: encode_fp4_records(
+        _randn((n, D_ATT), seed, _T_MAIN, c, device)))
+
+
+def compress_pairs_input(c, z):
+    """Input recipe for the m = 2 encoder cache: entry i, channel ch is the
+    softmax over the token pair (2i, 2i+1) of the logits z, applied to c
+    (V4.1 report reading section 4 and the xhh.club summary: non-overlapping
+    groups, per-channel softmax, no positional bias)."""
+    n = c.shape[0] // 2
+    c2 = c[: 2 * n].reshape(n, 2, -1)
+    z2 = z[: 2 * n].reshape(n, 2, -1)
+    wgt = torch.softmax(z2, dim=1)
+    return (wgt * c2).sum(dim=1)
+
+
+def _layer(seed, li, mode, Q, swa_rows, quantized, device, with_indexer):
+    base = 100 * (li + 1)
+    if quantized:
+        q = encode_bf16(_randn((Q, H_ATT, D_ATT), seed, _T_Q + base, 0, device))
+        swa = encode_swa_records(_randn((swa_rows, D_ATT), seed, _T_SWA + base, 0, device))
+    else:
+        q = _randn((Q, H_ATT, D_ATT), seed, _T_Q + base, 0, device)
+        swa = _randn((swa_rows, D_ATT), seed, _T_SWA + base, 0, device)
+    sink = _randn((H_ATT,), seed, _T_SINK + base, 0, device)
+    lay = Layer(mode=mode, q=q, swa=swa, sink=sink)
+    if with_indexer:
+        if quantized:
+            x = _randn((Q * H_IDX, D_IDX), seed, _T_QIDX + base, 0, device)
+            codes, sc = encode_e4m3_rows(x)
+            lay.q_idx = codes.reshape(Q, H_IDX, D_IDX)
+            lay.q_scale = sc.reshape(Q, H_IDX)
+            lay.w = encode_bf16(_randn((Q, H_IDX), seed, _T_W + base, 0, device))
+        else:
+            lay.q_idx = _randint(-4, 4, (Q, H_IDX, D_IDX), seed, _T_QIDX + base, 0, device)
+            lay.w = _randint(-2, 2, (Q, H_IDX), seed, _T_W + base, 0, device)
+    return lay
+
+
+def _decode_layout(n_entries, q_per_seq, ratio, device, positions=None):
+    """Decode-style layout: sequence b holds n_entries[b] entries; its queries
+    sit at the end of the sequence (or at explicit positions)."""
+    B = len(n_entries)
+    seq_base = torch.tensor(np.concatenate([[0], np.cumsum(n_entries)[:-1]]),
+                            dtype=torch.int64)
+    q_seq, q_pos = [], []
+    for b in range(B):
+        if positions is not None:
+            ps = positions[b]
+        else:
+            last = n_entries[b] * ratio - 1
+            ps = [last - i for i in range(q_per_seq)]
+        q_seq += [b] * len(ps)
+        q_pos += list(ps)
+    q_seq = torch.tensor(q_seq, dtype=torch.int32)
+    q_pos = torch.tensor(q_pos, dtype=torch.int32)
+    # SWA rows cover [min pos - window + 1, max pos] of each sequence
+    swa_pos0, swa_rows = [], []
+    for b in range(B):
+        ps = q_pos[q_seq == b]
+        lo = max(0, int(ps.min()) - WINDOW + 1) if len(ps) else 0
+        hi = int(ps.max()) if len(ps) else -1
+        swa_pos0.append(lo)
+        swa_rows.append(max(0, hi - lo + 1))
+    swa_base = torch.tensor(np.concatenate([[0], np.cumsum(swa_rows)[:-1]]),
+                            dtype=torch.int64)
+    return (seq_base.to(device), q_seq.to(device), q_pos.to(device),
+            swa_base.to(device), torch.tensor(swa_pos0, dtype=torch.int32).to(device),
+            int(sum(swa_rows)))
+
+
+def mini_workload(seed, n_entries, q_per_seq=1, ratio=1, quantized=True,
+                  modes=("full",), device="cpu", positions=None, topk=TOPK,
+                  n_blocks=N_BLOCKS, block_size=BLOCK):
+    """A small workload of the same structure, for parity tests."""
+    seq_base, q_seq, q_pos, swa_base, swa_pos0, swa_total = _decode_layout(
+        n_entries, q_per_seq, ratio, device, positions)
+    total = int(sum(n_entries))
+    k_idx, k_scale = _index_keys(seed, total, quantized, device)
+    main = _main_kv_gauss(seed, total, quantized, device)
+    Q = int(q_pos.shape[0])
+    layers = [_layer(seed, li, m, Q, swa_total, quantized, device,
+                     with_indexer=(m in ("full", "reindex")))
+              for li, m in enumerate(modes)]
+    return Workload(name="mini", seed=seed, quantized=quantized, ratio=ratio,
+                    n_entries=list(n_entries), seq_base=seq_base, q_seq=q_seq,
+                    q_pos=q_pos, k_idx=k_idx, k_scale=k_scale, main_kv=main,
+                    swa_base=swa_base, swa_pos0=swa_pos0, layers=layers,
+                    topk=topk, n_blocks=n_blocks, block_size=block_size)
+
+
+def _prefill_m2(seed, device):
+    """Encoder Full-layer prefill chunk: 65,536 tokens compressed in pairs to
+    32,768 entries; 4,096 causal queries at the end of the sequence."""
+    n_tok, n_q = 65536, 4096
+    n_ent = n_tok // 2
+    main_parts = []
+    for c, r0 in enumerate(range(0, n_ent, CHUNK_ROWS // 2)):
+        n = min(CHUNK_ROWS // 2, n_ent - r0)
+        cc = _randn((2 * n, D_ATT), seed, _T_C, c, device)
+        zz = _randn((2 * n, D_ATT), seed, _T_Z, c, device)
+        main_parts.append(encode_fp4_records(compress_pairs_input(cc, zz)))
+    main = torch.cat(main_parts, 0)
+    k_idx, k_scale = _index_keys(seed, n_ent, True, device)
+    positions = [list(range(n_tok - n_q, n_tok))]
+    seq_base, q_seq, q_pos, swa_base, swa_pos0, swa_total = _decode_layout(
+        [n_ent], None, 2, device, positions)
+    layers = [_layer(seed, 0, "full", n_q, swa_total, True, device, True)]
+    return Workload(name="prefill_m2_chunk", seed=seed, quantized=True, ratio=2,
+                    n_entries=[n_ent], seq_base=seq_base, q_seq=q_seq, q_pos=q_pos,
+                    k_idx=k_idx, k_scale=k_scale, main_kv=main, swa_base=swa_base,
+                    swa_pos0=swa_pos0, layers=layers)
+
+
+def make_workload(name, device="cpu"):
+    """The five configurations, by name (see CONFIG_NAMES)."""
+    if name == "tiny_full_fp32":
+        w = mini_workload(0, [2048], q_per_seq=16, ratio=1, quantized=False,
+                          modes=("full",), device=device)
+    elif name == "decode_128k":
+        # Full layer at 128K, batch 8; a Reindex layer on the same cache
+        # exercises pool scoring at the same context.
+        w = mini_workload(1, [131072] * 8, q_per_seq=1, ratio=1, quantized=True,
+                          modes=("full", "reindex"), device=device)
+    elif name == "prefill_m2_chunk":
+        w = _prefill_m2(2, device)
+    elif name == "reindex_1m":
+        w = mini_workload(3, [1 << 20] * 2, q_per_seq=1, ratio=1, quantized=True,
+                          modes=("full", "reindex"), device=device)
+    elif name == "decoder_group_256k":
+        w = mini_workload(4, [262144] * 64, q_per_seq=1, ratio=1, quantized=True,
+                          modes=("full", "reuse", "reuse", "reuse",
+                                 "reindex", "reuse", "reuse", "reuse"),
+                          device=device)
+    else:
+        raise ValueError(f"unknown workload {name!r}; known: {CONFIG_NAMES}")
+    w.name = name
+    return w

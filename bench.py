@@ -1,0 +1,265 @@
+"""Benchmark of the CSA2 hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+for the 128K decode workload (batch 8, 131,072 visible entries per query) the
+Full layer scores every visible index key, builds the block-max candidate
+pool, selects the top-512 and runs sparse attention; a Reindex layer on the
+same cache then scores only the pool, selects its own top-512 and runs its
+attention.  Inputs are resident in HBM before timing starts.  Steps rotate
+over several independent copies of the inputs so that the 256 MB
+Infinity Cache cannot serve a step from the previous step's reads.
+
+One JSON line is printed: whole-step throughput in index keys scored per
+second (plus sparse-attention queries per second), the roofline of the
+dominant kernel measured with HIP events on the launch stream, and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "index keys scored/s + sparse-attn queries/s at 128K ctx; % HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+ATTN_BYTES_PER_QUERY = 512 * 320 + 128 * 528 + 65536 + 65536 + 2048   # 364,544
+INDEX_BYTES_PER_KEY = 128 + 4 + 4                                       # key + scale + score
+SCORE_BYTES = 4
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="decode_128k")
+    ap.add_argument("--copies", type=int, default=3,
+                    help="independent input copies the steps rotate over")
+    ap.add_argument("--cpu-sample", type=int, default=None,
+                    help="queries of the CPU-oracle sample (default: all queries, max 8)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def _source_hash():
+    h = hashlib.sha1()
+    csrc = os.path.join(ROOT, "top_sparse_long_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def _stage_work(run, stage):
+    """Algorithmic bytes one launch of a stage moves (HBM-bound stages)."""
+    wl = run.wl
+    nvis = wl.n_vis().clamp(max=run.n_cols)
+    if stage == "index_scores_dense":
+        return float(nvis.sum().item()) * INDEX_BYTES_PER_KEY, int(nvis.sum().item())
+    if stage == "index_scores_pool":
+        return float(wl.Q * run.pool_cols) * INDEX_BYTES_PER_KEY, wl.Q * run.pool_cols
+    if stage in ("topk_dense", "block_candidates"):
+        return float(nvis.sum().item()) * SCORE_BYTES, int(nvis.sum().item())
+    if stage == "topk_pool":
+        return float(wl.Q * run.pool_cols) * SCORE_BYTES, wl.Q * run.pool_cols
+    if stage == "sparse_attn":
+        return float(wl.Q) * ATTN_BYTES_PER_QUERY, wl.Q
+    raise KeyError(stage)
+
+
+def _traffic(stage, workload, launches_bytes):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("source_sha1") != _source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, n_sample):
+    """Time the oracle on the first n_sample queries of the workload's whole
+    path (both layers), on the host cores."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+    import oracle
+
+    sample = list(range(min(n_sample, wl.Q)))
+    q_seq = wl.q_seq.cpu().numpy()
+    q_pos = wl.q_pos.cpu().numpy()
+    # host copies of the inputs the sample touches (not timed)
+    seqs = sorted(set(int(q_seq[t]) for t in sample))
+    inputs = {}
+    for b in seqs:
+        base, n = int(wl.seq_base[b]), int(wl.n_entries[b])
+        rows = torch.arange(base, base + n, device=wl.k_idx.device)
+        inputs[b] = (wl.k_idx[rows].cpu().numpy(), wl.k_scale[rows].cpu().numpy(),
+                     wl.main_kv[rows].cpu().numpy())
+    layers = []
+    for lay in wl.layers:
+        d = {"mode": lay.mode, "q": lay.q[sample].cpu().numpy(), "swa": lay.swa.cpu().numpy(),
+             "sink": lay.sink.cpu().numpy().astype(np.float64)}
+        if lay.q_idx is not None:
+            d["q_idx"] = lay.q_idx[sample].cpu().numpy()
+            d["q_scale"] = lay.q_scale[sample].cpu().numpy()
+            d["w"] = lay.w[sample].cpu().numpy()
+        layers.append(d)
+    swa_base = wl.swa_base.cpu().numpy()
+    swa_pos0 = wl.swa_pos0.cpu().numpy()
+
+    keys_scored = 0
+    t0 = time.perf_counter()
+    for j, t in enumerate(sample):
+        b = int(q_seq[t])
+        kc, ks, mk = inputs[b]
+        k_rows = oracle.decode_e4m3_rows(kc, ks)
+        main_rows = oracle.decode_fp4_records(mk)
+        pos1, seq0, base0 = np.array([q_pos[t]]), np.array([0]), np.array([0])
+        n = int(oracle.visible_count(pos1, wl.ratio)[0])
+        cand = idx = None
+        for li, lay in enumerate(layers):
+            if lay["mode"] in ("full", "reindex"):
+                qv = oracle.decode_e4m3_rows(lay["q_idx"][j:j + 1], lay["q_scale"][j:j + 1])
+                wv = oracle.decode_bf16(lay["w"][j:j + 1])
+            if lay["mode"] == "full":
+                sc = oracle.index_scores_dense(qv, wv, k_rows, base0, seq0, pos1, wl.ratio, n)
+                keys_scored += n
+                if any(l["mode"] == "reindex" for l in layers[li + 1:]):
+                    cand = oracle.block_candidates(sc, pos1, wl.ratio, wl.block_size, wl.n_blocks)
+                idx = oracle.topk_rows_dense(sc, pos1, wl.ratio, wl.topk)
+            elif lay["mode"] == "reindex":
+                sc = oracle.index_scores_pool(qv, wv, k_rows, base0, seq0, pos1, wl.ratio, cand,
+                                              wl.block_size)
+                keys_scored += sc.shape[1]
+                idx = oracle.topk_rows_pool(sc, cand, wl.block_size, wl.topk)
+            swa = oracle.decode_swa_records(lay["swa"])
+            oracle.sparse_attn(oracle.decode_bf16(lay["q"][j:j + 1]), main_rows, base0, idx, swa,
+                               swa_base[b:b + 1], swa_pos0[b:b + 1], None, wl.window, seq0, pos1,
+                               lay["sink"], wl.softmax_scale, wl.ratio)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": keys_scored / dt, "unit": "index keys scored/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(sample)} of {wl.Q} queries through every layer of the step "
+                      f"(float64 NumPy oracle, {dt:.1f} s wall)"}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
+              "path is a design in DESIGN.md, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    import top_sparse_long_amd as tsl
+    from top_sparse_long_amd.driver import LayerRunner
+
+    tsl.load()
+    dev = "cuda"
+    runs = [LayerRunner(synth.make_workload(args.workload, device=dev, seed_offset=1000 * c))
+            for c in range(max(1, args.copies))]
+    torch.cuda.synchronize()
+
+    # calibration copy for the counter runs (outside the timed region): a
+    # plain 256 MiB device copy whose FETCH/WRITE bytes are known
+    calib_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
+
+    for i in range(args.warmup):
+        runs[i % len(runs)].run()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    events = []
+
+    def make_mark(rec):
+        def mark(name):
+            ev = torch.cuda.Event(enable_timing=True)
+            ev.record(stream)
+            rec.append((name, ev))
+        return mark
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        rec = []
+        runs[i % len(runs)].run(mark=make_mark(rec))
+        events.append(rec)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-stage GPU time from the events
+    stage_ms, stage_n = {}, {}
+    for rec in events:
+        for (name, ev), (_, ev2) in zip(rec[:-1], rec[1:]):
+            stage_ms[name] = stage_ms.get(name, 0.0) + ev.elapsed_time(ev2)
+            stage_n[name] = stage_n.get(name, 0) + 1
+    run0 = runs[0]
+    stages = {}
+    for name in stage_ms:
+        avg_ms = stage_ms[name] / stage_n[name]
+        nbytes, units = _stage_work(run0, name)
+        stages[name] = {"avg_us": avg_ms * 1e3, "launches_per_step": stage_n[name] // args.steps,
+                        "algorithmic_bytes": nbytes, "units": units,
+                        "hbm_frac": nbytes / (avg_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+    dom = max(stages, key=lambda s: stages[s]["avg_us"] * stages[s]["launches_per_step"])
+    d = stages[dom]
+    achieved = d["algorithmic_bytes"] / (d["avg_us"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                "traffic": _traffic(dom, args.workload, d["algorithmic_bytes"])}
+
+    wl = run0.wl
+    keys = 0
+    n_attn = 0
+    for lay in wl.layers:
+        if lay.mode == "full":
+            keys += int(wl.n_vis().clamp(max=run0.n_cols).sum().item())
+        elif lay.mode == "reindex":
+            keys += wl.Q * run0.pool_cols
+        n_attn += wl.Q
+    value = keys / (ms_per_step * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        n_sample = args.cpu_sample if args.cpu_sample is not None else min(8, wl.Q)
+        cpu = cpu_baseline(wl, n_sample)
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "index keys scored/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 index scores, f16 attention (fp32 accumulate)", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": wl.Q, "ctx_entries": wl.max_cols(),
+                   "ratio": wl.ratio, "layers": [l.mode for l in wl.layers],
+                   "topk": wl.topk, "pool_blocks": wl.n_blocks, "block_size": wl.block_size,
+                   "input_copies": len(runs)},
+        "sparse_attn_queries_per_s": n_attn / (ms_per_step * 1e-3),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages": stages,
+        "source_sha1": _source_hash(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+/*
+ * csa2.h — C ABI of the CSA2 global-attention hot path for MI355X (gfx950).
+ *
+ * The four calls follow the pages' statement of the problem:
+ *   csa2_index_scores      Lightning-Indexer scores, dense or over a candidate pool
+ *   csa2_block_candidates  block-max candidate pool (hierarchical sparse indexer)
+ *   csa2_topk              token-level top-k selection
+ *   csa2_sparse_attn       joint-softmax sparse MQA attention with a sink
+ * Sources are cited as page + section:
+ *   [CSA2]   zdszero.github.io/csa2.html (CSA2 deep-dive)
+ *   [3MODES] xhh.club, "DeepSeek-V4.1 model structure (2): CSA2's three modes"
+ *   [REPORT] 10100.com, "DeepSeek-V4.1-Flash technical report reading"
+ *   [DSA]    zdszero.github.io/dsa.html (DeepSeek Sparse Attention)
+ *
+ * Conventions for every call:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
+ *     stated otherwise.  The library allocates no device memory, keeps no
+ *     state between calls and never synchronises: work is enqueued on
+ *     `stream` (a hipStream_t passed as void*; NULL = the null stream) and
+ *     the call returns once it is enqueued.  Calls are thread-safe.
+ *   - Return value: CSA2_OK (0) or a negative csa2_status.  Argument checks
+ *     run on the host before anything is enqueued; a failed check enqueues
+ *     nothing.  csa2_last_error() gives a message for the last failure on
+ *     the calling thread.  No C++ exception crosses this interface.
+ *   - Device-side contents (positions, indices, candidate ids) cannot be
+ *     checked on the host.  Out-of-range contents are clamped or skipped as
+ *     each call states; they never make a kernel read outside the buffers
+ *     the caller described.
+ *   - Integer positions are main-KV entry positions within a sequence
+ *     (0-based).  A query at token position p with compression ratio m sees
+ *     the entries [0, (p + 1) / m) of its sequence ([CSA2] "the pool does not
+ *     reduce storage").
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    CSA2_OK = 0,
+    CSA2_ERR_INVALID_ARG = -1,  /* null pointer, negative size, misaligned pointer or stride */
+    CSA2_ERR_UNSUPPORTED = -2,  /* a size or dtype combination outside the compiled kernels */
+    CSA2_ERR_WORKSPACE = -3,    /* workspace missing or smaller than the size query returns */
+    CSA2_ERR_HIP = -4           /* the HIP runtime reported an error while enqueuing */
+} csa2_status;
+
+typedef enum {
+    CSA2_F32 = 0,       /* IEEE binary32 */
+    CSA2_BF16 = 1,      /* bfloat16 */
+    CSA2_FP8_E4M3 = 2,  /* OCP FP8 E4M3FN codes, one byte per element, fp32 scales */
+    CSA2_FP4_E2M1 = 3   /* OCP FP4 E2M1 codes, two per byte (element 2i in the low
+                           nibble of byte i), one fp32 scale per 32 elements */
+} csa2_dtype;
+
+/*
+ * A [rows, dim] matrix, optionally quantized.  Row r's elements start at
+ * (const char*)data + r * row_stride; for quantized dtypes its scales start
+ * at scale + r * scale_stride (in floats) and element e of the row decodes
+ * to code(e) * scale[e / group], with group = 128 for FP8 index rows and SWA
+ * rows and group = 32 for FP4 main-KV rows.  A record layout (codes followed
+ * by scales in one row) is described by pointing `scale` into the first
+ * record.  `scale` is NULL for F32 and BF16.
+ * Alignment: data and row_stride multiples of 16 bytes; scale and
+ * scale_stride multiples of 4 bytes / 1 float.
+ */
+typedef struct {
+    const void* data;
+    const float* scale;
+    int64_t row_stride;     /* bytes */
+    int64_t scale_stride;   /* floats */
+    csa2_dtype dtype;
+} csa2_rows;
+
+/*
+ * csa2_index_scores — Lightning-Indexer scores
+ *   I[t, s] = sum_h w[t, h] * ReLU(q[t, h] . k[s])
+ * ([CSA2] "per-layer attention computation", item 4; [DSA] "Lightning
+ * Indexer"), with 32 heads x 128 dims.  q and k are the dequantized rows; for
+ * FP8 inputs the kernel multiplies codes exactly in fp32 and applies the
+ * q scale to the gate and the k scale after the head sum ([DSA] "fp8 and
+ * scale absorption"), which equals the dequantized formula because the
+ * scales are positive.  No 1/sqrt(d) or 1/sqrt(H) factor is applied: fold any
+ * such factor into w.
+ *
+ *   q_idx     rows = Q * H_I (row t*H_I + h is q[t, h]), dim d_I.
+ *             FP8_E4M3 with one scale per row, or F32.
+ *   w         [Q, H_I] contiguous gates, w_dtype BF16 or F32.
+ *   k_idx     rows = all entries of all sequences, dim d_I; same dtype as
+ *             q_idx (FP8_E4M3 with one scale per row, or F32).
+ *   seq_base  [B] int64: first k_idx row of each sequence.
+ *   q_seq     [Q] int32: sequence of each query (0 <= q_seq < B).
+ *   q_pos     [Q] int32: token position of each query (>= 0).
+ *   ratio     compression ratio m (1 or 2).
+ *   cand      NULL: dense mode.  Row t gets n_cols columns: column s < the
+ *             visible count holds I[t, s]; the others hold -inf.
+ *             Non-NULL: pool mode ([CSA2] "where attention is computed":
+ *             the candidate indexer scores only the candidate blocks).
+ *             [Q, n_cand_blocks] int32 block ids; column c*block_size + j of
+ *             row t holds I[t, cand[t, c]*block_size + j], or -inf when
+ *             cand[t, c] < 0 or that position is not visible.  n_cols must
+ *             equal n_cand_blocks * block_size.
+ *   scores    [Q, score_stride] fp32 output; score_stride >= n_cols,
+ *             multiple of 4; 16-byte aligned.
+ *   Supported: H_I = 32, d_I = 128 (FP8); H_I <= 64, d_I = 128 (F32);
+ *   block_size in {1, 2, 4, 8, 16, 32, 64}.
+ */
+int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
+                      const csa2_rows* k_idx, const int64_t* seq_base,
+                      const int32_t* q_seq, const int32_t* q_pos, int32_t ratio,
+                      const int32_t* cand, int32_t n_cand_blocks, int32_t block_size,
+                      float* scores, int64_t score_stride, int32_t n_cols,
+                      int32_t Q, int32_t H_I, int32_t d_I, void* stream);
+
+/*
+ * csa2_block_candidates — the candidate pool of the hierarchical sparse
+ * indexer ([CSA2] "hierarchical sparse indexer", "which positions are in the
+ * pool"; [REPORT] section 5).  For row t with n = min(visible, n_cols)
+ * columns: blocks of block_size positions are scored by their largest score
+ * (a partial last block uses its visible members), the block holding the
+ * latest visible position (n - 1) / block_size is always kept (it is ranked
+ * first), and the remaining places go to the best blocks, ties to the lower
+ * block id; blocks whose maximum is -inf are never chosen.
+ *   scores    dense scores as written by csa2_index_scores.
+ *   cand      [Q, n_blocks] int32 output: chosen block ids ascending, then -1.
+ *   workspace device memory of at least
+ *             csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks) bytes
+ *             (may be NULL when that size is 0).
+ *   Supported: n_blocks <= 4096, block_size in {1, 2, 4, 8, 16, 32, 64}.
+ */
+int csa2_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
+                          const int32_t* q_pos, int32_t ratio, int32_t block_size,
+                          int32_t n_blocks, int32_t* cand, void* workspace,
+                          size_t workspace_bytes, int32_t Q, void* stream);
+
+size_t csa2_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t block_size,
+                                            int32_t n_blocks);
+
+/*
+ * csa2_topk — token-level top-k ([CSA2] "per-layer attention computation",
+ * item 4; [DSA] "Top-k: tokens, not blocks").  Chooses the k largest finite
+ * scores of each row, ties to the lower position; -inf is never chosen, so a
+ * row with fewer than k finite scores yields all of them ([DSA] "design").
+ *   Dense mode (cand == NULL): row t has min(n_cols, visible) columns when
+ *             q_pos is given, n_cols when q_pos is NULL; column s is position s.
+ *   Pool mode (cand != NULL): rows are compact pool scores as written by
+ *             csa2_index_scores in pool mode; column c*block_size + j is
+ *             position cand[t, c]*block_size + j; columns with cand < 0 are
+ *             never chosen; n_cols must equal n_cand_blocks * block_size.
+ *             Ties go to the lower position, i.e. the lower column when cand
+ *             is ascending, as csa2_block_candidates writes it.
+ *   idx       [Q, k] int32 output: chosen positions ascending, then -1.
+ *   workspace at least csa2_topk_workspace_size(Q, n_cols, k) bytes.
+ *   Supported: 1 <= k <= 2048.
+ */
+int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols,
+              const int32_t* q_pos, int32_t ratio, const int32_t* cand,
+              int32_t n_cand_blocks, int32_t block_size, int32_t k, int32_t* idx,
+              void* workspace, size_t workspace_bytes, int32_t Q, void* stream);
+
+size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k);
+
+/*
+ * csa2_sparse_attn — core sparse attention ([CSA2] "per-layer attention
+ * computation"; [3MODES] Q&A on Reuse layers).  For query t at position p of
+ * sequence b and head i, the keys are the SWA rows of positions
+ * [max(lo_b, p - window + 1), p] (oldest first) followed by the main rows
+ * idx[t, j] >= 0; K = V (MQA, one 512-dim vector per key).  With
+ * z_j = softmax_scale * q[t, i] . K_j:
+ *   out[t, i] = sum_j exp(z_j) K_j / (sum_j exp(z_j) + exp(attn_sink[i]))
+ *   lse[t, i] = log(sum_j exp(z_j) + exp(attn_sink[i]))
+ * The sink is a raw logit and enters only the denominator.  A position in
+ * both the window and idx contributes both vectors.  RoPE is already applied
+ * to the cached rows; the kernel applies none.
+ *
+ *   q         [Q, H, D] contiguous, q_dtype BF16 or F32.
+ *   main_kv   rows = all main-KV entries: FP4_E2M1 with 16 scales per row
+ *             (e.g. 320-byte records: 256 code bytes then 16 fp32 scales),
+ *             or F32.
+ *   main_base [B] int64: first main_kv row of each sequence.
+ *   idx       [Q, k] int32 main positions; entries < 0 are skipped, and so
+ *             are entries at or beyond the query's visible count
+ *             (q_pos + 1) / ratio, so no row outside the visible prefix of the
+ *             sequence is read.
+ *   swa_kv    the layer's SWA rows: FP8_E4M3 with 4 scales per row (e.g.
+ *             528-byte records), or F32.  Position p of sequence b is row
+ *             swa_base[b] + p - swa_pos0[b]; positions below swa_pos0[b] are
+ *             skipped, so the caller stores at least the window of every query.
+ *   swa_lo    NULL (lo = 0) or [B] int32 first position of the bounded-replay
+ *             segment ([CSA2] "CED": the query at i sees SWA keys in
+ *             [max(s, i - W + 1), i]).
+ *   window    W >= 0 (128 in the pages' configuration).
+ *   attn_sink [H] fp32.
+ *   out       [Q, H, D] output, out_dtype BF16 or F32.
+ *   lse       NULL or [Q, H] fp32 output.
+ *   Supported: D = 512; H a multiple of 16 up to 128; k <= 2048.
+ *   Quantized path: q BF16, main FP4_E2M1, swa FP8_E4M3, out BF16 or F32.
+ *   Float path: q, main, swa F32, out F32.
+ */
+int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv,
+                     const int64_t* main_base, const int32_t* idx, int32_t k,
+                     const csa2_rows* swa_kv, const int64_t* swa_base,
+                     const int32_t* swa_pos0, const int32_t* swa_lo, int32_t window,
+                     const int32_t* q_seq, const int32_t* q_pos, int32_t ratio,
+                     const float* attn_sink, float softmax_scale, void* out,
+                     csa2_dtype out_dtype, float* lse, int32_t Q, int32_t H, int32_t D,
+                     void* stream);
+
+/* Name of a status code (static string). */
+const char* csa2_status_string(int status);
+
+/* Message describing the last failed call on the calling thread (static
+ * thread-local buffer; empty when no call has failed). */
+const char* csa2_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int csa2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

@@ -279,22 +279,24 @@ def block_candidates(scores, q_pos, ratio, block_size, n_blocks):
 
 
 def attention_keys(t, main_rows, main_base, idx, swa_rows, swa_base, swa_pos0,
-                   swa_lo, window, q_seq, q_pos):
-    """Key matrix of query t: SWA rows (oldest first), then main rows."""
+                   swa_lo, window, q_seq, q_pos, ratio=1):
+    """Key matrix of query t: SWA rows (oldest first), then main rows.
+    Reading: an idx entry that is negative or not visible to the query
+    ((pos+1)//ratio or beyond) names no key."""
     b = int(q_seq[t])
     p = int(q_pos[t])
     lo = 0 if swa_lo is None else int(swa_lo[b])
     first = max(lo, p - window + 1)
     swa_idx = int(swa_base[b]) + np.arange(first, p + 1) - int(swa_pos0[b])
     sel = np.asarray(idx[t], dtype=np.int64)
-    sel = sel[sel >= 0]
+    sel = sel[(sel >= 0) & (sel < (p + 1) // int(ratio))]
     main_idx = int(main_base[b]) + sel
     return np.concatenate([np.asarray(swa_rows[swa_idx], dtype=np.float64),
                            np.asarray(main_rows[main_idx], dtype=np.float64)], 0)
 
 
 def sparse_attn(q, main_rows, main_base, idx, swa_rows, swa_base, swa_pos0,
-                swa_lo, window, q_seq, q_pos, sink, scale):
+                swa_lo, window, q_seq, q_pos, sink, scale, ratio=1):
     """q [Q, H, D]; main_rows [sum N, D]; swa_rows [rows, D]; idx [Q, k] with
     -1 = no key; sink [H].  Returns (out [Q, H, D], lse [Q, H]) where
     lse = log(sum_j exp(z_j) + exp(sink))."""
@@ -305,7 +307,7 @@ def sparse_attn(q, main_rows, main_base, idx, swa_rows, swa_base, swa_pos0,
     lse = np.zeros((Q, H))
     for t in range(Q):
         K = attention_keys(t, main_rows, main_base, idx, swa_rows, swa_base,
-                           swa_pos0, swa_lo, window, q_seq, q_pos)   # [n, D]
+                           swa_pos0, swa_lo, window, q_seq, q_pos, ratio)   # [n, D]
         z = scale * (q[t] @ K.T)                                      # [H, n]
         zmax = z.max(axis=1) if z.shape[1] else np.full(H, NEG_INF)
         M = np.maximum(zmax, sink)
@@ -400,6 +402,6 @@ def run_layers(layers, k_rows, main_rows, seq_base, q_seq, q_pos, ratio,
         r["out"], r["lse"] = sparse_attn(lay["q"], main_rows, seq_base,
                                          slots["topk_idxs"], lay["swa_rows"],
                                          swa_base, swa_pos0, None, window,
-                                         q_seq, q_pos, lay["sink"], scale)
+                                         q_seq, q_pos, lay["sink"], scale, ratio)
         results.append(r)
     return results

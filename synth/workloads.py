@@ -110,6 +110,19 @@ class Workload:
     def max_cols(self):
         return int(self.n_vis().max().item())
 
+    def to(self, device):
+        """Copy every tensor to `device` (the values do not change)."""
+        def mv(x):
+            return None if x is None else x.to(device)
+        out = Workload(**{f: getattr(self, f) for f in self.__dataclass_fields__})
+        for f in ("seq_base", "q_seq", "q_pos", "k_idx", "k_scale", "main_kv", "swa_base",
+                  "swa_pos0"):
+            setattr(out, f, mv(getattr(self, f)))
+        out.layers = [Layer(mode=l.mode, q=mv(l.q), swa=mv(l.swa), sink=mv(l.sink),
+                            q_idx=mv(l.q_idx), q_scale=mv(l.q_scale), w=mv(l.w))
+                      for l in self.layers]
+        return out
+
 
 def _chunked(total, fn):
     parts = []
@@ -249,23 +262,25 @@ def _prefill_m2(seed, device):
                     swa_pos0=swa_pos0, layers=layers)
 
 
-def make_workload(name, device="cpu"):
-    """The five configurations, by name (see CONFIG_NAMES)."""
+def make_workload(name, device="cpu", seed_offset=0):
+    """The five configurations, by name (see CONFIG_NAMES).  seed_offset
+    draws an independent copy of the same shapes."""
+    o = seed_offset
     if name == "tiny_full_fp32":
-        w = mini_workload(0, [2048], q_per_seq=16, ratio=1, quantized=False,
+        w = mini_workload(0 + o, [2048], q_per_seq=16, ratio=1, quantized=False,
                           modes=("full",), device=device)
     elif name == "decode_128k":
         # Full layer at 128K, batch 8; a Reindex layer on the same cache
         # exercises pool scoring at the same context.
-        w = mini_workload(1, [131072] * 8, q_per_seq=1, ratio=1, quantized=True,
+        w = mini_workload(1 + o, [131072] * 8, q_per_seq=1, ratio=1, quantized=True,
                           modes=("full", "reindex"), device=device)
     elif name == "prefill_m2_chunk":
-        w = _prefill_m2(2, device)
+        w = _prefill_m2(2 + o, device)
     elif name == "reindex_1m":
-        w = mini_workload(3, [1 << 20] * 2, q_per_seq=1, ratio=1, quantized=True,
+        w = mini_workload(3 + o, [1 << 20] * 2, q_per_seq=1, ratio=1, quantized=True,
                           modes=("full", "reindex"), device=device)
     elif name == "decoder_group_256k":
-        w = mini_workload(4, [262144] * 64, q_per_seq=1, ratio=1, quantized=True,
+        w = mini_workload(4 + o, [262144] * 64, q_per_seq=1, ratio=1, quantized=True,
                           modes=("full", "reuse", "reuse", "reuse",
                                  "reindex", "reuse", "reuse", "reuse"),
                           device=device)

@@ -1,0 +1,163 @@
+"""The C-ABI library loads, exports what include/csa2.h declares, and rejects
+bad arguments on the host (no GPU needed: every call here fails its host
+checks before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import top_sparse_long_amd as tsl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tsl.load()
+    names = _declared()
+    assert set(tsl.EXPORTED) == set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    lib = tsl.load()
+    assert lib.csa2_version() >= 100
+    assert lib.csa2_status_string(0) == b"CSA2_OK"
+    assert lib.csa2_status_string(-3) == b"CSA2_ERR_WORKSPACE"
+    assert lib.csa2_status_string(7) == b"CSA2_ERR_UNKNOWN"
+
+
+FAKE = 0x100000   # never dereferenced: every call below fails a host check
+
+
+def _rows(dtype, stride=128, scale=True):
+    return tsl.csa2_rows(FAKE, FAKE if scale else None, stride, 1, dtype)
+
+
+def _scores(lib, **kw):
+    a = dict(q=_rows(tsl.CSA2_FP8_E4M3), w=FAKE, wdt=tsl.CSA2_BF16, k=_rows(tsl.CSA2_FP8_E4M3),
+             seq_base=FAKE, q_seq=FAKE, q_pos=FAKE, ratio=1, cand=None, ncb=0, bs=8,
+             scores=FAKE, stride=1024, n_cols=1024, Q=1, H=32, d=128)
+    a.update(kw)
+    st = lib.csa2_index_scores(ctypes.byref(a["q"]), a["w"], a["wdt"], ctypes.byref(a["k"]),
+                               a["seq_base"], a["q_seq"], a["q_pos"], a["ratio"], a["cand"],
+                               a["ncb"], a["bs"], a["scores"], a["stride"], a["n_cols"], a["Q"],
+                               a["H"], a["d"], None)
+    return st, lib.csa2_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(scores=None), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(q_pos=None), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(Q=-1), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(ratio=3), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(d=64), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(H=64), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(wdt=tsl.CSA2_FP8_E4M3), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(k=_rows(tsl.CSA2_F32, 512, False)), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(stride=1000), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(stride=1022), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(scores=FAKE + 4), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(q=_rows(tsl.CSA2_FP8_E4M3, 130)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(cand=FAKE, ncb=100, bs=8), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(cand=FAKE, ncb=128, bs=6, n_cols=768), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(q=_rows(tsl.CSA2_FP8_E4M3, scale=False), k=_rows(tsl.CSA2_FP8_E4M3, scale=False)),
+     tsl.CSA2_ERR_INVALID_ARG),
+])
+def test_index_scores_rejects(kw, status):
+    st, msg = _scores(tsl.load(), **kw)
+    assert st == status and msg.startswith("csa2_index_scores")
+
+
+def test_topk_rejects():
+    lib = tsl.load()
+    assert lib.csa2_topk(None, 64, 64, FAKE, 1, None, 0, 8, 8, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 1, None, 0, 8, 4096, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_UNSUPPORTED
+    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 1, None, 0, 8, 0, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_topk(FAKE, 32, 64, FAKE, 1, None, 0, 8, 8, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 5, None, 0, 8, 8, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_UNSUPPORTED
+    # long rows need a workspace
+    need = lib.csa2_topk_workspace_size(4, 200000, 512)
+    assert need > 0
+    st = lib.csa2_topk(FAKE, 200000, 200000, FAKE, 1, None, 0, 8, 512, FAKE, FAKE, need - 1, 4, None)
+    assert st == tsl.CSA2_ERR_WORKSPACE
+    assert "workspace" in lib.csa2_last_error().decode()
+
+
+def test_block_candidates_rejects():
+    lib = tsl.load()
+    assert lib.csa2_block_candidates(FAKE, 64, 64, None, 1, 8, 16, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert lib.csa2_block_candidates(FAKE, 64, 64, FAKE, 1, 12, 16, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_UNSUPPORTED
+    assert lib.csa2_block_candidates(FAKE, 64, 64, FAKE, 1, 8, 8192, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_UNSUPPORTED
+    need = lib.csa2_block_candidates_workspace_size(2, 1 << 20, 8, 2048)
+    assert need > 0
+    assert lib.csa2_block_candidates(FAKE, 1 << 20, 1 << 20, FAKE, 1, 8, 2048, FAKE, FAKE, 0, 2,
+                                     None) == tsl.CSA2_ERR_WORKSPACE
+
+
+def test_workspace_sizes():
+    lib = tsl.load()
+    assert lib.csa2_topk_workspace_size(64, 32768, 512) == 0      # one chunk per row
+    assert lib.csa2_topk_workspace_size(8, 131072, 512) > 0
+    assert lib.csa2_block_candidates_workspace_size(64, 262144, 8, 2048) == 0
+    assert lib.csa2_block_candidates_workspace_size(2, 1 << 20, 8, 2048) > 0
+    assert lib.csa2_topk_workspace_size(0, 100, 5) == 0
+
+
+def _attn(lib, **kw):
+    a = dict(q=FAKE, qdt=tsl.CSA2_BF16, main=tsl.csa2_rows(FAKE, FAKE, 320, 80, tsl.CSA2_FP4_E2M1),
+             main_base=FAKE, idx=FAKE, k=512,
+             swa=tsl.csa2_rows(FAKE, FAKE + 512, 528, 132, tsl.CSA2_FP8_E4M3),
+             swa_base=FAKE, swa_pos0=FAKE, swa_lo=None, window=128, q_seq=FAKE, q_pos=FAKE,
+             ratio=1, sink=FAKE, scale=0.044, out=FAKE, odt=tsl.CSA2_BF16, lse=None, Q=1, H=64,
+             D=512)
+    a.update(kw)
+    return lib.csa2_sparse_attn(a["q"], a["qdt"], ctypes.byref(a["main"]), a["main_base"],
+                                a["idx"], a["k"], ctypes.byref(a["swa"]), a["swa_base"],
+                                a["swa_pos0"], a["swa_lo"], a["window"], a["q_seq"], a["q_pos"],
+                                a["ratio"], a["sink"], ctypes.c_float(a["scale"]), a["out"],
+                                a["odt"], a["lse"], a["Q"], a["H"], a["D"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(sink=None), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(D=576), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(H=40), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(k=4096), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(window=-1), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(qdt=tsl.CSA2_F32), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(odt=tsl.CSA2_FP8_E4M3), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(out=FAKE + 8), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(main=tsl.csa2_rows(FAKE, FAKE + 4, 320, 80, tsl.CSA2_FP4_E2M1)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(main=tsl.csa2_rows(FAKE, None, 320, 80, tsl.CSA2_FP4_E2M1)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(ratio=4), tsl.CSA2_ERR_UNSUPPORTED),
+])
+def test_sparse_attn_rejects(kw, status):
+    lib = tsl.load()
+    assert _attn(lib, **kw) == status
+    assert lib.csa2_last_error().decode().startswith("csa2_sparse_attn")
+
+
+def test_zero_queries_is_a_no_op_after_checks():
+    lib = tsl.load()
+    # Q == 0 passes every check and enqueues nothing, so it is safe without a GPU
+    st, _ = _scores(lib, Q=0)
+    assert st == tsl.CSA2_OK
+    assert _attn(lib, Q=0) == tsl.CSA2_OK

@@ -1,0 +1,139 @@
+"""Parity at the five configurations' full sizes, in the launch configuration
+the benchmark times.  Every stage runs on the whole workload; the oracle then
+checks sampled queries stage by stage, each fed the GPU's own upstream
+outputs (scores for selection, the pool for pool scoring, the indices for
+attention), plus the end-to-end top-k sets against the oracle's own float64
+scores with the gap rule."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import top_sparse_long_amd as tsl
+from top_sparse_long_amd.driver import LayerRunner
+from tests import oracle_io
+from tests.parity import check_scores, check_index_table, check_topk_gap, check_attention, row_tau
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+SAMPLES = {"tiny_full_fp32": None, "decode_128k": [0, 5], "prefill_m2_chunk": [0, 1, 2047, 4095],
+           "reindex_1m": [0, 1], "decoder_group_256k": [0, 37]}
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tsl.load()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _seq_keys(wl, b, n):
+    base = int(wl.seq_base[b])
+    rows = torch.arange(base, base + n, device=wl.k_idx.device)
+    return oracle_io.index_k_rows(wl, rows)
+
+
+def _gathered_main(wl, b, idx_row, n_vis):
+    """Decode only the main rows a query's indices name; return them with
+    the indices renumbered into that compact array."""
+    sel = idx_row[idx_row >= 0]
+    assert np.all(sel < n_vis), "an index beyond the visible prefix"
+    rows = torch.from_numpy(int(wl.seq_base[b]) + sel).to(wl.main_kv.device)
+    compact = np.full_like(idx_row, -1)
+    compact[:len(sel)] = np.arange(len(sel))
+    return oracle_io.main_rows(wl, rows), compact
+
+
+@pytest.mark.parametrize("name", list(synth.CONFIG_NAMES))
+def test_config_parity(name):
+    print(f"[case] config {name}", flush=True)
+    gen_dev = "cpu" if name == "tiny_full_fp32" else DEV
+    wl = synth.make_workload(name, device=gen_dev).to(DEV)
+    run = LayerRunner(wl)
+    sample = SAMPLES[name] if SAMPLES[name] is not None else list(range(wl.Q))
+    q_seq, q_pos = _np(wl.q_seq), _np(wl.q_pos)
+    nvis = oracle.visible_count(q_pos, wl.ratio)
+    quant = wl.quantized
+    # per-sequence dequantized caches for the sampled queries only
+    keys = {}
+    for t in sample:
+        b = int(q_seq[t])
+        if b not in keys:
+            keys[b] = _seq_keys(wl, b, int(wl.n_entries[b]))
+    zero = np.zeros(1, dtype=np.int64)
+
+    def sub(t):
+        return keys[int(q_seq[t])], np.array([q_pos[t]]), np.array([0])
+
+    for li, lay in enumerate(wl.layers):
+        print(f"[case] config {name} layer {li} ({lay.mode})", flush=True)
+        if lay.mode == "full":
+            run.index_scores(li, pool=False)
+            if run.needs_pool[li]:
+                run.block_candidates()
+            run.topk(li, pool=False)
+        elif lay.mode == "reindex":
+            run.index_scores(li, pool=True)
+            run.topk(li, pool=True)
+        run.attention(li)
+        torch.cuda.synchronize()
+        idx = _np(run.slots.topk_idxs)[sample]
+        check_index_table(idx, wl.topk)
+        if lay.mode in ("full", "reindex"):
+            qi = oracle_io.index_q(lay, quant)[sample]
+            wi = oracle_io.index_w(lay, quant)[sample]
+        sel = torch.tensor(sample, device=lay.q.device)
+        qa = (oracle.decode_bf16(_np(lay.q[sel])) if quant
+              else _np(lay.q[sel]).astype(np.float64))
+        swa = oracle_io.swa_rows(lay, quant)
+        for j, t in enumerate(sample):
+            kr, pos1, seq0 = sub(t)
+            n = int(nvis[t])
+            if lay.mode == "full":
+                ref = oracle.index_scores_dense(qi[j:j + 1], wi[j:j + 1], kr, zero, seq0, pos1,
+                                                wl.ratio, run.n_cols)
+                g = _np(run.scores[t:t + 1, :run.n_cols])
+                check_scores(g, ref)
+                g64 = g.astype(np.float64)
+                assert np.array_equal(idx[j], oracle.topk_rows_dense(g64, pos1, wl.ratio, wl.topk)[0])
+                check_topk_gap(idx[j], ref[0, :n], np.arange(n), wl.topk, row_tau(ref[0]))
+                if run.needs_pool[li]:
+                    cand = _np(run.cand[t:t + 1])
+                    assert np.array_equal(cand, oracle.block_candidates(g64, pos1, wl.ratio, 8,
+                                                                        wl.n_blocks))
+            elif lay.mode == "reindex":
+                cand = _np(run.cand[t:t + 1])
+                ref = oracle.index_scores_pool(qi[j:j + 1], wi[j:j + 1], kr, zero, seq0, pos1,
+                                               wl.ratio, cand, 8)
+                g = _np(run.pool_scores[t:t + 1, :run.pool_cols])
+                check_scores(g, ref, "pool scores")
+                assert np.array_equal(idx[j], oracle.topk_rows_pool(g.astype(np.float64), cand, 8,
+                                                                    wl.topk)[0])
+                members = oracle.pool_positions(cand, 8)[0]
+                ok = members >= 0
+                check_topk_gap(idx[j], np.where(ok, ref[0], -np.inf), np.where(ok, members, 0),
+                               wl.topk, row_tau(ref[0]))
+            # attention on the GPU's indices
+            b = int(q_seq[t])
+            mr, cidx = _gathered_main(wl, b, idx[j], n)
+            out, lse = oracle.sparse_attn(qa[j:j + 1], mr, zero,
+                                          cidx[None], swa, _np(wl.swa_base)[b:b + 1],
+                                          _np(wl.swa_pos0)[b:b + 1], None, wl.window, seq0, pos1,
+                                          _np(lay.sink).astype(np.float64), wl.softmax_scale,
+                                          wl.ratio)
+            check_attention(_np(run.out[li][t:t + 1].float()), out, f"{name} layer {li} query {t}")
+            assert np.abs(_np(run.lse[li][t]) - lse[0]).max() < 1e-3
+        if name == "tiny_full_fp32" and lay.mode == "full":
+            # integer inputs: fp32 scores are exact, so the whole pipeline is exact
+            assert np.array_equal(_np(run.scores[:, :run.n_cols]).astype(np.float64),
+                                  oracle.index_scores_dense(oracle_io.index_q(lay, False),
+                                                            oracle_io.index_w(lay, False),
+                                                            oracle_io.index_k_rows(wl),
+                                                            _np(wl.seq_base), q_seq, q_pos, 1,
+                                                            run.n_cols))

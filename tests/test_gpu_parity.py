@@ -1,0 +1,327 @@
+"""Parity of the HIP path with the oracle on small inputs that still span
+several tiles, chunks and ragged tails.  Every call goes through libcsa2.so."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import top_sparse_long_amd as tsl
+from top_sparse_long_amd.driver import LayerRunner
+from tests import oracle_io
+from tests.parity import (check_scores, check_index_table, check_topk_gap, check_attention,
+                          row_tau)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tsl.load()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _announce(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# index scores
+
+@pytest.mark.parametrize("ratio", [1, 2])
+def test_index_scores_fp8_ragged(ratio):
+    n_entries = [5000, 7777, 1, 3, 2049]
+    positions = [[n * ratio - 1, n * ratio - 2, 17] for n in n_entries[:2]] + \
+                [[ratio - 1], [3 * ratio - 1, 0], [2049 * ratio - 1]]
+    _announce(f"index_scores fp8 ratio={ratio}")
+    wl = synth.mini_workload(10 + ratio, n_entries, ratio=ratio, positions=positions).to(DEV)
+    run = LayerRunner(wl)
+    run.index_scores(0, pool=False)
+    torch.cuda.synchronize()
+    gpu = _np(run.scores[:, :run.n_cols])
+    m = oracle_io.meta(wl)
+    ref = oracle.index_scores_dense(oracle_io.index_q(wl.layers[0], True),
+                                    oracle_io.index_w(wl.layers[0], True),
+                                    oracle_io.index_k_rows(wl), m["seq_base"], m["q_seq"],
+                                    m["q_pos"], ratio, run.n_cols)
+    check_scores(gpu, ref)
+
+
+def test_index_scores_f32_exact():
+    _announce("index_scores f32 integer-exact")
+    wl = synth.mini_workload(3, [3000, 777], q_per_seq=3, quantized=False).to(DEV)
+    run = LayerRunner(wl)
+    run.index_scores(0, pool=False)
+    torch.cuda.synchronize()
+    m = oracle_io.meta(wl)
+    ref = oracle.index_scores_dense(oracle_io.index_q(wl.layers[0], False),
+                                    oracle_io.index_w(wl.layers[0], False),
+                                    oracle_io.index_k_rows(wl), m["seq_base"], m["q_seq"],
+                                    m["q_pos"], 1, run.n_cols)
+    gpu = _np(run.scores[:, :run.n_cols]).astype(np.float64)
+    assert np.array_equal(gpu, ref)
+
+
+def test_pool_scores_fp8():
+    _announce("index_scores pool mode")
+    wl = synth.mini_workload(4, [9000, 4000], q_per_seq=2, modes=("reindex",),
+                             n_blocks=300).to(DEV)
+    rng = np.random.default_rng(4)
+    Q = wl.Q
+    cand = np.full((Q, 300), -1, dtype=np.int32)
+    nvis = _np(wl.n_vis())
+    for t in range(Q):
+        nb = -(-int(nvis[t]) // 8)
+        # include blocks past the visible range and the partial last block
+        pick = np.sort(rng.choice(nb + 5, size=min(250, nb + 5), replace=False))
+        cand[t, :len(pick)] = pick
+    run = LayerRunner(wl)
+    run.slots.candidates = torch.from_numpy(cand).to(DEV)
+    run.index_scores(0, pool=True)
+    torch.cuda.synchronize()
+    m = oracle_io.meta(wl)
+    ref = oracle.index_scores_pool(oracle_io.index_q(wl.layers[0], True),
+                                   oracle_io.index_w(wl.layers[0], True),
+                                   oracle_io.index_k_rows(wl), m["seq_base"], m["q_seq"],
+                                   m["q_pos"], 1, cand, 8)
+    check_scores(_np(run.pool_scores[:, :run.pool_cols]), ref, "pool scores")
+
+
+# ---------------------------------------------------------------------------
+# selection: the oracle reads the same fp32 scores, so indices are bit-exact
+
+def _tie_scores(rng, Q, n_cols, levels):
+    x = rng.integers(-levels, levels + 1, size=(Q, n_cols)).astype(np.float32)
+    return x
+
+
+@pytest.mark.parametrize("n_cols,k", [(1, 512), (100, 512), (511, 512), (513, 512),
+                                      (5000, 512), (32768, 512), (40000, 512),
+                                      (131072, 512), (300000, 2048), (1 << 20, 512)])
+def test_topk_dense_exact(n_cols, k):
+    _announce(f"topk dense n_cols={n_cols} k={k}")
+    rng = np.random.default_rng(n_cols)
+    Q = 3
+    sc = _tie_scores(rng, Q, n_cols, 50 if n_cols > 1000 else 3)
+    # visible prefixes: full, ragged, tiny
+    q_pos = np.array([n_cols - 1, max(0, (2 * n_cols) // 3 - 1), 0], dtype=np.int32)
+    stride = (n_cols + 63) // 64 * 64
+    dev = torch.full((Q, stride), float("nan"), device=DEV)
+    dev[:, :n_cols] = torch.from_numpy(sc).to(DEV)
+    qp = torch.from_numpy(q_pos).to(DEV)
+    idx = torch.empty((Q, k), dtype=torch.int32, device=DEV)
+    ws = torch.empty((max(16, tsl.csa2_topk_workspace_size(Q, n_cols, k)),), dtype=torch.uint8,
+                     device=DEV)
+    tsl.csa2_topk(dev, n_cols, qp, 1, k, idx, ws, Q)
+    torch.cuda.synchronize()
+    ref = oracle.topk_rows_dense(sc.astype(np.float64), q_pos, 1, k)
+    assert np.array_equal(_np(idx), ref)
+
+
+def test_topk_dense_with_neg_inf():
+    _announce("topk dense with -inf entries")
+    rng = np.random.default_rng(7)
+    sc = rng.normal(size=(4, 70000)).astype(np.float32)
+    sc[0, :] = -np.inf
+    sc[1, rng.random(70000) < 0.995] = -np.inf       # ~350 finite: fewer than k
+    sc[2, ::2] = -np.inf
+    dev = torch.from_numpy(sc).to(DEV)
+    idx = torch.empty((4, 512), dtype=torch.int32, device=DEV)
+    ws = torch.empty((tsl.csa2_topk_workspace_size(4, 70000, 512),), dtype=torch.uint8, device=DEV)
+    tsl.csa2_topk(dev, 70000, None, 1, 512, idx, ws, 4)
+    torch.cuda.synchronize()
+    ref = np.stack([oracle.topk(sc[t].astype(np.float64), np.arange(70000), 512) for t in range(4)])
+    assert np.array_equal(_np(idx), ref)
+    assert np.all(_np(idx)[0] == -1)
+
+
+def test_topk_pool_exact():
+    _announce("topk pool mode")
+    rng = np.random.default_rng(8)
+    Q, nb, bs = 3, 2048, 8
+    cand = np.full((Q, nb), -1, dtype=np.int32)
+    for t in range(Q):
+        n = [2048, 1500, 10][t]
+        cand[t, :n] = np.sort(rng.choice(200000, n, replace=False))
+    sc = _tie_scores(rng, Q, nb * bs, 20)
+    idx = torch.empty((Q, 512), dtype=torch.int32, device=DEV)
+    tsl.csa2_topk(torch.from_numpy(sc).to(DEV), nb * bs, None, 1, 512, idx, None, Q,
+                  cand=torch.from_numpy(cand).to(DEV), block_size=bs)
+    torch.cuda.synchronize()
+    ref = oracle.topk_rows_pool(sc.astype(np.float64), cand, bs, 512)
+    assert np.array_equal(_np(idx), ref)
+
+
+@pytest.mark.parametrize("n_cols,n_blocks", [(100, 16), (16000, 2048), (20000, 2048),
+                                             (300000, 2048), (1 << 20, 2048), (50000, 64)])
+def test_block_candidates_exact(n_cols, n_blocks):
+    _announce(f"block_candidates n_cols={n_cols} n_blocks={n_blocks}")
+    rng = np.random.default_rng(n_cols + n_blocks)
+    Q = 2
+    sc = _tie_scores(rng, Q, n_cols, 40)
+    q_pos = np.array([n_cols - 1, max(0, n_cols // 2 - 4)], dtype=np.int32)
+    cand = torch.empty((Q, n_blocks), dtype=torch.int32, device=DEV)
+    ws = torch.empty((max(16, tsl.csa2_block_candidates_workspace_size(Q, n_cols, 8, n_blocks)),),
+                     dtype=torch.uint8, device=DEV)
+    tsl.csa2_block_candidates(torch.from_numpy(sc).to(DEV), n_cols,
+                              torch.from_numpy(q_pos).to(DEV), 1, 8, n_blocks, cand, ws, Q)
+    torch.cuda.synchronize()
+    ref = oracle.block_candidates(sc.astype(np.float64), q_pos, 1, 8, n_blocks)
+    assert np.array_equal(_np(cand), ref)
+
+
+# ---------------------------------------------------------------------------
+# attention: the oracle runs on the same indices
+
+def _attn_case(wl, idx_np, layer=0, window=None):
+    run = LayerRunner(wl)
+    run.slots.topk_idxs = torch.from_numpy(idx_np.astype(np.int32)).to(DEV)
+    if window is not None:
+        wl.window = window
+    run.attention(layer)
+    torch.cuda.synchronize()
+    m = oracle_io.meta(wl)
+    lay = wl.layers[layer]
+    ref, ref_lse = oracle.sparse_attn(oracle_io.attn_q(lay, wl.quantized), oracle_io.main_rows(wl),
+                                      m["seq_base"], idx_np, oracle_io.swa_rows(lay, wl.quantized),
+                                      m["swa_base"], m["swa_pos0"], None, wl.window, m["q_seq"],
+                                      m["q_pos"], _np(lay.sink).astype(np.float64),
+                                      wl.softmax_scale, wl.ratio)
+    gpu = run.out[layer].float()
+    return _np(gpu), _np(run.lse[layer]), ref, ref_lse
+
+
+def _random_idx(rng, nvis, k, frac_valid=1.0):
+    idx = np.full((len(nvis), k), -1, dtype=np.int64)
+    for t, n in enumerate(nvis):
+        m = min(int(n), int(k * frac_valid))
+        idx[t, :m] = np.sort(rng.choice(int(n), m, replace=False))
+    return idx
+
+
+@pytest.mark.parametrize("ratio", [1, 2])
+def test_sparse_attn_quant(ratio):
+    _announce(f"sparse_attn quantized ratio={ratio}")
+    wl = synth.mini_workload(20 + ratio, [3000, 700, 200], ratio=ratio,
+                             positions=[[3000 * ratio - 1, 1500], [700 * ratio - 1], [5, 0]]).to(DEV)
+    rng = np.random.default_rng(ratio)
+    nvis = _np(wl.n_vis())
+    idx = _random_idx(rng, nvis, 512, 0.9)
+    idx[0, 5] = -1            # holes inside the table
+    idx = np.where(idx >= 0, idx, -1)
+    gpu, gl, ref, rl = _attn_case(wl, idx)
+    check_attention(gpu, ref)
+    assert np.abs(gl - rl).max() <= 1e-3
+
+
+def test_sparse_attn_quant_duplicates_and_out_of_range():
+    _announce("sparse_attn quantized duplicates / out-of-range indices")
+    wl = synth.mini_workload(31, [1000], q_per_seq=2).to(DEV)
+    idx = np.full((2, 512), -1, dtype=np.int64)
+    idx[0, :130] = np.arange(870, 1000)        # the window positions again (main rows)
+    idx[1, :10] = np.arange(10)
+    idx[1, 10:20] = 5000                       # beyond the visible count: skipped
+    gpu, gl, ref, rl = _attn_case(wl, idx)
+    check_attention(gpu, ref)
+
+
+def test_sparse_attn_empty_key_set():
+    _announce("sparse_attn empty key set")
+    wl = synth.mini_workload(32, [64], q_per_seq=1).to(DEV)
+    idx = np.full((1, 512), -1, dtype=np.int64)
+    gpu, gl, ref, rl = _attn_case(wl, idx, window=0)
+    assert np.all(gpu == 0)
+    assert np.allclose(gl[0], _np(wl.layers[0].sink), atol=1e-6)
+
+
+def test_sparse_attn_f32():
+    _announce("sparse_attn f32")
+    wl = synth.mini_workload(33, [2048], q_per_seq=4, quantized=False).to(DEV)
+    idx = _random_idx(np.random.default_rng(3), _np(wl.n_vis()), 512)
+    gpu, gl, ref, rl = _attn_case(wl, idx)
+    check_attention(gpu, ref)
+    assert np.abs(gpu - ref).max() < 1e-5
+    assert np.abs(gl - rl).max() < 1e-5
+
+
+# ---------------------------------------------------------------------------
+# a decoder group end to end, stage by stage
+
+def test_group_end_to_end():
+    _announce("group full/reuse/reindex/reuse")
+    wl = synth.mini_workload(40, [6000, 3333], q_per_seq=2,
+                             modes=("full", "reuse", "reindex", "reuse"),
+                             topk=128, n_blocks=60).to(DEV)
+    run = LayerRunner(wl)
+    m = oracle_io.meta(wl)
+    kr = oracle_io.index_k_rows(wl)
+    main = oracle_io.main_rows(wl)
+    # L0 Full
+    run.index_scores(0, pool=False)
+    run.block_candidates()
+    run.topk(0, pool=False)
+    run.attention(0)
+    torch.cuda.synchronize()
+    l0 = wl.layers[0]
+    q0, w0 = oracle_io.index_q(l0, True), oracle_io.index_w(l0, True)
+    ref_sc = oracle.index_scores_dense(q0, w0, kr, m["seq_base"], m["q_seq"], m["q_pos"], 1,
+                                       run.n_cols)
+    gsc = _np(run.scores[:, :run.n_cols])
+    check_scores(gsc, ref_sc)
+    gsc64 = gsc.astype(np.float64)
+    cand = _np(run.cand)
+    assert np.array_equal(cand, oracle.block_candidates(gsc64, m["q_pos"], 1, 8, 60))
+    idx0 = _np(run.idx[0])
+    assert np.array_equal(idx0, oracle.topk_rows_dense(gsc64, m["q_pos"], 1, 128))
+    check_index_table(idx0, 128)
+    nvis = oracle.visible_count(m["q_pos"], 1)
+    for t in range(wl.Q):
+        n = int(nvis[t])
+        check_topk_gap(idx0[t], ref_sc[t, :n], np.arange(n), 128, row_tau(ref_sc[t]))
+    # L1 Reuse reads the same indices
+    run.attention(1)
+    # L2 Reindex
+    run.index_scores(2, pool=True)
+    run.topk(2, pool=True)
+    run.attention(2)
+    run.attention(3)
+    torch.cuda.synchronize()
+    l2 = wl.layers[2]
+    ref_pool = oracle.index_scores_pool(oracle_io.index_q(l2, True), oracle_io.index_w(l2, True),
+                                        kr, m["seq_base"], m["q_seq"], m["q_pos"], 1, cand, 8)
+    gpool = _np(run.pool_scores[:, :run.pool_cols])
+    check_scores(gpool, ref_pool, "pool scores")
+    idx2 = _np(run.idx[2])
+    assert np.array_equal(idx2, oracle.topk_rows_pool(gpool.astype(np.float64), cand, 8, 128))
+    members = oracle.pool_positions(cand, 8)
+    for t in range(wl.Q):
+        assert set(idx2[t][idx2[t] >= 0]) <= set(members[t][members[t] >= 0])
+    for li, idx in [(0, idx0), (1, idx0), (2, idx2), (3, idx2)]:
+        lay = wl.layers[li]
+        ref, _ = oracle.sparse_attn(oracle_io.attn_q(lay, True), main, m["seq_base"], idx,
+                                    oracle_io.swa_rows(lay, True), m["swa_base"], m["swa_pos0"],
+                                    None, wl.window, m["q_seq"], m["q_pos"],
+                                    _np(lay.sink).astype(np.float64), wl.softmax_scale, 1)
+        check_attention(_np(run.out[li].float()), ref, f"layer {li}")
+
+
+def test_repeat_runs_are_bitwise_identical():
+    _announce("determinism")
+    wl = synth.mini_workload(41, [70000, 5000], q_per_seq=2, modes=("full", "reindex")).to(DEV)
+    run = LayerRunner(wl)
+    run.run()
+    torch.cuda.synchronize()
+    first = [o.clone() for o in run.out] + [run.idx[0].clone(), run.idx[1].clone(), run.cand.clone()]
+    run.run()
+    torch.cuda.synchronize()
+    second = list(run.out) + [run.idx[0], run.idx[1], run.cand]
+    for a, b in zip(first, second):
+        assert torch.equal(a, b)

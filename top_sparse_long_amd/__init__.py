@@ -1,0 +1,161 @@
+"""Python binding of libcsa2.so, the CSA2 global-attention hot path on MI355X.
+
+The four functions below carry the names of the C entry points and do only
+argument marshalling: tensors become device pointers, the current torch
+stream becomes the HIP stream, and a non-zero status raises Csa2Error.
+Every step of the path runs in the library's HIP kernels; there is no
+fallback.  PyTorch supplies device memory and streams.
+"""
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
+
+CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, -1, -2, -3, -4
+CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1 = 0, 1, 2, 3
+
+EXPORTED = ("csa2_index_scores", "csa2_block_candidates", "csa2_block_candidates_workspace_size",
+            "csa2_topk", "csa2_topk_workspace_size", "csa2_sparse_attn",
+            "csa2_status_string", "csa2_last_error", "csa2_version")
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class csa2_rows(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("row_stride", ctypes.c_int64), ("scale_stride", ctypes.c_int64),
+                ("dtype", ctypes.c_int)]
+
+
+_lib = None
+
+
+def load():
+    """Load libcsa2.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing; run `python -m top_sparse_long_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    RP = ctypes.POINTER(csa2_rows)
+    lib.csa2_index_scores.argtypes = [RP, P, ctypes.c_int, RP, P, P, P, I32, P, I32, I32, P, I64,
+                                      I32, I32, I32, I32, P]
+    lib.csa2_block_candidates.argtypes = [P, I64, I32, P, I32, I32, I32, P, P, SZ, I32, P]
+    lib.csa2_block_candidates_workspace_size.argtypes = [I32, I32, I32, I32]
+    lib.csa2_block_candidates_workspace_size.restype = SZ
+    lib.csa2_topk.argtypes = [P, I64, I32, P, I32, P, I32, I32, I32, P, P, SZ, I32, P]
+    lib.csa2_topk_workspace_size.argtypes = [I32, I32, I32]
+    lib.csa2_topk_workspace_size.restype = SZ
+    lib.csa2_sparse_attn.argtypes = [P, ctypes.c_int, RP, P, P, I32, RP, P, P, P, I32, P, P, I32,
+                                     P, ctypes.c_float, P, ctypes.c_int, P, I32, I32, I32, P]
+    lib.csa2_status_string.argtypes = [ctypes.c_int]
+    lib.csa2_status_string.restype = ctypes.c_char_p
+    lib.csa2_last_error.restype = ctypes.c_char_p
+    for fn in ("csa2_index_scores", "csa2_block_candidates", "csa2_topk", "csa2_sparse_attn",
+               "csa2_version"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != CSA2_OK:
+        lib = load()
+        raise Csa2Error(status, lib.csa2_last_error().decode() or
+                        lib.csa2_status_string(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is not None:
+        return ctypes.c_void_p(int(stream))
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+# ---------------------------------------------------------------------------
+# row descriptors
+
+def rows_f32(x):
+    """fp32 [n, dim] rows."""
+    assert x.dtype == torch.float32 and x.is_contiguous()
+    return csa2_rows(x.data_ptr(), None, x.shape[-1] * 4, 0, CSA2_F32)
+
+
+def rows_fp8(codes, scale):
+    """E4M3 codes [n, dim] (uint8) with one fp32 scale per row [n]."""
+    assert codes.dtype == torch.uint8 and codes.is_contiguous() and scale.dtype == torch.float32
+    return csa2_rows(codes.data_ptr(), scale.data_ptr(), codes.shape[-1],
+                     scale.stride(0) if scale.dim() else 1, CSA2_FP8_E4M3)
+
+
+def rows_fp4_records(rec):
+    """320-byte FP4 main-KV records [n, 320]: 256 code bytes, 16 fp32 scales."""
+    assert rec.dtype == torch.uint8 and rec.is_contiguous() and rec.shape[-1] == 320
+    return csa2_rows(rec.data_ptr(), rec.data_ptr() + 256, 320, 80, CSA2_FP4_E2M1)
+
+
+def rows_swa_records(rec):
+    """528-byte FP8 SWA records [n, 528]: 512 code bytes, 4 fp32 scales."""
+    assert rec.dtype == torch.uint8 and rec.is_contiguous() and rec.shape[-1] == 528
+    return csa2_rows(rec.data_ptr(), rec.data_ptr() + 512, 528, 132, CSA2_FP8_E4M3)
+
+
+# ---------------------------------------------------------------------------
+# the four calls
+
+def csa2_index_scores(q_rows, w, w_dtype, k_rows, seq_base, q_seq, q_pos, ratio, scores,
+                      n_cols, Q, cand=None, block_size=8, H_I=32, d_I=128, stream=None):
+    lib = load()
+    ncb = 0 if cand is None else cand.shape[-1]
+    _check(lib.csa2_index_scores(ctypes.byref(q_rows), _ptr(w), w_dtype, ctypes.byref(k_rows),
+                                 _ptr(seq_base), _ptr(q_seq), _ptr(q_pos), ratio, _ptr(cand), ncb,
+                                 block_size, _ptr(scores), scores.stride(0), n_cols, Q, H_I, d_I,
+                                 _stream(stream)))
+
+
+def csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks):
+    return load().csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks)
+
+
+def csa2_topk_workspace_size(Q, n_cols, k):
+    return load().csa2_topk_workspace_size(Q, n_cols, k)
+
+
+def csa2_block_candidates(scores, n_cols, q_pos, ratio, block_size, n_blocks, cand, workspace,
+                          Q, stream=None):
+    lib = load()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.csa2_block_candidates(_ptr(scores), scores.stride(0), n_cols, _ptr(q_pos), ratio,
+                                     block_size, n_blocks, _ptr(cand), _ptr(workspace), wsb, Q,
+                                     _stream(stream)))
+
+
+def csa2_topk(scores, n_cols, q_pos, ratio, k, idx, workspace, Q, cand=None, block_size=8,
+              stream=None):
+    lib = load()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    ncb = 0 if cand is None else cand.shape[-1]
+    _check(lib.csa2_topk(_ptr(scores), scores.stride(0), n_cols, _ptr(q_pos), ratio, _ptr(cand),
+                         ncb, block_size, k, _ptr(idx), _ptr(workspace), wsb, Q, _stream(stream)))
+
+
+def csa2_sparse_attn(q, q_dtype, main_rows, main_base, idx, k, swa_rows, swa_base, swa_pos0,
+                     swa_lo, window, q_seq, q_pos, ratio, attn_sink, softmax_scale, out,
+                     out_dtype, lse, Q, H=64, D=512, stream=None):
+    lib = load()
+    _check(lib.csa2_sparse_attn(_ptr(q), q_dtype, ctypes.byref(main_rows), _ptr(main_base),
+                                _ptr(idx), k, ctypes.byref(swa_rows), _ptr(swa_base),
+                                _ptr(swa_pos0), _ptr(swa_lo), window, _ptr(q_seq), _ptr(q_pos),
+                                ratio, _ptr(attn_sink), ctypes.c_float(softmax_scale), _ptr(out),
+                                out_dtype, _ptr(lse), Q, H, D, _stream(stream)))

@@ -1,0 +1,307 @@
+// C ABI of the CSA2 hot path: host-side argument checks, then the launchers.
+// Every check runs before anything is enqueued; no call allocates device
+// memory or synchronises.
+#include "../../include/csa2.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return CSA2_OK;
+  return fail(CSA2_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int log2_exact(int v) {
+  if (v <= 0 || (v & (v - 1))) return -1;
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+#define REQUIRE(cond, status, ...) \
+  do {                             \
+    if (!(cond)) return fail(status, __VA_ARGS__); \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(int status) {
+  switch (status) {
+    case CSA2_OK: return "CSA2_OK";
+    case CSA2_ERR_INVALID_ARG: return "CSA2_ERR_INVALID_ARG";
+    case CSA2_ERR_UNSUPPORTED: return "CSA2_ERR_UNSUPPORTED";
+    case CSA2_ERR_WORKSPACE: return "CSA2_ERR_WORKSPACE";
+    case CSA2_ERR_HIP: return "CSA2_ERR_HIP";
+    default: return "CSA2_ERR_UNKNOWN";
+  }
+}
+
+const char* csa2_last_error(void) { return g_err; }
+
+int csa2_version(void) { return 100; }
+
+int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
+                      const csa2_rows* k_idx, const int64_t* seq_base, const int32_t* q_seq,
+                      const int32_t* q_pos, int32_t ratio, const int32_t* cand,
+                      int32_t n_cand_blocks, int32_t block_size, float* scores,
+                      int64_t score_stride, int32_t n_cols, int32_t Q, int32_t H_I,
+                      int32_t d_I, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(q_idx && k_idx && w && seq_base && q_seq && q_pos && scores, CSA2_ERR_INVALID_ARG,
+          "csa2_index_scores: null pointer argument");
+  REQUIRE(q_idx->data && k_idx->data, CSA2_ERR_INVALID_ARG, "csa2_index_scores: null row data");
+  REQUIRE(Q >= 0 && n_cols >= 0, CSA2_ERR_INVALID_ARG, "csa2_index_scores: negative size");
+  REQUIRE(ratio == 1 || ratio == 2, CSA2_ERR_UNSUPPORTED, "csa2_index_scores: ratio must be 1 or 2");
+  REQUIRE(d_I == 128, CSA2_ERR_UNSUPPORTED, "csa2_index_scores: d_I must be 128 (got %d)", d_I);
+  REQUIRE(w_dtype == CSA2_BF16 || w_dtype == CSA2_F32, CSA2_ERR_UNSUPPORTED,
+          "csa2_index_scores: gates must be BF16 or F32");
+  REQUIRE(q_idx->dtype == k_idx->dtype, CSA2_ERR_UNSUPPORTED,
+          "csa2_index_scores: q_idx and k_idx must share a dtype");
+  REQUIRE(score_stride >= n_cols && score_stride % 4 == 0, CSA2_ERR_INVALID_ARG,
+          "csa2_index_scores: score_stride must be >= n_cols and a multiple of 4");
+  REQUIRE(aligned(scores, 16), CSA2_ERR_INVALID_ARG, "csa2_index_scores: scores must be 16-byte aligned");
+  REQUIRE(aligned(q_idx->data, 16) && aligned(k_idx->data, 16) && q_idx->row_stride % 16 == 0 &&
+              k_idx->row_stride % 16 == 0 && q_idx->row_stride > 0 && k_idx->row_stride > 0,
+          CSA2_ERR_INVALID_ARG, "csa2_index_scores: rows must be 16-byte aligned");
+  int bshift = 0;
+  if (cand) {
+    bshift = log2_exact(block_size);
+    REQUIRE(bshift >= 0 && bshift <= 6, CSA2_ERR_UNSUPPORTED,
+            "csa2_index_scores: block_size must be a power of two <= 64");
+    REQUIRE(n_cand_blocks >= 0 && (int64_t)n_cand_blocks * block_size == n_cols,
+            CSA2_ERR_INVALID_ARG, "csa2_index_scores: pool mode needs n_cols == n_cand_blocks * block_size");
+  }
+  csa2::IndexScoreArgs a = {};
+  a.q = (const uint8_t*)q_idx->data;
+  a.q_scale = q_idx->scale;
+  a.q_row_stride = q_idx->row_stride;
+  a.q_scale_stride = q_idx->scale_stride;
+  a.w = w;
+  a.w_bf16 = (w_dtype == CSA2_BF16);
+  a.k = (const uint8_t*)k_idx->data;
+  a.k_scale = k_idx->scale;
+  a.k_row_stride = k_idx->row_stride;
+  a.k_scale_stride = k_idx->scale_stride;
+  a.seq_base = seq_base;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.ratio = ratio;
+  a.cand = cand;
+  a.n_cand_blocks = n_cand_blocks;
+  a.block_shift = bshift;
+  a.scores = scores;
+  a.score_stride = score_stride;
+  a.n_cols = n_cols;
+  a.Q = Q;
+  a.H = H_I;
+  if (Q == 0 || n_cols == 0) return CSA2_OK;
+  if (q_idx->dtype == CSA2_FP8_E4M3) {
+    REQUIRE(H_I == 32, CSA2_ERR_UNSUPPORTED, "csa2_index_scores: FP8 path needs H_I == 32 (got %d)", H_I);
+    REQUIRE(q_idx->scale && k_idx->scale, CSA2_ERR_INVALID_ARG, "csa2_index_scores: FP8 rows need scales");
+    REQUIRE(q_idx->row_stride >= 128 && k_idx->row_stride >= 128, CSA2_ERR_INVALID_ARG,
+            "csa2_index_scores: FP8 row stride below 128 bytes");
+    return hip_status(csa2::launch_index_scores_fp8(a, (hipStream_t)stream), "csa2_index_scores");
+  }
+  if (q_idx->dtype == CSA2_F32) {
+    REQUIRE(H_I >= 1 && H_I <= 64, CSA2_ERR_UNSUPPORTED, "csa2_index_scores: F32 path needs 1 <= H_I <= 64");
+    REQUIRE(q_idx->row_stride >= 512 && k_idx->row_stride >= 512, CSA2_ERR_INVALID_ARG,
+            "csa2_index_scores: F32 row stride below 512 bytes");
+    return hip_status(csa2::launch_index_scores_f32(a, (hipStream_t)stream), "csa2_index_scores");
+  }
+  return fail(CSA2_ERR_UNSUPPORTED, "csa2_index_scores: rows must be FP8_E4M3 or F32");
+}
+
+size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k) {
+  if (Q <= 0 || n_cols <= 0 || k <= 0) return 0;
+  return csa2::select_workspace_bytes(Q, n_cols, k);
+}
+
+size_t csa2_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t block_size,
+                                            int32_t n_blocks) {
+  if (Q <= 0 || n_cols <= 0 || n_blocks <= 0 || block_size <= 0) return 0;
+  const int64_t nb = ((int64_t)n_cols + block_size - 1) / block_size;
+  return csa2::select_workspace_bytes(Q, nb, n_blocks);
+}
+
+static int check_select_common(const char* fn, const float* scores, int64_t score_stride,
+                               int32_t n_cols, int32_t k, const void* out, int32_t Q) {
+  REQUIRE(scores && out, CSA2_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  REQUIRE(Q >= 0 && n_cols >= 0, CSA2_ERR_INVALID_ARG, "%s: negative size", fn);
+  REQUIRE(score_stride >= n_cols, CSA2_ERR_INVALID_ARG, "%s: score_stride below n_cols", fn);
+  REQUIRE(k >= 1, CSA2_ERR_INVALID_ARG, "%s: k must be positive", fn);
+  return CSA2_OK;
+}
+
+int csa2_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
+                          const int32_t* q_pos, int32_t ratio, int32_t block_size,
+                          int32_t n_blocks, int32_t* cand, void* workspace,
+                          size_t workspace_bytes, int32_t Q, void* stream) {
+  g_err[0] = 0;
+  int st = check_select_common("csa2_block_candidates", scores, score_stride, n_cols, n_blocks,
+                               cand, Q);
+  if (st) return st;
+  REQUIRE(q_pos, CSA2_ERR_INVALID_ARG, "csa2_block_candidates: q_pos is required");
+  REQUIRE(ratio == 1 || ratio == 2, CSA2_ERR_UNSUPPORTED, "csa2_block_candidates: ratio must be 1 or 2");
+  const int bshift = log2_exact(block_size);
+  REQUIRE(bshift >= 0 && bshift <= 6, CSA2_ERR_UNSUPPORTED,
+          "csa2_block_candidates: block_size must be a power of two <= 64");
+  REQUIRE(n_blocks <= 4096, CSA2_ERR_UNSUPPORTED, "csa2_block_candidates: n_blocks above 4096");
+  const size_t need = csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks);
+  REQUIRE(workspace_bytes >= need && (need == 0 || workspace), CSA2_ERR_WORKSPACE,
+          "csa2_block_candidates: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  REQUIRE(aligned(workspace, 16), CSA2_ERR_INVALID_ARG, "csa2_block_candidates: workspace must be 16-byte aligned");
+  if (Q == 0) return CSA2_OK;
+  csa2::SelectArgs a = {};
+  a.scores = scores;
+  a.score_stride = score_stride;
+  a.n_cols = n_cols;
+  a.q_pos = q_pos;
+  a.ratio = ratio;
+  a.block_shift = bshift;
+  a.k = n_blocks;
+  a.out_idx = cand;
+  a.workspace = workspace;
+  a.Q = Q;
+  const int64_t nb = ((int64_t)n_cols + block_size - 1) / block_size;
+  return hip_status(csa2::launch_select(csa2::SEL_BLOCKMAX, a, nb, (hipStream_t)stream),
+                    "csa2_block_candidates");
+}
+
+int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols, const int32_t* q_pos,
+              int32_t ratio, const int32_t* cand, int32_t n_cand_blocks, int32_t block_size,
+              int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes, int32_t Q,
+              void* stream) {
+  g_err[0] = 0;
+  int st = check_select_common("csa2_topk", scores, score_stride, n_cols, k, idx, Q);
+  if (st) return st;
+  REQUIRE(k <= 2048, CSA2_ERR_UNSUPPORTED, "csa2_topk: k above 2048");
+  if (q_pos) REQUIRE(ratio == 1 || ratio == 2, CSA2_ERR_UNSUPPORTED, "csa2_topk: ratio must be 1 or 2");
+  int bshift = 0;
+  if (cand) {
+    bshift = log2_exact(block_size);
+    REQUIRE(bshift >= 0 && bshift <= 6, CSA2_ERR_UNSUPPORTED,
+            "csa2_topk: block_size must be a power of two <= 64");
+    REQUIRE(n_cand_blocks >= 0 && (int64_t)n_cand_blocks * block_size == n_cols,
+            CSA2_ERR_INVALID_ARG, "csa2_topk: pool mode needs n_cols == n_cand_blocks * block_size");
+  }
+  const size_t need = csa2_topk_workspace_size(Q, n_cols, k);
+  REQUIRE(workspace_bytes >= need && (need == 0 || workspace), CSA2_ERR_WORKSPACE,
+          "csa2_topk: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  REQUIRE(aligned(workspace, 16), CSA2_ERR_INVALID_ARG, "csa2_topk: workspace must be 16-byte aligned");
+  if (Q == 0) return CSA2_OK;
+  csa2::SelectArgs a = {};
+  a.scores = scores;
+  a.score_stride = score_stride;
+  a.n_cols = n_cols;
+  a.q_pos = cand ? nullptr : q_pos;
+  a.ratio = ratio;
+  a.cand = cand;
+  a.n_cand_blocks = n_cand_blocks;
+  a.block_shift = bshift;
+  a.k = k;
+  a.out_idx = idx;
+  a.workspace = workspace;
+  a.Q = Q;
+  return hip_status(csa2::launch_select(cand ? csa2::SEL_POOL : csa2::SEL_DENSE, a, n_cols,
+                                        (hipStream_t)stream),
+                    "csa2_topk");
+}
+
+int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv,
+                     const int64_t* main_base, const int32_t* idx, int32_t k,
+                     const csa2_rows* swa_kv, const int64_t* swa_base, const int32_t* swa_pos0,
+                     const int32_t* swa_lo, int32_t window, const int32_t* q_seq,
+                     const int32_t* q_pos, int32_t ratio, const float* attn_sink,
+                     float softmax_scale, void* out, csa2_dtype out_dtype, float* lse,
+                     int32_t Q, int32_t H, int32_t D, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(q && main_kv && main_base && idx && swa_kv && swa_base && swa_pos0 && q_seq && q_pos &&
+              attn_sink && out,
+          CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: null pointer argument");
+  REQUIRE(main_kv->data && swa_kv->data, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: null row data");
+  REQUIRE(Q >= 0 && k >= 0 && window >= 0, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: negative size");
+  REQUIRE(D == 512, CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn: D must be 512 (got %d)", D);
+  REQUIRE(H >= 16 && H <= 128 && H % 16 == 0, CSA2_ERR_UNSUPPORTED,
+          "csa2_sparse_attn: H must be a multiple of 16 in [16, 128] (got %d)", H);
+  REQUIRE(k <= 2048, CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn: k above 2048");
+  REQUIRE(ratio == 1 || ratio == 2, CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn: ratio must be 1 or 2");
+  REQUIRE(aligned(q, 16) && aligned(out, 16), CSA2_ERR_INVALID_ARG,
+          "csa2_sparse_attn: q and out must be 16-byte aligned");
+  REQUIRE(aligned(main_kv->data, 16) && aligned(swa_kv->data, 16) && main_kv->row_stride % 16 == 0 &&
+              swa_kv->row_stride % 16 == 0 && main_kv->row_stride > 0 && swa_kv->row_stride > 0,
+          CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: rows must be 16-byte aligned");
+  csa2::AttnArgs a = {};
+  a.q = q;
+  a.main = (const uint8_t*)main_kv->data;
+  a.main_scale = main_kv->scale;
+  a.main_stride = main_kv->row_stride;
+  a.main_scale_stride = main_kv->scale_stride;
+  a.main_base = main_base;
+  a.idx = idx;
+  a.k = k;
+  a.swa = (const uint8_t*)swa_kv->data;
+  a.swa_scale = swa_kv->scale;
+  a.swa_stride = swa_kv->row_stride;
+  a.swa_scale_stride = swa_kv->scale_stride;
+  a.swa_base = swa_base;
+  a.swa_pos0 = swa_pos0;
+  a.swa_lo = swa_lo;
+  a.window = window;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.ratio = ratio;
+  a.sink = attn_sink;
+  a.scale = softmax_scale;
+  a.out = out;
+  a.out_bf16 = (out_dtype == CSA2_BF16);
+  a.lse = lse;
+  a.Q = Q;
+  a.H = H;
+  const bool quant = q_dtype == CSA2_BF16 && main_kv->dtype == CSA2_FP4_E2M1 &&
+                     swa_kv->dtype == CSA2_FP8_E4M3 &&
+                     (out_dtype == CSA2_BF16 || out_dtype == CSA2_F32);
+  const bool f32 = q_dtype == CSA2_F32 && main_kv->dtype == CSA2_F32 && swa_kv->dtype == CSA2_F32 &&
+                   out_dtype == CSA2_F32;
+  REQUIRE(quant || f32, CSA2_ERR_UNSUPPORTED,
+          "csa2_sparse_attn: supported dtypes are (q BF16, main FP4_E2M1, swa FP8_E4M3, out BF16|F32) "
+          "and (all F32)");
+  if (quant) {
+    REQUIRE(main_kv->scale && swa_kv->scale, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: quantized rows need scales");
+    REQUIRE(main_kv->row_stride >= 256 && swa_kv->row_stride >= 512, CSA2_ERR_INVALID_ARG,
+            "csa2_sparse_attn: row stride below the code bytes of a row");
+    REQUIRE(aligned(main_kv->scale, 16) && main_kv->scale_stride % 4 == 0 && main_kv->scale_stride >= 16,
+            CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: FP4 scales must be 16-byte aligned rows of >= 16 floats");
+    REQUIRE(aligned(swa_kv->scale, 4) && swa_kv->scale_stride >= 4, CSA2_ERR_INVALID_ARG,
+            "csa2_sparse_attn: FP8 SWA rows need 4 scales each");
+  } else {
+    REQUIRE(main_kv->row_stride >= 2048 && swa_kv->row_stride >= 2048, CSA2_ERR_INVALID_ARG,
+            "csa2_sparse_attn: F32 row stride below 2048 bytes");
+    REQUIRE((int64_t)window + k <= 8192, CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn: F32 path needs window + k <= 8192");
+  }
+  if (Q == 0) return CSA2_OK;
+  if (quant) return hip_status(csa2::launch_sparse_attn_quant(a, (hipStream_t)stream), "csa2_sparse_attn");
+  return hip_status(csa2::launch_sparse_attn_f32(a, (hipStream_t)stream), "csa2_sparse_attn");
+}
+
+}  // extern "C"

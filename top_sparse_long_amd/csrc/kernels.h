@@ -1,0 +1,106 @@
+// Internal launch interface between the C-ABI layer (api.cpp) and the HIP
+// kernels.  Every launcher enqueues on the given stream and returns the HIP
+// status of the launch; argument validation happens before, in api.cpp.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+struct IndexScoreArgs {
+  const uint8_t* q;          // FP8 codes or fp32 values, row (t*H + h)
+  const float* q_scale;      // one per row (FP8), else null
+  int64_t q_row_stride;      // bytes
+  int64_t q_scale_stride;    // floats
+  const void* w;             // [Q, H] gates
+  int w_bf16;                // 1: bf16 gates, 0: fp32 gates
+  const uint8_t* k;          // index-K rows
+  const float* k_scale;
+  int64_t k_row_stride;
+  int64_t k_scale_stride;
+  const int64_t* seq_base;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int ratio;
+  const int32_t* cand;       // null: dense
+  int n_cand_blocks;
+  int block_shift;
+  float* scores;
+  int64_t score_stride;
+  int n_cols;
+  int Q;
+  int H;
+};
+
+hipError_t launch_index_scores_fp8(const IndexScoreArgs& a, hipStream_t s);
+hipError_t launch_index_scores_f32(const IndexScoreArgs& a, hipStream_t s);
+
+// Selection (top-k and block candidates) -------------------------------------
+enum SelMode { SEL_DENSE = 0, SEL_POOL = 1, SEL_BLOCKMAX = 2, SEL_LIST = 3 };
+
+constexpr int SEL_CAP = 32768;       // entries per chunk read from scores
+constexpr int SEL_CAP_LIST = 16384;  // (key, position) pairs per chunk
+
+struct SelectPlan {
+  int n_stages;          // launches
+  int chunk1;            // entries per chunk of the first stage
+  int n_chunks1;
+  int64_t list_len[8];   // length of the candidate list written by stage i
+  int64_t ws_list_max;   // longest list (entries per row)
+};
+
+// rows_len: the longest row (entries; blocks for block candidates)
+SelectPlan plan_select(int Q, int64_t rows_len, int k);
+size_t select_workspace_bytes(int Q, int64_t rows_len, int k);
+
+struct SelectArgs {
+  const float* scores;
+  int64_t score_stride;
+  int n_cols;
+  const int32_t* q_pos;      // may be null (dense top-k: rows of n_cols)
+  int ratio;
+  const int32_t* cand;       // pool mode
+  int n_cand_blocks;
+  int block_shift;
+  int k;
+  int32_t* out_idx;          // [Q, k]
+  void* workspace;
+  int Q;
+};
+
+hipError_t launch_select(int mode, const SelectArgs& a, int64_t rows_len, hipStream_t s);
+
+// Sparse attention -----------------------------------------------------------
+struct AttnArgs {
+  const void* q;             // [Q, H, 512] bf16 or fp32
+  const uint8_t* main;       // main-KV rows
+  const float* main_scale;
+  int64_t main_stride;       // bytes
+  int64_t main_scale_stride; // floats
+  const int64_t* main_base;
+  const int32_t* idx;
+  int k;
+  const uint8_t* swa;
+  const float* swa_scale;
+  int64_t swa_stride;
+  int64_t swa_scale_stride;
+  const int64_t* swa_base;
+  const int32_t* swa_pos0;
+  const int32_t* swa_lo;
+  int window;
+  const int32_t* q_seq;
+  const int32_t* q_pos;
+  int ratio;                 // visibility of idx entries
+  const float* sink;
+  float scale;               // softmax scale (natural-log units)
+  void* out;
+  int out_bf16;
+  float* lse;
+  int Q;
+  int H;
+};
+
+hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s);
+hipError_t launch_sparse_attn_f32(const AttnArgs& a, hipStream_t s);
+
+}  // namespace csa2

@@ -1,0 +1,152 @@
+"""Layer driver over the shared slot set (the cross-layer orchestration step).
+
+A decoder group runs its layers in order over one set of slots
+(xhh.club three-modes page, "shared pool mechanism": the runtime holds
+compress_kv, index_k, topk_idxs and candidates; CSA2 page, "three modes"):
+
+* Full    scores every visible entry, writes topk_idxs and, when a later
+          Reindex layer will use it, the candidate pool (CSA2 page,
+          "hierarchical sparse indexer");
+* Reindex scores only the pool with its own indexer query and rewrites
+          topk_idxs (without a pool it scores every visible entry);
+* Reuse   runs no indexer and reads topk_idxs.
+Every layer brings its own q, SWA rows and sink.  Only device pointers move
+between layers; every step is a call into libcsa2.so.
+
+The driver takes any object with the attributes of synth.Workload (the cache
+tensors, the per-query metadata and a list of layers).
+"""
+import math
+
+import torch
+
+from . import (csa2_index_scores, csa2_block_candidates, csa2_topk, csa2_sparse_attn,
+               csa2_block_candidates_workspace_size, csa2_topk_workspace_size,
+               rows_f32, rows_fp8, rows_fp4_records, rows_swa_records,
+               CSA2_F32, CSA2_BF16)
+
+
+def _round_up(x, m):
+    return (x + m - 1) // m * m
+
+
+class SlotSet:
+    """The four cross-layer slots.  compress_kv and index_k are the cache
+    row descriptors; topk_idxs and candidates are device tensors."""
+
+    def __init__(self, compress_kv, index_k):
+        self.compress_kv = compress_kv
+        self.index_k = index_k
+        self.topk_idxs = None
+        self.candidates = None
+
+
+class LayerRunner:
+    def __init__(self, wl, device="cuda"):
+        self.wl = wl
+        self.dev = device
+        Q = wl.Q
+        self.Q = Q
+        self.quant = wl.quantized
+        self.n_cols = wl.max_cols()
+        self.stride = _round_up(max(self.n_cols, 4), 64)
+        self.pool_cols = wl.n_blocks * wl.block_size
+        if self.quant:
+            self.k_rows = rows_fp8(wl.k_idx, wl.k_scale)
+            self.main_rows = rows_fp4_records(wl.main_kv)
+        else:
+            self.k_rows = rows_f32(wl.k_idx)
+            self.main_rows = rows_f32(wl.main_kv)
+        self.layer_rows = []
+        for lay in wl.layers:
+            d = {}
+            if self.quant:
+                d["swa"] = rows_swa_records(lay.swa)
+                if lay.q_idx is not None:
+                    d["q_idx"] = rows_fp8(lay.q_idx.reshape(Q * 32, 128), lay.q_scale.reshape(Q * 32))
+            else:
+                d["swa"] = rows_f32(lay.swa)
+                if lay.q_idx is not None:
+                    d["q_idx"] = rows_f32(lay.q_idx.reshape(Q * 32, 128))
+            self.layer_rows.append(d)
+        self.needs_pool = [any(l.mode == "reindex" for l in wl.layers[i + 1:])
+                           for i in range(len(wl.layers))]
+        f32 = torch.float32
+        self.scores = torch.empty((Q, self.stride), dtype=f32, device=device)
+        self.pool_scores = torch.empty((Q, _round_up(self.pool_cols, 64)), dtype=f32, device=device)
+        self.cand = torch.empty((Q, wl.n_blocks), dtype=torch.int32, device=device)
+        self.idx = {li: torch.empty((Q, wl.topk), dtype=torch.int32, device=device)
+                    for li, l in enumerate(wl.layers) if l.mode in ("full", "reindex")}
+        ws = max(csa2_topk_workspace_size(Q, self.n_cols, wl.topk),
+                 csa2_topk_workspace_size(Q, self.pool_cols, wl.topk),
+                 csa2_block_candidates_workspace_size(Q, self.n_cols, wl.block_size, wl.n_blocks))
+        self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=device)
+        odt = torch.bfloat16 if self.quant else f32
+        self.out = [torch.empty((Q, 64, 512), dtype=odt, device=device) for _ in wl.layers]
+        self.lse = [torch.empty((Q, 64), dtype=f32, device=device) for _ in wl.layers]
+        self.slots = SlotSet(self.main_rows, self.k_rows)
+
+    # -- steps -----------------------------------------------------------------
+    def index_scores(self, li, pool):
+        wl, lay = self.wl, self.wl.layers[li]
+        wdt = CSA2_BF16 if self.quant else CSA2_F32
+        if pool:
+            csa2_index_scores(self.layer_rows[li]["q_idx"], lay.w, wdt, self.slots.index_k,
+                              wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio, self.pool_scores,
+                              self.pool_cols, self.Q, cand=self.slots.candidates,
+                              block_size=wl.block_size)
+        else:
+            csa2_index_scores(self.layer_rows[li]["q_idx"], lay.w, wdt, self.slots.index_k,
+                              wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio, self.scores,
+                              self.n_cols, self.Q)
+
+    def block_candidates(self):
+        wl = self.wl
+        csa2_block_candidates(self.scores, self.n_cols, wl.q_pos, wl.ratio, wl.block_size,
+                              wl.n_blocks, self.cand, self.ws, self.Q)
+        self.slots.candidates = self.cand
+
+    def topk(self, li, pool):
+        wl = self.wl
+        idx = self.idx[li]
+        if pool:
+            csa2_topk(self.pool_scores, self.pool_cols, None, wl.ratio, wl.topk, idx, self.ws,
+                      self.Q, cand=self.slots.candidates, block_size=wl.block_size)
+        else:
+            csa2_topk(self.scores, self.n_cols, wl.q_pos, wl.ratio, wl.topk, idx, self.ws, self.Q)
+        self.slots.topk_idxs = idx
+
+    def attention(self, li):
+        wl, lay = self.wl, self.wl.layers[li]
+        qdt = CSA2_BF16 if self.quant else CSA2_F32
+        csa2_sparse_attn(lay.q, qdt, self.slots.compress_kv, wl.seq_base, self.slots.topk_idxs,
+                         wl.topk, self.layer_rows[li]["swa"], wl.swa_base, wl.swa_pos0, None,
+                         wl.window, wl.q_seq, wl.q_pos, wl.ratio, lay.sink, wl.softmax_scale,
+                         self.out[li], qdt if self.quant else CSA2_F32, self.lse[li], self.Q)
+
+    # -- a whole pass ----------------------------------------------------------
+    def run(self, mark=None):
+        """Run every layer once.  mark(name) is called before each step and
+        once at the end with None (the benchmark records events there)."""
+        mark = mark or (lambda name: None)
+        self.slots.topk_idxs = None
+        self.slots.candidates = None
+        for li, lay in enumerate(self.wl.layers):
+            if lay.mode == "full":
+                mark("index_scores_dense")
+                self.index_scores(li, pool=False)
+                if self.needs_pool[li]:
+                    mark("block_candidates")
+                    self.block_candidates()
+                mark("topk_dense")
+                self.topk(li, pool=False)
+            elif lay.mode == "reindex":
+                pool = self.slots.candidates is not None
+                mark("index_scores_pool" if pool else "index_scores_dense")
+                self.index_scores(li, pool=pool)
+                mark("topk_pool" if pool else "topk_dense")
+                self.topk(li, pool=pool)
+            mark("sparse_attn")
+            self.attention(li)
+        mark(None)
+        return self.out

@@ -45,6 +45,8 @@ def _parse():
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="queries of the CPU-oracle sample (default: all queries, max 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stage-reps", type=int, default=10,
+                    help="repetitions per input copy when timing single stages")
     return ap.parse_args()
 
 
@@ -182,45 +184,72 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
+    def capture(fns):
+        """Capture the calls into a HIP graph (launched on torch's current
+        stream at replay)."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for f in fns:
+                f()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f()
+        return g
+
+    step_graphs = [capture([f for _, f in r.steps()]) for r in runs]
     for i in range(args.warmup):
-        runs[i % len(runs)].run()
+        step_graphs[i % len(step_graphs)].replay()
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    events = []
-
-    def make_mark(rec):
-        def mark(name):
-            ev = torch.cuda.Event(enable_timing=True)
-            ev.record(stream)
-            rec.append((name, ev))
-        return mark
-
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for i in range(args.steps):
-        rec = []
-        runs[i % len(runs)].run(mark=make_mark(rec))
-        events.append(rec)
+        step_graphs[i % len(step_graphs)].replay()
+    ev1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
 
-    # per-stage GPU time from the events
-    stage_ms, stage_n = {}, {}
-    for rec in events:
-        for (name, ev), (_, ev2) in zip(rec[:-1], rec[1:]):
-            stage_ms[name] = stage_ms.get(name, 0.0) + ev.elapsed_time(ev2)
-            stage_n[name] = stage_n.get(name, 0) + 1
-    run0 = runs[0]
+    # per-stage launch durations: each stage's calls, rotated over the input
+    # copies and repeated, captured in one graph and timed with HIP events on
+    # the stream the kernels run on
+    reps = max(2, args.stage_reps)
     stages = {}
-    for name in stage_ms:
-        avg_ms = stage_ms[name] / stage_n[name]
+    run0 = runs[0]
+    names = []
+    for name, _ in run0.steps():
+        if name != "reset" and name not in names:
+            names.append(name)
+    for name in names:
+        fns = []
+        for _ in range(reps):
+            for r in runs:
+                fns += [f for n, f in r.steps() if n == name]
+        g = capture(fns)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        avg_ms = e0.elapsed_time(e1) / len(fns)
+        per_step = sum(1 for n, _ in run0.steps() if n == name)
         nbytes, units = _stage_work(run0, name)
-        stages[name] = {"avg_us": avg_ms * 1e3, "launches_per_step": stage_n[name] // args.steps,
+        stages[name] = {"avg_us": avg_ms * 1e3, "calls_per_step": per_step,
                         "algorithmic_bytes": nbytes, "units": units,
                         "hbm_frac": nbytes / (avg_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
-    dom = max(stages, key=lambda s: stages[s]["avg_us"] * stages[s]["launches_per_step"])
+        del g
+    dom = max(stages, key=lambda s: stages[s]["avg_us"] * stages[s]["calls_per_step"])
     d = stages[dom]
     achieved = d["algorithmic_bytes"] / (d["avg_us"] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
@@ -246,6 +275,7 @@ def main():
     out = {
         "metric": METRIC, "value": value, "unit": "index keys scored/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "gpu_ms_per_step": gpu_ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8 index scores, f16 attention (fp32 accumulate)", "data": "synthetic",
         "config": {"workload": args.workload, "batch": wl.Q, "ctx_entries": wl.max_cols(),

@@ -106,6 +106,14 @@ typedef struct {
  *             equal n_cand_blocks * block_size.
  *   scores    [Q, score_stride] fp32 output; score_stride >= n_cols,
  *             multiple of 4; 16-byte aligned.
+ *   block_max NULL, or (dense mode only) [Q, block_max_stride] fp32 output:
+ *             entry b of row t is the largest score of columns
+ *             [b*block_size, (b+1)*block_size) (-inf where none is visible),
+ *             for b < ceil(n_cols / block_size) — the block maxima of the
+ *             candidate pool ([CSA2] "blocks are not compression"), taken in
+ *             the same pass so csa2_block_candidates need not re-read the
+ *             scores.  Needs block_size <= 32 and block_max_stride >=
+ *             ceil(n_cols / block_size).
  *   Supported: H_I = 32, d_I = 128 (FP8); H_I <= 64, d_I = 128 (F32);
  *   block_size in {1, 2, 4, 8, 16, 32, 64}.
  */
@@ -114,6 +122,7 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
                       const int32_t* q_seq, const int32_t* q_pos, int32_t ratio,
                       const int32_t* cand, int32_t n_cand_blocks, int32_t block_size,
                       float* scores, int64_t score_stride, int32_t n_cols,
+                      float* block_max, int64_t block_max_stride,
                       int32_t Q, int32_t H_I, int32_t d_I, void* stream);
 
 /*
@@ -125,7 +134,11 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
  * latest visible position (n - 1) / block_size is always kept (it is ranked
  * first), and the remaining places go to the best blocks, ties to the lower
  * block id; blocks whose maximum is -inf are never chosen.
- *   scores    dense scores as written by csa2_index_scores.
+ *   scores    dense scores as written by csa2_index_scores ([Q, score_stride],
+ *             16-byte aligned, score_stride a multiple of 4); may be NULL
+ *             when block_max is given.
+ *   block_max NULL, or the block maxima csa2_index_scores wrote
+ *             ([Q, block_max_stride]); when given, only they are read.
  *   cand      [Q, n_blocks] int32 output: chosen block ids ascending, then -1.
  *   workspace device memory of at least
  *             csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks) bytes
@@ -133,6 +146,7 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
  *   Supported: n_blocks <= 4096, block_size in {1, 2, 4, 8, 16, 32, 64}.
  */
 int csa2_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
+                          const float* block_max, int64_t block_max_stride,
                           const int32_t* q_pos, int32_t ratio, int32_t block_size,
                           int32_t n_blocks, int32_t* cand, void* workspace,
                           size_t workspace_bytes, int32_t Q, void* stream);
@@ -153,6 +167,8 @@ size_t csa2_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t b
  *             never chosen; n_cols must equal n_cand_blocks * block_size.
  *             Ties go to the lower position, i.e. the lower column when cand
  *             is ascending, as csa2_block_candidates writes it.
+ *   scores    [Q, score_stride] fp32, 16-byte aligned, score_stride a
+ *             multiple of 4 (as csa2_index_scores writes them).
  *   idx       [Q, k] int32 output: chosen positions ascending, then -1.
  *   workspace at least csa2_topk_workspace_size(Q, n_cols, k) bytes.
  *   Supported: 1 <= k <= 2048.

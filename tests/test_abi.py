@@ -45,12 +45,12 @@ def _rows(dtype, stride=128, scale=True):
 def _scores(lib, **kw):
     a = dict(q=_rows(tsl.CSA2_FP8_E4M3), w=FAKE, wdt=tsl.CSA2_BF16, k=_rows(tsl.CSA2_FP8_E4M3),
              seq_base=FAKE, q_seq=FAKE, q_pos=FAKE, ratio=1, cand=None, ncb=0, bs=8,
-             scores=FAKE, stride=1024, n_cols=1024, Q=1, H=32, d=128)
+             scores=FAKE, stride=1024, n_cols=1024, bmax=None, bms=0, Q=1, H=32, d=128)
     a.update(kw)
     st = lib.csa2_index_scores(ctypes.byref(a["q"]), a["w"], a["wdt"], ctypes.byref(a["k"]),
                                a["seq_base"], a["q_seq"], a["q_pos"], a["ratio"], a["cand"],
-                               a["ncb"], a["bs"], a["scores"], a["stride"], a["n_cols"], a["Q"],
-                               a["H"], a["d"], None)
+                               a["ncb"], a["bs"], a["scores"], a["stride"], a["n_cols"],
+                               a["bmax"], a["bms"], a["Q"], a["H"], a["d"], None)
     return st, lib.csa2_last_error().decode()
 
 
@@ -71,6 +71,9 @@ def _scores(lib, **kw):
     (dict(cand=FAKE, ncb=128, bs=6, n_cols=768), tsl.CSA2_ERR_UNSUPPORTED),
     (dict(q=_rows(tsl.CSA2_FP8_E4M3, scale=False), k=_rows(tsl.CSA2_FP8_E4M3, scale=False)),
      tsl.CSA2_ERR_INVALID_ARG),
+    (dict(bmax=FAKE, bms=64), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(bmax=FAKE, bms=128, bs=64), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(bmax=FAKE, bms=128, cand=FAKE, ncb=128), tsl.CSA2_ERR_INVALID_ARG),
 ])
 def test_index_scores_rejects(kw, status):
     st, msg = _scores(tsl.load(), **kw)
@@ -99,16 +102,22 @@ def test_topk_rejects():
 
 def test_block_candidates_rejects():
     lib = tsl.load()
-    assert lib.csa2_block_candidates(FAKE, 64, 64, None, 1, 8, 16, FAKE, None, 0, 1, None) == \
+    bc = lib.csa2_block_candidates
+    assert bc(FAKE, 64, 64, None, 0, None, 1, 8, 16, FAKE, None, 0, 1, None) == \
         tsl.CSA2_ERR_INVALID_ARG
-    assert lib.csa2_block_candidates(FAKE, 64, 64, FAKE, 1, 12, 16, FAKE, None, 0, 1, None) == \
+    assert bc(FAKE, 64, 64, None, 0, FAKE, 1, 12, 16, FAKE, None, 0, 1, None) == \
         tsl.CSA2_ERR_UNSUPPORTED
-    assert lib.csa2_block_candidates(FAKE, 64, 64, FAKE, 1, 8, 8192, FAKE, None, 0, 1, None) == \
+    assert bc(FAKE, 64, 64, None, 0, FAKE, 1, 8, 8192, FAKE, None, 0, 1, None) == \
         tsl.CSA2_ERR_UNSUPPORTED
+    assert bc(FAKE + 4, 64, 64, None, 0, FAKE, 1, 8, 16, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    # with block maxima the scores are not needed, but the maxima stride is checked
+    assert bc(None, 0, 64, FAKE, 4, FAKE, 1, 8, 16, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
     need = lib.csa2_block_candidates_workspace_size(2, 1 << 20, 8, 2048)
     assert need > 0
-    assert lib.csa2_block_candidates(FAKE, 1 << 20, 1 << 20, FAKE, 1, 8, 2048, FAKE, FAKE, 0, 2,
-                                     None) == tsl.CSA2_ERR_WORKSPACE
+    assert bc(FAKE, 1 << 20, 1 << 20, None, 0, FAKE, 1, 8, 2048, FAKE, FAKE, 0, 2, None) == \
+        tsl.CSA2_ERR_WORKSPACE
 
 
 def test_workspace_sizes():

@@ -71,17 +71,14 @@ def test_config_parity(name):
     def sub(t):
         return keys[int(q_seq[t])], np.array([q_pos[t]]), np.array([0])
 
+    # the benchmark's own call sequence, checked after each layer's attention
+    steps = iter(run.steps())
     for li, lay in enumerate(wl.layers):
         print(f"[case] config {name} layer {li} ({lay.mode})", flush=True)
-        if lay.mode == "full":
-            run.index_scores(li, pool=False)
-            if run.needs_pool[li]:
-                run.block_candidates()
-            run.topk(li, pool=False)
-        elif lay.mode == "reindex":
-            run.index_scores(li, pool=True)
-            run.topk(li, pool=True)
-        run.attention(li)
+        for step_name, fn in steps:
+            fn()
+            if step_name == "sparse_attn":
+                break
         torch.cuda.synchronize()
         idx = _np(run.slots.topk_idxs)[sample]
         check_index_table(idx, wl.topk)

@@ -325,3 +325,62 @@ def test_repeat_runs_are_bitwise_identical():
     second = list(run.out) + [run.idx[0], run.idx[1], run.cand]
     for a, b in zip(first, second):
         assert torch.equal(a, b)
+
+
+def test_fused_block_max_matches_scores():
+    _announce("fused block maxima")
+    wl = synth.mini_workload(42, [50000, 9001], q_per_seq=2, modes=("full", "reindex"),
+                             positions=[[49999, 30000], [9000, 77]]).to(DEV)
+    run = LayerRunner(wl)
+    run.index_scores(0, pool=False, block_max=True)
+    torch.cuda.synchronize()
+    g = _np(run.scores[:, :run.n_cols]).astype(np.float64)
+    nb = -(-run.n_cols // 8)
+    bm = _np(run.block_max[:, :nb]).astype(np.float64)
+    nvis = oracle.visible_count(_np(wl.q_pos), 1)
+    for t in range(wl.Q):
+        n = int(nvis[t])
+        ref = oracle.block_maxima(g[t], n, 8)
+        assert np.array_equal(bm[t, :len(ref)], ref)
+        assert np.all(bm[t, len(ref):] == -np.inf)
+    run.block_candidates(from_block_max=True)
+    torch.cuda.synchronize()
+    a = _np(run.cand).copy()
+    run.block_candidates(from_block_max=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(a, _np(run.cand))
+    assert np.array_equal(a, oracle.block_candidates(g, _np(wl.q_pos), 1, 8, wl.n_blocks))
+
+
+def test_graph_replay_matches_eager():
+    """A captured pass replays to the eager result, several times, with eager
+    work and synchronisations between the replays."""
+    _announce("graph replay")
+    wl = synth.mini_workload(43, [70000, 20000], q_per_seq=2, modes=("full", "reuse", "reindex")).to(DEV)
+    run = LayerRunner(wl)
+    run.run()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in run.out] + [run.cand.clone()] + [v.clone() for v in run.idx.values()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run.run()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, fn in run.steps():
+            fn()
+    for rep in range(4):
+        for o in run.out:
+            o.zero_()
+        run.cand.fill_(-7)
+        for v in run.idx.values():
+            v.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = list(run.out) + [run.cand] + list(run.idx.values())
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        run.run()              # eager work between replays
+        torch.cuda.synchronize()

@@ -47,8 +47,8 @@ def load():
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     RP = ctypes.POINTER(csa2_rows)
     lib.csa2_index_scores.argtypes = [RP, P, ctypes.c_int, RP, P, P, P, I32, P, I32, I32, P, I64,
-                                      I32, I32, I32, I32, P]
-    lib.csa2_block_candidates.argtypes = [P, I64, I32, P, I32, I32, I32, P, P, SZ, I32, P]
+                                      I32, P, I64, I32, I32, I32, P]
+    lib.csa2_block_candidates.argtypes = [P, I64, I32, P, I64, P, I32, I32, I32, P, P, SZ, I32, P]
     lib.csa2_block_candidates_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.csa2_block_candidates_workspace_size.restype = SZ
     lib.csa2_topk.argtypes = [P, I64, I32, P, I32, P, I32, I32, I32, P, P, SZ, I32, P]
@@ -115,13 +115,15 @@ def rows_swa_records(rec):
 # the four calls
 
 def csa2_index_scores(q_rows, w, w_dtype, k_rows, seq_base, q_seq, q_pos, ratio, scores,
-                      n_cols, Q, cand=None, block_size=8, H_I=32, d_I=128, stream=None):
+                      n_cols, Q, cand=None, block_size=8, block_max=None, H_I=32, d_I=128,
+                      stream=None):
     lib = load()
     ncb = 0 if cand is None else cand.shape[-1]
+    bms = 0 if block_max is None else block_max.stride(0)
     _check(lib.csa2_index_scores(ctypes.byref(q_rows), _ptr(w), w_dtype, ctypes.byref(k_rows),
                                  _ptr(seq_base), _ptr(q_seq), _ptr(q_pos), ratio, _ptr(cand), ncb,
-                                 block_size, _ptr(scores), scores.stride(0), n_cols, Q, H_I, d_I,
-                                 _stream(stream)))
+                                 block_size, _ptr(scores), scores.stride(0), n_cols,
+                                 _ptr(block_max), bms, Q, H_I, d_I, _stream(stream)))
 
 
 def csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks):
@@ -133,12 +135,14 @@ def csa2_topk_workspace_size(Q, n_cols, k):
 
 
 def csa2_block_candidates(scores, n_cols, q_pos, ratio, block_size, n_blocks, cand, workspace,
-                          Q, stream=None):
+                          Q, block_max=None, stream=None):
     lib = load()
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.csa2_block_candidates(_ptr(scores), scores.stride(0), n_cols, _ptr(q_pos), ratio,
-                                     block_size, n_blocks, _ptr(cand), _ptr(workspace), wsb, Q,
-                                     _stream(stream)))
+    sst = 0 if scores is None else scores.stride(0)
+    bms = 0 if block_max is None else block_max.stride(0)
+    _check(lib.csa2_block_candidates(_ptr(scores), sst, n_cols, _ptr(block_max), bms,
+                                     _ptr(q_pos), ratio, block_size, n_blocks, _ptr(cand),
+                                     _ptr(workspace), wsb, Q, _stream(stream)))
 
 
 def csa2_topk(scores, n_cols, q_pos, ratio, k, idx, workspace, Q, cand=None, block_size=8,

@@ -65,8 +65,9 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
                       const csa2_rows* k_idx, const int64_t* seq_base, const int32_t* q_seq,
                       const int32_t* q_pos, int32_t ratio, const int32_t* cand,
                       int32_t n_cand_blocks, int32_t block_size, float* scores,
-                      int64_t score_stride, int32_t n_cols, int32_t Q, int32_t H_I,
-                      int32_t d_I, void* stream) {
+                      int64_t score_stride, int32_t n_cols, float* block_max,
+                      int64_t block_max_stride, int32_t Q, int32_t H_I, int32_t d_I,
+                      void* stream) {
   g_err[0] = 0;
   REQUIRE(q_idx && k_idx && w && seq_base && q_seq && q_pos && scores, CSA2_ERR_INVALID_ARG,
           "csa2_index_scores: null pointer argument");
@@ -85,12 +86,21 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
               k_idx->row_stride % 16 == 0 && q_idx->row_stride > 0 && k_idx->row_stride > 0,
           CSA2_ERR_INVALID_ARG, "csa2_index_scores: rows must be 16-byte aligned");
   int bshift = 0;
-  if (cand) {
+  if (cand || block_max) {
     bshift = log2_exact(block_size);
     REQUIRE(bshift >= 0 && bshift <= 6, CSA2_ERR_UNSUPPORTED,
             "csa2_index_scores: block_size must be a power of two <= 64");
+  }
+  if (cand) {
     REQUIRE(n_cand_blocks >= 0 && (int64_t)n_cand_blocks * block_size == n_cols,
             CSA2_ERR_INVALID_ARG, "csa2_index_scores: pool mode needs n_cols == n_cand_blocks * block_size");
+    REQUIRE(!block_max, CSA2_ERR_INVALID_ARG, "csa2_index_scores: block_max is a dense-mode output");
+  }
+  if (block_max) {
+    REQUIRE(bshift <= 5, CSA2_ERR_UNSUPPORTED, "csa2_index_scores: block_max needs block_size <= 32");
+    REQUIRE(block_max_stride >= ((int64_t)n_cols + block_size - 1) / block_size, CSA2_ERR_INVALID_ARG,
+            "csa2_index_scores: block_max_stride below ceil(n_cols / block_size)");
+    REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "csa2_index_scores: block_max must be 4-byte aligned");
   }
   csa2::IndexScoreArgs a = {};
   a.q = (const uint8_t*)q_idx->data;
@@ -113,6 +123,8 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
   a.scores = scores;
   a.score_stride = score_stride;
   a.n_cols = n_cols;
+  a.block_max = block_max;
+  a.block_max_stride = block_max_stride;
   a.Q = Q;
   a.H = H_I;
   if (Q == 0 || n_cols == 0) return CSA2_OK;
@@ -148,19 +160,33 @@ static int check_select_common(const char* fn, const float* scores, int64_t scor
                                int32_t n_cols, int32_t k, const void* out, int32_t Q) {
   REQUIRE(scores && out, CSA2_ERR_INVALID_ARG, "%s: null pointer argument", fn);
   REQUIRE(Q >= 0 && n_cols >= 0, CSA2_ERR_INVALID_ARG, "%s: negative size", fn);
-  REQUIRE(score_stride >= n_cols, CSA2_ERR_INVALID_ARG, "%s: score_stride below n_cols", fn);
+  REQUIRE(score_stride >= n_cols && score_stride % 4 == 0, CSA2_ERR_INVALID_ARG,
+          "%s: score_stride must be >= n_cols and a multiple of 4", fn);
+  REQUIRE(aligned(scores, 16), CSA2_ERR_INVALID_ARG, "%s: scores must be 16-byte aligned", fn);
   REQUIRE(k >= 1, CSA2_ERR_INVALID_ARG, "%s: k must be positive", fn);
   return CSA2_OK;
 }
 
 int csa2_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
+                          const float* block_max, int64_t block_max_stride,
                           const int32_t* q_pos, int32_t ratio, int32_t block_size,
                           int32_t n_blocks, int32_t* cand, void* workspace,
                           size_t workspace_bytes, int32_t Q, void* stream) {
   g_err[0] = 0;
-  int st = check_select_common("csa2_block_candidates", scores, score_stride, n_cols, n_blocks,
-                               cand, Q);
-  if (st) return st;
+  if (block_max) {
+    // the maxima replace the scores; the stride and alignment checks of the
+    // scores apply to a stand-in that is never read
+    REQUIRE(cand, CSA2_ERR_INVALID_ARG, "csa2_block_candidates: null pointer argument");
+    REQUIRE(Q >= 0 && n_cols >= 0 && n_blocks >= 1, CSA2_ERR_INVALID_ARG,
+            "csa2_block_candidates: bad size");
+    REQUIRE(block_size > 0 && block_max_stride >= ((int64_t)n_cols + block_size - 1) / block_size,
+            CSA2_ERR_INVALID_ARG, "csa2_block_candidates: block_max_stride below the block count");
+    REQUIRE(aligned(block_max, 4), CSA2_ERR_INVALID_ARG, "csa2_block_candidates: block_max must be 4-byte aligned");
+  } else {
+    int st = check_select_common("csa2_block_candidates", scores, score_stride, n_cols, n_blocks,
+                                 cand, Q);
+    if (st) return st;
+  }
   REQUIRE(q_pos, CSA2_ERR_INVALID_ARG, "csa2_block_candidates: q_pos is required");
   REQUIRE(ratio == 1 || ratio == 2, CSA2_ERR_UNSUPPORTED, "csa2_block_candidates: ratio must be 1 or 2");
   const int bshift = log2_exact(block_size);
@@ -176,6 +202,8 @@ int csa2_block_candidates(const float* scores, int64_t score_stride, int32_t n_c
   a.scores = scores;
   a.score_stride = score_stride;
   a.n_cols = n_cols;
+  a.block_max = block_max;
+  a.block_max_stride = block_max_stride;
   a.q_pos = q_pos;
   a.ratio = ratio;
   a.block_shift = bshift;

@@ -28,6 +28,8 @@ struct IndexScoreArgs {
   float* scores;
   int64_t score_stride;
   int n_cols;
+  float* block_max;          // optional fused block maxima (dense mode)
+  int64_t block_max_stride;
   int Q;
   int H;
 };
@@ -57,6 +59,8 @@ struct SelectArgs {
   const float* scores;
   int64_t score_stride;
   int n_cols;
+  const float* block_max;    // block candidates: precomputed maxima, or null
+  int64_t block_max_stride;
   const int32_t* q_pos;      // may be null (dense top-k: rows of n_cols)
   int ratio;
   const int32_t* cand;       // pool mode

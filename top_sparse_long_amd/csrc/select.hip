@@ -7,15 +7,17 @@
 // "where attention is computed" for the block pool with the latest block
 // forced).
 //
-// One workgroup of 1024 threads selects within a chunk of up to 32768
-// entries held in LDS as order-preserving 32-bit keys:
+// One workgroup of 512 threads selects within a chunk of up to 32768
+// entries, kept in registers as order-preserving 32-bit keys (entry
+// j * 512 + tid is thread tid's j-th key, so loads are coalesced):
 //   1. load the chunk (dense scores, pool scores, block maxima of 8-score
 //      blocks, or a (key, position) list from a previous stage);
 //   2. if more than k entries are selectable, radix-select the k-th largest
-//      key T with four 8-bit digit passes over LDS histograms;
-//   3. compact in position order with wave ballots: every key > T, then the
-//      first (k - #greater) keys equal to T, which applies the lower-position
-//      tie rule exactly.
+//      key T with 8-bit digit passes over LDS histograms, stopping as soon as
+//      the threshold bucket is taken whole;
+//   3. compact in position order: per-(round, wave) ballot counts, one scan
+//      and mbcnt ranks place every key > T, then the first (k - #greater)
+//      keys equal to T, which applies the lower-position tie rule exactly.
 // Long rows are cut into chunks; each chunk's k winners (already in position
 // order) form a shorter list, and further stages select from the lists until
 // one chunk holds the row.  A strict total order makes this exact: an entry
@@ -24,8 +26,9 @@
 
 namespace csa2 {
 
-constexpr int SEL_THREADS = 1024;
+constexpr int SEL_THREADS = 512;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_BATCH = 8;               // loads in flight per thread
 constexpr uint32_t KEY_NEG_INF = 0x007FFFFFu;  // key of -inf: selectable keys are larger
 constexpr uint32_t KEY_POS_INF = 0xFF800000u;  // key of +inf (the forced latest block)
 constexpr uint32_t KEY_PAD = 0u;               // padding in candidate lists
@@ -62,12 +65,18 @@ __device__ __forceinline__ int64_t row_length(const StageArgs& a, int t) {
   return a.in_len;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP (no LDS):
+// Hillis-Steele within each row of 16 lanes, then row_bcast:15 carries row
+// totals into rows 1 and 3 and row_bcast:31 carries the first half's total
+// into rows 2 and 3.
 __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
+  (void)lane;
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
   return x;
 }
 
@@ -75,14 +84,34 @@ __device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {
   return __popcll(mask & ((1ull << lane) - 1ull));
 }
 
+// Block-wide exclusive scan of one value per thread (1024 threads).
+__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, int lane, int wave,
+                                                    uint32_t* s_wsum, uint32_t* total) {
+  uint32_t incl = wave_incl_scan(x, lane);
+  if (lane == 63) s_wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    const uint32_t v = s_wsum[w];
+    before += (w < wave) ? v : 0u;
+    all += v;
+  }
+  *total = all;
+  return before + incl - x;
+}
+
 template <int MODE, int CAP>
 __global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
-  __shared__ uint32_t s_key[CAP];
-  __shared__ int32_t s_pos[MODE == SEL_LIST ? CAP : 1];
-  __shared__ uint32_t s_hist[256];
+  constexpr int EMAX = CAP / SEL_THREADS;   // entries per thread at most
+  // 16 interleaved copies of the 256-bin histogram (bin b, copy c at
+  // 16 b + c): lanes that hit the same bin land on 16 different banks, which
+  // keeps the first digit pass (where scores share few top bytes) from
+  // serialising on one address.
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[256 * 16];
+  __shared__ uint32_t s_cnt[EMAX * SEL_WAVES];   // per (round, wave) packed counts
   __shared__ uint32_t s_wsum[SEL_WAVES];
-  __shared__ uint32_t s_gt[SEL_WAVES], s_eq[SEL_WAVES];
-  __shared__ uint32_t s_bucket, s_above, s_nsel;
+  __shared__ uint32_t s_bucket, s_above, s_bcnt;
 
   const SelectArgs& s = a.s;
   const int t = blockIdx.y;
@@ -96,148 +125,203 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
   const int count = (int)max((int64_t)0, min((int64_t)a.chunk, L - g0));
   const float* row = s.scores + (int64_t)t * s.score_stride;
 
-  if (tid == 0) s_nsel = 0;
-  __syncthreads();
-
-  // 1. load keys ------------------------------------------------------------
-  uint32_t my_sel = 0;
-  for (int i = tid; i < count; i += SEL_THREADS) {
-    const int64_t g = g0 + i;
-    uint32_t key;
-    if (MODE == SEL_DENSE) {
-      key = float_key(row[g]);
-    } else if (MODE == SEL_POOL) {
-      const int cb = s.cand[(int64_t)t * s.n_cand_blocks + (int)(g >> s.block_shift)];
-      key = cb >= 0 ? float_key(row[g]) : KEY_NEG_INF;
-    } else if (MODE == SEL_BLOCKMAX) {
-      const int n = min(s.n_cols, sel_visible(s, t));
-      const int p0 = (int)(g << s.block_shift);
-      const int p1 = min(n, p0 + (1 << s.block_shift));
-      float m = -INFINITY;
-      for (int p = p0; p < p1; ++p) m = fmaxf(m, row[p]);
-      key = (g == L - 1) ? KEY_POS_INF : float_key(m);
-    } else {
-      key = a.in_key[(int64_t)t * a.in_len + g];
-      s_pos[i] = a.in_pos[(int64_t)t * a.in_len + g];
+  // Striped ownership: entry j * SEL_THREADS + tid of the chunk is this
+  // thread's j-th key, so every load instruction reads consecutive addresses.
+  // Loads are unconditional, from indices clamped into the chunk, and masked
+  // afterwards, so they are all in flight together.
+  uint32_t key[EMAX];
+  int32_t aux[(MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1];   // block id / position
+  if (count > 0) {
+    const int last = count - 1;
+    if (MODE == SEL_DENSE || MODE == SEL_POOL) {
+      float v[EMAX];
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j) v[j] = row[g0 + min(j * SEL_THREADS + tid, last)];
+      if (MODE == SEL_POOL) {
+#pragma unroll
+        for (int j = 0; j < EMAX; ++j) {
+          const int64_t g = g0 + min(j * SEL_THREADS + tid, last);
+          aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] =
+              s.cand[(int64_t)t * s.n_cand_blocks + (int)(g >> s.block_shift)];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j) {
+        const bool in = j * SEL_THREADS + tid < count;
+        uint32_t kk = in ? float_key(v[j]) : KEY_PAD;
+        if (MODE == SEL_POOL && in && aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] < 0)
+          kk = KEY_NEG_INF;
+        key[j] = kk;
+      }
+    } else if (MODE == SEL_LIST) {
+      const uint32_t* ik = a.in_key + (int64_t)t * a.in_len + g0;
+      const int32_t* ip = a.in_pos + (int64_t)t * a.in_len + g0;
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j) {
+        key[j] = ik[min(j * SEL_THREADS + tid, last)];
+        aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] = ip[min(j * SEL_THREADS + tid, last)];
+      }
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j)
+        if (j * SEL_THREADS + tid >= count) key[j] = KEY_PAD;
+    } else {   // SEL_BLOCKMAX
+      // blocks before the last visible one are complete; the last one is
+      // forced and never read (reads are clamped below it)
+      const int64_t lim = (L >= 2) ? L - 2 : 0;
+      float m[EMAX];
+      if (s.block_max) {
+#pragma unroll
+        for (int j = 0; j < EMAX; ++j)
+          m[j] = s.block_max[(int64_t)t * s.block_max_stride + min(g0 + min(j * SEL_THREADS + tid, last), lim)];
+      } else if (L >= 2) {
+        const int bs = 1 << s.block_shift;
+#pragma unroll
+        for (int j = 0; j < EMAX; ++j) {
+          const float* src = row + (min(g0 + min(j * SEL_THREADS + tid, last), lim) << s.block_shift);
+          float mm = -INFINITY;
+          if (bs >= 4) {
+            for (int p = 0; p < bs; p += 4) {
+              const float4 x = *(const float4*)(src + p);
+              mm = fmaxf(mm, fmaxf(fmaxf(x.x, x.y), fmaxf(x.z, x.w)));
+            }
+          } else {
+            for (int p = 0; p < bs; ++p) mm = fmaxf(mm, src[p]);
+          }
+          m[j] = mm;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < EMAX; ++j) m[j] = -INFINITY;
+      }
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j) {
+        const int i = j * SEL_THREADS + tid;
+        uint32_t kk = KEY_PAD;
+        // the block of the latest visible position is always kept
+        if (i < count) kk = (g0 + i == L - 1) ? KEY_POS_INF : float_key(m[j]);
+        key[j] = kk;
+      }
     }
-    s_key[i] = key;
-    my_sel += key > KEY_NEG_INF;
-  }
-  // block-wide count of selectable entries
-  for (int d = 32; d >= 1; d >>= 1) my_sel += __shfl_xor(my_sel, d);
-  if (lane == 0) atomicAdd(&s_nsel, my_sel);
-  __syncthreads();
-  const uint32_t nsel = s_nsel;
-  const int k = s.k;
-
-  // 2. radix select of the k-th largest key ---------------------------------
-  uint32_t T, keq;
-  if (nsel <= (uint32_t)k) {
-    T = KEY_NEG_INF;
-    keq = 0;
   } else {
+#pragma unroll
+    for (int j = 0; j < EMAX; ++j) key[j] = KEY_PAD;
+  }
+
+  const int k = s.k;
+  const uint32_t copy = (uint32_t)lane & 15u;
+
+  // radix select of the k-th largest selectable key ---------------------------
+  // Histograms count selectable keys only (above the -inf key), so the first
+  // pass also yields their number; a chunk with at most k of them takes all.
+  uint32_t T = KEY_NEG_INF, keq = 0;
+  {
     uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) s_hist[tid] = 0;
+      __syncthreads();   // previous readers of s_hist / s_wsum are done
+      for (int i = tid; i < 256 * 16; i += SEL_THREADS) s_hist[i] = 0;
       __syncthreads();
-      for (int i = tid; i < count; i += SEL_THREADS) {
-        const uint32_t key = s_key[i];
-        if ((key & mask) == prefix) atomicAdd(&s_hist[(key >> shift) & 255u], 1u);
-      }
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j)
+        if (key[j] > KEY_NEG_INF && (key[j] & mask) == prefix)
+          atomicAdd(&s_hist[((key[j] >> shift) & 255u) * 16u + copy], 1u);
       __syncthreads();
       // suffix counts over buckets, highest bucket first
-      const uint32_t cnt = (tid < 256) ? s_hist[255 - tid] : 0u;
-      uint32_t incl = wave_incl_scan(cnt, lane);
-      if (lane == 63) s_wsum[wave] = incl;
-      __syncthreads();
+      uint32_t cnt = 0;
       if (tid < 256) {
-        for (int w = 0; w < wave; ++w) incl += s_wsum[w];
-        const uint32_t excl = incl - cnt;
-        if (excl < krem && incl >= krem) {
-          s_bucket = 255u - (uint32_t)tid;
-          s_above = excl;
+        const uint4* hb = (const uint4*)(s_hist + (255 - tid) * 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint4 v = hb[q];
+          cnt += v.x + v.y + v.z + v.w;
         }
+      }
+      uint32_t all;
+      const uint32_t excl = block_excl_scan(cnt, lane, wave, s_wsum, &all);
+      if (shift == 24 && all <= (uint32_t)k) break;      // everything selectable is taken
+      if (tid < 256 && excl < krem && excl + cnt >= krem) {
+        s_bucket = 255u - (uint32_t)tid;
+        s_above = excl;
+        s_bcnt = cnt;
       }
       __syncthreads();
       krem -= s_above;
       prefix |= s_bucket << shift;
       mask |= 255u << shift;
+      if (s_bcnt == krem) {
+        // the whole threshold bucket is taken: the k best are the keys >= prefix
+        T = prefix - 1u;
+        keq = 0;
+        break;
+      }
+      if (shift == 0) {
+        T = prefix;
+        keq = krem;
+      }
     }
-    T = prefix;
-    keq = krem;
   }
 
-  // 3. order-preserving compaction ------------------------------------------
-  const int seg = ((count + SEL_WAVES - 1) / SEL_WAVES + 63) & ~63;
-  const int sb = min(count, wave * seg);
-  const int se = min(count, sb + seg);
-  uint32_t ngt = 0, neq = 0;
-  for (int i0 = sb; i0 < se; i0 += 64) {
-    const int i = i0 + lane;
-    const uint32_t key = (i < se) ? s_key[i] : KEY_PAD;
-    ngt += __popcll(__ballot(key > T));
-    neq += __popcll(__ballot(i < se && key == T));
-  }
-  if (lane == 0) {
-    s_gt[wave] = ngt;
-    s_eq[wave] = neq;
+  // order-preserving compaction ----------------------------------------------
+  // Position order is (round j, wave, lane).  Each wave counts, per round, its
+  // keys > T (low half) and == T (high half); one scan over the (round, wave)
+  // counts gives each group's offsets and mbcnt ranks place the lanes: a key
+  // is taken if it is > T, or == T among the first keq equal keys.
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {
+    const uint64_t gm = __ballot(key[j] > T);
+    const uint64_t em = __ballot(key[j] == T && j * SEL_THREADS + tid < count);
+    if (lane == 0) s_cnt[j * SEL_WAVES + wave] = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(em) << 16);
   }
   __syncthreads();
-  // equal keys are taken in position order: wave w takes
-  // min(eq_w, keq - (equal keys in earlier waves)) of them
-  uint32_t cum_eq = 0, sel_before = 0, total = 0, run_eq = 0;
-  for (int w = 0; w < SEL_WAVES; ++w) {
-    const uint32_t take_eq = min(s_eq[w], keq > cum_eq ? keq - cum_eq : 0u);
-    const uint32_t selw = s_gt[w] + take_eq;
-    if (w < wave) {
-      sel_before += selw;
-      run_eq += s_eq[w];
-    }
-    total += selw;
-    cum_eq += s_eq[w];
+  {
+    const uint32_t v = (tid < EMAX * SEL_WAVES) ? s_cnt[tid] : 0u;
+    uint32_t tot_packed;
+    const uint32_t ex = block_excl_scan(v, lane, wave, s_wsum, &tot_packed);
+    __syncthreads();
+    if (tid < EMAX * SEL_WAVES) s_cnt[tid] = ex;
+    if (tid == 0) s_bcnt = (tot_packed & 0xFFFFu) + min(tot_packed >> 16, keq);
+    __syncthreads();
   }
-  uint32_t run_sel = sel_before;
-  for (int i0 = sb; i0 < se; i0 += 64) {
-    const int i = i0 + lane;
-    const bool in = i < se;
-    const uint32_t key = in ? s_key[i] : KEY_PAD;
-    const bool is_gt = key > T;
-    const bool is_eq = in && key == T;
-    const uint64_t eqm = __ballot(is_eq);
-    const uint32_t eq_rank = run_eq + lanes_below(eqm, lane);
-    const bool take = is_gt || (is_eq && eq_rank < keq);
-    const uint64_t selm = __ballot(take);
-    if (take) {
-      const uint32_t o = run_sel + lanes_below(selm, lane);
-      const int64_t g = g0 + i;
+  const uint32_t total = s_bcnt;
+#pragma unroll
+  for (int j = 0; j < EMAX; ++j) {
+    const bool in = j * SEL_THREADS + tid < count;
+    const bool gt = key[j] > T;
+    const bool eq = in && key[j] == T;
+    const uint64_t gm = __ballot(gt);
+    const uint64_t em = __ballot(eq);
+    const uint32_t base = s_cnt[j * SEL_WAVES + wave];
+    const uint32_t gr = __builtin_amdgcn_mbcnt_hi((uint32_t)(gm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)gm, 0u));
+    const uint32_t er = __builtin_amdgcn_mbcnt_hi((uint32_t)(em >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)em, 0u));
+    const uint32_t eq_rank = (base >> 16) + er;
+    if (gt || (eq && eq_rank < keq)) {
+      const uint32_t o = (base & 0xFFFFu) + gr + min(eq_rank, keq);
+      const int64_t g = g0 + j * SEL_THREADS + tid;
       int32_t pos;
       if (MODE == SEL_DENSE || MODE == SEL_BLOCKMAX) {
         pos = (int32_t)g;
       } else if (MODE == SEL_POOL) {
-        const int cb = s.cand[(int64_t)t * s.n_cand_blocks + (int)(g >> s.block_shift)];
-        pos = (cb << s.block_shift) | (int)(g & ((1 << s.block_shift) - 1));
+        pos = (aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] << s.block_shift) |
+              (int)(g & ((1 << s.block_shift) - 1));
       } else {
-        pos = s_pos[i];
+        pos = aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)];
       }
       if (a.out_key) {
         const int64_t off = (int64_t)t * a.out_stride + (int64_t)c * k + o;
-        a.out_key[off] = key;
+        a.out_key[off] = key[j];
         a.out_pos[off] = pos;
       } else {
         s.out_idx[(int64_t)t * k + o] = pos;
       }
     }
-    run_eq += __popcll(eqm);
-    run_sel += __popcll(selm);
   }
   // padding
-  for (int o = (int)total + tid; o < k; o += SEL_THREADS) {
+  for (int q = (int)total + tid; q < k; q += SEL_THREADS) {
     if (a.out_key) {
-      const int64_t off = (int64_t)t * a.out_stride + (int64_t)c * k + o;
+      const int64_t off = (int64_t)t * a.out_stride + (int64_t)c * k + q;
       a.out_key[off] = KEY_PAD;
       a.out_pos[off] = -1;
     } else {
-      s.out_idx[(int64_t)t * k + o] = -1;
+      s.out_idx[(int64_t)t * k + q] = -1;
     }
   }
 }
@@ -287,11 +371,32 @@ size_t select_workspace_bytes(int Q, int64_t rows_len, int k) {
   return (size_t)2 * (size_t)Q * (size_t)p.ws_list_max * 8u;
 }
 
+// smallest compiled capacity that holds n entries
+static int fit_cap(int64_t n) {
+  if (n <= 4096) return 4096;
+  if (n <= 16384) return 16384;
+  return SEL_CAP;
+}
+
 template <int MODE>
-static hipError_t launch_first(const StageArgs& a, int nchunks, int Q, hipStream_t s) {
-  hipLaunchKernelGGL((select_kernel<MODE, SEL_CAP>), dim3(nchunks, Q), dim3(SEL_THREADS), 0,
-                     s, a);
+static hipError_t launch_stage(const StageArgs& a, int cap, int nchunks, int Q, hipStream_t s) {
+  const dim3 grid(nchunks, Q), block(SEL_THREADS);
+  if (cap <= 4096)
+    hipLaunchKernelGGL((select_kernel<MODE, 4096>), grid, block, 0, s, a);
+  else if (cap <= 16384)
+    hipLaunchKernelGGL((select_kernel<MODE, 16384>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((select_kernel<MODE, SEL_CAP>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+static hipError_t launch_first(int mode, const StageArgs& a, int cap, int nchunks, int Q,
+                               hipStream_t s) {
+  switch (mode) {
+    case SEL_DENSE: return launch_stage<SEL_DENSE>(a, cap, nchunks, Q, s);
+    case SEL_POOL: return launch_stage<SEL_POOL>(a, cap, nchunks, Q, s);
+    default: return launch_stage<SEL_BLOCKMAX>(a, cap, nchunks, Q, s);
+  }
 }
 
 hipError_t launch_select(int mode, const SelectArgs& sa, int64_t rows_len, hipStream_t s) {
@@ -299,13 +404,10 @@ hipError_t launch_select(int mode, const SelectArgs& sa, int64_t rows_len, hipSt
   StageArgs a = {};
   a.s = sa;
   if (p.n_stages == 1) {
-    a.chunk = SEL_CAP;
+    const int cap = fit_cap(rows_len);
+    a.chunk = cap;
     a.out_key = nullptr;
-    switch (mode) {
-      case SEL_DENSE: return launch_first<SEL_DENSE>(a, 1, sa.Q, s);
-      case SEL_POOL: return launch_first<SEL_POOL>(a, 1, sa.Q, s);
-      default: return launch_first<SEL_BLOCKMAX>(a, 1, sa.Q, s);
-    }
+    return launch_first(mode, a, cap, 1, sa.Q, s);
   }
   uint8_t* ws = (uint8_t*)sa.workspace;
   const size_t list_bytes = (size_t)sa.Q * (size_t)p.ws_list_max * 4u;
@@ -317,12 +419,7 @@ hipError_t launch_select(int mode, const SelectArgs& sa, int64_t rows_len, hipSt
   a.out_key = key_buf[0];
   a.out_pos = pos_buf[0];
   a.out_stride = p.list_len[0];
-  hipError_t e;
-  switch (mode) {
-    case SEL_DENSE: e = launch_first<SEL_DENSE>(a, p.n_chunks1, sa.Q, s); break;
-    case SEL_POOL: e = launch_first<SEL_POOL>(a, p.n_chunks1, sa.Q, s); break;
-    default: e = launch_first<SEL_BLOCKMAX>(a, p.n_chunks1, sa.Q, s); break;
-  }
+  hipError_t e = launch_first(mode, a, fit_cap(p.chunk1), p.n_chunks1, sa.Q, s);
   if (e != hipSuccess) return e;
   // list stages
   int cur = 0;
@@ -333,21 +430,21 @@ hipError_t launch_select(int mode, const SelectArgs& sa, int64_t rows_len, hipSt
     b.in_pos = pos_buf[cur];
     b.in_len = p.list_len[st - 1];
     const bool last = (st == p.n_stages - 1);
-    int nch;
+    int nch, cap;
     if (last) {
-      b.chunk = SEL_CAP_LIST;
+      cap = fit_cap(b.in_len);
+      b.chunk = cap;
       b.out_key = nullptr;
       nch = 1;
     } else {
-      b.chunk = SEL_CAP_LIST;
+      cap = SEL_CAP_LIST;
+      b.chunk = cap;
       b.out_key = key_buf[cur ^ 1];
       b.out_pos = pos_buf[cur ^ 1];
       b.out_stride = p.list_len[st];
-      nch = (int)((b.in_len + SEL_CAP_LIST - 1) / SEL_CAP_LIST);
+      nch = (int)((b.in_len + cap - 1) / cap);
     }
-    hipLaunchKernelGGL((select_kernel<SEL_LIST, SEL_CAP_LIST>), dim3(nch, sa.Q),
-                       dim3(SEL_THREADS), 0, s, b);
-    e = hipGetLastError();
+    e = launch_stage<SEL_LIST>(b, min(cap, SEL_CAP_LIST), nch, sa.Q, s);
     if (e != hipSuccess) return e;
     cur ^= 1;
   }

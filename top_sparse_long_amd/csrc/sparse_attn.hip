@@ -33,6 +33,10 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+struct v8s_pair {
+  v4s_t lo, hi;
+};
 
 constexpr int AT_WAVES = 4;
 constexpr int AT_HEADS = 16;
@@ -46,38 +50,28 @@ constexpr float RESCALE_SLACK = 8.0f;         // log2 units
 __device__ __forceinline__ uint32_t as_u32(v2h h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ v2h as_v2h(uint32_t u) { return __builtin_bit_cast(v2h, u); }
 
-// Eight E2M1 codes (one dword, element 2i in the low nibble of byte i) to
-// eight f16 values times `s`.  The f16 pattern of every E2M1 magnitude has a
-// zero low byte, so a v_perm byte table over the 3 magnitude bits gives the
-// high byte; the sign bit drops into bit 7 of that byte.
-__device__ __forceinline__ void dequant_fp4x8(uint32_t x, _Float16 s, uint32_t out[4]) {
-  const uint32_t tbl_lo = 0x3E3C3800u;  // codes 0..3 -> 0, 0.5, 1, 1.5
-  const uint32_t tbl_hi = 0x46444240u;  // codes 4..7 -> 2, 3, 4, 6
-  const uint32_t mag_even = x & 0x07070707u;
-  const uint32_t mag_odd = (x >> 4) & 0x07070707u;
-  const uint32_t hb_even = __builtin_amdgcn_perm(tbl_hi, tbl_lo, mag_even) | ((x << 4) & 0x80808080u);
-  const uint32_t hb_odd = __builtin_amdgcn_perm(tbl_hi, tbl_lo, mag_odd) | (x & 0x80808080u);
-  const v2h ss = {s, s};
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t sel = 0x0Cu | ((uint32_t)k << 8) | (0x0Cu << 16) | ((uint32_t)(4 + k) << 24);
-    const uint32_t pair = __builtin_amdgcn_perm(hb_odd, hb_even, sel);
-    out[k] = as_u32(as_v2h(pair) * ss);
-  }
+// Dequantization: gfx950's scaled converts (v_cvt_scalef32_pk_f16_fp4/fp8)
+// widen two codes to f16 and apply only the exponent of their fp32 scale
+// operand (a scale s acts as 2^floor(log2 s)).  The remaining mantissa factor
+// m = s / 2^floor(log2 s), in [1, 2), is applied with one packed f16
+// multiply, so value = code * s with a single f16 rounding of the product
+// (plus the rounding of m to f16).
+__device__ __forceinline__ _Float16 scale_mantissa(float s) {
+  return (_Float16)(2.0f * __builtin_amdgcn_frexp_mantf(s));
 }
 
-// Four E4M3 codes (one dword) to four f16 values times `s256` (the row scale
-// times 2^8): moving the 7 exponent/mantissa bits up by 7 gives the same
-// value times 2^-8 in f16, subnormals included.
-__device__ __forceinline__ void dequant_fp8x4(uint32_t x, _Float16 s256, uint32_t out[2]) {
-  const v2h ss = {s256, s256};
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const uint32_t sel = 0x0Cu | ((uint32_t)(2 * k) << 8) | (0x0Cu << 16) | ((uint32_t)(2 * k + 1) << 24);
-    const uint32_t y = __builtin_amdgcn_perm(0u, x, sel);  // bytes at bits 8..15 of each half
-    const uint32_t f = ((y >> 1) & 0x3F803F80u) | (y & 0x80008000u);
-    out[k] = as_u32(as_v2h(f) * ss);
-  }
+// Eight E2M1 codes (one dword, element 2i in the low nibble of byte i).
+__device__ __forceinline__ void dequant_fp4x8(uint32_t x, float s, v2h m2, uint32_t out[4]) {
+  out[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, s, 0) * m2);
+  out[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, s, 1) * m2);
+  out[2] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, s, 2) * m2);
+  out[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, s, 3) * m2);
+}
+
+// Four E4M3 codes (one dword).
+__device__ __forceinline__ void dequant_fp8x4(uint32_t x, float s, v2h m2, uint32_t out[2]) {
+  out[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, s, false) * m2);
+  out[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, s, true) * m2);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
@@ -134,11 +128,10 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
     }
   }
 
-  v4f O[4][8];
+  // O[T]: output columns d = 16 T + r, rows = heads 4 g + j
+  v4f O[32];
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) O[u][i] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < 32; ++u) O[u] = (v4f){0.f, 0.f, 0.f, 0.f};
   float m_s = -INFINITY;   // running maximum of head r (log2 units)
   float l_part = 0.f;      // this lane's share of the denominator of head r
   const float zscale = a.scale * LOG2E;
@@ -166,20 +159,22 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
       uint32_t kd[16][4];   // chunk c: dims 128 g + 8 c .. +8 as f16 pairs
       if (is_swa) {
         v4u raw[8];
-        _Float16 s256 = (_Float16)0.f;
+        float sc = 0.f;
         if (valid) {
           const uint8_t* src = a.swa + row * a.swa_stride + 128 * g;
 #pragma unroll
           for (int j = 0; j < 8; ++j) raw[j] = *(const v4u*)(src + 16 * j);
-          s256 = (_Float16)(a.swa_scale[row * a.swa_scale_stride + g] * 256.f);
+          sc = a.swa_scale[row * a.swa_scale_stride + g];
         } else {
 #pragma unroll
           for (int j = 0; j < 8; ++j) raw[j] = (v4u){0u, 0u, 0u, 0u};
         }
+        const _Float16 mh = scale_mantissa(sc);
+        const v2h m2 = {mh, mh};
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-          dequant_fp8x4(raw[c >> 1][(c & 1) * 2], s256, &kd[c][0]);
-          dequant_fp8x4(raw[c >> 1][(c & 1) * 2 + 1], s256, &kd[c][2]);
+          dequant_fp8x4(raw[c >> 1][(c & 1) * 2], sc, m2, &kd[c][0]);
+          dequant_fp8x4(raw[c >> 1][(c & 1) * 2 + 1], sc, m2, &kd[c][2]);
         }
       } else {
         v4u raw[4];
@@ -193,9 +188,12 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) raw[j] = (v4u){0u, 0u, 0u, 0u};
         }
-        const _Float16 s4[4] = {(_Float16)sc.x, (_Float16)sc.y, (_Float16)sc.z, (_Float16)sc.w};
+        const float s4[4] = {sc.x, sc.y, sc.z, sc.w};
 #pragma unroll
-        for (int c = 0; c < 16; ++c) dequant_fp4x8(raw[c >> 2][c & 3], s4[c >> 2], kd[c]);
+        for (int c = 0; c < 16; ++c) {
+          const _Float16 mh = scale_mantissa(s4[c >> 2]);
+          dequant_fp4x8(raw[c >> 2][c & 3], s4[c >> 2], (v2h){mh, mh}, kd[c]);
+        }
       }
       // S^T for keys kh*16 .. +16 and the 16 heads
       v4f s = {0.f, 0.f, 0.f, 0.f};
@@ -236,9 +234,7 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
       for (int j = 0; j < 4; ++j) {
         const float aj = __shfl(alpha, 4 * g + j);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) O[u][i][j] *= aj;
+        for (int u = 0; u < 32; ++u) O[u][j] *= aj;
       }
     }
     v8h P;
@@ -253,24 +249,26 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // O[h, d] += sum_keys P[h, key] V[key, d] with V read back transposed:
-    // MFMA (u, i) has output column r <-> d = 128 u + 8 r + i.
+    // O[h, d] += sum_keys P[h, key] V[key, d].  V is read transposed with
+    // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+    // i % 4 of the 8-byte rows addressed by lanes 4 j + i / 4 (j = 0..3).  Lane
+    // (r, g) addresses key 4 g + r / 4 (then 16 + 4 g + r / 4) at column
+    // 16 T + 4 (r % 4), so it receives V[4 g + j][16 T + r] (then the keys
+    // 16 + 4 g + j): exactly its B operand for output columns 16 T .. +16.
+    {
+      __attribute__((address_space(3))) uint8_t* tl =
+          (__attribute__((address_space(3))) uint8_t*)tile;
+      const int off_a = (4 * g + (r >> 2)) * AT_RS + 8 * (r & 3);
+      const int off_b = (16 + 4 * g + (r >> 2)) * AT_RS + 8 * (r & 3);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      v4u R[8];
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int key = (m < 4) ? (4 * g + m) : (16 + 4 * g + (m - 4));
-        R[m] = *(const v4u*)(tile + key * AT_RS + 256 * u + 16 * r);
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-        v4u bv;
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2)
-          bv[q2] = __builtin_amdgcn_perm(R[2 * q2 + 1][i >> 1], R[2 * q2][i >> 1], sel);
-        O[u][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, __builtin_bit_cast(v8h, bv), O[u][i], 0, 0, 0);
+      for (int u = 0; u < 32; ++u) {
+        const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(tl + off_a + 32 * u));
+        const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(tl + off_b + 32 * u));
+        const v8s_pair pr = {lo, hi};
+        const v8h bv = __builtin_bit_cast(v8h, pr);
+        O[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, bv, O[u], 0, 0, 0);
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -314,15 +312,9 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   // each wave writes its scaled partial output (fp32 [16][512]) over its tile
   float* part = (float*)tile;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 32; ++u)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float* dst = part + (4 * g + j) * AT_D + 128 * u + 8 * r;
-      const float4 v0 = make_float4(O[u][0][j] * fw[j], O[u][1][j] * fw[j], O[u][2][j] * fw[j], O[u][3][j] * fw[j]);
-      const float4 v1 = make_float4(O[u][4][j] * fw[j], O[u][5][j] * fw[j], O[u][6][j] * fw[j], O[u][7][j] * fw[j]);
-      *(float4*)dst = v0;
-      *(float4*)(dst + 4) = v1;
-    }
+    for (int j = 0; j < 4; ++j) part[(4 * g + j) * AT_D + 16 * u + r] = O[u][j] * fw[j];
   __syncthreads();
   const float* p0 = (const float*)(s_tile + 0 * AT_TILE_BYTES);
   const float* p1 = (const float*)(s_tile + 1 * AT_TILE_BYTES);

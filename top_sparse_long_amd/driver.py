@@ -73,6 +73,10 @@ class LayerRunner:
                            for i in range(len(wl.layers))]
         f32 = torch.float32
         self.scores = torch.empty((Q, self.stride), dtype=f32, device=device)
+        # block maxima written by the Full layer's scoring pass
+        self.fuse_block_max = wl.block_size <= 32
+        nbm = (self.n_cols + wl.block_size - 1) // wl.block_size
+        self.block_max = torch.empty((Q, _round_up(max(nbm, 1), 64)), dtype=f32, device=device)
         self.pool_scores = torch.empty((Q, _round_up(self.pool_cols, 64)), dtype=f32, device=device)
         self.cand = torch.empty((Q, wl.n_blocks), dtype=torch.int32, device=device)
         self.idx = {li: torch.empty((Q, wl.topk), dtype=torch.int32, device=device)
@@ -87,7 +91,7 @@ class LayerRunner:
         self.slots = SlotSet(self.main_rows, self.k_rows)
 
     # -- steps -----------------------------------------------------------------
-    def index_scores(self, li, pool):
+    def index_scores(self, li, pool, block_max=False):
         wl, lay = self.wl, self.wl.layers[li]
         wdt = CSA2_BF16 if self.quant else CSA2_F32
         if pool:
@@ -98,12 +102,14 @@ class LayerRunner:
         else:
             csa2_index_scores(self.layer_rows[li]["q_idx"], lay.w, wdt, self.slots.index_k,
                               wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio, self.scores,
-                              self.n_cols, self.Q)
+                              self.n_cols, self.Q, block_size=wl.block_size,
+                              block_max=self.block_max if block_max else None)
 
-    def block_candidates(self):
+    def block_candidates(self, from_block_max=False):
         wl = self.wl
         csa2_block_candidates(self.scores, self.n_cols, wl.q_pos, wl.ratio, wl.block_size,
-                              wl.n_blocks, self.cand, self.ws, self.Q)
+                              wl.n_blocks, self.cand, self.ws, self.Q,
+                              block_max=self.block_max if from_block_max else None)
         self.slots.candidates = self.cand
 
     def topk(self, li, pool):
@@ -125,28 +131,42 @@ class LayerRunner:
                          self.out[li], qdt if self.quant else CSA2_F32, self.lse[li], self.Q)
 
     # -- a whole pass ----------------------------------------------------------
+    def steps(self):
+        """The calls of one pass over every layer, in order, as (stage name,
+        callable) pairs."""
+        out = []
+
+        def reset():
+            self.slots.topk_idxs = None
+            self.slots.candidates = None
+        out.append(("reset", reset))
+        has_pool = False
+        for li, lay in enumerate(self.wl.layers):
+            if lay.mode == "full":
+                fuse = self.needs_pool[li] and self.fuse_block_max
+                out.append(("index_scores_dense",
+                            lambda li=li, fuse=fuse: self.index_scores(li, pool=False, block_max=fuse)))
+                if self.needs_pool[li]:
+                    out.append(("block_candidates",
+                                lambda fuse=fuse: self.block_candidates(from_block_max=fuse)))
+                    has_pool = True
+                out.append(("topk_dense", lambda li=li: self.topk(li, pool=False)))
+            elif lay.mode == "reindex":
+                pool = has_pool
+                out.append(("index_scores_pool" if pool else "index_scores_dense",
+                            lambda li=li, pool=pool: self.index_scores(li, pool=pool)))
+                out.append(("topk_pool" if pool else "topk_dense",
+                            lambda li=li, pool=pool: self.topk(li, pool=pool)))
+            out.append(("sparse_attn", lambda li=li: self.attention(li)))
+        return out
+
     def run(self, mark=None):
         """Run every layer once.  mark(name) is called before each step and
         once at the end with None (the benchmark records events there)."""
-        mark = mark or (lambda name: None)
-        self.slots.topk_idxs = None
-        self.slots.candidates = None
-        for li, lay in enumerate(self.wl.layers):
-            if lay.mode == "full":
-                mark("index_scores_dense")
-                self.index_scores(li, pool=False)
-                if self.needs_pool[li]:
-                    mark("block_candidates")
-                    self.block_candidates()
-                mark("topk_dense")
-                self.topk(li, pool=False)
-            elif lay.mode == "reindex":
-                pool = self.slots.candidates is not None
-                mark("index_scores_pool" if pool else "index_scores_dense")
-                self.index_scores(li, pool=pool)
-                mark("topk_pool" if pool else "topk_dense")
-                self.topk(li, pool=pool)
-            mark("sparse_attn")
-            self.attention(li)
-        mark(None)
+        for name, fn in self.steps():
+            if name != "reset" and mark:
+                mark(name)
+            fn()
+        if mark:
+            mark(None)
         return self.out

@@ -64,9 +64,14 @@ def _stage_work(run, stage):
     wl = run.wl
     nvis = wl.n_vis().clamp(max=run.n_cols)
     if stage == "index_scores_dense":
-        return float(nvis.sum().item()) * INDEX_BYTES_PER_KEY, int(nvis.sum().item())
+        # plus the fused block maxima (4 B per block) when the step emits them
+        extra = 4.0 / wl.block_size if run.fuse_block_max and any(run.needs_pool) else 0.0
+        return float(nvis.sum().item()) * (INDEX_BYTES_PER_KEY + extra), int(nvis.sum().item())
     if stage == "index_scores_pool":
         return float(wl.Q * run.pool_cols) * INDEX_BYTES_PER_KEY, wl.Q * run.pool_cols
+    if stage == "block_candidates" and run.fuse_block_max:
+        nblk = (nvis + wl.block_size - 1) // wl.block_size
+        return float(nblk.sum().item()) * SCORE_BYTES, int(nvis.sum().item())
     if stage in ("topk_dense", "block_candidates"):
         return float(nvis.sum().item()) * SCORE_BYTES, int(nvis.sum().item())
     if stage == "topk_pool":
@@ -277,7 +282,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "gpu_ms_per_step": gpu_ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "fp8 index scores, f16 attention (fp32 accumulate)", "data": "synthetic",
+        "dtype": "f16", "data": "synthetic",
         "config": {"workload": args.workload, "batch": wl.Q, "ctx_entries": wl.max_cols(),
                    "ratio": wl.ratio, "layers": [l.mode for l in wl.layers],
                    "topk": wl.topk, "pool_blocks": wl.n_blocks, "block_size": wl.block_size,

@@ -46,6 +46,8 @@ constexpr int AT_TILE_BYTES = 32 * AT_RS;     // one wave's 32-key tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_SLACK = 8.0f;         // log2 units
+constexpr int AT_MAX_K = 2048;                // largest top-k the kernel stages
+static_assert(32 * 64 * 16 <= AT_TILE_BYTES, "a wave's partial O must fit its tile");
 
 __device__ __forceinline__ uint32_t as_u32(v2h h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ v2h as_v2h(uint32_t u) { return __builtin_bit_cast(v2h, u); }
@@ -80,11 +82,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   return (uint16_t)(u >> 16);
 }
 
+// Raw bytes of one tile as one lane holds them while the previous tile is
+// computed.  Main tile: 64 E2M1 bytes and 4 scales of the lane's key in each
+// 16-key half kh (d[4 kh + j], s[kh]).  SWA tile: only the first half's 128
+// E4M3 codes and scale -- the second half is requested when the tile starts.
+struct MainTile {
+  v4u d[8];
+  float4 s[2];
+  bool ok[2];
+};
+struct SwaTile {
+  v4u d[8];
+  float s;
+  bool ok[2];
+};
+
 __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[AT_WAVES * AT_TILE_BYTES];
   __shared__ float s_m[AT_WAVES][AT_HEADS];
   __shared__ float s_l[AT_WAVES][AT_HEADS];
-  __shared__ float s_f[AT_HEADS];
+  __shared__ int32_t s_idx[AT_MAX_K];
 
   const int n_hg = a.H / AT_HEADS;
   int bid = blockIdx.x;
@@ -96,7 +113,8 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   const int hg = bid - t * n_hg;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave-uniform, so tile-type branches are scalar branches
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15;
   const int g = lane >> 4;
 
@@ -111,22 +129,83 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   const int64_t sbase = a.swa_base[b] + (first - sp0);
   const int n_swa_tiles = (n_swa + 31) >> 5;
   const int n_tiles = n_swa_tiles + ((a.k + 31) >> 5);
+  const int h_glob0 = hg * AT_HEADS;
+  // keys that do not exist are read from this query's own q row (always
+  // mapped, 64 KB) and given a zero scale, so every load is unconditional
+  const uint8_t* dummy = (const uint8_t*)a.q + (int64_t)t * a.H * AT_D * 2;
 
+  // ---- prologue: every independent load is issued before any is waited on
   // q as the B operand of S^T = K Q^T: head (16 hg + r), dims [128 g, +128),
   // chunk c holding dims 128 g + 8 c .. +8.
-  v8h qf[16];
+  v4u qraw[16];
   {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)t * a.H + hg * AT_HEADS + r) * AT_D + 128 * g;
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)t * a.H + h_glob0 + r) * AT_D + 128 * g;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const v4u raw = *(const v4u*)(qrow + 8 * c);
+    for (int c = 0; c < 16; ++c) qraw[c] = *(const v4u*)(qrow + 8 * c);
+  }
+  // the query's selected positions (staged in LDS below)
+  int32_t iv[AT_MAX_K / 256];
+  if (a.k > 0) {
+    const int32_t* irow = a.idx + (int64_t)t * a.k;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        qf[c][2 * e] = (_Float16)__uint_as_float(raw[e] << 16);
-        qf[c][2 * e + 1] = (_Float16)__uint_as_float(raw[e] & 0xFFFF0000u);
-      }
+    for (int j = 0; j < AT_MAX_K / 256; ++j) iv[j] = irow[min((int)threadIdx.x + 256 * j, a.k - 1)];
+  }
+  // sink logits of this lane's output rows (heads 4 g + j) and, for the
+  // first 16 threads, of head threadIdx.x
+  float sink_rows[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) sink_rows[j] = a.sink[h_glob0 + 4 * g + j];
+
+  // Loads of one tile; no branch depends on loaded data.
+  auto load_swa_half = [&](int slot, v4u* d, float& sc, bool& ok) {
+    // past the window's end: the last row again, masked later
+    const int64_t row = sbase + min(slot, n_swa - 1);
+    const uint8_t* src = a.swa + row * a.swa_stride + 128 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) d[j] = *(const v4u*)(src + 16 * j);
+    sc = a.swa_scale[row * a.swa_scale_stride + g];
+    ok = slot < n_swa;
+  };
+  auto load_swa = [&](int ti, SwaTile& S) {
+    load_swa_half(ti * 32 + r, S.d, S.s, S.ok[0]);
+    S.ok[1] = ti * 32 + 16 + r < n_swa;
+  };
+  auto load_main = [&](int ti, MainTile& M) {
+    const int slot0 = (ti - n_swa_tiles) * 32;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int slot = slot0 + kh * 16 + r;
+      const int pos = slot < a.k ? s_idx[slot] : -1;
+      const bool v = pos >= 0 && pos < nvis;
+      const uint8_t* src = v ? a.main + (mbase + pos) * a.main_stride : dummy;
+      const float* ssrc = v ? a.main_scale + (mbase + pos) * a.main_scale_stride : (const float*)dummy;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) M.d[4 * kh + j] = *(const v4u*)(src + 64 * g + 16 * j);
+      M.s[kh] = *(const float4*)(ssrc + 4 * g);
+      M.ok[kh] = v;
+    }
+  };
+
+  SwaTile S;
+  MainTile M;
+  if (wave < n_swa_tiles) load_swa(wave, S);   // needs no staged index
+
+  v8h qf[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qf[c][2 * e] = (_Float16)__uint_as_float(qraw[c][e] << 16);
+      qf[c][2 * e + 1] = (_Float16)__uint_as_float(qraw[c][e] & 0xFFFF0000u);
     }
   }
+  if (a.k > 0) {
+#pragma unroll
+    for (int j = 0; j < AT_MAX_K / 256; ++j)
+      if ((int)threadIdx.x + 256 * j < a.k) s_idx[threadIdx.x + 256 * j] = iv[j];
+  }
+  __syncthreads();   // s_idx
+  if (wave >= n_swa_tiles && wave < n_tiles) load_main(wave, M);
 
   // O[T]: output columns d = 16 T + r, rows = heads 4 g + j
   v4f O[32];
@@ -137,81 +216,58 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   const float zscale = a.scale * LOG2E;
   uint8_t* tile = s_tile + wave * AT_TILE_BYTES;
 
-  for (int ti = wave; ti < n_tiles; ti += AT_WAVES) {
-    const bool is_swa = ti < n_swa_tiles;
-    const int slot0 = (is_swa ? ti : ti - n_swa_tiles) * 32;
-    v4f acc[2];
-    uint64_t vmask[2];
+  // Dequantize tile ti chunk by chunk (8 dims of the lane's key per chunk):
+  // each chunk is written to the LDS tile for P V and is the A operand of
+  // S^T = K Q^T from registers.
+  auto stage_swa = [&](int ti, const SwaTile& S, v4f acc[2], uint64_t vmask[2]) {
+    v4u d1[8];
+    float sc1;
+    bool ok1;
+    load_swa_half(ti * 32 + 16 + r, d1, sc1, ok1);
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const int slot = slot0 + kh * 16 + r;
-      bool valid;
-      int64_t row;
-      if (is_swa) {
-        valid = slot < n_swa;
-        row = sbase + slot;
-      } else {
-        const int pos = slot < a.k ? a.idx[(int64_t)t * a.k + slot] : -1;
-        valid = pos >= 0 && pos < nvis;
-        row = mbase + pos;
-      }
-      vmask[kh] = __ballot(valid);
-      uint32_t kd[16][4];   // chunk c: dims 128 g + 8 c .. +8 as f16 pairs
-      if (is_swa) {
-        v4u raw[8];
-        float sc = 0.f;
-        if (valid) {
-          const uint8_t* src = a.swa + row * a.swa_stride + 128 * g;
-#pragma unroll
-          for (int j = 0; j < 8; ++j) raw[j] = *(const v4u*)(src + 16 * j);
-          sc = a.swa_scale[row * a.swa_scale_stride + g];
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) raw[j] = (v4u){0u, 0u, 0u, 0u};
-        }
-        const _Float16 mh = scale_mantissa(sc);
-        const v2h m2 = {mh, mh};
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          dequant_fp8x4(raw[c >> 1][(c & 1) * 2], sc, m2, &kd[c][0]);
-          dequant_fp8x4(raw[c >> 1][(c & 1) * 2 + 1], sc, m2, &kd[c][2]);
-        }
-      } else {
-        v4u raw[4];
-        float4 sc = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (valid) {
-          const uint8_t* src = a.main + row * a.main_stride + 64 * g;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) raw[j] = *(const v4u*)(src + 16 * j);
-          sc = *(const float4*)(a.main_scale + row * a.main_scale_stride + 4 * g);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) raw[j] = (v4u){0u, 0u, 0u, 0u};
-        }
-        const float s4[4] = {sc.x, sc.y, sc.z, sc.w};
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          const _Float16 mh = scale_mantissa(s4[c >> 2]);
-          dequant_fp4x8(raw[c >> 2][c & 3], s4[c >> 2], (v2h){mh, mh}, kd[c]);
-        }
-      }
-      // S^T for keys kh*16 .. +16 and the 16 heads
-      v4f s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        const v4u kv = {kd[c][0], kd[c][1], kd[c][2], kd[c][3]};
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qf[c], s, 0, 0, 0);
-      }
-      acc[kh] = s;
-      // stage the dequantized row for P V
+      const v4u* d = kh ? d1 : S.d;
+      const float sc = kh ? sc1 : S.s;
+      const _Float16 mh = scale_mantissa(sc);
+      const v2h m2 = {mh, mh};
       uint8_t* dst = tile + (kh * 16 + r) * AT_RS + 256 * g;
+      v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // two chains
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
-        const v4u kv = {kd[c][0], kd[c][1], kd[c][2], kd[c][3]};
+        uint32_t kd[4];
+        dequant_fp8x4(d[c >> 1][(c & 1) * 2], sc, m2, &kd[0]);
+        dequant_fp8x4(d[c >> 1][(c & 1) * 2 + 1], sc, m2, &kd[2]);
+        const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
         *(v4u*)(dst + 16 * c) = kv;
+        s[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qf[c], s[c & 1], 0, 0, 0);
       }
+      acc[kh] = s[0] + s[1];
+      vmask[kh] = __ballot(S.ok[kh]);
     }
+  };
+  auto stage_main = [&](const MainTile& M, v4f acc[2], uint64_t vmask[2]) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const float4 sc = M.ok[kh] ? M.s[kh] : make_float4(0.f, 0.f, 0.f, 0.f);
+      const float s4[4] = {sc.x, sc.y, sc.z, sc.w};
+      uint8_t* dst = tile + (kh * 16 + r) * AT_RS + 256 * g;
+      v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // two chains
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        uint32_t kd[4];
+        const _Float16 mh = scale_mantissa(s4[c >> 2]);
+        dequant_fp4x8(M.d[4 * kh + (c >> 2)][c & 3], s4[c >> 2], (v2h){mh, mh}, kd);
+        const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
+        *(v4u*)(dst + 16 * c) = kv;
+        s[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qf[c], s[c & 1], 0, 0, 0);
+      }
+      acc[kh] = s[0] + s[1];
+      vmask[kh] = __ballot(M.ok[kh]);
+    }
+  };
 
+  // Online softmax over the tile's scores and O += P V.
+  auto finish_tile = [&](const v4f acc[2], const uint64_t vmask[2]) {
     // scores of head r for keys {4g+i} and {16+4g+i}
     float z[8];
 #pragma unroll
@@ -274,9 +330,37 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // This wave's tiles are wave, wave + 4, ... (SWA tiles first).  The next
+  // tile's rows are requested as soon as the current tile's raw bytes have
+  // been dequantized, so they are in flight during the softmax and the
+  // LDS-bound P V product.
+  int ti = wave;
+  for (; ti < n_swa_tiles; ti += AT_WAVES) {
+    v4f acc[2];
+    uint64_t vmask[2];
+    stage_swa(ti, S, acc, vmask);
+    const int nx = ti + AT_WAVES;
+    if (nx < n_swa_tiles) load_swa(nx, S);
+    else if (nx < n_tiles) load_main(nx, M);
+    finish_tile(acc, vmask);
+  }
+  for (; ti < n_tiles; ti += AT_WAVES) {
+    v4f acc[2];
+    uint64_t vmask[2];
+    stage_main(M, acc, vmask);
+    if (ti + AT_WAVES < n_tiles) load_main(ti + AT_WAVES, M);
+    finish_tile(acc, vmask);
   }
 
   // ---- merge the four waves ------------------------------------------------
+  // Each wave's (m, l) per head go through LDS; every lane then forms, for
+  // its rows (heads 4 g + j), the factor that scales each wave's partial O
+  // onto the common maximum and divides by the full denominator (sink
+  // included).  Partials are exchanged in register layout (one 16-byte LDS
+  // store per accumulator), and wave w sums the column blocks u in
+  // [8 w, 8 w + 8) of all four.
   float l = l_part;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
@@ -284,57 +368,50 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
     s_m[wave][r] = m_s;
     s_l[wave][r] = l;
   }
-  __syncthreads();
-  const int h_glob0 = hg * AT_HEADS;
-  if (threadIdx.x < AT_HEADS) {
-    const int h = threadIdx.x;
-    const float sink2 = a.sink[h_glob0 + h] * LOG2E;
-    float M = sink2;
-    for (int w = 0; w < AT_WAVES; ++w) M = fmaxf(M, s_m[w][h]);
-    float den = (M == -INFINITY) ? 0.f : exp2f(sink2 - M);
-    for (int w = 0; w < AT_WAVES; ++w)
-      if (s_m[w][h] > -INFINITY) den += s_l[w][h] * exp2f(s_m[w][h] - M);
-    s_f[h] = (den > 0.f) ? 1.f / den : 0.f;
-    if (a.lse) a.lse[(int64_t)t * a.H + h_glob0 + h] = (M + log2f(den)) * LN2;
+  {
+    uint8_t* part = tile;
+#pragma unroll
+    for (int u = 0; u < 32; ++u) *(v4f*)(part + (u * 64 + lane) * 16) = O[u];
   }
   __syncthreads();
-  // factor of this wave for the rows it holds: heads 4g + j
-  float fw[4];
+  float fw[AT_WAVES][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int h = 4 * g + j;
-    const float sink2 = a.sink[h_glob0 + h] * LOG2E;
+    const float sink2 = sink_rows[j] * LOG2E;
     float M = sink2;
+#pragma unroll
     for (int w = 0; w < AT_WAVES; ++w) M = fmaxf(M, s_m[w][h]);
-    const float mw = s_m[wave][h];
-    fw[j] = (mw == -INFINITY) ? 0.f : exp2f(mw - M) * s_f[h];
+    float den = (M == -INFINITY) ? 0.f : exp2f(sink2 - M);
+    float e[AT_WAVES];
+#pragma unroll
+    for (int w = 0; w < AT_WAVES; ++w) {
+      const float mw = s_m[w][h];
+      e[w] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+      den += s_l[w][h] * e[w];
+    }
+    const float inv = (den > 0.f) ? 1.f / den : 0.f;
+#pragma unroll
+    for (int w = 0; w < AT_WAVES; ++w) fw[w][j] = e[w] * inv;
+    if (a.lse && wave == 0 && r == 0) a.lse[(int64_t)t * a.H + h_glob0 + h] = (M + log2f(den)) * LN2;
   }
-  // each wave writes its scaled partial output (fp32 [16][512]) over its tile
-  float* part = (float*)tile;
+  const int64_t obase = ((int64_t)t * a.H + h_glob0 + 4 * g) * AT_D + r;
 #pragma unroll
-  for (int u = 0; u < 32; ++u)
+  for (int uu = 0; uu < 32 / AT_WAVES; ++uu) {
+    const int u = wave * (32 / AT_WAVES) + uu;
+    v4f v = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) part[(4 * g + j) * AT_D + 16 * u + r] = O[u][j] * fw[j];
-  __syncthreads();
-  const float* p0 = (const float*)(s_tile + 0 * AT_TILE_BYTES);
-  const float* p1 = (const float*)(s_tile + 1 * AT_TILE_BYTES);
-  const float* p2 = (const float*)(s_tile + 2 * AT_TILE_BYTES);
-  const float* p3 = (const float*)(s_tile + 3 * AT_TILE_BYTES);
-  const int64_t obase = ((int64_t)t * a.H + h_glob0) * AT_D;
-  for (int e = threadIdx.x * 4; e < AT_HEADS * AT_D; e += 256 * 4) {
-    const float4 x0 = *(const float4*)(p0 + e);
-    const float4 x1 = *(const float4*)(p1 + e);
-    const float4 x2 = *(const float4*)(p2 + e);
-    const float4 x3 = *(const float4*)(p3 + e);
-    const float4 v = make_float4(x0.x + x1.x + x2.x + x3.x, x0.y + x1.y + x2.y + x3.y,
-                                 x0.z + x1.z + x2.z + x3.z, x0.w + x1.w + x2.w + x3.w);
-    if (a.out_bf16) {
-      uint2 pk;
-      pk.x = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
-      pk.y = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
-      *(uint2*)((uint16_t*)a.out + obase + e) = pk;
-    } else {
-      *(float4*)((float*)a.out + obase + e) = v;
+    for (int w = 0; w < AT_WAVES; ++w) {
+      const v4f x = *(const v4f*)(s_tile + w * AT_TILE_BYTES + (u * 64 + lane) * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] += x[j] * fw[w][j];
+    }
+    // rows 4 g + j, column 16 u + r: 16 lanes write 16 consecutive columns
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t o = obase + (int64_t)j * AT_D + 16 * u;
+      if (a.out_bf16) ((uint16_t*)a.out)[o] = f32_to_bf16_rne(v[j]);
+      else ((float*)a.out)[o] = v[j];
     }
   }
 }

@@ -47,6 +47,12 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stage-reps", type=int, default=10,
                     help="repetitions per input copy when timing single stages")
+    ap.add_argument("--summarize-profiles", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT_DIR"),
+                    help="no GPU: turn rocprofv3 CSV output of this benchmark (a --kernel-trace "
+                         "--stats run, a --pmc FETCH_SIZE run and a --pmc WRITE_SIZE run) into the "
+                         "text summaries and per-stage traffic records kept under profiles/")
+    ap.add_argument("--profile-command", default="",
+                    help="the benchmark command the profiles were taken on (recorded in the summaries)")
     return ap.parse_args()
 
 
@@ -94,6 +100,94 @@ def _traffic(stage, workload, launches_bytes):
     if rec.get("source_sha1") != _source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+# kernels of each stage, as they appear in the profiler's kernel names
+STAGE_KERNELS = {
+    "index_scores_dense": ("index_scores_fp8_kernel<false", "index_scores_f32_kernel"),
+    "index_scores_pool": ("index_scores_fp8_kernel<true",),
+    "block_candidates": ("select_kernel<2,",),
+    "topk_dense": ("select_kernel<0,", "select_kernel<3,"),
+    "topk_pool": ("select_kernel<1,",),
+    "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_f32_kernel"),
+}
+CALIB_KERNEL = "__amd_rocclr_copyBuffer"
+CALIB_KIB = 256 * 1024          # the benchmark's calibration copy moves 256 MiB each way
+
+
+def _find_csv(d, suffix):
+    for root, _, files in os.walk(d):
+        for f in files:
+            if f.endswith(suffix):
+                return os.path.join(root, f)
+    raise FileNotFoundError(f"no *{suffix} under {d}")
+
+
+def _counter_per_kernel(path):
+    import csv
+    per = {}
+    for row in csv.DictReader(open(path)):
+        per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return per
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, workload, command):
+    """Write kernels_<workload>.txt, counters_<workload>.txt and one
+    traffic_<stage>_<workload>.json per stage from rocprofv3 CSV output."""
+    import csv
+    os.makedirs(out_dir, exist_ok=True)
+    stats = list(csv.DictReader(open(_find_csv(trace_dir, "kernel_stats.csv"))))
+    lines = [f"# rocprofv3 kernel-trace summary, workload {workload}",
+             f"# command: rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -- {command}",
+             f"# columns: calls, average us, min us, max us, kernel", ""]
+    avg_us = {}
+    for row in stats:
+        name = row["Name"]
+        if "csa2::" not in name:
+            continue
+        avg = float(row["AverageNs"]) / 1e3
+        avg_us[name] = avg
+        lines.append(f"{int(row['Calls']):6d} {avg:10.2f} {float(row['MinNs']) / 1e3:10.2f} "
+                     f"{float(row['MaxNs']) / 1e3:10.2f}  {name}")
+    with open(os.path.join(out_dir, f"kernels_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    fetch = _counter_per_kernel(_find_csv(fetch_dir, "counter_collection.csv"))
+    write = _counter_per_kernel(_find_csv(write_dir, "counter_collection.csv"))
+    fscale = CALIB_KIB / max(fetch.get(CALIB_KERNEL, [CALIB_KIB]))
+    wscale = CALIB_KIB / max(write.get(CALIB_KERNEL, [CALIB_KIB]))
+    lines = [f"# rocprofv3 counter summary (KiB per dispatch, averaged), workload {workload}",
+             f"# commands: rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -- {command}",
+             f"#           rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -- {command}",
+             f"# calibration: the {CALIB_KIB} KiB device copy reads FETCH_SIZE "
+             f"{max(fetch.get(CALIB_KERNEL, [0])):.1f} KiB -> scale {fscale:.4f}; "
+             f"WRITE_SIZE {max(write.get(CALIB_KERNEL, [0])):.1f} KiB -> scale {wscale:.4f}",
+             "# columns: dispatches, FETCH_SIZE raw, WRITE_SIZE raw, scaled HBM MB (read + write), kernel", ""]
+    per_kernel_bytes = {}
+    for name in sorted(set(fetch) | set(write)):
+        if "csa2::" not in name:
+            continue
+        fr = sum(fetch.get(name, [0])) / max(1, len(fetch.get(name, [])))
+        wr = sum(write.get(name, [0])) / max(1, len(write.get(name, [])))
+        b = (fr * fscale + wr * wscale) * 1024
+        per_kernel_bytes[name] = b
+        lines.append(f"{len(fetch.get(name, [])):6d} {fr:12.1f} {wr:12.1f} {b / 1e6:12.3f}  {name}")
+    with open(os.path.join(out_dir, f"counters_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+    src = _source_hash()
+    for stage, pats in STAGE_KERNELS.items():
+        names = [n for n in per_kernel_bytes if any(p in n for p in pats)]
+        if not names:
+            continue
+        rec = {"stage": stage, "workload": workload, "kernels": names,
+               "hbm_bytes_per_launch": sum(per_kernel_bytes[n] for n in names),
+               "rocprof_avg_us": {n: avg_us.get(n) for n in names},
+               "fetch_scale": fscale, "write_scale": wscale, "source_sha1": src,
+               "command": command}
+        with open(os.path.join(out_dir, f"traffic_{stage}_{workload}.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
 
 
 def cpu_baseline(wl, n_sample):
@@ -166,6 +260,9 @@ def cpu_baseline(wl, n_sample):
 
 def main():
     args = _parse()
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, args.workload, args.profile_command)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
               "path is a design in DESIGN.md, not a measured configuration.", file=sys.stderr)

@@ -55,6 +55,50 @@ def test_index_scores_fp8_ragged(ratio):
     check_scores(gpu, ref)
 
 
+def _prefill_positions(n_tok, n_q, seed):
+    """n_q causal positions of one sequence of n_tok tokens: the chunk's tail
+    plus a few early positions (nearly empty rows)."""
+    rng = np.random.default_rng(seed)
+    tail = list(range(n_tok - (n_q - 6), n_tok))
+    early = sorted(rng.choice(np.arange(0, 64), size=6, replace=False).tolist())
+    return early + tail
+
+
+@pytest.mark.parametrize("case", ["one_sequence", "mixed_tiles"])
+def test_index_scores_prefill_fp8(case):
+    """Many queries (at least the query-tiled kernel's threshold): a ragged
+    count, causal m = 2 rows of different lengths, and, in the mixed case,
+    16-query tiles that straddle sequences."""
+    if case == "one_sequence":
+        n_entries = [5000]
+        positions = [_prefill_positions(10000, 300, 1)]
+    else:
+        n_entries = [3000, 2100, 4100]
+        positions = [_prefill_positions(2 * n, nq, 2 + i)
+                     for i, (n, nq) in enumerate(zip(n_entries, (101, 90, 83)))]
+    _announce(f"index_scores prefill fp8 {case}")
+    wl = synth.mini_workload(60, n_entries, ratio=2, positions=positions).to(DEV)
+    assert wl.Q >= 256
+    run = LayerRunner(wl)
+    run.index_scores(0, pool=False, block_max=True)
+    torch.cuda.synchronize()
+    gpu = _np(run.scores[:, :run.n_cols])
+    m = oracle_io.meta(wl)
+    ref = oracle.index_scores_dense(oracle_io.index_q(wl.layers[0], True),
+                                    oracle_io.index_w(wl.layers[0], True),
+                                    oracle_io.index_k_rows(wl), m["seq_base"], m["q_seq"],
+                                    m["q_pos"], 2, run.n_cols)
+    check_scores(gpu, ref)
+    # fused block maxima of the GPU's own scores
+    nb = -(-run.n_cols // 8)
+    bm = _np(run.block_max[:, :nb]).astype(np.float64)
+    nvis = oracle.visible_count(m["q_pos"], 2)
+    for t in range(wl.Q):
+        refb = oracle.block_maxima(gpu[t].astype(np.float64), int(nvis[t]), 8)
+        assert np.array_equal(bm[t, :len(refb)], refb), t
+        assert np.all(bm[t, len(refb):] == -np.inf), t
+
+
 def test_index_scores_f32_exact():
     _announce("index_scores f32 integer-exact")
     wl = synth.mini_workload(3, [3000, 777], q_per_seq=3, quantized=False).to(DEV)
@@ -350,6 +394,31 @@ def test_fused_block_max_matches_scores():
     torch.cuda.synchronize()
     assert np.array_equal(a, _np(run.cand))
     assert np.array_equal(a, oracle.block_candidates(g, _np(wl.q_pos), 1, 8, wl.n_blocks))
+
+
+@pytest.mark.parametrize("many", [False, True])
+@pytest.mark.parametrize("bs", [1, 2, 4, 16, 32])
+def test_fused_block_max_sizes(bs, many):
+    """Block maxima fused into scoring for every supported block size, on the
+    per-query kernel and on the query-tiled one (many queries)."""
+    _announce(f"fused block maxima bs={bs} many={many}")
+    if many:
+        wl = synth.mini_workload(44, [3333], ratio=2, block_size=bs,
+                                 positions=[_prefill_positions(6666, 260, 7)]).to(DEV)
+    else:
+        wl = synth.mini_workload(44, [7000, 333], q_per_seq=2, block_size=bs,
+                                 positions=[[6999, 4000], [332, 5]]).to(DEV)
+    run = LayerRunner(wl)
+    run.index_scores(0, pool=False, block_max=True)
+    torch.cuda.synchronize()
+    g = _np(run.scores[:, :run.n_cols]).astype(np.float64)
+    nb = -(-run.n_cols // bs)
+    bm = _np(run.block_max[:, :nb]).astype(np.float64)
+    nvis = oracle.visible_count(_np(wl.q_pos), wl.ratio)
+    for t in range(wl.Q):
+        ref = oracle.block_maxima(g[t], int(nvis[t]), bs)
+        assert np.array_equal(bm[t, :len(ref)], ref), t
+        assert np.all(bm[t, len(ref):] == -np.inf), t
 
 
 def test_graph_replay_matches_eager():

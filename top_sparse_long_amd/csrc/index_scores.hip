@@ -86,6 +86,33 @@ __device__ __forceinline__ v8h fp8x8_to_f16(uint32_t lo, uint32_t hi) {
   return (v8h){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// ReLU of a float as one integer max: non-negative floats are non-negative
+// as int32, negative floats are negative (so they become +0).
+__device__ __forceinline__ float relu(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
+// v + (the value of the lane 32 away), in every lane (gfx950 permlane swap:
+// no LDS round trip).
+__device__ __forceinline__ float add_half_swap(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Maximum over aligned groups of bs consecutive lanes (bs a power of two,
+// at most 32), valid at the first lane of each group.  DPP moves within
+// 16-lane rows; only bs = 32 crosses rows.
+__device__ __forceinline__ float group_max(float m, int bs) {
+#define CSA2_DPP(x, ctrl) __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), ctrl, 0xF, 0xF, false))
+  if (bs > 1) m = fmaxf(m, CSA2_DPP(m, 0xB1));   // quad_perm [1,0,3,2]: lane ^ 1
+  if (bs > 2) m = fmaxf(m, CSA2_DPP(m, 0x4E));   // quad_perm [2,3,0,1]: lane ^ 2
+  if (bs > 4) m = fmaxf(m, CSA2_DPP(m, 0x12C));  // row_ror 12: lane + 4 (mod 16)
+  if (bs > 8) m = fmaxf(m, CSA2_DPP(m, 0x128));  // row_ror 8: lane + 8 (mod 16)
+#undef CSA2_DPP
+  if (bs > 16) m = fmaxf(m, __shfl_xor(m, 16));
+  return m;
+}
+
 template <bool POOL, bool W_BF16>
 __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexScoreArgs a) {
   const int t = blockIdx.y;
@@ -175,17 +202,183 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
       }
       float v = 0.f;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) v = fmaf(gate[j], fmaxf(acc[j], 0.f), v);
-      v += __shfl_xor(v, 32);
+      for (int j = 0; j < 16; ++j) v = fmaf(gate[j], relu(acc[j]), v);
+      v = add_half_swap(v);
       sc = (pos[i] >= 0) ? v * ks[i] : -INFINITY;
     }
     if (half == 0 && col < a.n_cols) out[col] = sc;
     if (!POOL && a.block_max) {
       // maximum over aligned groups of block_size lanes (block_size <= 32)
-      float m = sc;
-      for (int sh = 1; sh < (1 << a.block_shift); sh <<= 1) m = fmaxf(m, __shfl_xor(m, sh));
+      const float m = group_max(sc, 1 << a.block_shift);
       if (half == 0 && (r & ((1 << a.block_shift) - 1)) == 0 && col < a.n_cols)
         a.block_max[(int64_t)t * a.block_max_stride + (col >> a.block_shift)] = m;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Many queries over one sequence (a prefill chunk): keys are shared, so the
+// contraction is a real matrix product and the kernel is MFMA-bound.
+//
+// One workgroup = 16 consecutive queries x a run of PF_BLOCKS blocks of 256
+// keys.  Each key block's E4M3 rows are widened to f16 once and staged in LDS
+// (double-buffered: the next block's bytes are in registers while the current
+// block is contracted); each of the 8 waves keeps the A operands of 2 queries
+// (32 heads x 128 dims each) in registers, reads every B operand once from
+// LDS and uses it for both queries.  Operand mapping and epilogue are those of
+// the per-query kernel above.  Queries of the tile that belong to different
+// sequences are handled in separate passes over the same key range.
+constexpr int PF_Q = 16;                 // queries per workgroup
+constexpr int PF_KB = 256;               // keys per staged block
+constexpr int PF_WAVES = 8;
+constexpr int PF_BLOCKS = 8;             // key blocks per workgroup
+constexpr int PF_RS = 272;               // LDS row stride of an f16 key row (bytes)
+
+template <bool W_BF16>
+__global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(IndexScoreArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_k[2][PF_KB * PF_RS];
+  __shared__ float s_ks[2][PF_KB];
+
+  const int t0 = blockIdx.y * PF_Q;
+  const int blk0 = blockIdx.x * PF_BLOCKS;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int half = lane >> 5;
+  const int r = lane & 31;
+  const int nq = min(PF_Q, a.Q - t0);
+  const int n_blk = min(PF_BLOCKS, (a.n_cols + PF_KB - 1) / PF_KB - blk0);
+
+  // this wave's two queries
+  int tq[2], nv[2], sq[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int qi = 2 * wave + i;
+    tq[i] = t0 + qi;
+    const bool live = qi < nq;
+    nv[i] = live ? visible_count(a.q_pos[tq[i]], a.ratio) : 0;
+    sq[i] = live ? a.q_seq[tq[i]] : -1;
+  }
+
+  // A operands (head r, bytes [64 half, +64) of the row) and gates
+  v8h qa[2][8];
+  float gate[2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int tt = min(tq[i], a.Q - 1);
+    const v4u* qsrc = (const v4u*)(a.q + (int64_t)(tt * 32 + r) * a.q_row_stride + 64 * half);
+    v4u qraw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) qraw[j] = qsrc[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qa[i][2 * j] = fp8x8_to_f16(qraw[j][0], qraw[j][1]);
+      qa[i][2 * j + 1] = fp8x8_to_f16(qraw[j][2], qraw[j][3]);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int h = 8 * (j >> 2) + 4 * half + (j & 3);
+      const float wv = W_BF16 ? bf16_to_f32(((const uint16_t*)a.w)[(int64_t)tt * 32 + h])
+                              : ((const float*)a.w)[(int64_t)tt * 32 + h];
+      gate[i][j] = wv * a.q_scale[(int64_t)(tt * 32 + h) * a.q_scale_stride];
+    }
+  }
+
+  // staging assignment: thread -> (key kk of the block, 64-byte half hh)
+  const int kk = threadIdx.x >> 1;
+  const int hh = threadIdx.x & 1;
+
+  for (int pass = 0; pass < nq; ++pass) {
+    // one pass per distinct sequence among the tile's queries (in order of
+    // first appearance); every value below is uniform across the workgroup
+    const int b = a.q_seq[t0 + pass];
+    bool seen = false;
+    for (int j = 0; j < pass; ++j) seen |= (a.q_seq[t0 + j] == b);
+    if (seen) continue;
+    int maxvis = 0;
+    for (int j = 0; j < nq; ++j)
+      if (a.q_seq[t0 + j] == b) maxvis = max(maxvis, visible_count(a.q_pos[t0 + j], a.ratio));
+    const int64_t base = a.seq_base[b];
+    const bool act[2] = {sq[0] == b, sq[1] == b};
+
+    // raw bytes of one block: key kk, bytes [64 hh, +64), and its scale
+    v4u kraw[4];
+    float kscale = 0.f;
+    auto load_block = [&](int blk) {
+      // rows past the last visible entry repeat it (masked later)
+      const int col = min(blk * PF_KB + kk, max(maxvis - 1, 0));
+      const int64_t row = base + col;
+      const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 64 * hh);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kraw[j] = src[j];
+      kscale = a.k_scale[row * a.k_scale_stride];
+    };
+    auto store_block = [&](int buf) {
+      uint8_t* dst = s_k[buf] + kk * PF_RS + 128 * hh;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *(v8h*)(dst + 32 * j) = fp8x8_to_f16(kraw[j][0], kraw[j][1]);
+        *(v8h*)(dst + 32 * j + 16) = fp8x8_to_f16(kraw[j][2], kraw[j][3]);
+      }
+      if (hh == 0) s_ks[buf][kk] = kscale;
+    };
+
+    if (maxvis > 0) {
+      load_block(blk0);
+      store_block(0);
+    }
+    __syncthreads();
+    for (int j = 0; j < n_blk; ++j) {
+      const int blk = blk0 + j;
+      const int buf = j & 1;
+      const int colb = blk * PF_KB;
+      const bool more = (j + 1 < n_blk) && maxvis > 0;
+      if (more) load_block(blk + 1);
+#pragma unroll 1
+      for (int tile = 0; tile < PF_KB / 32; ++tile) {
+        const int tcol = colb + tile * 32;
+        if (tcol >= a.n_cols) break;
+        const int col = tcol + r;
+        // does either query see any column of this tile?
+        const bool need0 = act[0] && tcol < nv[0];
+        const bool need1 = act[1] && tcol < nv[1];
+        float sc[2] = {-INFINITY, -INFINITY};
+        if (need0 || need1) {
+          const uint8_t* krow = s_k[buf] + (tile * 32 + r) * PF_RS + 128 * half;
+          v8h kb[8];
+#pragma unroll
+          for (int m = 0; m < 8; ++m) kb[m] = *(const v8h*)(krow + 16 * m);
+          const float ks = s_ks[buf][tile * 32 + r];
+          // both queries' chains interleaved (a query that sees none of the
+          // tile is computed anyway and masked)
+          v16f acc[2] = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f},
+                         {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][m], kb[m], acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][m], kb[m], acc[1], 0, 0, 0);
+          }
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            float v = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) v = fmaf(gate[i][jj], relu(acc[i][jj]), v);
+            v = add_half_swap(v);
+            sc[i] = (act[i] && col < nv[i]) ? v * ks : -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (!act[i]) continue;
+          if (half == 0 && col < a.n_cols) a.scores[(int64_t)tq[i] * a.score_stride + col] = sc[i];
+          if (a.block_max) {
+            const float mx = group_max(sc[i], 1 << a.block_shift);
+            if (half == 0 && (r & ((1 << a.block_shift) - 1)) == 0 && col < a.n_cols)
+              a.block_max[(int64_t)tq[i] * a.block_max_stride + (col >> a.block_shift)] = mx;
+          }
+        }
+      }
+      if (more) store_block(buf ^ 1);
+      __syncthreads();
     }
   }
 }
@@ -237,6 +430,15 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(IndexScoreArgs a)
 }
 
 hipError_t launch_index_scores_fp8(const IndexScoreArgs& a, hipStream_t s) {
+  if (!a.cand && a.Q >= PF_MIN_Q) {
+    // many queries: the query-tiled kernel shares every staged key block
+    dim3 grid((a.n_cols + PF_KB * PF_BLOCKS - 1) / (PF_KB * PF_BLOCKS), (a.Q + PF_Q - 1) / PF_Q);
+    if (a.w_bf16)
+      hipLaunchKernelGGL((index_scores_prefill_kernel<true>), grid, dim3(64 * PF_WAVES), 0, s, a);
+    else
+      hipLaunchKernelGGL((index_scores_prefill_kernel<false>), grid, dim3(64 * PF_WAVES), 0, s, a);
+    return hipGetLastError();
+  }
   dim3 grid((a.n_cols + IS_KEYS_PER_WG - 1) / IS_KEYS_PER_WG, a.Q);
   if (a.cand) {
     if (a.w_bf16)

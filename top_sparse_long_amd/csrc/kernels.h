@@ -34,6 +34,10 @@ struct IndexScoreArgs {
   int H;
 };
 
+// Dense FP8 calls with at least this many queries use the query-tiled
+// (prefill) kernel; smaller batches score each query on its own.
+constexpr int PF_MIN_Q = 256;
+
 hipError_t launch_index_scores_fp8(const IndexScoreArgs& a, hipStream_t s);
 hipError_t launch_index_scores_f32(const IndexScoreArgs& a, hipStream_t s);
 

@@ -51,6 +51,9 @@ def _parse():
                     help="no GPU: turn rocprofv3 CSV output of this benchmark (a --kernel-trace "
                          "--stats run, a --pmc FETCH_SIZE run and a --pmc WRITE_SIZE run) into the "
                          "text summaries and per-stage traffic records kept under profiles/")
+    ap.add_argument("--summarize-mfma", nargs=3, metavar=("MFMA_DIR", "TRACE_DIR", "OUT_DIR"),
+                    help="no GPU: summarize a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
+                         "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU run of this benchmark")
     ap.add_argument("--profile-command", default="",
                     help="the benchmark command the profiles were taken on (recorded in the summaries)")
     return ap.parse_args()
@@ -104,7 +107,8 @@ def _traffic(stage, workload, launches_bytes):
 
 # kernels of each stage, as they appear in the profiler's kernel names
 STAGE_KERNELS = {
-    "index_scores_dense": ("index_scores_fp8_kernel<false", "index_scores_f32_kernel"),
+    "index_scores_dense": ("index_scores_fp8_kernel<false", "index_scores_prefill_kernel",
+                           "index_scores_f32_kernel"),
     "index_scores_pool": ("index_scores_fp8_kernel<true",),
     "block_candidates": ("select_kernel<2,",),
     "topk_dense": ("select_kernel<0,", "select_kernel<3,"),
@@ -190,6 +194,45 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, workload, comma
             f.write("\n")
 
 
+F16_PEAK_TFLOPS = 2500.0
+N_SIMD = 256 * 4
+
+
+def summarize_mfma(mfma_dir, trace_dir, out_dir, workload, command):
+    """Write mfma_<workload>.txt: per csa2 kernel, MFMA busy share of the
+    SIMD cycles while it ran and the f16 MFMA FLOP rate it reached."""
+    import csv
+    os.makedirs(out_dir, exist_ok=True)
+    per = {}
+    for row in csv.DictReader(open(_find_csv(mfma_dir, "counter_collection.csv"))):
+        if "csa2::" not in row["Kernel_Name"]:
+            continue
+        d = per.setdefault(row["Kernel_Name"], {})
+        d.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    avg_us = {}
+    for row in csv.DictReader(open(_find_csv(trace_dir, "kernel_stats.csv"))):
+        avg_us[row["Name"]] = float(row["AverageNs"]) / 1e3
+    lines = [f"# rocprofv3 MFMA counters, workload {workload}",
+             f"# command: rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_F16 "
+             f"SQ_INSTS_VALU --output-format csv -d <dir> -- {command}",
+             "# busy% = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs * 1024 SIMDs);",
+             "# TFLOP/s = 512 * SQ_INSTS_VALU_MFMA_MOPS_F16 / average duration from the kernel trace;",
+             f"# frac = TFLOP/s / {F16_PEAK_TFLOPS:.0f} (dense f16 MFMA peak)",
+             "# columns: dispatches, busy%, f16 TFLOP/s, frac of f16 peak, VALU insts per dispatch, kernel", ""]
+    for name, d in sorted(per.items()):
+        mean = {k: sum(v) / len(v) for k, v in d.items()}
+        gui = mean.get("GRBM_GUI_ACTIVE", 0.0)
+        busy = mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0)
+        util = 100.0 * busy / (gui / 8.0 * N_SIMD) if gui else 0.0
+        flops = 512.0 * mean.get("SQ_INSTS_VALU_MFMA_MOPS_F16", 0.0)
+        us = avg_us.get(name)
+        tf = flops / (us * 1e-6) / 1e12 if us else 0.0
+        lines.append(f"{len(d.get('GRBM_GUI_ACTIVE', [])):6d} {util:7.1f} {tf:9.1f} {tf / F16_PEAK_TFLOPS:7.3f} "
+                     f"{mean.get('SQ_INSTS_VALU', 0.0):14.0f}  {name}")
+    with open(os.path.join(out_dir, f"mfma_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def cpu_baseline(wl, n_sample):
     """Time the oracle on the first n_sample queries of the workload's whole
     path (both layers), on the host cores."""
@@ -262,6 +305,9 @@ def main():
     args = _parse()
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, args.workload, args.profile_command)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma, args.workload, args.profile_command)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "

@@ -45,6 +45,10 @@ def _parse():
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="queries of the CPU-oracle sample (default: all queries, max 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--overlap-blocks", action="store_true",
+                    help="capture block-candidate selection on a second stream beside the Full "
+                         "layer's top-k and attention (HIP graphs on this ROCm replay the "
+                         "branches one after the other, so this measured no gain)")
     ap.add_argument("--stage-reps", type=int, default=10,
                     help="repetitions per input copy when timing single stages")
     ap.add_argument("--summarize-profiles", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT_DIR"),
@@ -347,7 +351,7 @@ def main():
                 f()
         return g
 
-    step_graphs = [capture([f for _, f in r.steps()]) for r in runs]
+    step_graphs = [capture([f for _, f in r.steps(concurrent=args.overlap_blocks)]) for r in runs]
     for i in range(args.warmup):
         step_graphs[i % len(step_graphs)].replay()
     torch.cuda.synchronize()
@@ -429,7 +433,7 @@ def main():
         "config": {"workload": args.workload, "batch": wl.Q, "ctx_entries": wl.max_cols(),
                    "ratio": wl.ratio, "layers": [l.mode for l in wl.layers],
                    "topk": wl.topk, "pool_blocks": wl.n_blocks, "block_size": wl.block_size,
-                   "input_copies": len(runs)},
+                   "input_copies": len(runs), "block_candidates_overlapped": bool(args.overlap_blocks)},
         "sparse_attn_queries_per_s": n_attn / (ms_per_step * 1e-3),
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -421,10 +421,12 @@ def test_fused_block_max_sizes(bs, many):
         assert np.all(bm[t, len(ref):] == -np.inf), t
 
 
-def test_graph_replay_matches_eager():
-    """A captured pass replays to the eager result, several times, with eager
-    work and synchronisations between the replays."""
-    _announce("graph replay")
+@pytest.mark.parametrize("concurrent", [False, True])
+def test_graph_replay_matches_eager(concurrent):
+    """A captured pass (optionally with block candidates on a second stream)
+    replays to the serial eager result, several times, with eager work and
+    synchronisations between the replays."""
+    _announce(f"graph replay concurrent={concurrent}")
     wl = synth.mini_workload(43, [70000, 20000], q_per_seq=2, modes=("full", "reuse", "reindex")).to(DEV)
     run = LayerRunner(wl)
     run.run()
@@ -433,11 +435,11 @@ def test_graph_replay_matches_eager():
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        run.run()
+        run.run(concurrent=concurrent)
     torch.cuda.current_stream().wait_stream(side)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _, fn in run.steps():
+        for _, fn in run.steps(concurrent=concurrent):
             fn()
     for rep in range(4):
         for o in run.out:

@@ -85,6 +85,12 @@ class LayerRunner:
                  csa2_topk_workspace_size(Q, self.pool_cols, wl.topk),
                  csa2_block_candidates_workspace_size(Q, self.n_cols, wl.block_size, wl.n_blocks))
         self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=device)
+        # block candidates may run beside the Full layer's top-k on a second
+        # stream, so they get a workspace of their own
+        ws_b = csa2_block_candidates_workspace_size(Q, self.n_cols, wl.block_size, wl.n_blocks)
+        self.ws_blocks = torch.empty((max(ws_b, 16),), dtype=torch.uint8, device=device)
+        self._side = None
+        self._joined = None
         odt = torch.bfloat16 if self.quant else f32
         self.out = [torch.empty((Q, 64, 512), dtype=odt, device=device) for _ in wl.layers]
         self.lse = [torch.empty((Q, 64), dtype=f32, device=device) for _ in wl.layers]
@@ -108,7 +114,7 @@ class LayerRunner:
     def block_candidates(self, from_block_max=False):
         wl = self.wl
         csa2_block_candidates(self.scores, self.n_cols, wl.q_pos, wl.ratio, wl.block_size,
-                              wl.n_blocks, self.cand, self.ws, self.Q,
+                              wl.n_blocks, self.cand, self.ws_blocks, self.Q,
                               block_max=self.block_max if from_block_max else None)
         self.slots.candidates = self.cand
 
@@ -131,9 +137,16 @@ class LayerRunner:
                          self.out[li], qdt if self.quant else CSA2_F32, self.lse[li], self.Q)
 
     # -- a whole pass ----------------------------------------------------------
-    def steps(self):
+    def steps(self, concurrent=False):
         """The calls of one pass over every layer, in order, as (stage name,
-        callable) pairs."""
+        callable) pairs.
+
+        concurrent=True runs the block-candidate selection on a second stream:
+        it needs only the Full layer's scores, so it overlaps that layer's
+        top-k and attention (and any Reuse layers after it); the pool scoring
+        of the Reindex layer waits for it.  Each callable launches on the
+        stream current when it is called, so the pass can be captured into
+        one graph."""
         out = []
 
         def reset():
@@ -147,24 +160,51 @@ class LayerRunner:
                 out.append(("index_scores_dense",
                             lambda li=li, fuse=fuse: self.index_scores(li, pool=False, block_max=fuse)))
                 if self.needs_pool[li]:
-                    out.append(("block_candidates",
-                                lambda fuse=fuse: self.block_candidates(from_block_max=fuse)))
+                    if concurrent:
+                        out.append(("block_candidates",
+                                    lambda fuse=fuse: self._fork_block_candidates(fuse)))
+                    else:
+                        out.append(("block_candidates",
+                                    lambda fuse=fuse: self.block_candidates(from_block_max=fuse)))
                     has_pool = True
                 out.append(("topk_dense", lambda li=li: self.topk(li, pool=False)))
             elif lay.mode == "reindex":
                 pool = has_pool
-                out.append(("index_scores_pool" if pool else "index_scores_dense",
-                            lambda li=li, pool=pool: self.index_scores(li, pool=pool)))
+                if pool and concurrent:
+                    out.append(("index_scores_pool",
+                                lambda li=li: (self._join(), self.index_scores(li, pool=True))))
+                else:
+                    out.append(("index_scores_pool" if pool else "index_scores_dense",
+                                lambda li=li, pool=pool: self.index_scores(li, pool=pool)))
                 out.append(("topk_pool" if pool else "topk_dense",
                             lambda li=li, pool=pool: self.topk(li, pool=pool)))
             out.append(("sparse_attn", lambda li=li: self.attention(li)))
+        if concurrent:
+            out.append(("join", self._join))
         return out
 
-    def run(self, mark=None):
+    def _fork_block_candidates(self, fuse):
+        main = torch.cuda.current_stream()
+        if self._side is None:
+            self._side = torch.cuda.Stream(device=main.device)   # default priority
+        fork = torch.cuda.Event()
+        fork.record(main)
+        self._side.wait_event(fork)
+        with torch.cuda.stream(self._side):
+            self.block_candidates(from_block_max=fuse)
+        self._joined = torch.cuda.Event()
+        self._joined.record(self._side)
+
+    def _join(self):
+        if self._joined is not None:
+            torch.cuda.current_stream().wait_event(self._joined)
+            self._joined = None
+
+    def run(self, mark=None, concurrent=False):
         """Run every layer once.  mark(name) is called before each step and
         once at the end with None (the benchmark records events there)."""
-        for name, fn in self.steps():
-            if name != "reset" and mark:
+        for name, fn in self.steps(concurrent):
+            if name not in ("reset", "join") and mark:
                 mark(name)
             fn()
         if mark:

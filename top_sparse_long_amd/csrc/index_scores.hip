@@ -32,6 +32,8 @@
 // "blocks are not compression"), taken over the scores in registers.
 #include "kernels.h"
 
+#include <algorithm>
+
 namespace csa2 {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
@@ -43,11 +45,15 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 #define CSA2_IS_WAVES 4
 #endif
 #ifndef CSA2_IS_TILES
-#define CSA2_IS_TILES 4
+#define CSA2_IS_TILES 2
 #endif
 constexpr int IS_WAVES = CSA2_IS_WAVES;                      // waves per workgroup
-constexpr int IS_TILES = CSA2_IS_TILES;                      // 32-key tiles per wave
-constexpr int IS_KEYS_PER_WG = IS_WAVES * 32 * IS_TILES;      // 512
+constexpr int IS_TILES = CSA2_IS_TILES;                      // 32-key tiles per wave per sub-chunk
+constexpr int IS_SUB = IS_WAVES * 32 * IS_TILES;             // columns per sub-chunk (256)
+#ifndef CSA2_IS_RESIDENT
+#define CSA2_IS_RESIDENT 768
+#endif
+constexpr int IS_RESIDENT_WGS = CSA2_IS_RESIDENT;            // about one round on 256 CUs
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
@@ -123,14 +129,15 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
 
   const int nvis = visible_count(a.q_pos[t], a.ratio);
   const int64_t base = a.seq_base[a.q_seq[t]];
-  const int col0 = blockIdx.x * IS_KEYS_PER_WG;
+  const int col_begin = blockIdx.x * a.sub_per_wg * IS_SUB;
+  const int col_end = min(a.n_cols, col_begin + a.sub_per_wg * IS_SUB);
   float* out = a.scores + (int64_t)t * a.score_stride;
   // Dense mode: columns past the visible prefix only need -inf.
   const int limit = (nvis <= 0) ? 0 : (POOL ? a.n_cols : min(a.n_cols, nvis));
 
   // q (head r, bytes [64 half, +64)) and the gate of head r are loaded
-  // first and used after the key loads are issued, so one round trip covers
-  // all of them.
+  // first and used after the first key loads are issued, so one round trip
+  // covers all of them.
   v4u qraw[4];
   {
     const v4u* qsrc = (const v4u*)(a.q + (int64_t)(t * 32 + r) * a.q_row_stride + 64 * half);
@@ -146,7 +153,7 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
 
   if (limit == 0) {
     // nothing visible: every column of this workgroup is -inf
-    for (int c = col0 + threadIdx.x; c < min(a.n_cols, col0 + IS_KEYS_PER_WG); c += 64 * IS_WAVES) {
+    for (int c = col_begin + threadIdx.x; c < col_end; c += 64 * IS_WAVES) {
       out[c] = -INFINITY;
       if (!POOL && a.block_max && (c & ((1 << a.block_shift) - 1)) == 0)
         a.block_max[(int64_t)t * a.block_max_stride + (c >> a.block_shift)] = -INFINITY;
@@ -154,23 +161,30 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
     return;
   }
 
-  // This wave's tiles: columns col0 + (i * IS_WAVES + wave) * 32 + [0, 32).
-  // Every load is unconditional: lanes whose column scores nothing read
-  // position 0 of the sequence (visible, since limit > 0) and are masked
-  // afterwards, so all tiles' loads are in flight together.
-  v4u raw[IS_TILES][4];
-  float ks[IS_TILES];
-  int pos[IS_TILES];
+  // One sub-chunk = IS_SUB columns; this wave's tiles in it are columns
+  // sc0 + (i * IS_WAVES + wave) * 32 + [0, 32).  Every load is
+  // unconditional: lanes whose column scores nothing read position 0 of the
+  // sequence (visible, since limit > 0) and are masked afterwards.
+  struct Sub {
+    v4u raw[IS_TILES][4];
+    float ks[IS_TILES];
+    int pos[IS_TILES];
+  };
+  auto load_sub = [&](int sc0, Sub& S) {
 #pragma unroll
-  for (int i = 0; i < IS_TILES; ++i) {
-    const int tcol = col0 + (i * IS_WAVES + wave) * 32;
-    pos[i] = (tcol < limit) ? column_position<POOL>(a, t, tcol + r, nvis) : -1;
-    const int64_t row = base + max(pos[i], 0);
-    const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 64 * half);
+    for (int i = 0; i < IS_TILES; ++i) {
+      const int tcol = sc0 + (i * IS_WAVES + wave) * 32;
+      S.pos[i] = (tcol < limit) ? column_position<POOL>(a, t, tcol + r, nvis) : -1;
+      const int64_t row = base + max(S.pos[i], 0);
+      const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 64 * half);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) raw[i][j] = src[j];
-    ks[i] = a.k_scale[row * a.k_scale_stride];
-  }
+      for (int j = 0; j < 4; ++j) S.raw[i][j] = src[j];
+      S.ks[i] = a.k_scale[row * a.k_scale_stride];
+    }
+  };
+
+  Sub A, B;
+  if (col_begin < col_end) load_sub(col_begin, A);
 
   // A operand widened to f16; gate of head r with the q scale folded in,
   // then the 16 heads this lane's accumulators hold.
@@ -185,34 +199,48 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
 #pragma unroll
   for (int j = 0; j < 16; ++j) gate[j] = __shfl(g_r, 8 * (j >> 2) + 4 * half + (j & 3));
 
+  auto compute_sub = [&](int sc0, const Sub& S) {
 #pragma unroll
-  for (int i = 0; i < IS_TILES; ++i) {
-    const int tcol = col0 + (i * IS_WAVES + wave) * 32;
-    if (tcol >= a.n_cols) break;
-    const int col = tcol + r;
-    float sc = -INFINITY;
-    if (tcol < limit) {
-      v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < IS_TILES; ++i) {
+      const int tcol = sc0 + (i * IS_WAVES + wave) * 32;
+      if (tcol >= col_end) break;
+      const int col = tcol + r;
+      float sc = -INFINITY;
+      if (tcol < limit) {
+        v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const v8h b0 = fp8x8_to_f16(raw[i][j][0], raw[i][j][1]);
-        const v8h b1 = fp8x8_to_f16(raw[i][j][2], raw[i][j][3]);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[2 * j], b0, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[2 * j + 1], b1, acc, 0, 0, 0);
+        for (int j = 0; j < 4; ++j) {
+          const v8h b0 = fp8x8_to_f16(S.raw[i][j][0], S.raw[i][j][1]);
+          const v8h b1 = fp8x8_to_f16(S.raw[i][j][2], S.raw[i][j][3]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[2 * j], b0, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[2 * j + 1], b1, acc, 0, 0, 0);
+        }
+        float v = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v = fmaf(gate[j], relu(acc[j]), v);
+        v = add_half_swap(v);
+        sc = (S.pos[i] >= 0) ? v * S.ks[i] : -INFINITY;
       }
-      float v = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) v = fmaf(gate[j], relu(acc[j]), v);
-      v = add_half_swap(v);
-      sc = (pos[i] >= 0) ? v * ks[i] : -INFINITY;
+      if (half == 0 && col < a.n_cols) out[col] = sc;
+      if (!POOL && a.block_max) {
+        // maximum over aligned groups of block_size lanes (block_size <= 32)
+        const float m = group_max(sc, 1 << a.block_shift);
+        if (half == 0 && (r & ((1 << a.block_shift) - 1)) == 0 && col < a.n_cols)
+          a.block_max[(int64_t)t * a.block_max_stride + (col >> a.block_shift)] = m;
+      }
     }
-    if (half == 0 && col < a.n_cols) out[col] = sc;
-    if (!POOL && a.block_max) {
-      // maximum over aligned groups of block_size lanes (block_size <= 32)
-      const float m = group_max(sc, 1 << a.block_shift);
-      if (half == 0 && (r & ((1 << a.block_shift) - 1)) == 0 && col < a.n_cols)
-        a.block_max[(int64_t)t * a.block_max_stride + (col >> a.block_shift)] = m;
-    }
+  };
+
+  // Stream over this workgroup's sub-chunks, double-buffered: the next
+  // sub-chunk's rows are in flight while the current one is contracted, so
+  // HBM stays busy for the whole life of the workgroup.
+  for (int c0 = col_begin; c0 < col_end; c0 += 2 * IS_SUB) {
+    const int c1 = c0 + IS_SUB;
+    if (c1 < col_end) load_sub(c1, B);
+    compute_sub(c0, A);
+    if (c1 >= col_end) break;
+    if (c1 + IS_SUB < col_end) load_sub(c1 + IS_SUB, A);
+    compute_sub(c1, B);
   }
 }
 
@@ -439,17 +467,22 @@ hipError_t launch_index_scores_fp8(const IndexScoreArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((index_scores_prefill_kernel<false>), grid, dim3(64 * PF_WAVES), 0, s, a);
     return hipGetLastError();
   }
-  dim3 grid((a.n_cols + IS_KEYS_PER_WG - 1) / IS_KEYS_PER_WG, a.Q);
+  // sub-chunks per workgroup: enough workgroups for about one resident
+  // round, each streaming over a contiguous column range of one query
+  IndexScoreArgs b = a;
+  const int64_t subs = (a.n_cols + IS_SUB - 1) / IS_SUB;
+  b.sub_per_wg = (int)std::max<int64_t>(1, (subs * a.Q + IS_RESIDENT_WGS - 1) / IS_RESIDENT_WGS);
+  dim3 grid((unsigned)((subs + b.sub_per_wg - 1) / b.sub_per_wg), a.Q);
   if (a.cand) {
     if (a.w_bf16)
-      hipLaunchKernelGGL((index_scores_fp8_kernel<true, true>), grid, dim3(64 * IS_WAVES), 0, s, a);
+      hipLaunchKernelGGL((index_scores_fp8_kernel<true, true>), grid, dim3(64 * IS_WAVES), 0, s, b);
     else
-      hipLaunchKernelGGL((index_scores_fp8_kernel<true, false>), grid, dim3(64 * IS_WAVES), 0, s, a);
+      hipLaunchKernelGGL((index_scores_fp8_kernel<true, false>), grid, dim3(64 * IS_WAVES), 0, s, b);
   } else {
     if (a.w_bf16)
-      hipLaunchKernelGGL((index_scores_fp8_kernel<false, true>), grid, dim3(64 * IS_WAVES), 0, s, a);
+      hipLaunchKernelGGL((index_scores_fp8_kernel<false, true>), grid, dim3(64 * IS_WAVES), 0, s, b);
     else
-      hipLaunchKernelGGL((index_scores_fp8_kernel<false, false>), grid, dim3(64 * IS_WAVES), 0, s, a);
+      hipLaunchKernelGGL((index_scores_fp8_kernel<false, false>), grid, dim3(64 * IS_WAVES), 0, s, b);
   }
   return hipGetLastError();
 }

@@ -213,6 +213,13 @@ size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k);
  *   attn_sink [H] fp32.
  *   out       [Q, H, D] output, out_dtype BF16 or F32.
  *   lse       NULL or [Q, H] fp32 output.
+ *   workspace NULL, or device memory of workspace_bytes bytes the call may
+ *             use (contents need not be initialised and are undefined
+ *             afterwards).  With at least csa2_sparse_attn_workspace_size(Q,
+ *             H, k, window) bytes, small batches split each query's keys
+ *             over several workgroups and combine their partial softmax
+ *             sums in a second kernel; results are the same up to rounding
+ *             order.  With less, each (query, 16 heads) is one workgroup.
  *   Supported: D = 512; H a multiple of 16 up to 128; k <= 2048.
  *   Quantized path: q BF16, main FP4_E2M1, swa FP8_E4M3, out BF16 or F32.
  *   Float path: q, main, swa F32, out F32.
@@ -223,8 +230,13 @@ int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv
                      const int32_t* swa_pos0, const int32_t* swa_lo, int32_t window,
                      const int32_t* q_seq, const int32_t* q_pos, int32_t ratio,
                      const float* attn_sink, float softmax_scale, void* out,
-                     csa2_dtype out_dtype, float* lse, int32_t Q, int32_t H, int32_t D,
-                     void* stream);
+                     csa2_dtype out_dtype, float* lse, void* workspace,
+                     size_t workspace_bytes, int32_t Q, int32_t H, int32_t D, void* stream);
+
+/* Workspace bytes csa2_sparse_attn uses to split keys for Q queries of H
+ * heads with k indices and an SWA window of `window` (0 when it would not
+ * split). */
+size_t csa2_sparse_attn_workspace_size(int32_t Q, int32_t H, int32_t k, int32_t window);
 
 /* Name of a status code (static string). */
 const char* csa2_status_string(int status);

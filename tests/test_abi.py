@@ -134,14 +134,14 @@ def _attn(lib, **kw):
              main_base=FAKE, idx=FAKE, k=512,
              swa=tsl.csa2_rows(FAKE, FAKE + 512, 528, 132, tsl.CSA2_FP8_E4M3),
              swa_base=FAKE, swa_pos0=FAKE, swa_lo=None, window=128, q_seq=FAKE, q_pos=FAKE,
-             ratio=1, sink=FAKE, scale=0.044, out=FAKE, odt=tsl.CSA2_BF16, lse=None, Q=1, H=64,
-             D=512)
+             ratio=1, sink=FAKE, scale=0.044, out=FAKE, odt=tsl.CSA2_BF16, lse=None, ws=None,
+             wsb=0, Q=1, H=64, D=512)
     a.update(kw)
     return lib.csa2_sparse_attn(a["q"], a["qdt"], ctypes.byref(a["main"]), a["main_base"],
                                 a["idx"], a["k"], ctypes.byref(a["swa"]), a["swa_base"],
                                 a["swa_pos0"], a["swa_lo"], a["window"], a["q_seq"], a["q_pos"],
                                 a["ratio"], a["sink"], ctypes.c_float(a["scale"]), a["out"],
-                                a["odt"], a["lse"], a["Q"], a["H"], a["D"], None)
+                                a["odt"], a["lse"], a["ws"], a["wsb"], a["Q"], a["H"], a["D"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -157,11 +157,24 @@ def _attn(lib, **kw):
     (dict(main=tsl.csa2_rows(FAKE, FAKE + 4, 320, 80, tsl.CSA2_FP4_E2M1)), tsl.CSA2_ERR_INVALID_ARG),
     (dict(main=tsl.csa2_rows(FAKE, None, 320, 80, tsl.CSA2_FP4_E2M1)), tsl.CSA2_ERR_INVALID_ARG),
     (dict(ratio=4), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(ws=FAKE + 4, wsb=1 << 30), tsl.CSA2_ERR_INVALID_ARG),
 ])
 def test_sparse_attn_rejects(kw, status):
     lib = tsl.load()
     assert _attn(lib, **kw) == status
     assert lib.csa2_last_error().decode().startswith("csa2_sparse_attn")
+
+
+def test_attention_workspace_sizes():
+    lib = tsl.load()
+    one = 16 + 16 + 16 * 512
+    # a small batch splits its 20 tiles five ways
+    assert lib.csa2_sparse_attn_workspace_size(8, 64, 512, 128) == 8 * 4 * 5 * one * 4
+    # a large batch fills the chip without splitting
+    assert lib.csa2_sparse_attn_workspace_size(64, 64, 512, 128) == 0
+    assert lib.csa2_sparse_attn_workspace_size(0, 64, 512, 128) == 0
+    # a tiny key set needs no split either
+    assert lib.csa2_sparse_attn_workspace_size(1, 16, 16, 0) == 0
 
 
 def test_zero_queries_is_a_no_op_after_checks():

@@ -225,8 +225,12 @@ def test_block_candidates_exact(n_cols, n_blocks):
 # ---------------------------------------------------------------------------
 # attention: the oracle runs on the same indices
 
-def _attn_case(wl, idx_np, layer=0, window=None):
+def _attn_case(wl, idx_np, layer=0, window=None, split=True):
     run = LayerRunner(wl)
+    if not split:
+        run.ws_attn = None      # one workgroup per (query, 16 heads)
+    else:
+        assert run.ws_attn is not None
     run.slots.topk_idxs = torch.from_numpy(idx_np.astype(np.int32)).to(DEV)
     if window is not None:
         wl.window = window
@@ -251,9 +255,10 @@ def _random_idx(rng, nvis, k, frac_valid=1.0):
     return idx
 
 
+@pytest.mark.parametrize("split", [True, False])
 @pytest.mark.parametrize("ratio", [1, 2])
-def test_sparse_attn_quant(ratio):
-    _announce(f"sparse_attn quantized ratio={ratio}")
+def test_sparse_attn_quant(ratio, split):
+    _announce(f"sparse_attn quantized ratio={ratio} split={split}")
     wl = synth.mini_workload(20 + ratio, [3000, 700, 200], ratio=ratio,
                              positions=[[3000 * ratio - 1, 1500], [700 * ratio - 1], [5, 0]]).to(DEV)
     rng = np.random.default_rng(ratio)
@@ -261,7 +266,7 @@ def test_sparse_attn_quant(ratio):
     idx = _random_idx(rng, nvis, 512, 0.9)
     idx[0, 5] = -1            # holes inside the table
     idx = np.where(idx >= 0, idx, -1)
-    gpu, gl, ref, rl = _attn_case(wl, idx)
+    gpu, gl, ref, rl = _attn_case(wl, idx, split=split)
     check_attention(gpu, ref)
     assert np.abs(gl - rl).max() <= 1e-3
 

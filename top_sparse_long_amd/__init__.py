@@ -18,6 +18,7 @@ CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1 = 0, 1, 2, 3
 
 EXPORTED = ("csa2_index_scores", "csa2_block_candidates", "csa2_block_candidates_workspace_size",
             "csa2_topk", "csa2_topk_workspace_size", "csa2_sparse_attn",
+            "csa2_sparse_attn_workspace_size",
             "csa2_status_string", "csa2_last_error", "csa2_version")
 
 
@@ -55,7 +56,9 @@ def load():
     lib.csa2_topk_workspace_size.argtypes = [I32, I32, I32]
     lib.csa2_topk_workspace_size.restype = SZ
     lib.csa2_sparse_attn.argtypes = [P, ctypes.c_int, RP, P, P, I32, RP, P, P, P, I32, P, P, I32,
-                                     P, ctypes.c_float, P, ctypes.c_int, P, I32, I32, I32, P]
+                                     P, ctypes.c_float, P, ctypes.c_int, P, P, SZ, I32, I32, I32, P]
+    lib.csa2_sparse_attn_workspace_size.argtypes = [I32, I32, I32, I32]
+    lib.csa2_sparse_attn_workspace_size.restype = SZ
     lib.csa2_status_string.argtypes = [ctypes.c_int]
     lib.csa2_status_string.restype = ctypes.c_char_p
     lib.csa2_last_error.restype = ctypes.c_char_p
@@ -154,12 +157,18 @@ def csa2_topk(scores, n_cols, q_pos, ratio, k, idx, workspace, Q, cand=None, blo
                          ncb, block_size, k, _ptr(idx), _ptr(workspace), wsb, Q, _stream(stream)))
 
 
+def csa2_sparse_attn_workspace_size(Q, H, k, window):
+    return load().csa2_sparse_attn_workspace_size(Q, H, k, window)
+
+
 def csa2_sparse_attn(q, q_dtype, main_rows, main_base, idx, k, swa_rows, swa_base, swa_pos0,
                      swa_lo, window, q_seq, q_pos, ratio, attn_sink, softmax_scale, out,
-                     out_dtype, lse, Q, H=64, D=512, stream=None):
+                     out_dtype, lse, Q, H=64, D=512, stream=None, workspace=None):
     lib = load()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.csa2_sparse_attn(_ptr(q), q_dtype, ctypes.byref(main_rows), _ptr(main_base),
                                 _ptr(idx), k, ctypes.byref(swa_rows), _ptr(swa_base),
                                 _ptr(swa_pos0), _ptr(swa_lo), window, _ptr(q_seq), _ptr(q_pos),
                                 ratio, _ptr(attn_sink), ctypes.c_float(softmax_scale), _ptr(out),
-                                out_dtype, _ptr(lse), Q, H, D, _stream(stream)))
+                                out_dtype, _ptr(lse), _ptr(workspace), wsb, Q, H, D,
+                                _stream(stream)))

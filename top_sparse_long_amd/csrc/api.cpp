@@ -262,7 +262,8 @@ int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv
                      const int32_t* swa_lo, int32_t window, const int32_t* q_seq,
                      const int32_t* q_pos, int32_t ratio, const float* attn_sink,
                      float softmax_scale, void* out, csa2_dtype out_dtype, float* lse,
-                     int32_t Q, int32_t H, int32_t D, void* stream) {
+                     void* workspace, size_t workspace_bytes, int32_t Q, int32_t H, int32_t D,
+                     void* stream) {
   g_err[0] = 0;
   REQUIRE(q && main_kv && main_base && idx && swa_kv && swa_base && swa_pos0 && q_seq && q_pos &&
               attn_sink && out,
@@ -328,8 +329,25 @@ int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv
     REQUIRE((int64_t)window + k <= 8192, CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn: F32 path needs window + k <= 8192");
   }
   if (Q == 0) return CSA2_OK;
+  a.n_split = 1;
+  a.part = nullptr;
+  if (quant && workspace) {
+    const size_t need = csa2_sparse_attn_workspace_size(Q, H, k, window);
+    if (need > 0 && workspace_bytes >= need) {
+      REQUIRE(aligned(workspace, 16), CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: workspace must be 16-byte aligned");
+      a.n_split = csa2::attn_splits(Q, H, k, window);
+      a.part = (float*)workspace;
+    }
+  }
   if (quant) return hip_status(csa2::launch_sparse_attn_quant(a, (hipStream_t)stream), "csa2_sparse_attn");
   return hip_status(csa2::launch_sparse_attn_f32(a, (hipStream_t)stream), "csa2_sparse_attn");
+}
+
+size_t csa2_sparse_attn_workspace_size(int32_t Q, int32_t H, int32_t k, int32_t window) {
+  if (Q <= 0 || H < 16 || k < 0 || window < 0) return 0;
+  const int ns = csa2::attn_splits(Q, H, k, window);
+  if (ns <= 1) return 0;
+  return (size_t)Q * (size_t)(H / 16) * (size_t)ns * csa2::ATTN_PART_FLOATS * sizeof(float);
 }
 
 }  // extern "C"

@@ -107,7 +107,13 @@ struct AttnArgs {
   float* lse;
   int Q;
   int H;
+  int n_split;               // key splits per (query, head group); 1 = no split
+  float* part;               // [Q][H/16][n_split] partial records when n_split > 1
 };
+
+// Partial record of one split: m[16] (log2 units), l[16], O[16][512], fp32.
+constexpr int ATTN_PART_FLOATS = 16 + 16 + 16 * 512;
+int attn_splits(int Q, int H, int k, int window);
 
 hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s);
 hipError_t launch_sparse_attn_f32(const AttnArgs& a, hipStream_t s);

@@ -106,11 +106,13 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   const int n_hg = a.H / AT_HEADS;
   int bid = blockIdx.x;
   const int nblk = gridDim.x;
-  // consecutive (query, head-group) pairs on one XCD: workgroups are handed
-  // to the 8 XCDs round-robin
+  // consecutive (query, head-group, split) triples on one XCD: workgroups
+  // are handed to the 8 XCDs round-robin
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int t = bid / n_hg;
-  const int hg = bid - t * n_hg;
+  const int split = bid % a.n_split;
+  const int tg = bid / a.n_split;
+  const int t = tg / n_hg;
+  const int hg = tg - t * n_hg;
 
   const int lane = threadIdx.x & 63;
   // wave-uniform, so tile-type branches are scalar branches
@@ -128,7 +130,12 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   const int n_swa = max(0, p - first + 1);
   const int64_t sbase = a.swa_base[b] + (first - sp0);
   const int n_swa_tiles = (n_swa + 31) >> 5;
-  const int n_tiles = n_swa_tiles + ((a.k + 31) >> 5);
+  const int n_tiles_all = n_swa_tiles + ((a.k + 31) >> 5);
+  // this workgroup's tiles: [tile_begin, n_tiles) of the query's tile list
+  // (SWA tiles first); the whole list when keys are not split
+  const int per_split = (n_tiles_all + a.n_split - 1) / a.n_split;
+  const int tile_begin = min(n_tiles_all, split * per_split);
+  const int n_tiles = min(n_tiles_all, tile_begin + per_split);
   const int h_glob0 = hg * AT_HEADS;
   // keys that do not exist are read from this query's own q row (always
   // mapped, 64 KB) and given a zero scale, so every load is unconditional
@@ -188,7 +195,8 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
 
   SwaTile S;
   MainTile M;
-  if (wave < n_swa_tiles) load_swa(wave, S);   // needs no staged index
+  const int ti0 = tile_begin + wave;
+  if (ti0 < n_tiles && ti0 < n_swa_tiles) load_swa(ti0, S);   // needs no staged index
 
   v8h qf[16];
 #pragma unroll
@@ -205,7 +213,7 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
       if ((int)threadIdx.x + 256 * j < a.k) s_idx[threadIdx.x + 256 * j] = iv[j];
   }
   __syncthreads();   // s_idx
-  if (wave >= n_swa_tiles && wave < n_tiles) load_main(wave, M);
+  if (ti0 >= n_swa_tiles && ti0 < n_tiles) load_main(ti0, M);
 
   // O[T]: output columns d = 16 T + r, rows = heads 4 g + j
   v4f O[32];
@@ -336,8 +344,8 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   // tile's rows are requested as soon as the current tile's raw bytes have
   // been dequantized, so they are in flight during the softmax and the
   // LDS-bound P V product.
-  int ti = wave;
-  for (; ti < n_swa_tiles; ti += AT_WAVES) {
+  int ti = ti0;
+  for (; ti < min(n_tiles, n_swa_tiles); ti += AT_WAVES) {
     v4f acc[2];
     uint64_t vmask[2];
     stage_swa(ti, S, acc, vmask);
@@ -374,6 +382,44 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
     for (int u = 0; u < 32; ++u) *(v4f*)(part + (u * 64 + lane) * 16) = O[u];
   }
   __syncthreads();
+  if (a.n_split > 1) {
+    // partial record of this split: per head the maximum over the waves
+    // (log2 units, no sink), the denominator and O scaled onto that maximum
+    float* rec = a.part + ((int64_t)tg * a.n_split + split) * ATTN_PART_FLOATS;
+    float ew[AT_WAVES][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 4 * g + j;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < AT_WAVES; ++w) M = fmaxf(M, s_m[w][h]);
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < AT_WAVES; ++w) {
+        const float mw = s_m[w][h];
+        ew[w][j] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        lsum += s_l[w][h] * ew[w][j];
+      }
+      if (wave == 0 && r == 0) {
+        rec[h] = M;
+        rec[16 + h] = lsum;
+      }
+    }
+#pragma unroll
+    for (int uu = 0; uu < 32 / AT_WAVES; ++uu) {
+      const int u = wave * (32 / AT_WAVES) + uu;
+      v4f v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < AT_WAVES; ++w) {
+        const v4f x = *(const v4f*)(s_tile + w * AT_TILE_BYTES + (u * 64 + lane) * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] += x[j] * ew[w][j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) rec[32 + (4 * g + j) * AT_D + 16 * u + r] = v[j];
+    }
+    return;
+  }
   float fw[AT_WAVES][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -494,9 +540,93 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs a) {
   if (tid == 0 && a.lse) a.lse[(int64_t)t * a.H + h] = M + logf(den);
 }
 
+// Combine the partial records of the key splits of one (query, 16 heads):
+// the common maximum includes the sink, which enters only the denominator.
+// 1024 threads, two 4-column groups each; every load (all splits' partial O
+// and their m, l) is issued before any is used, with split indices clamped
+// to the last split and zero factors past it, so one memory round trip
+// covers the whole combine.
+constexpr int ATTN_MAX_SPLIT = 8;
+
+__global__ __launch_bounds__(1024) void sparse_attn_combine_kernel(AttnArgs a) {
+  const int n_hg = a.H / AT_HEADS;
+  const int tg = blockIdx.x;
+  const int t = tg / n_hg;
+  const int h0 = (tg - t * n_hg) * AT_HEADS;
+  const float* rec0 = a.part + (int64_t)tg * a.n_split * ATTN_PART_FLOATS;
+  const int last = a.n_split - 1;
+  float4 x[2][ATTN_MAX_SPLIT];
+  float ms[2][ATTN_MAX_SPLIT], ls[2][ATTN_MAX_SPLIT];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = threadIdx.x * 4 + i * 4096;
+    const int h = e / AT_D;
+#pragma unroll
+    for (int sp = 0; sp < ATTN_MAX_SPLIT; ++sp) {
+      const float* rec = rec0 + min(sp, last) * ATTN_PART_FLOATS;
+      x[i][sp] = *(const float4*)(rec + 32 + e);
+      ms[i][sp] = rec[h];
+      ls[i][sp] = rec[16 + h];
+    }
+  }
+  const int64_t obase = ((int64_t)t * a.H + h0) * AT_D;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = threadIdx.x * 4 + i * 4096;
+    const int h = e / AT_D;
+    const float sink2 = a.sink[h0 + h] * LOG2E;
+    float M = sink2;
+#pragma unroll
+    for (int sp = 0; sp < ATTN_MAX_SPLIT; ++sp)
+      if (sp <= last) M = fmaxf(M, ms[i][sp]);
+    float den = (M == -INFINITY) ? 0.f : exp2f(sink2 - M);
+    float f[ATTN_MAX_SPLIT];
+#pragma unroll
+    for (int sp = 0; sp < ATTN_MAX_SPLIT; ++sp) {
+      f[sp] = (sp > last || ms[i][sp] == -INFINITY) ? 0.f : exp2f(ms[i][sp] - M);
+      den += ls[i][sp] * f[sp];
+    }
+    const float inv = (den > 0.f) ? 1.f / den : 0.f;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int sp = 0; sp < ATTN_MAX_SPLIT; ++sp) {
+      const float fs = f[sp] * inv;
+      v.x += x[i][sp].x * fs;
+      v.y += x[i][sp].y * fs;
+      v.z += x[i][sp].z * fs;
+      v.w += x[i][sp].w * fs;
+    }
+    if (a.lse && (e % AT_D) == 0) a.lse[(int64_t)t * a.H + h0 + h] = (M + log2f(den)) * LN2;
+    if (a.out_bf16) {
+      uint2 pk;
+      pk.x = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);
+      pk.y = (uint32_t)f32_to_bf16_rne(v.z) | ((uint32_t)f32_to_bf16_rne(v.w) << 16);
+      *(uint2*)((uint16_t*)a.out + obase + e) = pk;
+    } else {
+      *(float4*)((float*)a.out + obase + e) = v;
+    }
+  }
+}
+
+// Key splits per (query, 16 heads): only when the batch leaves most of the
+// chip idle; about four 32-key tiles per split (one per wave), at most 8.
+int attn_splits(int Q, int H, int k, int window) {
+  const int groups = Q * (H / AT_HEADS);
+  if (groups <= 0 || groups >= 128) return 1;
+  const int tiles = (window + 31) / 32 + (k + 31) / 32;
+  int ns = (tiles + AT_WAVES - 1) / AT_WAVES;
+  ns = min(ns, max(1, 256 / groups));
+  return max(1, min(ns, ATTN_MAX_SPLIT));
+}
+
 hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s) {
-  const int nblk = a.Q * (a.H / AT_HEADS);
-  hipLaunchKernelGGL(sparse_attn_quant_kernel, dim3(nblk), dim3(256), 0, s, a);
+  const int groups = a.Q * (a.H / AT_HEADS);
+  hipLaunchKernelGGL(sparse_attn_quant_kernel, dim3(groups * a.n_split), dim3(256), 0, s, a);
+  if (a.n_split > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3(groups), dim3(1024), 0, s, a);
+  }
   return hipGetLastError();
 }
 

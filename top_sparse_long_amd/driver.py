@@ -22,6 +22,7 @@ import torch
 
 from . import (csa2_index_scores, csa2_block_candidates, csa2_topk, csa2_sparse_attn,
                csa2_block_candidates_workspace_size, csa2_topk_workspace_size,
+               csa2_sparse_attn_workspace_size,
                rows_f32, rows_fp8, rows_fp4_records, rows_swa_records,
                CSA2_F32, CSA2_BF16)
 
@@ -91,6 +92,10 @@ class LayerRunner:
         self.ws_blocks = torch.empty((max(ws_b, 16),), dtype=torch.uint8, device=device)
         self._side = None
         self._joined = None
+        # attention splits keys over several workgroups at small batch sizes
+        ws_a = csa2_sparse_attn_workspace_size(Q, 64, wl.topk, wl.window)
+        self.ws_attn = (torch.empty((ws_a,), dtype=torch.uint8, device=device)
+                        if ws_a > 0 else None)
         odt = torch.bfloat16 if self.quant else f32
         self.out = [torch.empty((Q, 64, 512), dtype=odt, device=device) for _ in wl.layers]
         self.lse = [torch.empty((Q, 64), dtype=f32, device=device) for _ in wl.layers]
@@ -134,7 +139,8 @@ class LayerRunner:
         csa2_sparse_attn(lay.q, qdt, self.slots.compress_kv, wl.seq_base, self.slots.topk_idxs,
                          wl.topk, self.layer_rows[li]["swa"], wl.swa_base, wl.swa_pos0, None,
                          wl.window, wl.q_seq, wl.q_pos, wl.ratio, lay.sink, wl.softmax_scale,
-                         self.out[li], qdt if self.quant else CSA2_F32, self.lse[li], self.Q)
+                         self.out[li], qdt if self.quant else CSA2_F32, self.lse[li], self.Q,
+                         workspace=self.ws_attn)
 
     # -- a whole pass ----------------------------------------------------------
     def steps(self, concurrent=False):

@@ -117,7 +117,7 @@ STAGE_KERNELS = {
     "block_candidates": ("select_kernel<2,",),
     "topk_dense": ("select_kernel<0,", "select_kernel<3,"),
     "topk_pool": ("select_kernel<1,",),
-    "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_f32_kernel"),
+    "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_combine_kernel", "sparse_attn_f32_kernel"),
 }
 CALIB_KERNEL = "__amd_rocclr_copyBuffer"
 CALIB_KIB = 256 * 1024          # the benchmark's calibration copy moves 256 MiB each way

@@ -15,9 +15,10 @@
 //   2. if more than k entries are selectable, radix-select the k-th largest
 //      key T with 8-bit digit passes over LDS histograms, stopping as soon as
 //      the threshold bucket is taken whole;
-//   3. compact in position order: per-(round, wave) ballot counts, one scan
-//      and mbcnt ranks place every key > T, then the first (k - #greater)
-//      keys equal to T, which applies the lower-position tie rule exactly.
+//   3. move the keys to blocked ownership through LDS (thread tid holds
+//      entries [EMAX tid, +EMAX)) and compact in position order with one
+//      thread-level scan: every key > T, then the first (k - #greater) keys
+//      equal to T, which applies the lower-position tie rule exactly.
 // Long rows are cut into chunks; each chunk's k winners (already in position
 // order) form a shorter list, and further stages select from the lists until
 // one chunk holds the row.  A strict total order makes this exact: an entry
@@ -109,7 +110,9 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
   // keeps the first digit pass (where scores share few top bytes) from
   // serialising on one address.
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[256 * 16];
-  __shared__ uint32_t s_cnt[EMAX * SEL_WAVES];   // per (round, wave) packed counts
+  // transpose buffer: entry p of the chunk at p + 4 (p / EMAX), so that each
+  // thread's EMAX consecutive entries start on a different bank group
+  __shared__ __attribute__((aligned(16))) uint32_t s_tr[CAP + 4 * SEL_THREADS];
   __shared__ uint32_t s_wsum[SEL_WAVES];
   __shared__ uint32_t s_bucket, s_above, s_bcnt;
 
@@ -207,6 +210,44 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
     for (int j = 0; j < EMAX; ++j) key[j] = KEY_PAD;
   }
 
+  // Striped -> blocked ownership through LDS: thread tid now holds entries
+  // [EMAX tid, EMAX tid + EMAX) of the chunk in key[0..EMAX), so position
+  // order is (thread, j) and compaction needs one thread-level scan.
+  {
+#pragma unroll
+    for (int j = 0; j < EMAX; ++j) {
+      const int pe = j * SEL_THREADS + tid;
+      s_tr[pe + 4 * (pe / EMAX)] = key[j];
+    }
+    __syncthreads();
+    const uint32_t* src = s_tr + (EMAX + 4) * tid;
+#pragma unroll
+    for (int i = 0; i < EMAX / 4; ++i) {
+      const uint4 v = *(const uint4*)(src + 4 * i);
+      key[4 * i] = v.x;
+      key[4 * i + 1] = v.y;
+      key[4 * i + 2] = v.z;
+      key[4 * i + 3] = v.w;
+    }
+    if (MODE == SEL_POOL || MODE == SEL_LIST) {
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j) {
+        const int pe = j * SEL_THREADS + tid;
+        s_tr[pe + 4 * (pe / EMAX)] = (uint32_t)aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < EMAX / 4; ++i) {
+        const uint4 v = *(const uint4*)(src + 4 * i);
+        aux[(4 * i) % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] = (int32_t)v.x;
+        aux[(4 * i + 1) % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] = (int32_t)v.y;
+        aux[(4 * i + 2) % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] = (int32_t)v.z;
+        aux[(4 * i + 3) % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] = (int32_t)v.w;
+      }
+    }
+  }
+
   const int k = s.k;
   const uint32_t copy = (uint32_t)lane & 15u;
 
@@ -261,41 +302,29 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
   }
 
   // order-preserving compaction ----------------------------------------------
-  // Position order is (round j, wave, lane).  Each wave counts, per round, its
-  // keys > T (low half) and == T (high half); one scan over the (round, wave)
-  // counts gives each group's offsets and mbcnt ranks place the lanes: a key
-  // is taken if it is > T, or == T among the first keq equal keys.
+  // Thread tid holds positions [EMAX tid, +EMAX) in order.  One block scan of
+  // the packed per-thread counts (keys > T low half, keys == T high half)
+  // gives every thread the number of earlier keys > T and == T; an entry's
+  // output slot is (#earlier > T) + min(#earlier == T, keq), and a key == T
+  // is taken only among the first keq of them in position order.
+  const int my0 = EMAX * tid;   // first entry of this thread within the chunk
+  uint32_t cg = 0, ce = 0;
 #pragma unroll
   for (int j = 0; j < EMAX; ++j) {
-    const uint64_t gm = __ballot(key[j] > T);
-    const uint64_t em = __ballot(key[j] == T && j * SEL_THREADS + tid < count);
-    if (lane == 0) s_cnt[j * SEL_WAVES + wave] = (uint32_t)__popcll(gm) | ((uint32_t)__popcll(em) << 16);
+    cg += (key[j] > T) ? 1u : 0u;
+    ce += (key[j] == T && my0 + j < count) ? 1u : 0u;
   }
-  __syncthreads();
-  {
-    const uint32_t v = (tid < EMAX * SEL_WAVES) ? s_cnt[tid] : 0u;
-    uint32_t tot_packed;
-    const uint32_t ex = block_excl_scan(v, lane, wave, s_wsum, &tot_packed);
-    __syncthreads();
-    if (tid < EMAX * SEL_WAVES) s_cnt[tid] = ex;
-    if (tid == 0) s_bcnt = (tot_packed & 0xFFFFu) + min(tot_packed >> 16, keq);
-    __syncthreads();
-  }
-  const uint32_t total = s_bcnt;
+  uint32_t tot_packed;
+  const uint32_t ex = block_excl_scan(cg | (ce << 16), lane, wave, s_wsum, &tot_packed);
+  const uint32_t total = (tot_packed & 0xFFFFu) + min(tot_packed >> 16, keq);
+  uint32_t rg = ex & 0xFFFFu, re = ex >> 16;
 #pragma unroll
   for (int j = 0; j < EMAX; ++j) {
-    const bool in = j * SEL_THREADS + tid < count;
     const bool gt = key[j] > T;
-    const bool eq = in && key[j] == T;
-    const uint64_t gm = __ballot(gt);
-    const uint64_t em = __ballot(eq);
-    const uint32_t base = s_cnt[j * SEL_WAVES + wave];
-    const uint32_t gr = __builtin_amdgcn_mbcnt_hi((uint32_t)(gm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)gm, 0u));
-    const uint32_t er = __builtin_amdgcn_mbcnt_hi((uint32_t)(em >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)em, 0u));
-    const uint32_t eq_rank = (base >> 16) + er;
-    if (gt || (eq && eq_rank < keq)) {
-      const uint32_t o = (base & 0xFFFFu) + gr + min(eq_rank, keq);
-      const int64_t g = g0 + j * SEL_THREADS + tid;
+    const bool eq = key[j] == T && my0 + j < count;
+    if (gt || (eq && re < keq)) {
+      const uint32_t o = rg + min(re, keq);
+      const int64_t g = g0 + my0 + j;
       int32_t pos;
       if (MODE == SEL_DENSE || MODE == SEL_BLOCKMAX) {
         pos = (int32_t)g;
@@ -313,6 +342,8 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
         s.out_idx[(int64_t)t * k + o] = pos;
       }
     }
+    rg += gt ? 1u : 0u;
+    re += eq ? 1u : 0u;
   }
   // padding
   for (int q = (int)total + tid; q < k; q += SEL_THREADS) {

@@ -542,15 +542,19 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs a) {
 
 // Combine the partial records of the key splits of one (query, 16 heads):
 // the common maximum includes the sink, which enters only the denominator.
-// 1024 threads, two 4-column groups each; every load (all splits' partial O
-// and their m, l) is issued before any is used, with split indices clamped
-// to the last split and zero factors past it, so one memory round trip
-// covers the whole combine.
+// Four workgroups of 256 threads per (query, 16 heads), each taking 4 heads
+// (two 4-column groups per thread), so the partial records are read by many
+// CUs at once; every load (all splits' partial O and their m, l) is issued
+// before any is used, with split indices clamped to the last split and zero
+// factors past it, so one memory round trip covers the combine.
 constexpr int ATTN_MAX_SPLIT = 8;
 
-__global__ __launch_bounds__(1024) void sparse_attn_combine_kernel(AttnArgs a) {
+constexpr int ATTN_COMBINE_PARTS = 4;
+
+__global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs a) {
   const int n_hg = a.H / AT_HEADS;
-  const int tg = blockIdx.x;
+  const int tg = blockIdx.x / ATTN_COMBINE_PARTS;
+  const int e0 = (blockIdx.x % ATTN_COMBINE_PARTS) * (AT_HEADS * AT_D / ATTN_COMBINE_PARTS);
   const int t = tg / n_hg;
   const int h0 = (tg - t * n_hg) * AT_HEADS;
   const float* rec0 = a.part + (int64_t)tg * a.n_split * ATTN_PART_FLOATS;
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(1024) void sparse_attn_combine_kernel(AttnArgs a) {
   float ms[2][ATTN_MAX_SPLIT], ls[2][ATTN_MAX_SPLIT];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int e = threadIdx.x * 4 + i * 4096;
+    const int e = e0 + threadIdx.x * 4 + i * 1024;
     const int h = e / AT_D;
 #pragma unroll
     for (int sp = 0; sp < ATTN_MAX_SPLIT; ++sp) {
@@ -572,7 +576,7 @@ __global__ __launch_bounds__(1024) void sparse_attn_combine_kernel(AttnArgs a) {
   const int64_t obase = ((int64_t)t * a.H + h0) * AT_D;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int e = threadIdx.x * 4 + i * 4096;
+    const int e = e0 + threadIdx.x * 4 + i * 1024;
     const int h = e / AT_D;
     const float sink2 = a.sink[h0 + h] * LOG2E;
     float M = sink2;
@@ -625,7 +629,7 @@ hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s) {
   if (a.n_split > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3(groups), dim3(1024), 0, s, a);
+    hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3(groups * ATTN_COMBINE_PARTS), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

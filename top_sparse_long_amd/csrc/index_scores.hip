@@ -361,38 +361,39 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
       const int colb = blk * PF_KB;
       const bool more = (j + 1 < n_blk) && maxvis > 0;
       if (more) load_block(blk + 1);
+      // B operands of the next tile are read from LDS while the current
+      // tile's MFMAs and epilogue run
+      const int n_tiles = min(PF_KB / 32, (a.n_cols - colb + 31) / 32);
+      v8h kb[8];
+      auto read_kb = [&](int tile) {
+        const uint8_t* krow = s_k[buf] + (tile * 32 + r) * PF_RS + 128 * half;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) kb[m] = *(const v8h*)(krow + 16 * m);
+      };
+      if (n_tiles > 0) read_kb(0);
 #pragma unroll 1
-      for (int tile = 0; tile < PF_KB / 32; ++tile) {
+      for (int tile = 0; tile < n_tiles; ++tile) {
         const int tcol = colb + tile * 32;
-        if (tcol >= a.n_cols) break;
         const int col = tcol + r;
-        // does either query see any column of this tile?
-        const bool need0 = act[0] && tcol < nv[0];
-        const bool need1 = act[1] && tcol < nv[1];
-        float sc[2] = {-INFINITY, -INFINITY};
-        if (need0 || need1) {
-          const uint8_t* krow = s_k[buf] + (tile * 32 + r) * PF_RS + 128 * half;
-          v8h kb[8];
+        const float ks = s_ks[buf][tile * 32 + r];
+        // both queries' chains interleaved; every tile is contracted and
+        // columns a query does not see are masked
+        v16f acc[2] = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f},
+                       {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-          for (int m = 0; m < 8; ++m) kb[m] = *(const v8h*)(krow + 16 * m);
-          const float ks = s_ks[buf][tile * 32 + r];
-          // both queries' chains interleaved (a query that sees none of the
-          // tile is computed anyway and masked)
-          v16f acc[2] = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f},
-                         {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
+        for (int m = 0; m < 8; ++m) {
+          acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][m], kb[m], acc[0], 0, 0, 0);
+          acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][m], kb[m], acc[1], 0, 0, 0);
+        }
+        if (tile + 1 < n_tiles) read_kb(tile + 1);
+        float sc[2];
 #pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][m], kb[m], acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[1][m], kb[m], acc[1], 0, 0, 0);
-          }
+        for (int i = 0; i < 2; ++i) {
+          float v = 0.f;
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            float v = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) v = fmaf(gate[i][jj], relu(acc[i][jj]), v);
-            v = add_half_swap(v);
-            sc[i] = (act[i] && col < nv[i]) ? v * ks : -INFINITY;
-          }
+          for (int jj = 0; jj < 16; ++jj) v = fmaf(gate[i][jj], relu(acc[i][jj]), v);
+          v = add_half_swap(v);
+          sc[i] = (act[i] && col < nv[i]) ? v * ks : -INFINITY;
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {

@@ -45,6 +45,8 @@ def _parse():
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="queries of the CPU-oracle sample (default: all queries, max 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate-select", action="store_true",
+                    help="run the Full layer's top-k and block candidates as two calls")
     ap.add_argument("--overlap-blocks", action="store_true",
                     help="capture block-candidate selection on a second stream beside the Full "
                          "layer's top-k and attention (HIP graphs on this ROCm replay the "
@@ -85,6 +87,12 @@ def _stage_work(run, stage):
     if stage == "block_candidates" and run.fuse_block_max:
         nblk = (nvis + wl.block_size - 1) // wl.block_size
         return float(nblk.sum().item()) * SCORE_BYTES, int(nvis.sum().item())
+    if stage == "topk_and_blocks":
+        # the top-k reads every visible score; the pool reads the block
+        # maxima when the scoring pass wrote them, else the scores again
+        nblk = (nvis + wl.block_size - 1) // wl.block_size
+        pool = nblk if run.fuse_block_max else nvis
+        return float((nvis + pool).sum().item()) * SCORE_BYTES, int(nvis.sum().item())
     if stage in ("topk_dense", "block_candidates"):
         return float(nvis.sum().item()) * SCORE_BYTES, int(nvis.sum().item())
     if stage == "topk_pool":
@@ -117,6 +125,7 @@ STAGE_KERNELS = {
     "block_candidates": ("select_kernel<2,",),
     "topk_dense": ("select_kernel<0,", "select_kernel<3,"),
     "topk_pool": ("select_kernel<1,",),
+    "topk_and_blocks": ("select_pair_kernel", "select_kernel<3,"),
     "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_combine_kernel", "sparse_attn_f32_kernel"),
 }
 CALIB_KERNEL = "__amd_rocclr_copyBuffer"
@@ -351,7 +360,8 @@ def main():
                 f()
         return g
 
-    step_graphs = [capture([f for _, f in r.steps(concurrent=args.overlap_blocks)]) for r in runs]
+    step_graphs = [capture([f for _, f in r.steps(concurrent=args.overlap_blocks,
+                                                        separate_select=args.separate_select)]) for r in runs]
     for i in range(args.warmup):
         step_graphs[i % len(step_graphs)].replay()
     torch.cuda.synchronize()
@@ -377,14 +387,15 @@ def main():
     stages = {}
     run0 = runs[0]
     names = []
-    for name, _ in run0.steps():
+    sel = dict(separate_select=args.separate_select)
+    for name, _ in run0.steps(**sel):
         if name != "reset" and name not in names:
             names.append(name)
     for name in names:
         fns = []
         for _ in range(reps):
             for r in runs:
-                fns += [f for n, f in r.steps() if n == name]
+                fns += [f for n, f in r.steps(**sel) if n == name]
         g = capture(fns)
         g.replay()
         torch.cuda.synchronize()
@@ -395,7 +406,7 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         avg_ms = e0.elapsed_time(e1) / len(fns)
-        per_step = sum(1 for n, _ in run0.steps() if n == name)
+        per_step = sum(1 for n, _ in run0.steps(**sel) if n == name)
         nbytes, units = _stage_work(run0, name)
         stages[name] = {"avg_us": avg_ms * 1e3, "calls_per_step": per_step,
                         "algorithmic_bytes": nbytes, "units": units,
@@ -433,7 +444,9 @@ def main():
         "config": {"workload": args.workload, "batch": wl.Q, "ctx_entries": wl.max_cols(),
                    "ratio": wl.ratio, "layers": [l.mode for l in wl.layers],
                    "topk": wl.topk, "pool_blocks": wl.n_blocks, "block_size": wl.block_size,
-                   "input_copies": len(runs), "block_candidates_overlapped": bool(args.overlap_blocks)},
+                   "input_copies": len(runs), "block_candidates_overlapped": bool(args.overlap_blocks),
+                   "full_layer_selections": ("separate" if args.separate_select or args.overlap_blocks
+                                             else "shared launch")},
         "sparse_attn_queries_per_s": n_attn / (ms_per_step * 1e-3),
         "roofline": roofline,
         "cpu_baseline": cpu,

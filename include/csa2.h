@@ -1,10 +1,11 @@
 /*
  * csa2.h — C ABI of the CSA2 global-attention hot path for MI355X (gfx950).
  *
- * The four calls follow the pages' statement of the problem:
+ * The calls follow the pages' statement of the problem:
  *   csa2_index_scores      Lightning-Indexer scores, dense or over a candidate pool
  *   csa2_block_candidates  block-max candidate pool (hierarchical sparse indexer)
  *   csa2_topk              token-level top-k selection
+ *   csa2_topk_and_block_candidates  both selections of a Full layer at once
  *   csa2_sparse_attn       joint-softmax sparse MQA attention with a sink
  * Sources are cited as page + section:
  *   [CSA2]   zdszero.github.io/csa2.html (CSA2 deep-dive)
@@ -179,6 +180,32 @@ int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols,
               void* workspace, size_t workspace_bytes, int32_t Q, void* stream);
 
 size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k);
+
+/*
+ * csa2_topk_and_block_candidates — a Full layer's own top-k and the block
+ * candidate pool it hands to the Reuse layers that follow, from the one set
+ * of dense scores ([CSA2] "hierarchical sparse indexer", recall step: the
+ * first Full layer picks its own top-k and the candidate blocks from one
+ * scoring of every visible position).  The result equals
+ *   csa2_topk(scores, score_stride, n_cols, q_pos, ratio, NULL, 0, 1, k, idx, ...)
+ *   csa2_block_candidates(scores, score_stride, n_cols, block_max,
+ *                         block_max_stride, q_pos, ratio, block_size, n_blocks, cand, ...)
+ * bit for bit; the two selections run in shared launches, so neither waits
+ * for the other to drain the chip.  Arguments mean what they mean in those
+ * two calls; scores is required (the top-k reads it) and q_pos is required.
+ *   workspace at least csa2_topk_and_block_candidates_workspace_size(Q,
+ *             n_cols, k, block_size, n_blocks) bytes, 16-byte aligned.
+ *   Supported: the union of both calls' limits.
+ */
+int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
+                                   const float* block_max, int64_t block_max_stride,
+                                   const int32_t* q_pos, int32_t ratio, int32_t k, int32_t* idx,
+                                   int32_t block_size, int32_t n_blocks, int32_t* cand,
+                                   void* workspace, size_t workspace_bytes, int32_t Q,
+                                   void* stream);
+
+size_t csa2_topk_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t k,
+                                                     int32_t block_size, int32_t n_blocks);
 
 /*
  * csa2_sparse_attn — core sparse attention ([CSA2] "per-layer attention

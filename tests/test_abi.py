@@ -120,6 +120,35 @@ def test_block_candidates_rejects():
         tsl.CSA2_ERR_WORKSPACE
 
 
+def test_topk_and_block_candidates_rejects():
+    lib = tsl.load()
+    f = lib.csa2_topk_and_block_candidates
+    # scores, q_pos, block size, k and the pool size are checked as in the separate calls
+    assert f(None, 64, 64, None, 0, FAKE, 1, 8, FAKE, 8, 16, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert f(FAKE, 64, 64, None, 0, None, 1, 8, FAKE, 8, 16, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 8, FAKE, 12, 16, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_UNSUPPORTED
+    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 4096, FAKE, 8, 16, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_UNSUPPORTED
+    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 8, FAKE, 8, 8192, FAKE, None, 0, 1, None) == \
+        tsl.CSA2_ERR_UNSUPPORTED
+    # the workspace holds both selections' lists
+    Q, n = 2, 1 << 20
+    need = lib.csa2_topk_and_block_candidates_workspace_size(Q, n, 512, 8, 2048)
+    t = lib.csa2_topk_workspace_size(Q, n, 512)
+    b = lib.csa2_block_candidates_workspace_size(Q, n, 8, 2048)
+    assert t > 0 and b > 0 and need >= t + b and need - (t + b) < 16
+    for short in (need - 1, t, 0):
+        assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, FAKE, short, Q, None) == \
+            tsl.CSA2_ERR_WORKSPACE
+    assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, FAKE + 4, need, Q, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    # Q == 0 passes every check and enqueues nothing
+    assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, None, 0, 0, None) == tsl.CSA2_OK
+
+
 def test_workspace_sizes():
     lib = tsl.load()
     assert lib.csa2_topk_workspace_size(64, 32768, 512) == 0      # one chunk per row

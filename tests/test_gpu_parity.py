@@ -222,6 +222,56 @@ def test_block_candidates_exact(n_cols, n_blocks):
     assert np.array_equal(_np(cand), ref)
 
 
+@pytest.mark.parametrize("from_block_max", [False, True])
+@pytest.mark.parametrize("n_cols,n_blocks,k,ratio", [(100, 16, 512, 1), (20000, 2048, 512, 2),
+                                                     (131072, 2048, 512, 1),
+                                                     (300000, 2048, 2048, 1),
+                                                     (1 << 20, 2048, 512, 2)])
+def test_topk_and_block_candidates_exact(n_cols, n_blocks, k, ratio, from_block_max):
+    """The shared-launch call gives the oracle's top-k and pool, and the same
+    bits as the two separate calls."""
+    _announce(f"topk_and_block_candidates n_cols={n_cols} n_blocks={n_blocks} k={k} "
+              f"ratio={ratio} block_max={from_block_max}")
+    rng = np.random.default_rng(n_cols + k + ratio)
+    Q, bs = 3, 8
+    sc = _tie_scores(rng, Q, n_cols, 40)
+    last = [ratio * n_cols - 1, max(0, (ratio * n_cols) // 3 - 5), 0]
+    q_pos = np.array(last, dtype=np.int32)
+    nvis = oracle.visible_count(q_pos, ratio)
+    stride = (n_cols + 63) // 64 * 64
+    dev = torch.full((Q, stride), float("nan"), device=DEV)
+    dev[:, :n_cols] = torch.from_numpy(sc).to(DEV)
+    bm = None
+    if from_block_max:
+        nb = -(-n_cols // bs)
+        host = np.full((Q, nb), -np.inf)
+        for t in range(Q):
+            m = oracle.block_maxima(sc[t].astype(np.float64), int(min(nvis[t], n_cols)), bs)
+            host[t, :len(m)] = m
+        bm = torch.from_numpy(host.astype(np.float32)).to(DEV)
+    qp = torch.from_numpy(q_pos).to(DEV)
+    idx = torch.empty((Q, k), dtype=torch.int32, device=DEV)
+    cand = torch.empty((Q, n_blocks), dtype=torch.int32, device=DEV)
+    wsb = tsl.csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, bs, n_blocks)
+    ws = torch.randint(0, 255, (max(16, wsb),), dtype=torch.uint8, device=DEV)
+    tsl.csa2_topk_and_block_candidates(dev, n_cols, qp, ratio, k, idx, bs, n_blocks, cand, ws, Q,
+                                       block_max=bm)
+    torch.cuda.synchronize()
+    sc64 = sc.astype(np.float64)
+    assert np.array_equal(_np(idx), oracle.topk_rows_dense(sc64, q_pos, ratio, k))
+    assert np.array_equal(_np(cand), oracle.block_candidates(sc64, q_pos, ratio, bs, n_blocks))
+    # the separate calls, bit for bit
+    idx2, cand2 = torch.empty_like(idx), torch.empty_like(cand)
+    ws_t = torch.empty((max(16, tsl.csa2_topk_workspace_size(Q, n_cols, k)),), dtype=torch.uint8,
+                       device=DEV)
+    ws_b = torch.empty((max(16, tsl.csa2_block_candidates_workspace_size(Q, n_cols, bs, n_blocks)),),
+                       dtype=torch.uint8, device=DEV)
+    tsl.csa2_topk(dev, n_cols, qp, ratio, k, idx2, ws_t, Q)
+    tsl.csa2_block_candidates(dev, n_cols, qp, ratio, bs, n_blocks, cand2, ws_b, Q, block_max=bm)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2) and torch.equal(cand, cand2)
+
+
 # ---------------------------------------------------------------------------
 # attention: the oracle runs on the same indices
 

@@ -17,7 +17,8 @@ CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ER
 CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1 = 0, 1, 2, 3
 
 EXPORTED = ("csa2_index_scores", "csa2_block_candidates", "csa2_block_candidates_workspace_size",
-            "csa2_topk", "csa2_topk_workspace_size", "csa2_sparse_attn",
+            "csa2_topk", "csa2_topk_workspace_size", "csa2_topk_and_block_candidates",
+            "csa2_topk_and_block_candidates_workspace_size", "csa2_sparse_attn",
             "csa2_sparse_attn_workspace_size",
             "csa2_status_string", "csa2_last_error", "csa2_version")
 
@@ -55,6 +56,10 @@ def load():
     lib.csa2_topk.argtypes = [P, I64, I32, P, I32, P, I32, I32, I32, P, P, SZ, I32, P]
     lib.csa2_topk_workspace_size.argtypes = [I32, I32, I32]
     lib.csa2_topk_workspace_size.restype = SZ
+    lib.csa2_topk_and_block_candidates.argtypes = [P, I64, I32, P, I64, P, I32, I32, P, I32, I32,
+                                                   P, P, SZ, I32, P]
+    lib.csa2_topk_and_block_candidates_workspace_size.argtypes = [I32, I32, I32, I32, I32]
+    lib.csa2_topk_and_block_candidates_workspace_size.restype = SZ
     lib.csa2_sparse_attn.argtypes = [P, ctypes.c_int, RP, P, P, I32, RP, P, P, P, I32, P, P, I32,
                                      P, ctypes.c_float, P, ctypes.c_int, P, P, SZ, I32, I32, I32, P]
     lib.csa2_sparse_attn_workspace_size.argtypes = [I32, I32, I32, I32]
@@ -62,8 +67,8 @@ def load():
     lib.csa2_status_string.argtypes = [ctypes.c_int]
     lib.csa2_status_string.restype = ctypes.c_char_p
     lib.csa2_last_error.restype = ctypes.c_char_p
-    for fn in ("csa2_index_scores", "csa2_block_candidates", "csa2_topk", "csa2_sparse_attn",
-               "csa2_version"):
+    for fn in ("csa2_index_scores", "csa2_block_candidates", "csa2_topk",
+               "csa2_topk_and_block_candidates", "csa2_sparse_attn", "csa2_version"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -155,6 +160,22 @@ def csa2_topk(scores, n_cols, q_pos, ratio, k, idx, workspace, Q, cand=None, blo
     ncb = 0 if cand is None else cand.shape[-1]
     _check(lib.csa2_topk(_ptr(scores), scores.stride(0), n_cols, _ptr(q_pos), ratio, _ptr(cand),
                          ncb, block_size, k, _ptr(idx), _ptr(workspace), wsb, Q, _stream(stream)))
+
+
+def csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size, n_blocks):
+    return load().csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size,
+                                                                n_blocks)
+
+
+def csa2_topk_and_block_candidates(scores, n_cols, q_pos, ratio, k, idx, block_size, n_blocks,
+                                   cand, workspace, Q, block_max=None, stream=None):
+    lib = load()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    bms = 0 if block_max is None else block_max.stride(0)
+    _check(lib.csa2_topk_and_block_candidates(_ptr(scores), scores.stride(0), n_cols,
+                                              _ptr(block_max), bms, _ptr(q_pos), ratio, k,
+                                              _ptr(idx), block_size, n_blocks, _ptr(cand),
+                                              _ptr(workspace), wsb, Q, _stream(stream)))
 
 
 def csa2_sparse_attn_workspace_size(Q, H, k, window):

@@ -167,12 +167,14 @@ static int check_select_common(const char* fn, const float* scores, int64_t scor
   return CSA2_OK;
 }
 
-int csa2_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
-                          const float* block_max, int64_t block_max_stride,
-                          const int32_t* q_pos, int32_t ratio, int32_t block_size,
-                          int32_t n_blocks, int32_t* cand, void* workspace,
-                          size_t workspace_bytes, int32_t Q, void* stream) {
-  g_err[0] = 0;
+// Checks of csa2_block_candidates; fills the selection arguments and the
+// number of blocks per row.
+static int prep_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
+                                 const float* block_max, int64_t block_max_stride,
+                                 const int32_t* q_pos, int32_t ratio, int32_t block_size,
+                                 int32_t n_blocks, int32_t* cand, void* workspace,
+                                 size_t workspace_bytes, int32_t Q, csa2::SelectArgs* out,
+                                 int64_t* n_rows) {
   if (block_max) {
     // the maxima replace the scores; the stride and alignment checks of the
     // scores apply to a stand-in that is never read
@@ -197,7 +199,6 @@ int csa2_block_candidates(const float* scores, int64_t score_stride, int32_t n_c
   REQUIRE(workspace_bytes >= need && (need == 0 || workspace), CSA2_ERR_WORKSPACE,
           "csa2_block_candidates: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   REQUIRE(aligned(workspace, 16), CSA2_ERR_INVALID_ARG, "csa2_block_candidates: workspace must be 16-byte aligned");
-  if (Q == 0) return CSA2_OK;
   csa2::SelectArgs a = {};
   a.scores = scores;
   a.score_stride = score_stride;
@@ -211,16 +212,31 @@ int csa2_block_candidates(const float* scores, int64_t score_stride, int32_t n_c
   a.out_idx = cand;
   a.workspace = workspace;
   a.Q = Q;
-  const int64_t nb = ((int64_t)n_cols + block_size - 1) / block_size;
+  *out = a;
+  *n_rows = ((int64_t)n_cols + block_size - 1) / block_size;
+  return CSA2_OK;
+}
+
+int csa2_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
+                          const float* block_max, int64_t block_max_stride,
+                          const int32_t* q_pos, int32_t ratio, int32_t block_size,
+                          int32_t n_blocks, int32_t* cand, void* workspace,
+                          size_t workspace_bytes, int32_t Q, void* stream) {
+  g_err[0] = 0;
+  csa2::SelectArgs a;
+  int64_t nb = 0;
+  const int st = prep_block_candidates(scores, score_stride, n_cols, block_max, block_max_stride,
+                                       q_pos, ratio, block_size, n_blocks, cand, workspace,
+                                       workspace_bytes, Q, &a, &nb);
+  if (st != CSA2_OK || Q == 0) return st;
   return hip_status(csa2::launch_select(csa2::SEL_BLOCKMAX, a, nb, (hipStream_t)stream),
                     "csa2_block_candidates");
 }
 
-int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols, const int32_t* q_pos,
-              int32_t ratio, const int32_t* cand, int32_t n_cand_blocks, int32_t block_size,
-              int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes, int32_t Q,
-              void* stream) {
-  g_err[0] = 0;
+static int prep_topk(const float* scores, int64_t score_stride, int32_t n_cols,
+                     const int32_t* q_pos, int32_t ratio, const int32_t* cand,
+                     int32_t n_cand_blocks, int32_t block_size, int32_t k, int32_t* idx,
+                     void* workspace, size_t workspace_bytes, int32_t Q, csa2::SelectArgs* out) {
   int st = check_select_common("csa2_topk", scores, score_stride, n_cols, k, idx, Q);
   if (st) return st;
   REQUIRE(k <= 2048, CSA2_ERR_UNSUPPORTED, "csa2_topk: k above 2048");
@@ -237,7 +253,6 @@ int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols, const i
   REQUIRE(workspace_bytes >= need && (need == 0 || workspace), CSA2_ERR_WORKSPACE,
           "csa2_topk: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   REQUIRE(aligned(workspace, 16), CSA2_ERR_INVALID_ARG, "csa2_topk: workspace must be 16-byte aligned");
-  if (Q == 0) return CSA2_OK;
   csa2::SelectArgs a = {};
   a.scores = scores;
   a.score_stride = score_stride;
@@ -251,9 +266,55 @@ int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols, const i
   a.out_idx = idx;
   a.workspace = workspace;
   a.Q = Q;
+  *out = a;
+  return CSA2_OK;
+}
+
+int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols, const int32_t* q_pos,
+              int32_t ratio, const int32_t* cand, int32_t n_cand_blocks, int32_t block_size,
+              int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes, int32_t Q,
+              void* stream) {
+  g_err[0] = 0;
+  csa2::SelectArgs a;
+  const int st = prep_topk(scores, score_stride, n_cols, q_pos, ratio, cand, n_cand_blocks,
+                           block_size, k, idx, workspace, workspace_bytes, Q, &a);
+  if (st != CSA2_OK || Q == 0) return st;
   return hip_status(csa2::launch_select(cand ? csa2::SEL_POOL : csa2::SEL_DENSE, a, n_cols,
                                         (hipStream_t)stream),
                     "csa2_topk");
+}
+
+static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
+
+size_t csa2_topk_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t k,
+                                                     int32_t block_size, int32_t n_blocks) {
+  return align16(csa2_topk_workspace_size(Q, n_cols, k)) +
+         csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks);
+}
+
+int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
+                                   const float* block_max, int64_t block_max_stride,
+                                   const int32_t* q_pos, int32_t ratio, int32_t k, int32_t* idx,
+                                   int32_t block_size, int32_t n_blocks, int32_t* cand,
+                                   void* workspace, size_t workspace_bytes, int32_t Q,
+                                   void* stream) {
+  g_err[0] = 0;
+  REQUIRE(q_pos, CSA2_ERR_INVALID_ARG, "csa2_topk_and_block_candidates: q_pos is required");
+  // the top-k's workspace comes first, the pool's follows at a 16-byte boundary
+  const size_t ws_t = align16(csa2_topk_workspace_size(Q, n_cols, k));
+  const size_t ws_b = workspace_bytes > ws_t ? workspace_bytes - ws_t : 0;
+  uint8_t* ws = (uint8_t*)workspace;
+  csa2::SelectArgs at, ab;
+  int64_t nb = 0;
+  int st = prep_topk(scores, score_stride, n_cols, q_pos, ratio, nullptr, 0, block_size, k, idx,
+                     workspace, workspace_bytes < ws_t ? workspace_bytes : ws_t, Q, &at);
+  if (st != CSA2_OK) return st;
+  st = prep_block_candidates(scores, score_stride, n_cols, block_max, block_max_stride, q_pos,
+                             ratio, block_size, n_blocks, cand, ws_b ? ws + ws_t : nullptr, ws_b,
+                             Q, &ab, &nb);
+  if (st != CSA2_OK || Q == 0) return st;
+  return hip_status(csa2::launch_topk_and_blocks(at, n_cols, ab, nb, (hipStream_t)stream),
+                    "csa2_topk_and_block_candidates");
 }
 
 int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv,

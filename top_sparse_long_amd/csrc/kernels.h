@@ -78,6 +78,10 @@ struct SelectArgs {
 };
 
 hipError_t launch_select(int mode, const SelectArgs& a, int64_t rows_len, hipStream_t s);
+// Dense top-k and block candidates of the same rows: the first stages of
+// both run in one launch (their workspaces must not overlap).
+hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, const SelectArgs& blocks,
+                                  int64_t blocks_len, hipStream_t s);
 
 // Sparse attention -----------------------------------------------------------
 struct AttnArgs {

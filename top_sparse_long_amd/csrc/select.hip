@@ -102,23 +102,32 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, int lane, int wa
   return before + incl - x;
 }
 
+// LDS bytes of one selection body of capacity CAP (carved in this order).
+template <int CAP>
+struct SelSmem {
+  static constexpr int HIST = 256 * 16 * 4;
+  static constexpr int TR = (CAP + 4 * SEL_THREADS) * 4;
+  static constexpr int WSUM = 16 * 4;
+  static constexpr int BYTES = HIST + TR + WSUM + 16;
+};
+
 template <int MODE, int CAP>
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
+__device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, uint8_t* smem) {
   constexpr int EMAX = CAP / SEL_THREADS;   // entries per thread at most
   // 16 interleaved copies of the 256-bin histogram (bin b, copy c at
   // 16 b + c): lanes that hit the same bin land on 16 different banks, which
   // keeps the first digit pass (where scores share few top bytes) from
   // serialising on one address.
-  __shared__ __attribute__((aligned(16))) uint32_t s_hist[256 * 16];
+  uint32_t* s_hist = (uint32_t*)smem;
   // transpose buffer: entry p of the chunk at p + 4 (p / EMAX), so that each
   // thread's EMAX consecutive entries start on a different bank group
-  __shared__ __attribute__((aligned(16))) uint32_t s_tr[CAP + 4 * SEL_THREADS];
-  __shared__ uint32_t s_wsum[SEL_WAVES];
-  __shared__ uint32_t s_bucket, s_above, s_bcnt;
+  uint32_t* s_tr = (uint32_t*)(smem + SelSmem<CAP>::HIST);
+  uint32_t* s_wsum = (uint32_t*)(smem + SelSmem<CAP>::HIST + SelSmem<CAP>::TR);
+  uint32_t& s_bucket = *(uint32_t*)(smem + SelSmem<CAP>::HIST + SelSmem<CAP>::TR + SelSmem<CAP>::WSUM);
+  uint32_t& s_above = (&s_bucket)[1];
+  uint32_t& s_bcnt = (&s_bucket)[2];
 
   const SelectArgs& s = a.s;
-  const int t = blockIdx.y;
-  const int c = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -357,6 +366,25 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
   }
 }
 
+template <int MODE, int CAP>
+__global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SelSmem<CAP>::BYTES];
+  select_body<MODE, CAP>(a, blockIdx.x, blockIdx.y, smem);
+}
+
+// Two independent selections over the same queries in one launch (the
+// columns of the grid before n1 run the first, the rest the second), with
+// one LDS buffer sized for the larger of the two.
+template <int M1, int C1, int M2, int C2>
+__global__ __launch_bounds__(SEL_THREADS) void select_pair_kernel(StageArgs a1, StageArgs a2, int n1) {
+  constexpr int B1 = SelSmem<C1>::BYTES, B2 = SelSmem<C2>::BYTES;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[B1 > B2 ? B1 : B2];
+  if ((int)blockIdx.x < n1)
+    select_body<M1, C1>(a1, blockIdx.x, blockIdx.y, smem);
+  else
+    select_body<M2, C2>(a2, blockIdx.x - n1, blockIdx.y, smem);
+}
+
 // ---------------------------------------------------------------------------
 // host-side planning
 
@@ -430,37 +458,51 @@ static hipError_t launch_first(int mode, const StageArgs& a, int cap, int nchunk
   }
 }
 
-hipError_t launch_select(int mode, const SelectArgs& sa, int64_t rows_len, hipStream_t s) {
-  const SelectPlan p = plan_select(sa.Q, rows_len, sa.k);
-  StageArgs a = {};
-  a.s = sa;
-  if (p.n_stages == 1) {
-    const int cap = fit_cap(rows_len);
-    a.chunk = cap;
-    a.out_key = nullptr;
-    return launch_first(mode, a, cap, 1, sa.Q, s);
+// Argument blocks of a selection's stages; the first stage reads the
+// scores (or block maxima), list stages read the previous stage's lists.
+struct StagePlan {
+  SelectPlan p;
+  StageArgs first;
+  int first_cap;
+  int first_chunks;
+};
+
+static StagePlan make_stages(const SelectArgs& sa, int64_t rows_len) {
+  StagePlan sp = {};
+  sp.p = plan_select(sa.Q, rows_len, sa.k);
+  sp.first.s = sa;
+  if (sp.p.n_stages == 1) {
+    sp.first_cap = fit_cap(rows_len);
+    sp.first.chunk = sp.first_cap;
+    sp.first.out_key = nullptr;
+    sp.first_chunks = 1;
+    return sp;
   }
   uint8_t* ws = (uint8_t*)sa.workspace;
-  const size_t list_bytes = (size_t)sa.Q * (size_t)p.ws_list_max * 4u;
+  const size_t list_bytes = (size_t)sa.Q * (size_t)sp.p.ws_list_max * 4u;
+  sp.first.chunk = sp.p.chunk1;
+  sp.first.out_key = (uint32_t*)ws;
+  sp.first.out_pos = (int32_t*)(ws + list_bytes);
+  sp.first.out_stride = sp.p.list_len[0];
+  sp.first_cap = fit_cap(sp.p.chunk1);
+  sp.first_chunks = sp.p.n_chunks1;
+  return sp;
+}
+
+static hipError_t run_list_stages(const StagePlan& sp, const SelectArgs& sa, hipStream_t s) {
+  if (sp.p.n_stages == 1) return hipSuccess;
+  uint8_t* ws = (uint8_t*)sa.workspace;
+  const size_t list_bytes = (size_t)sa.Q * (size_t)sp.p.ws_list_max * 4u;
   uint32_t* key_buf[2] = {(uint32_t*)ws, (uint32_t*)(ws + 2 * list_bytes)};
   int32_t* pos_buf[2] = {(int32_t*)(ws + list_bytes), (int32_t*)(ws + 3 * list_bytes)};
-
-  // stage 1: from scores into list 0
-  a.chunk = p.chunk1;
-  a.out_key = key_buf[0];
-  a.out_pos = pos_buf[0];
-  a.out_stride = p.list_len[0];
-  hipError_t e = launch_first(mode, a, fit_cap(p.chunk1), p.n_chunks1, sa.Q, s);
-  if (e != hipSuccess) return e;
-  // list stages
   int cur = 0;
-  for (int st = 1; st < p.n_stages; ++st) {
+  for (int st = 1; st < sp.p.n_stages; ++st) {
     StageArgs b = {};
     b.s = sa;
     b.in_key = key_buf[cur];
     b.in_pos = pos_buf[cur];
-    b.in_len = p.list_len[st - 1];
-    const bool last = (st == p.n_stages - 1);
+    b.in_len = sp.p.list_len[st - 1];
+    const bool last = (st == sp.p.n_stages - 1);
     int nch, cap;
     if (last) {
       cap = fit_cap(b.in_len);
@@ -472,14 +514,50 @@ hipError_t launch_select(int mode, const SelectArgs& sa, int64_t rows_len, hipSt
       b.chunk = cap;
       b.out_key = key_buf[cur ^ 1];
       b.out_pos = pos_buf[cur ^ 1];
-      b.out_stride = p.list_len[st];
+      b.out_stride = sp.p.list_len[st];
       nch = (int)((b.in_len + cap - 1) / cap);
     }
-    e = launch_stage<SEL_LIST>(b, min(cap, SEL_CAP_LIST), nch, sa.Q, s);
+    const hipError_t e = launch_stage<SEL_LIST>(b, min(cap, SEL_CAP_LIST), nch, sa.Q, s);
     if (e != hipSuccess) return e;
     cur ^= 1;
   }
   return hipSuccess;
+}
+
+hipError_t launch_select(int mode, const SelectArgs& sa, int64_t rows_len, hipStream_t s) {
+  const StagePlan sp = make_stages(sa, rows_len);
+  const hipError_t e = launch_first(mode, sp.first, sp.first_cap, sp.first_chunks, sa.Q, s);
+  if (e != hipSuccess) return e;
+  return run_list_stages(sp, sa, s);
+}
+
+template <int C1, int C2>
+static void launch_pair(const StagePlan& t1, const StagePlan& t2, int Q, hipStream_t s) {
+  const dim3 grid(t1.first_chunks + t2.first_chunks, Q), block(SEL_THREADS);
+  hipLaunchKernelGGL((select_pair_kernel<SEL_DENSE, C1, SEL_BLOCKMAX, C2>), grid, block, 0, s,
+                     t1.first, t2.first, t1.first_chunks);
+}
+
+template <int C1>
+static void launch_pair_c2(const StagePlan& t1, const StagePlan& t2, int Q, hipStream_t s) {
+  if (t2.first_cap <= 4096) launch_pair<C1, 4096>(t1, t2, Q, s);
+  else if (t2.first_cap <= 16384) launch_pair<C1, 16384>(t1, t2, Q, s);
+  else launch_pair<C1, SEL_CAP>(t1, t2, Q, s);
+}
+
+hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, const SelectArgs& blocks,
+                                  int64_t blocks_len, hipStream_t s) {
+  const StagePlan t1 = make_stages(topk, topk_len);
+  const StagePlan t2 = make_stages(blocks, blocks_len);
+  // first stages of both selections share one launch; list stages follow
+  if (t1.first_cap <= 4096) launch_pair_c2<4096>(t1, t2, topk.Q, s);
+  else if (t1.first_cap <= 16384) launch_pair_c2<16384>(t1, t2, topk.Q, s);
+  else launch_pair_c2<SEL_CAP>(t1, t2, topk.Q, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = run_list_stages(t2, blocks, s);
+  if (e != hipSuccess) return e;
+  return run_list_stages(t1, topk, s);
 }
 
 }  // namespace csa2

@@ -21,6 +21,7 @@ import math
 import torch
 
 from . import (csa2_index_scores, csa2_block_candidates, csa2_topk, csa2_sparse_attn,
+               csa2_topk_and_block_candidates, csa2_topk_and_block_candidates_workspace_size,
                csa2_block_candidates_workspace_size, csa2_topk_workspace_size,
                csa2_sparse_attn_workspace_size,
                rows_f32, rows_fp8, rows_fp4_records, rows_swa_records,
@@ -84,7 +85,9 @@ class LayerRunner:
                     for li, l in enumerate(wl.layers) if l.mode in ("full", "reindex")}
         ws = max(csa2_topk_workspace_size(Q, self.n_cols, wl.topk),
                  csa2_topk_workspace_size(Q, self.pool_cols, wl.topk),
-                 csa2_block_candidates_workspace_size(Q, self.n_cols, wl.block_size, wl.n_blocks))
+                 csa2_block_candidates_workspace_size(Q, self.n_cols, wl.block_size, wl.n_blocks),
+                 csa2_topk_and_block_candidates_workspace_size(Q, self.n_cols, wl.topk,
+                                                               wl.block_size, wl.n_blocks))
         self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=device)
         # block candidates may run beside the Full layer's top-k on a second
         # stream, so they get a workspace of their own
@@ -133,6 +136,16 @@ class LayerRunner:
             csa2_topk(self.scores, self.n_cols, wl.q_pos, wl.ratio, wl.topk, idx, self.ws, self.Q)
         self.slots.topk_idxs = idx
 
+    def topk_and_blocks(self, li, from_block_max=False):
+        """The Full layer's top-k and the candidate pool in shared launches."""
+        wl = self.wl
+        idx = self.idx[li]
+        csa2_topk_and_block_candidates(self.scores, self.n_cols, wl.q_pos, wl.ratio, wl.topk, idx,
+                                       wl.block_size, wl.n_blocks, self.cand, self.ws, self.Q,
+                                       block_max=self.block_max if from_block_max else None)
+        self.slots.topk_idxs = idx
+        self.slots.candidates = self.cand
+
     def attention(self, li):
         wl, lay = self.wl, self.wl.layers[li]
         qdt = CSA2_BF16 if self.quant else CSA2_F32
@@ -143,9 +156,13 @@ class LayerRunner:
                          workspace=self.ws_attn)
 
     # -- a whole pass ----------------------------------------------------------
-    def steps(self, concurrent=False):
+    def steps(self, concurrent=False, separate_select=False):
         """The calls of one pass over every layer, in order, as (stage name,
         callable) pairs.
+
+        A Full layer that builds the pool makes both of its selections with
+        one call (csa2_topk_and_block_candidates) unless separate_select or
+        concurrent asks for two calls.
 
         concurrent=True runs the block-candidate selection on a second stream:
         it needs only the Full layer's scores, so it overlaps that layer's
@@ -165,6 +182,12 @@ class LayerRunner:
                 fuse = self.needs_pool[li] and self.fuse_block_max
                 out.append(("index_scores_dense",
                             lambda li=li, fuse=fuse: self.index_scores(li, pool=False, block_max=fuse)))
+                if self.needs_pool[li] and not (concurrent or separate_select):
+                    out.append(("topk_and_blocks",
+                                lambda li=li, fuse=fuse: self.topk_and_blocks(li, fuse)))
+                    out.append(("sparse_attn", lambda li=li: self.attention(li)))
+                    has_pool = True
+                    continue
                 if self.needs_pool[li]:
                     if concurrent:
                         out.append(("block_candidates",
@@ -206,10 +229,10 @@ class LayerRunner:
             torch.cuda.current_stream().wait_event(self._joined)
             self._joined = None
 
-    def run(self, mark=None, concurrent=False):
+    def run(self, mark=None, concurrent=False, separate_select=False):
         """Run every layer once.  mark(name) is called before each step and
         once at the end with None (the benchmark records events there)."""
-        for name, fn in self.steps(concurrent):
+        for name, fn in self.steps(concurrent, separate_select):
             if name not in ("reset", "join") and mark:
                 mark(name)
             fn()

@@ -449,115 +449,136 @@ static hipError_t launch_stage(const StageArgs& a, int cap, int nchunks, int Q, 
   return hipGetLastError();
 }
 
-static hipError_t launch_first(int mode, const StageArgs& a, int cap, int nchunks, int Q,
-                               hipStream_t s) {
-  switch (mode) {
-    case SEL_DENSE: return launch_stage<SEL_DENSE>(a, cap, nchunks, Q, s);
-    case SEL_POOL: return launch_stage<SEL_POOL>(a, cap, nchunks, Q, s);
-    default: return launch_stage<SEL_BLOCKMAX>(a, cap, nchunks, Q, s);
-  }
-}
-
-// Argument blocks of a selection's stages; the first stage reads the
-// scores (or block maxima), list stages read the previous stage's lists.
-struct StagePlan {
-  SelectPlan p;
-  StageArgs first;
-  int first_cap;
-  int first_chunks;
+// One launch of a selection: its mode, compiled capacity, chunk count and
+// arguments.  The first stage reads the scores (or block maxima); list
+// stages read the previous stage's (key, position) lists.
+struct Stage {
+  int mode;
+  int cap;
+  int nch;
+  StageArgs a;
 };
+constexpr int SEL_MAX_STAGES = 8;
 
-static StagePlan make_stages(const SelectArgs& sa, int64_t rows_len) {
-  StagePlan sp = {};
-  sp.p = plan_select(sa.Q, rows_len, sa.k);
-  sp.first.s = sa;
-  if (sp.p.n_stages == 1) {
-    sp.first_cap = fit_cap(rows_len);
-    sp.first.chunk = sp.first_cap;
-    sp.first.out_key = nullptr;
-    sp.first_chunks = 1;
-    return sp;
+static int make_stages(int first_mode, const SelectArgs& sa, int64_t rows_len, Stage* st) {
+  const SelectPlan p = plan_select(sa.Q, rows_len, sa.k);
+  Stage& f = st[0];
+  f = Stage{};
+  f.mode = first_mode;
+  f.a.s = sa;
+  if (p.n_stages == 1) {
+    f.cap = fit_cap(rows_len);
+    f.a.chunk = f.cap;
+    f.a.out_key = nullptr;
+    f.nch = 1;
+    return 1;
   }
   uint8_t* ws = (uint8_t*)sa.workspace;
-  const size_t list_bytes = (size_t)sa.Q * (size_t)sp.p.ws_list_max * 4u;
-  sp.first.chunk = sp.p.chunk1;
-  sp.first.out_key = (uint32_t*)ws;
-  sp.first.out_pos = (int32_t*)(ws + list_bytes);
-  sp.first.out_stride = sp.p.list_len[0];
-  sp.first_cap = fit_cap(sp.p.chunk1);
-  sp.first_chunks = sp.p.n_chunks1;
-  return sp;
-}
-
-static hipError_t run_list_stages(const StagePlan& sp, const SelectArgs& sa, hipStream_t s) {
-  if (sp.p.n_stages == 1) return hipSuccess;
-  uint8_t* ws = (uint8_t*)sa.workspace;
-  const size_t list_bytes = (size_t)sa.Q * (size_t)sp.p.ws_list_max * 4u;
+  const size_t list_bytes = (size_t)sa.Q * (size_t)p.ws_list_max * 4u;
   uint32_t* key_buf[2] = {(uint32_t*)ws, (uint32_t*)(ws + 2 * list_bytes)};
   int32_t* pos_buf[2] = {(int32_t*)(ws + list_bytes), (int32_t*)(ws + 3 * list_bytes)};
+  f.a.chunk = p.chunk1;
+  f.a.out_key = key_buf[0];
+  f.a.out_pos = pos_buf[0];
+  f.a.out_stride = p.list_len[0];
+  f.cap = fit_cap(p.chunk1);
+  f.nch = p.n_chunks1;
   int cur = 0;
-  for (int st = 1; st < sp.p.n_stages; ++st) {
-    StageArgs b = {};
-    b.s = sa;
-    b.in_key = key_buf[cur];
-    b.in_pos = pos_buf[cur];
-    b.in_len = sp.p.list_len[st - 1];
-    const bool last = (st == sp.p.n_stages - 1);
-    int nch, cap;
-    if (last) {
-      cap = fit_cap(b.in_len);
-      b.chunk = cap;
-      b.out_key = nullptr;
-      nch = 1;
+  for (int i = 1; i < p.n_stages; ++i) {
+    Stage& b = st[i];
+    b = Stage{};
+    b.mode = SEL_LIST;
+    b.a.s = sa;
+    b.a.in_key = key_buf[cur];
+    b.a.in_pos = pos_buf[cur];
+    b.a.in_len = p.list_len[i - 1];
+    if (i == p.n_stages - 1) {
+      b.cap = min(fit_cap(b.a.in_len), SEL_CAP_LIST);
+      b.a.chunk = fit_cap(b.a.in_len);
+      b.a.out_key = nullptr;
+      b.nch = 1;
     } else {
-      cap = SEL_CAP_LIST;
-      b.chunk = cap;
-      b.out_key = key_buf[cur ^ 1];
-      b.out_pos = pos_buf[cur ^ 1];
-      b.out_stride = sp.p.list_len[st];
-      nch = (int)((b.in_len + cap - 1) / cap);
+      b.cap = SEL_CAP_LIST;
+      b.a.chunk = SEL_CAP_LIST;
+      b.a.out_key = key_buf[cur ^ 1];
+      b.a.out_pos = pos_buf[cur ^ 1];
+      b.a.out_stride = p.list_len[i];
+      b.nch = (int)((b.a.in_len + SEL_CAP_LIST - 1) / SEL_CAP_LIST);
     }
-    const hipError_t e = launch_stage<SEL_LIST>(b, min(cap, SEL_CAP_LIST), nch, sa.Q, s);
-    if (e != hipSuccess) return e;
     cur ^= 1;
+  }
+  return p.n_stages;
+}
+
+static hipError_t launch_one(const Stage& st, int Q, hipStream_t s) {
+  switch (st.mode) {
+    case SEL_DENSE: return launch_stage<SEL_DENSE>(st.a, st.cap, st.nch, Q, s);
+    case SEL_POOL: return launch_stage<SEL_POOL>(st.a, st.cap, st.nch, Q, s);
+    case SEL_BLOCKMAX: return launch_stage<SEL_BLOCKMAX>(st.a, st.cap, st.nch, Q, s);
+    default: return launch_stage<SEL_LIST>(st.a, st.cap, st.nch, Q, s);
+  }
+}
+
+hipError_t launch_select(int mode, const SelectArgs& sa, int64_t rows_len, hipStream_t s) {
+  Stage st[SEL_MAX_STAGES];
+  const int n = make_stages(mode, sa, rows_len, st);
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = launch_one(st[i], sa.Q, s);
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }
 
-hipError_t launch_select(int mode, const SelectArgs& sa, int64_t rows_len, hipStream_t s) {
-  const StagePlan sp = make_stages(sa, rows_len);
-  const hipError_t e = launch_first(mode, sp.first, sp.first_cap, sp.first_chunks, sa.Q, s);
-  if (e != hipSuccess) return e;
-  return run_list_stages(sp, sa, s);
+// Paired launches: the first selection's stage in grid columns [0, n1), the
+// second's after it.  The first side is the dense top-k (DENSE first, then
+// LIST stages), the second the block candidates (BLOCKMAX, then LIST).
+template <int M1, int C1, int M2, int C2>
+static void launch_pair_k(const Stage& x, const Stage& y, int Q, hipStream_t s) {
+  const dim3 grid(x.nch + y.nch, Q), block(SEL_THREADS);
+  hipLaunchKernelGGL((select_pair_kernel<M1, C1, M2, C2>), grid, block, 0, s, x.a, y.a, x.nch);
 }
 
-template <int C1, int C2>
-static void launch_pair(const StagePlan& t1, const StagePlan& t2, int Q, hipStream_t s) {
-  const dim3 grid(t1.first_chunks + t2.first_chunks, Q), block(SEL_THREADS);
-  hipLaunchKernelGGL((select_pair_kernel<SEL_DENSE, C1, SEL_BLOCKMAX, C2>), grid, block, 0, s,
-                     t1.first, t2.first, t1.first_chunks);
+template <int M1, int C1, int M2>
+static void pair_c2(const Stage& x, const Stage& y, int Q, hipStream_t s) {
+  if (y.cap <= 4096) launch_pair_k<M1, C1, M2, 4096>(x, y, Q, s);
+  else if (y.cap <= 16384 || M2 == SEL_LIST) launch_pair_k<M1, C1, M2, 16384>(x, y, Q, s);
+  else launch_pair_k<M1, C1, M2, (M2 == SEL_LIST ? 16384 : SEL_CAP)>(x, y, Q, s);
 }
 
-template <int C1>
-static void launch_pair_c2(const StagePlan& t1, const StagePlan& t2, int Q, hipStream_t s) {
-  if (t2.first_cap <= 4096) launch_pair<C1, 4096>(t1, t2, Q, s);
-  else if (t2.first_cap <= 16384) launch_pair<C1, 16384>(t1, t2, Q, s);
-  else launch_pair<C1, SEL_CAP>(t1, t2, Q, s);
+template <int M1, int M2>
+static void pair_c1(const Stage& x, const Stage& y, int Q, hipStream_t s) {
+  if (x.cap <= 4096) pair_c2<M1, 4096, M2>(x, y, Q, s);
+  else if (x.cap <= 16384 || M1 == SEL_LIST) pair_c2<M1, 16384, M2>(x, y, Q, s);
+  else pair_c2<M1, (M1 == SEL_LIST ? 16384 : SEL_CAP), M2>(x, y, Q, s);
+}
+
+static hipError_t launch_pair(const Stage& x, const Stage& y, int Q, hipStream_t s) {
+  const bool l1 = x.mode == SEL_LIST, l2 = y.mode == SEL_LIST;
+  if (!l1 && !l2) pair_c1<SEL_DENSE, SEL_BLOCKMAX>(x, y, Q, s);
+  else if (!l1 && l2) pair_c1<SEL_DENSE, SEL_LIST>(x, y, Q, s);
+  else if (l1 && !l2) pair_c1<SEL_LIST, SEL_BLOCKMAX>(x, y, Q, s);
+  else pair_c1<SEL_LIST, SEL_LIST>(x, y, Q, s);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, const SelectArgs& blocks,
                                   int64_t blocks_len, hipStream_t s) {
-  const StagePlan t1 = make_stages(topk, topk_len);
-  const StagePlan t2 = make_stages(blocks, blocks_len);
-  // first stages of both selections share one launch; list stages follow
-  if (t1.first_cap <= 4096) launch_pair_c2<4096>(t1, t2, topk.Q, s);
-  else if (t1.first_cap <= 16384) launch_pair_c2<16384>(t1, t2, topk.Q, s);
-  else launch_pair_c2<SEL_CAP>(t1, t2, topk.Q, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  e = run_list_stages(t2, blocks, s);
-  if (e != hipSuccess) return e;
-  return run_list_stages(t1, topk, s);
+  Stage t[SEL_MAX_STAGES], b[SEL_MAX_STAGES];
+  const int nt = make_stages(SEL_DENSE, topk, topk_len, t);
+  const int nb = make_stages(SEL_BLOCKMAX, blocks, blocks_len, b);
+  // The two stage sequences are aligned at their ends, so the shorter one
+  // runs beside the longer one's last stages (the final stages are the
+  // single-workgroup-per-row ones that leave most of the chip idle).
+  const int n = max(nt, nb);
+  for (int j = 0; j < n; ++j) {
+    const int it = j - (n - nt), ib = j - (n - nb);
+    hipError_t e;
+    if (it >= 0 && ib >= 0) e = launch_pair(t[it], b[ib], topk.Q, s);
+    else if (it >= 0) e = launch_one(t[it], topk.Q, s);
+    else e = launch_one(b[ib], topk.Q, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace csa2

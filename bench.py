@@ -125,7 +125,7 @@ STAGE_KERNELS = {
     "block_candidates": ("select_kernel<2,",),
     "topk_dense": ("select_kernel<0,", "select_kernel<3,"),
     "topk_pool": ("select_kernel<1,",),
-    "topk_and_blocks": ("select_pair_kernel", "select_kernel<3,"),
+    "topk_and_blocks": ("select_pair_kernel", "select_kernel<0,", "select_kernel<2,", "select_kernel<3,"),
     "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_combine_kernel", "sparse_attn_f32_kernel"),
 }
 CALIB_KERNEL = "__amd_rocclr_copyBuffer"
@@ -194,9 +194,15 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, workload, comma
 
     src = _source_hash()
     for stage, pats in STAGE_KERNELS.items():
-        names = [n for n in per_kernel_bytes if any(p in n for p in pats)]
-        if not names:
+        # a stage is present when its first kernel is (list-stage kernels are
+        # shared between stages)
+        if not any(pats[0] in n for n in per_kernel_bytes):
             continue
+        # with the shared-launch call the separate-call stages do not occur
+        if stage in ("topk_dense", "block_candidates") and any(
+                "select_pair_kernel" in n for n in per_kernel_bytes):
+            continue
+        names = [n for n in per_kernel_bytes if any(p in n for p in pats)]
         rec = {"stage": stage, "workload": workload, "kernels": names,
                "hbm_bytes_per_launch": sum(per_kernel_bytes[n] for n in names),
                "rocprof_avg_us": {n: avg_us.get(n) for n in names},

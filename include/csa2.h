@@ -183,7 +183,7 @@ size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k);
 
 /*
  * csa2_topk_and_block_candidates — a Full layer's own top-k and the block
- * candidate pool it hands to the Reuse layers that follow, from the one set
+ * candidate pool it hands to the Reindex layers that follow, from the one set
  * of dense scores ([CSA2] "hierarchical sparse indexer", recall step: the
  * first Full layer picks its own top-k and the candidate blocks from one
  * scoring of every visible position).  The result equals
@@ -195,7 +195,8 @@ size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k);
  * two calls; scores is required (the top-k reads it) and q_pos is required.
  *   workspace at least csa2_topk_and_block_candidates_workspace_size(Q,
  *             n_cols, k, block_size, n_blocks) bytes, 16-byte aligned.
- *   Supported: the union of both calls' limits.
+ *   Supported: within both calls' limits (1 <= k <= 2048, n_blocks <= 4096,
+ *             block_size a power of two <= 64, ratio 1 or 2).
  */
 int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
                                    const float* block_max, int64_t block_max_stride,

@@ -31,6 +31,11 @@ HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 ATTN_BYTES_PER_QUERY = 512 * 320 + 128 * 528 + 65536 + 65536 + 2048   # 364,544
 INDEX_BYTES_PER_KEY = 128 + 4 + 4                                       # key + scale + score
+INDEX_BYTES_PER_KEY_FP4 = 64 + 8 + 4                                    # E2M1 key + 8 E4M3 scales + score
+
+
+def _index_bytes(wl):
+    return INDEX_BYTES_PER_KEY_FP4 if getattr(wl, "k_fmt", "fp8") == "fp4s16" else INDEX_BYTES_PER_KEY
 SCORE_BYTES = 4
 
 
@@ -81,9 +86,9 @@ def _stage_work(run, stage):
     if stage == "index_scores_dense":
         # plus the fused block maxima (4 B per block) when the step emits them
         extra = 4.0 / wl.block_size if run.fuse_block_max and any(run.needs_pool) else 0.0
-        return float(nvis.sum().item()) * (INDEX_BYTES_PER_KEY + extra), int(nvis.sum().item())
+        return float(nvis.sum().item()) * (_index_bytes(wl) + extra), int(nvis.sum().item())
     if stage == "index_scores_pool":
-        return float(wl.Q * run.pool_cols) * INDEX_BYTES_PER_KEY, wl.Q * run.pool_cols
+        return float(wl.Q * run.pool_cols) * _index_bytes(wl), wl.Q * run.pool_cols
     if stage == "block_candidates" and run.fuse_block_max:
         nblk = (nvis + wl.block_size - 1) // wl.block_size
         return float(nblk.sum().item()) * SCORE_BYTES, int(nvis.sum().item())
@@ -288,7 +293,8 @@ def cpu_baseline(wl, n_sample):
     for j, t in enumerate(sample):
         b = int(q_seq[t])
         kc, ks, mk = inputs[b]
-        k_rows = oracle.decode_e4m3_rows(kc, ks)
+        k_rows = (oracle.decode_fp4s16_rows(kc, ks) if getattr(wl, "k_fmt", "fp8") == "fp4s16"
+                  else oracle.decode_e4m3_rows(kc, ks))
         main_rows = oracle.decode_fp4_records(mk)
         pos1, seq0, base0 = np.array([q_pos[t]]), np.array([0]), np.array([0])
         n = int(oracle.visible_count(pos1, wl.ratio)[0])
@@ -450,6 +456,8 @@ def main():
         "config": {"workload": args.workload, "batch": wl.Q, "ctx_entries": wl.max_cols(),
                    "ratio": wl.ratio, "layers": [l.mode for l in wl.layers],
                    "topk": wl.topk, "pool_blocks": wl.n_blocks, "block_size": wl.block_size,
+                   "index_k_format": ("e2m1+e4m3/16" if getattr(wl, "k_fmt", "fp8") == "fp4s16"
+                                      else "e4m3+f32/row"),
                    "input_copies": len(runs), "block_candidates_overlapped": bool(args.overlap_blocks),
                    "full_layer_selections": ("separate" if args.separate_select or args.overlap_blocks
                                              else "shared launch")},

@@ -54,8 +54,12 @@ typedef enum {
     CSA2_F32 = 0,       /* IEEE binary32 */
     CSA2_BF16 = 1,      /* bfloat16 */
     CSA2_FP8_E4M3 = 2,  /* OCP FP8 E4M3FN codes, one byte per element, fp32 scales */
-    CSA2_FP4_E2M1 = 3   /* OCP FP4 E2M1 codes, two per byte (element 2i in the low
+    CSA2_FP4_E2M1 = 3,  /* OCP FP4 E2M1 codes, two per byte (element 2i in the low
                            nibble of byte i), one fp32 scale per 32 elements */
+    CSA2_FP4_E2M1_E4M3S16 = 4  /* E2M1 codes as above with one OCP E4M3 scale byte
+                                  per 16 elements: the pages' FP4 cache format
+                                  ([REPORT] section 6: E2M1 elements, an E4M3 scale
+                                  per 16 channels, no second-level scale) */
 } csa2_dtype;
 
 /*
@@ -63,11 +67,13 @@ typedef enum {
  * (const char*)data + r * row_stride; for quantized dtypes its scales start
  * at scale + r * scale_stride (in floats) and element e of the row decodes
  * to code(e) * scale[e / group], with group = 128 for FP8 index rows and SWA
- * rows and group = 32 for FP4 main-KV rows.  A record layout (codes followed
+ * rows and group = 32 for FP4 main-KV rows.  For CSA2_FP4_E2M1_E4M3S16 the
+ * scales are E4M3 bytes: `scale` points to bytes (cast to const float*),
+ * scale_stride counts bytes and group = 16.  A record layout (codes followed
  * by scales in one row) is described by pointing `scale` into the first
  * record.  `scale` is NULL for F32 and BF16.
  * Alignment: data and row_stride multiples of 16 bytes; scale and
- * scale_stride multiples of 4 bytes / 1 float.
+ * scale_stride multiples of 4 bytes (1 float, or 4 E4M3 bytes).
  */
 typedef struct {
     const void* data;
@@ -91,8 +97,13 @@ typedef struct {
  *   q_idx     rows = Q * H_I (row t*H_I + h is q[t, h]), dim d_I.
  *             FP8_E4M3 with one scale per row, or F32.
  *   w         [Q, H_I] contiguous gates, w_dtype BF16 or F32.
- *   k_idx     rows = all entries of all sequences, dim d_I; same dtype as
- *             q_idx (FP8_E4M3 with one scale per row, or F32).
+ *   k_idx     rows = all entries of all sequences, dim d_I.  With FP8 q_idx:
+ *             FP8_E4M3 with one scale per row, or FP4_E2M1_E4M3S16 (the
+ *             pages' FP4 index K: 64 code bytes per row, row_stride a
+ *             multiple of 16, and 8 E4M3 scale bytes per row at
+ *             scale + r * scale_stride bytes; those scales enter the dot
+ *             products, and the dequantized keys are exact in f16).  With
+ *             F32 q_idx: F32.
  *   seq_base  [B] int64: first k_idx row of each sequence.
  *   q_seq     [Q] int32: sequence of each query (0 <= q_seq < B).
  *   q_pos     [Q] int32: token position of each query (>= 0).

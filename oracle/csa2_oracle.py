@@ -93,6 +93,20 @@ def decode_fp4_records(rec):
     return E2M1_TABLE[codes] * np.repeat(scale, 32, axis=1)
 
 
+def decode_fp4s16_rows(codes, scales):
+    """FP4 rows in the pages' cache format ([REPORT] section 6: E2M1 elements
+    with one E4M3 scale per 16 channels and no second-level scale):
+    codes [n, d/2] (element 2i in the low nibble of byte i) and E4M3 scale
+    bytes [n, d/16] -> float64 [n, d]."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    n, half = codes.shape
+    e = np.empty((n, 2 * half), dtype=np.uint8)
+    e[:, 0::2] = codes & 0xF
+    e[:, 1::2] = codes >> 4
+    return E2M1_TABLE[e] * np.repeat(E4M3_TABLE[scales], 16, axis=1)
+
+
 def decode_swa_records(rec):
     """528-byte SWA records [n, 528] -> float64 [n, 512]: 512 E4M3 codes, then
     4 little-endian fp32 scales, one per 128 elements."""

@@ -12,6 +12,11 @@ report reading, section 6 on the FP4 main KV; DSA page, "two KV caches"):
   [256 B codes | 16 x fp32 scales].  scale = amax / 6.
 * SWA KV: FP8 E4M3FN codes with one fp32 scale per 128 elements, packed as a
   528-byte record [512 B codes | 4 x fp32 scales].
+* FP4 rows with E4M3 scales (the pages' own cache format: V4.1-Flash report
+  reading, section 6 -- E2M1 elements, one E4M3 scale per 16 channels, no
+  second-level scale): codes [n, d / 2] (two per byte, as above) and scale
+  bytes [n, d / 16].  scale = amax / 6 rounded to E4M3 (1.0 when amax = 0),
+  then each element rounds onto the E2M1 grid of value / scale, saturating.
 * bf16: round-to-nearest-even truncation of fp32.
 
 Every encoder rounds to nearest, ties to even, and saturates at the format's
@@ -71,6 +76,21 @@ def encode_fp4_records(x):
     rec[:, :256] = packed
     rec[:, 256:] = scale.contiguous().view(torch.uint8).reshape(n, 64)
     return rec
+
+
+def encode_fp4s16_rows(x):
+    """fp32 [n, d] -> (u8 codes [n, d // 2], u8 E4M3 scales [n, d // 16])."""
+    x = x.to(torch.float32)
+    n, d = x.shape
+    g = x.reshape(n, d // 16, 16)
+    amax = g.abs().amax(dim=2)
+    s = torch.where(amax > 0, amax / E2M1_MAX, torch.ones_like(amax))
+    s8 = s.clamp(max=E4M3_MAX).to(torch.float8_e4m3fn)
+    sdec = s8.to(torch.float32)
+    y = (g / sdec.unsqueeze(2)).clamp_(-E2M1_MAX, E2M1_MAX).reshape(n, d)
+    c = _e2m1_codes(y)
+    packed = (c[:, 0::2] | (c[:, 1::2] << 4)).contiguous()
+    return packed, s8.view(torch.uint8).contiguous()
 
 
 def encode_swa_records(x):

@@ -27,11 +27,13 @@ import math
 import numpy as np
 import torch
 
-from .formats import (encode_e4m3_rows, encode_fp4_records, encode_swa_records,
+from .formats import (encode_e4m3_rows, encode_fp4_records, encode_fp4s16_rows, encode_swa_records,
                       encode_bf16)
 
 CONFIG_NAMES = ("tiny_full_fp32", "decode_128k", "prefill_m2_chunk",
                 "reindex_1m", "decoder_group_256k")
+# further workloads of the same shapes in other cache formats
+EXTRA_WORKLOADS = ("decode_128k_fp4k",)
 
 H_IDX, D_IDX = 32, 128
 H_ATT, D_ATT = 64, 512
@@ -83,8 +85,8 @@ class Workload:
     seq_base: torch.Tensor         # [B] int64 first row of each sequence
     q_seq: torch.Tensor            # [Q] int32
     q_pos: torch.Tensor            # [Q] int32 token position of each query
-    k_idx: torch.Tensor            # [sum N, 128] u8 E4M3 codes, or fp32
-    k_scale: torch.Tensor          # [sum N] fp32 or None
+    k_idx: torch.Tensor            # [sum N, 128] u8 E4M3 codes ([sum N, 64] E2M1 pairs), or fp32
+    k_scale: torch.Tensor          # [sum N] fp32 ([sum N, 8] u8 E4M3 for E2M1 keys), or None
     main_kv: torch.Tensor          # [sum N, 320] u8 records, or [sum N, 512] fp32
     swa_base: torch.Tensor         # [B] int64 first SWA row of each sequence
     swa_pos0: torch.Tensor         # [B] int32 token position of that row
@@ -94,6 +96,7 @@ class Workload:
     n_blocks: int = N_BLOCKS
     window: int = WINDOW
     softmax_scale: float = 1.0 / math.sqrt(D_ATT)
+    k_fmt: str = "fp8"             # index-K format: "fp8" (E4M3 + fp32 per row) or "fp4s16"
 
     @property
     def Q(self):
@@ -131,17 +134,20 @@ def _chunked(total, fn):
     return torch.cat(parts, 0) if len(parts) > 1 else parts[0]
 
 
-def _index_keys(seed, total, quantized, device):
+def _index_keys(seed, total, quantized, device, k_fmt="fp8"):
     if not quantized:
         return _randint(-4, 4, (total, D_IDX), seed, _T_KIDX, 0, device), None
+    enc = encode_fp4s16_rows if k_fmt == "fp4s16" else encode_e4m3_rows
 
     def one(c, n):
-        return encode_e4m3_rows(_randn((n, D_IDX), seed, _T_KIDX, c, device))
+        return enc(_randn((n, D_IDX), seed, _T_KIDX, c, device))
     parts = []
     for c, r0 in enumerate(range(0, total, CHUNK_ROWS)):
         parts.append(one(c, min(CHUNK_ROWS, total - r0)))
     codes = torch.cat([p[0] for p in parts], 0)
-    scale = torch.cat([p[1] for p in parts], 0).reshape(total)
+    scale = torch.cat([p[1] for p in parts], 0)
+    if k_fmt != "fp4s16":
+        scale = scale.reshape(total)
     return codes, scale
 
 
@@ -221,12 +227,12 @@ def _decode_layout(n_entries, q_per_seq, ratio, device, positions=None):
 
 def mini_workload(seed, n_entries, q_per_seq=1, ratio=1, quantized=True,
                   modes=("full",), device="cpu", positions=None, topk=TOPK,
-                  n_blocks=N_BLOCKS, block_size=BLOCK):
+                  n_blocks=N_BLOCKS, block_size=BLOCK, k_fmt="fp8"):
     """A small workload of the same structure, for parity tests."""
     seq_base, q_seq, q_pos, swa_base, swa_pos0, swa_total = _decode_layout(
         n_entries, q_per_seq, ratio, device, positions)
     total = int(sum(n_entries))
-    k_idx, k_scale = _index_keys(seed, total, quantized, device)
+    k_idx, k_scale = _index_keys(seed, total, quantized, device, k_fmt)
     main = _main_kv_gauss(seed, total, quantized, device)
     Q = int(q_pos.shape[0])
     layers = [_layer(seed, li, m, Q, swa_total, quantized, device,
@@ -236,7 +242,8 @@ def mini_workload(seed, n_entries, q_per_seq=1, ratio=1, quantized=True,
                     n_entries=list(n_entries), seq_base=seq_base, q_seq=q_seq,
                     q_pos=q_pos, k_idx=k_idx, k_scale=k_scale, main_kv=main,
                     swa_base=swa_base, swa_pos0=swa_pos0, layers=layers,
-                    topk=topk, n_blocks=n_blocks, block_size=block_size)
+                    topk=topk, n_blocks=n_blocks, block_size=block_size,
+                    k_fmt=k_fmt if quantized else "fp8")
 
 
 def _prefill_m2(seed, device):
@@ -276,6 +283,11 @@ def make_workload(name, device="cpu", seed_offset=0):
                           modes=("full", "reindex"), device=device)
     elif name == "prefill_m2_chunk":
         w = _prefill_m2(2 + o, device)
+    elif name == "decode_128k_fp4k":
+        # decode_128k with index K in the pages' FP4 format (E2M1 + an E4M3
+        # scale per 16 dims, 72 B per key instead of 132)
+        w = mini_workload(1 + o, [131072] * 8, q_per_seq=1, ratio=1, quantized=True,
+                          modes=("full", "reindex"), device=device, k_fmt="fp4s16")
     elif name == "reindex_1m":
         w = mini_workload(3 + o, [1 << 20] * 2, q_per_seq=1, ratio=1, quantized=True,
                           modes=("full", "reindex"), device=device)
@@ -285,6 +297,6 @@ def make_workload(name, device="cpu", seed_offset=0):
                                  "reindex", "reuse", "reuse", "reuse"),
                           device=device)
     else:
-        raise ValueError(f"unknown workload {name!r}; known: {CONFIG_NAMES}")
+        raise ValueError(f"unknown workload {name!r}; known: {CONFIG_NAMES + EXTRA_WORKLOADS}")
     w.name = name
     return w

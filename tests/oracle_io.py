@@ -28,6 +28,8 @@ def index_k_rows(wl, rows=None):
     k = wl.k_idx if rows is None else wl.k_idx[rows]
     if wl.quantized:
         s = wl.k_scale if rows is None else wl.k_scale[rows]
+        if getattr(wl, "k_fmt", "fp8") == "fp4s16":
+            return oracle.decode_fp4s16_rows(_np(k), _np(s))
         return oracle.decode_e4m3_rows(_np(k), _np(s))
     return _np(k).astype(np.float64)
 

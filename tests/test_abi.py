@@ -149,6 +149,28 @@ def test_topk_and_block_candidates_rejects():
     assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, None, 0, 0, None) == tsl.CSA2_OK
 
 
+def test_index_scores_fp4_key_checks():
+    """FP4 keys with E4M3 scales: only beside FP8 queries, scales 4-byte aligned
+    with a stride of at least 8 bytes."""
+    lib = tsl.load()
+    q = tsl.csa2_rows(FAKE, FAKE, 128, 1, tsl.CSA2_FP8_E4M3)
+    k_ok = tsl.csa2_rows(FAKE, FAKE, 64, 8, tsl.CSA2_FP4_E2M1_E4M3S16)
+
+    def call(qr, kr, Q=1):
+        return lib.csa2_index_scores(ctypes.byref(qr), FAKE, tsl.CSA2_BF16, ctypes.byref(kr), FAKE,
+                                     FAKE, FAKE, 1, None, 0, 8, FAKE, 64, 64, None, 0, Q, 32, 128,
+                                     None)
+    assert call(q, k_ok, Q=0) == tsl.CSA2_OK
+    assert call(q, tsl.csa2_rows(FAKE, FAKE + 2, 64, 8, tsl.CSA2_FP4_E2M1_E4M3S16)) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert call(q, tsl.csa2_rows(FAKE, FAKE, 64, 4, tsl.CSA2_FP4_E2M1_E4M3S16)) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert call(q, tsl.csa2_rows(FAKE, FAKE, 48, 8, tsl.CSA2_FP4_E2M1_E4M3S16)) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    qf = tsl.csa2_rows(FAKE, None, 512, 0, tsl.CSA2_F32)
+    assert call(qf, k_ok) == tsl.CSA2_ERR_UNSUPPORTED
+
+
 def test_workspace_sizes():
     lib = tsl.load()
     assert lib.csa2_topk_workspace_size(64, 32768, 512) == 0      # one chunk per row

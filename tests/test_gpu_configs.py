@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 SAMPLES = {"tiny_full_fp32": None, "decode_128k": [0, 5], "prefill_m2_chunk": [0, 1, 2047, 4095],
-           "reindex_1m": [0, 1], "decoder_group_256k": [0, 37]}
+           "reindex_1m": [0, 1], "decoder_group_256k": [0, 37], "decode_128k_fp4k": [2, 7]}
 
 
 @pytest.fixture(autouse=True)
@@ -50,7 +50,7 @@ def _gathered_main(wl, b, idx_row, n_vis):
     return oracle_io.main_rows(wl, rows), compact
 
 
-@pytest.mark.parametrize("name", list(synth.CONFIG_NAMES))
+@pytest.mark.parametrize("name", list(synth.CONFIG_NAMES) + list(synth.EXTRA_WORKLOADS))
 def test_config_parity(name):
     print(f"[case] config {name}", flush=True)
     gen_dev = "cpu" if name == "tiny_full_fp32" else DEV

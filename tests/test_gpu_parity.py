@@ -36,13 +36,15 @@ def _announce(msg):
 # ---------------------------------------------------------------------------
 # index scores
 
+@pytest.mark.parametrize("k_fmt", ["fp8", "fp4s16"])
 @pytest.mark.parametrize("ratio", [1, 2])
-def test_index_scores_fp8_ragged(ratio):
+def test_index_scores_fp8_ragged(ratio, k_fmt):
     n_entries = [5000, 7777, 1, 3, 2049]
     positions = [[n * ratio - 1, n * ratio - 2, 17] for n in n_entries[:2]] + \
                 [[ratio - 1], [3 * ratio - 1, 0], [2049 * ratio - 1]]
-    _announce(f"index_scores fp8 ratio={ratio}")
-    wl = synth.mini_workload(10 + ratio, n_entries, ratio=ratio, positions=positions).to(DEV)
+    _announce(f"index_scores fp8 ratio={ratio} keys={k_fmt}")
+    wl = synth.mini_workload(10 + ratio, n_entries, ratio=ratio, positions=positions,
+                             k_fmt=k_fmt).to(DEV)
     run = LayerRunner(wl)
     run.index_scores(0, pool=False)
     torch.cuda.synchronize()
@@ -64,8 +66,9 @@ def _prefill_positions(n_tok, n_q, seed):
     return early + tail
 
 
+@pytest.mark.parametrize("k_fmt", ["fp8", "fp4s16"])
 @pytest.mark.parametrize("case", ["one_sequence", "mixed_tiles"])
-def test_index_scores_prefill_fp8(case):
+def test_index_scores_prefill_fp8(case, k_fmt):
     """Many queries (at least the query-tiled kernel's threshold): a ragged
     count, causal m = 2 rows of different lengths, and, in the mixed case,
     16-query tiles that straddle sequences."""
@@ -76,8 +79,8 @@ def test_index_scores_prefill_fp8(case):
         n_entries = [3000, 2100, 4100]
         positions = [_prefill_positions(2 * n, nq, 2 + i)
                      for i, (n, nq) in enumerate(zip(n_entries, (101, 90, 83)))]
-    _announce(f"index_scores prefill fp8 {case}")
-    wl = synth.mini_workload(60, n_entries, ratio=2, positions=positions).to(DEV)
+    _announce(f"index_scores prefill fp8 {case} keys={k_fmt}")
+    wl = synth.mini_workload(60, n_entries, ratio=2, positions=positions, k_fmt=k_fmt).to(DEV)
     assert wl.Q >= 256
     run = LayerRunner(wl)
     run.index_scores(0, pool=False, block_max=True)
@@ -114,10 +117,11 @@ def test_index_scores_f32_exact():
     assert np.array_equal(gpu, ref)
 
 
-def test_pool_scores_fp8():
-    _announce("index_scores pool mode")
+@pytest.mark.parametrize("k_fmt", ["fp8", "fp4s16"])
+def test_pool_scores_fp8(k_fmt):
+    _announce(f"index_scores pool mode keys={k_fmt}")
     wl = synth.mini_workload(4, [9000, 4000], q_per_seq=2, modes=("reindex",),
-                             n_blocks=300).to(DEV)
+                             n_blocks=300, k_fmt=k_fmt).to(DEV)
     rng = np.random.default_rng(4)
     Q = wl.Q
     cand = np.full((Q, 300), -1, dtype=np.int32)

@@ -87,6 +87,32 @@ def test_swa_record_hand_decoded():
     assert np.count_nonzero(v) == 4
 
 
+def test_fp4s16_rows_hand_decoded():
+    """The pages' FP4 format: element 2i in the low nibble of byte i, E4M3
+    scale byte g covering elements 16g..16g+15."""
+    codes = np.zeros((1, 64), dtype=np.uint8)
+    scales = np.zeros((1, 8), dtype=np.uint8)
+    codes[0, 0] = 0x71        # element 0 = code 1 (0.5), element 1 = code 7 (6)
+    codes[0, 7] = 0xA3        # element 14 = code 3 (1.5), element 15 = code 0xA (-1)
+    codes[0, 8] = 0x0E        # element 16 = code 0xE (-4)
+    codes[0, 63] = 0x50       # element 127 = code 5 (3)
+    scales[0] = [0x40, 0x30, 0, 0, 0, 0, 0, 0x01]   # 2.0, 0.5, ..., 2^-9
+    v = oracle.decode_fp4s16_rows(codes, scales)[0]
+    assert v.shape == (128,)
+    assert v[0] == 1.0 and v[1] == 12.0 and v[14] == 3.0 and v[15] == -2.0
+    assert v[16] == -2.0 and v[127] == 3.0 * 2.0 ** -9
+    assert np.count_nonzero(v) == 6
+
+
+def test_fp4s16_values_are_exact_in_f16():
+    """Every finite E2M1 code times every finite E4M3 scale is an f16 value:
+    the kernels widen these rows to f16 without rounding."""
+    e2m1 = oracle.E2M1_TABLE
+    e4m3 = oracle.E4M3_TABLE[np.isfinite(oracle.E4M3_TABLE)]
+    prod = np.outer(e2m1, e4m3).ravel()
+    assert np.array_equal(prod.astype(np.float16).astype(np.float64), prod)
+
+
 def _nearest_grid_ok(x, decoded, grid):
     """decoded must be a nearest grid point of x (ties: either neighbour)."""
     dist = np.abs(x[..., None] - grid)
@@ -150,3 +176,19 @@ def test_generator_is_deterministic():
         assert torch.equal(x, y)
     c = synth.mini_workload(8, [100, 37], q_per_seq=2, quantized=True)
     assert not torch.equal(a.k_idx, c.k_idx)
+
+
+def test_generator_fp4s16_rows():
+    """Scale = amax/16-group / 6 rounded to E4M3; each element is a nearest
+    E2M1 point of value / decoded scale (saturating at 6)."""
+    x = torch.randn(48, 128, generator=torch.Generator().manual_seed(5))
+    codes, scales = synth.encode_fp4s16_rows(x)
+    assert codes.shape == (48, 64) and scales.shape == (48, 8)
+    amax = x.reshape(48, 8, 16).abs().amax(dim=2)
+    want = (amax / 6.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    assert torch.equal(scales, want)
+    sdec = oracle.E4M3_TABLE[scales.numpy()]
+    dec = oracle.decode_fp4s16_rows(codes.numpy(), scales.numpy())
+    y = (x.double().numpy().reshape(48, 8, 16) / sdec[:, :, None]).reshape(48, 128)
+    y = np.clip(y, -6.0, 6.0)
+    assert _nearest_grid_ok(y, dec / np.repeat(sdec, 16, axis=1), oracle.E2M1_TABLE)

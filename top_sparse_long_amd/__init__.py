@@ -14,7 +14,7 @@ import torch
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libcsa2.so")
 
 CSA2_OK, CSA2_ERR_INVALID_ARG, CSA2_ERR_UNSUPPORTED, CSA2_ERR_WORKSPACE, CSA2_ERR_HIP = 0, -1, -2, -3, -4
-CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1 = 0, 1, 2, 3
+CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1, CSA2_FP4_E2M1_E4M3S16 = 0, 1, 2, 3, 4
 
 EXPORTED = ("csa2_index_scores", "csa2_block_candidates", "csa2_block_candidates_workspace_size",
             "csa2_topk", "csa2_topk_workspace_size", "csa2_topk_and_block_candidates",
@@ -105,6 +105,15 @@ def rows_fp8(codes, scale):
     assert codes.dtype == torch.uint8 and codes.is_contiguous() and scale.dtype == torch.float32
     return csa2_rows(codes.data_ptr(), scale.data_ptr(), codes.shape[-1],
                      scale.stride(0) if scale.dim() else 1, CSA2_FP8_E4M3)
+
+
+def rows_fp4s16(codes, scales):
+    """E2M1 codes [n, dim / 2] (uint8, two per byte) with one E4M3 scale byte
+    per 16 elements [n, dim / 16] (uint8): the pages' FP4 cache format."""
+    assert codes.dtype == torch.uint8 and codes.is_contiguous()
+    assert scales.dtype == torch.uint8 and scales.dim() == 2
+    return csa2_rows(codes.data_ptr(), scales.data_ptr(), codes.shape[-1], scales.stride(0),
+                     CSA2_FP4_E2M1_E4M3S16)
 
 
 def rows_fp4_records(rec):

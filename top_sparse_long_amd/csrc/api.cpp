@@ -77,8 +77,10 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
   REQUIRE(d_I == 128, CSA2_ERR_UNSUPPORTED, "csa2_index_scores: d_I must be 128 (got %d)", d_I);
   REQUIRE(w_dtype == CSA2_BF16 || w_dtype == CSA2_F32, CSA2_ERR_UNSUPPORTED,
           "csa2_index_scores: gates must be BF16 or F32");
-  REQUIRE(q_idx->dtype == k_idx->dtype, CSA2_ERR_UNSUPPORTED,
-          "csa2_index_scores: q_idx and k_idx must share a dtype");
+  const bool k_fp4 = k_idx->dtype == CSA2_FP4_E2M1_E4M3S16;
+  REQUIRE(q_idx->dtype == k_idx->dtype || (q_idx->dtype == CSA2_FP8_E4M3 && k_fp4),
+          CSA2_ERR_UNSUPPORTED,
+          "csa2_index_scores: k_idx must share q_idx's dtype (or be FP4_E2M1_E4M3S16 with FP8 q_idx)");
   REQUIRE(score_stride >= n_cols && score_stride % 4 == 0, CSA2_ERR_INVALID_ARG,
           "csa2_index_scores: score_stride must be >= n_cols and a multiple of 4");
   REQUIRE(aligned(scores, 16), CSA2_ERR_INVALID_ARG, "csa2_index_scores: scores must be 16-byte aligned");
@@ -113,6 +115,7 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
   a.k_scale = k_idx->scale;
   a.k_row_stride = k_idx->row_stride;
   a.k_scale_stride = k_idx->scale_stride;
+  a.k_fp4 = k_fp4 ? 1 : 0;
   a.seq_base = seq_base;
   a.q_seq = q_seq;
   a.q_pos = q_pos;
@@ -131,8 +134,12 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
   if (q_idx->dtype == CSA2_FP8_E4M3) {
     REQUIRE(H_I == 32, CSA2_ERR_UNSUPPORTED, "csa2_index_scores: FP8 path needs H_I == 32 (got %d)", H_I);
     REQUIRE(q_idx->scale && k_idx->scale, CSA2_ERR_INVALID_ARG, "csa2_index_scores: FP8 rows need scales");
-    REQUIRE(q_idx->row_stride >= 128 && k_idx->row_stride >= 128, CSA2_ERR_INVALID_ARG,
-            "csa2_index_scores: FP8 row stride below 128 bytes");
+    REQUIRE(q_idx->row_stride >= 128 && k_idx->row_stride >= (k_fp4 ? 64 : 128), CSA2_ERR_INVALID_ARG,
+            "csa2_index_scores: row stride below the row's code bytes");
+    if (k_fp4)
+      REQUIRE(aligned(k_idx->scale, 4) && k_idx->scale_stride >= 8 && k_idx->scale_stride % 4 == 0,
+              CSA2_ERR_INVALID_ARG,
+              "csa2_index_scores: FP4 key scales need 4-byte alignment and a stride >= 8 bytes, multiple of 4");
     return hip_status(csa2::launch_index_scores_fp8(a, (hipStream_t)stream), "csa2_index_scores");
   }
   if (q_idx->dtype == CSA2_F32) {

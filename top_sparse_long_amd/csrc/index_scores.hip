@@ -92,6 +92,36 @@ __device__ __forceinline__ v8h fp8x8_to_f16(uint32_t lo, uint32_t hi) {
   return (v8h){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// 8 E2M1 codes (one dword, element 2i in the low nibble of byte i) times an
+// E4M3 scale already widened to f16 -> 8 f16 values, exactly: a code has at
+// most 2 significant bits and an E4M3 scale at most 4, so the product fits
+// f16's 11 (and 6 * 448 is far inside its range).
+__device__ __forceinline__ v8h fp4x8_to_f16(uint32_t x, _Float16 s) {
+  const v2h s2 = {s, s};
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * s2;
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * s2;
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * s2;
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s2;
+  return (v8h){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// The 16-dim groups j = 0..3 of a lane's 64 dims as B operands: FP8 codes in
+// raw[j] (16 bytes), or E2M1 codes in raw[j / 2][2 (j % 2)], raw[..][+1] with
+// the E4M3 scales of the four groups in one dword.
+template <bool K4>
+__device__ __forceinline__ void key_operands(const v4u raw[4], uint32_t scales, int j, v8h& b0, v8h& b1) {
+  if (K4) {
+    const v2h s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scales, 1.0f, false);
+    const v2h s23 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scales, 1.0f, true);
+    const _Float16 sj = (j == 0) ? s01[0] : (j == 1) ? s01[1] : (j == 2) ? s23[0] : s23[1];
+    b0 = fp4x8_to_f16(raw[j >> 1][2 * (j & 1)], sj);
+    b1 = fp4x8_to_f16(raw[j >> 1][2 * (j & 1) + 1], sj);
+  } else {
+    b0 = fp8x8_to_f16(raw[j][0], raw[j][1]);
+    b1 = fp8x8_to_f16(raw[j][2], raw[j][3]);
+  }
+}
+
 // ReLU of a float as one integer max: non-negative floats are non-negative
 // as int32, negative floats are negative (so they become +0).
 __device__ __forceinline__ float relu(float x) {
@@ -119,7 +149,7 @@ __device__ __forceinline__ float group_max(float m, int bs) {
   return m;
 }
 
-template <bool POOL, bool W_BF16>
+template <bool POOL, bool W_BF16, bool K4>
 __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexScoreArgs a) {
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -176,10 +206,19 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
       const int tcol = sc0 + (i * IS_WAVES + wave) * 32;
       S.pos[i] = (tcol < limit) ? column_position<POOL>(a, t, tcol + r, nvis) : -1;
       const int64_t row = base + max(S.pos[i], 0);
-      const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 64 * half);
+      if (K4) {
+        // 32 code bytes and the dword of the four E4M3 scales of this half
+        const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 32 * half);
+        S.raw[i][0] = src[0];
+        S.raw[i][1] = src[1];
+        S.ks[i] = __uint_as_float(
+            *(const uint32_t*)((const uint8_t*)a.k_scale + row * a.k_scale_stride + 4 * half));
+      } else {
+        const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 64 * half);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) S.raw[i][j] = src[j];
-      S.ks[i] = a.k_scale[row * a.k_scale_stride];
+        for (int j = 0; j < 4; ++j) S.raw[i][j] = src[j];
+        S.ks[i] = a.k_scale[row * a.k_scale_stride];
+      }
     }
   };
 
@@ -210,8 +249,8 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
         v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const v8h b0 = fp8x8_to_f16(S.raw[i][j][0], S.raw[i][j][1]);
-          const v8h b1 = fp8x8_to_f16(S.raw[i][j][2], S.raw[i][j][3]);
+          v8h b0, b1;
+          key_operands<K4>(S.raw[i], __float_as_uint(S.ks[i]), j, b0, b1);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[2 * j], b0, acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[2 * j + 1], b1, acc, 0, 0, 0);
         }
@@ -219,7 +258,9 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
 #pragma unroll
         for (int j = 0; j < 16; ++j) v = fmaf(gate[j], relu(acc[j]), v);
         v = add_half_swap(v);
-        sc = (S.pos[i] >= 0) ? v * S.ks[i] : -INFINITY;
+        // FP8 keys: the per-key scale multiplies the head sum; FP4 keys
+        // carry their scales inside the operands
+        sc = (S.pos[i] >= 0) ? (K4 ? v : v * S.ks[i]) : -INFINITY;
       }
       if (half == 0 && col < a.n_cols) out[col] = sc;
       if (!POOL && a.block_max) {
@@ -262,7 +303,7 @@ constexpr int PF_WAVES = 8;
 constexpr int PF_BLOCKS = 8;             // key blocks per workgroup
 constexpr int PF_RS = 272;               // LDS row stride of an f16 key row (bytes)
 
-template <bool W_BF16>
+template <bool W_BF16, bool K4>
 __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(IndexScoreArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][PF_KB * PF_RS];
   __shared__ float s_ks[2][PF_KB];
@@ -335,19 +376,29 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
       // rows past the last visible entry repeat it (masked later)
       const int col = min(blk * PF_KB + kk, max(maxvis - 1, 0));
       const int64_t row = base + col;
-      const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 64 * hh);
+      if (K4) {
+        const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 32 * hh);
+        kraw[0] = src[0];
+        kraw[1] = src[1];
+        kscale = __uint_as_float(
+            *(const uint32_t*)((const uint8_t*)a.k_scale + row * a.k_scale_stride + 4 * hh));
+      } else {
+        const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 64 * hh);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) kraw[j] = src[j];
-      kscale = a.k_scale[row * a.k_scale_stride];
+        for (int j = 0; j < 4; ++j) kraw[j] = src[j];
+        kscale = a.k_scale[row * a.k_scale_stride];
+      }
     };
     auto store_block = [&](int buf) {
       uint8_t* dst = s_k[buf] + kk * PF_RS + 128 * hh;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        *(v8h*)(dst + 32 * j) = fp8x8_to_f16(kraw[j][0], kraw[j][1]);
-        *(v8h*)(dst + 32 * j + 16) = fp8x8_to_f16(kraw[j][2], kraw[j][3]);
+        v8h b0, b1;
+        key_operands<K4>(kraw, __float_as_uint(kscale), j, b0, b1);
+        *(v8h*)(dst + 32 * j) = b0;
+        *(v8h*)(dst + 32 * j + 16) = b1;
       }
-      if (hh == 0) s_ks[buf][kk] = kscale;
+      if (hh == 0) s_ks[buf][kk] = K4 ? 1.0f : kscale;
     };
 
     if (maxvis > 0) {
@@ -458,33 +509,41 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(IndexScoreArgs a)
   }
 }
 
-hipError_t launch_index_scores_fp8(const IndexScoreArgs& a, hipStream_t s) {
-  if (!a.cand && a.Q >= PF_MIN_Q) {
-    // many queries: the query-tiled kernel shares every staged key block
-    dim3 grid((a.n_cols + PF_KB * PF_BLOCKS - 1) / (PF_KB * PF_BLOCKS), (a.Q + PF_Q - 1) / PF_Q);
-    if (a.w_bf16)
-      hipLaunchKernelGGL((index_scores_prefill_kernel<true>), grid, dim3(64 * PF_WAVES), 0, s, a);
-    else
-      hipLaunchKernelGGL((index_scores_prefill_kernel<false>), grid, dim3(64 * PF_WAVES), 0, s, a);
-    return hipGetLastError();
-  }
+template <bool W_BF16, bool K4>
+static void launch_prefill(const IndexScoreArgs& a, hipStream_t s) {
+  dim3 grid((a.n_cols + PF_KB * PF_BLOCKS - 1) / (PF_KB * PF_BLOCKS), (a.Q + PF_Q - 1) / PF_Q);
+  hipLaunchKernelGGL((index_scores_prefill_kernel<W_BF16, K4>), grid, dim3(64 * PF_WAVES), 0, s, a);
+}
+
+template <bool POOL, bool W_BF16, bool K4>
+static void launch_decode(const IndexScoreArgs& a, hipStream_t s) {
   // sub-chunks per workgroup: enough workgroups for about one resident
   // round, each streaming over a contiguous column range of one query
   IndexScoreArgs b = a;
   const int64_t subs = (a.n_cols + IS_SUB - 1) / IS_SUB;
   b.sub_per_wg = (int)std::max<int64_t>(1, (subs * a.Q + IS_RESIDENT_WGS - 1) / IS_RESIDENT_WGS);
   dim3 grid((unsigned)((subs + b.sub_per_wg - 1) / b.sub_per_wg), a.Q);
-  if (a.cand) {
-    if (a.w_bf16)
-      hipLaunchKernelGGL((index_scores_fp8_kernel<true, true>), grid, dim3(64 * IS_WAVES), 0, s, b);
-    else
-      hipLaunchKernelGGL((index_scores_fp8_kernel<true, false>), grid, dim3(64 * IS_WAVES), 0, s, b);
+  hipLaunchKernelGGL((index_scores_fp8_kernel<POOL, W_BF16, K4>), grid, dim3(64 * IS_WAVES), 0, s, b);
+}
+
+template <bool K4>
+static void launch_quant(const IndexScoreArgs& a, hipStream_t s) {
+  if (!a.cand && a.Q >= PF_MIN_Q) {
+    // many queries: the query-tiled kernel shares every staged key block
+    if (a.w_bf16) launch_prefill<true, K4>(a, s);
+    else launch_prefill<false, K4>(a, s);
+  } else if (a.cand) {
+    if (a.w_bf16) launch_decode<true, true, K4>(a, s);
+    else launch_decode<true, false, K4>(a, s);
   } else {
-    if (a.w_bf16)
-      hipLaunchKernelGGL((index_scores_fp8_kernel<false, true>), grid, dim3(64 * IS_WAVES), 0, s, b);
-    else
-      hipLaunchKernelGGL((index_scores_fp8_kernel<false, false>), grid, dim3(64 * IS_WAVES), 0, s, b);
+    if (a.w_bf16) launch_decode<false, true, K4>(a, s);
+    else launch_decode<false, false, K4>(a, s);
   }
+}
+
+hipError_t launch_index_scores_fp8(const IndexScoreArgs& a, hipStream_t s) {
+  if (a.k_fp4) launch_quant<true>(a, s);
+  else launch_quant<false>(a, s);
   return hipGetLastError();
 }
 

@@ -15,9 +15,11 @@ struct IndexScoreArgs {
   const void* w;             // [Q, H] gates
   int w_bf16;                // 1: bf16 gates, 0: fp32 gates
   const uint8_t* k;          // index-K rows
-  const float* k_scale;
+  const float* k_scale;      // FP8 keys: one fp32 scale per row
   int64_t k_row_stride;
-  int64_t k_scale_stride;
+  int64_t k_scale_stride;    // floats (FP8 keys) or bytes (FP4 keys)
+  int k_fp4;                 // 1: E2M1 keys (64 B per row), one E4M3 scale byte per 16 dims at
+                             //    (const uint8_t*)k_scale + row * k_scale_stride
   const int64_t* seq_base;
   const int32_t* q_seq;
   const int32_t* q_pos;

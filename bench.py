@@ -30,6 +30,7 @@ METRIC = "index keys scored/s + sparse-attn queries/s at 128K ctx; % HBM/MFMA ro
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
 ATTN_BYTES_PER_QUERY = 512 * 320 + 128 * 528 + 65536 + 65536 + 2048   # 364,544
+ATTN_BYTES_PER_QUERY_S16 = 512 * 288 + 128 * 528 + 65536 + 65536 + 2048   # the 288-B record
 INDEX_BYTES_PER_KEY = 128 + 4 + 4                                       # key + scale + score
 INDEX_BYTES_PER_KEY_FP4 = 64 + 8 + 4                                    # E2M1 key + 8 E4M3 scales + score
 
@@ -103,7 +104,9 @@ def _stage_work(run, stage):
     if stage == "topk_pool":
         return float(wl.Q * run.pool_cols) * SCORE_BYTES, wl.Q * run.pool_cols
     if stage == "sparse_attn":
-        return float(wl.Q) * ATTN_BYTES_PER_QUERY, wl.Q
+        per_q = (ATTN_BYTES_PER_QUERY_S16 if getattr(wl, "main_fmt", "fp4") == "fp4s16"
+                 else ATTN_BYTES_PER_QUERY)
+        return float(wl.Q) * per_q, wl.Q
     raise KeyError(stage)
 
 
@@ -295,7 +298,8 @@ def cpu_baseline(wl, n_sample):
         kc, ks, mk = inputs[b]
         k_rows = (oracle.decode_fp4s16_rows(kc, ks) if getattr(wl, "k_fmt", "fp8") == "fp4s16"
                   else oracle.decode_e4m3_rows(kc, ks))
-        main_rows = oracle.decode_fp4_records(mk)
+        main_rows = (oracle.decode_fp4s16_records(mk) if getattr(wl, "main_fmt", "fp4") == "fp4s16"
+                     else oracle.decode_fp4_records(mk))
         pos1, seq0, base0 = np.array([q_pos[t]]), np.array([0]), np.array([0])
         n = int(oracle.visible_count(pos1, wl.ratio)[0])
         cand = idx = None
@@ -458,6 +462,8 @@ def main():
                    "topk": wl.topk, "pool_blocks": wl.n_blocks, "block_size": wl.block_size,
                    "index_k_format": ("e2m1+e4m3/16" if getattr(wl, "k_fmt", "fp8") == "fp4s16"
                                       else "e4m3+f32/row"),
+                   "main_kv_record": ("288 B e2m1+e4m3/16" if getattr(wl, "main_fmt", "fp4") == "fp4s16"
+                                      else "320 B e2m1+f32/32"),
                    "input_copies": len(runs), "block_candidates_overlapped": bool(args.overlap_blocks),
                    "full_layer_selections": ("separate" if args.separate_select or args.overlap_blocks
                                              else "shared launch")},

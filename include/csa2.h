@@ -235,7 +235,9 @@ size_t csa2_topk_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, 
  *   q         [Q, H, D] contiguous, q_dtype BF16 or F32.
  *   main_kv   rows = all main-KV entries: FP4_E2M1 with 16 scales per row
  *             (e.g. 320-byte records: 256 code bytes then 16 fp32 scales),
- *             or F32.
+ *             FP4_E2M1_E4M3S16 with 32 E4M3 scale bytes per row (the pages'
+ *             288-byte record: 256 code bytes then the scales; [CSA2] SGLang
+ *             section; scale rows 8-byte aligned), or F32.
  *   main_base [B] int64: first main_kv row of each sequence.
  *   idx       [Q, k] int32 main positions; entries < 0 are skipped, and so
  *             are entries at or beyond the query's visible count

@@ -107,6 +107,14 @@ def decode_fp4s16_rows(codes, scales):
     return E2M1_TABLE[e] * np.repeat(E4M3_TABLE[scales], 16, axis=1)
 
 
+def decode_fp4s16_records(rec):
+    """The pages' 288-byte main-KV records [n, 288] -> float64 [n, 512]:
+    256 bytes of E2M1 pairs, then 32 E4M3 scale bytes, one per 16 elements
+    ([CSA2] SGLang section: 256 B of data + 32 B of scale)."""
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    return decode_fp4s16_rows(rec[:, :256], rec[:, 256:288])
+
+
 def decode_swa_records(rec):
     """528-byte SWA records [n, 528] -> float64 [n, 512]: 512 E4M3 codes, then
     4 little-endian fp32 scales, one per 128 elements."""

@@ -7,7 +7,8 @@ arithmetic: both the HIP path and the CPU oracle consume the bytes it writes,
 and the oracle decodes them with its own tables.
 """
 from .formats import (  # noqa: F401
-    encode_e4m3_rows, encode_fp4_records, encode_fp4s16_rows, encode_swa_records, encode_bf16,
+    encode_e4m3_rows, encode_fp4_records, encode_fp4s16_rows, encode_fp4s16_records,
+    encode_swa_records, encode_bf16, FP4S16_RECORD_BYTES,
     E4M3_MAX, E2M1_MAX,
     FP4_RECORD_BYTES, SWA_RECORD_BYTES,
 )

@@ -29,6 +29,7 @@ E4M3_MAX = 448.0
 E2M1_MAX = 6.0
 FP4_RECORD_BYTES = 320      # 256 B of E2M1 pairs + 16 fp32 scales
 SWA_RECORD_BYTES = 528      # 512 B of E4M3 + 4 fp32 scales
+FP4S16_RECORD_BYTES = 288   # 256 B of E2M1 pairs + 32 E4M3 scales (the pages' record)
 
 
 def _group_scale(x, group, fmax):
@@ -91,6 +92,18 @@ def encode_fp4s16_rows(x):
     c = _e2m1_codes(y)
     packed = (c[:, 0::2] | (c[:, 1::2] << 4)).contiguous()
     return packed, s8.view(torch.uint8).contiguous()
+
+
+def encode_fp4s16_records(x):
+    """fp32 [n, 512] -> u8 records [n, 288]: the codes of encode_fp4s16_rows,
+    then its 32 scale bytes."""
+    n, d = x.shape
+    assert d == 512
+    codes, scales = encode_fp4s16_rows(x)
+    rec = torch.empty((n, FP4S16_RECORD_BYTES), dtype=torch.uint8, device=x.device)
+    rec[:, :256] = codes
+    rec[:, 256:] = scales
+    return rec
 
 
 def encode_swa_records(x):

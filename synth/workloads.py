@@ -27,13 +27,14 @@ import math
 import numpy as np
 import torch
 
-from .formats import (encode_e4m3_rows, encode_fp4_records, encode_fp4s16_rows, encode_swa_records,
+from .formats import (encode_e4m3_rows, encode_fp4_records, encode_fp4s16_rows,
+                      encode_fp4s16_records, encode_swa_records,
                       encode_bf16)
 
 CONFIG_NAMES = ("tiny_full_fp32", "decode_128k", "prefill_m2_chunk",
                 "reindex_1m", "decoder_group_256k")
 # further workloads of the same shapes in other cache formats
-EXTRA_WORKLOADS = ("decode_128k_fp4k",)
+EXTRA_WORKLOADS = ("decode_128k_pages_formats",)
 
 H_IDX, D_IDX = 32, 128
 H_ATT, D_ATT = 64, 512
@@ -87,7 +88,7 @@ class Workload:
     q_pos: torch.Tensor            # [Q] int32 token position of each query
     k_idx: torch.Tensor            # [sum N, 128] u8 E4M3 codes ([sum N, 64] E2M1 pairs), or fp32
     k_scale: torch.Tensor          # [sum N] fp32 ([sum N, 8] u8 E4M3 for E2M1 keys), or None
-    main_kv: torch.Tensor          # [sum N, 320] u8 records, or [sum N, 512] fp32
+    main_kv: torch.Tensor          # [sum N, 320] u8 records ([sum N, 288] for "fp4s16"), or fp32
     swa_base: torch.Tensor         # [B] int64 first SWA row of each sequence
     swa_pos0: torch.Tensor         # [B] int32 token position of that row
     layers: list = field(default_factory=list)
@@ -97,6 +98,7 @@ class Workload:
     window: int = WINDOW
     softmax_scale: float = 1.0 / math.sqrt(D_ATT)
     k_fmt: str = "fp8"             # index-K format: "fp8" (E4M3 + fp32 per row) or "fp4s16"
+    main_fmt: str = "fp4"          # main-KV record: "fp4" (320 B, fp32 per 32) or "fp4s16" (288 B)
 
     @property
     def Q(self):
@@ -151,11 +153,11 @@ def _index_keys(seed, total, quantized, device, k_fmt="fp8"):
     return codes, scale
 
 
-def _main_kv_gauss(seed, total, quantized, device):
+def _main_kv_gauss(seed, total, quantized, device, main_fmt="fp4"):
     if not quantized:
         return _randn((total, D_ATT), seed, _T_MAIN, 0, device)
-    return _chunked(total, lambda c, n: encode_fp4_records(
-        _randn((n, D_ATT), seed, _T_MAIN, c, device)))
+    enc = encode_fp4s16_records if main_fmt == "fp4s16" else encode_fp4_records
+    return _chunked(total, lambda c, n: enc(_randn((n, D_ATT), seed, _T_MAIN, c, device)))
 
 
 def compress_pairs_input(c, z):
@@ -227,13 +229,13 @@ def _decode_layout(n_entries, q_per_seq, ratio, device, positions=None):
 
 def mini_workload(seed, n_entries, q_per_seq=1, ratio=1, quantized=True,
                   modes=("full",), device="cpu", positions=None, topk=TOPK,
-                  n_blocks=N_BLOCKS, block_size=BLOCK, k_fmt="fp8"):
+                  n_blocks=N_BLOCKS, block_size=BLOCK, k_fmt="fp8", main_fmt="fp4"):
     """A small workload of the same structure, for parity tests."""
     seq_base, q_seq, q_pos, swa_base, swa_pos0, swa_total = _decode_layout(
         n_entries, q_per_seq, ratio, device, positions)
     total = int(sum(n_entries))
     k_idx, k_scale = _index_keys(seed, total, quantized, device, k_fmt)
-    main = _main_kv_gauss(seed, total, quantized, device)
+    main = _main_kv_gauss(seed, total, quantized, device, main_fmt)
     Q = int(q_pos.shape[0])
     layers = [_layer(seed, li, m, Q, swa_total, quantized, device,
                      with_indexer=(m in ("full", "reindex")))
@@ -243,7 +245,8 @@ def mini_workload(seed, n_entries, q_per_seq=1, ratio=1, quantized=True,
                     q_pos=q_pos, k_idx=k_idx, k_scale=k_scale, main_kv=main,
                     swa_base=swa_base, swa_pos0=swa_pos0, layers=layers,
                     topk=topk, n_blocks=n_blocks, block_size=block_size,
-                    k_fmt=k_fmt if quantized else "fp8")
+                    k_fmt=k_fmt if quantized else "fp8",
+                    main_fmt=main_fmt if quantized else "fp4")
 
 
 def _prefill_m2(seed, device):
@@ -283,11 +286,13 @@ def make_workload(name, device="cpu", seed_offset=0):
                           modes=("full", "reindex"), device=device)
     elif name == "prefill_m2_chunk":
         w = _prefill_m2(2 + o, device)
-    elif name == "decode_128k_fp4k":
-        # decode_128k with index K in the pages' FP4 format (E2M1 + an E4M3
-        # scale per 16 dims, 72 B per key instead of 132)
+    elif name == "decode_128k_pages_formats":
+        # decode_128k in the pages' own cache formats: index K as E2M1 with an
+        # E4M3 scale per 16 dims (72 B per key instead of 132) and the 288-B
+        # main-KV record (instead of 320)
         w = mini_workload(1 + o, [131072] * 8, q_per_seq=1, ratio=1, quantized=True,
-                          modes=("full", "reindex"), device=device, k_fmt="fp4s16")
+                          modes=("full", "reindex"), device=device, k_fmt="fp4s16",
+                          main_fmt="fp4s16")
     elif name == "reindex_1m":
         w = mini_workload(3 + o, [1 << 20] * 2, q_per_seq=1, ratio=1, quantized=True,
                           modes=("full", "reindex"), device=device)

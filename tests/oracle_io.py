@@ -37,6 +37,8 @@ def index_k_rows(wl, rows=None):
 def main_rows(wl, rows=None):
     m = wl.main_kv if rows is None else wl.main_kv[rows]
     if wl.quantized:
+        if getattr(wl, "main_fmt", "fp4") == "fp4s16":
+            return oracle.decode_fp4s16_records(_np(m))
         return oracle.decode_fp4_records(_np(m))
     return _np(m).astype(np.float64)
 

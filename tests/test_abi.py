@@ -208,6 +208,10 @@ def _attn(lib, **kw):
     (dict(main=tsl.csa2_rows(FAKE, FAKE + 4, 320, 80, tsl.CSA2_FP4_E2M1)), tsl.CSA2_ERR_INVALID_ARG),
     (dict(main=tsl.csa2_rows(FAKE, None, 320, 80, tsl.CSA2_FP4_E2M1)), tsl.CSA2_ERR_INVALID_ARG),
     (dict(ratio=4), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(main=tsl.csa2_rows(FAKE, FAKE + 4, 288, 288, tsl.CSA2_FP4_E2M1_E4M3S16)),
+     tsl.CSA2_ERR_INVALID_ARG),
+    (dict(main=tsl.csa2_rows(FAKE, FAKE + 256, 288, 20, tsl.CSA2_FP4_E2M1_E4M3S16)),
+     tsl.CSA2_ERR_INVALID_ARG),
     (dict(ws=FAKE + 4, wsb=1 << 30), tsl.CSA2_ERR_INVALID_ARG),
 ])
 def test_sparse_attn_rejects(kw, status):
@@ -234,3 +238,6 @@ def test_zero_queries_is_a_no_op_after_checks():
     st, _ = _scores(lib, Q=0)
     assert st == tsl.CSA2_OK
     assert _attn(lib, Q=0) == tsl.CSA2_OK
+    # the pages' 288-byte main-KV record passes the same checks
+    assert _attn(lib, Q=0, main=tsl.csa2_rows(FAKE, FAKE + 256, 288, 288,
+                                              tsl.CSA2_FP4_E2M1_E4M3S16)) == tsl.CSA2_OK

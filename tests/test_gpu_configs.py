@@ -19,7 +19,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 SAMPLES = {"tiny_full_fp32": None, "decode_128k": [0, 5], "prefill_m2_chunk": [0, 1, 2047, 4095],
-           "reindex_1m": [0, 1], "decoder_group_256k": [0, 37], "decode_128k_fp4k": [2, 7]}
+           "reindex_1m": [0, 1], "decoder_group_256k": [0, 37], "decode_128k_pages_formats": [2, 7]}
 
 
 @pytest.fixture(autouse=True)

@@ -309,12 +309,14 @@ def _random_idx(rng, nvis, k, frac_valid=1.0):
     return idx
 
 
+@pytest.mark.parametrize("main_fmt", ["fp4", "fp4s16"])
 @pytest.mark.parametrize("split", [True, False])
 @pytest.mark.parametrize("ratio", [1, 2])
-def test_sparse_attn_quant(ratio, split):
-    _announce(f"sparse_attn quantized ratio={ratio} split={split}")
+def test_sparse_attn_quant(ratio, split, main_fmt):
+    _announce(f"sparse_attn quantized ratio={ratio} split={split} main={main_fmt}")
     wl = synth.mini_workload(20 + ratio, [3000, 700, 200], ratio=ratio,
-                             positions=[[3000 * ratio - 1, 1500], [700 * ratio - 1], [5, 0]]).to(DEV)
+                             positions=[[3000 * ratio - 1, 1500], [700 * ratio - 1], [5, 0]],
+                             main_fmt=main_fmt).to(DEV)
     rng = np.random.default_rng(ratio)
     nvis = _np(wl.n_vis())
     idx = _random_idx(rng, nvis, 512, 0.9)

@@ -192,3 +192,27 @@ def test_generator_fp4s16_rows():
     y = (x.double().numpy().reshape(48, 8, 16) / sdec[:, :, None]).reshape(48, 128)
     y = np.clip(y, -6.0, 6.0)
     assert _nearest_grid_ok(y, dec / np.repeat(sdec, 16, axis=1), oracle.E2M1_TABLE)
+
+
+def test_fp4s16_record_hand_decoded():
+    """The pages' 288-byte record: 256 code bytes, then one E4M3 scale byte per
+    16 elements."""
+    rec = np.zeros((1, 288), dtype=np.uint8)
+    rec[0, 0] = 0x71          # elements 0, 1 = 0.5, 6
+    rec[0, 255] = 0x90        # element 510 = 0, element 511 = code 9 (-0.5)
+    rec[0, 256] = 0x40        # scale of elements 0..15: 2.0
+    rec[0, 287] = 0x7E        # scale of elements 496..511: 448
+    v = oracle.decode_fp4s16_records(rec)[0]
+    assert v.shape == (512,)
+    assert v[0] == 1.0 and v[1] == 12.0 and v[511] == -224.0
+    assert np.count_nonzero(v) == 3
+
+
+def test_generator_fp4s16_records():
+    x = torch.randn(16, 512, generator=torch.Generator().manual_seed(6))
+    rec = synth.encode_fp4s16_records(x)
+    assert rec.shape == (16, synth.FP4S16_RECORD_BYTES) == (16, 288)
+    codes, scales = synth.encode_fp4s16_rows(x)
+    assert torch.equal(rec[:, :256], codes) and torch.equal(rec[:, 256:], scales)
+    assert np.array_equal(oracle.decode_fp4s16_records(rec.numpy()),
+                          oracle.decode_fp4s16_rows(codes.numpy(), scales.numpy()))

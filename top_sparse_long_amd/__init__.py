@@ -122,6 +122,13 @@ def rows_fp4_records(rec):
     return csa2_rows(rec.data_ptr(), rec.data_ptr() + 256, 320, 80, CSA2_FP4_E2M1)
 
 
+def rows_fp4s16_records(rec):
+    """The pages' 288-byte main-KV records [n, 288]: 256 code bytes, then 32
+    E4M3 scale bytes (one per 16 elements)."""
+    assert rec.dtype == torch.uint8 and rec.is_contiguous() and rec.shape[-1] == 288
+    return csa2_rows(rec.data_ptr(), rec.data_ptr() + 256, 288, 288, CSA2_FP4_E2M1_E4M3S16)
+
+
 def rows_swa_records(rec):
     """528-byte FP8 SWA records [n, 528]: 512 code bytes, 4 fp32 scales."""
     assert rec.dtype == torch.uint8 and rec.is_contiguous() and rec.shape[-1] == 528

@@ -354,6 +354,7 @@ int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv
   a.main_scale = main_kv->scale;
   a.main_stride = main_kv->row_stride;
   a.main_scale_stride = main_kv->scale_stride;
+  a.main_s16 = main_kv->dtype == CSA2_FP4_E2M1_E4M3S16 ? 1 : 0;
   a.main_base = main_base;
   a.idx = idx;
   a.k = k;
@@ -375,20 +376,27 @@ int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv
   a.lse = lse;
   a.Q = Q;
   a.H = H;
-  const bool quant = q_dtype == CSA2_BF16 && main_kv->dtype == CSA2_FP4_E2M1 &&
+  const bool s16 = main_kv->dtype == CSA2_FP4_E2M1_E4M3S16;
+  const bool quant = q_dtype == CSA2_BF16 && (main_kv->dtype == CSA2_FP4_E2M1 || s16) &&
                      swa_kv->dtype == CSA2_FP8_E4M3 &&
                      (out_dtype == CSA2_BF16 || out_dtype == CSA2_F32);
   const bool f32 = q_dtype == CSA2_F32 && main_kv->dtype == CSA2_F32 && swa_kv->dtype == CSA2_F32 &&
                    out_dtype == CSA2_F32;
   REQUIRE(quant || f32, CSA2_ERR_UNSUPPORTED,
-          "csa2_sparse_attn: supported dtypes are (q BF16, main FP4_E2M1, swa FP8_E4M3, out BF16|F32) "
+          "csa2_sparse_attn: supported dtypes are (q BF16, main FP4_E2M1 or FP4_E2M1_E4M3S16, "
+          "swa FP8_E4M3, out BF16|F32) "
           "and (all F32)");
   if (quant) {
     REQUIRE(main_kv->scale && swa_kv->scale, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: quantized rows need scales");
     REQUIRE(main_kv->row_stride >= 256 && swa_kv->row_stride >= 512, CSA2_ERR_INVALID_ARG,
             "csa2_sparse_attn: row stride below the code bytes of a row");
-    REQUIRE(aligned(main_kv->scale, 16) && main_kv->scale_stride % 4 == 0 && main_kv->scale_stride >= 16,
-            CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: FP4 scales must be 16-byte aligned rows of >= 16 floats");
+    if (s16)
+      REQUIRE(aligned(main_kv->scale, 8) && main_kv->scale_stride % 8 == 0 && main_kv->scale_stride >= 32,
+              CSA2_ERR_INVALID_ARG,
+              "csa2_sparse_attn: E4M3 main-KV scales must be 8-byte aligned rows of >= 32 bytes");
+    else
+      REQUIRE(aligned(main_kv->scale, 16) && main_kv->scale_stride % 4 == 0 && main_kv->scale_stride >= 16,
+              CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: FP4 scales must be 16-byte aligned rows of >= 16 floats");
     REQUIRE(aligned(swa_kv->scale, 4) && swa_kv->scale_stride >= 4, CSA2_ERR_INVALID_ARG,
             "csa2_sparse_attn: FP8 SWA rows need 4 scales each");
   } else {

@@ -89,9 +89,10 @@ hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, cons
 struct AttnArgs {
   const void* q;             // [Q, H, 512] bf16 or fp32
   const uint8_t* main;       // main-KV rows
-  const float* main_scale;
+  const float* main_scale;   // fp32 per 32 dims, or E4M3 bytes per 16 dims (main_s16)
   int64_t main_stride;       // bytes
-  int64_t main_scale_stride; // floats
+  int64_t main_scale_stride; // floats, or bytes (main_s16)
+  int main_s16;              // 1: the pages' 288-B record scales (E4M3, one per 16 dims)
   const int64_t* main_base;
   const int32_t* idx;
   int k;

@@ -70,6 +70,16 @@ __device__ __forceinline__ void dequant_fp4x8(uint32_t x, float s, v2h m2, uint3
   out[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, s, 3) * m2);
 }
 
+// Eight E2M1 codes times an E4M3 scale widened to f16: exact (a code has at
+// most 2 significant bits, an E4M3 scale at most 4).
+__device__ __forceinline__ void dequant_fp4x8_h(uint32_t x, _Float16 s, uint32_t out[4]) {
+  const v2h s2 = {s, s};
+  out[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 0) * s2);
+  out[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 1) * s2);
+  out[2] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 2) * s2);
+  out[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(x, 1.0f, 3) * s2);
+}
+
 // Four E4M3 codes (one dword).
 __device__ __forceinline__ void dequant_fp8x4(uint32_t x, float s, v2h m2, uint32_t out[2]) {
   out[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, s, false) * m2);
@@ -83,8 +93,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 }
 
 // Raw bytes of one tile as one lane holds them while the previous tile is
-// computed.  Main tile: 64 E2M1 bytes and 4 scales of the lane's key in each
-// 16-key half kh (d[4 kh + j], s[kh]).  SWA tile: only the first half's 128
+// computed.  Main tile: 64 E2M1 bytes and the scales of the lane's key in
+// each 16-key half kh (d[4 kh + j], s[kh]: 4 fp32 scales, or 8 E4M3 scale
+// bytes in the first two words for the 288-byte record).  SWA tile: only the first half's 128
 // E4M3 codes and scale -- the second half is requested when the tile starts.
 struct MainTile {
   v4u d[8];
@@ -97,6 +108,7 @@ struct SwaTile {
   bool ok[2];
 };
 
+template <bool S16>
 __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[AT_WAVES * AT_TILE_BYTES];
   __shared__ float s_m[AT_WAVES][AT_HEADS];
@@ -185,10 +197,17 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
       const int pos = slot < a.k ? s_idx[slot] : -1;
       const bool v = pos >= 0 && pos < nvis;
       const uint8_t* src = v ? a.main + (mbase + pos) * a.main_stride : dummy;
-      const float* ssrc = v ? a.main_scale + (mbase + pos) * a.main_scale_stride : (const float*)dummy;
 #pragma unroll
       for (int j = 0; j < 4; ++j) M.d[4 * kh + j] = *(const v4u*)(src + 64 * g + 16 * j);
-      M.s[kh] = *(const float4*)(ssrc + 4 * g);
+      if (S16) {
+        // 8 E4M3 scales of dims [128 g, +128)
+        const uint8_t* ssrc = v ? (const uint8_t*)a.main_scale + (mbase + pos) * a.main_scale_stride : dummy;
+        const uint2 sb = *(const uint2*)(ssrc + 8 * g);
+        M.s[kh] = make_float4(__uint_as_float(sb.x), __uint_as_float(sb.y), 0.f, 0.f);
+      } else {
+        const float* ssrc = v ? a.main_scale + (mbase + pos) * a.main_scale_stride : (const float*)dummy;
+        M.s[kh] = *(const float4*)(ssrc + 4 * g);
+      }
       M.ok[kh] = v;
     }
   };
@@ -258,13 +277,30 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
     for (int kh = 0; kh < 2; ++kh) {
       const float4 sc = M.ok[kh] ? M.s[kh] : make_float4(0.f, 0.f, 0.f, 0.f);
       const float s4[4] = {sc.x, sc.y, sc.z, sc.w};
+      // E4M3 scales of the 8 16-dim groups, widened to f16 (exact)
+      _Float16 s8[8];
+      if (S16) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__float_as_uint(s4[w]), 1.0f, false);
+          const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__float_as_uint(s4[w]), 1.0f, true);
+          s8[4 * w] = lo[0];
+          s8[4 * w + 1] = lo[1];
+          s8[4 * w + 2] = hi[0];
+          s8[4 * w + 3] = hi[1];
+        }
+      }
       uint8_t* dst = tile + (kh * 16 + r) * AT_RS + 256 * g;
       v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // two chains
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
         uint32_t kd[4];
-        const _Float16 mh = scale_mantissa(s4[c >> 2]);
-        dequant_fp4x8(M.d[4 * kh + (c >> 2)][c & 3], s4[c >> 2], (v2h){mh, mh}, kd);
+        if (S16) {
+          dequant_fp4x8_h(M.d[4 * kh + (c >> 2)][c & 3], s8[c >> 1], kd);
+        } else {
+          const _Float16 mh = scale_mantissa(s4[c >> 2]);
+          dequant_fp4x8(M.d[4 * kh + (c >> 2)][c & 3], s4[c >> 2], (v2h){mh, mh}, kd);
+        }
         const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
         *(v4u*)(dst + 16 * c) = kv;
         s[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qf[c], s[c & 1], 0, 0, 0);
@@ -625,7 +661,10 @@ int attn_splits(int Q, int H, int k, int window) {
 
 hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s) {
   const int groups = a.Q * (a.H / AT_HEADS);
-  hipLaunchKernelGGL(sparse_attn_quant_kernel, dim3(groups * a.n_split), dim3(256), 0, s, a);
+  if (a.main_s16)
+    hipLaunchKernelGGL(sparse_attn_quant_kernel<true>, dim3(groups * a.n_split), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(sparse_attn_quant_kernel<false>, dim3(groups * a.n_split), dim3(256), 0, s, a);
   if (a.n_split > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -24,7 +24,8 @@ from . import (csa2_index_scores, csa2_block_candidates, csa2_topk, csa2_sparse_
                csa2_topk_and_block_candidates, csa2_topk_and_block_candidates_workspace_size,
                csa2_block_candidates_workspace_size, csa2_topk_workspace_size,
                csa2_sparse_attn_workspace_size,
-               rows_f32, rows_fp8, rows_fp4s16, rows_fp4_records, rows_swa_records,
+               rows_f32, rows_fp8, rows_fp4s16, rows_fp4_records, rows_fp4s16_records,
+               rows_swa_records,
                CSA2_F32, CSA2_BF16)
 
 
@@ -58,7 +59,10 @@ class LayerRunner:
                 self.k_rows = rows_fp4s16(wl.k_idx, wl.k_scale)
             else:
                 self.k_rows = rows_fp8(wl.k_idx, wl.k_scale)
-            self.main_rows = rows_fp4_records(wl.main_kv)
+            if getattr(wl, "main_fmt", "fp4") == "fp4s16":
+                self.main_rows = rows_fp4s16_records(wl.main_kv)
+            else:
+                self.main_rows = rows_fp4_records(wl.main_kv)
         else:
             self.k_rows = rows_f32(wl.k_idx)
             self.main_rows = rows_f32(wl.main_kv)

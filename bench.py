@@ -202,9 +202,12 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, workload, comma
 
     src = _source_hash()
     for stage, pats in STAGE_KERNELS.items():
-        # a stage is present when its first kernel is (list-stage kernels are
-        # shared between stages)
-        if not any(pats[0] in n for n in per_kernel_bytes):
+        # a stage is present when one of its own kernels is (the selection
+        # list-stage kernels are shared between stages and do not count)
+        own = [p for p in pats if p != "select_kernel<3,"]
+        if stage == "topk_and_blocks":
+            own = ["select_pair_kernel"]
+        if not any(p in n for p in own for n in per_kernel_bytes):
             continue
         # with the shared-launch call the separate-call stages do not occur
         if stage in ("topk_dense", "block_candidates") and any(

@@ -364,6 +364,194 @@ def compress(c, z, m):
 
 
 # ----------------------------------------------------------------------------
+# Full-layer cache write ([CSA2] "per-layer attention computation", item 3:
+# the compressed entry passes RMSNorm to a latent taken before RoPE; one copy
+# gets RoPE and FP4 quantization for the main-KV cache, the other is
+# projected, normalised, rotated and quantized into the index key.  [3MODES]
+# Q&A "how is indexer K generated": k = RMSNorm(C W_IK) with W_IK 512 x 128,
+# applied to the latent before RoPE, with RoPE on the last 64 dims after the
+# projection.  [REPORT] section 6: quantization comes after RoPE.  [CSA2]
+# "the pool does not reduce storage": with m = 2 an entry is written only once
+# both tokens of its pair exist, so n tokens hold n // 2 entries.)
+#
+# Readings where the pages are silent:
+#  * RMSNorm(x) = x / sqrt(mean(x^2) + eps) * weight.
+#  * RoPE turns adjacent pairs (2j, 2j+1) of the rotated dims by the angle of
+#    frequency j, with cos/sin read from a per-position table:
+#      x'[2j] = x[2j] cos_j - x[2j+1] sin_j,  x'[2j+1] = x[2j] sin_j + x[2j+1] cos_j.
+#    The main latent and the index key use the same table.
+#  * The RoPE position of entry e is the position of its first token, e * m.
+#  * The index-key weight is stored as a linear layer's [128, 512] matrix:
+#    k[n] = sum_c u[c] W[n, c].
+#  * Quantization: per group, scale = amax / fmax (fmax = 6 for E2M1, 448 for
+#    E4M3), kept in fp32 (1.0 for an all-zero group), or rounded to E4M3 for
+#    the per-16 format (0x38 = 1.0 for an all-zero group, the smallest
+#    positive E4M3 value when the rounding gives zero).  Each element becomes
+#    the representable value nearest to x / scale, ties to the even code,
+#    saturating at the largest magnitude.
+# ----------------------------------------------------------------------------
+
+E2M1_GRID = E2M1_TABLE[:8]     # codes 0..7: 0, .5, 1, 1.5, 2, 3, 4, 6
+E4M3_GRID = E4M3_TABLE[:127]   # codes 0..126: 0 .. 448 (0x7f is NaN)
+
+
+def rms_norm(x, weight, eps):
+    x = np.asarray(x, dtype=np.float64)
+    r = np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x / r * np.asarray(weight, dtype=np.float64)
+
+
+def rope_tail(x, cos, sin):
+    """Rotate the last 2 * len(cos) dims of x (one row, or rows with one
+    cos/sin row each) in adjacent pairs."""
+    x = np.array(x, dtype=np.float64)
+    cos = np.asarray(cos, dtype=np.float64)
+    sin = np.asarray(sin, dtype=np.float64)
+    r = 2 * cos.shape[-1]
+    d = x.shape[-1]
+    a = x[..., d - r::2].copy()
+    b = x[..., d - r + 1::2].copy()
+    x[..., d - r::2] = a * cos - b * sin
+    x[..., d - r + 1::2] = a * sin + b * cos
+    return x
+
+
+def _nearest_index(mag, grid):
+    """Index of the grid value nearest to each magnitude; at a midpoint the
+    even index wins (neighbouring codes alternate their lowest bit, so this is
+    ties-to-even); magnitudes beyond the top saturate to it."""
+    mag = np.asarray(mag, dtype=np.float64)
+    hi = np.clip(np.searchsorted(grid, mag, side="left"), 1, len(grid) - 1)
+    lo = hi - 1
+    mid = (grid[lo] + grid[hi]) / 2.0
+    up = (mag > mid) | ((mag == mid) & (hi % 2 == 0))
+    return np.where(up, hi, lo)
+
+
+def encode_e2m1(x):
+    """float64 -> E2M1 codes (sign in bit 3; a negative value that rounds to
+    zero keeps its sign bit)."""
+    x = np.asarray(x, dtype=np.float64)
+    code = _nearest_index(np.abs(x), E2M1_GRID).astype(np.uint8)
+    return code | ((x < 0).astype(np.uint8) << 3)
+
+
+def encode_e4m3(x):
+    """float64 -> E4M3FN codes (sign in bit 7), saturating at 448."""
+    x = np.asarray(x, dtype=np.float64)
+    code = _nearest_index(np.abs(x), E4M3_GRID).astype(np.uint8)
+    return code | ((x < 0).astype(np.uint8) << 7)
+
+
+def quantize_fp32_scaled(x, group, kind):
+    """x [n, d] -> (codes [n, d] uint8, fp32 scales [n, d // group]);
+    kind 'e2m1' (fmax 6) or 'e4m3' (fmax 448)."""
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    fmax, enc = (6.0, encode_e2m1) if kind == "e2m1" else (448.0, encode_e4m3)
+    g = x.reshape(n, d // group, group)
+    amax = np.abs(g).max(axis=2)
+    scale = np.where(amax > 0, amax / fmax, 1.0).astype(np.float32)
+    codes = enc(g / scale.astype(np.float64)[..., None])
+    return codes.reshape(n, d), scale
+
+
+def quantize_e2m1_e4m3s16(x):
+    """The pages' FP4 format: x [n, d] -> (E2M1 codes [n, d], E4M3 scale
+    bytes [n, d // 16])."""
+    x = np.asarray(x, dtype=np.float64)
+    n, d = x.shape
+    g = x.reshape(n, d // 16, 16)
+    amax = np.abs(g).max(axis=2)
+    sc = encode_e4m3(amax / 6.0)
+    sc = np.where(amax == 0, 0x38, np.where(sc == 0, 0x01, sc)).astype(np.uint8)
+    codes = encode_e2m1(g / E4M3_TABLE[sc][..., None])
+    return codes.reshape(n, d), sc
+
+
+def pack_e2m1(codes):
+    """E2M1 codes [n, d] -> bytes [n, d / 2], element 2i in the low nibble."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def fp4_records(x):
+    """[n, 512] -> 320-byte records: packed E2M1, then 16 fp32 scales."""
+    codes, scale = quantize_fp32_scaled(x, 32, "e2m1")
+    return np.concatenate([pack_e2m1(codes),
+                           scale.astype("<f4").view(np.uint8).reshape(len(x), 64)], axis=1)
+
+
+def fp4s16_records(x):
+    """[n, 512] -> the pages' 288-byte records: packed E2M1, then 32 E4M3 scales."""
+    codes, sc = quantize_e2m1_e4m3s16(x)
+    return np.concatenate([pack_e2m1(codes), sc], axis=1)
+
+
+def cache_write(c, z, tok_seq, tok_pos, ratio, n_seq, pend_c, pend_z, kv_norm_w,
+                w_ik, k_norm_w, eps, rope_cos, rope_sin):
+    """A Full layer's cache write for one call's tokens.
+
+    c, z [T, 512] token rows (z is unused with ratio 1); tok_seq, tok_pos [T];
+    pend_c, pend_z: None, or [n_seq, 512] rows of the token that opened each
+    sequence's incomplete pair in an earlier call; w_ik [128, 512];
+    rope_cos, rope_sin [n_pos, 32].
+
+    A token at position p closes entry e = p // m when (p + 1) % m == 0.  With
+    m = 2 its partner at p - 1 is the previous token of the call when that is
+    the same sequence at p - 1, else the pending row; without either, or with
+    the RoPE position outside the table, or with a sequence id outside
+    [0, n_seq), the token writes nothing.  Returns (entries, main, k, pend_c',
+    pend_z'): entries lists (seq, e) in token order, main [n, 512] and k
+    [n, 128] are the post-RoPE values before quantization, and the pending
+    rows are updated from the token that ends each sequence's run at an even
+    position (after every entry has read the old ones)."""
+    m = int(ratio)
+    c = np.asarray(c, dtype=np.float64)
+    z = None if z is None else np.asarray(z, dtype=np.float64)
+    T = len(tok_seq)
+    entries, mains, ks = [], [], []
+    for t in range(T):
+        s, p = int(tok_seq[t]), int(tok_pos[t])
+        if s < 0 or s >= n_seq or p < 0 or (p + 1) % m:
+            continue
+        if m == 1:
+            cg, zg = c[t:t + 1], None
+        elif t > 0 and int(tok_seq[t - 1]) == s and int(tok_pos[t - 1]) == p - 1:
+            cg, zg = c[t - 1:t + 1], z[t - 1:t + 1]
+        elif pend_c is not None:
+            cg = np.stack([np.asarray(pend_c[s], np.float64), c[t]])
+            zg = np.stack([np.asarray(pend_z[s], np.float64), z[t]])
+        else:
+            continue
+        e = p // m
+        if e * m >= len(rope_cos):
+            continue
+        u = rms_norm(compress(cg, zg, m)[0], kv_norm_w, eps)
+        main = rope_tail(u, rope_cos[e * m], rope_sin[e * m])
+        k = rms_norm(u @ np.asarray(w_ik, np.float64).T, k_norm_w, eps)
+        k = rope_tail(k, rope_cos[e * m], rope_sin[e * m])
+        entries.append((s, e))
+        mains.append(main)
+        ks.append(k)
+    new_c = None if pend_c is None else np.array(pend_c, dtype=np.float64)
+    new_z = None if pend_z is None else np.array(pend_z, dtype=np.float64)
+    if m == 2 and new_c is not None:
+        for t in range(T):
+            s, p = int(tok_seq[t]), int(tok_pos[t])
+            if s < 0 or s >= n_seq or p < 0 or p % 2:
+                continue
+            last = (t == T - 1 or int(tok_seq[t + 1]) != s
+                    or int(tok_pos[t + 1]) != p + 1)
+            if last:
+                new_c[s] = c[t]
+                new_z[s] = z[t]
+    main = np.array(mains).reshape(-1, c.shape[1])
+    k = np.array(ks).reshape(-1, 128)
+    return entries, main, k, new_c, new_z
+
+
+# ----------------------------------------------------------------------------
 # Layer roles and the shared slot set ([3MODES] "shared pool mechanism": the
 # SharedAttentionRuntime holds four slots compress_kv, index_k, topk_idxs and
 # candidates; Full writes them, Reindex rewrites topk_idxs from the pool,

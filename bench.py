@@ -57,6 +57,8 @@ def _parse():
                     help="capture block-candidate selection on a second stream beside the Full "
                          "layer's top-k and attention (HIP graphs on this ROCm replay the "
                          "branches one after the other, so this measured no gain)")
+    ap.add_argument("--no-cache-write", action="store_true",
+                    help="skip the Full-layer cache-write measurement")
     ap.add_argument("--stage-reps", type=int, default=10,
                     help="repetitions per input copy when timing single stages")
     ap.add_argument("--summarize-profiles", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT_DIR"),
@@ -135,6 +137,7 @@ STAGE_KERNELS = {
     "topk_pool": ("select_kernel<1,",),
     "topk_and_blocks": ("select_pair_kernel", "select_kernel<0,", "select_kernel<2,", "select_kernel<3,"),
     "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_combine_kernel", "sparse_attn_f32_kernel"),
+    "cache_write": ("cache_write_kernel", "cache_pend_kernel"),
 }
 CALIB_KERNEL = "__amd_rocclr_copyBuffer"
 CALIB_KIB = 256 * 1024          # the benchmark's calibration copy moves 256 MiB each way
@@ -333,6 +336,105 @@ def cpu_baseline(wl, n_sample):
                       f"(float64 NumPy oracle, {dt:.1f} s wall)"}
 
 
+# Full-layer cache write of the encoder prefill chunk: per entry, two tokens'
+# bf16 c and z rows in, the RoPE table row, the 320-byte main record and the
+# 132 bytes of FP8 index key out, and the two tokens' ids and positions
+CW_TOKENS = 65536
+CW_BYTES_PER_ENTRY = 2 * (1024 + 1024) + 256 + 320 + 128 + 4 + 2 * 8
+CW_BYTES_PER_CALL = 128 * 512 * 2 + 512 * 4 + 128 * 4      # W_IK and the two norm weights
+
+
+def cache_write_stage(torch, synth, tsl, wl, reps, n_copies, workload):
+    """Time csa2_cache_write on (a) the 65,536-token m = 2 encoder prefill
+    chunk (32,768 entries; roofline) and (b) the decode batch of the bench
+    workload (one token per query at its ratio and cache formats)."""
+    dev = "cuda"
+
+    def outputs(n, main_fmt, k_fmt):
+        if main_fmt == "fp4s16":
+            main = torch.empty((n, 288), dtype=torch.uint8, device=dev)
+            mrows = tsl.rows_fp4s16_records(main)
+        else:
+            main = torch.empty((n, 320), dtype=torch.uint8, device=dev)
+            mrows = tsl.rows_fp4_records(main)
+        if k_fmt == "fp4s16":
+            kc = torch.empty((n, 64), dtype=torch.uint8, device=dev)
+            ks = torch.empty((n, 8), dtype=torch.uint8, device=dev)
+            krows = tsl.rows_fp4s16(kc, ks)
+        else:
+            kc = torch.empty((n, 128), dtype=torch.uint8, device=dev)
+            ks = torch.empty((n,), dtype=torch.float32, device=dev)
+            krows = tsl.rows_fp8(kc, ks)
+        return (main, kc, ks), mrows, krows
+
+    def timed(fns):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for f in fns:
+                f()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(torch.cuda.current_stream())
+        g.replay()
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / len(fns)
+
+    def call(inp, bufs, base, n):
+        _, mrows, krows = bufs
+        return lambda: tsl.csa2_cache_write(inp.c, inp.z if inp.ratio == 2 else None, inp.tok_seq,
+                                            inp.tok_pos, inp.ratio, inp.pend, inp.n_seq,
+                                            inp.kv_norm_w, inp.w_ik, inp.k_norm_w, inp.eps,
+                                            inp.rope_cs, mrows, base, n, krows, base, n)
+
+    # (a) the prefill chunk, rotated over input copies
+    n_ent = CW_TOKENS // 2
+    inps = [synth.cache_write_inputs(7000 + c, [(0, 0, CW_TOKENS)], 2, dev) for c in range(n_copies)]
+    bufs = outputs(n_ent, "fp4", "fp8")
+    zero = torch.zeros(1, dtype=torch.int64, device=dev)
+    fns = [call(i, bufs, zero, n_ent) for _ in range(reps) for i in inps]
+    us = timed(fns)
+    nbytes = n_ent * CW_BYTES_PER_ENTRY + CW_BYTES_PER_CALL
+    achieved = nbytes / (us * 1e-6) / 1e9
+    prefill = {"workload": "encoder prefill chunk: 65,536 tokens at m = 2 -> 32,768 entries, "
+                           "320-B main records + FP8 index keys",
+               "avg_us": us, "entries_per_s": n_ent / (us * 1e-6),
+               "roofline": {"bound": "hbm", "kernel": "cache_write", "achieved": achieved,
+                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                            "traffic": _traffic("cache_write", workload, nbytes),
+                            "algorithmic_bytes": nbytes}}
+    del inps, bufs, fns
+    # (b) the decode batch: each query's sequence gets its newest token
+    pos = wl.q_pos.cpu().tolist()
+    seqs = wl.q_seq.cpu().tolist()
+    runs = [(s, p, 1) for s, p in zip(seqs, pos)]
+    inp = synth.cache_write_inputs(7100, runs, wl.ratio, dev, n_seq=max(seqs) + 1)
+    if len(set(seqs)) == len(seqs):
+        # one token per sequence: sequence s's entry lands in row s
+        base_l = [0] * inp.n_seq
+        for s_, p_ in zip(seqs, pos):
+            base_l[s_] = s_ - p_ // wl.ratio
+        n_rows = inp.n_seq
+    else:
+        span = max(p // wl.ratio for p in pos) + 1
+        base_l = [s_ * span for s_ in range(inp.n_seq)]
+        n_rows = inp.n_seq * span
+    base = torch.tensor(base_l, dtype=torch.int64, device=dev)
+    bufs = outputs(n_rows, getattr(wl, "main_fmt", "fp4"), getattr(wl, "k_fmt", "fp8"))
+    us_dec = timed([call(inp, bufs, base, n_rows) for _ in range(reps * n_copies)])
+    decode = {"workload": f"one new token for each of the {len(runs)} queries at m = {wl.ratio}",
+              "avg_us": us_dec}
+    return {"prefill_chunk": prefill, "decode_batch": decode}
+
+
 def main():
     args = _parse()
     if args.summarize_profiles:
@@ -449,6 +551,10 @@ def main():
         n_attn += wl.Q
     value = keys / (ms_per_step * 1e-3)
 
+    cache_write = None
+    if not args.no_cache_write:
+        cache_write = cache_write_stage(torch, synth, tsl, wl, reps, len(runs), args.workload)
+
     cpu = None
     if not args.no_cpu_baseline:
         n_sample = args.cpu_sample if args.cpu_sample is not None else min(8, wl.Q)
@@ -474,6 +580,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,
+        "cache_write": cache_write,
         "source_sha1": _source_hash(),
     }
     print(json.dumps(out), flush=True)

@@ -7,6 +7,7 @@
  *   csa2_topk              token-level top-k selection
  *   csa2_topk_and_block_candidates  both selections of a Full layer at once
  *   csa2_sparse_attn       joint-softmax sparse MQA attention with a sink
+ *   csa2_cache_write       a Full layer's main-KV entries and index keys
  * Sources are cited as page + section:
  *   [CSA2]   zdszero.github.io/csa2.html (CSA2 deep-dive)
  *   [3MODES] xhh.club, "DeepSeek-V4.1 model structure (2): CSA2's three modes"
@@ -278,6 +279,76 @@ int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv
  * heads with k indices and an SWA window of `window` (0 when it would not
  * split). */
 size_t csa2_sparse_attn_workspace_size(int32_t Q, int32_t H, int32_t k, int32_t window);
+
+/*
+ * csa2_cache_write — a Full layer's write of its main-KV entries and index
+ * keys ([CSA2] "per-layer attention computation", item 3; [3MODES]
+ * "compression operator simplified" and Q&A "how is indexer K generated";
+ * [REPORT] section 6: quantization after RoPE).  A token at position p of
+ * sequence s closes entry e = p / ratio when p % ratio == ratio - 1; from the
+ * entry's tokens (p - ratio + 1 .. p):
+ *   cbar[ch] = sum_j softmax_j(z[j, ch]) c[j, ch]     (ratio 2; c itself for ratio 1)
+ *   u        = cbar / sqrt(mean(cbar^2) + eps) * kv_norm_w   (the latent before RoPE)
+ *   main     = RoPE(u)                                 dims 448..511 turn
+ *   k        = RMSNorm(u W_IK^T) * k_norm_w, then RoPE  dims 64..127 turn
+ * and writes main to row main_base[s] + e of main_out and k to row
+ * k_base[s] + e of k_out, quantized to their dtypes.  RoPE turns adjacent
+ * pairs (2i, 2i+1) of the turned dims by angle i of table row e * ratio (the
+ * entry's first token): x' = x cos - y sin, y' = x sin + y cos.  Quantization:
+ * per group, scale = amax / 6 (E2M1) or amax / 448 (E4M3) kept in fp32 (1.0
+ * for an all-zero group), or for FP4_E2M1_E4M3S16 amax / 6 rounded to E4M3
+ * (1.0 for an all-zero group, 2^-9 where the rounding gives zero); each
+ * element is the nearest code of x / scale, ties to even, saturating.  With
+ * ratio 2 an entry exists only once both of its tokens do ([CSA2] "the pool
+ * does not reduce storage": n tokens hold n / 2 entries).
+ *
+ *   c, z      bf16 token rows, row t at (const char*)c + t * cz_stride (512
+ *             values each; cz_stride >= 1024, both 16-byte aligned).  z holds
+ *             the compressor's gate logits and is required for ratio 2 (NULL
+ *             allowed for ratio 1).
+ *   tok_seq   [T] int32 sequence of each token (tokens of sequence ids outside
+ *             [0, B) write nothing).
+ *   tok_pos   [T] int32 position of each token (negative: nothing written).
+ *             A sequence's tokens in one call are consecutive rows at
+ *             consecutive positions.
+ *   ratio     m, 1 or 2.
+ *   pend      NULL, or (ratio 2) bf16 [B, 2, 512]: the c row then the z row of
+ *             the token that opened each sequence's incomplete pair, 16-byte
+ *             aligned.  A token at an odd position whose partner is not the
+ *             previous row of the call takes the partner from pend (without
+ *             pend it writes nothing).  After every entry has read it, the
+ *             call stores there the token that ends each sequence's run at an
+ *             even position.  Calls that share pend must not overlap.
+ *   B         number of sequences (length of main_base, k_base and pend).
+ *   kv_norm_w [512] fp32, 16-byte aligned.
+ *   w_ik      bf16 [128, 512] row-major (a linear layer's weight:
+ *             k[n] = sum_c u[c] w_ik[n, c]), 16-byte aligned; required when
+ *             k_out is given.
+ *   k_norm_w  [128] fp32, 16-byte aligned; required when k_out is given.
+ *   eps       RMSNorm epsilon (>= 0), both norms.
+ *   rope_cs   fp32 [n_rope, 64], 16-byte aligned: row r holds cos of the 32
+ *             angles of position r, then their sin.  An entry whose row
+ *             e * ratio is >= n_rope writes nothing.
+ *   main_out  NULL, or rows written: F32 (512 floats), FP4_E2M1 (256 code
+ *             bytes and 16 fp32 scales, e.g. the 320-byte record) or
+ *             FP4_E2M1_E4M3S16 (256 code bytes and 32 E4M3 scale bytes, e.g.
+ *             the pages' 288-byte record).
+ *   main_base [B] int64 first main_out row of each sequence; rows outside
+ *             [0, main_rows) are not written.
+ *   k_out     NULL, or rows written: F32 (128 floats), FP8_E4M3 (128 code
+ *             bytes and one fp32 scale) or FP4_E2M1_E4M3S16 (64 code bytes
+ *             and 8 E4M3 scale bytes).
+ *   k_base    [B] int64 first k_out row of each sequence; rows outside
+ *             [0, k_rows) are not written.
+ *   At least one of main_out and k_out is given.  Rows follow the csa2_rows
+ *   alignment rules (F32 rows 16-byte aligned).
+ */
+int csa2_cache_write(const void* c, const void* z, int64_t cz_stride, const int32_t* tok_seq,
+                     const int32_t* tok_pos, int32_t T, int32_t ratio, void* pend, int32_t B,
+                     const float* kv_norm_w, const void* w_ik, const float* k_norm_w, float eps,
+                     const float* rope_cs, int32_t n_rope, const csa2_rows* main_out,
+                     const int64_t* main_base, int64_t main_rows, const csa2_rows* k_out,
+                     const int64_t* k_base, int64_t k_rows, void* stream);
 
 /* Name of a status code (static string). */
 const char* csa2_status_string(int status);

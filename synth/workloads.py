@@ -44,6 +44,7 @@ CHUNK_ROWS = 1 << 20
 # tensor ids for the seed derivation
 _T_KIDX, _T_MAIN, _T_C, _T_Z = 1, 2, 3, 4
 _T_QIDX, _T_W, _T_Q, _T_SWA, _T_SINK = 10, 11, 12, 13, 14
+_T_CW_C, _T_CW_Z, _T_CW_KVW, _T_CW_KW, _T_CW_WIK, _T_CW_PEND = 20, 21, 22, 23, 24, 25
 
 
 def _gen(seed, tid, sub, device):
@@ -305,3 +306,66 @@ def make_workload(name, device="cpu", seed_offset=0):
         raise ValueError(f"unknown workload {name!r}; known: {CONFIG_NAMES + EXTRA_WORKLOADS}")
     w.name = name
     return w
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the Full-layer cache write
+
+@dataclass
+class CacheWriteInputs:
+    """Token rows and parameters of one cache-write call.  c, z: bf16 [T, 512]
+    compressor projections (z: gate logits); tok_seq, tok_pos: int32 [T];
+    pend: bf16 [B, 2, 512] pending rows (or None); kv_norm_w [512] and
+    k_norm_w [128] fp32 RMSNorm weights; w_ik bf16 [128, 512]; rope_cs fp32
+    [n_rope, 64] (cos of the 32 angles of each position, then their sin)."""
+    c: torch.Tensor
+    z: torch.Tensor
+    tok_seq: torch.Tensor
+    tok_pos: torch.Tensor
+    ratio: int
+    n_seq: int
+    pend: torch.Tensor
+    kv_norm_w: torch.Tensor
+    k_norm_w: torch.Tensor
+    w_ik: torch.Tensor
+    rope_cs: torch.Tensor
+    eps: float = 1e-6
+
+
+def rope_table(n_pos, device, base=10000.0):
+    """cos / sin of position p times the 32 frequencies base^(-2i/64), the
+    usual rotary table for 64 rotated dims (drawn in float64, stored fp32)."""
+    f = base ** (-torch.arange(32, dtype=torch.float64) * 2.0 / 64.0)
+    ang = torch.arange(n_pos, dtype=torch.float64)[:, None] * f[None, :]
+    return torch.cat([torch.cos(ang), torch.sin(ang)], 1).to(torch.float32).to(device).contiguous()
+
+
+def cache_write_inputs(seed, runs, ratio, device, n_seq=None, with_pend=True, n_rope=None):
+    """runs: list of (seq, first_position, n_tokens), one run of consecutive
+    positions per sequence, in call order.  c and z are N(0, 1) draws
+    rounded to bf16; the RMSNorm weights are 1 + N(0, 0.1^2) (the report
+    reading's section 6 puts the weights' magnitude near 1); W_IK is
+    N(0, 1/512), so index keys have unit scale before their norm; the pending
+    rows are N(0, 1) bf16 draws."""
+    seq = torch.cat([torch.full((n,), s, dtype=torch.int32) for s, _, n in runs])
+    pos = torch.cat([torch.arange(p0, p0 + n, dtype=torch.int32) for _, p0, n in runs])
+    T = int(seq.numel())
+    n_seq = (max(s for s, _, _ in runs) + 1) if n_seq is None else n_seq
+    rows = []
+    for tid in (_T_CW_C, _T_CW_Z):
+        parts = [encode_bf16(_randn((min(CHUNK_ROWS, T - r0), D_ATT), seed, tid, ci, device))
+                 for ci, r0 in enumerate(range(0, T, CHUNK_ROWS))]
+        rows.append(torch.cat(parts, 0) if parts else
+                    torch.empty((0, D_ATT), dtype=torch.bfloat16, device=device))
+    pend = None
+    if with_pend:
+        pend = encode_bf16(_randn((n_seq * 2, D_ATT), seed, _T_CW_PEND, 0, device)).reshape(n_seq, 2, D_ATT)
+    kvw = 1.0 + 0.1 * _randn((D_ATT,), seed, _T_CW_KVW, 0, device)
+    kw = 1.0 + 0.1 * _randn((D_IDX,), seed, _T_CW_KW, 0, device)
+    w_ik = encode_bf16(_randn((D_IDX, D_ATT), seed, _T_CW_WIK, 0, device) / math.sqrt(D_ATT))
+    max_pos = max(p0 + n for _, p0, n in runs)
+    rope = rope_table(max_pos if n_rope is None else n_rope, device)
+    return CacheWriteInputs(c=rows[0].contiguous(), z=rows[1].contiguous(),
+                            tok_seq=seq.to(device), tok_pos=pos.to(device), ratio=ratio,
+                            n_seq=n_seq, pend=pend, kv_norm_w=kvw.contiguous(),
+                            k_norm_w=kw.contiguous(), w_ik=w_ik.contiguous(), rope_cs=rope)

@@ -241,3 +241,64 @@ def test_zero_queries_is_a_no_op_after_checks():
     # the pages' 288-byte main-KV record passes the same checks
     assert _attn(lib, Q=0, main=tsl.csa2_rows(FAKE, FAKE + 256, 288, 288,
                                               tsl.CSA2_FP4_E2M1_E4M3S16)) == tsl.CSA2_OK
+
+
+def _cw(lib, **kw):
+    a = dict(c=FAKE, z=FAKE, stride=1024, seq=FAKE, pos=FAKE, T=4, ratio=2, pend=FAKE, B=2,
+             kvw=FAKE, wik=FAKE, kw=FAKE, eps=1e-6, rope=FAKE, n_rope=64,
+             main=tsl.csa2_rows(FAKE, FAKE + 256, 320, 80, tsl.CSA2_FP4_E2M1), mbase=FAKE,
+             mrows=16, k=tsl.csa2_rows(FAKE, FAKE, 128, 1, tsl.CSA2_FP8_E4M3), kbase=FAKE,
+             krows=16)
+    a.update(kw)
+    st = lib.csa2_cache_write(a["c"], a["z"], a["stride"], a["seq"], a["pos"], a["T"], a["ratio"],
+                              a["pend"], a["B"], a["kvw"], a["wik"], a["kw"],
+                              ctypes.c_float(a["eps"]), a["rope"], a["n_rope"],
+                              None if a["main"] is None else ctypes.byref(a["main"]), a["mbase"],
+                              a["mrows"], None if a["k"] is None else ctypes.byref(a["k"]),
+                              a["kbase"], a["krows"], None)
+    return st, lib.csa2_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(c=None), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(z=None), tsl.CSA2_ERR_INVALID_ARG),                 # ratio 2 needs the gates
+    (dict(ratio=4), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(T=-1), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(seq=None), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(stride=1008), tsl.CSA2_ERR_INVALID_ARG),            # below one 512-value bf16 row
+    (dict(stride=1032), tsl.CSA2_ERR_INVALID_ARG),            # not 16-byte aligned
+    (dict(c=FAKE + 8), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(pend=FAKE + 4), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(eps=-1.0), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(eps=float("inf")), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(main=None, k=None), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(mbase=None), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(wik=None), tsl.CSA2_ERR_INVALID_ARG),               # index keys need W_IK
+    (dict(kw=FAKE + 4), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(main=tsl.csa2_rows(FAKE, None, 320, 80, tsl.CSA2_FP4_E2M1)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(main=tsl.csa2_rows(FAKE, FAKE, 320, 8, tsl.CSA2_FP4_E2M1)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(main=tsl.csa2_rows(FAKE, FAKE, 288, 16, tsl.CSA2_FP4_E2M1_E4M3S16)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(main=tsl.csa2_rows(FAKE, None, 1024, 0, tsl.CSA2_F32)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(main=tsl.csa2_rows(FAKE, FAKE, 528, 132, tsl.CSA2_FP8_E4M3)), tsl.CSA2_ERR_UNSUPPORTED),
+    (dict(k=tsl.csa2_rows(FAKE, FAKE, 64, 4, tsl.CSA2_FP4_E2M1_E4M3S16)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(k=tsl.csa2_rows(FAKE, None, 128, 1, tsl.CSA2_FP8_E4M3)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(k=tsl.csa2_rows(FAKE, FAKE, 256, 8, tsl.CSA2_FP4_E2M1)), tsl.CSA2_ERR_UNSUPPORTED),
+])
+def test_cache_write_rejects(kw, status):
+    st, msg = _cw(tsl.load(), **kw)
+    assert st == status, msg
+    assert msg.startswith("csa2_cache_write")
+
+
+def test_cache_write_zero_tokens_is_a_no_op_after_checks():
+    lib = tsl.load()
+    assert _cw(lib, T=0)[0] == tsl.CSA2_OK
+    # every output format passes the same checks
+    for main, k in [(tsl.csa2_rows(FAKE, None, 2048, 0, tsl.CSA2_F32),
+                     tsl.csa2_rows(FAKE, None, 512, 0, tsl.CSA2_F32)),
+                    (tsl.csa2_rows(FAKE, FAKE + 256, 288, 288, tsl.CSA2_FP4_E2M1_E4M3S16),
+                     tsl.csa2_rows(FAKE, FAKE + 4096, 64, 8, tsl.CSA2_FP4_E2M1_E4M3S16)),
+                    (None, tsl.csa2_rows(FAKE, FAKE + 8192, 128, 1, tsl.CSA2_FP8_E4M3))]:
+        assert _cw(lib, T=0, main=main, k=k)[0] == tsl.CSA2_OK, lib.csa2_last_error()
+    # ratio 1 needs neither gates nor a pending row
+    assert _cw(lib, T=0, ratio=1, z=None, pend=None)[0] == tsl.CSA2_OK

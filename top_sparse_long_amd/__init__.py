@@ -1,6 +1,6 @@
 """Python binding of libcsa2.so, the CSA2 global-attention hot path on MI355X.
 
-The four functions below carry the names of the C entry points and do only
+The functions below carry the names of the C entry points and do only
 argument marshalling: tensors become device pointers, the current torch
 stream becomes the HIP stream, and a non-zero status raises Csa2Error.
 Every step of the path runs in the library's HIP kernels; there is no
@@ -19,7 +19,7 @@ CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1, CSA2_FP4_E2M1_E4M3S16 = 0, 1,
 EXPORTED = ("csa2_index_scores", "csa2_block_candidates", "csa2_block_candidates_workspace_size",
             "csa2_topk", "csa2_topk_workspace_size", "csa2_topk_and_block_candidates",
             "csa2_topk_and_block_candidates_workspace_size", "csa2_sparse_attn",
-            "csa2_sparse_attn_workspace_size",
+            "csa2_sparse_attn_workspace_size", "csa2_cache_write",
             "csa2_status_string", "csa2_last_error", "csa2_version")
 
 
@@ -64,11 +64,14 @@ def load():
                                      P, ctypes.c_float, P, ctypes.c_int, P, P, SZ, I32, I32, I32, P]
     lib.csa2_sparse_attn_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.csa2_sparse_attn_workspace_size.restype = SZ
+    lib.csa2_cache_write.argtypes = [P, P, I64, P, P, I32, I32, P, I32, P, P, P, ctypes.c_float,
+                                     P, I32, RP, P, I64, RP, P, I64, P]
     lib.csa2_status_string.argtypes = [ctypes.c_int]
     lib.csa2_status_string.restype = ctypes.c_char_p
     lib.csa2_last_error.restype = ctypes.c_char_p
     for fn in ("csa2_index_scores", "csa2_block_candidates", "csa2_topk",
-               "csa2_topk_and_block_candidates", "csa2_sparse_attn", "csa2_version"):
+               "csa2_topk_and_block_candidates", "csa2_sparse_attn", "csa2_cache_write",
+               "csa2_version"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -136,7 +139,7 @@ def rows_swa_records(rec):
 
 
 # ---------------------------------------------------------------------------
-# the four calls
+# the calls
 
 def csa2_index_scores(q_rows, w, w_dtype, k_rows, seq_base, q_seq, q_pos, ratio, scores,
                       n_cols, Q, cand=None, block_size=8, block_max=None, H_I=32, d_I=128,
@@ -209,3 +212,19 @@ def csa2_sparse_attn(q, q_dtype, main_rows, main_base, idx, k, swa_rows, swa_bas
                                 ratio, _ptr(attn_sink), ctypes.c_float(softmax_scale), _ptr(out),
                                 out_dtype, _ptr(lse), _ptr(workspace), wsb, Q, H, D,
                                 _stream(stream)))
+
+
+def csa2_cache_write(c, z, tok_seq, tok_pos, ratio, pend, n_seq, kv_norm_w, w_ik, k_norm_w,
+                     eps, rope_cs, main_rows, main_base, n_main_rows, k_rows, k_base,
+                     n_k_rows, stream=None):
+    """main_rows / k_rows: csa2_rows descriptors of the output rows, or None."""
+    lib = load()
+    T = 0 if tok_seq is None else tok_seq.numel()
+    _check(lib.csa2_cache_write(_ptr(c), _ptr(z), c.stride(0) * c.element_size(), _ptr(tok_seq),
+                                _ptr(tok_pos), T, ratio, _ptr(pend), n_seq, _ptr(kv_norm_w),
+                                _ptr(w_ik), _ptr(k_norm_w), ctypes.c_float(eps), _ptr(rope_cs),
+                                rope_cs.shape[0],
+                                None if main_rows is None else ctypes.byref(main_rows),
+                                _ptr(main_base), n_main_rows,
+                                None if k_rows is None else ctypes.byref(k_rows),
+                                _ptr(k_base), n_k_rows, _stream(stream)))

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -424,6 +425,112 @@ size_t csa2_sparse_attn_workspace_size(int32_t Q, int32_t H, int32_t k, int32_t 
   const int ns = csa2::attn_splits(Q, H, k, window);
   if (ns <= 1) return 0;
   return (size_t)Q * (size_t)(H / 16) * (size_t)ns * csa2::ATTN_PART_FLOATS * sizeof(float);
+}
+
+int csa2_cache_write(const void* c, const void* z, int64_t cz_stride, const int32_t* tok_seq,
+                     const int32_t* tok_pos, int32_t T, int32_t ratio, void* pend, int32_t B,
+                     const float* kv_norm_w, const void* w_ik, const float* k_norm_w, float eps,
+                     const float* rope_cs, int32_t n_rope, const csa2_rows* main_out,
+                     const int64_t* main_base, int64_t main_rows, const csa2_rows* k_out,
+                     const int64_t* k_base, int64_t k_rows, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(c && kv_norm_w && rope_cs, CSA2_ERR_INVALID_ARG, "csa2_cache_write: null pointer argument");
+  REQUIRE(T >= 0 && B >= 0 && n_rope >= 0 && main_rows >= 0 && k_rows >= 0, CSA2_ERR_INVALID_ARG,
+          "csa2_cache_write: negative size");
+  REQUIRE(T == 0 || (tok_seq && tok_pos), CSA2_ERR_INVALID_ARG, "csa2_cache_write: null token arrays");
+  REQUIRE(ratio == 1 || ratio == 2, CSA2_ERR_UNSUPPORTED, "csa2_cache_write: ratio must be 1 or 2");
+  REQUIRE(ratio == 1 || z, CSA2_ERR_INVALID_ARG, "csa2_cache_write: ratio 2 needs the gate rows z");
+  REQUIRE(main_out || k_out, CSA2_ERR_INVALID_ARG, "csa2_cache_write: no output rows given");
+  REQUIRE(eps >= 0.f && eps < INFINITY, CSA2_ERR_INVALID_ARG, "csa2_cache_write: eps must be finite and >= 0");
+  REQUIRE(cz_stride >= 1024 && cz_stride % 16 == 0 && aligned(c, 16) && (!z || aligned(z, 16)),
+          CSA2_ERR_INVALID_ARG, "csa2_cache_write: c and z rows must be 16-byte aligned with stride >= 1024 bytes");
+  REQUIRE(aligned(kv_norm_w, 16) && aligned(rope_cs, 16), CSA2_ERR_INVALID_ARG,
+          "csa2_cache_write: kv_norm_w and rope_cs must be 16-byte aligned");
+  REQUIRE(!pend || aligned(pend, 16), CSA2_ERR_INVALID_ARG, "csa2_cache_write: pend must be 16-byte aligned");
+  csa2::CacheWriteArgs a = {};
+  a.c = (const uint16_t*)c;
+  a.z = (const uint16_t*)z;
+  a.cz_stride = cz_stride;
+  a.tok_seq = tok_seq;
+  a.tok_pos = tok_pos;
+  a.T = T;
+  a.ratio = ratio;
+  a.pend = ratio == 2 ? (uint16_t*)pend : nullptr;
+  a.B = B;
+  a.kv_w = kv_norm_w;
+  a.eps = eps;
+  a.rope = rope_cs;
+  a.n_rope = n_rope;
+  if (main_out) {
+    REQUIRE(main_base && main_out->data, CSA2_ERR_INVALID_ARG, "csa2_cache_write: main_out needs data and main_base");
+    REQUIRE(aligned(main_out->data, 16) && main_out->row_stride % 16 == 0, CSA2_ERR_INVALID_ARG,
+            "csa2_cache_write: main rows must be 16-byte aligned");
+    a.main = (uint8_t*)main_out->data;
+    a.main_stride = main_out->row_stride;
+    a.main_base = main_base;
+    a.main_rows = main_rows;
+    switch (main_out->dtype) {
+      case CSA2_F32:
+        REQUIRE(main_out->row_stride >= 2048, CSA2_ERR_INVALID_ARG, "csa2_cache_write: F32 main rows below 2048 bytes");
+        a.main_fmt = csa2::CW_F32;
+        break;
+      case CSA2_FP4_E2M1:
+        REQUIRE(main_out->row_stride >= 256 && main_out->scale && aligned(main_out->scale, 4) &&
+                    main_out->scale_stride >= 16,
+                CSA2_ERR_INVALID_ARG, "csa2_cache_write: FP4 main rows need 256 code bytes and 16 fp32 scales");
+        a.main_fmt = csa2::CW_FP4;
+        a.main_scale = (uint8_t*)main_out->scale;
+        a.main_scale_stride = main_out->scale_stride * 4;
+        break;
+      case CSA2_FP4_E2M1_E4M3S16:
+        REQUIRE(main_out->row_stride >= 256 && main_out->scale && main_out->scale_stride >= 32, CSA2_ERR_INVALID_ARG,
+                "csa2_cache_write: FP4 main rows need 256 code bytes and 32 E4M3 scale bytes");
+        a.main_fmt = csa2::CW_S16;
+        a.main_scale = (uint8_t*)main_out->scale;
+        a.main_scale_stride = main_out->scale_stride;
+        break;
+      default:
+        return fail(CSA2_ERR_UNSUPPORTED, "csa2_cache_write: main rows must be F32, FP4_E2M1 or FP4_E2M1_E4M3S16");
+    }
+  }
+  if (k_out) {
+    REQUIRE(k_base && k_out->data && w_ik && k_norm_w, CSA2_ERR_INVALID_ARG,
+            "csa2_cache_write: k_out needs data, k_base, w_ik and k_norm_w");
+    REQUIRE(aligned(w_ik, 16) && aligned(k_norm_w, 16), CSA2_ERR_INVALID_ARG,
+            "csa2_cache_write: w_ik and k_norm_w must be 16-byte aligned");
+    REQUIRE(aligned(k_out->data, 16) && k_out->row_stride % 16 == 0, CSA2_ERR_INVALID_ARG,
+            "csa2_cache_write: index-key rows must be 16-byte aligned");
+    a.w_ik = (const uint16_t*)w_ik;
+    a.k_w = k_norm_w;
+    a.kd = (uint8_t*)k_out->data;
+    a.k_stride = k_out->row_stride;
+    a.k_base = k_base;
+    a.k_rows = k_rows;
+    switch (k_out->dtype) {
+      case CSA2_F32:
+        REQUIRE(k_out->row_stride >= 512, CSA2_ERR_INVALID_ARG, "csa2_cache_write: F32 key rows below 512 bytes");
+        a.k_fmt = csa2::CW_F32;
+        break;
+      case CSA2_FP8_E4M3:
+        REQUIRE(k_out->row_stride >= 128 && k_out->scale && aligned(k_out->scale, 4) && k_out->scale_stride >= 1,
+                CSA2_ERR_INVALID_ARG, "csa2_cache_write: FP8 key rows need 128 code bytes and one fp32 scale");
+        a.k_fmt = csa2::CW_FP8;
+        a.k_scale = (uint8_t*)k_out->scale;
+        a.k_scale_stride = k_out->scale_stride * 4;
+        break;
+      case CSA2_FP4_E2M1_E4M3S16:
+        REQUIRE(k_out->row_stride >= 64 && k_out->scale && k_out->scale_stride >= 8, CSA2_ERR_INVALID_ARG,
+                "csa2_cache_write: FP4 key rows need 64 code bytes and 8 E4M3 scale bytes");
+        a.k_fmt = csa2::CW_S16;
+        a.k_scale = (uint8_t*)k_out->scale;
+        a.k_scale_stride = k_out->scale_stride;
+        break;
+      default:
+        return fail(CSA2_ERR_UNSUPPORTED, "csa2_cache_write: key rows must be F32, FP8_E4M3 or FP4_E2M1_E4M3S16");
+    }
+  }
+  if (T == 0) return CSA2_OK;
+  return hip_status(csa2::launch_cache_write(a, (hipStream_t)stream), "csa2_cache_write");
 }
 
 }  // extern "C"

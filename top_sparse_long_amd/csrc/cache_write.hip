@@ -1,0 +1,436 @@
+// Full-layer cache write: pair compressor, RMSNorm, RoPE, quantize-on-write
+// of the main-KV entry, and the index key projected from the same latent.
+//
+// What is computed (CSA2 deep-dive page, "per-layer attention computation"
+// item 3; three-modes page, "compression operator simplified" and the Q&A on
+// how the index key is generated; V4.1-Flash report reading, section 6):
+//   entry e of a sequence closes at token position p = e*m + m - 1;
+//   cbar[ch] = softmax over the m tokens of z[., ch], weighting c[., ch]
+//   u = RMSNorm(cbar) * kv_norm_w                 (the latent before RoPE)
+//   main row = quantize(RoPE(u))                  RoPE on dims 448..511
+//   k = RMSNorm(u W_IK^T) * k_norm_w; index row = quantize(RoPE(k)), dims 64..127
+// RoPE turns adjacent pairs by the angles of a caller-supplied cos/sin table
+// row, the row of the entry's first token e*m.
+//
+// Kernel layout (one workgroup of 4 waves per 32*m tokens):
+//   scan     wave 0 finds the tokens that close an entry (ballot compaction);
+//   phase 1  one entry per wave at a time, lane l owning channels 8l..8l+7:
+//            16-byte bf16 loads of c and z (and of the pair partner), the
+//            per-channel softmax, a wave-wide sum of squares, the main-KV
+//            RoPE and quantization (groups of 32 or 16 channels are 4 or 2
+//            lanes), and the latent written to LDS split as bf16 hi + lo;
+//   phase 2  u W_IK^T on v_mfma_f32_32x32x16_bf16: W_IK is bf16, the latent
+//            is hi + lo (16 significant bits), so the products are exact and
+//            the sums fp32; wave w owns output columns 32w..32w+31;
+//   phase 3  the 32x128 result goes through LDS back to one entry per wave
+//            (lane l owning dims 2l, 2l+1): RMSNorm, RoPE, quantization.
+// Quantization: scale = amax / 6 (E2M1) or amax / 448 (E4M3), in fp32, or
+// rounded to E4M3 for the per-16 format; elements round to nearest even,
+// saturating.  A second, small kernel then stores the token that leaves each
+// sequence's pair open (m = 2), after every entry has read the old one.
+#include "kernels.h"
+
+namespace csa2 {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int CW_ENT = 32;          // entries per MFMA chunk
+constexpr int CW_LDA = 512 + 8;     // LDS latent row, bf16 elements (padding staggers banks)
+constexpr int CW_LDK = 128 + 4;     // LDS projected row, floats
+
+struct CwSmem {
+  union {
+    struct {
+      uint16_t hi[CW_ENT][CW_LDA];
+      uint16_t lo[CW_ENT][CW_LDA];
+    } a;
+    float k[CW_ENT][CW_LDK];
+  } u;
+  int ent_t[64];
+  int ent_src[64];   // partner token row, or -1 - seq for the pending row
+  int ent_s[64];
+  int ent_p[64];
+  int n_ent;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ uint32_t to_bf16_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// Cross-lane steps on DPP (full-rate VALU): quad permutations and the row
+// mirrors combine lanes inside a row of 16; row totals meet through
+// readlane, so a wave-wide result is uniform and its order fixed.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int DPP_XOR1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141;
+constexpr int DPP_MIRROR = 0x140;
+
+__device__ __forceinline__ float readlane(float v, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp<DPP_XOR1>(v);
+  v += dpp<DPP_XOR2>(v);
+  v += dpp<DPP_HALF_MIRROR>(v);
+  v += dpp<DPP_MIRROR>(v);
+  return (readlane(v, 0) + readlane(v, 16)) + (readlane(v, 32) + readlane(v, 48));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  v = fmaxf(v, dpp<DPP_XOR2>(v));
+  v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  v = fmaxf(v, dpp<DPP_MIRROR>(v));
+  return fmaxf(fmaxf(readlane(v, 0), readlane(v, 16)), fmaxf(readlane(v, 32), readlane(v, 48)));
+}
+
+// maximum over aligned groups of 2, 4 or 8 lanes
+template <int LANES>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp<DPP_XOR1>(v));
+  if (LANES >= 4) v = fmaxf(v, dpp<DPP_XOR2>(v));
+  if (LANES >= 8) v = fmaxf(v, dpp<DPP_HALF_MIRROR>(v));
+  return v;
+}
+
+// E2M1 codes of (a, b) into byte `sel` of w (a in the low nibble): the
+// hardware conversion rounds to nearest even and saturates at 6.
+template <int SEL>
+__device__ __forceinline__ uint32_t put_e2m1x2(uint32_t w, float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a, b, 1.0f, SEL);
+}
+
+// E4M3FN code of a finite a >= 0: round to nearest even, saturating at 448.
+// Below 2^-6 the spacing is 2^-9; in [2^E, 2^(E+1)) it is 2^(E-3), and a
+// mantissa that rounds up to 16 carries into the next exponent by itself.
+__device__ __forceinline__ uint32_t e4m3_mag(float a) {
+  if (a >= 448.f) return 0x7Eu;
+  if (a < 0.015625f) return (uint32_t)rintf(a * 512.f);
+  const int E = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;
+  const float q = rintf(a * __uint_as_float((uint32_t)(130 - E) << 23));
+  return (uint32_t)((E + 7) << 3) + (uint32_t)q - 8u;
+}
+
+__device__ __forceinline__ float e4m3_val(uint32_t c) {
+  const uint32_t e = c >> 3, m = c & 7u;
+  return e == 0 ? (float)m * 0.001953125f : __uint_as_float((e + 120u) << 23) * (1.f + 0.125f * (float)m);
+}
+
+// E4M3 scale byte of a group of the per-16 format
+__device__ __forceinline__ uint32_t s16_scale(float amax) {
+  if (!(amax > 0.f)) return 0x38u;
+  const uint32_t c = e4m3_mag(amax / 6.0f);
+  return c == 0 ? 1u : c;
+}
+
+template <int R, bool PRE_W>
+__global__ __launch_bounds__(256, PRE_W ? 1 : 2) void cache_write_kernel(CacheWriteArgs a) {
+  __shared__ CwSmem sm;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int TT = 32 * R;
+  const int t0 = blockIdx.x * TT;
+
+  // this wave's W_IK fragments (output columns 32w..32w+31): loaded first
+  // when the tile is the whole job, so their latency hides behind the scan
+  // and phase 1
+  const int r32 = lane & 31, half = lane >> 5;
+  const uint16_t* wrow = a.w_ik + (int64_t)(32 * wave + r32) * 512 + 8 * half;
+  v8bf wf[PRE_W ? 32 : 1];
+  if (PRE_W && a.kd) {
+#pragma unroll
+    for (int ks = 0; ks < 32; ++ks) wf[ks] = *(const v8bf*)(wrow + 16 * ks);
+  }
+
+  if (wave == 0) {
+    const int t = t0 + lane;
+    bool ok = false;
+    int src = 0, s = 0, p = 0;
+    if (lane < TT && t < a.T) {
+      s = a.tok_seq[t];
+      p = a.tok_pos[t];
+      if (s >= 0 && s < a.B && p >= 0 && p % R == R - 1 && p - (R - 1) < a.n_rope) {
+        if (R == 1) {
+          ok = true;
+          src = t;
+        } else if (t > 0 && a.tok_seq[t - 1] == s && a.tok_pos[t - 1] == p - 1) {
+          ok = true;
+          src = t - 1;
+        } else if (a.pend) {
+          ok = true;
+          src = -1 - s;
+        }
+      }
+    }
+    const uint64_t m = __ballot(ok);
+    const int idx = __popcll(m & ((1ull << lane) - 1ull));
+    if (ok) {
+      sm.ent_t[idx] = t;
+      sm.ent_src[idx] = src;
+      sm.ent_s[idx] = s;
+      sm.ent_p[idx] = p;
+    }
+    if (lane == 0) sm.n_ent = __popcll(m);
+  }
+  __syncthreads();
+  const int n_ent = sm.n_ent;
+  if (n_ent == 0) return;
+
+  float g8[8];
+  {
+    const float4 g0 = *(const float4*)(a.kv_w + 8 * lane);
+    const float4 g1 = *(const float4*)(a.kv_w + 8 * lane + 4);
+    g8[0] = g0.x; g8[1] = g0.y; g8[2] = g0.z; g8[3] = g0.w;
+    g8[4] = g1.x; g8[5] = g1.y; g8[6] = g1.z; g8[7] = g1.w;
+  }
+  const uint8_t* cbase = (const uint8_t*)a.c + 16 * lane;
+  const uint8_t* zbase = (const uint8_t*)a.z + 16 * lane;
+
+  for (int base = 0; base < n_ent; base += CW_ENT) {
+    const int nc = min(CW_ENT, n_ent - base);
+
+    // ---- phase 1: compress, normalise, main-KV row, latent to LDS ----------
+    for (int j0 = wave; j0 < nc; j0 += 16) {
+      uint4 cv[4], cq[4], zv[4], zq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 4 * i;
+        if (j < nc) {
+          const int t = sm.ent_t[base + j];
+          cv[i] = *(const uint4*)(cbase + (int64_t)t * a.cz_stride);
+          if (R == 2) {
+            zv[i] = *(const uint4*)(zbase + (int64_t)t * a.cz_stride);
+            const int src = sm.ent_src[base + j];
+            if (src >= 0) {
+              cq[i] = *(const uint4*)(cbase + (int64_t)src * a.cz_stride);
+              zq[i] = *(const uint4*)(zbase + (int64_t)src * a.cz_stride);
+            } else {
+              const uint8_t* pr = (const uint8_t*)a.pend + (int64_t)(-1 - src) * 2048 + 16 * lane;
+              cq[i] = *(const uint4*)pr;
+              zq[i] = *(const uint4*)(pr + 1024);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = j0 + 4 * i;
+        if (j >= nc) break;
+        float cb[8];
+        unpack8(cv[i], cb);
+        if (R == 2) {
+          // weight of the later token: e^z1 / (e^z0 + e^z1) = 1 / (1 + e^(z0 - z1))
+          float c0[8], z0[8], z1[8];
+          unpack8(cq[i], c0);
+          unpack8(zq[i], z0);
+          unpack8(zv[i], z1);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float w1 = __builtin_amdgcn_rcpf(1.0f + __expf(z0[q] - z1[q]));
+            cb[q] = fmaf(cb[q] - c0[q], w1, c0[q]);
+          }
+        }
+        float ss = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ss = fmaf(cb[q], cb[q], ss);
+        ss = wave_sum(ss);
+        const float r = 1.0f / sqrtf(ss * (1.0f / 512.0f) + a.eps);
+        float u[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) u[q] = cb[q] * r * g8[q];
+
+        // latent (before RoPE) for the projection, as bf16 hi + lo
+        if (a.kd) {
+          v8bf h, l;
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            h[q] = (__bf16)u[q];
+            l[q] = (__bf16)(u[q] - (float)h[q]);
+          }
+          *(v8bf*)&sm.u.a.hi[j][8 * lane] = h;
+          *(v8bf*)&sm.u.a.lo[j][8 * lane] = l;
+        }
+
+        if (a.main) {
+          const int s = sm.ent_s[base + j], p = sm.ent_p[base + j];
+          const int64_t row = a.main_base[s] + p / R;
+          if (row >= 0 && row < a.main_rows) {
+            if (lane >= 56) {
+              const float* cs = a.rope + (int64_t)(p + 1 - R) * 64 + 4 * (lane - 56);
+              const float4 co = *(const float4*)cs, si = *(const float4*)(cs + 32);
+              const float cc[4] = {co.x, co.y, co.z, co.w}, sn[4] = {si.x, si.y, si.z, si.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float x = u[2 * q], y = u[2 * q + 1];
+                u[2 * q] = x * cc[q] - y * sn[q];
+                u[2 * q + 1] = x * sn[q] + y * cc[q];
+              }
+            }
+            uint8_t* dst = a.main + row * a.main_stride;
+            if (a.main_fmt == CW_F32) {
+              *(float4*)(dst + 32 * lane) = make_float4(u[0], u[1], u[2], u[3]);
+              *(float4*)(dst + 32 * lane + 16) = make_float4(u[4], u[5], u[6], u[7]);
+            } else {
+              float am = 0.f;
+#pragma unroll
+              for (int q = 0; q < 8; ++q) am = fmaxf(am, fabsf(u[q]));
+              float sc;
+              uint32_t sbyte = 0;
+              if (a.main_fmt == CW_FP4) {
+                am = group_max<4>(am);
+                sc = am > 0.f ? am / 6.0f : 1.0f;
+              } else {
+                am = group_max<2>(am);
+                sbyte = s16_scale(am);
+                sc = e4m3_val(sbyte);
+              }
+              const float inv = __builtin_amdgcn_rcpf(sc);
+              uint32_t w = 0;
+              w = put_e2m1x2<0>(w, u[0] * inv, u[1] * inv);
+              w = put_e2m1x2<1>(w, u[2] * inv, u[3] * inv);
+              w = put_e2m1x2<2>(w, u[4] * inv, u[5] * inv);
+              w = put_e2m1x2<3>(w, u[6] * inv, u[7] * inv);
+              *(uint32_t*)(dst + 4 * lane) = w;
+              uint8_t* sdst = a.main_scale + row * a.main_scale_stride;
+              if (a.main_fmt == CW_FP4) {
+                if ((lane & 3) == 0) ((float*)sdst)[lane >> 2] = sc;
+              } else if ((lane & 1) == 0) {
+                sdst[lane >> 1] = (uint8_t)sbyte;
+              }
+            }
+          }
+        }
+      }
+    }
+    if (!a.kd) continue;   // uniform: no LDS is shared when only the main rows are written
+    __syncthreads();
+
+    // ---- phase 2: k = u W_IK^T on the matrix cores --------------------------
+    {
+      v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 32; ++ks) {
+        const v8bf b = PRE_W ? wf[PRE_W ? ks : 0] : *(const v8bf*)(wrow + 16 * ks);
+        const v8bf ah = *(const v8bf*)&sm.u.a.hi[r32][16 * ks + 8 * half];
+        const v8bf al = *(const v8bf*)&sm.u.a.lo[r32][16 * ks + 8 * half];
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b, acc, 0, 0, 0);
+      }
+      __syncthreads();   // every wave has read the latent before it is overwritten
+#pragma unroll
+      for (int jj = 0; jj < 16; ++jj)
+        sm.u.k[8 * (jj >> 2) + 4 * half + (jj & 3)][32 * wave + r32] = acc[jj];
+    }
+    __syncthreads();
+
+    // ---- phase 3: index-key RMSNorm, RoPE, quantization --------------------
+    {
+      const float2 gk = *(const float2*)(a.k_w + 2 * lane);
+      for (int j = wave; j < nc; j += 4) {
+        const int s = sm.ent_s[base + j], p = sm.ent_p[base + j];
+        const int64_t row = a.k_base[s] + p / R;
+        if (row < 0 || row >= a.k_rows) continue;   // uniform across the wave
+        const float2 kv = *(const float2*)&sm.u.k[j][2 * lane];
+        const float ss = wave_sum(kv.x * kv.x + kv.y * kv.y);
+        const float rr = 1.0f / sqrtf(ss * (1.0f / 128.0f) + a.eps);
+        float x0 = kv.x * rr * gk.x, x1 = kv.y * rr * gk.y;
+        if (lane >= 32) {
+          const float* cs = a.rope + (int64_t)(p + 1 - R) * 64 + (lane - 32);
+          const float co = cs[0], sn = cs[32];
+          const float y0 = x0 * co - x1 * sn, y1 = x0 * sn + x1 * co;
+          x0 = y0;
+          x1 = y1;
+        }
+        uint8_t* dst = a.kd + row * a.k_stride;
+        if (a.k_fmt == CW_F32) {
+          *(float2*)(dst + 8 * lane) = make_float2(x0, x1);
+        } else if (a.k_fmt == CW_FP8) {
+          const float am = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+          const float sc = am > 0.f ? am / 448.0f : 1.0f;
+          const float inv = __builtin_amdgcn_rcpf(sc);
+          // |x| * inv stays within 448 (1 + 2^-22); the clamp keeps the
+          // conversion, which gives NaN from 464 up, in range regardless
+          const float y0 = fminf(fmaxf(x0 * inv, -448.f), 448.f);
+          const float y1 = fminf(fmaxf(x1 * inv, -448.f), 448.f);
+          *(uint16_t*)(dst + 2 * lane) = (uint16_t)__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+          if (lane == 0) *(float*)(a.k_scale + row * a.k_scale_stride) = sc;
+        } else {
+          const float am = group_max<8>(fmaxf(fabsf(x0), fabsf(x1)));
+          const uint32_t sbyte = s16_scale(am);
+          const float inv = __builtin_amdgcn_rcpf(e4m3_val(sbyte));
+          dst[lane] = (uint8_t)put_e2m1x2<0>(0u, x0 * inv, x1 * inv);
+          if ((lane & 7) == 0) a.k_scale[row * a.k_scale_stride + (lane >> 3)] = (uint8_t)sbyte;
+        }
+      }
+    }
+    __syncthreads();   // the next chunk's latent reuses the LDS
+  }
+}
+
+// m = 2: the token that ends a sequence's run at an even position opens a
+// pair the next call closes; its c and z rows become the pending row.
+__global__ __launch_bounds__(256) void cache_pend_kernel(CacheWriteArgs a) {
+  __shared__ int list[64];
+  __shared__ int cnt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    const int t = blockIdx.x * 64 + lane;
+    bool ok = false;
+    if (t < a.T) {
+      const int s = a.tok_seq[t], p = a.tok_pos[t];
+      ok = s >= 0 && s < a.B && p >= 0 && (p & 1) == 0 &&
+           (t == a.T - 1 || a.tok_seq[t + 1] != s || (int64_t)a.tok_pos[t + 1] != (int64_t)p + 1);
+    }
+    const uint64_t m = __ballot(ok);
+    if (ok) list[__popcll(m & ((1ull << lane) - 1ull))] = t;
+    if (lane == 0) cnt = __popcll(m);
+  }
+  __syncthreads();
+  const int n = cnt;
+  // four 1 KB rows per pass: (token i, c or z) per wave
+  for (int i = wave >> 1; i < n; i += 2) {
+    const int t = list[i];
+    const int s = a.tok_seq[t];
+    const int zrow = wave & 1;
+    const uint8_t* src = (const uint8_t*)(zrow ? a.z : a.c) + (int64_t)t * a.cz_stride + 16 * lane;
+    uint8_t* dst = (uint8_t*)a.pend + (int64_t)s * 2048 + 1024 * zrow + 16 * lane;
+    *(uint4*)dst = *(const uint4*)src;
+  }
+}
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s) {
+  if (a.T == 0) return hipSuccess;
+  const int tt = 32 * a.ratio;
+  const unsigned grid = (unsigned)((a.T + tt - 1) / tt);
+  // a single tile waits on every latency in turn: its W_IK fragments are
+  // fetched before the token scan
+  const bool pre = grid <= 64;
+  if (a.ratio == 1) {
+    if (pre) hipLaunchKernelGGL((cache_write_kernel<1, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((cache_write_kernel<1, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (pre) hipLaunchKernelGGL((cache_write_kernel<2, true>), dim3(grid), dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((cache_write_kernel<2, false>), dim3(grid), dim3(256), 0, s, a);
+  }
+  if (a.ratio == 2 && a.pend)
+    hipLaunchKernelGGL(cache_pend_kernel, dim3((unsigned)((a.T + 63) / 64)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace csa2

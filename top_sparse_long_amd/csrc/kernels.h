@@ -125,4 +125,41 @@ int attn_splits(int Q, int H, int k, int window);
 hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s);
 hipError_t launch_sparse_attn_f32(const AttnArgs& a, hipStream_t s);
 
+// Full-layer cache write ------------------------------------------------------
+enum CacheFmt { CW_F32 = 0, CW_FP4 = 1, CW_FP8 = 1, CW_S16 = 2 };
+
+struct CacheWriteArgs {
+  const uint16_t* c;         // bf16 token rows [T, 512]
+  const uint16_t* z;         // bf16 gate rows (ratio 2)
+  int64_t cz_stride;         // bytes
+  const int32_t* tok_seq;
+  const int32_t* tok_pos;
+  int T;
+  int ratio;
+  uint16_t* pend;            // [B][2][512] bf16 (c row, z row), or null
+  int B;
+  const float* kv_w;         // [512] RMSNorm weight of the latent
+  const uint16_t* w_ik;      // [128, 512] bf16
+  const float* k_w;          // [128] RMSNorm weight of the index key
+  float eps;
+  const float* rope;         // [n_rope][64]: cos of the 32 frequencies, then sin
+  int n_rope;
+  uint8_t* main;             // main-KV rows (null: not written)
+  uint8_t* main_scale;
+  int64_t main_stride;       // bytes
+  int64_t main_scale_stride; // bytes
+  int main_fmt;              // CW_F32, CW_FP4 (fp32 scale per 32), CW_S16 (E4M3 per 16)
+  const int64_t* main_base;
+  int64_t main_rows;
+  uint8_t* kd;               // index-key rows (null: not written)
+  uint8_t* k_scale;
+  int64_t k_stride;
+  int64_t k_scale_stride;    // bytes
+  int k_fmt;                 // CW_F32, CW_FP8 (fp32 scale per row), CW_S16
+  const int64_t* k_base;
+  int64_t k_rows;
+};
+
+hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
+
 }  // namespace csa2

@@ -137,7 +137,9 @@ STAGE_KERNELS = {
     "topk_pool": ("select_kernel<1,",),
     "topk_and_blocks": ("select_pair_kernel", "select_kernel<0,", "select_kernel<2,", "select_kernel<3,"),
     "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_combine_kernel", "sparse_attn_f32_kernel"),
-    "cache_write": ("cache_write_kernel", "cache_pend_kernel"),
+    # the 65,536-token m = 2 chunk (the decode-batch calls use the prefetching
+    # variant, cache_write_kernel<m, true>, and are not part of this record)
+    "cache_write": ("cache_write_kernel<2, false>", "cache_pend_kernel"),
 }
 CALIB_KERNEL = "__amd_rocclr_copyBuffer"
 CALIB_KIB = 256 * 1024          # the benchmark's calibration copy moves 256 MiB each way

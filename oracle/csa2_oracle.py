@@ -615,3 +615,48 @@ def run_layers(layers, k_rows, main_rows, seq_base, q_seq, q_pos, ratio,
                                          q_seq, q_pos, lay["sink"], scale, ratio)
         results.append(r)
     return results
+
+
+# ----------------------------------------------------------------------------
+# Serving-shaped I/O ([DSA] top-k section: the KV cache is paged, so each
+# selected position p becomes the physical slot table[p // 64] * 64 + p % 64
+# of a 64-slot page, -1 staying -1, and the sparse kernel gathers by slot;
+# [CSA2] core formula: the attention output is turned back by RoPE before
+# the output projection)
+#
+# Readings: a page-table entry that is negative, or a page past the row's
+# width, names no slot (-1).  The output's turned dims (the last 64 of each
+# head) are turned back by the query's own position with the table the cache
+# write used; a position outside the table leaves the output as it is.
+# ----------------------------------------------------------------------------
+
+PAGE_SLOTS = 64
+
+
+def slots_from_positions(idx, q_seq, page_table):
+    """idx [Q, k] positions (-1 padded), q_seq [Q], page_table [B, n_pages]
+    -> [Q, k] physical slots."""
+    idx = np.asarray(idx, dtype=np.int64)
+    table = np.asarray(page_table, dtype=np.int64)
+    out = np.full(idx.shape, -1, dtype=np.int64)
+    for t in range(idx.shape[0]):
+        row = table[int(q_seq[t])]
+        for j in range(idx.shape[1]):
+            p = int(idx[t, j])
+            if p < 0 or p // PAGE_SLOTS >= len(row):
+                continue
+            page = int(row[p // PAGE_SLOTS])
+            if page >= 0:
+                out[t, j] = page * PAGE_SLOTS + p % PAGE_SLOTS
+    return out
+
+
+def unturn_heads(out, q_pos, rope_cos, rope_sin):
+    """out [Q, H, D]: the last 64 dims of every head turned back by the
+    query's position (the inverse of rope_tail at that position)."""
+    out = np.array(out, dtype=np.float64)
+    for t in range(out.shape[0]):
+        p = int(q_pos[t])
+        if 0 <= p < len(rope_cos):
+            out[t] = rope_tail(out[t], rope_cos[p], -np.asarray(rope_sin[p], dtype=np.float64))
+    return out

@@ -274,3 +274,43 @@ def test_cache_write_decode_batch_and_skips():
     assert np.allclose(main[0], oracle.rope_tail(u, cos[4], sin[4]), atol=1e-13)
     assert np.array_equal(nc[1], c[1]) and np.array_equal(nz[1], z[1])
     assert np.array_equal(nc[0], pc[0]) and np.array_equal(nc[2], pc[2])
+
+
+# --------------------------------------------------------------------------
+# Serving-shaped I/O (DSA page, top-k section; CSA2 core formula)
+
+def test_slots_from_positions_by_hand():
+    table = np.array([[3, 0, 7], [5, -1, 2]])
+    idx = np.array([[0, 63, 64, 130, -1], [1, 70, 128, 191, 200]])
+    got = oracle.slots_from_positions(idx, np.array([0, 1]), table)
+    assert got.tolist() == [[192, 255, 0, 450, -1],
+                            [321, -1, 128, 191, -1]]   # page -1 and a page past the row
+
+
+def test_slots_of_an_identity_table_are_flat_rows():
+    rng = np.random.default_rng(16)
+    B, n_pages = 3, 5
+    table = np.arange(B * n_pages).reshape(B, n_pages)
+    idx = rng.integers(-1, n_pages * 64, size=(6, 40))
+    q_seq = np.array([0, 1, 2, 2, 1, 0])
+    got = oracle.slots_from_positions(idx, q_seq, table)
+    want = np.where(idx >= 0, q_seq[:, None] * n_pages * 64 + idx, -1)
+    assert np.array_equal(got, want)
+
+
+def test_unturn_gives_the_relative_turn():
+    """A key turned at position s, attended from position t and turned back
+    there, is turned by the angle difference s - t."""
+    cos, sin = _table(300)
+    rng = np.random.default_rng(17)
+    v = rng.normal(size=(1, 2, 512))
+    s_pos, t_pos = 37, 251
+    keyed = oracle.rope_tail(v, cos[s_pos], sin[s_pos])
+    got = oracle.unturn_heads(keyed, np.array([t_pos]), cos, sin)
+    f = 10000.0 ** (-np.arange(32) * 2.0 / 64.0)
+    d = (s_pos - t_pos) * f
+    want = oracle.rope_tail(v, np.cos(d), np.sin(d))
+    assert np.allclose(got, want, atol=1e-12)
+    assert np.array_equal(got[0, :, :448], v[0, :, :448])
+    # outside the table: unchanged
+    assert np.array_equal(oracle.unturn_heads(keyed, np.array([300]), cos, sin), keyed)

@@ -85,6 +85,27 @@ typedef struct {
 } csa2_rows;
 
 /*
+ * Paged caches ([DSA] top-k section: the KV cache is paged, so position p of
+ * a sequence lives in slot table[p / 64] * 64 + p % 64 of a pool of 64-slot
+ * pages, and the top-k hands the sparse kernel slots, not positions; [DSA]
+ * implementation notes: a page of the index-key cache holds its 64 keys
+ * (64 x 128 B) and then their 64 fp32 scales, 8448 B).
+ */
+typedef struct {
+    const int32_t* table;   /* [B, table_stride] int32: the physical page of each
+                               64-position page of each sequence; a negative entry,
+                               or a page at or past table_stride, is missing */
+    int64_t table_stride;   /* entries per sequence (>= 1) */
+    int32_t n_pages;        /* csa2_index_scores: pages in the pool; entries at or
+                               past it are missing (>= 1) */
+    int64_t page_stride;    /* csa2_index_scores: bytes from one page to the next, in
+                               k_idx's data and in its scales alike (the 8448-B page:
+                               8448, with scale = data + 8192); 0 = flat rows, page P
+                               holding rows 64P .. 64P + 63 of both arrays */
+    const int32_t* q_seq;   /* csa2_topk: [Q] sequence of each score row */
+} csa2_pages;
+
+/*
  * csa2_index_scores — Lightning-Indexer scores
  *   I[t, s] = sum_h w[t, h] * ReLU(q[t, h] . k[s])
  * ([CSA2] "per-layer attention computation", item 4; [DSA] "Lightning
@@ -127,6 +148,11 @@ typedef struct {
  *             the same pass so csa2_block_candidates need not re-read the
  *             scores.  Needs block_size <= 32 and block_max_stride >=
  *             ceil(n_cols / block_size).
+ *   pages     NULL, or a paged index-key cache (csa2_pages): position p of
+ *             sequence q_seq[t] is read from slot (table[p / 64], p % 64) of
+ *             k_idx, at page * page_stride + (p % 64) * row_stride (scales
+ *             alike); seq_base is not used (may be NULL); a position whose
+ *             page is missing scores -inf.
  *   Supported: H_I = 32, d_I = 128 (FP8); H_I <= 64, d_I = 128 (F32);
  *   block_size in {1, 2, 4, 8, 16, 32, 64}.
  */
@@ -136,7 +162,8 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
                       const int32_t* cand, int32_t n_cand_blocks, int32_t block_size,
                       float* scores, int64_t score_stride, int32_t n_cols,
                       float* block_max, int64_t block_max_stride,
-                      int32_t Q, int32_t H_I, int32_t d_I, void* stream);
+                      int32_t Q, int32_t H_I, int32_t d_I, const csa2_pages* pages,
+                      void* stream);
 
 /*
  * csa2_block_candidates — the candidate pool of the hierarchical sparse
@@ -184,12 +211,18 @@ size_t csa2_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t b
  *             multiple of 4 (as csa2_index_scores writes them).
  *   idx       [Q, k] int32 output: chosen positions ascending, then -1.
  *   workspace at least csa2_topk_workspace_size(Q, n_cols, k) bytes.
+ *   pages     NULL, or a page table (csa2_pages: table, table_stride, q_seq):
+ *             each chosen position p of row t is written as the slot
+ *             table[q_seq[t]][p / 64] * 64 + p % 64, in the same order, and
+ *             as -1 when its page is missing — the translation the sparse
+ *             kernel's slot mode (csa2_attn_io.idx_slots) reads.
  *   Supported: 1 <= k <= 2048.
  */
 int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols,
               const int32_t* q_pos, int32_t ratio, const int32_t* cand,
               int32_t n_cand_blocks, int32_t block_size, int32_t k, int32_t* idx,
-              void* workspace, size_t workspace_bytes, int32_t Q, void* stream);
+              void* workspace, size_t workspace_bytes, int32_t Q, const csa2_pages* pages,
+              void* stream);
 
 size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k);
 
@@ -207,6 +240,9 @@ size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k);
  * two calls; scores is required (the top-k reads it) and q_pos is required.
  *   workspace at least csa2_topk_and_block_candidates_workspace_size(Q,
  *             n_cols, k, block_size, n_blocks) bytes, 16-byte aligned.
+ *   pages     NULL, or a page table for the top-k output as in csa2_topk
+ *             (the candidate blocks stay block ids: pool scoring reads them
+ *             through the same table).
  *   Supported: within both calls' limits (1 <= k <= 2048, n_blocks <= 4096,
  *             block_size a power of two <= 64, ratio 1 or 2).
  */
@@ -215,7 +251,7 @@ int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, in
                                    const int32_t* q_pos, int32_t ratio, int32_t k, int32_t* idx,
                                    int32_t block_size, int32_t n_blocks, int32_t* cand,
                                    void* workspace, size_t workspace_bytes, int32_t Q,
-                                   void* stream);
+                                   const csa2_pages* pages, void* stream);
 
 size_t csa2_topk_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t k,
                                                      int32_t block_size, int32_t n_blocks);
@@ -262,10 +298,31 @@ size_t csa2_topk_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, 
  *             over several workgroups and combine their partial softmax
  *             sums in a second kernel; results are the same up to rounding
  *             order.  With less, each (query, 16 heads) is one workgroup.
+ *   io        NULL, or serving-shaped options (csa2_attn_io below).
  *   Supported: D = 512; H a multiple of 16 up to 128; k <= 2048.
  *   Quantized path: q BF16, main FP4_E2M1, swa FP8_E4M3, out BF16 or F32.
  *   Float path: q, main, swa F32, out F32.
  */
+typedef struct {
+    /* NULL, or fp32 [n_rope, 64]: row r holds cos of the 32 RoPE angles of
+     * position r, then their sin (the table csa2_cache_write takes).  Dims
+     * 448..511 of every head's output are turned back by the query's
+     * position before it is written ([CSA2] core formula: the output is
+     * inverse-RoPE'd before the grouped output projection): for the pair
+     * (x, y) = dims (448 + 2i, 449 + 2i), x' = x cos_i + y sin_i and
+     * y' = y cos_i - x sin_i.  A query whose position is outside the table
+     * is written unturned.  16-byte aligned. */
+    const float* rope_cs;
+    int32_t n_rope;
+    /* Nonzero: idx holds physical main_kv rows, as csa2_topk writes them
+     * through a page table ([DSA] top-k section: the sparse kernel gathers
+     * by slot and never needs the positions); entries outside
+     * [0, n_main_rows) are skipped, and main_base and the visibility bound
+     * are not used (main_base may be NULL). */
+    int32_t idx_slots;
+    int64_t n_main_rows;
+} csa2_attn_io;
+
 int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv,
                      const int64_t* main_base, const int32_t* idx, int32_t k,
                      const csa2_rows* swa_kv, const int64_t* swa_base,
@@ -273,7 +330,8 @@ int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv
                      const int32_t* q_seq, const int32_t* q_pos, int32_t ratio,
                      const float* attn_sink, float softmax_scale, void* out,
                      csa2_dtype out_dtype, float* lse, void* workspace,
-                     size_t workspace_bytes, int32_t Q, int32_t H, int32_t D, void* stream);
+                     size_t workspace_bytes, int32_t Q, int32_t H, int32_t D,
+                     const csa2_attn_io* io, void* stream);
 
 /* Workspace bytes csa2_sparse_attn uses to split keys for Q queries of H
  * heads with k indices and an SWA window of `window` (0 when it would not

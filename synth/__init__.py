@@ -14,5 +14,5 @@ from .formats import (  # noqa: F401
 )
 from .workloads import (  # noqa: F401
     Workload, make_workload, mini_workload, CONFIG_NAMES, EXTRA_WORKLOADS,
-    CacheWriteInputs, cache_write_inputs, rope_table,
+    CacheWriteInputs, cache_write_inputs, rope_table, PagedLayout, paged_layout,
 )

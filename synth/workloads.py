@@ -369,3 +369,71 @@ def cache_write_inputs(seed, runs, ratio, device, n_seq=None, with_pend=True, n_
                             tok_seq=seq.to(device), tok_pos=pos.to(device), ratio=ratio,
                             n_seq=n_seq, pend=pend, kv_norm_w=kvw.contiguous(),
                             k_norm_w=kw.contiguous(), w_ik=w_ik.contiguous(), rope_cs=rope)
+
+
+# ---------------------------------------------------------------------------
+# Paged serving layout of a workload's caches (DSA page, top-k section and
+# implementation notes: 64-slot pages; an index-key page holds its 64 keys and
+# then their 64 scales, 8448 B for FP8 keys with fp32 scales)
+
+PAGE_SLOTS = 64
+
+
+@dataclass
+class PagedLayout:
+    """page_table int32 [B, pages of the longest sequence] (-1 past a
+    sequence's pages); k_pool u8 [n_pages, k_page_bytes]: each page holds
+    64 key rows of k_row_bytes, then 64 scale rows of k_scale_row_bytes from
+    k_scale_offset; main_pool u8 [n_pages * 64, record bytes] (slot rows);
+    rope_cs fp32 [positions, 64]."""
+    page_table: torch.Tensor
+    n_pages: int
+    k_pool: torch.Tensor
+    k_page_bytes: int
+    k_row_bytes: int
+    k_scale_offset: int
+    k_scale_row_bytes: int
+    main_pool: torch.Tensor
+    rope_cs: torch.Tensor
+
+
+def paged_layout(wl, seed, spare_pages=3):
+    """Scatter a quantized workload's index keys and main-KV records into a
+    pool of 64-slot pages in a seeded random page order (plus a few pages no
+    sequence uses).  Only bytes move; values are the workload's."""
+    assert wl.quantized
+    dev = wl.k_idx.device
+    per = [(n + PAGE_SLOTS - 1) // PAGE_SLOTS for n in wl.n_entries]
+    n_pages = sum(per) + spare_pages
+    g = torch.Generator()
+    g.manual_seed(int(np.random.SeedSequence([int(seed), 90]).generate_state(1, np.uint64)[0]) & ((1 << 63) - 1))
+    perm = torch.randperm(n_pages, generator=g).to(torch.int32)
+    table = torch.full((wl.B, max(per)), -1, dtype=torch.int32)
+    o = 0
+    for b, n in enumerate(per):
+        table[b, :n] = perm[o:o + n]
+        o += n
+    table = table.to(dev)
+    fp4 = getattr(wl, "k_fmt", "fp8") == "fp4s16"
+    kb = 64 if fp4 else 128
+    sb = 8 if fp4 else 4
+    page_bytes = PAGE_SLOTS * (kb + sb)
+    k_pool = torch.zeros((n_pages, page_bytes), dtype=torch.uint8, device=dev)
+    rec = wl.main_kv.shape[1]
+    main_pool = torch.zeros((n_pages * PAGE_SLOTS, rec), dtype=torch.uint8, device=dev)
+    k_scale_bytes = wl.k_scale.contiguous().view(torch.uint8).reshape(wl.k_idx.shape[0], sb)
+    for b, n in enumerate(wl.n_entries):
+        p = torch.arange(n, device=dev)
+        page = table[b, p // PAGE_SLOTS].to(torch.int64)
+        slot = p % PAGE_SLOTS
+        rows = int(wl.seq_base[b].item()) + p
+        kflat = k_pool.view(-1)
+        kidx = (page * page_bytes + slot * kb)[:, None] + torch.arange(kb, device=dev)[None, :]
+        kflat[kidx.reshape(-1)] = wl.k_idx[rows].reshape(-1)
+        sidx = (page * page_bytes + PAGE_SLOTS * kb + slot * sb)[:, None] + torch.arange(sb, device=dev)[None, :]
+        kflat[sidx.reshape(-1)] = k_scale_bytes[rows].reshape(-1)
+        main_pool[page * PAGE_SLOTS + slot] = wl.main_kv[rows]
+    rope = rope_table(int(wl.q_pos.max().item()) + 1, dev)
+    return PagedLayout(page_table=table.contiguous(), n_pages=n_pages, k_pool=k_pool,
+                       k_page_bytes=page_bytes, k_row_bytes=kb, k_scale_offset=PAGE_SLOTS * kb,
+                       k_scale_row_bytes=sb, main_pool=main_pool, rope_cs=rope)

@@ -45,12 +45,14 @@ def _rows(dtype, stride=128, scale=True):
 def _scores(lib, **kw):
     a = dict(q=_rows(tsl.CSA2_FP8_E4M3), w=FAKE, wdt=tsl.CSA2_BF16, k=_rows(tsl.CSA2_FP8_E4M3),
              seq_base=FAKE, q_seq=FAKE, q_pos=FAKE, ratio=1, cand=None, ncb=0, bs=8,
-             scores=FAKE, stride=1024, n_cols=1024, bmax=None, bms=0, Q=1, H=32, d=128)
+             scores=FAKE, stride=1024, n_cols=1024, bmax=None, bms=0, Q=1, H=32, d=128,
+             pages=None)
     a.update(kw)
     st = lib.csa2_index_scores(ctypes.byref(a["q"]), a["w"], a["wdt"], ctypes.byref(a["k"]),
                                a["seq_base"], a["q_seq"], a["q_pos"], a["ratio"], a["cand"],
                                a["ncb"], a["bs"], a["scores"], a["stride"], a["n_cols"],
-                               a["bmax"], a["bms"], a["Q"], a["H"], a["d"], None)
+                               a["bmax"], a["bms"], a["Q"], a["H"], a["d"],
+                               None if a["pages"] is None else ctypes.byref(a["pages"]), None)
     return st, lib.csa2_last_error().decode()
 
 
@@ -82,20 +84,20 @@ def test_index_scores_rejects(kw, status):
 
 def test_topk_rejects():
     lib = tsl.load()
-    assert lib.csa2_topk(None, 64, 64, FAKE, 1, None, 0, 8, 8, FAKE, None, 0, 1, None) == \
+    assert lib.csa2_topk(None, 64, 64, FAKE, 1, None, 0, 8, 8, FAKE, None, 0, 1, None, None) == \
         tsl.CSA2_ERR_INVALID_ARG
-    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 1, None, 0, 8, 4096, FAKE, None, 0, 1, None) == \
+    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 1, None, 0, 8, 4096, FAKE, None, 0, 1, None, None) == \
         tsl.CSA2_ERR_UNSUPPORTED
-    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 1, None, 0, 8, 0, FAKE, None, 0, 1, None) == \
+    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 1, None, 0, 8, 0, FAKE, None, 0, 1, None, None) == \
         tsl.CSA2_ERR_INVALID_ARG
-    assert lib.csa2_topk(FAKE, 32, 64, FAKE, 1, None, 0, 8, 8, FAKE, None, 0, 1, None) == \
+    assert lib.csa2_topk(FAKE, 32, 64, FAKE, 1, None, 0, 8, 8, FAKE, None, 0, 1, None, None) == \
         tsl.CSA2_ERR_INVALID_ARG
-    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 5, None, 0, 8, 8, FAKE, None, 0, 1, None) == \
+    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 5, None, 0, 8, 8, FAKE, None, 0, 1, None, None) == \
         tsl.CSA2_ERR_UNSUPPORTED
     # long rows need a workspace
     need = lib.csa2_topk_workspace_size(4, 200000, 512)
     assert need > 0
-    st = lib.csa2_topk(FAKE, 200000, 200000, FAKE, 1, None, 0, 8, 512, FAKE, FAKE, need - 1, 4, None)
+    st = lib.csa2_topk(FAKE, 200000, 200000, FAKE, 1, None, 0, 8, 512, FAKE, FAKE, need - 1, 4, None, None)
     assert st == tsl.CSA2_ERR_WORKSPACE
     assert "workspace" in lib.csa2_last_error().decode()
 
@@ -124,15 +126,15 @@ def test_topk_and_block_candidates_rejects():
     lib = tsl.load()
     f = lib.csa2_topk_and_block_candidates
     # scores, q_pos, block size, k and the pool size are checked as in the separate calls
-    assert f(None, 64, 64, None, 0, FAKE, 1, 8, FAKE, 8, 16, FAKE, None, 0, 1, None) == \
+    assert f(None, 64, 64, None, 0, FAKE, 1, 8, FAKE, 8, 16, FAKE, None, 0, 1, None, None) == \
         tsl.CSA2_ERR_INVALID_ARG
-    assert f(FAKE, 64, 64, None, 0, None, 1, 8, FAKE, 8, 16, FAKE, None, 0, 1, None) == \
+    assert f(FAKE, 64, 64, None, 0, None, 1, 8, FAKE, 8, 16, FAKE, None, 0, 1, None, None) == \
         tsl.CSA2_ERR_INVALID_ARG
-    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 8, FAKE, 12, 16, FAKE, None, 0, 1, None) == \
+    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 8, FAKE, 12, 16, FAKE, None, 0, 1, None, None) == \
         tsl.CSA2_ERR_UNSUPPORTED
-    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 4096, FAKE, 8, 16, FAKE, None, 0, 1, None) == \
+    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 4096, FAKE, 8, 16, FAKE, None, 0, 1, None, None) == \
         tsl.CSA2_ERR_UNSUPPORTED
-    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 8, FAKE, 8, 8192, FAKE, None, 0, 1, None) == \
+    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 8, FAKE, 8, 8192, FAKE, None, 0, 1, None, None) == \
         tsl.CSA2_ERR_UNSUPPORTED
     # the workspace holds both selections' lists
     Q, n = 2, 1 << 20
@@ -141,12 +143,12 @@ def test_topk_and_block_candidates_rejects():
     b = lib.csa2_block_candidates_workspace_size(Q, n, 8, 2048)
     assert t > 0 and b > 0 and need >= t + b and need - (t + b) < 16
     for short in (need - 1, t, 0):
-        assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, FAKE, short, Q, None) == \
+        assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, FAKE, short, Q, None, None) == \
             tsl.CSA2_ERR_WORKSPACE
-    assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, FAKE + 4, need, Q, None) == \
+    assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, FAKE + 4, need, Q, None, None) == \
         tsl.CSA2_ERR_INVALID_ARG
     # Q == 0 passes every check and enqueues nothing
-    assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, None, 0, 0, None) == tsl.CSA2_OK
+    assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, None, 0, 0, None, None) == tsl.CSA2_OK
 
 
 def test_index_scores_fp4_key_checks():
@@ -159,7 +161,7 @@ def test_index_scores_fp4_key_checks():
     def call(qr, kr, Q=1):
         return lib.csa2_index_scores(ctypes.byref(qr), FAKE, tsl.CSA2_BF16, ctypes.byref(kr), FAKE,
                                      FAKE, FAKE, 1, None, 0, 8, FAKE, 64, 64, None, 0, Q, 32, 128,
-                                     None)
+                                     None, None)
     assert call(q, k_ok, Q=0) == tsl.CSA2_OK
     assert call(q, tsl.csa2_rows(FAKE, FAKE + 2, 64, 8, tsl.CSA2_FP4_E2M1_E4M3S16)) == \
         tsl.CSA2_ERR_INVALID_ARG
@@ -186,13 +188,14 @@ def _attn(lib, **kw):
              swa=tsl.csa2_rows(FAKE, FAKE + 512, 528, 132, tsl.CSA2_FP8_E4M3),
              swa_base=FAKE, swa_pos0=FAKE, swa_lo=None, window=128, q_seq=FAKE, q_pos=FAKE,
              ratio=1, sink=FAKE, scale=0.044, out=FAKE, odt=tsl.CSA2_BF16, lse=None, ws=None,
-             wsb=0, Q=1, H=64, D=512)
+             wsb=0, Q=1, H=64, D=512, io=None)
     a.update(kw)
     return lib.csa2_sparse_attn(a["q"], a["qdt"], ctypes.byref(a["main"]), a["main_base"],
                                 a["idx"], a["k"], ctypes.byref(a["swa"]), a["swa_base"],
                                 a["swa_pos0"], a["swa_lo"], a["window"], a["q_seq"], a["q_pos"],
                                 a["ratio"], a["sink"], ctypes.c_float(a["scale"]), a["out"],
-                                a["odt"], a["lse"], a["ws"], a["wsb"], a["Q"], a["H"], a["D"], None)
+                                a["odt"], a["lse"], a["ws"], a["wsb"], a["Q"], a["H"], a["D"],
+                                None if a["io"] is None else ctypes.byref(a["io"]), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -213,6 +216,10 @@ def _attn(lib, **kw):
     (dict(main=tsl.csa2_rows(FAKE, FAKE + 256, 288, 20, tsl.CSA2_FP4_E2M1_E4M3S16)),
      tsl.CSA2_ERR_INVALID_ARG),
     (dict(ws=FAKE + 4, wsb=1 << 30), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(io=tsl.csa2_attn_io(FAKE + 4, 64, 0, 0)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(io=tsl.csa2_attn_io(FAKE, -1, 0, 0)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(io=tsl.csa2_attn_io(None, 0, 1, -5)), tsl.CSA2_ERR_INVALID_ARG),
+    (dict(main_base=None), tsl.CSA2_ERR_INVALID_ARG),         # needed unless idx holds slots
 ])
 def test_sparse_attn_rejects(kw, status):
     lib = tsl.load()
@@ -238,6 +245,9 @@ def test_zero_queries_is_a_no_op_after_checks():
     st, _ = _scores(lib, Q=0)
     assert st == tsl.CSA2_OK
     assert _attn(lib, Q=0) == tsl.CSA2_OK
+    # slot indices need no main_base; an inverse-RoPE table passes the checks
+    assert _attn(lib, Q=0, main_base=None, io=tsl.csa2_attn_io(None, 0, 1, 1 << 20)) == tsl.CSA2_OK
+    assert _attn(lib, Q=0, io=tsl.csa2_attn_io(FAKE, 4096, 0, 0)) == tsl.CSA2_OK
     # the pages' 288-byte main-KV record passes the same checks
     assert _attn(lib, Q=0, main=tsl.csa2_rows(FAKE, FAKE + 256, 288, 288,
                                               tsl.CSA2_FP4_E2M1_E4M3S16)) == tsl.CSA2_OK
@@ -302,3 +312,27 @@ def test_cache_write_zero_tokens_is_a_no_op_after_checks():
         assert _cw(lib, T=0, main=main, k=k)[0] == tsl.CSA2_OK, lib.csa2_last_error()
     # ratio 1 needs neither gates nor a pending row
     assert _cw(lib, T=0, ratio=1, z=None, pend=None)[0] == tsl.CSA2_OK
+
+
+def test_page_table_checks():
+    lib = tsl.load()
+    good = tsl.csa2_pages(FAKE, 16, 100, 8448, FAKE)
+    # index scores: seq_base may be NULL with pages; the table, its width, the
+    # pool size and a 16-byte page stride are required
+    st, msg = _scores(lib, Q=0, seq_base=None, pages=good)
+    assert st == tsl.CSA2_OK, msg
+    assert _scores(lib, seq_base=None)[0] == tsl.CSA2_ERR_INVALID_ARG
+    for bad in (tsl.csa2_pages(None, 16, 100, 8448, None), tsl.csa2_pages(FAKE, 0, 100, 8448, None),
+                tsl.csa2_pages(FAKE, 16, 0, 8448, None), tsl.csa2_pages(FAKE, 16, 100, 8440, None),
+                tsl.csa2_pages(FAKE, 16, 100, -16, None)):
+        st, msg = _scores(lib, pages=bad)
+        assert st == tsl.CSA2_ERR_INVALID_ARG and "pages" in msg
+    # top-k: the table and the row sequences are required
+    pp = ctypes.byref
+    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 1, None, 0, 8, 8, FAKE, None, 0, 0, pp(good), None) == \
+        tsl.CSA2_OK
+    assert lib.csa2_topk(FAKE, 64, 64, FAKE, 1, None, 0, 8, 8, FAKE, None, 0, 1,
+                         pp(tsl.csa2_pages(FAKE, 16, 0, 0, None)), None) == tsl.CSA2_ERR_INVALID_ARG
+    f = lib.csa2_topk_and_block_candidates
+    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 8, FAKE, 8, 16, FAKE, None, 0, 1,
+             pp(tsl.csa2_pages(None, 16, 0, 0, FAKE)), None) == tsl.CSA2_ERR_INVALID_ARG

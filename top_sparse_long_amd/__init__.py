@@ -29,6 +29,24 @@ class Csa2Error(RuntimeError):
         self.status = status
 
 
+class csa2_pages(ctypes.Structure):
+    _fields_ = [("table", ctypes.c_void_p), ("table_stride", ctypes.c_int64),
+                ("n_pages", ctypes.c_int32), ("page_stride", ctypes.c_int64),
+                ("q_seq", ctypes.c_void_p)]
+
+
+def pages_of(table, n_pages=0, page_stride=0, q_seq=None):
+    """csa2_pages over an int32 [B, n] page table tensor."""
+    assert table.dtype == torch.int32 and table.is_contiguous() and table.dim() == 2
+    return csa2_pages(table.data_ptr(), table.shape[1], n_pages, page_stride,
+                      None if q_seq is None else q_seq.data_ptr())
+
+
+class csa2_attn_io(ctypes.Structure):
+    _fields_ = [("rope_cs", ctypes.c_void_p), ("n_rope", ctypes.c_int32),
+                ("idx_slots", ctypes.c_int32), ("n_main_rows", ctypes.c_int64)]
+
+
 class csa2_rows(ctypes.Structure):
     _fields_ = [("data", ctypes.c_void_p), ("scale", ctypes.c_void_p),
                 ("row_stride", ctypes.c_int64), ("scale_stride", ctypes.c_int64),
@@ -48,20 +66,22 @@ def load():
     lib = ctypes.CDLL(_LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     RP = ctypes.POINTER(csa2_rows)
+    PP = ctypes.POINTER(csa2_pages)
     lib.csa2_index_scores.argtypes = [RP, P, ctypes.c_int, RP, P, P, P, I32, P, I32, I32, P, I64,
-                                      I32, P, I64, I32, I32, I32, P]
+                                      I32, P, I64, I32, I32, I32, PP, P]
     lib.csa2_block_candidates.argtypes = [P, I64, I32, P, I64, P, I32, I32, I32, P, P, SZ, I32, P]
     lib.csa2_block_candidates_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.csa2_block_candidates_workspace_size.restype = SZ
-    lib.csa2_topk.argtypes = [P, I64, I32, P, I32, P, I32, I32, I32, P, P, SZ, I32, P]
+    lib.csa2_topk.argtypes = [P, I64, I32, P, I32, P, I32, I32, I32, P, P, SZ, I32, PP, P]
     lib.csa2_topk_workspace_size.argtypes = [I32, I32, I32]
     lib.csa2_topk_workspace_size.restype = SZ
     lib.csa2_topk_and_block_candidates.argtypes = [P, I64, I32, P, I64, P, I32, I32, P, I32, I32,
-                                                   P, P, SZ, I32, P]
+                                                   P, P, SZ, I32, PP, P]
     lib.csa2_topk_and_block_candidates_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.csa2_topk_and_block_candidates_workspace_size.restype = SZ
     lib.csa2_sparse_attn.argtypes = [P, ctypes.c_int, RP, P, P, I32, RP, P, P, P, I32, P, P, I32,
-                                     P, ctypes.c_float, P, ctypes.c_int, P, P, SZ, I32, I32, I32, P]
+                                     P, ctypes.c_float, P, ctypes.c_int, P, P, SZ, I32, I32, I32,
+                                     ctypes.POINTER(csa2_attn_io), P]
     lib.csa2_sparse_attn_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.csa2_sparse_attn_workspace_size.restype = SZ
     lib.csa2_cache_write.argtypes = [P, P, I64, P, P, I32, I32, P, I32, P, P, P, ctypes.c_float,
@@ -141,16 +161,22 @@ def rows_swa_records(rec):
 # ---------------------------------------------------------------------------
 # the calls
 
+def _byref(x):
+    return None if x is None else ctypes.byref(x)
+
+
 def csa2_index_scores(q_rows, w, w_dtype, k_rows, seq_base, q_seq, q_pos, ratio, scores,
                       n_cols, Q, cand=None, block_size=8, block_max=None, H_I=32, d_I=128,
-                      stream=None):
+                      stream=None, pages=None):
+    """pages: an optional csa2_pages (paged index-key cache)."""
     lib = load()
     ncb = 0 if cand is None else cand.shape[-1]
     bms = 0 if block_max is None else block_max.stride(0)
     _check(lib.csa2_index_scores(ctypes.byref(q_rows), _ptr(w), w_dtype, ctypes.byref(k_rows),
                                  _ptr(seq_base), _ptr(q_seq), _ptr(q_pos), ratio, _ptr(cand), ncb,
                                  block_size, _ptr(scores), scores.stride(0), n_cols,
-                                 _ptr(block_max), bms, Q, H_I, d_I, _stream(stream)))
+                                 _ptr(block_max), bms, Q, H_I, d_I, _byref(pages),
+                                 _stream(stream)))
 
 
 def csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks):
@@ -173,12 +199,14 @@ def csa2_block_candidates(scores, n_cols, q_pos, ratio, block_size, n_blocks, ca
 
 
 def csa2_topk(scores, n_cols, q_pos, ratio, k, idx, workspace, Q, cand=None, block_size=8,
-              stream=None):
+              stream=None, pages=None):
+    """pages: an optional csa2_pages (table, q_seq): idx receives slots."""
     lib = load()
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     ncb = 0 if cand is None else cand.shape[-1]
     _check(lib.csa2_topk(_ptr(scores), scores.stride(0), n_cols, _ptr(q_pos), ratio, _ptr(cand),
-                         ncb, block_size, k, _ptr(idx), _ptr(workspace), wsb, Q, _stream(stream)))
+                         ncb, block_size, k, _ptr(idx), _ptr(workspace), wsb, Q, _byref(pages),
+                         _stream(stream)))
 
 
 def csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size, n_blocks):
@@ -187,14 +215,15 @@ def csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size, n_bl
 
 
 def csa2_topk_and_block_candidates(scores, n_cols, q_pos, ratio, k, idx, block_size, n_blocks,
-                                   cand, workspace, Q, block_max=None, stream=None):
+                                   cand, workspace, Q, block_max=None, stream=None, pages=None):
     lib = load()
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     bms = 0 if block_max is None else block_max.stride(0)
     _check(lib.csa2_topk_and_block_candidates(_ptr(scores), scores.stride(0), n_cols,
                                               _ptr(block_max), bms, _ptr(q_pos), ratio, k,
                                               _ptr(idx), block_size, n_blocks, _ptr(cand),
-                                              _ptr(workspace), wsb, Q, _stream(stream)))
+                                              _ptr(workspace), wsb, Q, _byref(pages),
+                                              _stream(stream)))
 
 
 def csa2_sparse_attn_workspace_size(Q, H, k, window):
@@ -203,15 +232,23 @@ def csa2_sparse_attn_workspace_size(Q, H, k, window):
 
 def csa2_sparse_attn(q, q_dtype, main_rows, main_base, idx, k, swa_rows, swa_base, swa_pos0,
                      swa_lo, window, q_seq, q_pos, ratio, attn_sink, softmax_scale, out,
-                     out_dtype, lse, Q, H=64, D=512, stream=None, workspace=None):
+                     out_dtype, lse, Q, H=64, D=512, stream=None, workspace=None, rope_cs=None,
+                     idx_slots=False, n_main_rows=0):
+    """rope_cs: optional [n, 64] fp32 table (the output is turned back by
+    each query's position); idx_slots: idx holds physical main rows."""
     lib = load()
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    io = None
+    if rope_cs is not None or idx_slots:
+        io = csa2_attn_io(None if rope_cs is None else rope_cs.data_ptr(),
+                          0 if rope_cs is None else rope_cs.shape[0], int(bool(idx_slots)),
+                          n_main_rows)
     _check(lib.csa2_sparse_attn(_ptr(q), q_dtype, ctypes.byref(main_rows), _ptr(main_base),
                                 _ptr(idx), k, ctypes.byref(swa_rows), _ptr(swa_base),
                                 _ptr(swa_pos0), _ptr(swa_lo), window, _ptr(q_seq), _ptr(q_pos),
                                 ratio, _ptr(attn_sink), ctypes.c_float(softmax_scale), _ptr(out),
                                 out_dtype, _ptr(lse), _ptr(workspace), wsb, Q, H, D,
-                                _stream(stream)))
+                                None if io is None else ctypes.byref(io), _stream(stream)))
 
 
 def csa2_cache_write(c, z, tok_seq, tok_pos, ratio, pend, n_seq, kv_norm_w, w_ik, k_norm_w,

@@ -68,10 +68,16 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
                       int32_t n_cand_blocks, int32_t block_size, float* scores,
                       int64_t score_stride, int32_t n_cols, float* block_max,
                       int64_t block_max_stride, int32_t Q, int32_t H_I, int32_t d_I,
-                      void* stream) {
+                      const csa2_pages* pages, void* stream) {
   g_err[0] = 0;
-  REQUIRE(q_idx && k_idx && w && seq_base && q_seq && q_pos && scores, CSA2_ERR_INVALID_ARG,
+  REQUIRE(q_idx && k_idx && w && (seq_base || pages) && q_seq && q_pos && scores, CSA2_ERR_INVALID_ARG,
           "csa2_index_scores: null pointer argument");
+  if (pages)
+    REQUIRE(pages->table && pages->table_stride >= 1 && pages->n_pages >= 1 && pages->page_stride >= 0 &&
+                pages->page_stride % 16 == 0,
+            CSA2_ERR_INVALID_ARG,
+            "csa2_index_scores: pages needs a table, table_stride >= 1, n_pages >= 1 and a page_stride "
+            ">= 0, multiple of 16");
   REQUIRE(q_idx->data && k_idx->data, CSA2_ERR_INVALID_ARG, "csa2_index_scores: null row data");
   REQUIRE(Q >= 0 && n_cols >= 0, CSA2_ERR_INVALID_ARG, "csa2_index_scores: negative size");
   REQUIRE(ratio == 1 || ratio == 2, CSA2_ERR_UNSUPPORTED, "csa2_index_scores: ratio must be 1 or 2");
@@ -116,7 +122,15 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
   a.k_scale = k_idx->scale;
   a.k_row_stride = k_idx->row_stride;
   a.k_scale_stride = k_idx->scale_stride;
+  a.k_scale_bytes = k_fp4 ? k_idx->scale_stride : k_idx->scale_stride * (int64_t)sizeof(float);
   a.k_fp4 = k_fp4 ? 1 : 0;
+  if (pages) {
+    a.page_table = pages->table;
+    a.pt_stride = pages->table_stride;
+    a.n_pages = pages->n_pages;
+    a.k_page_bytes = pages->page_stride ? pages->page_stride : csa2::PAGE_SLOTS * k_idx->row_stride;
+    a.s_page_bytes = pages->page_stride ? pages->page_stride : csa2::PAGE_SLOTS * a.k_scale_bytes;
+  }
   a.seq_base = seq_base;
   a.q_seq = q_seq;
   a.q_pos = q_pos;
@@ -244,9 +258,13 @@ int csa2_block_candidates(const float* scores, int64_t score_stride, int32_t n_c
 static int prep_topk(const float* scores, int64_t score_stride, int32_t n_cols,
                      const int32_t* q_pos, int32_t ratio, const int32_t* cand,
                      int32_t n_cand_blocks, int32_t block_size, int32_t k, int32_t* idx,
-                     void* workspace, size_t workspace_bytes, int32_t Q, csa2::SelectArgs* out) {
+                     void* workspace, size_t workspace_bytes, int32_t Q, const csa2_pages* pages,
+                     csa2::SelectArgs* out) {
   int st = check_select_common("csa2_topk", scores, score_stride, n_cols, k, idx, Q);
   if (st) return st;
+  if (pages)
+    REQUIRE(pages->table && pages->q_seq && pages->table_stride >= 1, CSA2_ERR_INVALID_ARG,
+            "csa2_topk: pages needs a table, q_seq and table_stride >= 1");
   REQUIRE(k <= 2048, CSA2_ERR_UNSUPPORTED, "csa2_topk: k above 2048");
   if (q_pos) REQUIRE(ratio == 1 || ratio == 2, CSA2_ERR_UNSUPPORTED, "csa2_topk: ratio must be 1 or 2");
   int bshift = 0;
@@ -274,6 +292,11 @@ static int prep_topk(const float* scores, int64_t score_stride, int32_t n_cols,
   a.out_idx = idx;
   a.workspace = workspace;
   a.Q = Q;
+  if (pages) {
+    a.page_table = pages->table;
+    a.pt_stride = pages->table_stride;
+    a.pt_seq = pages->q_seq;
+  }
   *out = a;
   return CSA2_OK;
 }
@@ -281,11 +304,11 @@ static int prep_topk(const float* scores, int64_t score_stride, int32_t n_cols,
 int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols, const int32_t* q_pos,
               int32_t ratio, const int32_t* cand, int32_t n_cand_blocks, int32_t block_size,
               int32_t k, int32_t* idx, void* workspace, size_t workspace_bytes, int32_t Q,
-              void* stream) {
+              const csa2_pages* pages, void* stream) {
   g_err[0] = 0;
   csa2::SelectArgs a;
   const int st = prep_topk(scores, score_stride, n_cols, q_pos, ratio, cand, n_cand_blocks,
-                           block_size, k, idx, workspace, workspace_bytes, Q, &a);
+                           block_size, k, idx, workspace, workspace_bytes, Q, pages, &a);
   if (st != CSA2_OK || Q == 0) return st;
   return hip_status(csa2::launch_select(cand ? csa2::SEL_POOL : csa2::SEL_DENSE, a, n_cols,
                                         (hipStream_t)stream),
@@ -305,7 +328,7 @@ int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, in
                                    const int32_t* q_pos, int32_t ratio, int32_t k, int32_t* idx,
                                    int32_t block_size, int32_t n_blocks, int32_t* cand,
                                    void* workspace, size_t workspace_bytes, int32_t Q,
-                                   void* stream) {
+                                   const csa2_pages* pages, void* stream) {
   g_err[0] = 0;
   REQUIRE(q_pos, CSA2_ERR_INVALID_ARG, "csa2_topk_and_block_candidates: q_pos is required");
   // the top-k's workspace comes first, the pool's follows at a 16-byte boundary
@@ -315,7 +338,7 @@ int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, in
   csa2::SelectArgs at, ab;
   int64_t nb = 0;
   int st = prep_topk(scores, score_stride, n_cols, q_pos, ratio, nullptr, 0, block_size, k, idx,
-                     workspace, workspace_bytes < ws_t ? workspace_bytes : ws_t, Q, &at);
+                     workspace, workspace_bytes < ws_t ? workspace_bytes : ws_t, Q, pages, &at);
   if (st != CSA2_OK) return st;
   st = prep_block_candidates(scores, score_stride, n_cols, block_max, block_max_stride, q_pos,
                              ratio, block_size, n_blocks, cand, ws_b ? ws + ws_t : nullptr, ws_b,
@@ -332,11 +355,18 @@ int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv
                      const int32_t* q_pos, int32_t ratio, const float* attn_sink,
                      float softmax_scale, void* out, csa2_dtype out_dtype, float* lse,
                      void* workspace, size_t workspace_bytes, int32_t Q, int32_t H, int32_t D,
-                     void* stream) {
+                     const csa2_attn_io* io, void* stream) {
   g_err[0] = 0;
-  REQUIRE(q && main_kv && main_base && idx && swa_kv && swa_base && swa_pos0 && q_seq && q_pos &&
-              attn_sink && out,
+  const bool slots = io && io->idx_slots;
+  REQUIRE(q && main_kv && (main_base || slots) && idx && swa_kv && swa_base && swa_pos0 && q_seq &&
+              q_pos && attn_sink && out,
           CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: null pointer argument");
+  if (io) {
+    REQUIRE(io->n_rope >= 0 && (!slots || io->n_main_rows >= 0), CSA2_ERR_INVALID_ARG,
+            "csa2_sparse_attn: negative size in io");
+    REQUIRE(!io->rope_cs || aligned(io->rope_cs, 16), CSA2_ERR_INVALID_ARG,
+            "csa2_sparse_attn: io->rope_cs must be 16-byte aligned");
+  }
   REQUIRE(main_kv->data && swa_kv->data, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: null row data");
   REQUIRE(Q >= 0 && k >= 0 && window >= 0, CSA2_ERR_INVALID_ARG, "csa2_sparse_attn: negative size");
   REQUIRE(D == 512, CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn: D must be 512 (got %d)", D);
@@ -377,6 +407,10 @@ int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv
   a.lse = lse;
   a.Q = Q;
   a.H = H;
+  a.idx_slots = slots ? 1 : 0;
+  a.n_main_rows = slots ? io->n_main_rows : 0;
+  a.rope = io ? io->rope_cs : nullptr;
+  a.n_rope = io ? io->n_rope : 0;
   const bool s16 = main_kv->dtype == CSA2_FP4_E2M1_E4M3S16;
   const bool quant = q_dtype == CSA2_BF16 && (main_kv->dtype == CSA2_FP4_E2M1 || s16) &&
                      swa_kv->dtype == CSA2_FP8_E4M3 &&

@@ -158,7 +158,8 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
   const int r = lane & 31;
 
   const int nvis = visible_count(a.q_pos[t], a.ratio);
-  const int64_t base = a.seq_base[a.q_seq[t]];
+  const int bseq = a.q_seq[t];
+  const int64_t base = a.page_table ? 0 : a.seq_base[bseq];
   const int col_begin = blockIdx.x * a.sub_per_wg * IS_SUB;
   const int col_end = min(a.n_cols, col_begin + a.sub_per_wg * IS_SUB);
   float* out = a.scores + (int64_t)t * a.score_stride;
@@ -205,19 +206,19 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
     for (int i = 0; i < IS_TILES; ++i) {
       const int tcol = sc0 + (i * IS_WAVES + wave) * 32;
       S.pos[i] = (tcol < limit) ? column_position<POOL>(a, t, tcol + r, nvis) : -1;
-      const int64_t row = base + max(S.pos[i], 0);
+      int64_t ko, so;
+      if (!key_offsets(a, bseq, base, max(S.pos[i], 0), ko, so)) S.pos[i] = -1;
       if (K4) {
         // 32 code bytes and the dword of the four E4M3 scales of this half
-        const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 32 * half);
+        const v4u* src = (const v4u*)(a.k + ko + 32 * half);
         S.raw[i][0] = src[0];
         S.raw[i][1] = src[1];
-        S.ks[i] = __uint_as_float(
-            *(const uint32_t*)((const uint8_t*)a.k_scale + row * a.k_scale_stride + 4 * half));
+        S.ks[i] = __uint_as_float(*(const uint32_t*)((const uint8_t*)a.k_scale + so + 4 * half));
       } else {
-        const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 64 * half);
+        const v4u* src = (const v4u*)(a.k + ko + 64 * half);
 #pragma unroll
         for (int j = 0; j < 4; ++j) S.raw[i][j] = src[j];
-        S.ks[i] = a.k_scale[row * a.k_scale_stride];
+        S.ks[i] = *(const float*)((const uint8_t*)a.k_scale + so);
       }
     }
   };
@@ -366,27 +367,28 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
     int maxvis = 0;
     for (int j = 0; j < nq; ++j)
       if (a.q_seq[t0 + j] == b) maxvis = max(maxvis, visible_count(a.q_pos[t0 + j], a.ratio));
-    const int64_t base = a.seq_base[b];
+    const int64_t base = a.page_table ? 0 : a.seq_base[b];
     const bool act[2] = {sq[0] == b, sq[1] == b};
 
     // raw bytes of one block: key kk, bytes [64 hh, +64), and its scale
     v4u kraw[4];
     float kscale = 0.f;
+    bool kok = true;   // false: the key's page is missing (its scale is staged as NaN)
     auto load_block = [&](int blk) {
       // rows past the last visible entry repeat it (masked later)
       const int col = min(blk * PF_KB + kk, max(maxvis - 1, 0));
-      const int64_t row = base + col;
+      int64_t ko, so;
+      kok = key_offsets(a, b, base, col, ko, so);
       if (K4) {
-        const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 32 * hh);
+        const v4u* src = (const v4u*)(a.k + ko + 32 * hh);
         kraw[0] = src[0];
         kraw[1] = src[1];
-        kscale = __uint_as_float(
-            *(const uint32_t*)((const uint8_t*)a.k_scale + row * a.k_scale_stride + 4 * hh));
+        kscale = __uint_as_float(*(const uint32_t*)((const uint8_t*)a.k_scale + so + 4 * hh));
       } else {
-        const v4u* src = (const v4u*)(a.k + row * a.k_row_stride + 64 * hh);
+        const v4u* src = (const v4u*)(a.k + ko + 64 * hh);
 #pragma unroll
         for (int j = 0; j < 4; ++j) kraw[j] = src[j];
-        kscale = a.k_scale[row * a.k_scale_stride];
+        kscale = *(const float*)((const uint8_t*)a.k_scale + so);
       }
     };
     auto store_block = [&](int buf) {
@@ -398,7 +400,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
         *(v8h*)(dst + 32 * j) = b0;
         *(v8h*)(dst + 32 * j + 16) = b1;
       }
-      if (hh == 0) s_ks[buf][kk] = K4 ? 1.0f : kscale;
+      if (hh == 0) s_ks[buf][kk] = kok ? (K4 ? 1.0f : kscale) : __uint_as_float(0x7FC00000u);
     };
 
     if (maxvis > 0) {
@@ -444,7 +446,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
 #pragma unroll
           for (int jj = 0; jj < 16; ++jj) v = fmaf(gate[i][jj], relu(acc[i][jj]), v);
           v = add_half_swap(v);
-          sc[i] = (act[i] && col < nv[i]) ? v * ks : -INFINITY;
+          sc[i] = (act[i] && col < nv[i] && ks == ks) ? v * ks : -INFINITY;
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -478,13 +480,16 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(IndexScoreArgs a)
   for (int h = threadIdx.x; h < H; h += 256) sw[h] = load_gate(a, t, h);
   __syncthreads();
   const int nvis = visible_count(a.q_pos[t], a.ratio);
-  const int64_t base = a.seq_base[a.q_seq[t]];
+  const int bseq = a.q_seq[t];
+  const int64_t base = a.page_table ? 0 : a.seq_base[bseq];
   const int col = blockIdx.x * 256 + threadIdx.x;
   float* out = a.scores + (int64_t)t * a.score_stride;
-  const int p = column_position<POOL>(a, t, col, nvis);
+  int p = column_position<POOL>(a, t, col, nvis);
   float tot = -INFINITY;
+  int64_t ko = 0, so = 0;
+  if (p >= 0 && !key_offsets(a, bseq, base, p, ko, so)) p = -1;
   if (p >= 0) {
-    const float* krow = (const float*)(a.k + (base + p) * a.k_row_stride);
+    const float* krow = (const float*)(a.k + ko);
     float kv[128];
 #pragma unroll
     for (int d = 0; d < 128; d += 4) {

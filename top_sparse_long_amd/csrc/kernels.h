@@ -35,7 +35,38 @@ struct IndexScoreArgs {
   int sub_per_wg;            // 256-column sub-chunks streamed by one workgroup (set at launch)
   int Q;
   int H;
+  int64_t k_scale_bytes;     // scale stride of a key row in bytes
+  // paged keys: position p of sequence b is slot (page_table[b][p / 64], p % 64);
+  // a slot's key and scale sit page * page_bytes + (p % 64) * stride into k and k_scale
+  const int32_t* page_table; // null: flat rows from seq_base
+  int64_t pt_stride;
+  int n_pages;
+  int64_t k_page_bytes;
+  int64_t s_page_bytes;
 };
+
+constexpr int PAGE_SLOTS = 64;
+
+// Byte offsets of the key row and of its scale(s) for position pos (>= 0)
+// of sequence b (rows from base when not paged).  A missing page (negative,
+// past the table row or past the pool) reads slot 0 and reports false.
+__device__ __forceinline__ bool key_offsets(const IndexScoreArgs& a, int b, int64_t base, int pos,
+                                            int64_t& ko, int64_t& so) {
+  if (!a.page_table) {
+    const int64_t row = base + pos;
+    ko = row * a.k_row_stride;
+    so = row * a.k_scale_bytes;
+    return true;
+  }
+  const int pi = pos >> 6;
+  int pg = pi < a.pt_stride ? a.page_table[(int64_t)b * a.pt_stride + pi] : -1;
+  const bool ok = pg >= 0 && pg < a.n_pages;
+  if (!ok) pg = 0;
+  const int o = pos & (PAGE_SLOTS - 1);
+  ko = (int64_t)pg * a.k_page_bytes + (int64_t)o * a.k_row_stride;
+  so = (int64_t)pg * a.s_page_bytes + (int64_t)o * a.k_scale_bytes;
+  return ok;
+}
 
 // Dense FP8 calls with at least this many queries use the query-tiled
 // (prefill) kernel; smaller batches score each query on its own.
@@ -77,6 +108,11 @@ struct SelectArgs {
   int32_t* out_idx;          // [Q, k]
   void* workspace;
   int Q;
+  // top-k output through a page table: position p of row t is written as
+  // slot page_table[pt_seq[t]][p / 64] * 64 + p % 64 (-1 for a missing page)
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* pt_seq;
 };
 
 hipError_t launch_select(int mode, const SelectArgs& a, int64_t rows_len, hipStream_t s);
@@ -116,6 +152,10 @@ struct AttnArgs {
   int H;
   int n_split;               // key splits per (query, head group); 1 = no split
   float* part;               // [Q][H/16][n_split] partial records when n_split > 1
+  int idx_slots;             // 1: idx holds physical main rows, bounded by n_main_rows
+  int64_t n_main_rows;
+  const float* rope;         // null, or [n_rope][64] cos / sin: the output's dims 448..511
+  int n_rope;                //   are turned back by the query's position
 };
 
 // Partial record of one split: m[16] (log2 units), l[16], O[16][512], fp32.

@@ -50,6 +50,15 @@ struct StageArgs {
   int64_t out_stride;
 };
 
+// A selected position as written: itself, or its physical slot through the
+// page table (-1 when its page is missing).
+__device__ __forceinline__ int32_t out_slot(const SelectArgs& s, int t, int32_t pos) {
+  if (!s.page_table || pos < 0) return pos;
+  const int64_t pi = pos >> 6;
+  const int32_t pg = pi < s.pt_stride ? s.page_table[(int64_t)s.pt_seq[t] * s.pt_stride + pi] : -1;
+  return pg >= 0 ? pg * PAGE_SLOTS + (pos & (PAGE_SLOTS - 1)) : -1;
+}
+
 __device__ __forceinline__ int sel_visible(const SelectArgs& s, int t) {
   return (int)(((int64_t)s.q_pos[t] + 1) / s.ratio);
 }
@@ -348,7 +357,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
         a.out_key[off] = key[j];
         a.out_pos[off] = pos;
       } else {
-        s.out_idx[(int64_t)t * k + o] = pos;
+        s.out_idx[(int64_t)t * k + o] = out_slot(s, t, pos);
       }
     }
     rg += gt ? 1u : 0u;

@@ -86,6 +86,19 @@ __device__ __forceinline__ void dequant_fp8x4(uint32_t x, float s, v2h m2, uint3
   out[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, s, true) * m2);
 }
 
+// value of the neighbouring lane (lane ^ 1) through DPP
+__device__ __forceinline__ float lane_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+
+// Inverse RoPE of one output pair (x, y) = dims (2i, 2i+1) of the turned
+// range: x' = x cos + y sin, y' = y cos - x sin.
+__device__ __forceinline__ void unturn(float& x, float& y, float c, float s) {
+  const float x0 = x, y0 = y;
+  x = x0 * c + y0 * s;
+  y = y0 * c - x0 * s;
+}
+
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   uint32_t u = __float_as_uint(v);
   u += 0x7FFFu + ((u >> 16) & 1u);
@@ -134,8 +147,10 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
 
   const int b = a.q_seq[t];
   const int p = a.q_pos[t];
-  const int nvis = (int)(((int64_t)p + 1) / a.ratio);
-  const int64_t mbase = a.main_base[b];
+  // an idx entry names main row mbase + pos when 0 <= pos < lim: positions
+  // below the visible count of the sequence, or physical rows of the cache
+  const int64_t lim = a.idx_slots ? a.n_main_rows : ((int64_t)p + 1) / a.ratio;
+  const int64_t mbase = a.idx_slots ? 0 : a.main_base[b];
   const int lo = a.swa_lo ? a.swa_lo[b] : 0;
   const int sp0 = a.swa_pos0[b];
   const int first = max(max(lo, sp0), max(0, p - a.window + 1));
@@ -195,7 +210,7 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
     for (int kh = 0; kh < 2; ++kh) {
       const int slot = slot0 + kh * 16 + r;
       const int pos = slot < a.k ? s_idx[slot] : -1;
-      const bool v = pos >= 0 && pos < nvis;
+      const bool v = pos >= 0 && pos < lim;
       const uint8_t* src = v ? a.main + (mbase + pos) * a.main_stride : dummy;
 #pragma unroll
       for (int j = 0; j < 4; ++j) M.d[4 * kh + j] = *(const v4u*)(src + 64 * g + 16 * j);
@@ -478,6 +493,19 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
     if (a.lse && wave == 0 && r == 0) a.lse[(int64_t)t * a.H + h_glob0 + h] = (M + log2f(den)) * LN2;
   }
   const int64_t obase = ((int64_t)t * a.H + h_glob0 + 4 * g) * AT_D + r;
+  // inverse RoPE of dims 448..511 (column groups u = 28..31, the last
+  // wave's): the pair (2i, 2i+1) sits in lanes r, r ^ 1
+  constexpr int U_TURN = 28;
+  const bool turn = a.rope != nullptr && p >= 0 && p < a.n_rope && wave == AT_WAVES - 1;
+  float tc[4] = {1.f, 1.f, 1.f, 1.f}, ts[4] = {0.f, 0.f, 0.f, 0.f};
+  if (turn) {
+    const float* cs = a.rope + (int64_t)p * 64;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tc[q] = cs[8 * q + (r >> 1)];
+      ts[q] = cs[32 + 8 * q + (r >> 1)];
+    }
+  }
 #pragma unroll
   for (int uu = 0; uu < 32 / AT_WAVES; ++uu) {
     const int u = wave * (32 / AT_WAVES) + uu;
@@ -487,6 +515,15 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
       const v4f x = *(const v4f*)(s_tile + w * AT_TILE_BYTES + (u * 64 + lane) * 16);
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] += x[j] * fw[w][j];
+    }
+    if (turn && u >= U_TURN) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float o = lane_xor1(v[j]);
+        float x = (r & 1) ? o : v[j], y = (r & 1) ? v[j] : o;
+        unturn(x, y, tc[u - U_TURN], ts[u - U_TURN]);
+        v[j] = (r & 1) ? y : x;
+      }
     }
     // rows 4 g + j, column 16 u + r: 16 lanes write 16 consecutive columns
 #pragma unroll
@@ -512,8 +549,8 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs a) {
   for (int d = tid; d < AT_D; d += 256) sq[d] = qrow[d];
   const int b = a.q_seq[t];
   const int p = a.q_pos[t];
-  const int nvis = (int)(((int64_t)p + 1) / a.ratio);
-  const int64_t mbase = a.main_base[b];
+  const int64_t lim = a.idx_slots ? a.n_main_rows : ((int64_t)p + 1) / a.ratio;
+  const int64_t mbase = a.idx_slots ? 0 : a.main_base[b];
   const int lo = a.swa_lo ? a.swa_lo[b] : 0;
   const int sp0 = a.swa_pos0[b];
   const int first = max(max(lo, sp0), max(0, p - a.window + 1));
@@ -525,7 +562,7 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs a) {
   auto key_row = [&](int j) -> const float* {
     if (j < n_swa) return (const float*)(a.swa + (sbase + j) * a.swa_stride);
     const int pos = a.idx[(int64_t)t * a.k + (j - n_swa)];
-    if (pos < 0 || pos >= nvis) return nullptr;
+    if (pos < 0 || pos >= lim) return nullptr;
     return (const float*)(a.main + (mbase + pos) * a.main_stride);
   };
 
@@ -564,6 +601,7 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs a) {
   }
   const float den = red[0] + ((M == -INFINITY) ? 0.f : expf(sink - M));
   const float inv = den > 0.f ? 1.f / den : 0.f;
+  const bool turn = a.rope != nullptr && p >= 0 && p < a.n_rope;
   for (int d = tid; d < AT_D; d += 256) {
     float acc = 0.f;
     for (int j = 0; j < n_slots; ++j) {
@@ -571,7 +609,16 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs a) {
       if (e == 0.f) continue;
       acc = fmaf(e, key_row(j)[d], acc);
     }
-    ((float*)a.out)[((int64_t)t * a.H + h) * AT_D + d] = acc * inv;
+    float o = acc * inv;
+    if (turn && d >= 448) {   // whole waves: threads 192..255 in the second pass
+      const float other = __shfl_xor(o, 1);
+      const int i = (d - 448) >> 1;
+      const float c = a.rope[(int64_t)p * 64 + i], sn = a.rope[(int64_t)p * 64 + 32 + i];
+      float x = (d & 1) ? other : o, y = (d & 1) ? o : other;
+      unturn(x, y, c, sn);
+      o = (d & 1) ? y : x;
+    }
+    ((float*)a.out)[((int64_t)t * a.H + h) * AT_D + d] = o;
   }
   if (tid == 0 && a.lse) a.lse[(int64_t)t * a.H + h] = M + logf(den);
 }
@@ -610,6 +657,9 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs a) {
     }
   }
   const int64_t obase = ((int64_t)t * a.H + h0) * AT_D;
+  // inverse RoPE of dims 448..511: a thread's four columns are two pairs
+  const int p = a.rope ? a.q_pos[t] : 0;
+  const bool turn = a.rope != nullptr && p >= 0 && p < a.n_rope;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int e = e0 + threadIdx.x * 4 + i * 1024;
@@ -637,6 +687,12 @@ __global__ __launch_bounds__(256) void sparse_attn_combine_kernel(AttnArgs a) {
       v.w += x[i][sp].w * fs;
     }
     if (a.lse && (e % AT_D) == 0) a.lse[(int64_t)t * a.H + h0 + h] = (M + log2f(den)) * LN2;
+    const int col = e % AT_D;
+    if (turn && col >= 448) {
+      const float* cs = a.rope + (int64_t)p * 64 + ((col - 448) >> 1);
+      unturn(v.x, v.y, cs[0], cs[32]);
+      unturn(v.z, v.w, cs[1], cs[33]);
+    }
     if (a.out_bf16) {
       uint2 pk;
       pk.x = (uint32_t)f32_to_bf16_rne(v.x) | ((uint32_t)f32_to_bf16_rne(v.y) << 16);

@@ -23,10 +23,10 @@ import torch
 from . import (csa2_index_scores, csa2_block_candidates, csa2_topk, csa2_sparse_attn,
                csa2_topk_and_block_candidates, csa2_topk_and_block_candidates_workspace_size,
                csa2_block_candidates_workspace_size, csa2_topk_workspace_size,
-               csa2_sparse_attn_workspace_size,
+               csa2_sparse_attn_workspace_size, csa2_rows, csa2_pages,
                rows_f32, rows_fp8, rows_fp4s16, rows_fp4_records, rows_fp4s16_records,
                rows_swa_records,
-               CSA2_F32, CSA2_BF16)
+               CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1_E4M3S16)
 
 
 def _round_up(x, m):
@@ -45,9 +45,16 @@ class SlotSet:
 
 
 class LayerRunner:
-    def __init__(self, wl, device="cuda"):
+    """paged: an optional synth.PagedLayout — index keys are read through its
+    page table, the top-k writes physical slots and attention gathers by
+    slot; rope_cs: an optional [positions, 64] table — attention turns its
+    output back by each query's position (the layout's table when paged)."""
+
+    def __init__(self, wl, device="cuda", paged=None, rope_cs=None):
         self.wl = wl
         self.dev = device
+        self.paged = paged
+        self.rope_cs = paged.rope_cs if (paged is not None and rope_cs is None) else rope_cs
         Q = wl.Q
         self.Q = Q
         self.quant = wl.quantized
@@ -109,6 +116,22 @@ class LayerRunner:
         odt = torch.bfloat16 if self.quant else f32
         self.out = [torch.empty((Q, 64, 512), dtype=odt, device=device) for _ in wl.layers]
         self.lse = [torch.empty((Q, 64), dtype=f32, device=device) for _ in wl.layers]
+        self.pages_scores = self.pages_topk = None
+        self.n_main_rows = 0
+        if paged is not None:
+            pl = paged
+            base = pl.k_pool.data_ptr()
+            fp4 = getattr(wl, "k_fmt", "fp8") == "fp4s16"
+            self.k_rows = csa2_rows(base, base + pl.k_scale_offset, pl.k_row_bytes,
+                                    8 if fp4 else 1,
+                                    CSA2_FP4_E2M1_E4M3S16 if fp4 else CSA2_FP8_E4M3)
+            self.main_rows = (rows_fp4s16_records(pl.main_pool) if pl.main_pool.shape[1] == 288
+                              else rows_fp4_records(pl.main_pool))
+            self.n_main_rows = pl.main_pool.shape[0]
+            self.pages_scores = csa2_pages(pl.page_table.data_ptr(), pl.page_table.shape[1],
+                                           pl.n_pages, pl.k_page_bytes, None)
+            self.pages_topk = csa2_pages(pl.page_table.data_ptr(), pl.page_table.shape[1],
+                                         pl.n_pages, 0, wl.q_seq.data_ptr())
         self.slots = SlotSet(self.main_rows, self.k_rows)
 
     # -- steps -----------------------------------------------------------------
@@ -119,12 +142,13 @@ class LayerRunner:
             csa2_index_scores(self.layer_rows[li]["q_idx"], lay.w, wdt, self.slots.index_k,
                               wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio, self.pool_scores,
                               self.pool_cols, self.Q, cand=self.slots.candidates,
-                              block_size=wl.block_size)
+                              block_size=wl.block_size, pages=self.pages_scores)
         else:
             csa2_index_scores(self.layer_rows[li]["q_idx"], lay.w, wdt, self.slots.index_k,
                               wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio, self.scores,
                               self.n_cols, self.Q, block_size=wl.block_size,
-                              block_max=self.block_max if block_max else None)
+                              block_max=self.block_max if block_max else None,
+                              pages=self.pages_scores)
 
     def block_candidates(self, from_block_max=False):
         wl = self.wl
@@ -138,9 +162,11 @@ class LayerRunner:
         idx = self.idx[li]
         if pool:
             csa2_topk(self.pool_scores, self.pool_cols, None, wl.ratio, wl.topk, idx, self.ws,
-                      self.Q, cand=self.slots.candidates, block_size=wl.block_size)
+                      self.Q, cand=self.slots.candidates, block_size=wl.block_size,
+                      pages=self.pages_topk)
         else:
-            csa2_topk(self.scores, self.n_cols, wl.q_pos, wl.ratio, wl.topk, idx, self.ws, self.Q)
+            csa2_topk(self.scores, self.n_cols, wl.q_pos, wl.ratio, wl.topk, idx, self.ws, self.Q,
+                      pages=self.pages_topk)
         self.slots.topk_idxs = idx
 
     def topk_and_blocks(self, li, from_block_max=False):
@@ -149,7 +175,8 @@ class LayerRunner:
         idx = self.idx[li]
         csa2_topk_and_block_candidates(self.scores, self.n_cols, wl.q_pos, wl.ratio, wl.topk, idx,
                                        wl.block_size, wl.n_blocks, self.cand, self.ws, self.Q,
-                                       block_max=self.block_max if from_block_max else None)
+                                       block_max=self.block_max if from_block_max else None,
+                                       pages=self.pages_topk)
         self.slots.topk_idxs = idx
         self.slots.candidates = self.cand
 
@@ -160,7 +187,8 @@ class LayerRunner:
                          wl.topk, self.layer_rows[li]["swa"], wl.swa_base, wl.swa_pos0, None,
                          wl.window, wl.q_seq, wl.q_pos, wl.ratio, lay.sink, wl.softmax_scale,
                          self.out[li], qdt if self.quant else CSA2_F32, self.lse[li], self.Q,
-                         workspace=self.ws_attn)
+                         workspace=self.ws_attn, rope_cs=self.rope_cs,
+                         idx_slots=self.paged is not None, n_main_rows=self.n_main_rows)
 
     # -- a whole pass ----------------------------------------------------------
     def steps(self, concurrent=False, separate_select=False):

@@ -57,6 +57,8 @@ def _parse():
                     help="capture block-candidate selection on a second stream beside the Full "
                          "layer's top-k and attention (HIP graphs on this ROCm replay the "
                          "branches one after the other, so this measured no gain)")
+    ap.add_argument("--no-serving", action="store_true",
+                    help="skip the serving-shaped step (paged caches, slots, inverse RoPE)")
     ap.add_argument("--no-cache-write", action="store_true",
                     help="skip the Full-layer cache-write measurement")
     ap.add_argument("--stage-reps", type=int, default=10,
@@ -507,34 +509,39 @@ def main():
     # copies and repeated, captured in one graph and timed with HIP events on
     # the stream the kernels run on
     reps = max(2, args.stage_reps)
-    stages = {}
-    run0 = runs[0]
-    names = []
     sel = dict(separate_select=args.separate_select)
-    for name, _ in run0.steps(**sel):
-        if name != "reset" and name not in names:
-            names.append(name)
-    for name in names:
-        fns = []
-        for _ in range(reps):
-            for r in runs:
-                fns += [f for n, f in r.steps(**sel) if n == name]
-        g = capture(fns)
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        g.replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        avg_ms = e0.elapsed_time(e1) / len(fns)
-        per_step = sum(1 for n, _ in run0.steps(**sel) if n == name)
-        nbytes, units = _stage_work(run0, name)
-        stages[name] = {"avg_us": avg_ms * 1e3, "calls_per_step": per_step,
-                        "algorithmic_bytes": nbytes, "units": units,
-                        "hbm_frac": nbytes / (avg_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
-        del g
+
+    def stage_times(rs):
+        out = {}
+        names = []
+        for name, _ in rs[0].steps(**sel):
+            if name != "reset" and name not in names:
+                names.append(name)
+        for name in names:
+            fns = []
+            for _ in range(reps):
+                for r in rs:
+                    fns += [f for n, f in r.steps(**sel) if n == name]
+            g = capture(fns)
+            g.replay()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            avg_ms = e0.elapsed_time(e1) / len(fns)
+            per_step = sum(1 for n, _ in rs[0].steps(**sel) if n == name)
+            nbytes, units = _stage_work(rs[0], name)
+            out[name] = {"avg_us": avg_ms * 1e3, "calls_per_step": per_step,
+                         "algorithmic_bytes": nbytes, "units": units,
+                         "hbm_frac": nbytes / (avg_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
+            del g
+        return out
+
+    run0 = runs[0]
+    stages = stage_times(runs)
     dom = max(stages, key=lambda s: stages[s]["avg_us"] * stages[s]["calls_per_step"])
     d = stages[dom]
     achieved = d["algorithmic_bytes"] / (d["avg_us"] * 1e-6) / 1e9
@@ -552,6 +559,35 @@ def main():
             keys += wl.Q * run0.pool_cols
         n_attn += wl.Q
     value = keys / (ms_per_step * 1e-3)
+
+    # the same step with serving-shaped I/O: index keys and main-KV records in
+    # 64-slot pages of a random page order (index-key pages of 64 keys, then
+    # their 64 scales), the top-k writing physical slots, attention gathering
+    # by slot and turning its output back by RoPE
+    serving = None
+    if not args.no_serving and wl.quantized:
+        pruns = [LayerRunner(r.wl, paged=synth.paged_layout(r.wl, 900 + c))
+                 for c, r in enumerate(runs)]
+        pgraphs = [capture([f for _, f in r.steps(separate_select=args.separate_select)])
+                   for r in pruns]
+        for i in range(args.warmup):
+            pgraphs[i % len(pgraphs)].replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            pgraphs[i % len(pgraphs)].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / args.steps
+        del pgraphs
+        serving = {"io": "64-slot pages in random order; index-key pages of 64 keys then 64 "
+                         "scales; top-k written as slots; attention by slot with inverse RoPE",
+                   "gpu_ms_per_step": sms, "value": keys / (sms * 1e-3),
+                   "unit": "index keys scored/s",
+                   "stages_us": {k: v["avg_us"] for k, v in stage_times(pruns).items()}}
+        del pruns
 
     cache_write = None
     if not args.no_cache_write:
@@ -582,6 +618,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,
+        "serving_io": serving,
         "cache_write": cache_write,
         "source_sha1": _source_hash(),
     }

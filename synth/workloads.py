@@ -422,16 +422,15 @@ def paged_layout(wl, seed, spare_pages=3):
     rec = wl.main_kv.shape[1]
     main_pool = torch.zeros((n_pages * PAGE_SLOTS, rec), dtype=torch.uint8, device=dev)
     k_scale_bytes = wl.k_scale.contiguous().view(torch.uint8).reshape(wl.k_idx.shape[0], sb)
+    keys = k_pool[:, :PAGE_SLOTS * kb].view(n_pages, PAGE_SLOTS, kb)     # strided views
+    scales = k_pool[:, PAGE_SLOTS * kb:].view(n_pages, PAGE_SLOTS, sb)
     for b, n in enumerate(wl.n_entries):
         p = torch.arange(n, device=dev)
         page = table[b, p // PAGE_SLOTS].to(torch.int64)
         slot = p % PAGE_SLOTS
         rows = int(wl.seq_base[b].item()) + p
-        kflat = k_pool.view(-1)
-        kidx = (page * page_bytes + slot * kb)[:, None] + torch.arange(kb, device=dev)[None, :]
-        kflat[kidx.reshape(-1)] = wl.k_idx[rows].reshape(-1)
-        sidx = (page * page_bytes + PAGE_SLOTS * kb + slot * sb)[:, None] + torch.arange(sb, device=dev)[None, :]
-        kflat[sidx.reshape(-1)] = k_scale_bytes[rows].reshape(-1)
+        keys[page, slot] = wl.k_idx[rows]
+        scales[page, slot] = k_scale_bytes[rows]
         main_pool[page * PAGE_SLOTS + slot] = wl.main_kv[rows]
     rope = rope_table(int(wl.q_pos.max().item()) + 1, dev)
     return PagedLayout(page_table=table.contiguous(), n_pages=n_pages, k_pool=k_pool,

@@ -149,7 +149,7 @@ __device__ __forceinline__ float group_max(float m, int bs) {
   return m;
 }
 
-template <bool POOL, bool W_BF16, bool K4>
+template <bool POOL, bool W_BF16, bool K4, bool PAGED>
 __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexScoreArgs a) {
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
 
   const int nvis = visible_count(a.q_pos[t], a.ratio);
   const int bseq = a.q_seq[t];
-  const int64_t base = a.page_table ? 0 : a.seq_base[bseq];
+  const int64_t base = PAGED ? 0 : a.seq_base[bseq];
   const int col_begin = blockIdx.x * a.sub_per_wg * IS_SUB;
   const int col_end = min(a.n_cols, col_begin + a.sub_per_wg * IS_SUB);
   float* out = a.scores + (int64_t)t * a.score_stride;
@@ -206,8 +206,16 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
     for (int i = 0; i < IS_TILES; ++i) {
       const int tcol = sc0 + (i * IS_WAVES + wave) * 32;
       S.pos[i] = (tcol < limit) ? column_position<POOL>(a, t, tcol + r, nvis) : -1;
+      int pg = 0;
+      if (PAGED) {
+        // dense: a 32-column tile lies in one 64-slot page (one scalar
+        // lookup per tile); pool: each lane's position has its own page
+        pg = POOL ? key_page(a, bseq, max(S.pos[i], 0) >> 6)
+                  : key_page(a, bseq, __builtin_amdgcn_readfirstlane(tcol >> 6));
+        if (pg < 0) S.pos[i] = -1;
+      }
       int64_t ko, so;
-      if (!key_offsets(a, bseq, base, max(S.pos[i], 0), ko, so)) S.pos[i] = -1;
+      key_offsets<PAGED>(a, base, max(S.pos[i], 0), pg, ko, so);
       if (K4) {
         // 32 code bytes and the dword of the four E4M3 scales of this half
         const v4u* src = (const v4u*)(a.k + ko + 32 * half);
@@ -304,7 +312,7 @@ constexpr int PF_WAVES = 8;
 constexpr int PF_BLOCKS = 8;             // key blocks per workgroup
 constexpr int PF_RS = 272;               // LDS row stride of an f16 key row (bytes)
 
-template <bool W_BF16, bool K4>
+template <bool W_BF16, bool K4, bool PAGED>
 __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(IndexScoreArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][PF_KB * PF_RS];
   __shared__ float s_ks[2][PF_KB];
@@ -367,7 +375,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
     int maxvis = 0;
     for (int j = 0; j < nq; ++j)
       if (a.q_seq[t0 + j] == b) maxvis = max(maxvis, visible_count(a.q_pos[t0 + j], a.ratio));
-    const int64_t base = a.page_table ? 0 : a.seq_base[b];
+    const int64_t base = PAGED ? 0 : a.seq_base[b];
     const bool act[2] = {sq[0] == b, sq[1] == b};
 
     // raw bytes of one block: key kk, bytes [64 hh, +64), and its scale
@@ -377,8 +385,10 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
     auto load_block = [&](int blk) {
       // rows past the last visible entry repeat it (masked later)
       const int col = min(blk * PF_KB + kk, max(maxvis - 1, 0));
+      const int pg = PAGED ? key_page(a, b, col >> 6) : 0;
+      kok = pg >= 0;
       int64_t ko, so;
-      kok = key_offsets(a, b, base, col, ko, so);
+      key_offsets<PAGED>(a, base, col, pg, ko, so);
       if (K4) {
         const v4u* src = (const v4u*)(a.k + ko + 32 * hh);
         kraw[0] = src[0];
@@ -487,7 +497,15 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(IndexScoreArgs a)
   int p = column_position<POOL>(a, t, col, nvis);
   float tot = -INFINITY;
   int64_t ko = 0, so = 0;
-  if (p >= 0 && !key_offsets(a, bseq, base, p, ko, so)) p = -1;
+  if (p >= 0) {
+    if (a.page_table) {
+      const int pg = key_page(a, bseq, p >> 6);
+      if (pg < 0) p = -1;
+      else key_offsets<true>(a, base, p, pg, ko, so);
+    } else {
+      key_offsets<false>(a, base, p, 0, ko, so);
+    }
+  }
   if (p >= 0) {
     const float* krow = (const float*)(a.k + ko);
     float kv[128];
@@ -514,13 +532,13 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(IndexScoreArgs a)
   }
 }
 
-template <bool W_BF16, bool K4>
+template <bool W_BF16, bool K4, bool PAGED>
 static void launch_prefill(const IndexScoreArgs& a, hipStream_t s) {
   dim3 grid((a.n_cols + PF_KB * PF_BLOCKS - 1) / (PF_KB * PF_BLOCKS), (a.Q + PF_Q - 1) / PF_Q);
-  hipLaunchKernelGGL((index_scores_prefill_kernel<W_BF16, K4>), grid, dim3(64 * PF_WAVES), 0, s, a);
+  hipLaunchKernelGGL((index_scores_prefill_kernel<W_BF16, K4, PAGED>), grid, dim3(64 * PF_WAVES), 0, s, a);
 }
 
-template <bool POOL, bool W_BF16, bool K4>
+template <bool POOL, bool W_BF16, bool K4, bool PAGED>
 static void launch_decode(const IndexScoreArgs& a, hipStream_t s) {
   // sub-chunks per workgroup: enough workgroups for about one resident
   // round, each streaming over a contiguous column range of one query
@@ -528,27 +546,32 @@ static void launch_decode(const IndexScoreArgs& a, hipStream_t s) {
   const int64_t subs = (a.n_cols + IS_SUB - 1) / IS_SUB;
   b.sub_per_wg = (int)std::max<int64_t>(1, (subs * a.Q + IS_RESIDENT_WGS - 1) / IS_RESIDENT_WGS);
   dim3 grid((unsigned)((subs + b.sub_per_wg - 1) / b.sub_per_wg), a.Q);
-  hipLaunchKernelGGL((index_scores_fp8_kernel<POOL, W_BF16, K4>), grid, dim3(64 * IS_WAVES), 0, s, b);
+  hipLaunchKernelGGL((index_scores_fp8_kernel<POOL, W_BF16, K4, PAGED>), grid, dim3(64 * IS_WAVES), 0, s, b);
 }
 
-template <bool K4>
+template <bool K4, bool PAGED>
 static void launch_quant(const IndexScoreArgs& a, hipStream_t s) {
   if (!a.cand && a.Q >= PF_MIN_Q) {
     // many queries: the query-tiled kernel shares every staged key block
-    if (a.w_bf16) launch_prefill<true, K4>(a, s);
-    else launch_prefill<false, K4>(a, s);
+    if (a.w_bf16) launch_prefill<true, K4, PAGED>(a, s);
+    else launch_prefill<false, K4, PAGED>(a, s);
   } else if (a.cand) {
-    if (a.w_bf16) launch_decode<true, true, K4>(a, s);
-    else launch_decode<true, false, K4>(a, s);
+    if (a.w_bf16) launch_decode<true, true, K4, PAGED>(a, s);
+    else launch_decode<true, false, K4, PAGED>(a, s);
   } else {
-    if (a.w_bf16) launch_decode<false, true, K4>(a, s);
-    else launch_decode<false, false, K4>(a, s);
+    if (a.w_bf16) launch_decode<false, true, K4, PAGED>(a, s);
+    else launch_decode<false, false, K4, PAGED>(a, s);
   }
 }
 
 hipError_t launch_index_scores_fp8(const IndexScoreArgs& a, hipStream_t s) {
-  if (a.k_fp4) launch_quant<true>(a, s);
-  else launch_quant<false>(a, s);
+  if (a.page_table) {
+    if (a.k_fp4) launch_quant<true, true>(a, s);
+    else launch_quant<false, true>(a, s);
+  } else {
+    if (a.k_fp4) launch_quant<true, false>(a, s);
+    else launch_quant<false, false>(a, s);
+  }
   return hipGetLastError();
 }
 

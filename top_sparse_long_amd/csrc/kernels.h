@@ -47,25 +47,29 @@ struct IndexScoreArgs {
 
 constexpr int PAGE_SLOTS = 64;
 
+// Physical page of position-page pi of sequence b, or -1 when it is missing
+// (negative, past the table row or past the pool).
+__device__ __forceinline__ int key_page(const IndexScoreArgs& a, int b, int pi) {
+  const int pg = pi < a.pt_stride ? a.page_table[(int64_t)b * a.pt_stride + pi] : -1;
+  return (pg >= 0 && pg < a.n_pages) ? pg : -1;
+}
+
 // Byte offsets of the key row and of its scale(s) for position pos (>= 0)
-// of sequence b (rows from base when not paged).  A missing page (negative,
-// past the table row or past the pool) reads slot 0 and reports false.
-__device__ __forceinline__ bool key_offsets(const IndexScoreArgs& a, int b, int64_t base, int pos,
+// of sequence b: rows from base, or (PAGED) slot pos % 64 of page pg (slot 0
+// of page 0 when pg < 0).
+template <bool PAGED>
+__device__ __forceinline__ void key_offsets(const IndexScoreArgs& a, int64_t base, int pos, int pg,
                                             int64_t& ko, int64_t& so) {
-  if (!a.page_table) {
+  if (!PAGED) {
     const int64_t row = base + pos;
     ko = row * a.k_row_stride;
     so = row * a.k_scale_bytes;
-    return true;
+    return;
   }
-  const int pi = pos >> 6;
-  int pg = pi < a.pt_stride ? a.page_table[(int64_t)b * a.pt_stride + pi] : -1;
-  const bool ok = pg >= 0 && pg < a.n_pages;
-  if (!ok) pg = 0;
-  const int o = pos & (PAGE_SLOTS - 1);
-  ko = (int64_t)pg * a.k_page_bytes + (int64_t)o * a.k_row_stride;
-  so = (int64_t)pg * a.s_page_bytes + (int64_t)o * a.k_scale_bytes;
-  return ok;
+  const int o = pg < 0 ? 0 : (pos & (PAGE_SLOTS - 1));
+  const int64_t p = pg < 0 ? 0 : pg;
+  ko = p * a.k_page_bytes + (int64_t)o * a.k_row_stride;
+  so = p * a.s_page_bytes + (int64_t)o * a.k_scale_bytes;
 }
 
 // Dense FP8 calls with at least this many queries use the query-tiled

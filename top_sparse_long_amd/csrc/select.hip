@@ -319,6 +319,10 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
     }
   }
 
+  // a final top-k through a page table stages its positions in the (now
+  // free) transpose buffer and translates them in one pass at the end
+  const bool stage_out = !a.out_key && s.page_table != nullptr;
+
   // order-preserving compaction ----------------------------------------------
   // Thread tid holds positions [EMAX tid, +EMAX) in order.  One block scan of
   // the packed per-thread counts (keys > T low half, keys == T high half)
@@ -356,8 +360,10 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
         const int64_t off = (int64_t)t * a.out_stride + (int64_t)c * k + o;
         a.out_key[off] = key[j];
         a.out_pos[off] = pos;
+      } else if (stage_out) {
+        s_tr[o] = (uint32_t)pos;
       } else {
-        s.out_idx[(int64_t)t * k + o] = out_slot(s, t, pos);
+        s.out_idx[(int64_t)t * k + o] = pos;
       }
     }
     rg += gt ? 1u : 0u;
@@ -369,9 +375,18 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
       const int64_t off = (int64_t)t * a.out_stride + (int64_t)c * k + q;
       a.out_key[off] = KEY_PAD;
       a.out_pos[off] = -1;
+    } else if (stage_out) {
+      s_tr[q] = 0xFFFFFFFFu;
     } else {
       s.out_idx[(int64_t)t * k + q] = -1;
     }
+  }
+  if (stage_out) {
+    // positions through the page table: every row's page lookups are
+    // issued together, then the slots are written in order
+    __syncthreads();
+    for (int q = tid; q < k; q += SEL_THREADS)
+      s.out_idx[(int64_t)t * k + q] = out_slot(s, t, (int32_t)s_tr[q]);
   }
 }
 

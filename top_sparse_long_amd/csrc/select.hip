@@ -274,35 +274,56 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
   // pass also yields their number; a chunk with at most k of them takes all.
   uint32_t T = KEY_NEG_INF, keq = 0;
   {
+    // The histogram starts zeroed and wave 0, which reads a pass's counts,
+    // clears them for the next pass, so a pass costs two barriers: one
+    // after the counting atomics, one after wave 0 has found the threshold
+    // bucket.  Lane l of wave 0 owns buckets 255 - l - 64 q (q = 0..3):
+    // consecutive lanes read consecutive buckets, and bucket order (highest
+    // first) is q-major, so four wave scans give the suffix counts.
+    uint32_t& s_all = (&s_bucket)[3];
+    for (int i = tid; i < 256 * 16; i += SEL_THREADS) s_hist[i] = 0;
+    __syncthreads();
     uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      __syncthreads();   // previous readers of s_hist / s_wsum are done
-      for (int i = tid; i < 256 * 16; i += SEL_THREADS) s_hist[i] = 0;
-      __syncthreads();
+      // branch-free counting: every key adds 1 (selectable and inside the
+      // current prefix) or 0 to its own bucket
 #pragma unroll
-      for (int j = 0; j < EMAX; ++j)
-        if (key[j] > KEY_NEG_INF && (key[j] & mask) == prefix)
-          atomicAdd(&s_hist[((key[j] >> shift) & 255u) * 16u + copy], 1u);
+      for (int j = 0; j < EMAX; ++j) {
+        const uint32_t inc = (key[j] > KEY_NEG_INF && (key[j] & mask) == prefix) ? 1u : 0u;
+        __hip_atomic_fetch_add(&s_hist[((key[j] >> shift) & 255u) * 16u + copy], inc,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
       __syncthreads();
-      // suffix counts over buckets, highest bucket first
-      uint32_t cnt = 0;
-      if (tid < 256) {
-        const uint4* hb = (const uint4*)(s_hist + (255 - tid) * 16);
+      if (wave == 0) {
+        uint32_t cq[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint4 v = hb[q];
-          cnt += v.x + v.y + v.z + v.w;
+          uint4* hb = (uint4*)(s_hist + (255 - lane - 64 * q) * 16);
+          uint32_t c4 = 0;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 v = hb[i];
+            c4 += v.x + v.y + v.z + v.w;
+            hb[i] = make_uint4(0u, 0u, 0u, 0u);
+          }
+          cq[q] = c4;
         }
-      }
-      uint32_t all;
-      const uint32_t excl = block_excl_scan(cnt, lane, wave, s_wsum, &all);
-      if (shift == 24 && all <= (uint32_t)k) break;      // everything selectable is taken
-      if (tid < 256 && excl < krem && excl + cnt >= krem) {
-        s_bucket = 255u - (uint32_t)tid;
-        s_above = excl;
-        s_bcnt = cnt;
+        uint32_t base = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t incl = wave_incl_scan(cq[q], lane);
+          const uint32_t run = base + incl - cq[q];   // keys in higher buckets
+          if (run < krem && run + cq[q] >= krem) {
+            s_bucket = 255u - (uint32_t)(lane + 64 * q);
+            s_above = run;
+            s_bcnt = cq[q];
+          }
+          base += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+        }
+        if (lane == 0) s_all = base;
       }
       __syncthreads();
+      if (shift == 24 && s_all <= (uint32_t)k) break;   // everything selectable is taken
       krem -= s_above;
       prefix |= s_bucket << shift;
       mask |= 255u << shift;

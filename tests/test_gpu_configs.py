@@ -134,3 +134,31 @@ def test_config_parity(name):
                                                             oracle_io.index_k_rows(wl),
                                                             _np(wl.seq_base), q_seq, q_pos, 1,
                                                             run.n_cols))
+
+
+@pytest.mark.parametrize("name", [n for n in list(synth.CONFIG_NAMES) + list(synth.EXTRA_WORKLOADS)
+                                  if n != "tiny_full_fp32"])
+def test_config_serving_io_equals_flat(name):
+    """Full size, serving-shaped I/O (DSA page, top-k section): the caches in
+    64-slot pages of random order, the top-k writing slots, attention by slot
+    with the inverse RoPE.  Against the flat run with the same RoPE table:
+    every top-k table is the oracle's translation of the flat positions and
+    every layer's output and LSE are bit-identical."""
+    print(f"[case] serving I/O at full size: {name}", flush=True)
+    wl = synth.make_workload(name, device=DEV)
+    pl = synth.paged_layout(wl, 11)
+    flat = LayerRunner(wl, rope_cs=pl.rope_cs)
+    paged = LayerRunner(wl, paged=pl)
+    flat.run()
+    paged.run()
+    torch.cuda.synchronize()
+    table = _np(pl.page_table)
+    q_seq = _np(wl.q_seq)
+    for li in flat.idx:
+        fidx = _np(flat.idx[li])
+        want = oracle.slots_from_positions(fidx, q_seq, table)
+        assert (fidx >= 0).sum() > 0 and np.any(want != fidx), li   # real selections, translated
+        assert np.array_equal(_np(paged.idx[li]), want), li
+    for li in range(len(wl.layers)):
+        assert torch.equal(paged.out[li], flat.out[li]), li
+        assert torch.equal(paged.lse[li], flat.lse[li]), li

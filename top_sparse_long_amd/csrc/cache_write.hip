@@ -146,7 +146,7 @@ template <int R, bool PRE_W>
 __global__ __launch_bounds__(256, PRE_W ? 1 : 2) void cache_write_kernel(CacheWriteArgs a) {
   __shared__ CwSmem sm;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int TT = 32 * R;
+  constexpr int TT = CW_ENT * R;        // tokens of one workgroup
   const int t0 = blockIdx.x * TT;
 
   // this wave's W_IK fragments (output columns 32w..32w+31): loaded first
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(256) void cache_pend_kernel(CacheWriteArgs a) {
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s) {
   if (a.T == 0) return hipSuccess;
-  const int tt = 32 * a.ratio;
+  const int tt = CW_ENT * a.ratio;     // tokens of one workgroup (the kernel's TT)
   const unsigned grid = (unsigned)((a.T + tt - 1) / tt);
   // a single tile waits on every latency in turn: its W_IK fragments are
   // fetched before the token scan

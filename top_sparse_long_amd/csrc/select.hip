@@ -7,9 +7,9 @@
 // "where attention is computed" for the block pool with the latest block
 // forced).
 //
-// One workgroup of 512 threads selects within a chunk of up to 32768
+// One workgroup of 1024 threads selects within a chunk of up to 32768
 // entries, kept in registers as order-preserving 32-bit keys (entry
-// j * 512 + tid is thread tid's j-th key, so loads are coalesced):
+// j * 1024 + tid is thread tid's j-th key, so loads are coalesced):
 //   1. load the chunk (dense scores, pool scores, block maxima of 8-score
 //      blocks, or a (key, position) list from a previous stage);
 //   2. if more than k entries are selectable, radix-select the k-th largest
@@ -27,7 +27,7 @@
 
 namespace csa2 {
 
-constexpr int SEL_THREADS = 512;
+constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 constexpr int SEL_BATCH = 8;               // loads in flight per thread
 constexpr uint32_t KEY_NEG_INF = 0x007FFFFFu;  // key of -inf: selectable keys are larger
@@ -111,28 +111,30 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, int lane, int wa
   return before + incl - x;
 }
 
-// LDS bytes of one selection body of capacity CAP (carved in this order).
+// LDS bytes of one selection body of capacity CAP: the radix histogram
+// shares its bytes with the transpose buffer (the two are never live at the
+// same time), then the scan partials and the threshold words.
 template <int CAP>
 struct SelSmem {
-  static constexpr int HIST = 256 * 16 * 4;
+  static constexpr int HIST = (256 * 16 + 256) * 4;
   static constexpr int TR = (CAP + 4 * SEL_THREADS) * 4;
   static constexpr int WSUM = 16 * 4;
-  static constexpr int BYTES = HIST + TR + WSUM + 16;
+  static constexpr int BODY = HIST > TR ? HIST : TR;
+  static constexpr int BYTES = BODY + WSUM + 16;
 };
 
 template <int MODE, int CAP>
 __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, uint8_t* smem) {
   constexpr int EMAX = CAP / SEL_THREADS;   // entries per thread at most
-  // 16 interleaved copies of the 256-bin histogram (bin b, copy c at
-  // 16 b + c): lanes that hit the same bin land on 16 different banks, which
-  // keeps the first digit pass (where scores share few top bytes) from
-  // serialising on one address.
+  // first digit: 16 interleaved copies of the 256-bin histogram (bin b,
+  // copy c at 16 b + c), so lanes that hit the same bin land on 16 different
+  // banks (scores share few top bytes); later digits: one copy after them.
   uint32_t* s_hist = (uint32_t*)smem;
   // transpose buffer: entry p of the chunk at p + 4 (p / EMAX), so that each
   // thread's EMAX consecutive entries start on a different bank group
-  uint32_t* s_tr = (uint32_t*)(smem + SelSmem<CAP>::HIST);
-  uint32_t* s_wsum = (uint32_t*)(smem + SelSmem<CAP>::HIST + SelSmem<CAP>::TR);
-  uint32_t& s_bucket = *(uint32_t*)(smem + SelSmem<CAP>::HIST + SelSmem<CAP>::TR + SelSmem<CAP>::WSUM);
+  uint32_t* s_tr = (uint32_t*)smem;   // same bytes as s_hist
+  uint32_t* s_wsum = (uint32_t*)(smem + SelSmem<CAP>::BODY);
+  uint32_t& s_bucket = *(uint32_t*)(smem + SelSmem<CAP>::BODY + SelSmem<CAP>::WSUM);
   uint32_t& s_above = (&s_bucket)[1];
   uint32_t& s_bcnt = (&s_bucket)[2];
 
@@ -274,39 +276,59 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
   // pass also yields their number; a chunk with at most k of them takes all.
   uint32_t T = KEY_NEG_INF, keq = 0;
   {
-    // The histogram starts zeroed and wave 0, which reads a pass's counts,
-    // clears them for the next pass, so a pass costs two barriers: one
-    // after the counting atomics, one after wave 0 has found the threshold
-    // bucket.  Lane l of wave 0 owns buckets 255 - l - 64 q (q = 0..3):
-    // consecutive lanes read consecutive buckets, and bucket order (highest
-    // first) is q-major, so four wave scans give the suffix counts.
+    // The first digit counts every selectable key into 16 interleaved
+    // copies; later digits count only the keys inside the current prefix
+    // (few, so the atomics are predicated) into one plain 256-bin copy,
+    // which wave 0 reads and clears for the next pass.  A pass costs two
+    // barriers: one after the counting atomics, one after wave 0 has found
+    // the threshold bucket.  Lane l of wave 0 owns buckets 255 - l - 64 q
+    // (q = 0..3): consecutive lanes read consecutive buckets, and bucket
+    // order (highest first) is q-major, so four wave scans give the suffix
+    // counts.
     uint32_t& s_all = (&s_bucket)[3];
-    for (int i = tid; i < 256 * 16; i += SEL_THREADS) s_hist[i] = 0;
+    __syncthreads();   // the transposed entries have been read: s_tr becomes the histogram
+    uint32_t* s_hist1 = s_hist + 256 * 16;
+    for (int i = tid; i < 256 * 16 + 256; i += SEL_THREADS) s_hist[i] = 0;
     __syncthreads();
     uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      // branch-free counting: every key adds 1 (selectable and inside the
-      // current prefix) or 0 to its own bucket
+      if (shift == 24) {
 #pragma unroll
-      for (int j = 0; j < EMAX; ++j) {
-        const uint32_t inc = (key[j] > KEY_NEG_INF && (key[j] & mask) == prefix) ? 1u : 0u;
-        __hip_atomic_fetch_add(&s_hist[((key[j] >> shift) & 255u) * 16u + copy], inc,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        for (int j = 0; j < EMAX; ++j) {
+          const uint32_t inc = (key[j] > KEY_NEG_INF) ? 1u : 0u;
+          __hip_atomic_fetch_add(&s_hist[((key[j] >> 24) & 255u) * 16u + copy], inc,
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < EMAX; ++j) {
+          if (key[j] > KEY_NEG_INF && (key[j] & mask) == prefix)
+            __hip_atomic_fetch_add(&s_hist1[(key[j] >> shift) & 255u], 1u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
       }
       __syncthreads();
       if (wave == 0) {
         uint32_t cq[4];
+        if (shift == 24) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint4* hb = (uint4*)(s_hist + (255 - lane - 64 * q) * 16);
-          uint32_t c4 = 0;
+          for (int q = 0; q < 4; ++q) {
+            const uint4* hb = (const uint4*)(s_hist + (255 - lane - 64 * q) * 16);
+            uint32_t c4 = 0;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint4 v = hb[i];
-            c4 += v.x + v.y + v.z + v.w;
-            hb[i] = make_uint4(0u, 0u, 0u, 0u);
+            for (int i = 0; i < 4; ++i) {
+              const uint4 v = hb[i];
+              c4 += v.x + v.y + v.z + v.w;
+            }
+            cq[q] = c4;
           }
-          cq[q] = c4;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            uint32_t* hb = s_hist1 + 255 - lane - 64 * q;
+            cq[q] = *hb;
+            *hb = 0u;
+          }
         }
         uint32_t base = 0;
 #pragma unroll

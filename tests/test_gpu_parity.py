@@ -327,6 +327,40 @@ def test_sparse_attn_quant(ratio, split, main_fmt):
     assert np.abs(gl - rl).max() <= 1e-3
 
 
+def test_sparse_attn_split_workspace_reuse():
+    """One attention workspace across calls of different batch shapes: the
+    split records hold nothing that outlives a call, so a repeated call is
+    bit-identical and a smaller batch in between does not disturb it."""
+    _announce("sparse_attn split workspace reused across batch shapes")
+    big = synth.mini_workload(34, [3000, 2500, 2000, 1500, 1000, 900, 800, 700]).to(DEV)
+    small = synth.mini_workload(35, [4000, 600, 90], q_per_seq=1).to(DEV)
+    rb, rs = LayerRunner(big), LayerRunner(small)
+    assert rb.ws_attn is not None and rs.ws_attn is not None
+    rs.ws_attn = rb.ws_attn
+    rng = np.random.default_rng(36)
+    ib = _random_idx(rng, _np(big.n_vis()), 512, 0.9)
+    isml = _random_idx(rng, _np(small.n_vis()), 512, 0.7)
+    rb.slots.topk_idxs = torch.from_numpy(ib.astype(np.int32)).to(DEV)
+    rs.slots.topk_idxs = torch.from_numpy(isml.astype(np.int32)).to(DEV)
+    rb.attention(0)
+    torch.cuda.synchronize()
+    first, first_lse = rb.out[0].clone(), rb.lse[0].clone()
+    for _ in range(3):
+        rs.attention(0)
+        rb.attention(0)
+    torch.cuda.synchronize()
+    assert torch.equal(rb.out[0], first) and torch.equal(rb.lse[0], first_lse)
+    for wl, run, idx in ((big, rb, ib), (small, rs, isml)):
+        m = oracle_io.meta(wl)
+        lay = wl.layers[0]
+        ref, _ = oracle.sparse_attn(oracle_io.attn_q(lay, wl.quantized), oracle_io.main_rows(wl),
+                                    m["seq_base"], idx, oracle_io.swa_rows(lay, wl.quantized),
+                                    m["swa_base"], m["swa_pos0"], None, wl.window, m["q_seq"],
+                                    m["q_pos"], _np(lay.sink).astype(np.float64),
+                                    wl.softmax_scale, wl.ratio)
+        check_attention(_np(run.out[0].float()), ref)
+
+
 def test_sparse_attn_quant_duplicates_and_out_of_range():
     _announce("sparse_attn quantized duplicates / out-of-range indices")
     wl = synth.mini_workload(31, [1000], q_per_seq=2).to(DEV)

@@ -86,11 +86,6 @@ __device__ __forceinline__ void dequant_fp8x4(uint32_t x, float s, v2h m2, uint3
   out[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, s, true) * m2);
 }
 
-// value of the neighbouring lane (lane ^ 1) through DPP
-__device__ __forceinline__ float lane_xor1(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
-}
-
 // Inverse RoPE of one output pair (x, y) = dims (2i, 2i+1) of the turned
 // range: x' = x cos + y sin, y' = y cos - x sin.
 __device__ __forceinline__ void unturn(float& x, float& y, float c, float s) {
@@ -121,7 +116,9 @@ struct SwaTile {
   bool ok[2];
 };
 
-template <bool S16>
+// TURN: the output's inverse RoPE is applied here (unsplit calls with a
+// table); calls without one run the kernel without that epilogue code.
+template <bool S16, bool TURN>
 __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[AT_WAVES * AT_TILE_BYTES];
   __shared__ float s_m[AT_WAVES][AT_HEADS];
@@ -494,18 +491,12 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   }
   const int64_t obase = ((int64_t)t * a.H + h_glob0 + 4 * g) * AT_D + r;
   // inverse RoPE of dims 448..511 (column groups u = 28..31, the last
-  // wave's): the pair (2i, 2i+1) sits in lanes r, r ^ 1
+  // wave's): the pair (2i, 2i+1) sits in lanes r, r ^ 1, so a turning lane
+  // also merges its partner's column from LDS (a DPP exchange here instead
+  // made the compiler duplicate the key loop, a third slower)
   constexpr int U_TURN = 28;
-  const bool turn = a.rope != nullptr && p >= 0 && p < a.n_rope && wave == AT_WAVES - 1;
-  float tc[4] = {1.f, 1.f, 1.f, 1.f}, ts[4] = {0.f, 0.f, 0.f, 0.f};
-  if (turn) {
-    const float* cs = a.rope + (int64_t)p * 64;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      tc[q] = cs[8 * q + (r >> 1)];
-      ts[q] = cs[32 + 8 * q + (r >> 1)];
-    }
-  }
+  const bool turn = TURN && a.rope != nullptr && p >= 0 && p < a.n_rope && wave == AT_WAVES - 1;
+  const float* cs = a.rope + (int64_t)max(p, 0) * 64;   // read only when turning
 #pragma unroll
   for (int uu = 0; uu < 32 / AT_WAVES; ++uu) {
     const int u = wave * (32 / AT_WAVES) + uu;
@@ -517,11 +508,19 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
       for (int j = 0; j < 4; ++j) v[j] += x[j] * fw[w][j];
     }
     if (turn && u >= U_TURN) {
+      // the partner column (lane ^ 1, same rows) merged the same way
+      v4f vp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < AT_WAVES; ++w) {
+        const v4f x = *(const v4f*)(s_tile + w * AT_TILE_BYTES + (u * 64 + (lane ^ 1)) * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vp[j] += x[j] * fw[w][j];
+      }
+      const float c = cs[8 * (u - U_TURN) + (r >> 1)], sn = cs[32 + 8 * (u - U_TURN) + (r >> 1)];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float o = lane_xor1(v[j]);
-        float x = (r & 1) ? o : v[j], y = (r & 1) ? v[j] : o;
-        unturn(x, y, tc[u - U_TURN], ts[u - U_TURN]);
+        float x = (r & 1) ? vp[j] : v[j], y = (r & 1) ? v[j] : vp[j];
+        unturn(x, y, c, sn);
         v[j] = (r & 1) ? y : x;
       }
     }
@@ -717,10 +716,16 @@ int attn_splits(int Q, int H, int k, int window) {
 
 hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s) {
   const int groups = a.Q * (a.H / AT_HEADS);
-  if (a.main_s16)
-    hipLaunchKernelGGL(sparse_attn_quant_kernel<true>, dim3(groups * a.n_split), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(sparse_attn_quant_kernel<false>, dim3(groups * a.n_split), dim3(256), 0, s, a);
+  const dim3 grid(groups * a.n_split);
+  // split calls turn the output in the combine kernel
+  const bool turn = a.rope != nullptr && a.n_split == 1;
+  if (a.main_s16) {
+    if (turn) hipLaunchKernelGGL((sparse_attn_quant_kernel<true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((sparse_attn_quant_kernel<true, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (turn) hipLaunchKernelGGL((sparse_attn_quant_kernel<false, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((sparse_attn_quant_kernel<false, false>), grid, dim3(256), 0, s, a);
+  }
   if (a.n_split > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

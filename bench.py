@@ -75,6 +75,9 @@ def _parse():
     return ap.parse_args()
 
 
+STAGE_TIMED_REPLAYS = 5
+
+
 def _source_hash():
     h = hashlib.sha1()
     csrc = os.path.join(ROOT, "top_sparse_long_amd", "csrc")
@@ -384,13 +387,16 @@ def cache_write_stage(torch, synth, tsl, wl, reps, n_copies, workload):
                 f()
         g.replay()
         torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(torch.cuda.current_stream())
-        g.replay()
-        e1.record(torch.cuda.current_stream())
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / len(fns)
+        times = []
+        for _ in range(STAGE_TIMED_REPLAYS):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(torch.cuda.current_stream())
+            g.replay()
+            e1.record(torch.cuda.current_stream())
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return sorted(times)[len(times) // 2] * 1e3 / len(fns)
 
     def call(inp, bufs, base, n):
         _, mrows, krows = bufs
@@ -525,13 +531,18 @@ def main():
             g = capture(fns)
             g.replay()
             torch.cuda.synchronize()
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            avg_ms = e0.elapsed_time(e1) / len(fns)
+            # the median of several timed replays, so one slow replay (a
+            # clock ramp, say) does not become the stage's time
+            times = []
+            for _ in range(STAGE_TIMED_REPLAYS):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                g.replay()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times.append(e0.elapsed_time(e1))
+            avg_ms = sorted(times)[len(times) // 2] / len(fns)
             per_step = sum(1 for n, _ in rs[0].steps(**sel) if n == name)
             nbytes, units = _stage_work(rs[0], name)
             out[name] = {"avg_us": avg_ms * 1e3, "calls_per_step": per_step,

@@ -509,10 +509,10 @@ static hipError_t launch_stage(const StageArgs& a, int cap, int nchunks, int Q, 
   const dim3 grid(nchunks, Q), block(SEL_THREADS);
   if (cap <= 4096)
     hipLaunchKernelGGL((select_kernel<MODE, 4096>), grid, block, 0, s, a);
-  else if (cap <= 16384)
+  else if (MODE == SEL_LIST || cap <= 16384)   // list stages hold at most SEL_CAP_LIST
     hipLaunchKernelGGL((select_kernel<MODE, 16384>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((select_kernel<MODE, SEL_CAP>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((select_kernel<MODE, (MODE == SEL_LIST ? 16384 : SEL_CAP)>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 

@@ -454,8 +454,8 @@ def main():
         summarize_mfma(*args.summarize_mfma, args.workload, args.profile_command)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the multi-GPU "
-              "path is a design in DESIGN.md, not a measured configuration.", file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); sharding the path "
+              "over several GPUs is designed, not built or measured.", file=sys.stderr)
         sys.exit(2)
     import torch
     import synth

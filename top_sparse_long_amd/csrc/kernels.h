@@ -33,6 +33,7 @@ struct IndexScoreArgs {
   float* block_max;          // optional fused block maxima (dense mode)
   int64_t block_max_stride;
   int sub_per_wg;            // 256-column sub-chunks streamed by one workgroup (sizes the grid at launch)
+  int blocks_per_wg;         // query-tiled kernel: 256-key blocks streamed by one workgroup (set at launch)
   int Q;
   int H;
   int64_t k_scale_bytes;     // scale stride of a key row in bytes

@@ -67,14 +67,19 @@ def _prefill_positions(n_tok, n_q, seed):
 
 
 @pytest.mark.parametrize("k_fmt", ["fp8", "fp4s16"])
-@pytest.mark.parametrize("case", ["one_sequence", "mixed_tiles"])
+@pytest.mark.parametrize("case", ["one_sequence", "mixed_tiles", "long_runs"])
 def test_index_scores_prefill_fp8(case, k_fmt):
     """Many queries (at least the query-tiled kernel's threshold): a ragged
-    count, causal m = 2 rows of different lengths, and, in the mixed case,
-    16-query tiles that straddle sequences."""
+    count, causal m = 2 rows of different lengths, in the mixed case 16-query
+    tiles that straddle sequences, and with long_runs enough work that each
+    workgroup streams a run of more than the minimum eight key blocks (83
+    blocks in runs of 10, the last one short)."""
     if case == "one_sequence":
         n_entries = [5000]
         positions = [_prefill_positions(10000, 300, 1)]
+    elif case == "long_runs":
+        n_entries = [21200]
+        positions = [_prefill_positions(42400, 512, 9)]
     else:
         n_entries = [3000, 2100, 4100]
         positions = [_prefill_positions(2 * n, nq, 2 + i)

@@ -31,6 +31,7 @@ namespace csa2 {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 typedef short v4s_t __attribute__((ext_vector_type(4)));
@@ -534,6 +535,352 @@ __global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Unsplit calls (many queries): the same arithmetic at two waves per SIMD.
+// One workgroup = one query x 16 heads, eight waves over 16-key tiles (SWA
+// tiles first).  q is staged once in LDS as f16 and read per 8-dim chunk as
+// the B operand of S^T = K Q^T, so a wave holds only O (128 registers), one
+// tile's raw bytes and its working set, and two waves share each SIMD.  P V
+// runs on v_mfma_f32_16x16x16_f16, whose A operand is S^T's accumulator
+// layout for 16 keys (lane (r, g): head r, keys 4 g .. 4 g + 3) and whose B
+// operand is what ds_read_b64_tr_b16 returns from the tile.  The eight
+// waves' partial results are merged through LDS, one half of the 512 output
+// columns at a time.
+constexpr int AW_WAVES = 8;
+constexpr int AW_TILE_BYTES = 16 * AT_RS;     // one wave's 16-key tile
+static_assert(AW_WAVES * AW_TILE_BYTES >= AW_WAVES * 16 * 64 * 16, "half of every wave's O must fit the tiles");
+
+template <bool S16, bool TURN>
+__global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_wide_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_tile[AW_WAVES * AW_TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[AT_HEADS * AT_RS];
+  __shared__ float s_m[AW_WAVES][AT_HEADS];
+  __shared__ float s_l[AW_WAVES][AT_HEADS];
+  __shared__ int32_t s_idx[AT_MAX_K];
+
+  const int n_hg = a.H / AT_HEADS;
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  // the workgroups of a query on one XCD (handed out round-robin)
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int t = bid / n_hg;
+  const int hg = bid - t * n_hg;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15;
+  const int g = lane >> 4;
+
+  const int b = a.q_seq[t];
+  const int p = a.q_pos[t];
+  const int64_t lim = a.idx_slots ? a.n_main_rows : ((int64_t)p + 1) / a.ratio;
+  const int64_t mbase = a.idx_slots ? 0 : a.main_base[b];
+  const int lo = a.swa_lo ? a.swa_lo[b] : 0;
+  const int sp0 = a.swa_pos0[b];
+  const int first = max(max(lo, sp0), max(0, p - a.window + 1));
+  const int n_swa = max(0, p - first + 1);
+  const int64_t sbase = a.swa_base[b] + (first - sp0);
+  const int n_swa_tiles = (n_swa + 15) >> 4;
+  const int n_tiles = n_swa_tiles + ((a.k + 15) >> 4);
+  const int h_glob0 = hg * AT_HEADS;
+  // keys that do not exist are read from this query's own q row (always
+  // mapped, 64 KB) and given a zero scale, so every load is unconditional
+  const uint8_t* dummy = (const uint8_t*)a.q + (int64_t)t * a.H * AT_D * 2;
+
+  // One 16-key tile as a lane holds it while the previous tile is computed:
+  // key r of the tile, dims [128 g, +128).
+  struct WSwa {
+    v4u d[8];    // 128 E4M3 codes
+    float s;     // the row's scale of these dims
+    bool ok;
+  };
+  struct WMain {
+    v4u d[4];    // 128 E2M1 codes
+    float4 s;    // 4 fp32 scales, or 8 E4M3 scale bytes in the first two words
+    bool ok;
+  };
+  auto load_swa = [&](int ti, WSwa& S) {
+    const int slot = ti * 16 + r;
+    // past the window's end: the last row again, masked later
+    const int64_t row = sbase + min(slot, n_swa - 1);
+    const uint8_t* src = a.swa + row * a.swa_stride + 128 * g;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) S.d[j] = *(const v4u*)(src + 16 * j);
+    S.s = a.swa_scale[row * a.swa_scale_stride + g];
+    S.ok = slot < n_swa;
+  };
+  auto load_main = [&](int ti, WMain& M) {
+    const int slot = (ti - n_swa_tiles) * 16 + r;
+    const int pos = slot < a.k ? s_idx[slot] : -1;
+    const bool v = pos >= 0 && pos < lim;
+    const uint8_t* src = v ? a.main + (mbase + pos) * a.main_stride : dummy;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) M.d[j] = *(const v4u*)(src + 64 * g + 16 * j);
+    if (S16) {
+      const uint8_t* ssrc = v ? (const uint8_t*)a.main_scale + (mbase + pos) * a.main_scale_stride : dummy;
+      const uint2 sb = *(const uint2*)(ssrc + 8 * g);
+      M.s = make_float4(__uint_as_float(sb.x), __uint_as_float(sb.y), 0.f, 0.f);
+    } else {
+      const float* ssrc = v ? a.main_scale + (mbase + pos) * a.main_scale_stride : (const float*)dummy;
+      M.s = *(const float4*)(ssrc + 4 * g);
+    }
+    M.ok = v;
+  };
+
+  // ---- prologue: every independent load is issued before any is waited on
+  WSwa S;
+  WMain M;
+  const int ti0 = wave;
+  if (ti0 < n_swa_tiles) load_swa(ti0, S);   // needs no staged index
+  // q of the 16 heads: thread i converts dims [16 (i % 32), +16) of head i / 32
+  v4u qraw[2];
+  const int qh = threadIdx.x >> 5, qd = (threadIdx.x & 31) * 16;
+  {
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)t * a.H + h_glob0 + qh) * AT_D + qd;
+    qraw[0] = *(const v4u*)qrow;
+    qraw[1] = *(const v4u*)(qrow + 8);
+  }
+  int32_t iv[AT_MAX_K / (64 * AW_WAVES)];
+  if (a.k > 0) {
+    const int32_t* irow = a.idx + (int64_t)t * a.k;
+#pragma unroll
+    for (int j = 0; j < AT_MAX_K / (64 * AW_WAVES); ++j)
+      iv[j] = irow[min((int)threadIdx.x + 64 * AW_WAVES * j, a.k - 1)];
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    v8h h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[2 * e] = (_Float16)__uint_as_float(qraw[i][e] << 16);
+      h[2 * e + 1] = (_Float16)__uint_as_float(qraw[i][e] & 0xFFFF0000u);
+    }
+    *(v8h*)(s_q + qh * AT_RS + 2 * qd + 16 * i) = h;
+  }
+  if (a.k > 0) {
+#pragma unroll
+    for (int j = 0; j < AT_MAX_K / (64 * AW_WAVES); ++j)
+      if ((int)threadIdx.x + 64 * AW_WAVES * j < a.k) s_idx[threadIdx.x + 64 * AW_WAVES * j] = iv[j];
+  }
+  __syncthreads();   // s_q, s_idx
+  if (ti0 >= n_swa_tiles && ti0 < n_tiles) load_main(ti0, M);
+
+  // O[u]: output columns d = 16 u + r, rows = heads 4 g + j
+  v4f O[32];
+#pragma unroll
+  for (int u = 0; u < 32; ++u) O[u] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_s = -INFINITY;   // running maximum of head r (log2 units)
+  float l_part = 0.f;      // this lane's share of the denominator of head r
+  const float zscale = a.scale * LOG2E;
+  uint8_t* tile = s_tile + wave * AW_TILE_BYTES;
+  const uint8_t* qsrc = s_q + r * AT_RS + 256 * g;
+
+  // S^T for the tile from dequantized 8-dim chunks (each also written to the
+  // wave's LDS tile for P V) and q chunks read from LDS.
+  auto stage_swa = [&](const WSwa& T, v4f& acc, uint64_t& vmask) {
+    const _Float16 mh = scale_mantissa(T.s);
+    const v2h m2 = {mh, mh};
+    uint8_t* dst = tile + r * AT_RS + 256 * g;
+    v4f s2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      uint32_t kd[4];
+      dequant_fp8x4(T.d[c >> 1][(c & 1) * 2], T.s, m2, &kd[0]);
+      dequant_fp8x4(T.d[c >> 1][(c & 1) * 2 + 1], T.s, m2, &kd[2]);
+      const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
+      *(v4u*)(dst + 16 * c) = kv;
+      const v8h qc = *(const v8h*)(qsrc + 16 * c);
+      s2[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qc, s2[c & 1], 0, 0, 0);
+    }
+    acc = s2[0] + s2[1];
+    vmask = __ballot(T.ok);
+  };
+  auto stage_main = [&](const WMain& T, v4f& acc, uint64_t& vmask) {
+    const float4 sc = T.ok ? T.s : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float s4[4] = {sc.x, sc.y, sc.z, sc.w};
+    _Float16 s8[8];
+    if (S16) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const v2h lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__float_as_uint(s4[w]), 1.0f, false);
+        const v2h hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__float_as_uint(s4[w]), 1.0f, true);
+        s8[4 * w] = lo2[0];
+        s8[4 * w + 1] = lo2[1];
+        s8[4 * w + 2] = hi2[0];
+        s8[4 * w + 3] = hi2[1];
+      }
+    }
+    uint8_t* dst = tile + r * AT_RS + 256 * g;
+    v4f s2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      uint32_t kd[4];
+      if (S16) {
+        dequant_fp4x8_h(T.d[c >> 2][c & 3], s8[c >> 1], kd);
+      } else {
+        const _Float16 mh = scale_mantissa(s4[c >> 2]);
+        dequant_fp4x8(T.d[c >> 2][c & 3], s4[c >> 2], (v2h){mh, mh}, kd);
+      }
+      const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
+      *(v4u*)(dst + 16 * c) = kv;
+      const v8h qc = *(const v8h*)(qsrc + 16 * c);
+      s2[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qc, s2[c & 1], 0, 0, 0);
+    }
+    acc = s2[0] + s2[1];
+    vmask = __ballot(T.ok);
+  };
+
+  // Online softmax over the tile's 16 scores of each head and O += P V.
+  auto finish_tile = [&](const v4f acc, const uint64_t vmask) {
+    float z[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = ((vmask >> (4 * g + i)) & 1ull) ? acc[i] * zscale : -INFINITY;
+    float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    const bool raise = mt > m_s + RESCALE_SLACK || (m_s == -INFINITY && mt > -INFINITY);
+    if (__any(raise)) {
+      const float m_new = fmaxf(m_s, mt);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_s - m_new);
+      l_part *= alpha;
+      m_s = m_new;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float aj = __shfl(alpha, 4 * g + j);
+#pragma unroll
+        for (int u = 0; u < 32; ++u) O[u][j] *= aj;
+      }
+    }
+    v4h P;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pv = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - m_s);
+      l_part += pv;
+      P[i] = (_Float16)pv;
+    }
+
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // lane (r, g) receives V[4 g + j][16 u + r] (j = 0..3): its B operand
+    {
+      __attribute__((address_space(3))) uint8_t* tl =
+          (__attribute__((address_space(3))) uint8_t*)tile;
+      const int off = (4 * g + (r >> 2)) * AT_RS + 8 * (r & 3);
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const v4s_t vv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s_t*)(tl + off + 32 * u));
+        O[u] = __builtin_amdgcn_mfma_f32_16x16x16f16(P, __builtin_bit_cast(v4h, vv), O[u], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+
+  // This wave's tiles are wave, wave + 8, ... (SWA tiles first); the next
+  // tile's rows are requested once the current tile's bytes are staged.
+  int ti = ti0;
+  for (; ti < min(n_tiles, n_swa_tiles); ti += AW_WAVES) {
+    v4f acc;
+    uint64_t vmask;
+    stage_swa(S, acc, vmask);
+    const int nx = ti + AW_WAVES;
+    if (nx < n_swa_tiles) load_swa(nx, S);
+    else if (nx < n_tiles) load_main(nx, M);
+    finish_tile(acc, vmask);
+  }
+  for (; ti < n_tiles; ti += AW_WAVES) {
+    v4f acc;
+    uint64_t vmask;
+    stage_main(M, acc, vmask);
+    if (ti + AW_WAVES < n_tiles) load_main(ti + AW_WAVES, M);
+    finish_tile(acc, vmask);
+  }
+
+  // ---- merge the eight waves ----------------------------------------------
+  float l = l_part;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (g == 0) {
+    s_m[wave][r] = m_s;
+    s_l[wave][r] = l;
+  }
+  __syncthreads();   // every wave is done with its tile; s_m, s_l
+  float fw[AW_WAVES][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int h = 4 * g + j;
+    const float sink2 = a.sink[h_glob0 + h] * LOG2E;
+    float Mx = sink2;
+#pragma unroll
+    for (int w = 0; w < AW_WAVES; ++w) Mx = fmaxf(Mx, s_m[w][h]);
+    float den = (Mx == -INFINITY) ? 0.f : exp2f(sink2 - Mx);
+#pragma unroll
+    for (int w = 0; w < AW_WAVES; ++w) {
+      const float mw = s_m[w][h];
+      fw[w][j] = (mw == -INFINITY) ? 0.f : exp2f(mw - Mx);
+      den += s_l[w][h] * fw[w][j];
+    }
+    const float inv = (den > 0.f) ? 1.f / den : 0.f;
+#pragma unroll
+    for (int w = 0; w < AW_WAVES; ++w) fw[w][j] *= inv;
+    if (a.lse && wave == 0 && r == 0) a.lse[(int64_t)t * a.H + h_glob0 + h] = (Mx + log2f(den)) * LN2;
+  }
+  const int64_t obase = ((int64_t)t * a.H + h_glob0 + 4 * g) * AT_D + r;
+  // inverse RoPE of dims 448..511 (column blocks 28..31): the pair (2i, 2i+1)
+  // sits in lanes r, r ^ 1, so a turning lane also merges its partner's column
+  const bool turn = TURN && a.rope != nullptr && p >= 0 && p < a.n_rope;
+  const float* cs = a.rope + (int64_t)max(p, 0) * 64;   // read only when turning
+  constexpr int U_TURN = 28;
+  constexpr int HALF_BYTES = 16 * 64 * 16;               // 16 column blocks of one wave
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    uint8_t* part = s_tile + wave * HALF_BYTES;
+#pragma unroll
+    for (int uu = 0; uu < 16; ++uu) *(v4f*)(part + (uu * 64 + lane) * 16) = O[16 * half + uu];
+    __syncthreads();
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int uu = 2 * wave + k2;
+      const int u = 16 * half + uu;
+      v4f v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < AW_WAVES; ++w) {
+        const v4f x = *(const v4f*)(s_tile + w * HALF_BYTES + (uu * 64 + lane) * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] += x[j] * fw[w][j];
+      }
+      if (turn && u >= U_TURN) {
+        v4f vp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < AW_WAVES; ++w) {
+          const v4f x = *(const v4f*)(s_tile + w * HALF_BYTES + (uu * 64 + (lane ^ 1)) * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) vp[j] += x[j] * fw[w][j];
+        }
+        const float c = cs[8 * (u - U_TURN) + (r >> 1)], sn = cs[32 + 8 * (u - U_TURN) + (r >> 1)];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x = (r & 1) ? vp[j] : v[j], y = (r & 1) ? v[j] : vp[j];
+          unturn(x, y, c, sn);
+          v[j] = (r & 1) ? y : x;
+        }
+      }
+      // rows 4 g + j, column 16 u + r: 16 lanes write 16 consecutive columns
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t o = obase + (int64_t)j * AT_D + 16 * u;
+        if (a.out_bf16) ((uint16_t*)a.out)[o] = f32_to_bf16_rne(v[j]);
+        else ((float*)a.out)[o] = v[j];
+      }
+    }
+    __syncthreads();   // the next half reuses the tiles
+  }
+}
+
 // fp32 path: one workgroup per (query, head); plain loops.
 constexpr int AF_MAX_SLOTS = 8192;
 
@@ -725,6 +1072,19 @@ int attn_splits(int Q, int H, int k, int window) {
 
 hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s) {
   const int groups = a.Q * (a.H / AT_HEADS);
+  if (a.n_split == 1) {
+    // unsplit (many queries): eight waves, two per SIMD
+    const bool turn = a.rope != nullptr;
+    const dim3 g1(groups), blk(64 * AW_WAVES);
+    if (a.main_s16) {
+      if (turn) hipLaunchKernelGGL((sparse_attn_quant_wide_kernel<true, true>), g1, blk, 0, s, a);
+      else hipLaunchKernelGGL((sparse_attn_quant_wide_kernel<true, false>), g1, blk, 0, s, a);
+    } else {
+      if (turn) hipLaunchKernelGGL((sparse_attn_quant_wide_kernel<false, true>), g1, blk, 0, s, a);
+      else hipLaunchKernelGGL((sparse_attn_quant_wide_kernel<false, false>), g1, blk, 0, s, a);
+    }
+    return hipGetLastError();
+  }
   const dim3 grid(groups * a.n_split);
   // split calls turn the output in the combine kernel
   const bool turn = a.rope != nullptr && a.n_split == 1;

@@ -9,19 +9,21 @@
 //
 // Quantized path (bf16 q, FP4 main KV with 16 fp32 scales per row, FP8 SWA
 // with 4 fp32 scales per row):
-//   * one workgroup = one query x 16 heads; 4 waves split the key tiles
-//     (32 keys each); the workgroups of a query sit on one XCD so its
-//     gathered rows are shared through that XCD's L2;
+//   * one workgroup = one query x 16 heads (x one key split at small
+//     batches); 8 waves, two per SIMD, split the key tiles (16 keys each);
+//     the workgroups of a query sit on one XCD so its gathered rows are
+//     shared through that XCD's L2;
 //   * rows are gathered straight from HBM into registers, dequantized to f16
 //     (exact E2M1/E4M3 codes times the scale, one f16 rounding), used at once
 //     as the K operand of S^T = K Q^T on v_mfma_f32_16x16x32_f16, and written
 //     to the wave's LDS tile for the P V product, which needs the same data
 //     with keys along the reduction axis;
-//   * S^T's accumulator layout puts 8 keys of one head in each lane, which is
-//     exactly P's operand layout for P V, so the probabilities never move;
+//   * S^T's accumulator layout puts 4 keys of one head in each lane, which is
+//     exactly P's operand layout for P V (v_mfma_f32_16x16x16_f16), so the
+//     probabilities never move;
 //   * online softmax in base 2 with lazy rescaling: the running maximum is
 //     only raised when a tile's maximum exceeds it by more than 8 (so
-//     probabilities stay below 2^8 in f16), and the four waves' partial
+//     probabilities stay below 2^8 in f16), and the eight waves' partial
 //     results are merged through LDS at the end.
 // q is converted from bf16 to f16 (exact for |q| in the f16 normal range),
 // so operands carry 11 significant bits; accumulation is fp32.
@@ -39,16 +41,13 @@ struct v8s_pair {
   v4s_t lo, hi;
 };
 
-constexpr int AT_WAVES = 4;
 constexpr int AT_HEADS = 16;
 constexpr int AT_D = 512;
 constexpr int AT_RS = AT_D * 2 + 16;          // LDS row stride (bytes) of an f16 key row
-constexpr int AT_TILE_BYTES = 32 * AT_RS;     // one wave's 32-key tile
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float RESCALE_SLACK = 8.0f;         // log2 units
 constexpr int AT_MAX_K = 2048;                // largest top-k the kernel stages
-static_assert(32 * 64 * 16 <= AT_TILE_BYTES, "a wave's partial O must fit its tile");
 
 __device__ __forceinline__ uint32_t as_u32(v2h h) { return __builtin_bit_cast(uint32_t, h); }
 __device__ __forceinline__ v2h as_v2h(uint32_t u) { return __builtin_bit_cast(v2h, u); }
@@ -101,457 +100,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   return (uint16_t)(u >> 16);
 }
 
-// Raw bytes of one tile as one lane holds them while the previous tile is
-// computed.  Main tile: 64 E2M1 bytes and the scales of the lane's key in
-// each 16-key half kh (d[4 kh + j], s[kh]: 4 fp32 scales, or 8 E4M3 scale
-// bytes in the first two words for the 288-byte record).  SWA tile: only the first half's 128
-// E4M3 codes and scale -- the second half is requested when the tile starts.
-struct MainTile {
-  v4u d[8];
-  float4 s[2];
-  bool ok[2];
-};
-struct SwaTile {
-  v4u d[8];
-  float s;
-  bool ok[2];
-};
-
-// TURN: the output's inverse RoPE is applied here (unsplit calls with a
-// table); calls without one run the kernel without that epilogue code.
-template <bool S16, bool TURN>
-__global__ __launch_bounds__(256) void sparse_attn_quant_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_tile[AT_WAVES * AT_TILE_BYTES];
-  __shared__ float s_m[AT_WAVES][AT_HEADS];
-  __shared__ float s_l[AT_WAVES][AT_HEADS];
-  __shared__ int32_t s_idx[AT_MAX_K];
-
-  const int n_hg = a.H / AT_HEADS;
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  // consecutive (query, head-group, split) triples on one XCD: workgroups
-  // are handed to the 8 XCDs round-robin
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int split = bid % a.n_split;
-  const int tg = bid / a.n_split;
-  const int t = tg / n_hg;
-  const int hg = tg - t * n_hg;
-
-  const int lane = threadIdx.x & 63;
-  // wave-uniform, so tile-type branches are scalar branches
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r = lane & 15;
-  const int g = lane >> 4;
-
-  const int b = a.q_seq[t];
-  const int p = a.q_pos[t];
-  // an idx entry names main row mbase + pos when 0 <= pos < lim: positions
-  // below the visible count of the sequence, or physical rows of the cache
-  const int64_t lim = a.idx_slots ? a.n_main_rows : ((int64_t)p + 1) / a.ratio;
-  const int64_t mbase = a.idx_slots ? 0 : a.main_base[b];
-  const int lo = a.swa_lo ? a.swa_lo[b] : 0;
-  const int sp0 = a.swa_pos0[b];
-  const int first = max(max(lo, sp0), max(0, p - a.window + 1));
-  const int n_swa = max(0, p - first + 1);
-  const int64_t sbase = a.swa_base[b] + (first - sp0);
-  const int n_swa_tiles = (n_swa + 31) >> 5;
-  const int n_tiles_all = n_swa_tiles + ((a.k + 31) >> 5);
-  // this workgroup's tiles: [tile_begin, n_tiles) of the query's tile list
-  // (SWA tiles first); the whole list when keys are not split
-  const int per_split = (n_tiles_all + a.n_split - 1) / a.n_split;
-  const int tile_begin = min(n_tiles_all, split * per_split);
-  const int n_tiles = min(n_tiles_all, tile_begin + per_split);
-  const int h_glob0 = hg * AT_HEADS;
-  // keys that do not exist are read from this query's own q row (always
-  // mapped, 64 KB) and given a zero scale, so every load is unconditional
-  const uint8_t* dummy = (const uint8_t*)a.q + (int64_t)t * a.H * AT_D * 2;
-
-  // ---- prologue: every independent load is issued before any is waited on
-  // q as the B operand of S^T = K Q^T: head (16 hg + r), dims [128 g, +128),
-  // chunk c holding dims 128 g + 8 c .. +8.
-  v4u qraw[16];
-  {
-    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)t * a.H + h_glob0 + r) * AT_D + 128 * g;
-#pragma unroll
-    for (int c = 0; c < 16; ++c) qraw[c] = *(const v4u*)(qrow + 8 * c);
-  }
-  // the query's selected positions (staged in LDS below)
-  int32_t iv[AT_MAX_K / 256];
-  if (a.k > 0) {
-    const int32_t* irow = a.idx + (int64_t)t * a.k;
-#pragma unroll
-    for (int j = 0; j < AT_MAX_K / 256; ++j) iv[j] = irow[min((int)threadIdx.x + 256 * j, a.k - 1)];
-  }
-  // sink logits of this lane's output rows (heads 4 g + j) and, for the
-  // first 16 threads, of head threadIdx.x
-  float sink_rows[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) sink_rows[j] = a.sink[h_glob0 + 4 * g + j];
-
-  // Loads of one tile; no branch depends on loaded data.
-  auto load_swa_half = [&](int slot, v4u* d, float& sc, bool& ok) {
-    // past the window's end: the last row again, masked later
-    const int64_t row = sbase + min(slot, n_swa - 1);
-    const uint8_t* src = a.swa + row * a.swa_stride + 128 * g;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) d[j] = *(const v4u*)(src + 16 * j);
-    sc = a.swa_scale[row * a.swa_scale_stride + g];
-    ok = slot < n_swa;
-  };
-  auto load_swa = [&](int ti, SwaTile& S) {
-    load_swa_half(ti * 32 + r, S.d, S.s, S.ok[0]);
-    S.ok[1] = ti * 32 + 16 + r < n_swa;
-  };
-  auto load_main = [&](int ti, MainTile& M) {
-    const int slot0 = (ti - n_swa_tiles) * 32;
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int slot = slot0 + kh * 16 + r;
-      const int pos = slot < a.k ? s_idx[slot] : -1;
-      const bool v = pos >= 0 && pos < lim;
-      const uint8_t* src = v ? a.main + (mbase + pos) * a.main_stride : dummy;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) M.d[4 * kh + j] = *(const v4u*)(src + 64 * g + 16 * j);
-      if (S16) {
-        // 8 E4M3 scales of dims [128 g, +128)
-        const uint8_t* ssrc = v ? (const uint8_t*)a.main_scale + (mbase + pos) * a.main_scale_stride : dummy;
-        const uint2 sb = *(const uint2*)(ssrc + 8 * g);
-        M.s[kh] = make_float4(__uint_as_float(sb.x), __uint_as_float(sb.y), 0.f, 0.f);
-      } else {
-        const float* ssrc = v ? a.main_scale + (mbase + pos) * a.main_scale_stride : (const float*)dummy;
-        M.s[kh] = *(const float4*)(ssrc + 4 * g);
-      }
-      M.ok[kh] = v;
-    }
-  };
-
-  SwaTile S;
-  MainTile M;
-  const int ti0 = tile_begin + wave;
-  if (ti0 < n_tiles && ti0 < n_swa_tiles) load_swa(ti0, S);   // needs no staged index
-
-  v8h qf[16];
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qf[c][2 * e] = (_Float16)__uint_as_float(qraw[c][e] << 16);
-      qf[c][2 * e + 1] = (_Float16)__uint_as_float(qraw[c][e] & 0xFFFF0000u);
-    }
-  }
-  if (a.k > 0) {
-#pragma unroll
-    for (int j = 0; j < AT_MAX_K / 256; ++j)
-      if ((int)threadIdx.x + 256 * j < a.k) s_idx[threadIdx.x + 256 * j] = iv[j];
-  }
-  __syncthreads();   // s_idx
-  if (ti0 >= n_swa_tiles && ti0 < n_tiles) load_main(ti0, M);
-
-  // O[T]: output columns d = 16 T + r, rows = heads 4 g + j
-  v4f O[32];
-#pragma unroll
-  for (int u = 0; u < 32; ++u) O[u] = (v4f){0.f, 0.f, 0.f, 0.f};
-  float m_s = -INFINITY;   // running maximum of head r (log2 units)
-  float l_part = 0.f;      // this lane's share of the denominator of head r
-  const float zscale = a.scale * LOG2E;
-  uint8_t* tile = s_tile + wave * AT_TILE_BYTES;
-
-  // Dequantize tile ti chunk by chunk (8 dims of the lane's key per chunk):
-  // each chunk is written to the LDS tile for P V and is the A operand of
-  // S^T = K Q^T from registers.
-  auto stage_swa = [&](int ti, const SwaTile& S, v4f acc[2], uint64_t vmask[2]) {
-    v4u d1[8];
-    float sc1;
-    bool ok1;
-    load_swa_half(ti * 32 + 16 + r, d1, sc1, ok1);
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const v4u* d = kh ? d1 : S.d;
-      const float sc = kh ? sc1 : S.s;
-      const _Float16 mh = scale_mantissa(sc);
-      const v2h m2 = {mh, mh};
-      uint8_t* dst = tile + (kh * 16 + r) * AT_RS + 256 * g;
-      v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // two chains
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        uint32_t kd[4];
-        dequant_fp8x4(d[c >> 1][(c & 1) * 2], sc, m2, &kd[0]);
-        dequant_fp8x4(d[c >> 1][(c & 1) * 2 + 1], sc, m2, &kd[2]);
-        const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
-        *(v4u*)(dst + 16 * c) = kv;
-        s[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qf[c], s[c & 1], 0, 0, 0);
-      }
-      acc[kh] = s[0] + s[1];
-      vmask[kh] = __ballot(S.ok[kh]);
-    }
-  };
-  auto stage_main = [&](const MainTile& M, v4f acc[2], uint64_t vmask[2]) {
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const float4 sc = M.ok[kh] ? M.s[kh] : make_float4(0.f, 0.f, 0.f, 0.f);
-      const float s4[4] = {sc.x, sc.y, sc.z, sc.w};
-      // E4M3 scales of the 8 16-dim groups, widened to f16 (exact)
-      _Float16 s8[8];
-      if (S16) {
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const v2h lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__float_as_uint(s4[w]), 1.0f, false);
-          const v2h hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__float_as_uint(s4[w]), 1.0f, true);
-          s8[4 * w] = lo[0];
-          s8[4 * w + 1] = lo[1];
-          s8[4 * w + 2] = hi[0];
-          s8[4 * w + 3] = hi[1];
-        }
-      }
-      uint8_t* dst = tile + (kh * 16 + r) * AT_RS + 256 * g;
-      v4f s[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};   // two chains
-#pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        uint32_t kd[4];
-        if (S16) {
-          dequant_fp4x8_h(M.d[4 * kh + (c >> 2)][c & 3], s8[c >> 1], kd);
-        } else {
-          const _Float16 mh = scale_mantissa(s4[c >> 2]);
-          dequant_fp4x8(M.d[4 * kh + (c >> 2)][c & 3], s4[c >> 2], (v2h){mh, mh}, kd);
-        }
-        const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
-        *(v4u*)(dst + 16 * c) = kv;
-        s[c & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qf[c], s[c & 1], 0, 0, 0);
-      }
-      acc[kh] = s[0] + s[1];
-      vmask[kh] = __ballot(M.ok[kh]);
-    }
-  };
-
-  // Online softmax over the tile's scores and O += P V.
-  auto finish_tile = [&](const v4f acc[2], const uint64_t vmask[2]) {
-    // scores of head r for keys {4g+i} and {16+4g+i}
-    float z[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      z[i] = ((vmask[0] >> (4 * g + i)) & 1ull) ? acc[0][i] * zscale : -INFINITY;
-      z[4 + i] = ((vmask[1] >> (4 * g + i)) & 1ull) ? acc[1][i] * zscale : -INFINITY;
-    }
-    float mt = z[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, z[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const bool raise = mt > m_s + RESCALE_SLACK || (m_s == -INFINITY && mt > -INFINITY);
-    if (__any(raise)) {
-      const float m_new = fmaxf(m_s, mt);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_s - m_new);
-      l_part *= alpha;
-      m_s = m_new;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float aj = __shfl(alpha, 4 * g + j);
-#pragma unroll
-        for (int u = 0; u < 32; ++u) O[u][j] *= aj;
-      }
-    }
-    v8h P;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float pv = (z[i] == -INFINITY) ? 0.f : exp2f(z[i] - m_s);
-      l_part += pv;
-      P[i] = (_Float16)pv;
-    }
-
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-    // O[h, d] += sum_keys P[h, key] V[key, d].  V is read transposed with
-    // ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
-    // i % 4 of the 8-byte rows addressed by lanes 4 j + i / 4 (j = 0..3).  Lane
-    // (r, g) addresses key 4 g + r / 4 (then 16 + 4 g + r / 4) at column
-    // 16 T + 4 (r % 4), so it receives V[4 g + j][16 T + r] (then the keys
-    // 16 + 4 g + j): exactly its B operand for output columns 16 T .. +16.
-    {
-      __attribute__((address_space(3))) uint8_t* tl =
-          (__attribute__((address_space(3))) uint8_t*)tile;
-      const int off_a = (4 * g + (r >> 2)) * AT_RS + 8 * (r & 3);
-      const int off_b = (16 + 4 * g + (r >> 2)) * AT_RS + 8 * (r & 3);
-#pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s_t*)(tl + off_a + 32 * u));
-        const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s_t*)(tl + off_b + 32 * u));
-        const v8s_pair pr = {lo, hi};
-        const v8h bv = __builtin_bit_cast(v8h, pr);
-        O[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, bv, O[u], 0, 0, 0);
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  };
-
-  // This wave's tiles are wave, wave + 4, ... (SWA tiles first).  The next
-  // tile's rows are requested as soon as the current tile's raw bytes have
-  // been dequantized, so they are in flight during the softmax and the
-  // LDS-bound P V product.
-  int ti = ti0;
-  for (; ti < min(n_tiles, n_swa_tiles); ti += AT_WAVES) {
-    v4f acc[2];
-    uint64_t vmask[2];
-    stage_swa(ti, S, acc, vmask);
-    const int nx = ti + AT_WAVES;
-    if (nx < n_swa_tiles) load_swa(nx, S);
-    else if (nx < n_tiles) load_main(nx, M);
-    finish_tile(acc, vmask);
-  }
-  for (; ti < n_tiles; ti += AT_WAVES) {
-    v4f acc[2];
-    uint64_t vmask[2];
-    stage_main(M, acc, vmask);
-    if (ti + AT_WAVES < n_tiles) load_main(ti + AT_WAVES, M);
-    finish_tile(acc, vmask);
-  }
-
-  // ---- merge the four waves ------------------------------------------------
-  // Each wave's (m, l) per head go through LDS; every lane then forms, for
-  // its rows (heads 4 g + j), the factor that scales each wave's partial O
-  // onto the common maximum and divides by the full denominator (sink
-  // included).  Partials are exchanged in register layout (one 16-byte LDS
-  // store per accumulator), and wave w sums the column blocks u in
-  // [8 w, 8 w + 8) of all four.
-  float l = l_part;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (g == 0) {
-    s_m[wave][r] = m_s;
-    s_l[wave][r] = l;
-  }
-  {
-    uint8_t* part = tile;
-#pragma unroll
-    for (int u = 0; u < 32; ++u) *(v4f*)(part + (u * 64 + lane) * 16) = O[u];
-  }
-  __syncthreads();
-  if (a.n_split > 1) {
-    // partial record of this split: per head the maximum over the waves
-    // (log2 units, no sink), the denominator and O scaled onto that maximum
-    float* rec = a.part + ((int64_t)tg * a.n_split + split) * ATTN_PART_FLOATS;
-    float ew[AT_WAVES][4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int h = 4 * g + j;
-      float M = -INFINITY;
-#pragma unroll
-      for (int w = 0; w < AT_WAVES; ++w) M = fmaxf(M, s_m[w][h]);
-      float lsum = 0.f;
-#pragma unroll
-      for (int w = 0; w < AT_WAVES; ++w) {
-        const float mw = s_m[w][h];
-        ew[w][j] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        lsum += s_l[w][h] * ew[w][j];
-      }
-      if (wave == 0 && r == 0) {
-        rec[h] = M;
-        rec[16 + h] = lsum;
-      }
-    }
-#pragma unroll
-    for (int uu = 0; uu < 32 / AT_WAVES; ++uu) {
-      const int u = wave * (32 / AT_WAVES) + uu;
-      v4f v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < AT_WAVES; ++w) {
-        const v4f x = *(const v4f*)(s_tile + w * AT_TILE_BYTES + (u * 64 + lane) * 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] += x[j] * ew[w][j];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) rec[32 + (4 * g + j) * AT_D + 16 * u + r] = v[j];
-    }
-    return;
-  }
-  float fw[AT_WAVES][4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int h = 4 * g + j;
-    const float sink2 = sink_rows[j] * LOG2E;
-    float M = sink2;
-#pragma unroll
-    for (int w = 0; w < AT_WAVES; ++w) M = fmaxf(M, s_m[w][h]);
-    float den = (M == -INFINITY) ? 0.f : exp2f(sink2 - M);
-    float e[AT_WAVES];
-#pragma unroll
-    for (int w = 0; w < AT_WAVES; ++w) {
-      const float mw = s_m[w][h];
-      e[w] = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-      den += s_l[w][h] * e[w];
-    }
-    const float inv = (den > 0.f) ? 1.f / den : 0.f;
-#pragma unroll
-    for (int w = 0; w < AT_WAVES; ++w) fw[w][j] = e[w] * inv;
-    if (a.lse && wave == 0 && r == 0) a.lse[(int64_t)t * a.H + h_glob0 + h] = (M + log2f(den)) * LN2;
-  }
-  const int64_t obase = ((int64_t)t * a.H + h_glob0 + 4 * g) * AT_D + r;
-  // inverse RoPE of dims 448..511 (column groups u = 28..31, the last
-  // wave's): the pair (2i, 2i+1) sits in lanes r, r ^ 1, so a turning lane
-  // also merges its partner's column from LDS (a DPP exchange here instead
-  // made the compiler duplicate the key loop, a third slower)
-  constexpr int U_TURN = 28;
-  const bool turn = TURN && a.rope != nullptr && p >= 0 && p < a.n_rope && wave == AT_WAVES - 1;
-  const float* cs = a.rope + (int64_t)max(p, 0) * 64;   // read only when turning
-#pragma unroll
-  for (int uu = 0; uu < 32 / AT_WAVES; ++uu) {
-    const int u = wave * (32 / AT_WAVES) + uu;
-    v4f v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < AT_WAVES; ++w) {
-      const v4f x = *(const v4f*)(s_tile + w * AT_TILE_BYTES + (u * 64 + lane) * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) v[j] += x[j] * fw[w][j];
-    }
-    if (turn && u >= U_TURN) {
-      // the partner column (lane ^ 1, same rows) merged the same way
-      v4f vp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < AT_WAVES; ++w) {
-        const v4f x = *(const v4f*)(s_tile + w * AT_TILE_BYTES + (u * 64 + (lane ^ 1)) * 16);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vp[j] += x[j] * fw[w][j];
-      }
-      const float c = cs[8 * (u - U_TURN) + (r >> 1)], sn = cs[32 + 8 * (u - U_TURN) + (r >> 1)];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float x = (r & 1) ? vp[j] : v[j], y = (r & 1) ? v[j] : vp[j];
-        unturn(x, y, c, sn);
-        v[j] = (r & 1) ? y : x;
-      }
-    }
-    // rows 4 g + j, column 16 u + r: 16 lanes write 16 consecutive columns
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t o = obase + (int64_t)j * AT_D + 16 * u;
-      if (a.out_bf16) ((uint16_t*)a.out)[o] = f32_to_bf16_rne(v[j]);
-      else ((float*)a.out)[o] = v[j];
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// Unsplit calls (many queries): the same arithmetic at two waves per SIMD.
-// One workgroup = one query x 16 heads, eight waves over 16-key tiles (SWA
-// tiles first).  q is staged once in LDS as f16 and read per 8-dim chunk as
+// One workgroup = one query x 16 heads (x one key split), eight waves over
+// 16-key tiles (SWA tiles first), two waves per SIMD.  q is staged once in LDS
+// as f16 and read per 8-dim chunk as
 // the B operand of S^T = K Q^T, so a wave holds only O (128 registers), one
 // tile's raw bytes and its working set, and two waves share each SIMD.  P V
 // runs on v_mfma_f32_16x16x16_f16, whose A operand is S^T's accumulator
 // layout for 16 keys (lane (r, g): head r, keys 4 g .. 4 g + 3) and whose B
 // operand is what ds_read_b64_tr_b16 returns from the tile.  The eight
 // waves' partial results are merged through LDS, one half of the 512 output
-// columns at a time.
+// columns at a time, into the output or (key splits) a partial record.
+// (A four-wave form with 32-key tiles and q in registers needed ~500
+// registers, one wave per SIMD: 26.3 us per 64-query group call against
+// 21.9 us here, and 1.41 ms against 1.18 ms on the 4,096-query chunk.)
 constexpr int AW_WAVES = 8;
 constexpr int AW_TILE_BYTES = 16 * AT_RS;     // one wave's 16-key tile
 static_assert(AW_WAVES * AW_TILE_BYTES >= AW_WAVES * 16 * 64 * 16, "half of every wave's O must fit the tiles");
 
 template <bool S16, bool TURN>
-__global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_wide_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_tile[AW_WAVES * AW_TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t s_q[AT_HEADS * AT_RS];
   __shared__ float s_m[AW_WAVES][AT_HEADS];
@@ -563,8 +131,10 @@ __global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_wide_kernel(A
   const int nblk = gridDim.x;
   // the workgroups of a query on one XCD (handed out round-robin)
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  const int t = bid / n_hg;
-  const int hg = bid - t * n_hg;
+  const int split = bid % a.n_split;
+  const int tg = bid / a.n_split;
+  const int t = tg / n_hg;
+  const int hg = tg - t * n_hg;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -581,7 +151,12 @@ __global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_wide_kernel(A
   const int n_swa = max(0, p - first + 1);
   const int64_t sbase = a.swa_base[b] + (first - sp0);
   const int n_swa_tiles = (n_swa + 15) >> 4;
-  const int n_tiles = n_swa_tiles + ((a.k + 15) >> 4);
+  const int n_tiles_all = n_swa_tiles + ((a.k + 15) >> 4);
+  // this workgroup's tiles: [tile_begin, n_tiles) of the query's tile list
+  // (SWA tiles first); the whole list when keys are not split
+  const int per_split = (n_tiles_all + a.n_split - 1) / a.n_split;
+  const int tile_begin = min(n_tiles_all, split * per_split);
+  const int n_tiles = min(n_tiles_all, tile_begin + per_split);
   const int h_glob0 = hg * AT_HEADS;
   // keys that do not exist are read from this query's own q row (always
   // mapped, 64 KB) and given a zero scale, so every load is unconditional
@@ -630,8 +205,8 @@ __global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_wide_kernel(A
   // ---- prologue: every independent load is issued before any is waited on
   WSwa S;
   WMain M;
-  const int ti0 = wave;
-  if (ti0 < n_swa_tiles) load_swa(ti0, S);   // needs no staged index
+  const int ti0 = tile_begin + wave;
+  if (ti0 < n_tiles && ti0 < n_swa_tiles) load_swa(ti0, S);   // needs no staged index
   // q of the 16 heads: thread i converts dims [16 (i % 32), +16) of head i / 32
   v4u qraw[2];
   const int qh = threadIdx.x >> 5, qd = (threadIdx.x & 31) * 16;
@@ -809,6 +384,54 @@ __global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_wide_kernel(A
     s_l[wave][r] = l;
   }
   __syncthreads();   // every wave is done with its tile; s_m, s_l
+  constexpr int HALF_BYTES = 16 * 64 * 16;               // 16 column blocks of one wave
+  if (a.n_split > 1) {
+    // partial record of this split: per head the maximum over the waves
+    // (log2 units, no sink), the denominator and O scaled onto that maximum
+    float* rec = a.part + ((int64_t)tg * a.n_split + split) * ATTN_PART_FLOATS;
+    float ew[AW_WAVES][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int h = 4 * g + j;
+      float Mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < AW_WAVES; ++w) Mx = fmaxf(Mx, s_m[w][h]);
+      float lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < AW_WAVES; ++w) {
+        const float mw = s_m[w][h];
+        ew[w][j] = (mw == -INFINITY) ? 0.f : exp2f(mw - Mx);
+        lsum += s_l[w][h] * ew[w][j];
+      }
+      if (wave == 0 && r == 0) {
+        rec[h] = Mx;
+        rec[16 + h] = lsum;
+      }
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint8_t* part = s_tile + wave * HALF_BYTES;
+#pragma unroll
+      for (int uu = 0; uu < 16; ++uu) *(v4f*)(part + (uu * 64 + lane) * 16) = O[16 * half + uu];
+      __syncthreads();
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const int uu = 2 * wave + k2;
+        const int u = 16 * half + uu;
+        v4f v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int w = 0; w < AW_WAVES; ++w) {
+          const v4f x = *(const v4f*)(s_tile + w * HALF_BYTES + (uu * 64 + lane) * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] += x[j] * ew[w][j];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rec[32 + (4 * g + j) * AT_D + 16 * u + r] = v[j];
+      }
+      __syncthreads();   // the next half reuses the tiles
+    }
+    return;
+  }
   float fw[AW_WAVES][4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -835,7 +458,6 @@ __global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_wide_kernel(A
   const bool turn = TURN && a.rope != nullptr && p >= 0 && p < a.n_rope;
   const float* cs = a.rope + (int64_t)max(p, 0) * 64;   // read only when turning
   constexpr int U_TURN = 28;
-  constexpr int HALF_BYTES = 16 * 64 * 16;               // 16 column blocks of one wave
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     uint8_t* part = s_tile + wave * HALF_BYTES;
@@ -1060,40 +682,27 @@ __global__ __launch_bounds__(ATTN_COMBINE_THREADS) void sparse_attn_combine_kern
 }
 
 // Key splits per (query, 16 heads): only when the batch leaves most of the
-// chip idle; about four 32-key tiles per split (one per wave), at most 8.
+// chip idle; about eight 16-key tiles per split (one per wave), at most 8.
 int attn_splits(int Q, int H, int k, int window) {
   const int groups = Q * (H / AT_HEADS);
   if (groups <= 0 || groups >= 128) return 1;
-  const int tiles = (window + 31) / 32 + (k + 31) / 32;
-  int ns = (tiles + AT_WAVES - 1) / AT_WAVES;
+  const int tiles = (window + 15) / 16 + (k + 15) / 16;   // 16-key tiles
+  int ns = (tiles + AW_WAVES - 1) / AW_WAVES;             // about one per wave
   ns = min(ns, max(1, 256 / groups));
   return max(1, min(ns, ATTN_MAX_SPLIT));
 }
 
 hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s) {
   const int groups = a.Q * (a.H / AT_HEADS);
-  if (a.n_split == 1) {
-    // unsplit (many queries): eight waves, two per SIMD
-    const bool turn = a.rope != nullptr;
-    const dim3 g1(groups), blk(64 * AW_WAVES);
-    if (a.main_s16) {
-      if (turn) hipLaunchKernelGGL((sparse_attn_quant_wide_kernel<true, true>), g1, blk, 0, s, a);
-      else hipLaunchKernelGGL((sparse_attn_quant_wide_kernel<true, false>), g1, blk, 0, s, a);
-    } else {
-      if (turn) hipLaunchKernelGGL((sparse_attn_quant_wide_kernel<false, true>), g1, blk, 0, s, a);
-      else hipLaunchKernelGGL((sparse_attn_quant_wide_kernel<false, false>), g1, blk, 0, s, a);
-    }
-    return hipGetLastError();
-  }
-  const dim3 grid(groups * a.n_split);
   // split calls turn the output in the combine kernel
   const bool turn = a.rope != nullptr && a.n_split == 1;
+  const dim3 grid(groups * a.n_split), block(64 * AW_WAVES);
   if (a.main_s16) {
-    if (turn) hipLaunchKernelGGL((sparse_attn_quant_kernel<true, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((sparse_attn_quant_kernel<true, false>), grid, dim3(256), 0, s, a);
+    if (turn) hipLaunchKernelGGL((sparse_attn_quant_kernel<true, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((sparse_attn_quant_kernel<true, false>), grid, block, 0, s, a);
   } else {
-    if (turn) hipLaunchKernelGGL((sparse_attn_quant_kernel<false, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((sparse_attn_quant_kernel<false, false>), grid, dim3(256), 0, s, a);
+    if (turn) hipLaunchKernelGGL((sparse_attn_quant_kernel<false, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((sparse_attn_quant_kernel<false, false>), grid, block, 0, s, a);
   }
   if (a.n_split > 1) {
     hipError_t e = hipGetLastError();

@@ -428,7 +428,7 @@ __global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_kernel(AttnAr
 #pragma unroll
         for (int j = 0; j < 4; ++j) rec[32 + (4 * g + j) * AT_D + 16 * u + r] = v[j];
       }
-      __syncthreads();   // the next half reuses the tiles
+      if (half == 0) __syncthreads();   // the second half reuses the tiles
     }
     return;
   }
@@ -499,7 +499,7 @@ __global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_kernel(AttnAr
         else ((float*)a.out)[o] = v[j];
       }
     }
-    __syncthreads();   // the next half reuses the tiles
+    if (half == 0) __syncthreads();   // the second half reuses the tiles
   }
 }
 

@@ -48,12 +48,14 @@ def _random_idx(rng, nvis, k, frac_valid=1.0):
 # ---------------------------------------------------------------------------
 # inverse RoPE of the attention output
 
-@pytest.mark.parametrize("quantized,split", [(True, True), (True, False), (False, False)])
-def test_attention_output_is_turned_back(quantized, split):
-    _announce(f"attention inverse RoPE quantized={quantized} split={split}")
+@pytest.mark.parametrize("quantized,split,main_fmt", [(True, True, "fp4"), (True, False, "fp4"),
+                                                     (True, True, "fp4s16"), (True, False, "fp4s16"),
+                                                     (False, False, "fp4")])
+def test_attention_output_is_turned_back(quantized, split, main_fmt):
+    _announce(f"attention inverse RoPE quantized={quantized} split={split} main={main_fmt}")
     wl = synth.mini_workload(70, [3000, 700, 200], ratio=1,
                              positions=[[2999, 1500], [699], [150, 0]],
-                             quantized=quantized).to(DEV)
+                             quantized=quantized, main_fmt=main_fmt).to(DEV)
     rope = synth.rope_table(3000, DEV)
     run = LayerRunner(wl, rope_cs=rope)
     if not split:

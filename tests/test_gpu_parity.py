@@ -366,6 +366,20 @@ def test_sparse_attn_split_workspace_reuse():
         check_attention(_np(run.out[0].float()), ref)
 
 
+@pytest.mark.parametrize("split", [True, False])
+def test_sparse_attn_ragged_k_and_window(split):
+    """A top-k count and a window that are not multiples of the 16-key tile:
+    the last main and SWA tiles are partial."""
+    _announce(f"sparse_attn ragged k=77 window=50 split={split}")
+    wl = synth.mini_workload(37, [3000, 900, 400], topk=77,
+                             positions=[[2999, 1200], [899], [399, 30]]).to(DEV)
+    rng = np.random.default_rng(38)
+    idx = _random_idx(rng, _np(wl.n_vis()), 77, 0.95)
+    gpu, gl, ref, rl = _attn_case(wl, idx, window=50, split=split)
+    check_attention(gpu, ref)
+    assert np.abs(gl - rl).max() <= 1e-3
+
+
 def test_sparse_attn_quant_duplicates_and_out_of_range():
     _announce("sparse_attn quantized duplicates / out-of-range indices")
     wl = synth.mini_workload(31, [1000], q_per_seq=2).to(DEV)

@@ -380,6 +380,18 @@ def test_sparse_attn_ragged_k_and_window(split):
     assert np.abs(gl - rl).max() <= 1e-3
 
 
+@pytest.mark.parametrize("split", [True, False])
+def test_sparse_attn_largest_k(split):
+    """The largest top-k the kernel stages (2048 indices per query)."""
+    _announce(f"sparse_attn k=2048 split={split}")
+    wl = synth.mini_workload(39, [6000, 2500], q_per_seq=2, topk=2048).to(DEV)
+    rng = np.random.default_rng(40)
+    idx = _random_idx(rng, _np(wl.n_vis()), 2048, 1.0)
+    gpu, gl, ref, rl = _attn_case(wl, idx, split=split)
+    check_attention(gpu, ref)
+    assert np.abs(gl - rl).max() <= 1e-3
+
+
 def test_sparse_attn_quant_duplicates_and_out_of_range():
     _announce("sparse_attn quantized duplicates / out-of-range indices")
     wl = synth.mini_workload(31, [1000], q_per_seq=2).to(DEV)

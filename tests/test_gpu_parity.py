@@ -392,6 +392,41 @@ def test_sparse_attn_largest_k(split):
     assert np.abs(gl - rl).max() <= 1e-3
 
 
+@pytest.mark.parametrize("H,split", [(16, True), (16, False), (128, True), (128, False)])
+def test_sparse_attn_head_counts(H, split):
+    """Head counts other than 64 (one and eight 16-head groups per query),
+    through the C ABI with random bf16 queries and sinks over a workload's
+    caches."""
+    _announce(f"sparse_attn H={H} split={split}")
+    wl = synth.mini_workload(41, [2000, 700], q_per_seq=2).to(DEV)
+    run = LayerRunner(wl)
+    rng = np.random.default_rng(42)
+    q = torch.from_numpy(rng.standard_normal((wl.Q, H, 512)).astype(np.float32)).to(torch.bfloat16).to(DEV)
+    sink = torch.from_numpy(rng.standard_normal(H).astype(np.float32)).to(DEV)
+    idx_np = _random_idx(rng, _np(wl.n_vis()), 512, 0.9)
+    idx = torch.from_numpy(idx_np.astype(np.int32)).to(DEV)
+    out = torch.empty((wl.Q, H, 512), dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty((wl.Q, H), dtype=torch.float32, device=DEV)
+    ws = None
+    if split:
+        nb = tsl.csa2_sparse_attn_workspace_size(wl.Q, H, 512, wl.window)
+        assert nb > 0
+        ws = torch.zeros((nb,), dtype=torch.uint8, device=DEV)
+    tsl.csa2_sparse_attn(q, tsl.CSA2_BF16, run.slots.compress_kv, wl.seq_base, idx, 512,
+                         run.layer_rows[0]["swa"], wl.swa_base, wl.swa_pos0, None, wl.window,
+                         wl.q_seq, wl.q_pos, wl.ratio, sink, wl.softmax_scale, out, tsl.CSA2_BF16,
+                         lse, wl.Q, H=H, workspace=ws)
+    torch.cuda.synchronize()
+    m = oracle_io.meta(wl)
+    ref, ref_lse = oracle.sparse_attn(_np(q.float()).astype(np.float64), oracle_io.main_rows(wl),
+                                      m["seq_base"], idx_np, oracle_io.swa_rows(wl.layers[0], True),
+                                      m["swa_base"], m["swa_pos0"], None, wl.window, m["q_seq"],
+                                      m["q_pos"], _np(sink).astype(np.float64), wl.softmax_scale,
+                                      wl.ratio)
+    check_attention(_np(out.float()), ref)
+    assert np.abs(_np(lse) - ref_lse).max() <= 1e-3
+
+
 def test_sparse_attn_quant_duplicates_and_out_of_range():
     _announce("sparse_attn quantized duplicates / out-of-range indices")
     wl = synth.mini_workload(31, [1000], q_per_seq=2).to(DEV)

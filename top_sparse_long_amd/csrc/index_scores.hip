@@ -49,7 +49,10 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 #endif
 constexpr int IS_WAVES = CSA2_IS_WAVES;                      // waves per workgroup
 constexpr int IS_TILES = CSA2_IS_TILES;                      // 32-key tiles per wave per sub-chunk
-constexpr int IS_SUB = IS_WAVES * 32 * IS_TILES;             // columns per sub-chunk (256)
+// Dense calls of at most this many keys (queries x columns) use one tile per
+// wave per sub-chunk: twice the workgroups, each lighter (measured: 128K x 8
+// queries 33.4 against 34.4 us; neutral at 2M keys, slower at 16M).
+constexpr int64_t IS_ONE_TILE_MAX_KEYS = 3 << 19;
 #ifndef CSA2_IS_RESIDENT
 #define CSA2_IS_RESIDENT 768
 #endif
@@ -149,8 +152,9 @@ __device__ __forceinline__ float group_max(float m, int bs) {
   return m;
 }
 
-template <bool POOL, bool W_BF16, bool K4, bool PAGED>
+template <bool POOL, bool W_BF16, bool K4, bool PAGED, int TILES>
 __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexScoreArgs a) {
+  constexpr int SUB = IS_WAVES * 32 * TILES;   // columns per sub-chunk
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -163,9 +167,9 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
   // This workgroup's sub-chunks are blockIdx.x, blockIdx.x + gridDim.x, ...
   // of the row, so at any moment the workgroups of a query stream
   // neighbouring sub-chunks (measured about 4 % faster than contiguous runs).
-  const int col_begin = blockIdx.x * IS_SUB;
+  const int col_begin = blockIdx.x * SUB;
   const int col_end = a.n_cols;
-  const int col_step = gridDim.x * IS_SUB;
+  const int col_step = gridDim.x * SUB;
   float* out = a.scores + (int64_t)t * a.score_stride;
   // Dense mode: columns past the visible prefix only need -inf.
   const int limit = (nvis <= 0) ? 0 : (POOL ? a.n_cols : min(a.n_cols, nvis));
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
   if (limit == 0) {
     // nothing visible: every column of this workgroup is -inf
     for (int c0 = col_begin; c0 < col_end; c0 += col_step)
-      for (int c = c0 + threadIdx.x; c < min(col_end, c0 + IS_SUB); c += 64 * IS_WAVES) {
+      for (int c = c0 + threadIdx.x; c < min(col_end, c0 + SUB); c += 64 * IS_WAVES) {
         out[c] = -INFINITY;
         if (!POOL && a.block_max && (c & ((1 << a.block_shift) - 1)) == 0)
           a.block_max[(int64_t)t * a.block_max_stride + (c >> a.block_shift)] = -INFINITY;
@@ -197,18 +201,18 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
     return;
   }
 
-  // One sub-chunk = IS_SUB columns; this wave's tiles in it are columns
+  // One sub-chunk = SUB columns; this wave's tiles in it are columns
   // sc0 + (i * IS_WAVES + wave) * 32 + [0, 32).  Every load is
   // unconditional: lanes whose column scores nothing read position 0 of the
   // sequence (visible, since limit > 0) and are masked afterwards.
   struct Sub {
-    v4u raw[IS_TILES][4];
-    float ks[IS_TILES];
-    int pos[IS_TILES];
+    v4u raw[TILES][4];
+    float ks[TILES];
+    int pos[TILES];
   };
   auto load_sub = [&](int sc0, Sub& S) {
 #pragma unroll
-    for (int i = 0; i < IS_TILES; ++i) {
+    for (int i = 0; i < TILES; ++i) {
       const int tcol = sc0 + (i * IS_WAVES + wave) * 32;
       S.pos[i] = (tcol < limit) ? column_position<POOL>(a, t, tcol + r, nvis) : -1;
       int pg = 0;
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
 
   auto compute_sub = [&](int sc0, const Sub& S) {
 #pragma unroll
-    for (int i = 0; i < IS_TILES; ++i) {
+    for (int i = 0; i < TILES; ++i) {
       const int tcol = sc0 + (i * IS_WAVES + wave) * 32;
       if (tcol >= col_end) break;
       const int col = tcol + r;
@@ -554,15 +558,24 @@ static void launch_prefill(const IndexScoreArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((index_scores_prefill_kernel<W_BF16, K4, PAGED>), grid, dim3(64 * PF_WAVES), 0, s, b);
 }
 
-template <bool POOL, bool W_BF16, bool K4, bool PAGED>
-static void launch_decode(const IndexScoreArgs& a, hipStream_t s) {
+template <bool POOL, bool W_BF16, bool K4, bool PAGED, int TILES>
+static void launch_decode_t(const IndexScoreArgs& a, hipStream_t s) {
   // sub-chunks per workgroup: enough workgroups for about one resident
   // round, each striding over the sub-chunks of one query's row
+  constexpr int SUB = IS_WAVES * 32 * TILES;
   IndexScoreArgs b = a;
-  const int64_t subs = (a.n_cols + IS_SUB - 1) / IS_SUB;
+  const int64_t subs = (a.n_cols + SUB - 1) / SUB;
   b.sub_per_wg = (int)std::max<int64_t>(1, (subs * a.Q + IS_RESIDENT_WGS - 1) / IS_RESIDENT_WGS);
   dim3 grid((unsigned)((subs + b.sub_per_wg - 1) / b.sub_per_wg), a.Q);
-  hipLaunchKernelGGL((index_scores_fp8_kernel<POOL, W_BF16, K4, PAGED>), grid, dim3(64 * IS_WAVES), 0, s, b);
+  hipLaunchKernelGGL((index_scores_fp8_kernel<POOL, W_BF16, K4, PAGED, TILES>), grid, dim3(64 * IS_WAVES), 0, s, b);
+}
+
+template <bool POOL, bool W_BF16, bool K4, bool PAGED>
+static void launch_decode(const IndexScoreArgs& a, hipStream_t s) {
+  if (!POOL && (int64_t)a.n_cols * a.Q <= IS_ONE_TILE_MAX_KEYS)
+    launch_decode_t<POOL, W_BF16, K4, PAGED, 1>(a, s);
+  else
+    launch_decode_t<POOL, W_BF16, K4, PAGED, IS_TILES>(a, s);
 }
 
 template <bool K4, bool PAGED>

@@ -303,12 +303,15 @@ def block_candidates(scores, q_pos, ratio, block_size, n_blocks):
 def attention_keys(t, main_rows, main_base, idx, swa_rows, swa_base, swa_pos0,
                    swa_lo, window, q_seq, q_pos, ratio=1):
     """Key matrix of query t: SWA rows (oldest first), then main rows.
-    Reading: an idx entry that is negative or not visible to the query
-    ((pos+1)//ratio or beyond) names no key."""
+    Readings: an idx entry that is negative or not visible to the query
+    ((pos+1)//ratio or beyond) names no key; SWA positions below swa_pos0[b]
+    (rows the caller does not hold) are not in the window."""
     b = int(q_seq[t])
     p = int(q_pos[t])
     lo = 0 if swa_lo is None else int(swa_lo[b])
-    first = max(lo, p - window + 1)
+    # the window starts at the replay start, at the oldest stored SWA row
+    # (position swa_pos0[b]) and at position 0, whichever is latest
+    first = max(lo, int(swa_pos0[b]), p - window + 1, 0)
     swa_idx = int(swa_base[b]) + np.arange(first, p + 1) - int(swa_pos0[b])
     sel = np.asarray(idx[t], dtype=np.int64)
     sel = sel[(sel >= 0) & (sel < (p + 1) // int(ratio))]

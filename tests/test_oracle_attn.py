@@ -135,3 +135,83 @@ def test_empty_key_set_gives_zero():
                                   np.zeros((1, 4)), [0], [0], None, 0, [0], [0],
                                   np.array([0.0, 1.0]), 1.0)
     assert np.all(out == 0) and np.allclose(lse, [0.0, 1.0])
+
+
+def _dense_reference(q, keys, mask, sink, scale):
+    """Plain softmax over every candidate key row with -inf outside `mask`,
+    plus one sink column whose value row is zero: [H, D]."""
+    H, D = q.shape
+    allk = np.concatenate([keys, np.zeros((1, D))])
+    m = np.append(mask, True)
+    out = np.zeros((H, D))
+    for h in range(H):
+        z = np.append(scale * keys @ q[h], sink[h])
+        z[~m] = -np.inf
+        pr = np.exp(z - z.max())
+        out[h] = (pr / pr.sum()) @ allk
+    return out
+
+
+@pytest.mark.parametrize("ratio", [1, 2])
+def test_invalid_indices_name_no_key(ratio):
+    """Reading 22: an idx entry that is negative or at/after the query's
+    visible count (p+1)//m names no key.  Brute force: a dense mask over every
+    main row of the sequence, built from the entries that lie in [0, n_vis),
+    gives the same output; and replacing the invalid entries by -1 changes
+    nothing.  The entries n_vis - 1 (kept) and n_vis (dropped) pin the
+    boundary."""
+    rng = np.random.default_rng(11)
+    H, D, N = 3, 8, 50
+    p = 37
+    n_vis = (p + 1) // ratio
+    q = rng.normal(size=(1, H, D))
+    main = rng.normal(size=(N, D))
+    swa = rng.normal(size=(4, D))
+    sink = rng.normal(size=H)
+    idx = np.array([[2, n_vis - 1, n_vis, n_vis + 5, N - 1, -1, -7, 5]])
+    args = dict(main_rows=main, main_base=[0], swa_rows=swa, swa_base=[0], swa_pos0=[p - 3],
+                swa_lo=None, window=4, q_seq=[0], q_pos=[p], sink=sink, scale=0.4, ratio=ratio)
+    out, _ = oracle.sparse_attn(q, idx=idx, **args)
+    clean = np.where((idx >= 0) & (idx < n_vis), idx, -1)
+    out_clean, _ = oracle.sparse_attn(q, idx=clean, **args)
+    assert np.array_equal(out, out_clean)
+    keys = np.concatenate([swa, main])
+    mask = np.concatenate([np.ones(4, bool),
+                           np.isin(np.arange(N), [2, n_vis - 1, 5]) & (np.arange(N) < n_vis)])
+    assert np.allclose(out[0], _dense_reference(q[0], keys, mask, sink, 0.4), rtol=1e-12, atol=1e-13)
+    K = oracle.attention_keys(0, main, [0], idx, swa, [0], [p - 3], None, 4, [0], [p], ratio)
+    assert K.shape[0] == 4 + 3
+
+
+@pytest.mark.parametrize("pos0_offset,lo_offset,expect_swa", [
+    (0, None, 10),      # every stored row inside the window
+    (4, None, 6),       # oldest stored row after p - W + 1: the window starts there
+    (4, 7, 3),          # replay start after the stored rows: it wins
+    (4, 10, 0),         # replay start past p: no SWA key at all
+    (0, 2, 8),          # replay start inside the window
+])
+def test_window_starts_at_latest_of_replay_stored_and_window(pos0_offset, lo_offset, expect_swa):
+    """CSA2 page, 'CED' (bounded replay): the query at p sees the SWA keys of
+    [max(s, p-W+1), p].  Rows before the oldest stored position swa_pos0 do
+    not exist and are skipped (the stored rows start at swa_base).  Brute
+    force over the stored rows with an explicit position mask."""
+    rng = np.random.default_rng(12)
+    H, D, W = 2, 6, 10
+    p = 40
+    pos0 = p - W + 1 + pos0_offset
+    n_stored = p - pos0 + 1
+    q = rng.normal(size=(1, H, D))
+    swa = rng.normal(size=(3 + n_stored, D))      # three rows of another sequence first
+    main = rng.normal(size=(20, D))
+    sink = rng.normal(size=H)
+    idx = np.array([[3, 9, -1]])
+    lo = None if lo_offset is None else np.array([p - W + 1 + lo_offset])
+    out, _ = oracle.sparse_attn(q, main, [0], idx, swa, [3], [pos0], lo, W, [0], [p], sink, 0.5)
+    K = oracle.attention_keys(0, main, [0], idx, swa, [3], [pos0], lo, W, [0], [p])
+    assert K.shape[0] == expect_swa + 2
+    pos = pos0 + np.arange(n_stored)
+    start = p - W + 1 if lo is None else max(p - W + 1, int(lo[0]))
+    keys = np.concatenate([swa[3:], main])
+    mask = np.concatenate([(pos >= start) & (pos <= p), np.isin(np.arange(20), [3, 9])])
+    assert mask[:n_stored].sum() == expect_swa
+    assert np.allclose(out[0], _dense_reference(q[0], keys, mask, sink, 0.5), rtol=1e-12, atol=1e-13)

@@ -107,6 +107,45 @@ def test_index_scores_prefill_fp8(case, k_fmt):
         assert np.all(bm[t, len(refb):] == -np.inf), t
 
 
+ONE_TILE_MAX_KEYS = 3 << 19      # dense decode calls above this many query x column keys
+
+
+@pytest.mark.parametrize("k_fmt", ["fp8", "fp4s16"])
+def test_index_scores_dense_two_tile_ragged(k_fmt):
+    """Dense decode calls of more than 1.5M keys (queries x columns) run the
+    two-tile-per-wave kernel.  Eight queries over ragged rows of up to
+    200,003 columns reach it: partial last sub-chunks, fused block maxima on
+    ragged tails, and (paged) page lookups at the rows' ends.  The paged run
+    moves the same bytes through other addresses and must equal the flat run
+    bit for bit."""
+    n_entries = [200003, 150001, 77, 199990]
+    positions = [[200002, 123457], [150000, 149999], [76, 3], [199989, 511]]
+    _announce(f"index_scores dense two-tile kernel keys={k_fmt}")
+    wl = synth.mini_workload(45, n_entries, positions=positions, k_fmt=k_fmt).to(DEV)
+    flat = LayerRunner(wl)
+    assert wl.Q * flat.n_cols > ONE_TILE_MAX_KEYS
+    paged = LayerRunner(wl, paged=synth.paged_layout(wl, 46))
+    for run in (flat, paged):
+        run.index_scores(0, pool=False, block_max=True)
+    torch.cuda.synchronize()
+    gpu = _np(flat.scores[:, :flat.n_cols])
+    m = oracle_io.meta(wl)
+    ref = oracle.index_scores_dense(oracle_io.index_q(wl.layers[0], True),
+                                    oracle_io.index_w(wl.layers[0], True),
+                                    oracle_io.index_k_rows(wl), m["seq_base"], m["q_seq"],
+                                    m["q_pos"], 1, flat.n_cols)
+    check_scores(gpu, ref)
+    nb = -(-flat.n_cols // 8)
+    bm = _np(flat.block_max[:, :nb]).astype(np.float64)
+    nvis = oracle.visible_count(m["q_pos"], 1)
+    for t in range(wl.Q):
+        refb = oracle.block_maxima(gpu[t].astype(np.float64), int(nvis[t]), 8)
+        assert np.array_equal(bm[t, :len(refb)], refb), t
+        assert np.all(bm[t, len(refb):] == -np.inf), t
+    assert torch.equal(flat.scores[:, :flat.n_cols], paged.scores[:, :paged.n_cols])
+    assert torch.equal(flat.block_max[:, :nb], paged.block_max[:, :nb])
+
+
 def test_index_scores_f32_exact():
     _announce("index_scores f32 integer-exact")
     wl = synth.mini_workload(3, [3000, 777], q_per_seq=3, quantized=False).to(DEV)
@@ -445,6 +484,71 @@ def test_sparse_attn_empty_key_set():
     gpu, gl, ref, rl = _attn_case(wl, idx, window=0)
     assert np.all(gpu == 0)
     assert np.allclose(gl[0], _np(wl.layers[0].sink), atol=1e-6)
+
+
+@pytest.mark.parametrize("quantized,main_fmt,split", [(True, "fp4", True), (True, "fp4", False),
+                                                     (True, "fp4s16", True), (True, "fp4s16", False),
+                                                     (False, "fp4", False)])
+def test_sparse_attn_bounded_replay_window(quantized, main_fmt, split):
+    """CSA2 page, 'CED' (bounded replay): the query at p sees the SWA keys of
+    [max(s, p-W+1), p] for the replay start s (swa_lo), and none before the
+    oldest stored row (swa_pos0).  Five sequences mix the cases: s inside the
+    window, s = p (the current token only), s = p + 1 (no SWA key), stored
+    rows that start after p - W + 1, and the whole window."""
+    _announce(f"sparse_attn swa_lo/swa_pos0 quantized={quantized} main={main_fmt} split={split}")
+    n_entries = [3000, 1500, 900, 2600, 700]
+    wl = synth.mini_workload(43, n_entries, quantized=quantized, main_fmt=main_fmt).to(DEV)
+    run = LayerRunner(wl)
+    if not split:
+        run.ws_attn = None
+    else:
+        assert run.ws_attn is not None
+    q_pos = _np(wl.q_pos).astype(np.int64)
+    lo = np.zeros(5, dtype=np.int64)
+    lo[0] = q_pos[0] - 60
+    lo[1] = q_pos[1]
+    lo[2] = q_pos[2] + 1
+    # sequence 3 holds only its last 88 SWA rows: the same rows, with the
+    # oldest stored position moved up by 40
+    pos0 = _np(wl.swa_pos0).astype(np.int64)
+    base = _np(wl.swa_base).astype(np.int64)
+    assert pos0[3] == q_pos[3] - wl.window + 1
+    pos0[3] += 40
+    base[3] += 40
+    swa_lo = torch.from_numpy(lo.astype(np.int32)).to(DEV)
+    swa_pos0 = torch.from_numpy(pos0.astype(np.int32)).to(DEV)
+    swa_base = torch.from_numpy(base).to(DEV)
+    rng = np.random.default_rng(44)
+    idx_np = _random_idx(rng, _np(wl.n_vis()), 512, 0.9)
+    idx = torch.from_numpy(idx_np.astype(np.int32)).to(DEV)
+    lay = wl.layers[0]
+    dt = tsl.CSA2_BF16 if quantized else tsl.CSA2_F32
+    tsl.csa2_sparse_attn(lay.q, dt, run.slots.compress_kv, wl.seq_base, idx, 512,
+                         run.layer_rows[0]["swa"], swa_base, swa_pos0, swa_lo, wl.window,
+                         wl.q_seq, wl.q_pos, wl.ratio, lay.sink, wl.softmax_scale, run.out[0], dt,
+                         run.lse[0], wl.Q, workspace=run.ws_attn)
+    torch.cuda.synchronize()
+    m = oracle_io.meta(wl)
+    ref, ref_lse = oracle.sparse_attn(oracle_io.attn_q(lay, quantized), oracle_io.main_rows(wl),
+                                      m["seq_base"], idx_np, oracle_io.swa_rows(lay, quantized),
+                                      base, pos0, lo, wl.window, m["q_seq"], m["q_pos"],
+                                      _np(lay.sink).astype(np.float64), wl.softmax_scale, wl.ratio)
+    n_swa = [oracle.attention_keys(t, oracle_io.main_rows(wl), m["seq_base"], np.full((5, 1), -1),
+                                   oracle_io.swa_rows(lay, quantized), base, pos0, lo, wl.window,
+                                   m["q_seq"], m["q_pos"]).shape[0] for t in range(5)]
+    assert n_swa == [61, 1, 0, 88, 128]
+    gpu = _np(run.out[0].float())
+    check_attention(gpu, ref)
+    assert np.abs(_np(run.lse[0]) - ref_lse).max() <= 1e-3
+    # the unbounded call differs exactly on the bounded sequences
+    full, _ = oracle.sparse_attn(oracle_io.attn_q(lay, quantized), oracle_io.main_rows(wl),
+                                 m["seq_base"], idx_np, oracle_io.swa_rows(lay, quantized),
+                                 m["swa_base"], m["swa_pos0"], None, wl.window, m["q_seq"],
+                                 m["q_pos"], _np(lay.sink).astype(np.float64), wl.softmax_scale,
+                                 wl.ratio)
+    assert np.array_equal(full[4], ref[4])
+    for t in range(4):
+        assert np.abs(full[t] - ref[t]).max() > 1e-2, t
 
 
 def test_sparse_attn_f32():

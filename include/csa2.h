@@ -257,6 +257,33 @@ size_t csa2_topk_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, 
                                                      int32_t block_size, int32_t n_blocks);
 
 /*
+ * csa2_topk_and_block_candidates_noalloc — csa2_topk_and_block_candidates
+ * without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The selection lists live in a static device buffer of
+ * csa2_noalloc_scratch_bytes() bytes (16 MiB) that the library holds on every
+ * device it runs on until the process ends.  Arguments, outputs and limits
+ * are those of csa2_topk_and_block_candidates, and so is the result, bit for
+ * bit.  The call allocates nothing; its first call on a device looks the
+ * buffer's address up (no allocation) and keeps it.
+ *   Errors: CSA2_ERR_WORKSPACE when the sizes need more than the buffer
+ *   (csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size,
+ *   n_blocks) > csa2_noalloc_scratch_bytes()); nothing is enqueued then.
+ *   Every call on one device shares that device's buffer: calls that may
+ *   overlap on one device (different streams, different threads without
+ *   ordering) race and must not be issued.  The buffer needs no clearing.
+ */
+int csa2_topk_and_block_candidates_noalloc(const float* scores, int64_t score_stride,
+                                           int32_t n_cols, const float* block_max,
+                                           int64_t block_max_stride, const int32_t* q_pos,
+                                           int32_t ratio, int32_t k, int32_t* idx,
+                                           int32_t block_size, int32_t n_blocks, int32_t* cand,
+                                           int32_t Q, const csa2_pages* pages, void* stream);
+
+/* Size in bytes of the static buffer behind the _noalloc entry point. */
+size_t csa2_noalloc_scratch_bytes(void);
+
+/*
  * csa2_sparse_attn — core sparse attention ([CSA2] "per-layer attention
  * computation"; [3MODES] Q&A on Reuse layers).  For query t at position p of
  * sequence b and head i, the keys are the SWA rows of positions

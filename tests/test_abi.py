@@ -151,6 +151,30 @@ def test_topk_and_block_candidates_rejects():
     assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, None, 0, 0, None, None) == tsl.CSA2_OK
 
 
+def test_topk_and_block_candidates_noalloc_rejects_sizes_past_the_scratch():
+    """The allocation-free variant refuses, before anything is enqueued, any
+    shape whose selection lists exceed its static buffer; its other argument
+    checks are those of the workspace call."""
+    lib = tsl.load()
+    f = lib.csa2_topk_and_block_candidates_noalloc
+    cap = lib.csa2_noalloc_scratch_bytes()
+    assert cap == 16 << 20
+    Q, n = 64, 1 << 20
+    need = lib.csa2_topk_and_block_candidates_workspace_size(Q, n, 512, 8, 2048)
+    assert need > cap
+    assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, Q, None, None) == \
+        tsl.CSA2_ERR_WORKSPACE
+    assert b"static buffer" in lib.csa2_last_error()
+    # shapes that fit still meet the ordinary checks first (null scores, bad block size)
+    assert lib.csa2_topk_and_block_candidates_workspace_size(8, 1 << 17, 512, 8, 2048) <= cap
+    assert f(None, 1 << 17, 1 << 17, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, 8, None, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert f(FAKE, 64, 64, None, 0, FAKE, 1, 8, FAKE, 12, 16, FAKE, 1, None, None) == \
+        tsl.CSA2_ERR_UNSUPPORTED
+    # Q == 0 needs no scratch and enqueues nothing
+    assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, 0, None, None) == tsl.CSA2_OK
+
+
 def test_index_scores_fp4_key_checks():
     """FP4 keys with E4M3 scales: only beside FP8 queries, scales 4-byte aligned
     with a stride of at least 8 bytes."""

@@ -18,7 +18,8 @@ CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1, CSA2_FP4_E2M1_E4M3S16 = 0, 1,
 
 EXPORTED = ("csa2_index_scores", "csa2_block_candidates", "csa2_block_candidates_workspace_size",
             "csa2_topk", "csa2_topk_workspace_size", "csa2_topk_and_block_candidates",
-            "csa2_topk_and_block_candidates_workspace_size", "csa2_sparse_attn",
+            "csa2_topk_and_block_candidates_workspace_size",
+            "csa2_topk_and_block_candidates_noalloc", "csa2_noalloc_scratch_bytes", "csa2_sparse_attn",
             "csa2_sparse_attn_workspace_size", "csa2_cache_write",
             "csa2_status_string", "csa2_last_error", "csa2_version")
 
@@ -79,6 +80,10 @@ def load():
                                                    P, P, SZ, I32, PP, P]
     lib.csa2_topk_and_block_candidates_workspace_size.argtypes = [I32, I32, I32, I32, I32]
     lib.csa2_topk_and_block_candidates_workspace_size.restype = SZ
+    lib.csa2_topk_and_block_candidates_noalloc.argtypes = [P, I64, I32, P, I64, P, I32, I32, P, I32,
+                                                           I32, P, I32, PP, P]
+    lib.csa2_noalloc_scratch_bytes.argtypes = []
+    lib.csa2_noalloc_scratch_bytes.restype = SZ
     lib.csa2_sparse_attn.argtypes = [P, ctypes.c_int, RP, P, P, I32, RP, P, P, P, I32, P, P, I32,
                                      P, ctypes.c_float, P, ctypes.c_int, P, P, SZ, I32, I32, I32,
                                      ctypes.POINTER(csa2_attn_io), P]
@@ -90,7 +95,8 @@ def load():
     lib.csa2_status_string.restype = ctypes.c_char_p
     lib.csa2_last_error.restype = ctypes.c_char_p
     for fn in ("csa2_index_scores", "csa2_block_candidates", "csa2_topk",
-               "csa2_topk_and_block_candidates", "csa2_sparse_attn", "csa2_cache_write",
+               "csa2_topk_and_block_candidates", "csa2_topk_and_block_candidates_noalloc",
+               "csa2_sparse_attn", "csa2_cache_write",
                "csa2_version"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -212,6 +218,21 @@ def csa2_topk(scores, n_cols, q_pos, ratio, k, idx, workspace, Q, cand=None, blo
 def csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size, n_blocks):
     return load().csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size,
                                                                 n_blocks)
+
+
+def csa2_noalloc_scratch_bytes():
+    return load().csa2_noalloc_scratch_bytes()
+
+
+def csa2_topk_and_block_candidates_noalloc(scores, n_cols, q_pos, ratio, k, idx, block_size,
+                                           n_blocks, cand, Q, block_max=None, stream=None,
+                                           pages=None):
+    lib = load()
+    bms = 0 if block_max is None else block_max.stride(0)
+    _check(lib.csa2_topk_and_block_candidates_noalloc(_ptr(scores), scores.stride(0), n_cols,
+                                                      _ptr(block_max), bms, _ptr(q_pos), ratio, k,
+                                                      _ptr(idx), block_size, n_blocks, _ptr(cand), Q,
+                                                      _byref(pages), _stream(stream)))
 
 
 def csa2_topk_and_block_candidates(scores, n_cols, q_pos, ratio, k, idx, block_size, n_blocks,

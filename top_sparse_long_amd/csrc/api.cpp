@@ -323,16 +323,30 @@ size_t csa2_topk_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, 
          csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks);
 }
 
-int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
-                                   const float* block_max, int64_t block_max_stride,
-                                   const int32_t* q_pos, int32_t ratio, int32_t k, int32_t* idx,
-                                   int32_t block_size, int32_t n_blocks, int32_t* cand,
-                                   void* workspace, size_t workspace_bytes, int32_t Q,
-                                   const csa2_pages* pages, void* stream) {
-  g_err[0] = 0;
-  REQUIRE(q_pos, CSA2_ERR_INVALID_ARG, "csa2_topk_and_block_candidates: q_pos is required");
+// Both selections of a Full layer.  With from_scratch the lists go to the
+// library's static scratch buffer instead of a caller workspace: the checks
+// run against a stand-in address (never dereferenced), and the real address
+// is looked up only once every check has passed.
+static int topk_and_blocks(const float* scores, int64_t score_stride, int32_t n_cols,
+                           const float* block_max, int64_t block_max_stride, const int32_t* q_pos,
+                           int32_t ratio, int32_t k, int32_t* idx, int32_t block_size,
+                           int32_t n_blocks, int32_t* cand, void* workspace,
+                           size_t workspace_bytes, int32_t Q, const csa2_pages* pages,
+                           void* stream, bool from_scratch) {
+  const char* fn = from_scratch ? "csa2_topk_and_block_candidates_noalloc"
+                                : "csa2_topk_and_block_candidates";
+  REQUIRE(q_pos, CSA2_ERR_INVALID_ARG, "%s: q_pos is required", fn);
   // the top-k's workspace comes first, the pool's follows at a 16-byte boundary
   const size_t ws_t = align16(csa2_topk_workspace_size(Q, n_cols, k));
+  if (from_scratch) {
+    const size_t need = csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size, n_blocks);
+    REQUIRE(need <= csa2::SELECT_SCRATCH_BYTES, CSA2_ERR_WORKSPACE,
+            "%s: these sizes need %zu bytes of scratch, above the %zu-byte static buffer "
+            "(use csa2_topk_and_block_candidates with a workspace)",
+            fn, need, csa2::SELECT_SCRATCH_BYTES);
+    workspace = (void*)(uintptr_t)256;   // stand-in for the checks only
+    workspace_bytes = need;
+  }
   const size_t ws_b = workspace_bytes > ws_t ? workspace_bytes - ws_t : 0;
   uint8_t* ws = (uint8_t*)workspace;
   csa2::SelectArgs at, ab;
@@ -344,8 +358,41 @@ int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, in
                              ratio, block_size, n_blocks, cand, ws_b ? ws + ws_t : nullptr, ws_b,
                              Q, &ab, &nb);
   if (st != CSA2_OK || Q == 0) return st;
-  return hip_status(csa2::launch_topk_and_blocks(at, n_cols, ab, nb, (hipStream_t)stream),
-                    "csa2_topk_and_block_candidates");
+  if (from_scratch) {
+    void* base = nullptr;
+    if (workspace_bytes > 0) {
+      const hipError_t e = csa2::select_scratch(&base);
+      if (e != hipSuccess) return hip_status(e, "csa2_topk_and_block_candidates_noalloc: scratch lookup");
+    }
+    at.workspace = base;
+    ab.workspace = ws_b ? (uint8_t*)base + ws_t : nullptr;
+  }
+  return hip_status(csa2::launch_topk_and_blocks(at, n_cols, ab, nb, (hipStream_t)stream), fn);
+}
+
+int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,
+                                   const float* block_max, int64_t block_max_stride,
+                                   const int32_t* q_pos, int32_t ratio, int32_t k, int32_t* idx,
+                                   int32_t block_size, int32_t n_blocks, int32_t* cand,
+                                   void* workspace, size_t workspace_bytes, int32_t Q,
+                                   const csa2_pages* pages, void* stream) {
+  g_err[0] = 0;
+  return topk_and_blocks(scores, score_stride, n_cols, block_max, block_max_stride, q_pos, ratio, k,
+                         idx, block_size, n_blocks, cand, workspace, workspace_bytes, Q, pages,
+                         stream, false);
+}
+
+size_t csa2_noalloc_scratch_bytes(void) { return csa2::SELECT_SCRATCH_BYTES; }
+
+int csa2_topk_and_block_candidates_noalloc(const float* scores, int64_t score_stride,
+                                           int32_t n_cols, const float* block_max,
+                                           int64_t block_max_stride, const int32_t* q_pos,
+                                           int32_t ratio, int32_t k, int32_t* idx,
+                                           int32_t block_size, int32_t n_blocks, int32_t* cand,
+                                           int32_t Q, const csa2_pages* pages, void* stream) {
+  g_err[0] = 0;
+  return topk_and_blocks(scores, score_stride, n_cols, block_max, block_max_stride, q_pos, ratio, k,
+                         idx, block_size, n_blocks, cand, nullptr, 0, Q, pages, stream, true);
 }
 
 int csa2_sparse_attn(const void* q, csa2_dtype q_dtype, const csa2_rows* main_kv,

@@ -121,6 +121,11 @@ struct SelectArgs {
 };
 
 hipError_t launch_select(int mode, const SelectArgs& a, int64_t rows_len, hipStream_t s);
+// The allocation-free selection entry point's scratch: a static device array
+// of SELECT_SCRATCH_BYTES per device; select_scratch() gives its address on
+// the current device (looked up once per device).
+constexpr size_t SELECT_SCRATCH_BYTES = (size_t)16 << 20;
+hipError_t select_scratch(void** ptr);
 // Dense top-k and block candidates of the same rows: the first stages of
 // both run in one launch (their workspaces must not overlap).
 hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, const SelectArgs& blocks,

@@ -25,6 +25,8 @@
 // among the row's k best is among its chunk's k best.
 #include "kernels.h"
 
+#include <mutex>
+
 namespace csa2 {
 
 constexpr int SEL_THREADS = 1024;
@@ -488,6 +490,35 @@ SelectPlan plan_select(int Q, int64_t rows_len, int k) {
   }
   p.n_stages = st + 1;
   return p;
+}
+
+// Scratch of the allocation-free entry point: the selection lists live in a
+// file-scope device array instead of a caller workspace.  Host code never
+// passes the array's name to a kernel (on the host it is a stand-in, not a
+// device address): the address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and kept.  Every call on a
+// device shares that device's array; the lists are written before they are
+// read, so nothing needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[SELECT_SCRATCH_BYTES];
+
+hipError_t select_scratch(void** ptr) {
+  constexpr int MAX_DEVICES = 64;
+  static std::mutex mu;
+  static void* addr[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 size_t select_workspace_bytes(int Q, int64_t rows_len, int k) {

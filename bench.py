@@ -51,18 +51,16 @@ def _parse():
     ap.add_argument("--cpu-sample", type=int, default=None,
                     help="queries of the CPU-oracle sample (default: all queries, max 8)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--separate-select", action="store_true",
-                    help="run the Full layer's top-k and block candidates as two calls")
-    ap.add_argument("--overlap-blocks", action="store_true",
-                    help="capture block-candidate selection on a second stream beside the Full "
-                         "layer's top-k and attention (HIP graphs on this ROCm replay the "
-                         "branches one after the other, so this measured no gain)")
     ap.add_argument("--no-serving", action="store_true",
                     help="skip the serving-shaped step (paged caches, slots, inverse RoPE)")
     ap.add_argument("--no-cache-write", action="store_true",
                     help="skip the Full-layer cache-write measurement")
-    ap.add_argument("--stage-reps", type=int, default=10,
-                    help="repetitions per input copy when timing single stages")
+    ap.add_argument("--no-targets", action="store_true",
+                    help="skip the two target workloads (prefill chunk scoring, decoder-group attention)")
+    ap.add_argument("--samples", type=int, default=50,
+                    help="timed samples per stage and protocol (median, p10, p90 reported)")
+    ap.add_argument("--stage-reps", type=int, default=8,
+                    help="rounds over the input copies in one rotated stage sample")
     ap.add_argument("--summarize-profiles", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT_DIR"),
                     help="no GPU: turn rocprofv3 CSV output of this benchmark (a --kernel-trace "
                          "--stats run, a --pmc FETCH_SIZE run and a --pmc WRITE_SIZE run) into the "
@@ -87,33 +85,49 @@ def _source_hash():
     return h.hexdigest()[:16]
 
 
+PREFILL_MIN_Q = 256                      # batches this large share every staged key / row
+INDEX_FLOPS_PER_PAIR = 2 * 32 * 128      # 32 heads x 128 dims, multiply + add
+ATTN_KEYS = 128 + 512                    # SWA window + top-k per query
+ATTN_FLOPS_PER_QUERY = 2 * 64 * ATTN_KEYS * 512 * 2   # S = q K^T and O = P V: 83.9 MFLOP
+
+
 def _stage_work(run, stage):
-    """Algorithmic bytes one launch of a stage moves (HBM-bound stages)."""
+    """(algorithmic bytes, FLOPs, units, bound) of one launch of a stage.
+
+    bound is the roofline that limits the stage at full efficiency: "mfma"
+    for index scoring and attention when the batch shares every staged key
+    (query-tiled prefill: 8,192 FLOP per (query, key) pair, 83.9 MFLOP per
+    attention query), else "hbm" (the bytes the method must move)."""
     wl = run.wl
     nvis = wl.n_vis().clamp(max=run.n_cols)
+    shared = wl.Q >= PREFILL_MIN_Q
     if stage == "index_scores_dense":
         # plus the fused block maxima (4 B per block) when the step emits them
         extra = 4.0 / wl.block_size if run.fuse_block_max and any(run.needs_pool) else 0.0
-        return float(nvis.sum().item()) * (_index_bytes(wl) + extra), int(nvis.sum().item())
+        pairs = int(nvis.sum().item())
+        return (float(pairs) * (_index_bytes(wl) + extra), float(pairs) * INDEX_FLOPS_PER_PAIR, pairs,
+                "mfma" if shared else "hbm")
     if stage == "index_scores_pool":
-        return float(wl.Q * run.pool_cols) * _index_bytes(wl), wl.Q * run.pool_cols
+        pairs = wl.Q * run.pool_cols
+        return float(pairs) * _index_bytes(wl), float(pairs) * INDEX_FLOPS_PER_PAIR, pairs, "hbm"
     if stage == "block_candidates" and run.fuse_block_max:
         nblk = (nvis + wl.block_size - 1) // wl.block_size
-        return float(nblk.sum().item()) * SCORE_BYTES, int(nvis.sum().item())
+        return float(nblk.sum().item()) * SCORE_BYTES, 0.0, int(nvis.sum().item()), "hbm"
     if stage == "topk_and_blocks":
         # the top-k reads every visible score; the pool reads the block
         # maxima when the scoring pass wrote them, else the scores again
         nblk = (nvis + wl.block_size - 1) // wl.block_size
         pool = nblk if run.fuse_block_max else nvis
-        return float((nvis + pool).sum().item()) * SCORE_BYTES, int(nvis.sum().item())
+        return float((nvis + pool).sum().item()) * SCORE_BYTES, 0.0, int(nvis.sum().item()), "hbm"
     if stage in ("topk_dense", "block_candidates"):
-        return float(nvis.sum().item()) * SCORE_BYTES, int(nvis.sum().item())
+        return float(nvis.sum().item()) * SCORE_BYTES, 0.0, int(nvis.sum().item()), "hbm"
     if stage == "topk_pool":
-        return float(wl.Q * run.pool_cols) * SCORE_BYTES, wl.Q * run.pool_cols
+        return float(wl.Q * run.pool_cols) * SCORE_BYTES, 0.0, wl.Q * run.pool_cols, "hbm"
     if stage == "sparse_attn":
         per_q = (ATTN_BYTES_PER_QUERY_S16 if getattr(wl, "main_fmt", "fp4") == "fp4s16"
                  else ATTN_BYTES_PER_QUERY)
-        return float(wl.Q) * per_q, wl.Q
+        return (float(wl.Q) * per_q, float(wl.Q) * ATTN_FLOPS_PER_QUERY, wl.Q,
+                "mfma" if shared else "hbm")
     raise KeyError(stage)
 
 
@@ -273,53 +287,63 @@ def summarize_mfma(mfma_dir, trace_dir, out_dir, workload, command):
         f.write("\n".join(lines) + "\n")
 
 
-def cpu_baseline(wl, n_sample):
-    """Time the oracle on the first n_sample queries of the workload's whole
-    path (both layers), on the host cores."""
+def _host_inputs(wl, sample):
+    """Host copies of what the oracle needs for the sampled queries (not timed)."""
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
-    import oracle
-
-    sample = list(range(min(n_sample, wl.Q)))
     q_seq = wl.q_seq.cpu().numpy()
-    q_pos = wl.q_pos.cpu().numpy()
-    # host copies of the inputs the sample touches (not timed)
     seqs = sorted(set(int(q_seq[t]) for t in sample))
     inputs = {}
     for b in seqs:
         base, n = int(wl.seq_base[b]), int(wl.n_entries[b])
         rows = torch.arange(base, base + n, device=wl.k_idx.device)
-        inputs[b] = (wl.k_idx[rows].cpu().numpy(), wl.k_scale[rows].cpu().numpy(),
-                     wl.main_kv[rows].cpu().numpy())
+        ks = wl.k_scale[rows].cpu().numpy() if wl.k_scale is not None else None
+        inputs[b] = (wl.k_idx[rows].cpu().numpy(), ks, wl.main_kv[rows].cpu().numpy())
     layers = []
     for lay in wl.layers:
         d = {"mode": lay.mode, "q": lay.q[sample].cpu().numpy(), "swa": lay.swa.cpu().numpy(),
              "sink": lay.sink.cpu().numpy().astype(np.float64)}
         if lay.q_idx is not None:
             d["q_idx"] = lay.q_idx[sample].cpu().numpy()
-            d["q_scale"] = lay.q_scale[sample].cpu().numpy()
+            d["q_scale"] = lay.q_scale[sample].cpu().numpy() if lay.q_scale is not None else None
             d["w"] = lay.w[sample].cpu().numpy()
         layers.append(d)
+    return inputs, layers
+
+
+def _oracle_pass(wl, sample, inputs, layers):
+    """The oracle over every layer of the step for the sampled queries; returns
+    (index keys scored, seconds).  Decoding each query's rows is timed too."""
+    import numpy as np
+    import oracle
+    q_seq = wl.q_seq.cpu().numpy()
+    q_pos = wl.q_pos.cpu().numpy()
     swa_base = wl.swa_base.cpu().numpy()
     swa_pos0 = wl.swa_pos0.cpu().numpy()
-
+    quant = wl.quantized
     keys_scored = 0
     t0 = time.perf_counter()
     for j, t in enumerate(sample):
         b = int(q_seq[t])
         kc, ks, mk = inputs[b]
-        k_rows = (oracle.decode_fp4s16_rows(kc, ks) if getattr(wl, "k_fmt", "fp8") == "fp4s16"
-                  else oracle.decode_e4m3_rows(kc, ks))
-        main_rows = (oracle.decode_fp4s16_records(mk) if getattr(wl, "main_fmt", "fp4") == "fp4s16"
-                     else oracle.decode_fp4_records(mk))
+        if not quant:
+            k_rows, main_rows = kc.astype(np.float64), mk.astype(np.float64)
+        else:
+            k_rows = (oracle.decode_fp4s16_rows(kc, ks) if getattr(wl, "k_fmt", "fp8") == "fp4s16"
+                      else oracle.decode_e4m3_rows(kc, ks))
+            main_rows = (oracle.decode_fp4s16_records(mk) if getattr(wl, "main_fmt", "fp4") == "fp4s16"
+                         else oracle.decode_fp4_records(mk))
         pos1, seq0, base0 = np.array([q_pos[t]]), np.array([0]), np.array([0])
         n = int(oracle.visible_count(pos1, wl.ratio)[0])
         cand = idx = None
         for li, lay in enumerate(layers):
             if lay["mode"] in ("full", "reindex"):
-                qv = oracle.decode_e4m3_rows(lay["q_idx"][j:j + 1], lay["q_scale"][j:j + 1])
-                wv = oracle.decode_bf16(lay["w"][j:j + 1])
+                if quant:
+                    qv = oracle.decode_e4m3_rows(lay["q_idx"][j:j + 1], lay["q_scale"][j:j + 1])
+                    wv = oracle.decode_bf16(lay["w"][j:j + 1])
+                else:
+                    qv = lay["q_idx"][j:j + 1].astype(np.float64)
+                    wv = lay["w"][j:j + 1].astype(np.float64)
             if lay["mode"] == "full":
                 sc = oracle.index_scores_dense(qv, wv, k_rows, base0, seq0, pos1, wl.ratio, n)
                 keys_scored += n
@@ -331,16 +355,54 @@ def cpu_baseline(wl, n_sample):
                                               wl.block_size)
                 keys_scored += sc.shape[1]
                 idx = oracle.topk_rows_pool(sc, cand, wl.block_size, wl.topk)
-            swa = oracle.decode_swa_records(lay["swa"])
-            oracle.sparse_attn(oracle.decode_bf16(lay["q"][j:j + 1]), main_rows, base0, idx, swa,
-                               swa_base[b:b + 1], swa_pos0[b:b + 1], None, wl.window, seq0, pos1,
-                               lay["sink"], wl.softmax_scale, wl.ratio)
-    dt = time.perf_counter() - t0
+            swa = oracle.decode_swa_records(lay["swa"]) if quant else lay["swa"].astype(np.float64)
+            qa = oracle.decode_bf16(lay["q"][j:j + 1]) if quant else lay["q"][j:j + 1].astype(np.float64)
+            oracle.sparse_attn(qa, main_rows, base0, idx, swa, swa_base[b:b + 1], swa_pos0[b:b + 1],
+                               None, wl.window, seq0, pos1, lay["sink"], wl.softmax_scale, wl.ratio)
+    return keys_scored, time.perf_counter() - t0
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(wl, n_sample):
+    """Time the oracle on the first n_sample queries of the workload's whole
+    path (both layers), on the host cores with the BLAS threads it gets."""
+    from threadpoolctl import threadpool_info
+    sample = list(range(min(n_sample, wl.Q)))
+    inputs, layers = _host_inputs(wl, sample)
+    keys, dt = _oracle_pass(wl, sample, inputs, layers)
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": keys_scored / dt, "unit": "index keys scored/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": keys / dt, "unit": "index keys scored/s", "cores": int(threads),
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "host_cpus": {"os_cpu_count": os.cpu_count(), "affinity": len(os.sched_getaffinity(0))},
             "sample": f"{len(sample)} of {wl.Q} queries through every layer of the step "
                       f"(float64 NumPy oracle, {dt:.1f} s wall)"}
+
+
+def cpu_single_core(synth):
+    """The oracle on one thread: all 16 queries of the tiny fp32 Full layer
+    (2,048 entries) and two queries of the 128K decode step (both layers)."""
+    from threadpoolctl import threadpool_limits
+    out = {}
+    with threadpool_limits(limits=1):
+        for name, n in (("tiny_full_fp32", 16), ("decode_128k", 2)):
+            wl = synth.make_workload(name, device="cuda")
+            sample = list(range(min(n, wl.Q)))
+            inputs, layers = _host_inputs(wl, sample)
+            keys, dt = _oracle_pass(wl, sample, inputs, layers)
+            out[name] = {"value": keys / dt, "unit": "index keys scored/s", "cores": 1,
+                         "queries_per_s": len(sample) / dt,
+                         "sample": f"{len(sample)} of {wl.Q} queries, {dt:.2f} s wall"}
+            del wl, inputs, layers
+    return {"single_core": out}
 
 
 # Full-layer cache write of the encoder prefill chunk: per entry, two tokens'
@@ -445,6 +507,232 @@ def cache_write_stage(torch, synth, tsl, wl, reps, n_copies, workload):
     return {"prefill_chunk": prefill, "decode_batch": decode}
 
 
+def _pct(xs, q):
+    xs = sorted(xs)
+    i = min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))
+    return xs[i]
+
+
+def _stats(us):
+    return {"median_us": _pct(us, 0.5), "p10_us": _pct(us, 0.1), "p90_us": _pct(us, 0.9),
+            "samples": len(us)}
+
+
+class Timer:
+    """HIP-graph capture and event timing on torch's current stream (the
+    stream the library's kernels are launched on)."""
+
+    def __init__(self, torch, cold_bytes):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        # read before every cold sample, outside the timed region, so the
+        # sample's reads find neither the L2 nor the 256 MB Infinity Cache
+        # warm (a read leaves no dirty lines to write back during the sample)
+        self.flush_buf = torch.ones((cold_bytes // 4,), dtype=torch.float32, device="cuda")
+        # a GPU-side spin before each timed region lets the host enqueue the
+        # region's graph before the GPU reaches its start event
+        self.spin_cycles = 1 << 20
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        torch.cuda._sleep(self.spin_cycles)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3
+        self.spin_cycles = max(1, int(self.spin_cycles * 60.0 / max(us, 1e-3)))   # about 60 us
+
+    def flush(self):
+        self.flush_sink = self.flush_buf.amax()
+
+    def spin(self):
+        self.torch.cuda._sleep(self.spin_cycles)
+
+    def capture(self, fns):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for f in fns:
+                f()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for f in fns:
+                f()
+        return g
+
+    def sample(self, n, body):
+        """n timed samples; body(i) enqueues sample i's untimed prefix and
+        returns what to time: a graph (replayed) or a list of calls (launched
+        directly, which adds no graph dispatch to a region of one or a few
+        launches).  Everything is enqueued back to back and read after one
+        synchronisation.  Returns milliseconds per sample."""
+        torch = self.torch
+        evs = []
+        for i in range(n):
+            work = body(i)
+            self.spin()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+            if isinstance(work, list):
+                for f in work:
+                    f()
+            else:
+                work.replay()
+            e1.record(self.stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) for a, b in evs]
+
+
+def stage_stats(timer, rs, n_samples, reps, protocols=("rotated", "cold", "warm")):
+    """Per stage of one step, launch durations in microseconds:
+
+    rotated  graph replays of every input copy's calls of the stage, `reps`
+             times over (so no launch reads what the launch before it read);
+             each sample is one replay, divided by its launches;
+    cold     one copy's calls after a 1 GiB read that evicts the L2 and the
+             Infinity Cache;
+    warm     one copy's calls right after the same calls ran.
+    The medians of `rotated` are the stage times the roofline uses."""
+    names = []
+    for name, _ in rs[0].steps():
+        if name != "reset" and name not in names:
+            names.append(name)
+    out = {}
+    for name in names:
+        per_copy = [[f for n, f in r.steps() if n == name] for r in rs]
+        calls = len(per_copy[0])
+        rot = timer.capture([f for _ in range(reps) for r in rs for n, f in r.steps() if n == name])
+        rot.replay()
+        for fns in per_copy:
+            for f in fns:
+                f()
+        timer.torch.cuda.synchronize()
+        nbytes, flops, units, bound = _stage_work(rs[0], name)
+        rec = {"calls_per_step": calls, "algorithmic_bytes": nbytes, "flops": flops,
+               "units": units, "bound": bound}
+        if "rotated" in protocols:
+            ms = timer.sample(n_samples, lambda i: rot)
+            rec["rotated"] = _stats([m * 1e3 / (reps * len(rs) * calls) for m in ms])
+        if "cold" in protocols:
+            def cold(i):
+                timer.flush()
+                return per_copy[i % len(rs)]
+            rec["cold"] = _stats([m * 1e3 / calls for m in timer.sample(n_samples, cold)])
+        if "warm" in protocols:
+            def warm(i):
+                fns = per_copy[i % len(rs)]
+                for f in fns:
+                    f()
+                return fns
+            rec["warm"] = _stats([m * 1e3 / calls for m in timer.sample(n_samples, warm)])
+        t = rec["rotated"]["median_us"] * 1e-6
+        rec["avg_us"] = rec["rotated"]["median_us"]
+        rec["hbm_frac"] = nbytes / t / (HBM_PEAK_GBS * 1e9)
+        if flops:
+            rec["mfma_frac_f16"] = flops / t / (F16_PEAK_TFLOPS * 1e12)
+            if name.startswith("index_scores"):
+                rec["mfma_frac_fp8"] = flops / t / (FP8_PEAK_TFLOPS * 1e12)
+        for proto in ("cold", "warm"):
+            if proto in rec:
+                rec[proto]["hbm_frac"] = nbytes / (rec[proto]["median_us"] * 1e-6) / (HBM_PEAK_GBS * 1e9)
+        out[name] = rec
+        del per_copy, rot
+    return out
+
+
+def measure_workload(torch, synth, LayerRunner, timer, name, args, copies, steps, warmup):
+    """Whole-step time and per-stage times of one workload."""
+    runs = [LayerRunner(synth.make_workload(name, device="cuda", seed_offset=1000 * c))
+            for c in range(max(1, copies))]
+    torch.cuda.synchronize()
+    step_graphs = [timer.capture([f for _, f in r.steps()]) for r in runs]
+    for i in range(warmup):
+        step_graphs[i % len(step_graphs)].replay()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(timer.stream)
+    for i in range(steps):
+        step_graphs[i % len(step_graphs)].replay()
+    ev1.record(timer.stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    del step_graphs
+    stages = stage_stats(timer, runs, args.samples, args.stage_reps)
+    run0 = runs[0]
+    wl = run0.wl
+    keys = 0
+    n_attn = 0
+    for lay in wl.layers:
+        if lay.mode == "full":
+            keys += int(wl.n_vis().clamp(max=run0.n_cols).sum().item())
+        elif lay.mode == "reindex":
+            keys += wl.Q * run0.pool_cols
+        n_attn += wl.Q
+    return {"runs": runs, "ms_per_step": (t1 - t0) * 1e3 / steps,
+            "gpu_ms_per_step": ev0.elapsed_time(ev1) / steps, "stages": stages,
+            "index_keys_per_step": keys, "attn_queries_per_step": n_attn}
+
+
+def _roofline(stage, rec, workload):
+    """The roofline record of one stage from its rotated median."""
+    t = rec["avg_us"] * 1e-6
+    if rec["bound"] == "mfma":
+        achieved = rec["flops"] / t / 1e12
+        peak = FP8_PEAK_TFLOPS if stage.startswith("index_scores") else F16_PEAK_TFLOPS
+        r = {"bound": "mfma", "kernel": stage, "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+             "frac": achieved / peak}
+        if stage.startswith("index_scores"):
+            r["frac_of_f16_peak"] = achieved / F16_PEAK_TFLOPS
+        r["traffic"] = _traffic(stage, workload, rec["algorithmic_bytes"])
+        return r
+    achieved = rec["algorithmic_bytes"] / t / 1e9
+    return {"bound": "hbm", "kernel": stage, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": _traffic(stage, workload, rec["algorithmic_bytes"])}
+
+
+def targets(torch, synth, LayerRunner, timer, args):
+    """The two stated targets, each on its own workload: prefill index
+    scoring at >= 0.5 of the FP8 MFMA peak (the 4,096-query m = 2 chunk) and
+    decode sparse attention at >= 0.6 of HBM (the batch-64, 262,144-entry
+    decoder group, per layer)."""
+    out = {}
+    for name in ("prefill_m2_chunk", "decoder_group_256k"):
+        m = measure_workload(torch, synth, LayerRunner, timer, name, args, args.copies,
+                             max(3, args.steps // 4), max(1, args.warmup // 2))
+        st = m["stages"]
+        rec = {"ms_per_step": m["gpu_ms_per_step"],
+               "stages": {k: {kk: vv for kk, vv in v.items()} for k, v in st.items()}}
+        if name == "prefill_m2_chunk":
+            sc = st["index_scores_dense"]
+            rec["target"] = {"stage": "index_scores_dense", "what": "MFMA FLOP rate against the FP8 peak",
+                             "frac": sc["mfma_frac_fp8"], "frac_of_f16_peak": sc["mfma_frac_f16"],
+                             "goal": 0.5, "met": sc["mfma_frac_fp8"] >= 0.5,
+                             "pairs_per_s": sc["units"] / (sc["avg_us"] * 1e-6)}
+            rec["roofline_scores"] = _roofline("index_scores_dense", sc, name)
+            rec["roofline_attention"] = _roofline("sparse_attn", st["sparse_attn"], name)
+        else:
+            at = st["sparse_attn"]
+            rec["target"] = {"stage": "sparse_attn", "what": "algorithmic bytes per layer call against HBM",
+                             "frac": at["hbm_frac"], "frac_cold": at["cold"]["hbm_frac"],
+                             "frac_warm": at["warm"]["hbm_frac"], "goal": 0.6,
+                             "met": at["hbm_frac"] >= 0.6,
+                             "us_per_layer": at["avg_us"],
+                             "queries_per_s": at["units"] / (at["avg_us"] * 1e-6)}
+            rec["roofline_attention"] = _roofline("sparse_attn", at, name)
+            rec["roofline_scores"] = _roofline("index_scores_dense", st["index_scores_dense"], name)
+        out[name] = rec
+        del m
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = _parse()
     if args.summarize_profiles:
@@ -464,9 +752,7 @@ def main():
 
     tsl.load()
     dev = "cuda"
-    runs = [LayerRunner(synth.make_workload(args.workload, device=dev, seed_offset=1000 * c))
-            for c in range(max(1, args.copies))]
-    torch.cuda.synchronize()
+    timer = Timer(torch, 1 << 30)
 
     # calibration copy for the counter runs (outside the timed region): a
     # plain 256 MiB device copy whose FETCH/WRITE bytes are known
@@ -476,100 +762,20 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
-    def capture(fns):
-        """Capture the calls into a HIP graph (launched on torch's current
-        stream at replay)."""
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for f in fns:
-                f()
-        torch.cuda.current_stream().wait_stream(side)
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for f in fns:
-                f()
-        return g
-
-    step_graphs = [capture([f for _, f in r.steps(concurrent=args.overlap_blocks,
-                                                        separate_select=args.separate_select)]) for r in runs]
-    for i in range(args.warmup):
-        step_graphs[i % len(step_graphs)].replay()
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step_graphs[i % len(step_graphs)].replay()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    gpu_ms_per_step = ev0.elapsed_time(ev1) / args.steps
-
-    # per-stage launch durations: each stage's calls, rotated over the input
-    # copies and repeated, captured in one graph and timed with HIP events on
-    # the stream the kernels run on
-    reps = max(2, args.stage_reps)
-    sel = dict(separate_select=args.separate_select)
-
-    def stage_times(rs):
-        out = {}
-        names = []
-        for name, _ in rs[0].steps(**sel):
-            if name != "reset" and name not in names:
-                names.append(name)
-        for name in names:
-            fns = []
-            for _ in range(reps):
-                for r in rs:
-                    fns += [f for n, f in r.steps(**sel) if n == name]
-            g = capture(fns)
-            g.replay()
-            torch.cuda.synchronize()
-            # the median of several timed replays, so one slow replay (a
-            # clock ramp, say) does not become the stage's time
-            times = []
-            for _ in range(STAGE_TIMED_REPLAYS):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                g.replay()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                times.append(e0.elapsed_time(e1))
-            avg_ms = sorted(times)[len(times) // 2] / len(fns)
-            per_step = sum(1 for n, _ in rs[0].steps(**sel) if n == name)
-            nbytes, units = _stage_work(rs[0], name)
-            out[name] = {"avg_us": avg_ms * 1e3, "calls_per_step": per_step,
-                         "algorithmic_bytes": nbytes, "units": units,
-                         "hbm_frac": nbytes / (avg_ms * 1e-3) / (HBM_PEAK_GBS * 1e9)}
-            del g
-        return out
-
-    run0 = runs[0]
-    stages = stage_times(runs)
+    m = measure_workload(torch, synth, LayerRunner, timer, args.workload, args, args.copies,
+                         args.steps, args.warmup)
+    runs = m["runs"]
+    stages = m["stages"]
+    ms_per_step = m["ms_per_step"]
+    gpu_ms_per_step = m["gpu_ms_per_step"]
     dom = max(stages, key=lambda s: stages[s]["avg_us"] * stages[s]["calls_per_step"])
-    d = stages[dom]
-    achieved = d["algorithmic_bytes"] / (d["avg_us"] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                "traffic": _traffic(dom, args.workload, d["algorithmic_bytes"])}
-
-    wl = run0.wl
-    keys = 0
-    n_attn = 0
-    for lay in wl.layers:
-        if lay.mode == "full":
-            keys += int(wl.n_vis().clamp(max=run0.n_cols).sum().item())
-        elif lay.mode == "reindex":
-            keys += wl.Q * run0.pool_cols
-        n_attn += wl.Q
-    value = keys / (ms_per_step * 1e-3)
+    roofline = _roofline(dom, stages[dom], args.workload)
+    roofline["achieved_from"] = ("median of per-launch times over graph replays rotated across "
+                                 "the input copies, HIP events on the launch stream")
+    wl = runs[0].wl
+    value = m["index_keys_per_step"] / (ms_per_step * 1e-3)
+    attn = stages.get("sparse_attn")
+    attn_qps = attn["units"] / (attn["avg_us"] * 1e-6) if attn else None
 
     # the same step with serving-shaped I/O: index keys and main-KV records in
     # 64-slot pages of a random page order (index-key pages of 64 keys, then
@@ -579,35 +785,42 @@ def main():
     if not args.no_serving and wl.quantized:
         pruns = [LayerRunner(r.wl, paged=synth.paged_layout(r.wl, 900 + c))
                  for c, r in enumerate(runs)]
-        pgraphs = [capture([f for _, f in r.steps(separate_select=args.separate_select)])
-                   for r in pruns]
+        pgraphs = [timer.capture([f for _, f in r.steps()]) for r in pruns]
         for i in range(args.warmup):
             pgraphs[i % len(pgraphs)].replay()
         torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
+        e0.record(timer.stream)
         for i in range(args.steps):
             pgraphs[i % len(pgraphs)].replay()
-        e1.record(stream)
+        e1.record(timer.stream)
         torch.cuda.synchronize()
         sms = e0.elapsed_time(e1) / args.steps
         del pgraphs
+        pst = stage_stats(timer, pruns, args.samples, args.stage_reps, protocols=("rotated",))
         serving = {"io": "64-slot pages in random order; index-key pages of 64 keys then 64 "
                          "scales; top-k written as slots; attention by slot with inverse RoPE",
-                   "gpu_ms_per_step": sms, "value": keys / (sms * 1e-3),
+                   "gpu_ms_per_step": sms, "value": m["index_keys_per_step"] / (sms * 1e-3),
                    "unit": "index keys scored/s",
-                   "stages_us": {k: v["avg_us"] for k, v in stage_times(pruns).items()}}
+                   "stages_us": {k: v["avg_us"] for k, v in pst.items()}}
         del pruns
 
     cache_write = None
     if not args.no_cache_write:
-        cache_write = cache_write_stage(torch, synth, tsl, wl, reps, len(runs), args.workload)
+        cache_write = cache_write_stage(torch, synth, tsl, wl, args.stage_reps, len(runs), args.workload)
+
+    del runs, m
+    torch.cuda.empty_cache()
+    tgt = None
+    if not args.no_targets:
+        tgt = targets(torch, synth, LayerRunner, timer, args)
 
     cpu = None
     if not args.no_cpu_baseline:
         n_sample = args.cpu_sample if args.cpu_sample is not None else min(8, wl.Q)
         cpu = cpu_baseline(wl, n_sample)
+        cpu.update(cpu_single_core(synth))
 
     out = {
         "metric": METRIC, "value": value, "unit": "index keys scored/s", "n_gpus": 1,
@@ -622,13 +835,12 @@ def main():
                                       else "e4m3+f32/row"),
                    "main_kv_record": ("288 B e2m1+e4m3/16" if getattr(wl, "main_fmt", "fp4") == "fp4s16"
                                       else "320 B e2m1+f32/32"),
-                   "input_copies": len(runs), "block_candidates_overlapped": bool(args.overlap_blocks),
-                   "full_layer_selections": ("separate" if args.separate_select or args.overlap_blocks
-                                             else "shared launch")},
-        "sparse_attn_queries_per_s": n_attn / (ms_per_step * 1e-3),
+                   "input_copies": args.copies, "full_layer_selections": "shared launch"},
+        "sparse_attn_queries_per_s": attn_qps,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "stages": stages,
+        "targets": tgt,
         "serving_io": serving,
         "cache_write": cache_write,
         "source_sha1": _source_hash(),

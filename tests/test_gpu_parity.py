@@ -551,6 +551,64 @@ def test_sparse_attn_bounded_replay_window(quantized, main_fmt, split):
         assert np.abs(full[t] - ref[t]).max() > 1e-2, t
 
 
+WIDE_MIN_Q = 256     # 64-head batches of at least this many queries run one workgroup per query
+
+
+@pytest.mark.parametrize("case", ["fp4_rope_holes", "fp4s16_m2_ragged", "fp4_bounded_window"])
+def test_sparse_attn_wide_batch(case):
+    """Batches of at least 256 queries with 64 heads run the wide form (all
+    heads of a query in one workgroup, rounds of 128 keys, P V from the raw
+    codes through transposing LDS reads).  Three hundred queries over ragged
+    caches: holes, duplicates and indices past the visible count; the inverse
+    RoPE of the output; the pages' 288-byte records at m = 2 with a top-k
+    count and window that leave partial tiles and rounds; and the
+    bounded-replay window (CSA2 page, CED section)."""
+    _announce(f"sparse_attn wide batch {case}")
+    ratio = 2 if case == "fp4s16_m2_ragged" else 1
+    main_fmt = "fp4s16" if case == "fp4s16_m2_ragged" else "fp4"
+    topk = 77 if case == "fp4s16_m2_ragged" else 512
+    wl = synth.mini_workload(47, [3000, 1700, 900], q_per_seq=100, ratio=ratio, main_fmt=main_fmt,
+                             topk=topk).to(DEV)
+    assert wl.Q >= WIDE_MIN_Q
+    window = 50 if case == "fp4s16_m2_ragged" else wl.window
+    rope = synth.rope_table(3000 * ratio, DEV) if case == "fp4_rope_holes" else None
+    run = LayerRunner(wl, rope_cs=rope)
+    rng = np.random.default_rng(48)
+    idx = _random_idx(rng, _np(wl.n_vis()), topk, 0.95)
+    if case == "fp4_rope_holes":
+        idx[0, 5] = -1
+        idx[1, :130] = np.arange(870, 1000)       # duplicates of window positions
+        idx[2, 10:20] = 10 ** 6                   # past the visible count
+        idx[3, :] = -1                            # only the window
+    q_pos = _np(wl.q_pos).astype(np.int64)
+    pos0 = _np(wl.swa_pos0).astype(np.int64)
+    base = _np(wl.swa_base).astype(np.int64)
+    lo = None
+    if case == "fp4_bounded_window":
+        q_seq = _np(wl.q_seq)
+        lo = np.zeros(wl.B, dtype=np.int64)
+        lo[0] = q_pos[q_seq == 0].max() - 60      # inside the window of the sequence's last query
+        lo[1] = q_pos[q_seq == 1].max() + 1       # past every query of the sequence: no SWA key
+    lo_t = None if lo is None else torch.from_numpy(lo.astype(np.int32)).to(DEV)
+    idx_t = torch.from_numpy(idx.astype(np.int32)).to(DEV)
+    lay = wl.layers[0]
+    tsl.csa2_sparse_attn(lay.q, tsl.CSA2_BF16, run.slots.compress_kv, wl.seq_base, idx_t, topk,
+                         run.layer_rows[0]["swa"], wl.swa_base, wl.swa_pos0, lo_t, window, wl.q_seq,
+                         wl.q_pos, wl.ratio, lay.sink, wl.softmax_scale, run.out[0], tsl.CSA2_BF16,
+                         run.lse[0], wl.Q, workspace=run.ws_attn, rope_cs=rope)
+    torch.cuda.synchronize()
+    m = oracle_io.meta(wl)
+    ref, ref_lse = oracle.sparse_attn(oracle_io.attn_q(lay, True), oracle_io.main_rows(wl),
+                                      m["seq_base"], idx, oracle_io.swa_rows(lay, True), base, pos0,
+                                      lo, window, m["q_seq"], m["q_pos"],
+                                      _np(lay.sink).astype(np.float64), wl.softmax_scale, wl.ratio)
+    if rope is not None:
+        r = _np(rope).astype(np.float64)
+        ref = oracle.unturn_heads(ref, m["q_pos"], r[:, :32], r[:, 32:])
+    check_attention(_np(run.out[0].float()), ref)
+    assert np.abs(_np(run.lse[0]) - ref_lse).max() <= 1e-3
+
+
 def test_sparse_attn_f32():
     _announce("sparse_attn f32")
     wl = synth.mini_workload(33, [2048], q_per_seq=4, quantized=False).to(DEV)

@@ -29,6 +29,8 @@
 // so operands carry 11 significant bits; accumulation is fp32.
 #include "kernels.h"
 
+#include <type_traits>
+
 namespace csa2 {
 
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -115,6 +117,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
 // registers, one wave per SIMD: 26.3 us per 64-query group call against
 // 21.9 us here, and 1.41 ms against 1.18 ms on the 4,096-query chunk.)
 constexpr int AW_WAVES = 8;
+constexpr int V3_RS = 528;                                     // LDS row stride of raw key bytes
+constexpr int V3_SG = 32;                                      // scale groups staged per key (max)
+constexpr int V3_QS = AT_D * 2 + 16;                           // LDS row stride of staged f16 q (bytes)
+// LDS byte offset of raw key row `row` of a round: every 16-row block is
+// shifted by 8 bytes, so the transposing reads of two 16-lane groups (two
+// different 16-row blocks at the same column) use disjoint banks.
+__device__ __forceinline__ int v3_row(int row) { return row * V3_RS + (row >> 4) * 8; }
+typedef int v2i_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 constexpr int AW_TILE_BYTES = 16 * AT_RS;     // one wave's 16-key tile
 static_assert(AW_WAVES * AW_TILE_BYTES >= AW_WAVES * 16 * 64 * 16, "half of every wave's O must fit the tiles");
 
@@ -503,6 +514,516 @@ __global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_kernel(AttnAr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide form for 64 heads: one workgroup = one query (x one key split), all
+// 64 heads, eight waves (two per SIMD).  Heads are the M dimension of every
+// product, so each gathered key row is dequantized once per query instead of
+// once per 16-head group.  Keys go in rounds of 128 (SWA rounds first, then
+// main rounds; a round holds keys of one format):
+//
+//   A  wave w takes keys 16 w .. 16 w + 15 of the round (raw bytes requested
+//      into registers during the previous round's phase C): dequantized in
+//      registers, they are the K operand of S^T = K Q^T for the four 16-head
+//      blocks (q of all heads is staged once in LDS as f16).  The tile's
+//      per-head maxima go to LDS;
+//   B  after a barrier every wave forms the same running maxima (raised only
+//      when a tile exceeds them by more than 8, so P < 2^8 in f16), writes
+//      its tile's P, its keys' scales (f16, zero for keys that do not exist)
+//      and its raw bytes to the round's LDS tile;
+//   C  after a second barrier wave w owns columns 64 w .. 64 w + 63 for all
+//      64 heads: one transposing read of the raw tile (ds_read_b64_tr_b4: 16
+//      keys of one column per lane; ds_read_b64_tr_b8: 8 keys) widens
+//      exactly to f16, is multiplied by the keys' scales, and feeds the P V
+//      products of all four head blocks.
+// The LDS tile is written in B and read in C, so one copy suffices: a wave
+// writing round r + 1's tile has passed round r + 1's first barrier, which
+// every wave reaches only after its phase C of round r.
+constexpr int WD_WAVES = 8;
+constexpr int WD_ROUND = 16 * WD_WAVES;                        // keys per round
+constexpr int WD_RBUF = WD_ROUND * V3_RS + (WD_ROUND / 16) * 8;
+constexpr int WD_PS = 2 * WD_ROUND + 16;                       // LDS row stride of P (bytes)
+constexpr int WD_H = 64;
+// batches of at least this many 64-head queries use the wide form (one
+// workgroup per query fills the chip); smaller ones the 16-head groups
+constexpr int WD_MIN_Q = 256;
+
+template <bool S16, bool TURN>
+__global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_wide_kernel(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_q[WD_H * V3_QS];
+  __shared__ __attribute__((aligned(16))) uint8_t s_raw[WD_RBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t s_p[WD_H * WD_PS];
+  __shared__ __attribute__((aligned(16))) _Float16 s_scl[V3_SG][WD_ROUND];
+  __shared__ float s_m[WD_WAVES][WD_H];
+
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  // the workgroups of a query on one XCD (handed out round-robin)
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  const int split = bid % a.n_split;
+  const int t = bid / a.n_split;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15;
+  const int g = lane >> 4;
+
+  const int b = a.q_seq[t];
+  const int p = a.q_pos[t];
+  const int64_t lim = a.idx_slots ? a.n_main_rows : ((int64_t)p + 1) / a.ratio;
+  const int64_t mbase = a.idx_slots ? 0 : a.main_base[b];
+  const int lo = a.swa_lo ? a.swa_lo[b] : 0;
+  const int sp0 = a.swa_pos0[b];
+  const int first = max(max(lo, sp0), max(0, p - a.window + 1));
+  const int n_swa = max(0, p - first + 1);
+  const int64_t sbase = a.swa_base[b] + (first - sp0);
+  const int n_swa_rounds = (n_swa + WD_ROUND - 1) / WD_ROUND;
+  const int n_rounds = n_swa_rounds + (a.k + WD_ROUND - 1) / WD_ROUND;
+  // this workgroup's rounds: [rb, re), the rounds dealt out evenly
+  const int rb = (int)((int64_t)split * n_rounds / a.n_split);
+  const int re = (int)((int64_t)(split + 1) * n_rounds / a.n_split);
+  const int32_t* irow = a.idx + (int64_t)t * a.k;
+  // keys that do not exist are read from this query's own q row (always
+  // mapped, 64 KB) and get a zero scale and probability
+  const uint8_t* dummy = (const uint8_t*)a.q + (int64_t)t * WD_H * AT_D * 2;
+
+  struct Raw {
+    v4u d[8];
+    float4 s;
+    bool ok;
+  };
+  // the main-KV position of lane (r, g)'s key in round rd (requested a round
+  // ahead, so the row loads never wait on it)
+  auto key_pos = [&](int rd) -> int {
+    const int slot = (rd - n_swa_rounds) * WD_ROUND + 16 * wave + r;
+    return (rd >= n_swa_rounds && slot < a.k) ? irow[slot] : -1;
+  };
+  // lane (r, g): key r of the wave's 16, dims [128 g, +128); pos from key_pos
+  auto load_tile = [&](int rd, int pos, Raw& R) {
+    if (rd < n_swa_rounds) {
+      const int slot = rd * WD_ROUND + 16 * wave + r;
+      const int64_t row = sbase + min(slot, max(n_swa - 1, 0));   // past the window: the last row again
+      const uint8_t* src = a.swa + row * a.swa_stride + 128 * g;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) R.d[j] = *(const v4u*)(src + 16 * j);
+      R.s = make_float4(a.swa_scale[row * a.swa_scale_stride + g], 0.f, 0.f, 0.f);
+      R.ok = slot < n_swa;
+    } else {
+      const bool v = pos >= 0 && pos < lim;
+      const uint8_t* src = v ? a.main + (mbase + pos) * a.main_stride : dummy;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) R.d[j] = *(const v4u*)(src + 64 * g + 16 * j);
+      if (S16) {
+        const uint8_t* ssrc = v ? (const uint8_t*)a.main_scale + (mbase + pos) * a.main_scale_stride : dummy;
+        const uint2 sb = *(const uint2*)(ssrc + 8 * g);
+        R.s = make_float4(__uint_as_float(sb.x), __uint_as_float(sb.y), 0.f, 0.f);
+      } else {
+        const float* ssrc = v ? a.main_scale + (mbase + pos) * a.main_scale_stride : (const float*)dummy;
+        R.s = *(const float4*)(ssrc + 4 * g);
+      }
+      R.ok = v;
+    }
+  };
+
+  // ---- prologue
+  Raw R;
+  if (rb < re) load_tile(rb, key_pos(rb), R);
+  {
+    // q of all heads to LDS as f16: thread i converts 64 consecutive dims
+    const int qh = threadIdx.x >> 3, qd = (threadIdx.x & 7) * 64;
+    const uint16_t* qrow = (const uint16_t*)a.q + ((int64_t)t * WD_H + qh) * AT_D + qd;
+    v4u qraw[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qraw[c] = *(const v4u*)(qrow + 8 * c);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      v8h h;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h[2 * e] = (_Float16)__uint_as_float(qraw[c][e] << 16);
+        h[2 * e + 1] = (_Float16)__uint_as_float(qraw[c][e] & 0xFFFF0000u);
+      }
+      *(v8h*)(s_q + qh * V3_QS + 2 * qd + 16 * c) = h;
+    }
+  }
+  float sink2[4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) sink2[hb] = a.sink[16 * hb + r] * LOG2E;
+  __syncthreads();   // s_q
+
+  // O[hb][cb]: heads 16 hb + 4 g + j, column 64 wave + 16 cb + r
+  v4f O[4][4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) O[hb][cb] = (v4f){0.f, 0.f, 0.f, 0.f};
+  float m_s[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};   // head 16 hb + r, log2 units
+  float l_part[4] = {0.f, 0.f, 0.f, 0.f};   // head 16 hb + r over this wave's keys
+  const float zscale = a.scale * LOG2E;
+  const int c0 = 64 * wave;
+  const uint8_t* qsrc = s_q + r * V3_QS + 256 * g;
+
+  // one round; SWA and main rounds are compiled apart so neither path keeps
+  // the other's registers alive
+  auto round = [&](auto swa_tag, int rd) {
+    constexpr bool swa_round = decltype(swa_tag)::value;
+    const int pos_next = (rd + 1 < re) ? key_pos(rd + 1) : -1;
+    // ---- phase A: S^T of the wave's 16 keys for all 64 heads
+    v4f acc[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) acc[hb] = (v4f){0.f, 0.f, 0.f, 0.f};
+    if constexpr (swa_round) {
+      const float sc = R.s.x;
+      const _Float16 mh = scale_mantissa(sc);
+      const v2h m2 = {mh, mh};
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        uint32_t kd[4];
+        dequant_fp8x4(R.d[c >> 1][(c & 1) * 2], sc, m2, &kd[0]);
+        dequant_fp8x4(R.d[c >> 1][(c & 1) * 2 + 1], sc, m2, &kd[2]);
+        const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          const v8h qv = *(const v8h*)(qsrc + 16 * hb * V3_QS + 16 * c);
+          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qv, acc[hb], 0, 0, 0);
+        }
+      }
+    } else {
+      const float s4[4] = {R.s.x, R.s.y, R.s.z, R.s.w};
+      _Float16 s8[8];
+      if (S16) {
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const v2h lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__float_as_uint(s4[w]), 1.0f, false);
+          const v2h hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(__float_as_uint(s4[w]), 1.0f, true);
+          s8[4 * w] = lo2[0];
+          s8[4 * w + 1] = lo2[1];
+          s8[4 * w + 2] = hi2[0];
+          s8[4 * w + 3] = hi2[1];
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        uint32_t kd[4];
+        if (S16) {
+          dequant_fp4x8_h(R.d[c >> 2][c & 3], s8[c >> 1], kd);
+        } else {
+          const _Float16 mh = scale_mantissa(s4[c >> 2]);
+          dequant_fp4x8(R.d[c >> 2][c & 3], s4[c >> 2], (v2h){mh, mh}, kd);
+        }
+        const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+          const v8h qv = *(const v8h*)(qsrc + 16 * hb * V3_QS + 16 * c);
+          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qv, acc[hb], 0, 0, 0);
+        }
+      }
+    }
+    // lane (r, g) of S^T holds keys 4 g + i of the tile for head 16 hb + r
+    const uint64_t vmask = __ballot(R.ok);
+    float z[4][4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[hb][i] = ((vmask >> (4 * g + i)) & 1ull) ? acc[hb][i] * zscale : -INFINITY;
+      float mt = fmaxf(fmaxf(z[hb][0], z[hb][1]), fmaxf(z[hb][2], z[hb][3]));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      if (g == 0) s_m[wave][4 * r + hb] = mt;
+    }
+    __syncthreads();
+
+    // ---- phase B: running maxima (raised lazily, the same in every wave),
+    // P, scales, raw bytes
+    {
+      bool raise = false;
+      float alpha[4];
+      // the maxima are stored [wave][r][head block]: one 16-byte read per wave
+      v4f mx4 = *(const v4f*)(&s_m[0][4 * r]);
+#pragma unroll
+      for (int w = 1; w < WD_WAVES; ++w) {
+        const v4f x = *(const v4f*)(&s_m[w][4 * r]);
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) mx4[hb] = fmaxf(mx4[hb], x[hb]);
+      }
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        const float mx = mx4[hb];
+        const bool up = mx > m_s[hb] + RESCALE_SLACK || (m_s[hb] == -INFINITY && mx > -INFINITY);
+        const float m_new = up ? mx : m_s[hb];
+        alpha[hb] = (m_new == -INFINITY || !up) ? 1.f : __builtin_amdgcn_exp2f(m_s[hb] - m_new);
+        raise |= up;
+        m_s[hb] = m_new;
+        // z - m_new <= 8 here, and -inf gives 0
+        float pv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(z[hb][i] - m_new);
+        l_part[hb] = l_part[hb] * alpha[hb] + ((pv[0] + pv[1]) + (pv[2] + pv[3]));
+        const v4h P4 = {(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
+        *(v4h*)(s_p + (16 * hb + r) * WD_PS + 2 * (16 * wave + 4 * g)) = P4;
+      }
+      const float4 cs4 = R.ok ? R.s : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int key = 16 * wave + r;
+      uint8_t* dst = s_raw + v3_row(key);
+      if constexpr (swa_round) {
+        s_scl[g][key] = (_Float16)cs4.x;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) *(v4u*)(dst + 128 * g + 16 * j) = R.d[j];
+      } else {
+        if (S16) {
+          const uint32_t w0 = __float_as_uint(cs4.x), w1 = __float_as_uint(cs4.y);
+          const v2h a0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+          const v2h a1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+          const v2h a2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+          const v2h a3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+          s_scl[8 * g + 0][key] = a0[0];
+          s_scl[8 * g + 1][key] = a0[1];
+          s_scl[8 * g + 2][key] = a1[0];
+          s_scl[8 * g + 3][key] = a1[1];
+          s_scl[8 * g + 4][key] = a2[0];
+          s_scl[8 * g + 5][key] = a2[1];
+          s_scl[8 * g + 6][key] = a3[0];
+          s_scl[8 * g + 7][key] = a3[1];
+        } else {
+          s_scl[4 * g + 0][key] = (_Float16)cs4.x;
+          s_scl[4 * g + 1][key] = (_Float16)cs4.y;
+          s_scl[4 * g + 2][key] = (_Float16)cs4.z;
+          s_scl[4 * g + 3][key] = (_Float16)cs4.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *(v4u*)(dst + 64 * g + 16 * j) = R.d[j];
+      }
+      // every wave takes the same decision (same maxima, same rule)
+      if (__any(raise)) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float aj = __shfl(alpha[hb], 4 * g + j);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) O[hb][cb][j] *= aj;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // the next round's rows (this round's bytes are in LDS now)
+    if (rd + 1 < re) load_tile(rd + 1, pos_next, R);
+
+    // ---- phase C: O[64 x 64] += P (V * scale) over the round's keys
+    {
+      const lds_u8* rawl = (const lds_u8*)s_raw;
+      if constexpr (swa_round) {
+        // 32-key blocks: lane group g holds keys 32 kb + 8 g .. + 7; the
+        // wave's 64 columns lie in one 128-dim scale group.  The four column
+        // blocks' V operands are widened first, then P streams by head block.
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int k0 = 32 * kb + 8 * g;
+          const v8h S8 = *(const v8h*)(&s_scl[wave >> 1][k0]);
+          const int rrow = v3_row(k0 + (r >> 1));
+          v8h B[4];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const v2i_t tv = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (__attribute__((address_space(3))) v2i_t*)(rawl + rrow + c0 + 16 * cb + 8 * (r & 1)));
+            const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)tv[0], 1.0f, false);
+            const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)tv[0], 1.0f, true);
+            const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)tv[1], 1.0f, false);
+            const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)tv[1], 1.0f, true);
+            B[cb] = (v8h){h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]} * S8;
+          }
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) {
+            const v8h P = *(const v8h*)(s_p + (16 * hb + r) * WD_PS + 2 * k0);
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) O[hb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, B[cb], O[hb][cb], 0, 0, 0);
+          }
+        }
+      } else {
+        // halves of 64 keys: lane group g holds tile 4 half + g (16 keys);
+        // one transposing read gives those 16 keys of one column (keys 0..7
+        // and 8..15 feed two products).  V operands first, then P by head block.
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kt = 16 * (4 * half + g);
+          const int rrow = v3_row(kt + r);
+          v8h B1[4], B2[4];
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            // scale group of columns c0 + 16 cb .. + 15
+            const int grp = S16 ? (4 * wave + cb) : (2 * wave + (cb >> 1));
+            const v8h S1 = *(const v8h*)(&s_scl[grp][kt]);
+            const v8h S2 = *(const v8h*)(&s_scl[grp][kt + 8]);
+            const v2i_t tv = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+                (__attribute__((address_space(3))) v2i_t*)(rawl + rrow + (c0 + 16 * cb) / 2));
+            uint32_t b1[4], b2[4];
+            b1[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[0], 1.0f, 0));
+            b1[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[0], 1.0f, 1));
+            b1[2] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[0], 1.0f, 2));
+            b1[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[0], 1.0f, 3));
+            b2[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[1], 1.0f, 0));
+            b2[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[1], 1.0f, 1));
+            b2[2] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[1], 1.0f, 2));
+            b2[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[1], 1.0f, 3));
+            const v4u u1 = {b1[0], b1[1], b1[2], b1[3]}, u2 = {b2[0], b2[1], b2[2], b2[3]};
+            B1[cb] = __builtin_bit_cast(v8h, u1) * S1;
+            B2[cb] = __builtin_bit_cast(v8h, u2) * S2;
+          }
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) {
+            const v8h P1 = *(const v8h*)(s_p + (16 * hb + r) * WD_PS + 2 * kt);
+            const v8h P2 = *(const v8h*)(s_p + (16 * hb + r) * WD_PS + 2 * (kt + 8));
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+              O[hb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P1, B1[cb], O[hb][cb], 0, 0, 0);
+              O[hb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P2, B2[cb], O[hb][cb], 0, 0, 0);
+            }
+          }
+        }
+      }
+    }
+  };
+  int rd = rb;
+  for (; rd < min(re, n_swa_rounds); ++rd) round(std::true_type{}, rd);
+  for (; rd < re; ++rd) round(std::false_type{}, rd);
+
+  // ---- epilogue: denominators, sink, output (or partial records)
+  __syncthreads();   // every wave is past its last read of s_m, s_raw and s_p
+  // per head: the running maximum and this wave's denominator share, then
+  // the row factors of O (heads 16 hb + 4 g + j) from LDS
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    float l = l_part[hb];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (g == 0) s_m[wave][16 * hb + r] = l;
+  }
+  float* s_mx = (float*)s_p;   // [64] running maxima, [64] sink logits (log2 units)
+  if (wave == 0 && g == 0) {
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      s_mx[16 * hb + r] = m_s[hb];
+      s_mx[64 + 16 * hb + r] = sink2[hb];
+    }
+  }
+  __syncthreads();
+  float Lh[4][4], Mh[4][4], Sk[4][4];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const v4f mv = *(const v4f*)(s_mx + 16 * hb + 4 * g);
+    const v4f sv = *(const v4f*)(s_mx + 64 + 16 * hb + 4 * g);
+    v4f L = (v4f){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < WD_WAVES; ++w) L += *(const v4f*)(&s_m[w][16 * hb + 4 * g]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      Lh[hb][j] = L[j];
+      Mh[hb][j] = mv[j];
+      Sk[hb][j] = sv[j];
+    }
+  }
+  if (a.n_split > 1) {
+    // partial records, one per 16-head block (the layout the combine reads):
+    // per head the running maximum (log2 units, no sink), the denominator and
+    // O, all relative to that maximum
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      float* rec = a.part + (((int64_t)t * 4 + hb) * a.n_split + split) * ATTN_PART_FLOATS;
+      if (wave == 0 && r == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          rec[4 * g + j] = Mh[hb][j];
+          rec[16 + 4 * g + j] = Lh[hb][j];
+        }
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) rec[32 + (4 * g + j) * AT_D + c0 + 16 * cb + r] = O[hb][cb][j];
+    }
+    return;
+  }
+  float fo[4][4];
+  const bool write_lse = a.lse && wave == 0 && r == 0;
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float sk = Sk[hb][j];
+      const float Mx = fmaxf(Mh[hb][j], sk);
+      const float e_keys = (Mh[hb][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mh[hb][j] - Mx);
+      const float den = Lh[hb][j] * e_keys + ((Mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sk - Mx));
+      fo[hb][j] = (den > 0.f) ? e_keys * __builtin_amdgcn_rcpf(den) : 0.f;
+      if (write_lse) a.lse[(int64_t)t * WD_H + 16 * hb + 4 * g + j] = (Mx + log2f(den)) * LN2;
+    }
+  // inverse RoPE of dims 448..511 (wave 7's columns): the pair (2i, 2i+1)
+  // sits in lanes r, r ^ 1
+  const bool turn = TURN && a.rope != nullptr && p >= 0 && p < a.n_rope && wave == 7;
+  const float* cs = a.rope + (int64_t)max(p, 0) * 64;   // read only when turning
+  // output through LDS (the raw tile is free), one 16-head block at a time:
+  // each wave stages its 16 x 64 block, then every lane stores a 16-byte run
+  constexpr int OSB = 64 * 4 + 16;                       // staged row stride (bytes), room for fp32
+  static_assert(WD_WAVES * 16 * OSB <= WD_RBUF, "the staged output fits the raw tile");
+  uint8_t* ob = s_raw + wave * 16 * OSB;
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      v4f v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = O[hb][cb][j] * fo[hb][j];
+      if (TURN) {
+        v4f vp;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vp[j] = __shfl_xor(v[j], 1);
+        if (turn) {
+          const int i = (16 * cb + r) >> 1;
+          const float c = cs[i], sn = cs[32 + i];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float x = (r & 1) ? vp[j] : v[j], y = (r & 1) ? v[j] : vp[j];
+            unturn(x, y, c, sn);
+            v[j] = (r & 1) ? y : x;
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(float*)(ob + (4 * g + j) * OSB + 4 * (16 * cb + r)) = v[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 16 rows of 64 fp32 columns: bf16 out, 8 lanes x 8 columns per row
+    // (hardware round-to-nearest-even conversion); fp32 out, 16 lanes x 4
+    if (a.out_bf16) {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int row = 8 * it + (lane >> 3);
+        const v4f x0 = *(const v4f*)(ob + row * OSB + 32 * (lane & 7));
+        const v4f x1 = *(const v4f*)(ob + row * OSB + 32 * (lane & 7) + 16);
+        v4u pk;
+        pk[0] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0[1]) << 16);
+        pk[1] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x0[3]) << 16);
+        pk[2] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1[1]) << 16);
+        pk[3] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x1[3]) << 16);
+        const int64_t o = ((int64_t)t * WD_H + 16 * hb + row) * AT_D + c0 + 8 * (lane & 7);
+        *(v4u*)((uint16_t*)a.out + o) = pk;
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = 4 * it + (lane >> 4);
+        const v4u v = *(const v4u*)(ob + row * OSB + 16 * (lane & 15));
+        const int64_t o = ((int64_t)t * WD_H + 16 * hb + row) * AT_D + c0 + 4 * (lane & 15);
+        *(v4u*)((float*)a.out + o) = v;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // fp32 path: one workgroup per (query, head); plain loops.
 constexpr int AF_MAX_SLOTS = 8192;
 
@@ -600,7 +1121,7 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs a) {
 // O and their m, l) is issued before any is used, with split indices clamped
 // to the last split and zero factors past it, so one memory round trip
 // covers the combine.
-constexpr int ATTN_MAX_SPLIT = 8;
+constexpr int ATTN_MAX_SPLIT = 16;
 
 #ifndef CSA2_COMBINE_PARTS
 #define CSA2_COMBINE_PARTS 8
@@ -684,6 +1205,8 @@ __global__ __launch_bounds__(ATTN_COMBINE_THREADS) void sparse_attn_combine_kern
 // Key splits per (query, 16 heads): only when the batch leaves most of the
 // chip idle; about eight 16-key tiles per split (one per wave), at most 8.
 int attn_splits(int Q, int H, int k, int window) {
+  if (Q <= 0) return 1;
+  if (H == WD_H && Q >= WD_MIN_Q) return 1;   // wide form, one workgroup per query
   const int groups = Q * (H / AT_HEADS);
   if (groups <= 0 || groups >= 128) return 1;
   const int tiles = (window + 15) / 16 + (k + 15) / 16;   // 16-key tiles
@@ -694,6 +1217,25 @@ int attn_splits(int Q, int H, int k, int window) {
 
 hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s) {
   const int groups = a.Q * (a.H / AT_HEADS);
+  if (a.H == WD_H && a.Q >= WD_MIN_Q) {
+    // split calls turn the output in the combine kernel
+    const bool turn = a.rope != nullptr && a.n_split == 1;
+    const dim3 grid(a.Q * a.n_split), block(64 * WD_WAVES);
+    if (a.main_s16) {
+      if (turn) hipLaunchKernelGGL((sparse_attn_wide_kernel<true, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((sparse_attn_wide_kernel<true, false>), grid, block, 0, s, a);
+    } else {
+      if (turn) hipLaunchKernelGGL((sparse_attn_wide_kernel<false, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((sparse_attn_wide_kernel<false, false>), grid, block, 0, s, a);
+    }
+    if (a.n_split > 1) {
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3(groups * ATTN_COMBINE_PARTS),
+                         dim3(ATTN_COMBINE_THREADS), 0, s, a);
+    }
+    return hipGetLastError();
+  }
   // split calls turn the output in the combine kernel
   const bool turn = a.rope != nullptr && a.n_split == 1;
   const dim3 grid(groups * a.n_split), block(64 * AW_WAVES);

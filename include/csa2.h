@@ -284,6 +284,26 @@ int csa2_topk_and_block_candidates_noalloc(const float* scores, int64_t score_st
 size_t csa2_noalloc_scratch_bytes(void);
 
 /*
+ * Diagnostics (not on the hot path).
+ *
+ * csa2_diag_index_scores_fp8_mfma — the dense scores of csa2_index_scores for
+ * FP8 q_idx and k_idx (flat rows, H_I = 32, d_I = 128, the same score
+ * definition: [DSA] Lightning Indexer, FP8 section), with every 128-dim dot
+ * product taken on the FP8 matrix cores straight from the E4M3 codes.
+ * csa2_index_scores widens the codes to f16 exactly and accumulates in fp32;
+ * this form exists so the FP8 instructions' accumulation can be measured
+ * against the 1e-3 score bound.  Arguments as in csa2_index_scores (scores
+ * [Q, score_stride], n_cols columns, -inf past the visible count).
+ *   Errors: CSA2_ERR_INVALID_ARG / CSA2_ERR_UNSUPPORTED on the host as in
+ *   csa2_index_scores; CSA2_ERR_HIP if the launch fails.
+ */
+int csa2_diag_index_scores_fp8_mfma(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
+                                    const csa2_rows* k_idx, const int64_t* seq_base,
+                                    const int32_t* q_seq, const int32_t* q_pos, int32_t ratio,
+                                    float* scores, int64_t score_stride, int32_t n_cols, int32_t Q,
+                                    void* stream);
+
+/*
  * csa2_sparse_attn — core sparse attention ([CSA2] "per-layer attention
  * computation"; [3MODES] Q&A on Reuse layers).  For query t at position p of
  * sequence b and head i, the keys are the SWA rows of positions

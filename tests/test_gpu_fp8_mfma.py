@@ -1,0 +1,104 @@
+"""Why index scoring widens E4M3 codes to f16 instead of using the FP8 matrix
+cores: both contractions on the same inputs, against the oracle.
+
+csa2_index_scores (the hot path) widens the E4M3 codes exactly to f16 and
+accumulates the products in fp32; csa2_diag_index_scores_fp8_mfma takes
+each 128-dim dot product on v_mfma_scale_f32_32x32x64_f8f6f4 straight from
+the codes.  Score bound (DSA page, Lightning Indexer and FP8 sections; the
+1e-3 relative bound with the row-RMS floor):
+|dI| <= 1e-3 (|I| + 0.01 RMS of the row).
+
+* Small-integer q, k and gates (exact E4M3 codes, unit scales): every
+  product and partial sum is an exact small integer, so both forms must
+  equal the oracle exactly -- this pins the FP8 form's operand layout.
+* Unit-variance Gaussian q and k quantized to E4M3 with one scale per row,
+  bf16 gates (the distributions of the prefill and decode workloads): the
+  f16 form meets the bound; the FP8 form's accumulation does not."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import top_sparse_long_amd as tsl
+from top_sparse_long_amd.driver import LayerRunner
+from tests import oracle_io
+from tests.parity import row_tau
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    tsl.load()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _both(q_rows, w, k_rows, seq_base, q_seq, q_pos, Q, n_cols):
+    stride = (n_cols + 63) // 64 * 64
+    f16 = torch.empty((Q, stride), dtype=torch.float32, device=DEV)
+    f8 = torch.empty((Q, stride), dtype=torch.float32, device=DEV)
+    tsl.csa2_index_scores(q_rows, w, tsl.CSA2_BF16, k_rows, seq_base, q_seq, q_pos, 1, f16, n_cols, Q)
+    tsl.csa2_diag_index_scores_fp8_mfma(q_rows, w, tsl.CSA2_BF16, k_rows, seq_base, q_seq, q_pos, 1,
+                                        f8, n_cols, Q)
+    torch.cuda.synchronize()
+    return _np(f16[:, :n_cols]).astype(np.float64), _np(f8[:, :n_cols]).astype(np.float64)
+
+
+def _bound_ratio(gpu, ref):
+    """max over the visible entries of |dI| / (1e-3 (|I| + tau_row))."""
+    vis = np.isfinite(ref)
+    assert np.array_equal(vis, np.isfinite(gpu))
+    tau = np.array([row_tau(row) for row in ref])
+    lim = 1e-3 * (np.abs(ref) + tau[:, None])
+    return float(np.max(np.where(vis, np.abs(gpu - ref) / lim, 0.0)))
+
+
+def test_small_integers_are_exact_in_both_forms():
+    print("[case] fp8 mfma diagnostic, small integers", flush=True)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(61)
+    Q, N = 48, 3000
+    q = torch.randint(-4, 5, (Q, 32, 128), generator=g, device=DEV).to(torch.float32)
+    k = torch.randint(-4, 5, (N, 128), generator=g, device=DEV).to(torch.float32)
+    w = torch.randint(-2, 3, (Q, 32), generator=g, device=DEV).to(torch.float32)
+    q8 = q.to(torch.float8_e4m3fn).view(torch.uint8).reshape(Q * 32, 128).contiguous()
+    k8 = k.to(torch.float8_e4m3fn).view(torch.uint8).contiguous()
+    qs = torch.ones(Q * 32, dtype=torch.float32, device=DEV)
+    ks = torch.ones(N, dtype=torch.float32, device=DEV)
+    wb = w.to(torch.bfloat16).view(torch.int16).contiguous()
+    pos = torch.arange(N - Q, N, dtype=torch.int32, device=DEV)
+    seq = torch.zeros(Q, dtype=torch.int32, device=DEV)
+    base = torch.zeros(1, dtype=torch.int64, device=DEV)
+    f16, f8 = _both(tsl.rows_fp8(q8, qs), wb, tsl.rows_fp8(k8, ks), base, seq, pos, Q, N)
+    ref = oracle.index_scores_dense(_np(q).astype(np.float64), _np(w).astype(np.float64),
+                                    _np(k).astype(np.float64), np.zeros(1, np.int64), _np(seq),
+                                    _np(pos), 1, N)
+    assert np.array_equal(f16, ref)
+    assert np.array_equal(f8, ref)
+
+
+def test_gaussian_scores_fp8_accumulation_breaks_the_bound():
+    print("[case] fp8 mfma diagnostic, unit-variance Gaussian inputs", flush=True)
+    wl = synth.mini_workload(62, [8192, 5000], q_per_seq=32).to(DEV)
+    run = LayerRunner(wl)
+    f16, f8 = _both(run.layer_rows[0]["q_idx"], wl.layers[0].w, run.slots.index_k, wl.seq_base,
+                    wl.q_seq, wl.q_pos, wl.Q, run.n_cols)
+    m = oracle_io.meta(wl)
+    ref = oracle.index_scores_dense(oracle_io.index_q(wl.layers[0], True),
+                                    oracle_io.index_w(wl.layers[0], True), oracle_io.index_k_rows(wl),
+                                    m["seq_base"], m["q_seq"], m["q_pos"], 1, run.n_cols)
+    r16, r8 = _bound_ratio(f16, ref), _bound_ratio(f8, ref)
+    tau = np.array([row_tau(row) for row in ref])
+    vis = np.isfinite(ref)
+    frac8 = float(np.mean((np.abs(f8 - ref) > 1e-3 * (np.abs(ref) + tau[:, None]))[vis]))
+    print(f"worst |dI| / bound: f16 MFMA {r16:.3g}, FP8 MFMA {r8:.3g}; "
+          f"FP8 entries past the bound {100 * frac8:.3f} %", flush=True)
+    assert r16 <= 1.0
+    assert r8 > 1.0

@@ -19,7 +19,8 @@ CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1, CSA2_FP4_E2M1_E4M3S16 = 0, 1,
 EXPORTED = ("csa2_index_scores", "csa2_block_candidates", "csa2_block_candidates_workspace_size",
             "csa2_topk", "csa2_topk_workspace_size", "csa2_topk_and_block_candidates",
             "csa2_topk_and_block_candidates_workspace_size",
-            "csa2_topk_and_block_candidates_noalloc", "csa2_noalloc_scratch_bytes", "csa2_sparse_attn",
+            "csa2_topk_and_block_candidates_noalloc", "csa2_noalloc_scratch_bytes",
+            "csa2_diag_index_scores_fp8_mfma", "csa2_sparse_attn",
             "csa2_sparse_attn_workspace_size", "csa2_cache_write",
             "csa2_status_string", "csa2_last_error", "csa2_version")
 
@@ -82,6 +83,8 @@ def load():
     lib.csa2_topk_and_block_candidates_workspace_size.restype = SZ
     lib.csa2_topk_and_block_candidates_noalloc.argtypes = [P, I64, I32, P, I64, P, I32, I32, P, I32,
                                                            I32, P, I32, PP, P]
+    lib.csa2_diag_index_scores_fp8_mfma.argtypes = [RP, P, ctypes.c_int, RP, P, P, P, I32, P, I64, I32,
+                                                    I32, P]
     lib.csa2_noalloc_scratch_bytes.argtypes = []
     lib.csa2_noalloc_scratch_bytes.restype = SZ
     lib.csa2_sparse_attn.argtypes = [P, ctypes.c_int, RP, P, P, I32, RP, P, P, P, I32, P, P, I32,
@@ -96,6 +99,7 @@ def load():
     lib.csa2_last_error.restype = ctypes.c_char_p
     for fn in ("csa2_index_scores", "csa2_block_candidates", "csa2_topk",
                "csa2_topk_and_block_candidates", "csa2_topk_and_block_candidates_noalloc",
+               "csa2_diag_index_scores_fp8_mfma",
                "csa2_sparse_attn", "csa2_cache_write",
                "csa2_version"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -218,6 +222,15 @@ def csa2_topk(scores, n_cols, q_pos, ratio, k, idx, workspace, Q, cand=None, blo
 def csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size, n_blocks):
     return load().csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size,
                                                                 n_blocks)
+
+
+def csa2_diag_index_scores_fp8_mfma(q_rows, w, w_dtype, k_rows, seq_base, q_seq, q_pos, ratio,
+                                    scores, n_cols, Q, stream=None):
+    """Diagnostic: dense FP8 scores with the dot products on the FP8 matrix cores."""
+    _check(load().csa2_diag_index_scores_fp8_mfma(ctypes.byref(q_rows), _ptr(w), w_dtype,
+                                                  ctypes.byref(k_rows), _ptr(seq_base), _ptr(q_seq),
+                                                  _ptr(q_pos), ratio, _ptr(scores), scores.stride(0),
+                                                  n_cols, Q, _stream(stream)))
 
 
 def csa2_noalloc_scratch_bytes():

@@ -166,6 +166,51 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
   return fail(CSA2_ERR_UNSUPPORTED, "csa2_index_scores: rows must be FP8_E4M3 or F32");
 }
 
+int csa2_diag_index_scores_fp8_mfma(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
+                                    const csa2_rows* k_idx, const int64_t* seq_base,
+                                    const int32_t* q_seq, const int32_t* q_pos, int32_t ratio,
+                                    float* scores, int64_t score_stride, int32_t n_cols, int32_t Q,
+                                    void* stream) {
+  g_err[0] = 0;
+  REQUIRE(q_idx && k_idx && w && seq_base && q_seq && q_pos && scores && q_idx->data && k_idx->data &&
+              q_idx->scale && k_idx->scale,
+          CSA2_ERR_INVALID_ARG, "csa2_diag_index_scores_fp8_mfma: null pointer argument");
+  REQUIRE(q_idx->dtype == CSA2_FP8_E4M3 && k_idx->dtype == CSA2_FP8_E4M3, CSA2_ERR_UNSUPPORTED,
+          "csa2_diag_index_scores_fp8_mfma: q_idx and k_idx must be FP8_E4M3");
+  REQUIRE(w_dtype == CSA2_BF16 || w_dtype == CSA2_F32, CSA2_ERR_UNSUPPORTED,
+          "csa2_diag_index_scores_fp8_mfma: gates must be BF16 or F32");
+  REQUIRE(ratio == 1 || ratio == 2, CSA2_ERR_UNSUPPORTED, "csa2_diag_index_scores_fp8_mfma: ratio must be 1 or 2");
+  REQUIRE(Q >= 0 && n_cols >= 0 && score_stride >= n_cols, CSA2_ERR_INVALID_ARG,
+          "csa2_diag_index_scores_fp8_mfma: bad size or stride");
+  REQUIRE(aligned(q_idx->data, 16) && aligned(k_idx->data, 16) && q_idx->row_stride % 16 == 0 &&
+              k_idx->row_stride % 16 == 0 && q_idx->row_stride >= 128 && k_idx->row_stride >= 128,
+          CSA2_ERR_INVALID_ARG, "csa2_diag_index_scores_fp8_mfma: rows must be 16-byte aligned, >= 128 bytes");
+  if (Q == 0 || n_cols == 0) return CSA2_OK;
+  csa2::IndexScoreArgs a = {};
+  a.q = (const uint8_t*)q_idx->data;
+  a.q_scale = q_idx->scale;
+  a.q_row_stride = q_idx->row_stride;
+  a.q_scale_stride = q_idx->scale_stride;
+  a.w = w;
+  a.w_bf16 = (w_dtype == CSA2_BF16);
+  a.k = (const uint8_t*)k_idx->data;
+  a.k_scale = k_idx->scale;
+  a.k_row_stride = k_idx->row_stride;
+  a.k_scale_stride = k_idx->scale_stride;
+  a.k_scale_bytes = k_idx->scale_stride * (int64_t)sizeof(float);
+  a.seq_base = seq_base;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.ratio = ratio;
+  a.scores = scores;
+  a.score_stride = score_stride;
+  a.n_cols = n_cols;
+  a.Q = Q;
+  a.H = 32;
+  return hip_status(csa2::launch_index_scores_fp8mma_diag(a, (hipStream_t)stream),
+                    "csa2_diag_index_scores_fp8_mfma");
+}
+
 size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k) {
   if (Q <= 0 || n_cols <= 0 || k <= 0) return 0;
   return csa2::select_workspace_bytes(Q, n_cols, k);

@@ -432,11 +432,14 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
       const int blk = blk0 + j;
       const int buf = j & 1;
       const int colb = blk * PF_KB;
-      const bool more = (j + 1 < n_blk) && maxvis > 0;
+      // blocks wholly past the pass's furthest visible column are not staged
+      const bool more = (j + 1 < n_blk) && (blk + 1) * PF_KB < maxvis;
       if (more) load_block(blk + 1);
       // B operands of the next tile are read from LDS while the current
-      // tile's MFMAs and epilogue run
-      const int n_tiles = min(PF_KB / 32, (a.n_cols - colb + 31) / 32);
+      // tile's MFMAs and epilogue run; tiles past maxvis are not contracted
+      // (causal skip), their columns are written -inf below
+      const int n_col_tiles = min(PF_KB / 32, (a.n_cols - colb + 31) / 32);
+      const int n_tiles = min(n_col_tiles, max(0, (maxvis - colb + 31) / 32));
       v8h kb[8];
       auto read_kb = [&](int tile) {
         const uint8_t* krow = s_k[buf] + (tile * 32 + r) * PF_RS + 128 * half;
@@ -449,8 +452,8 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
         const int tcol = colb + tile * 32;
         const int col = tcol + r;
         const float ks = s_ks[buf][tile * 32 + r];
-        // both queries' chains interleaved; every tile is contracted and
-        // columns a query does not see are masked
+        // both queries' chains interleaved; columns a query does not see
+        // (within the pass's visible range) are masked
         v16f acc[2] = {{0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f},
                        {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -479,10 +482,69 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
           }
         }
       }
+      for (int tile = n_tiles; tile < n_col_tiles; ++tile) {
+        const int col = colb + tile * 32 + r;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          if (!act[i] || col >= a.n_cols) continue;
+          if (half == 0) a.scores[(int64_t)tq[i] * a.score_stride + col] = -INFINITY;
+          if (a.block_max && half == 0 && (r & ((1 << a.block_shift) - 1)) == 0)
+            a.block_max[(int64_t)tq[i] * a.block_max_stride + (col >> a.block_shift)] = -INFINITY;
+        }
+      }
       if (more) store_block(buf ^ 1);
       __syncthreads();
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Diagnostic form, not on the hot path: the same dense scores with each
+// query-key block of 32 heads x 32 keys contracted on the FP8 matrix cores
+// (v_mfma_scale_f32_32x32x64_f8f6f4, unit E8M0 scales) straight from the E4M3
+// codes, every other step as in the kernels above.  It exists to measure that
+// instruction's accumulation against the score bound; the hot path widens
+// the codes to f16 instead (exact) and accumulates in fp32.
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(64) void index_scores_fp8mma_diag_kernel(IndexScoreArgs a) {
+  const int t = blockIdx.y;
+  const int col0 = blockIdx.x * 32;
+  const int lane = threadIdx.x;
+  const int r = lane & 31, g = lane >> 5;
+  const int nvis = visible_count(a.q_pos[t], a.ratio);
+  const int64_t base = a.seq_base[a.q_seq[t]];
+  const int col = col0 + r;
+  const int kc = min(col, max(nvis - 1, 0));   // rows past the visible range repeat the last (masked)
+  // A: head r, dims [64 s + 32 g, +32); B: key col0 + r, the same dims
+  const uint8_t* qrow = a.q + (int64_t)(t * 32 + r) * a.q_row_stride;
+  const uint8_t* krow = a.k + (base + kc) * a.k_row_stride;
+  v16f acc = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const v8i_t qa = *(const v8i_t*)(qrow + 64 * st + 32 * g);
+    const v8i_t kb = *(const v8i_t*)(krow + 64 * st + 32 * g);
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kb, acc, 0, 0, 0, 127, 0, 127);
+  }
+  // lane (r, g) holds key col0 + r for heads 8 j + 4 g + i
+  float v = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 8 * j + 4 * g + i;
+      const float gw = load_gate(a, t, h) * a.q_scale[(int64_t)(t * 32 + h) * a.q_scale_stride];
+      v = fmaf(gw, relu(acc[4 * j + i]), v);
+    }
+  v = add_half_swap(v);
+  const float ks = *(const float*)((const uint8_t*)a.k_scale + (base + kc) * a.k_scale_bytes);
+  if (g == 0 && col < a.n_cols) a.scores[(int64_t)t * a.score_stride + col] = (col < nvis) ? v * ks : -INFINITY;
+}
+
+hipError_t launch_index_scores_fp8mma_diag(const IndexScoreArgs& a, hipStream_t s) {
+  dim3 grid((a.n_cols + 31) / 32, a.Q);
+  hipLaunchKernelGGL(index_scores_fp8mma_diag_kernel, grid, dim3(64), 0, s, a);
+  return hipGetLastError();
 }
 
 // fp32 rows: one thread per column, heads and dims in a plain loop.  Used for

@@ -79,6 +79,8 @@ constexpr int PF_MIN_Q = 256;
 
 hipError_t launch_index_scores_fp8(const IndexScoreArgs& a, hipStream_t s);
 hipError_t launch_index_scores_f32(const IndexScoreArgs& a, hipStream_t s);
+// Diagnostic: dense FP8 scores with the contraction on the FP8 matrix cores.
+hipError_t launch_index_scores_fp8mma_diag(const IndexScoreArgs& a, hipStream_t s);
 
 // Selection (top-k and block candidates) -------------------------------------
 enum SelMode { SEL_DENSE = 0, SEL_POOL = 1, SEL_BLOCKMAX = 2, SEL_LIST = 3 };

@@ -103,7 +103,8 @@ def _stage_work(run, stage):
     shared = wl.Q >= PREFILL_MIN_Q
     if stage == "index_scores_dense":
         # plus the fused block maxima (4 B per block) when the step emits them
-        extra = 4.0 / wl.block_size if run.fuse_block_max and any(run.needs_pool) else 0.0
+        fused = any(run.fuses_block_max(li) for li, l in enumerate(wl.layers) if l.mode == "full")
+        extra = 4.0 / wl.block_size if fused else 0.0
         pairs = int(nvis.sum().item())
         return (float(pairs) * (_index_bytes(wl) + extra), float(pairs) * INDEX_FLOPS_PER_PAIR, pairs,
                 "mfma" if shared else "hbm")
@@ -113,12 +114,19 @@ def _stage_work(run, stage):
     if stage == "block_candidates" and run.fuse_block_max:
         nblk = (nvis + wl.block_size - 1) // wl.block_size
         return float(nblk.sum().item()) * SCORE_BYTES, 0.0, int(nvis.sum().item()), "hbm"
+    nblk = (nvis + wl.block_size - 1) // wl.block_size
+    # the top-k through block maxima reads the maxima, then the scores of the
+    # k best blocks (the library takes this route when k * block_size <= 32,768)
+    via = (run.via_blocks and run.fuse_block_max and wl.topk * wl.block_size <= 32768)
+    topk_read = nblk + nvis.clamp(max=wl.topk * wl.block_size) if via else nvis
     if stage == "topk_and_blocks":
-        # the top-k reads every visible score; the pool reads the block
-        # maxima when the scoring pass wrote them, else the scores again
-        nblk = (nvis + wl.block_size - 1) // wl.block_size
+        # the pool reads the block maxima when the scoring pass wrote them,
+        # else the scores again
         pool = nblk if run.fuse_block_max else nvis
-        return float((nvis + pool).sum().item()) * SCORE_BYTES, 0.0, int(nvis.sum().item()), "hbm"
+        return (float((topk_read + pool).sum().item()) * SCORE_BYTES, 0.0, int(nvis.sum().item()),
+                "hbm")
+    if stage == "topk_blocks":
+        return float(topk_read.sum().item()) * SCORE_BYTES, 0.0, int(nvis.sum().item()), "hbm"
     if stage in ("topk_dense", "block_candidates"):
         return float(nvis.sum().item()) * SCORE_BYTES, 0.0, int(nvis.sum().item()), "hbm"
     if stage == "topk_pool":
@@ -154,7 +162,9 @@ STAGE_KERNELS = {
     "block_candidates": ("select_kernel<2,",),
     "topk_dense": ("select_kernel<0,", "select_kernel<3,"),
     "topk_pool": ("select_kernel<1,",),
-    "topk_and_blocks": ("select_pair_kernel", "select_kernel<0,", "select_kernel<2,", "select_kernel<3,"),
+    "topk_blocks": ("select_kernel<5,", "select_kernel<4,"),
+    "topk_and_blocks": ("select_pair_kernel", "select_kernel<0,", "select_kernel<2,", "select_kernel<3,",
+                        "select_kernel<4,", "select_kernel<5,"),
     "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_combine_kernel", "sparse_attn_f32_kernel"),
     # the 65,536-token m = 2 chunk (the decode-batch calls use the prefetching
     # variant, cache_write_kernel<m, true>, and are not part of this record)
@@ -234,7 +244,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, workload, comma
         if not any(p in n for p in own for n in per_kernel_bytes):
             continue
         # with the shared-launch call the separate-call stages do not occur
-        if stage in ("topk_dense", "block_candidates") and any(
+        if stage in ("topk_dense", "block_candidates", "topk_blocks") and any(
                 "select_pair_kernel" in n for n in per_kernel_bytes):
             continue
         names = [n for n in per_kernel_bytes if any(p in n for p in pats)]

@@ -227,6 +227,40 @@ int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols,
 size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k);
 
 /*
+ * csa2_topk_from_block_max — the dense top-k of csa2_topk (the same indices,
+ * bit for bit) computed through the block maxima of the same scores
+ * ([CSA2] "hierarchical sparse indexer": the maximum of every 8 consecutive
+ * scores is taken in the scoring pass; here it narrows the top-k): the k best
+ * blocks under (maximum desc, block asc), then the k best of those blocks'
+ * k * block_size scores.  Exact: every score above the k-th best lies in one
+ * of at most k - 1 blocks whose maximum exceeds it, and a tied score the
+ * lower-position rule takes lies in a block of maximum >= it that the same
+ * rule on blocks keeps.
+ *   scores     [Q, score_stride] dense rows as in csa2_topk (q_pos required).
+ *   block_max  [Q, block_max_stride]: entry b = max of the visible scores
+ *              [b block_size, (b + 1) block_size) (-inf if none), as
+ *              csa2_index_scores writes them; block_max_stride >=
+ *              ceil(n_cols / block_size).
+ *   block_size a power of two <= 32.
+ *   workspace  at least csa2_topk_from_block_max_workspace_size(Q, n_cols,
+ *              k, block_size) bytes, 16-byte aligned.
+ *   pages      NULL, or a page table for the output as in csa2_topk.
+ *   With k * block_size above 32,768 the rows are selected by the plain
+ *   dense top-k (same result, its own workspace size, which the size query
+ *   returns).
+ *   Errors: as csa2_topk; CSA2_ERR_INVALID_ARG for a missing or misaligned
+ *   block_max.
+ */
+int csa2_topk_from_block_max(const float* scores, int64_t score_stride, int32_t n_cols,
+                             const float* block_max, int64_t block_max_stride, const int32_t* q_pos,
+                             int32_t ratio, int32_t block_size, int32_t k, int32_t* idx,
+                             void* workspace, size_t workspace_bytes, int32_t Q,
+                             const csa2_pages* pages, void* stream);
+
+size_t csa2_topk_from_block_max_workspace_size(int32_t Q, int32_t n_cols, int32_t k,
+                                                int32_t block_size);
+
+/*
  * csa2_topk_and_block_candidates — a Full layer's own top-k and the block
  * candidate pool it hands to the Reindex layers that follow, from the one set
  * of dense scores ([CSA2] "hierarchical sparse indexer", recall step: the

@@ -151,6 +151,50 @@ def test_topk_and_block_candidates_rejects():
     assert f(FAKE, n, n, None, 0, FAKE, 1, 512, FAKE, 8, 2048, FAKE, None, 0, 0, None, None) == tsl.CSA2_OK
 
 
+def test_topk_from_block_max_rejects():
+    lib = tsl.load()
+    f = lib.csa2_topk_from_block_max
+    n, Q, k = 32768, 4, 512
+    nb = n // 8
+    need = lib.csa2_topk_from_block_max_workspace_size(Q, n, k, 8)
+    assert need >= Q * k * 8
+    # block maxima are required, 4-byte aligned, with a stride covering every block
+    assert f(FAKE, n, n, None, 0, FAKE, 1, 8, k, FAKE, FAKE, need, Q, None, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert f(FAKE, n, n, FAKE, nb - 1, FAKE, 1, 8, k, FAKE, FAKE, need, Q, None, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    assert f(FAKE, n, n, FAKE + 2, nb, FAKE, 1, 8, k, FAKE, FAKE, need, Q, None, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    # q_pos is required; the block size is a power of two up to 32
+    assert f(FAKE, n, n, FAKE, nb, None, 1, 8, k, FAKE, FAKE, need, Q, None, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    for bs in (12, 64):
+        assert f(FAKE, n, n, FAKE, n, FAKE, 1, bs, k, FAKE, FAKE, need, Q, None, None) == \
+            tsl.CSA2_ERR_UNSUPPORTED
+    # the workspace holds the k best blocks of every row
+    assert f(FAKE, n, n, FAKE, nb, FAKE, 1, 8, k, FAKE, FAKE, need - 1, Q, None, None) == \
+        tsl.CSA2_ERR_WORKSPACE
+    assert f(FAKE, n, n, FAKE, nb, FAKE, 1, 8, k, FAKE, FAKE + 4, need, Q, None, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    # the plain top-k's checks apply (k, ratio, scores)
+    assert f(FAKE, n, n, FAKE, nb, FAKE, 1, 8, 4096, FAKE, FAKE, 1 << 30, Q, None, None) == \
+        tsl.CSA2_ERR_UNSUPPORTED
+    assert f(FAKE, n, n, FAKE, nb, FAKE, 3, 8, k, FAKE, FAKE, need, Q, None, None) == \
+        tsl.CSA2_ERR_UNSUPPORTED
+    assert f(None, n, n, FAKE, nb, FAKE, 1, 8, k, FAKE, FAKE, need, Q, None, None) == \
+        tsl.CSA2_ERR_INVALID_ARG
+    # k * block_size above 32,768 takes the dense top-k and its workspace size
+    big = 300000
+    assert lib.csa2_topk_from_block_max_workspace_size(Q, big, 2048, 32) == \
+        lib.csa2_topk_workspace_size(Q, big, 2048)
+    # the block ranking's lists, else the k best blocks of every row
+    assert lib.csa2_topk_from_block_max_workspace_size(Q, big, 2048, 8) == \
+        max(lib.csa2_topk_workspace_size(Q, -(-big // 8), 2048), Q * 2048 * 8)
+    assert lib.csa2_topk_from_block_max_workspace_size(Q, 4096, 512, 8) == Q * 512 * 8
+    # Q == 0 passes every check and enqueues nothing
+    assert f(FAKE, n, n, FAKE, nb, FAKE, 1, 8, k, FAKE, None, 0, 0, None, None) == tsl.CSA2_OK
+
+
 def test_topk_and_block_candidates_noalloc_rejects_sizes_past_the_scratch():
     """The allocation-free variant refuses, before anything is enqueued, any
     shape whose selection lists exceed its static buffer; its other argument

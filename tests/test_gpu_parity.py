@@ -320,6 +320,45 @@ def test_topk_and_block_candidates_exact(n_cols, n_blocks, k, ratio, from_block_
     assert torch.equal(idx, idx2) and torch.equal(cand, cand2)
 
 
+@pytest.mark.parametrize("n_cols,k,ratio,levels,bs", [(100, 512, 1, 3, 8), (4099, 512, 1, 2, 8),
+                                                       (20000, 512, 2, 40, 8), (32768, 512, 2, 40, 8),
+                                                       (32768, 512, 2, 1, 8), (131072, 512, 1, 50, 8),
+                                                       (200000, 2048, 1, 50, 8),
+                                                       (300000, 2048, 1, 50, 8),
+                                                       (1 << 20, 512, 1, 60, 8),
+                                                       (50000, 512, 1, 30, 32),
+                                                       (70000, 2048, 2, 30, 32)])
+def test_topk_from_block_max_exact(n_cols, k, ratio, levels, bs):
+    """The top-k through the block maxima equals the oracle's dense top-k bit
+    for bit, ties included (integer scores with few levels make many blocks
+    share their maximum).  The block ranking takes one, two and three
+    selection stages; k * block_size above 32,768 takes the dense fallback."""
+    _announce(f"topk_from_block_max n_cols={n_cols} k={k} ratio={ratio} levels={levels} bs={bs}")
+    rng = np.random.default_rng(n_cols + 3 * k + ratio + levels + bs)
+    Q = 4
+    sc = _tie_scores(rng, Q, n_cols, levels)
+    last = [ratio * n_cols - 1, max(0, (ratio * n_cols) // 3 - 5), ratio * 700 + 1, 0]
+    q_pos = np.array(last, dtype=np.int32)
+    nvis = oracle.visible_count(q_pos, ratio)
+    stride = (n_cols + 63) // 64 * 64
+    dev = torch.full((Q, stride), float("nan"), device=DEV)
+    dev[:, :n_cols] = torch.from_numpy(sc).to(DEV)
+    nb = -(-n_cols // bs)
+    host = np.full((Q, nb + 5), np.nan)
+    host[:, :nb] = -np.inf
+    for t in range(Q):
+        m = oracle.block_maxima(sc[t].astype(np.float64), int(min(nvis[t], n_cols)), bs)
+        host[t, :len(m)] = m
+    bm = torch.from_numpy(host.astype(np.float32)).to(DEV)
+    qp = torch.from_numpy(q_pos).to(DEV)
+    idx = torch.full((Q, k), -7, dtype=torch.int32, device=DEV)
+    wsb = tsl.csa2_topk_from_block_max_workspace_size(Q, n_cols, k, bs)
+    ws = torch.randint(0, 255, (max(16, wsb),), dtype=torch.uint8, device=DEV)
+    tsl.csa2_topk_from_block_max(dev, n_cols, bm, qp, ratio, bs, k, idx, ws, Q)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(idx), oracle.topk_rows_dense(sc.astype(np.float64), q_pos, ratio, k))
+
+
 # ---------------------------------------------------------------------------
 # attention: the oracle runs on the same indices
 

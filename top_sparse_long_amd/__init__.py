@@ -20,7 +20,8 @@ EXPORTED = ("csa2_index_scores", "csa2_block_candidates", "csa2_block_candidates
             "csa2_topk", "csa2_topk_workspace_size", "csa2_topk_and_block_candidates",
             "csa2_topk_and_block_candidates_workspace_size",
             "csa2_topk_and_block_candidates_noalloc", "csa2_noalloc_scratch_bytes",
-            "csa2_diag_index_scores_fp8_mfma", "csa2_sparse_attn",
+            "csa2_diag_index_scores_fp8_mfma", "csa2_topk_from_block_max",
+            "csa2_topk_from_block_max_workspace_size", "csa2_sparse_attn",
             "csa2_sparse_attn_workspace_size", "csa2_cache_write",
             "csa2_status_string", "csa2_last_error", "csa2_version")
 
@@ -83,6 +84,9 @@ def load():
     lib.csa2_topk_and_block_candidates_workspace_size.restype = SZ
     lib.csa2_topk_and_block_candidates_noalloc.argtypes = [P, I64, I32, P, I64, P, I32, I32, P, I32,
                                                            I32, P, I32, PP, P]
+    lib.csa2_topk_from_block_max.argtypes = [P, I64, I32, P, I64, P, I32, I32, I32, P, P, SZ, I32, PP, P]
+    lib.csa2_topk_from_block_max_workspace_size.argtypes = [I32, I32, I32, I32]
+    lib.csa2_topk_from_block_max_workspace_size.restype = SZ
     lib.csa2_diag_index_scores_fp8_mfma.argtypes = [RP, P, ctypes.c_int, RP, P, P, P, I32, P, I64, I32,
                                                     I32, P]
     lib.csa2_noalloc_scratch_bytes.argtypes = []
@@ -99,7 +103,7 @@ def load():
     lib.csa2_last_error.restype = ctypes.c_char_p
     for fn in ("csa2_index_scores", "csa2_block_candidates", "csa2_topk",
                "csa2_topk_and_block_candidates", "csa2_topk_and_block_candidates_noalloc",
-               "csa2_diag_index_scores_fp8_mfma",
+               "csa2_diag_index_scores_fp8_mfma", "csa2_topk_from_block_max",
                "csa2_sparse_attn", "csa2_cache_write",
                "csa2_version"):
         getattr(lib, fn).restype = ctypes.c_int
@@ -231,6 +235,20 @@ def csa2_diag_index_scores_fp8_mfma(q_rows, w, w_dtype, k_rows, seq_base, q_seq,
                                                   ctypes.byref(k_rows), _ptr(seq_base), _ptr(q_seq),
                                                   _ptr(q_pos), ratio, _ptr(scores), scores.stride(0),
                                                   n_cols, Q, _stream(stream)))
+
+
+def csa2_topk_from_block_max_workspace_size(Q, n_cols, k, block_size):
+    return load().csa2_topk_from_block_max_workspace_size(Q, n_cols, k, block_size)
+
+
+def csa2_topk_from_block_max(scores, n_cols, block_max, q_pos, ratio, block_size, k, idx, workspace,
+                             Q, stream=None, pages=None):
+    lib = load()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.csa2_topk_from_block_max(_ptr(scores), scores.stride(0), n_cols, _ptr(block_max),
+                                        block_max.stride(0), _ptr(q_pos), ratio, block_size, k,
+                                        _ptr(idx), _ptr(workspace), wsb, Q, _byref(pages),
+                                        _stream(stream)))
 
 
 def csa2_noalloc_scratch_bytes():

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -362,9 +363,67 @@ int csa2_topk(const float* scores, int64_t score_stride, int32_t n_cols, const i
 
 static size_t align16(size_t x) { return (x + 15) & ~(size_t)15; }
 
+size_t csa2_topk_from_block_max_workspace_size(int32_t Q, int32_t n_cols, int32_t k,
+                                                int32_t block_size) {
+  if (Q <= 0 || n_cols <= 0 || k <= 0 || block_size <= 0) return 0;
+  const int shift = log2_exact(block_size);
+  const int64_t nb = ((int64_t)n_cols + block_size - 1) / block_size;
+  if (shift >= 0 && csa2::top_via_blocks_supported(k, shift))
+    return csa2::top_via_blocks_workspace_bytes(Q, nb, k);
+  return csa2_topk_workspace_size(Q, n_cols, k);
+}
+
+int csa2_topk_from_block_max(const float* scores, int64_t score_stride, int32_t n_cols,
+                             const float* block_max, int64_t block_max_stride, const int32_t* q_pos,
+                             int32_t ratio, int32_t block_size, int32_t k, int32_t* idx,
+                             void* workspace, size_t workspace_bytes, int32_t Q,
+                             const csa2_pages* pages, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(q_pos, CSA2_ERR_INVALID_ARG, "csa2_topk_from_block_max: q_pos is required");
+  const int shift = log2_exact(block_size);
+  REQUIRE(shift >= 0 && shift <= 5, CSA2_ERR_UNSUPPORTED,
+          "csa2_topk_from_block_max: block_size must be a power of two <= 32");
+  REQUIRE(block_max && block_max_stride >= ((int64_t)n_cols + block_size - 1) / block_size &&
+              aligned(block_max, 4),
+          CSA2_ERR_INVALID_ARG,
+          "csa2_topk_from_block_max: block_max must be 4-byte aligned with a stride >= ceil(n_cols / block_size)");
+  const int64_t nb = ((int64_t)n_cols + block_size - 1) / block_size;
+  if (!csa2::top_via_blocks_supported(k, shift))
+    return csa2_topk(scores, score_stride, n_cols, q_pos, ratio, nullptr, 0, block_size, k, idx,
+                     workspace, workspace_bytes, Q, pages, stream);
+  const size_t need = Q > 0 && k > 0 && n_cols > 0 ? csa2::top_via_blocks_workspace_bytes(Q, nb, k) : 0;
+  REQUIRE(workspace_bytes >= need && (need == 0 || workspace), CSA2_ERR_WORKSPACE,
+          "csa2_topk_from_block_max: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  csa2::SelectArgs a;
+  // the plain top-k's argument checks (its own workspace size does not apply here)
+  int st = prep_topk(scores, score_stride, n_cols, q_pos, ratio, nullptr, 0, block_size, k, idx,
+                     workspace, (size_t)-1, Q, pages, &a);
+  if (st != CSA2_OK) return st;
+  if (Q == 0 || n_cols == 0) return CSA2_OK;
+  a.block_max = block_max;
+  a.block_max_stride = block_max_stride;
+  a.block_shift = shift;
+  a.workspace = workspace;
+  return hip_status(csa2::launch_topk_via_blocks(a, nb, (hipStream_t)stream), "csa2_topk_from_block_max");
+}
+
+
+
+// Workspace of the combined call's top-k: enough for the dense route and,
+// when the shapes allow it, for the route through block maxima.
+static size_t pair_topk_bytes(int32_t Q, int32_t n_cols, int32_t k, int32_t block_size) {
+  size_t b = csa2_topk_workspace_size(Q, n_cols, k);
+  const int shift = log2_exact(block_size);
+  if (Q > 0 && n_cols > 0 && k > 0 && shift >= 0 && csa2::top_via_blocks_supported(k, shift)) {
+    const int64_t nb = ((int64_t)n_cols + block_size - 1) / block_size;
+    b = std::max(b, csa2::top_via_blocks_workspace_bytes(Q, nb, k));
+  }
+  return b;
+}
+
 size_t csa2_topk_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t k,
                                                      int32_t block_size, int32_t n_blocks) {
-  return align16(csa2_topk_workspace_size(Q, n_cols, k)) +
+  return align16(pair_topk_bytes(Q, n_cols, k, block_size)) +
          csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks);
 }
 
@@ -382,7 +441,7 @@ static int topk_and_blocks(const float* scores, int64_t score_stride, int32_t n_
                                 : "csa2_topk_and_block_candidates";
   REQUIRE(q_pos, CSA2_ERR_INVALID_ARG, "%s: q_pos is required", fn);
   // the top-k's workspace comes first, the pool's follows at a 16-byte boundary
-  const size_t ws_t = align16(csa2_topk_workspace_size(Q, n_cols, k));
+  const size_t ws_t = align16(pair_topk_bytes(Q, n_cols, k, block_size));
   if (from_scratch) {
     const size_t need = csa2_topk_and_block_candidates_workspace_size(Q, n_cols, k, block_size, n_blocks);
     REQUIRE(need <= csa2::SELECT_SCRATCH_BYTES, CSA2_ERR_WORKSPACE,
@@ -412,7 +471,16 @@ static int topk_and_blocks(const float* scores, int64_t score_stride, int32_t n_
     at.workspace = base;
     ab.workspace = ws_b ? (uint8_t*)base + ws_t : nullptr;
   }
-  return hip_status(csa2::launch_topk_and_blocks(at, n_cols, ab, nb, (hipStream_t)stream), fn);
+  // with block maxima the top-k ranks blocks first (same result)
+  const bool via = block_max && csa2::top_via_blocks_supported(k, ab.block_shift);
+  int64_t t_len = n_cols;
+  if (via) {
+    at.block_max = block_max;
+    at.block_max_stride = block_max_stride;
+    at.block_shift = ab.block_shift;
+    t_len = ((int64_t)n_cols + block_size - 1) / block_size;
+  }
+  return hip_status(csa2::launch_topk_and_blocks(at, t_len, via, ab, nb, (hipStream_t)stream), fn);
 }
 
 int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, int32_t n_cols,

@@ -83,7 +83,11 @@ hipError_t launch_index_scores_f32(const IndexScoreArgs& a, hipStream_t s);
 hipError_t launch_index_scores_fp8mma_diag(const IndexScoreArgs& a, hipStream_t s);
 
 // Selection (top-k and block candidates) -------------------------------------
-enum SelMode { SEL_DENSE = 0, SEL_POOL = 1, SEL_BLOCKMAX = 2, SEL_LIST = 3 };
+// SEL_BLOCKMAX ranks blocks with the latest visible one forced in (block
+// candidates); SEL_BLOCKTOP ranks every block by its maximum; SEL_GATHER
+// selects among the scores of the blocks a SEL_BLOCKTOP list names.
+enum SelMode { SEL_DENSE = 0, SEL_POOL = 1, SEL_BLOCKMAX = 2, SEL_LIST = 3, SEL_GATHER = 4,
+               SEL_BLOCKTOP = 5 };
 
 constexpr int SEL_CAP = 32768;       // entries per chunk read from scores
 constexpr int SEL_CAP_LIST = 16384;  // (key, position) pairs per chunk
@@ -128,10 +132,19 @@ hipError_t launch_select(int mode, const SelectArgs& a, int64_t rows_len, hipStr
 // the current device (looked up once per device).
 constexpr size_t SELECT_SCRATCH_BYTES = (size_t)16 << 20;
 hipError_t select_scratch(void** ptr);
-// Dense top-k and block candidates of the same rows: the first stages of
-// both run in one launch (their workspaces must not overlap).
-hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, const SelectArgs& blocks,
-                                  int64_t blocks_len, hipStream_t s);
+// Top-k and block candidates of the same rows: the stages of both run
+// paired in shared launches (their workspaces must not overlap).  With
+// topk_via_blocks the top-k goes through the block maxima (topk_len is then
+// the blocks per row, and topk.block_max the maxima).
+hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, bool topk_via_blocks,
+                                  const SelectArgs& blocks, int64_t blocks_len, hipStream_t s);
+// Top-k through the block maxima: the k best blocks (ranked in the stages of
+// an ordinary selection over the maxima), then the k best of their
+// k * block_size scores in one chunk, so k * block_size is at most SEL_CAP;
+// workspace: top_via_blocks_workspace_bytes.
+bool top_via_blocks_supported(int k, int block_shift);
+size_t top_via_blocks_workspace_bytes(int Q, int64_t n_blocks, int k);
+hipError_t launch_topk_via_blocks(const SelectArgs& a, int64_t n_blocks, hipStream_t s);
 
 // Sparse attention -----------------------------------------------------------
 struct AttnArgs {

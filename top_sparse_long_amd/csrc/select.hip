@@ -25,6 +25,7 @@
 // among the row's k best is among its chunk's k best.
 #include "kernels.h"
 
+#include <algorithm>
 #include <mutex>
 
 namespace csa2 {
@@ -70,10 +71,11 @@ __device__ __forceinline__ int64_t row_length(const StageArgs& a, int t) {
   const SelectArgs& s = a.s;
   if (MODE == SEL_DENSE) return s.q_pos ? min(s.n_cols, sel_visible(s, t)) : s.n_cols;
   if (MODE == SEL_POOL) return s.n_cols;
-  if (MODE == SEL_BLOCKMAX) {
+  if (MODE == SEL_BLOCKMAX || MODE == SEL_BLOCKTOP) {
     const int n = min(s.n_cols, sel_visible(s, t));
     return n <= 0 ? 0 : ((n - 1) >> s.block_shift) + 1;
   }
+  if (MODE == SEL_GATHER) return a.in_len << s.block_shift;
   return a.in_len;
 }
 
@@ -128,6 +130,7 @@ struct SelSmem {
 template <int MODE, int CAP>
 __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, uint8_t* smem) {
   constexpr int EMAX = CAP / SEL_THREADS;   // entries per thread at most
+  constexpr int NAUX = (MODE == SEL_POOL || MODE == SEL_LIST || MODE == SEL_GATHER) ? EMAX : 1;
   // first digit: 16 interleaved copies of the 256-bin histogram (bin b,
   // copy c at 16 b + c), so lanes that hit the same bin land on 16 different
   // banks (scores share few top bytes); later digits: one copy after them.
@@ -155,7 +158,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
   // Loads are unconditional, from indices clamped into the chunk, and masked
   // afterwards, so they are all in flight together.
   uint32_t key[EMAX];
-  int32_t aux[(MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1];   // block id / position
+  int32_t aux[(MODE == SEL_POOL || MODE == SEL_LIST || MODE == SEL_GATHER) ? EMAX : 1];   // block id / position
   if (count > 0) {
     const int last = count - 1;
     if (MODE == SEL_DENSE || MODE == SEL_POOL) {
@@ -166,7 +169,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
 #pragma unroll
         for (int j = 0; j < EMAX; ++j) {
           const int64_t g = g0 + min(j * SEL_THREADS + tid, last);
-          aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] =
+          aux[j % NAUX] =
               s.cand[(int64_t)t * s.n_cand_blocks + (int)(g >> s.block_shift)];
         }
       }
@@ -174,7 +177,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
       for (int j = 0; j < EMAX; ++j) {
         const bool in = j * SEL_THREADS + tid < count;
         uint32_t kk = in ? float_key(v[j]) : KEY_PAD;
-        if (MODE == SEL_POOL && in && aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] < 0)
+        if (MODE == SEL_POOL && in && aux[j % NAUX] < 0)
           kk = KEY_NEG_INF;
         key[j] = kk;
       }
@@ -184,21 +187,46 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
 #pragma unroll
       for (int j = 0; j < EMAX; ++j) {
         key[j] = ik[min(j * SEL_THREADS + tid, last)];
-        aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] = ip[min(j * SEL_THREADS + tid, last)];
+        aux[j % NAUX] = ip[min(j * SEL_THREADS + tid, last)];
       }
 #pragma unroll
       for (int j = 0; j < EMAX; ++j)
         if (j * SEL_THREADS + tid >= count) key[j] = KEY_PAD;
-    } else {   // SEL_BLOCKMAX
+    } else if (MODE == SEL_GATHER) {
+      // entry e is score (block << shift) + (e % block_size) of list block
+      // e / block_size (block -1: nothing); positions past the row or the
+      // visible count are not selectable
+      const int32_t* ib = a.in_pos + (int64_t)t * a.in_len;
+      const int bs = 1 << s.block_shift;
+      const int nv = min(s.n_cols, sel_visible(s, t));
+      int32_t blk[EMAX];
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j) blk[j] = ib[(g0 + min(j * SEL_THREADS + tid, last)) >> s.block_shift];
+      float v[EMAX];
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j) {
+        const int e = (int)(g0 + min(j * SEL_THREADS + tid, last));
+        const int p = blk[j] >= 0 ? (blk[j] << s.block_shift) + (e & (bs - 1)) : -1;
+        aux[j] = (p >= 0 && p < nv) ? p : -1;
+        v[j] = row[max(aux[j], 0)];
+      }
+#pragma unroll
+      for (int j = 0; j < EMAX; ++j) {
+        const bool in = j * SEL_THREADS + tid < count;
+        key[j] = !in ? KEY_PAD : (aux[j] >= 0 ? float_key(v[j]) : KEY_NEG_INF);
+      }
+    } else {   // SEL_BLOCKMAX, SEL_BLOCKTOP
       // blocks before the last visible one are complete; the last one is
-      // forced and never read (reads are clamped below it)
-      const int64_t lim = (L >= 2) ? L - 2 : 0;
+      // forced and never read (reads are clamped below it) -- unless every
+      // block is ranked by its maximum (SEL_BLOCKTOP), when all are read
+      constexpr bool FORCE = MODE == SEL_BLOCKMAX;
+      const int64_t lim = FORCE ? ((L >= 2) ? L - 2 : 0) : max(L - 1, (int64_t)0);
       float m[EMAX];
       if (s.block_max) {
 #pragma unroll
         for (int j = 0; j < EMAX; ++j)
           m[j] = s.block_max[(int64_t)t * s.block_max_stride + min(g0 + min(j * SEL_THREADS + tid, last), lim)];
-      } else if (L >= 2) {
+      } else if (L >= (FORCE ? 2 : 1)) {
         const int bs = 1 << s.block_shift;
 #pragma unroll
         for (int j = 0; j < EMAX; ++j) {
@@ -222,8 +250,9 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
       for (int j = 0; j < EMAX; ++j) {
         const int i = j * SEL_THREADS + tid;
         uint32_t kk = KEY_PAD;
-        // the block of the latest visible position is always kept
-        if (i < count) kk = (g0 + i == L - 1) ? KEY_POS_INF : float_key(m[j]);
+        // the block of the latest visible position is always kept (unless
+        // every block is ranked by its maximum)
+        if (i < count) kk = (FORCE && g0 + i == L - 1) ? KEY_POS_INF : float_key(m[j]);
         key[j] = kk;
       }
     }
@@ -251,21 +280,21 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
       key[4 * i + 2] = v.z;
       key[4 * i + 3] = v.w;
     }
-    if (MODE == SEL_POOL || MODE == SEL_LIST) {
+    if (MODE == SEL_POOL || MODE == SEL_LIST || MODE == SEL_GATHER) {
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < EMAX; ++j) {
         const int pe = j * SEL_THREADS + tid;
-        s_tr[pe + 4 * (pe / EMAX)] = (uint32_t)aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)];
+        s_tr[pe + 4 * (pe / EMAX)] = (uint32_t)aux[j % NAUX];
       }
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < EMAX / 4; ++i) {
         const uint4 v = *(const uint4*)(src + 4 * i);
-        aux[(4 * i) % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] = (int32_t)v.x;
-        aux[(4 * i + 1) % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] = (int32_t)v.y;
-        aux[(4 * i + 2) % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] = (int32_t)v.z;
-        aux[(4 * i + 3) % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] = (int32_t)v.w;
+        aux[(4 * i) % NAUX] = (int32_t)v.x;
+        aux[(4 * i + 1) % NAUX] = (int32_t)v.y;
+        aux[(4 * i + 2) % NAUX] = (int32_t)v.z;
+        aux[(4 * i + 3) % NAUX] = (int32_t)v.w;
       }
     }
   }
@@ -393,13 +422,13 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
       const uint32_t o = rg + min(re, keq);
       const int64_t g = g0 + my0 + j;
       int32_t pos;
-      if (MODE == SEL_DENSE || MODE == SEL_BLOCKMAX) {
+      if (MODE == SEL_DENSE || MODE == SEL_BLOCKMAX || MODE == SEL_BLOCKTOP) {
         pos = (int32_t)g;
       } else if (MODE == SEL_POOL) {
-        pos = (aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)] << s.block_shift) |
+        pos = (aux[j % NAUX] << s.block_shift) |
               (int)(g & ((1 << s.block_shift) - 1));
-      } else {
-        pos = aux[j % ((MODE == SEL_POOL || MODE == SEL_LIST) ? EMAX : 1)];
+      } else {   // SEL_LIST, SEL_GATHER
+        pos = aux[j % NAUX];
       }
       if (a.out_key) {
         const int64_t off = (int64_t)t * a.out_stride + (int64_t)c * k + o;
@@ -610,9 +639,11 @@ static int make_stages(int first_mode, const SelectArgs& sa, int64_t rows_len, S
 
 static hipError_t launch_one(const Stage& st, int Q, hipStream_t s) {
   switch (st.mode) {
+    case SEL_GATHER: return launch_stage<SEL_GATHER>(st.a, st.cap, st.nch, Q, s);
     case SEL_DENSE: return launch_stage<SEL_DENSE>(st.a, st.cap, st.nch, Q, s);
     case SEL_POOL: return launch_stage<SEL_POOL>(st.a, st.cap, st.nch, Q, s);
     case SEL_BLOCKMAX: return launch_stage<SEL_BLOCKMAX>(st.a, st.cap, st.nch, Q, s);
+    case SEL_BLOCKTOP: return launch_stage<SEL_BLOCKTOP>(st.a, st.cap, st.nch, Q, s);
     default: return launch_stage<SEL_LIST>(st.a, st.cap, st.nch, Q, s);
   }
 }
@@ -627,9 +658,75 @@ hipError_t launch_select(int mode, const SelectArgs& sa, int64_t rows_len, hipSt
   return hipSuccess;
 }
 
+// Top-k through the block maxima (exact).  Let T be the k-th best score of
+// the row.  Every score above T lies in a block whose maximum is above T, and
+// there are at most k - 1 such blocks, so all of them are among the k best
+// blocks under (maximum desc, block asc).  The scores equal to T that the
+// tie rule takes are the lowest-position ones; a block holding one has
+// maximum >= T, and if its maximum equals T, every block of maximum T before
+// it also holds a score T at a lower position, so it is among the first
+// blocks of maximum T and is kept too.  Hence the k best scores are the k
+// best among the k best blocks' scores.  The first stages rank the blocks
+// (the latest block is not forced here) into a (key, block) list in block
+// order; the last gathers each listed block's scores and selects from them,
+// so the positions come out ascending.
+bool top_via_blocks_supported(int k, int block_shift) {
+  return ((int64_t)k << block_shift) <= SEL_CAP;
+}
+
+size_t top_via_blocks_workspace_bytes(int Q, int64_t n_blocks, int k) {
+  return std::max(select_workspace_bytes(Q, n_blocks, k), (size_t)Q * (size_t)k * 8u);
+}
+
+// The stages of the top-k through block maxima: the ranking's stages, the
+// last of them writing its k blocks as a (key, block) list (at the start of
+// the workspace when it is the only stage, else into the ping-pong buffer it
+// does not read), then the gather.  Returns the number of stages.
+static int make_via_blocks_stages(const SelectArgs& sa, int64_t n_blocks, Stage* st) {
+  SelectArgs sb = sa;
+  sb.page_table = nullptr;   // the ranking lists blocks, not positions
+  const int n = make_stages(SEL_BLOCKTOP, sb, n_blocks, st);
+  uint8_t* ws = (uint8_t*)sa.workspace;
+  uint8_t* list = ws;
+  size_t list_bytes = (size_t)sa.Q * (size_t)sa.k * 4u;
+  if (n > 1) {
+    const SelectPlan p = plan_select(sa.Q, n_blocks, sa.k);
+    list_bytes = (size_t)sa.Q * (size_t)p.ws_list_max * 4u;
+    if ((const uint8_t*)st[n - 1].a.in_key == ws) list = ws + 2 * list_bytes;
+  }
+  Stage& last = st[n - 1];
+  last.a.out_key = (uint32_t*)list;
+  last.a.out_pos = (int32_t*)(list + list_bytes);
+  last.a.out_stride = sa.k;
+  Stage& g = st[n];
+  const int64_t n2 = (int64_t)sa.k << sa.block_shift;
+  g = Stage{};
+  g.mode = SEL_GATHER;
+  g.a.s = sa;
+  g.a.in_key = last.a.out_key;
+  g.a.in_pos = last.a.out_pos;
+  g.a.in_len = sa.k;
+  g.a.chunk = fit_cap(n2);
+  g.cap = fit_cap(n2);
+  g.nch = 1;
+  g.a.out_key = nullptr;
+  return n + 1;
+}
+
+hipError_t launch_topk_via_blocks(const SelectArgs& sa, int64_t n_blocks, hipStream_t s) {
+  Stage st[SEL_MAX_STAGES + 1];
+  const int n = make_via_blocks_stages(sa, n_blocks, st);
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = launch_one(st[i], sa.Q, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // Paired launches: the first selection's stage in grid columns [0, n1), the
-// second's after it.  The first side is the dense top-k (DENSE first, then
-// LIST stages), the second the block candidates (BLOCKMAX, then LIST).
+// second's after it.  The first side is the top-k (DENSE first, then LIST
+// stages; or through block maxima: BLOCKTOP, LIST stages, GATHER), the
+// second the block candidates (BLOCKMAX, then LIST).
 template <int M1, int C1, int M2, int C2>
 static void launch_pair_k(const Stage& x, const Stage& y, int Q, hipStream_t s) {
   const dim3 grid(x.nch + y.nch, Q), block(SEL_THREADS);
@@ -650,29 +747,41 @@ static void pair_c1(const Stage& x, const Stage& y, int Q, hipStream_t s) {
   else pair_c2<M1, (M1 == SEL_LIST ? 16384 : SEL_CAP), M2>(x, y, Q, s);
 }
 
+template <int M1>
+static void pair_m2(const Stage& x, const Stage& y, int Q, hipStream_t s) {
+  if (y.mode == SEL_LIST) pair_c1<M1, SEL_LIST>(x, y, Q, s);
+  else pair_c1<M1, SEL_BLOCKMAX>(x, y, Q, s);
+}
+
 static hipError_t launch_pair(const Stage& x, const Stage& y, int Q, hipStream_t s) {
-  const bool l1 = x.mode == SEL_LIST, l2 = y.mode == SEL_LIST;
-  if (!l1 && !l2) pair_c1<SEL_DENSE, SEL_BLOCKMAX>(x, y, Q, s);
-  else if (!l1 && l2) pair_c1<SEL_DENSE, SEL_LIST>(x, y, Q, s);
-  else if (l1 && !l2) pair_c1<SEL_LIST, SEL_BLOCKMAX>(x, y, Q, s);
-  else pair_c1<SEL_LIST, SEL_LIST>(x, y, Q, s);
+  switch (x.mode) {
+    case SEL_DENSE: pair_m2<SEL_DENSE>(x, y, Q, s); break;
+    case SEL_BLOCKTOP: pair_m2<SEL_BLOCKTOP>(x, y, Q, s); break;
+    case SEL_GATHER: pair_m2<SEL_GATHER>(x, y, Q, s); break;
+    default: pair_m2<SEL_LIST>(x, y, Q, s); break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, const SelectArgs& blocks,
-                                  int64_t blocks_len, hipStream_t s) {
-  Stage t[SEL_MAX_STAGES], b[SEL_MAX_STAGES];
-  const int nt = make_stages(SEL_DENSE, topk, topk_len, t);
+hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, bool topk_via_blocks,
+                                  const SelectArgs& blocks, int64_t blocks_len, hipStream_t s) {
+  Stage t[SEL_MAX_STAGES + 1], b[SEL_MAX_STAGES];
+  const int nt = topk_via_blocks ? make_via_blocks_stages(topk, topk_len, t)
+                                 : make_stages(SEL_DENSE, topk, topk_len, t);
   const int nb = make_stages(SEL_BLOCKMAX, blocks, blocks_len, b);
-  // The two stage sequences are aligned at their ends, so the shorter one
-  // runs beside the longer one's last stages (the final stages are the
-  // single-workgroup-per-row ones that leave most of the chip idle).
+  // The dense route's stages are aligned at their ends, so the shorter
+  // sequence runs beside the longer one's last stages (the final stages are
+  // the single-workgroup-per-row ones that leave most of the chip idle).
+  // Through block maxima both sequences open with a pass over the same
+  // maxima, so they are aligned at their starts and the gather runs last.
   const int n = max(nt, nb);
   for (int j = 0; j < n; ++j) {
-    const int it = j - (n - nt), ib = j - (n - nb);
+    const int it = topk_via_blocks ? j : j - (n - nt);
+    const int ib = topk_via_blocks ? j : j - (n - nb);
     hipError_t e;
-    if (it >= 0 && ib >= 0) e = launch_pair(t[it], b[ib], topk.Q, s);
-    else if (it >= 0) e = launch_one(t[it], topk.Q, s);
+    const bool ht = it >= 0 && it < nt, hb = ib >= 0 && ib < nb;
+    if (ht && hb) e = launch_pair(t[it], b[ib], topk.Q, s);
+    else if (ht) e = launch_one(t[it], topk.Q, s);
     else e = launch_one(b[ib], topk.Q, s);
     if (e != hipSuccess) return e;
   }

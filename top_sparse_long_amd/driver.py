@@ -24,6 +24,7 @@ from . import (csa2_index_scores, csa2_block_candidates, csa2_topk, csa2_sparse_
                csa2_topk_and_block_candidates, csa2_topk_and_block_candidates_workspace_size,
                csa2_block_candidates_workspace_size, csa2_topk_workspace_size,
                csa2_sparse_attn_workspace_size, csa2_rows, csa2_pages,
+               csa2_topk_from_block_max, csa2_topk_from_block_max_workspace_size,
                rows_f32, rows_fp8, rows_fp4s16, rows_fp4_records, rows_fp4s16_records,
                rows_swa_records,
                CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1_E4M3S16)
@@ -50,7 +51,7 @@ class LayerRunner:
     slot; rope_cs: an optional [positions, 64] table — attention turns its
     output back by each query's position (the layout's table when paged)."""
 
-    def __init__(self, wl, device="cuda", paged=None, rope_cs=None):
+    def __init__(self, wl, device="cuda", paged=None, rope_cs=None, via_blocks=True):
         self.wl = wl
         self.dev = device
         self.paged = paged
@@ -91,6 +92,8 @@ class LayerRunner:
         self.scores = torch.empty((Q, self.stride), dtype=f32, device=device)
         # block maxima written by the Full layer's scoring pass
         self.fuse_block_max = wl.block_size <= 32
+        # a Full layer's top-k ranks blocks by those maxima first
+        self.via_blocks = via_blocks and self.fuse_block_max
         nbm = (self.n_cols + wl.block_size - 1) // wl.block_size
         self.block_max = torch.empty((Q, _round_up(max(nbm, 1), 64)), dtype=f32, device=device)
         self.pool_scores = torch.empty((Q, _round_up(self.pool_cols, 64)), dtype=f32, device=device)
@@ -101,7 +104,8 @@ class LayerRunner:
                  csa2_topk_workspace_size(Q, self.pool_cols, wl.topk),
                  csa2_block_candidates_workspace_size(Q, self.n_cols, wl.block_size, wl.n_blocks),
                  csa2_topk_and_block_candidates_workspace_size(Q, self.n_cols, wl.topk,
-                                                               wl.block_size, wl.n_blocks))
+                                                               wl.block_size, wl.n_blocks),
+                 csa2_topk_from_block_max_workspace_size(Q, self.n_cols, wl.topk, wl.block_size))
         self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=device)
         # block candidates may run beside the Full layer's top-k on a second
         # stream, so they get a workspace of their own
@@ -157,10 +161,14 @@ class LayerRunner:
                               block_max=self.block_max if from_block_max else None)
         self.slots.candidates = self.cand
 
-    def topk(self, li, pool):
+    def topk(self, li, pool, via_blocks=False):
         wl = self.wl
         idx = self.idx[li]
-        if pool:
+        if via_blocks:
+            csa2_topk_from_block_max(self.scores, self.n_cols, self.block_max, wl.q_pos, wl.ratio,
+                                     wl.block_size, wl.topk, idx, self.ws, self.Q,
+                                     pages=self.pages_topk)
+        elif pool:
             csa2_topk(self.pool_scores, self.pool_cols, None, wl.ratio, wl.topk, idx, self.ws,
                       self.Q, cand=self.slots.candidates, block_size=wl.block_size,
                       pages=self.pages_topk)
@@ -191,13 +199,21 @@ class LayerRunner:
                          idx_slots=self.paged is not None, n_main_rows=self.n_main_rows)
 
     # -- a whole pass ----------------------------------------------------------
+    def fuses_block_max(self, li):
+        """Whether layer li's dense scoring pass also writes block maxima."""
+        return self.fuse_block_max and (self.needs_pool[li] or self.via_blocks)
+
     def steps(self, concurrent=False, separate_select=False):
         """The calls of one pass over every layer, in order, as (stage name,
         callable) pairs.
 
-        A Full layer that builds the pool makes both of its selections with
-        one call (csa2_topk_and_block_candidates) unless separate_select or
-        concurrent asks for two calls.
+        A Full layer's dense scoring writes the block maxima when its top-k
+        ranks blocks first (via_blocks) or a later layer needs the pool; the
+        selections then read those maxima.  A Full layer that builds the pool
+        makes both of its selections with one call
+        (csa2_topk_and_block_candidates) unless separate_select or concurrent
+        asks for two calls; a Full layer's own top-k alone is
+        csa2_topk_from_block_max (via_blocks) or csa2_topk.
 
         concurrent=True runs the block-candidate selection on a second stream:
         it needs only the Full layer's scores, so it overlaps that layer's
@@ -214,7 +230,7 @@ class LayerRunner:
         has_pool = False
         for li, lay in enumerate(self.wl.layers):
             if lay.mode == "full":
-                fuse = self.needs_pool[li] and self.fuse_block_max
+                fuse = self.fuses_block_max(li)
                 out.append(("index_scores_dense",
                             lambda li=li, fuse=fuse: self.index_scores(li, pool=False, block_max=fuse)))
                 if self.needs_pool[li] and not (concurrent or separate_select):
@@ -231,7 +247,10 @@ class LayerRunner:
                         out.append(("block_candidates",
                                     lambda fuse=fuse: self.block_candidates(from_block_max=fuse)))
                     has_pool = True
-                out.append(("topk_dense", lambda li=li: self.topk(li, pool=False)))
+                if self.via_blocks:
+                    out.append(("topk_blocks", lambda li=li: self.topk(li, pool=False, via_blocks=True)))
+                else:
+                    out.append(("topk_dense", lambda li=li: self.topk(li, pool=False)))
             elif lay.mode == "reindex":
                 pool = has_pool
                 if pool and concurrent:

@@ -642,6 +642,8 @@ def stage_stats(timer, rs, n_samples, reps, protocols=("rotated", "cold", "warm"
         t = rec["rotated"]["median_us"] * 1e-6
         rec["avg_us"] = rec["rotated"]["median_us"]
         rec["hbm_frac"] = nbytes / t / (HBM_PEAK_GBS * 1e9)
+        if READ_CEILING:
+            rec["hbm_frac_of_read_ceiling"] = nbytes / t / (READ_CEILING["GB/s"] * 1e9)
         if flops:
             rec["mfma_frac_f16"] = flops / t / (F16_PEAK_TFLOPS * 1e12)
             if name.startswith("index_scores"):
@@ -689,6 +691,39 @@ def measure_workload(torch, synth, LayerRunner, timer, name, args, copies, steps
             "index_keys_per_step": keys, "attn_queries_per_step": n_attn}
 
 
+READ_CEILING = {}   # the measured streaming-read rate, filled by read_ceiling()
+
+
+def read_ceiling(torch, tsl, gib=2, reps=10):
+    """The chip's practical HBM read rate: csa2_diag_stream_read over a
+    2 GiB buffer (16-byte non-temporal loads, nothing computed), median of
+    reps timed launches on the launch stream."""
+    src = torch.ones((gib << 30) // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    for _ in range(2):
+        tsl.csa2_diag_stream_read(src, sink)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tsl.csa2_diag_stream_read(src, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    ts.sort()
+    t = ts[len(ts) // 2]
+    gbs = src.numel() * 4 / t / 1e9
+    del src, sink
+    torch.cuda.empty_cache()
+    READ_CEILING["GB/s"] = gbs
+    return {"kernel": "csa2_diag_stream_read", "bytes": gib << 30, "median_us": t * 1e6,
+            "achieved": gbs, "unit": "GB/s", "frac_of_peak": gbs / HBM_PEAK_GBS,
+            "what": "16-byte non-temporal loads in a grid-stride loop over 2 GiB, nothing computed: "
+                    "the practical read ceiling for the HBM-bound stages"}
+
+
 def _roofline(stage, rec, workload):
     """The roofline record of one stage from its rotated median."""
     t = rec["avg_us"] * 1e-6
@@ -702,9 +737,12 @@ def _roofline(stage, rec, workload):
         r["traffic"] = _traffic(stage, workload, rec["algorithmic_bytes"])
         return r
     achieved = rec["algorithmic_bytes"] / t / 1e9
-    return {"bound": "hbm", "kernel": stage, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS,
-            "traffic": _traffic(stage, workload, rec["algorithmic_bytes"])}
+    r = {"bound": "hbm", "kernel": stage, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "frac": achieved / HBM_PEAK_GBS,
+         "traffic": _traffic(stage, workload, rec["algorithmic_bytes"])}
+    if READ_CEILING:
+        r["frac_of_read_ceiling"] = achieved / READ_CEILING["GB/s"]
+    return r
 
 
 def targets(torch, synth, LayerRunner, timer, args):
@@ -762,6 +800,7 @@ def main():
 
     tsl.load()
     dev = "cuda"
+    ceiling = read_ceiling(torch, tsl)
     timer = Timer(torch, 1 << 30)
 
     # calibration copy for the counter runs (outside the timed region): a
@@ -845,9 +884,11 @@ def main():
                                       else "e4m3+f32/row"),
                    "main_kv_record": ("288 B e2m1+e4m3/16" if getattr(wl, "main_fmt", "fp4") == "fp4s16"
                                       else "320 B e2m1+f32/32"),
-                   "input_copies": args.copies, "full_layer_selections": "shared launch"},
+                   "input_copies": args.copies,
+                   "full_layer_selections": "shared launch; the top-k ranks blocks by their fused maxima first"},
         "sparse_attn_queries_per_s": attn_qps,
         "roofline": roofline,
+        "hbm_read_ceiling": ceiling,
         "cpu_baseline": cpu,
         "stages": stages,
         "targets": tgt,

@@ -338,6 +338,20 @@ int csa2_diag_index_scores_fp8_mfma(const csa2_rows* q_idx, const void* w, csa2_
                                     void* stream);
 
 /*
+ * csa2_diag_stream_read — reads bytes from src once, as fast as the chip
+ * allows (16-byte non-temporal loads in a grid-stride loop), and computes
+ * nothing from them: the practical HBM read ceiling against which the
+ * hot path's HBM-bound stages are judged.
+ *   src          device memory, 16-byte aligned; bytes a multiple of 16.
+ *   sink         device memory of sink_floats floats (>= 1); the kernel runs
+ *                min(4096, sink_floats) workgroups, and workgroup i may write
+ *                sink[i] (it does so only for a sum no real input reaches).
+ *   Errors: CSA2_ERR_INVALID_ARG for null or misaligned arguments;
+ *   CSA2_ERR_HIP if the launch fails.
+ */
+int csa2_diag_stream_read(const void* src, size_t bytes, float* sink, size_t sink_floats, void* stream);
+
+/*
  * csa2_sparse_attn — core sparse attention ([CSA2] "per-layer attention
  * computation"; [3MODES] Q&A on Reuse layers).  For query t at position p of
  * sequence b and head i, the keys are the SWA rows of positions

@@ -195,6 +195,18 @@ def test_topk_from_block_max_rejects():
     assert f(FAKE, n, n, FAKE, nb, FAKE, 1, 8, k, FAKE, None, 0, 0, None, None) == tsl.CSA2_OK
 
 
+def test_diag_stream_read_rejects():
+    lib = tsl.load()
+    f = lib.csa2_diag_stream_read
+    assert f(None, 1024, FAKE, 16, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert f(FAKE, 1024, None, 16, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert f(FAKE + 4, 1024, FAKE, 16, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert f(FAKE, 1000, FAKE, 16, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert f(FAKE, 1024, FAKE, 0, None) == tsl.CSA2_ERR_INVALID_ARG
+    # nothing to read: nothing is enqueued
+    assert f(FAKE, 0, FAKE, 16, None) == tsl.CSA2_OK
+
+
 def test_topk_and_block_candidates_noalloc_rejects_sizes_past_the_scratch():
     """The allocation-free variant refuses, before anything is enqueued, any
     shape whose selection lists exceed its static buffer; its other argument

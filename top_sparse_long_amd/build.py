@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa2.so")
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "index_scores.hip", "select.hip", "sparse_attn.hip", "cache_write.hip"]
+SOURCES = ["api.cpp", "index_scores.hip", "select.hip", "sparse_attn.hip", "cache_write.hip", "diag.hip"]
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-command-line-argument", f"-I{os.path.join(ROOT, 'include')}"]

@@ -212,6 +212,18 @@ int csa2_diag_index_scores_fp8_mfma(const csa2_rows* q_idx, const void* w, csa2_
                     "csa2_diag_index_scores_fp8_mfma");
 }
 
+int csa2_diag_stream_read(const void* src, size_t bytes, float* sink, size_t sink_floats, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(src && sink, CSA2_ERR_INVALID_ARG, "csa2_diag_stream_read: null pointer argument");
+  REQUIRE(aligned(src, 16) && bytes % 16 == 0, CSA2_ERR_INVALID_ARG,
+          "csa2_diag_stream_read: src must be 16-byte aligned and bytes a multiple of 16");
+  REQUIRE(sink_floats >= 1, CSA2_ERR_INVALID_ARG, "csa2_diag_stream_read: sink must hold at least one float");
+  if (bytes == 0) return CSA2_OK;
+  const int n_blocks = (int)std::min<size_t>(4096, sink_floats);
+  return hip_status(csa2::launch_stream_read(src, bytes, sink, n_blocks, (hipStream_t)stream),
+                    "csa2_diag_stream_read");
+}
+
 size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k) {
   if (Q <= 0 || n_cols <= 0 || k <= 0) return 0;
   return csa2::select_workspace_bytes(Q, n_cols, k);

@@ -40,6 +40,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 
 #ifndef CSA2_IS_WAVES
 #define CSA2_IS_WAVES 4
@@ -52,11 +53,20 @@ constexpr int IS_TILES = CSA2_IS_TILES;                      // 32-key tiles per
 // Dense calls of at most this many keys (queries x columns) use one tile per
 // wave per sub-chunk: twice the workgroups, each lighter (measured: 128K x 8
 // queries 33.4 against 34.4 us; neutral at 2M keys, slower at 16M).
-constexpr int64_t IS_ONE_TILE_MAX_KEYS = 3 << 19;
+#ifndef CSA2_IS_ONE_TILE
+#define CSA2_IS_ONE_TILE (3 << 19)
+#endif
+constexpr int64_t IS_ONE_TILE_MAX_KEYS = CSA2_IS_ONE_TILE;
 #ifndef CSA2_IS_RESIDENT
 #define CSA2_IS_RESIDENT 768
 #endif
 constexpr int IS_RESIDENT_WGS = CSA2_IS_RESIDENT;            // about one round on 256 CUs
+#ifndef CSA2_IS_NBUF
+#define CSA2_IS_NBUF 2
+#endif
+// sub-chunk buffers per wave (measured on 64 x 256K keys: 2 buffers 469 us,
+// 3 557 us, 4 555 us -- the extra registers cost occupancy)
+constexpr int IS_NBUF = CSA2_IS_NBUF;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
@@ -240,8 +250,10 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
     }
   };
 
-  Sub A, B;
-  if (col_begin < col_end) load_sub(col_begin, A);
+  Sub buf[IS_NBUF];
+#pragma unroll
+  for (int k = 0; k + 1 < IS_NBUF; ++k)
+    if (col_begin + k * col_step < col_end) load_sub(col_begin + k * col_step, buf[k]);
 
   // A operand widened to f16; gate of head r with the q scale folded in,
   // then the 16 heads this lane's accumulators hold.
@@ -290,16 +302,19 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
     }
   };
 
-  // Stream over this workgroup's sub-chunks, double-buffered: the next
-  // sub-chunk's rows are in flight while the current one is contracted, so
-  // HBM stays busy for the whole life of the workgroup.
-  for (int c0 = col_begin; c0 < col_end; c0 += 2 * col_step) {
-    const int c1 = c0 + col_step;
-    if (c1 < col_end) load_sub(c1, B);
-    compute_sub(c0, A);
-    if (c1 >= col_end) break;
-    if (c1 + col_step < col_end) load_sub(c1 + col_step, A);
-    compute_sub(c1, B);
+  // Stream over this workgroup's sub-chunks through a ring of IS_NBUF
+  // buffers: the next IS_NBUF - 1 sub-chunks' rows are in flight while the
+  // current one is contracted, so HBM stays busy for the whole life of the
+  // workgroup.
+  for (int c0 = col_begin; c0 < col_end; c0 += IS_NBUF * col_step) {
+#pragma unroll
+    for (int ph = 0; ph < IS_NBUF; ++ph) {
+      const int cc = c0 + ph * col_step;
+      if (cc >= col_end) break;
+      const int cn = cc + (IS_NBUF - 1) * col_step;
+      if (cn < col_end) load_sub(cn, buf[(ph + IS_NBUF - 1) % IS_NBUF]);
+      compute_sub(cc, buf[ph]);
+    }
   }
 }
 
@@ -326,6 +341,12 @@ template <bool W_BF16, bool K4, bool PAGED>
 __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(IndexScoreArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t s_k[2][PF_KB * PF_RS];
   __shared__ float s_ks[2][PF_KB];
+  // Each wave's scores of the current block for its two queries, stored to
+  // memory (with their block maxima) at the start of the next block.  Stores
+  // in the block loop would otherwise be outstanding when the next block's
+  // staged rows are waited for (vector memory counters retire in order),
+  // stalling every block on the latency of its last stores.  Wave-private.
+  __shared__ __attribute__((aligned(16))) float s_out[PF_WAVES][2][PF_KB];
 
   const int t0 = blockIdx.y * PF_Q;
   const int blk0 = blockIdx.x * a.blocks_per_wg;
@@ -374,6 +395,49 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
   // staging assignment: thread -> (key kk of the block, 64-byte half hh)
   const int kk = threadIdx.x >> 1;
   const int hh = threadIdx.x & 1;
+
+  const int bshift = a.block_shift;
+  const bool vec_out = ((uintptr_t)a.scores & 15) == 0 && (a.score_stride & 3) == 0;
+  // store the staged block starting at column colb (lane: 4 consecutive
+  // columns of each active query's row), then its block maxima, taken here
+  // from the staged scores (lane: one block)
+  auto flush = [&](int colb, bool act0, bool act1) {
+    const int ncols = min(PF_KB, a.n_cols - colb);
+    const int c = 4 * lane;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      if (!(i ? act1 : act0)) continue;
+      const v4f v = *(const v4f*)&s_out[wave][i][c];
+      float* dst = a.scores + (int64_t)tq[i] * a.score_stride + colb + c;
+      if (vec_out && c + 4 <= ncols) {
+        *(v4f*)dst = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (c + e < ncols) dst[e] = v[e];
+      }
+      if (a.block_max) {
+        const int bs = 1 << bshift;
+        float* bm = a.block_max + (int64_t)tq[i] * a.block_max_stride;
+        if (bs >= 4) {
+          // the lane's 4 columns, then aligned groups of bs / 4 lanes
+          float m = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) m = fmaxf(m, (c + e < ncols) ? v[e] : -INFINITY);
+          m = group_max(m, bs >> 2);
+          if ((lane & ((bs >> 2) - 1)) == 0 && c < ncols) bm[(colb + c) >> bshift] = m;
+        } else {
+          const int nb = (ncols + bs - 1) >> bshift;
+          for (int bi = lane; bi < nb; bi += 64) {
+            const int e_end = min(bs, ncols - bi * bs);
+            float m = -INFINITY;
+            for (int e = 0; e < e_end; ++e) m = fmaxf(m, s_out[wave][i][bi * bs + e]);
+            bm[(colb >> bshift) + bi] = m;
+          }
+        }
+      }
+    }
+  };
 
   for (int pass = 0; pass < nq; ++pass) {
     // one pass per distinct sequence among the tile's queries (in order of
@@ -432,6 +496,8 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
       const int blk = blk0 + j;
       const int buf = j & 1;
       const int colb = blk * PF_KB;
+      // the previous block's results go out before this block's loads
+      if (j > 0) flush(colb - PF_KB, act[0], act[1]);
       // blocks wholly past the pass's furthest visible column are not staged
       const bool more = (j + 1 < n_blk) && (blk + 1) * PF_KB < maxvis;
       if (more) load_block(blk + 1);
@@ -474,27 +540,20 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           if (!act[i]) continue;
-          if (half == 0 && col < a.n_cols) a.scores[(int64_t)tq[i] * a.score_stride + col] = sc[i];
-          if (a.block_max) {
-            const float mx = group_max(sc[i], 1 << a.block_shift);
-            if (half == 0 && (r & ((1 << a.block_shift) - 1)) == 0 && col < a.n_cols)
-              a.block_max[(int64_t)tq[i] * a.block_max_stride + (col >> a.block_shift)] = mx;
-          }
+          if (half == 0) s_out[wave][i][tile * 32 + r] = sc[i];
         }
       }
       for (int tile = n_tiles; tile < n_col_tiles; ++tile) {
-        const int col = colb + tile * 32 + r;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          if (!act[i] || col >= a.n_cols) continue;
-          if (half == 0) a.scores[(int64_t)tq[i] * a.score_stride + col] = -INFINITY;
-          if (a.block_max && half == 0 && (r & ((1 << a.block_shift) - 1)) == 0)
-            a.block_max[(int64_t)tq[i] * a.block_max_stride + (col >> a.block_shift)] = -INFINITY;
+          if (!act[i]) continue;
+          if (half == 0) s_out[wave][i][tile * 32 + r] = -INFINITY;
         }
       }
       if (more) store_block(buf ^ 1);
       __syncthreads();
     }
+    if (n_blk > 0) flush((blk0 + n_blk - 1) * PF_KB, act[0], act[1]);
   }
 }
 

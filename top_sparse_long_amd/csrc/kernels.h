@@ -227,4 +227,8 @@ struct CacheWriteArgs {
 
 hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
 
+// Diagnostics ------------------------------------------------------------------
+// Streaming read of bytes (a multiple of 16) from src by n_blocks workgroups.
+hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, int n_blocks, hipStream_t s);
+
 }  // namespace csa2

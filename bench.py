@@ -165,13 +165,17 @@ STAGE_KERNELS = {
     "topk_blocks": ("select_kernel<5,", "select_kernel<4,"),
     "topk_and_blocks": ("select_pair_kernel", "select_kernel<0,", "select_kernel<2,", "select_kernel<3,",
                         "select_kernel<4,", "select_kernel<5,"),
-    "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_combine_kernel", "sparse_attn_f32_kernel"),
+    "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_wide_kernel", "sparse_attn_combine_kernel",
+                    "sparse_attn_f32_kernel"),
     # the 65,536-token m = 2 chunk (the decode-batch calls use the prefetching
     # variant, cache_write_kernel<m, true>, and are not part of this record)
     "cache_write": ("cache_write_kernel<2, false>", "cache_pend_kernel"),
 }
-CALIB_KERNEL = "__amd_rocclr_copyBuffer"
-CALIB_KIB = 256 * 1024          # the benchmark's calibration copy moves 256 MiB each way
+# counter calibration: the benchmark's streaming read and write of 2 GiB each
+# (csa2_diag_stream_read / _write, run by read_ceiling) move known bytes
+CALIB_READ_KERNEL = "stream_read_kernel"
+CALIB_WRITE_KERNEL = "stream_write_kernel"
+CALIB_KIB = 2 * 1024 * 1024
 
 
 def _find_csv(d, suffix):
@@ -213,14 +217,19 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, workload, comma
 
     fetch = _counter_per_kernel(_find_csv(fetch_dir, "counter_collection.csv"))
     write = _counter_per_kernel(_find_csv(write_dir, "counter_collection.csv"))
-    fscale = CALIB_KIB / max(fetch.get(CALIB_KERNEL, [CALIB_KIB]))
-    wscale = CALIB_KIB / max(write.get(CALIB_KERNEL, [CALIB_KIB]))
+    def _calib(per, pat):
+        vals = sorted(v for n, vs in per.items() if pat in n for v in vs)
+        return vals[len(vals) // 2] if vals else None
+    fraw = _calib(fetch, CALIB_READ_KERNEL)
+    wraw = _calib(write, CALIB_WRITE_KERNEL)
+    fscale = CALIB_KIB / fraw if fraw else 1.0
+    wscale = CALIB_KIB / wraw if wraw else 1.0
     lines = [f"# rocprofv3 counter summary (KiB per dispatch, averaged), workload {workload}",
              f"# commands: rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -- {command}",
              f"#           rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -- {command}",
-             f"# calibration: the {CALIB_KIB} KiB device copy reads FETCH_SIZE "
-             f"{max(fetch.get(CALIB_KERNEL, [0])):.1f} KiB -> scale {fscale:.4f}; "
-             f"WRITE_SIZE {max(write.get(CALIB_KERNEL, [0])):.1f} KiB -> scale {wscale:.4f}",
+             f"# calibration: the {CALIB_KIB} KiB streaming read reads FETCH_SIZE "
+             f"{fraw or 0:.1f} KiB -> scale {fscale:.4f}; the {CALIB_KIB} KiB streaming write "
+             f"writes WRITE_SIZE {wraw or 0:.1f} KiB -> scale {wscale:.4f} (median dispatch)",
              "# columns: dispatches, FETCH_SIZE raw, WRITE_SIZE raw, scaled HBM MB (read + write), kernel", ""]
     per_kernel_bytes = {}
     for name in sorted(set(fetch) | set(write)):
@@ -715,13 +724,29 @@ def read_ceiling(torch, tsl, gib=2, reps=10):
     ts.sort()
     t = ts[len(ts) // 2]
     gbs = src.numel() * 4 / t / 1e9
+    # the write counterpart over the same buffer
+    for _ in range(2):
+        tsl.csa2_diag_stream_write(src, 0.5)
+    torch.cuda.synchronize()
+    tw = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tsl.csa2_diag_stream_write(src, 0.5)
+        e1.record()
+        torch.cuda.synchronize()
+        tw.append(e0.elapsed_time(e1) * 1e-3)
+    tw.sort()
+    wgbs = src.numel() * 4 / tw[len(tw) // 2] / 1e9
     del src, sink
     torch.cuda.empty_cache()
     READ_CEILING["GB/s"] = gbs
     return {"kernel": "csa2_diag_stream_read", "bytes": gib << 30, "median_us": t * 1e6,
             "achieved": gbs, "unit": "GB/s", "frac_of_peak": gbs / HBM_PEAK_GBS,
-            "what": "16-byte non-temporal loads in a grid-stride loop over 2 GiB, nothing computed: "
-                    "the practical read ceiling for the HBM-bound stages"}
+            "write_achieved": wgbs, "write_kernel": "csa2_diag_stream_write",
+            "what": "16-byte non-temporal loads (stores) in a grid-stride loop over 2 GiB, nothing "
+                    "computed: the practical read ceiling for the HBM-bound stages"}
 
 
 def _roofline(stage, rec, workload):
@@ -802,14 +827,6 @@ def main():
     dev = "cuda"
     ceiling = read_ceiling(torch, tsl)
     timer = Timer(torch, 1 << 30)
-
-    # calibration copy for the counter runs (outside the timed region): a
-    # plain 256 MiB device copy whose FETCH/WRITE bytes are known
-    calib_src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
-    calib_dst = torch.empty_like(calib_src)
-    calib_dst.copy_(calib_src)
-    torch.cuda.synchronize()
-    del calib_src, calib_dst
 
     m = measure_workload(torch, synth, LayerRunner, timer, args.workload, args, args.copies,
                          args.steps, args.warmup)

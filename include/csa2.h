@@ -352,6 +352,17 @@ int csa2_diag_index_scores_fp8_mfma(const csa2_rows* q_idx, const void* w, csa2_
 int csa2_diag_stream_read(const void* src, size_t bytes, float* sink, size_t sink_floats, void* stream);
 
 /*
+ * csa2_diag_stream_write — fills bytes of dst with value (16-byte
+ * non-temporal stores, 4096 workgroups in a grid-stride loop): the write
+ * counterpart of csa2_diag_stream_read, and a write of known size for
+ * calibrating memory-traffic counters.
+ *   dst   device memory, 16-byte aligned; bytes a multiple of 16.
+ *   Errors: CSA2_ERR_INVALID_ARG for null or misaligned arguments;
+ *   CSA2_ERR_HIP if the launch fails.
+ */
+int csa2_diag_stream_write(void* dst, size_t bytes, float value, void* stream);
+
+/*
  * csa2_sparse_attn — core sparse attention ([CSA2] "per-layer attention
  * computation"; [3MODES] Q&A on Reuse layers).  For query t at position p of
  * sequence b and head i, the keys are the SWA rows of positions

@@ -195,7 +195,7 @@ def test_topk_from_block_max_rejects():
     assert f(FAKE, n, n, FAKE, nb, FAKE, 1, 8, k, FAKE, None, 0, 0, None, None) == tsl.CSA2_OK
 
 
-def test_diag_stream_read_rejects():
+def test_diag_stream_read_and_write_reject():
     lib = tsl.load()
     f = lib.csa2_diag_stream_read
     assert f(None, 1024, FAKE, 16, None) == tsl.CSA2_ERR_INVALID_ARG
@@ -205,6 +205,11 @@ def test_diag_stream_read_rejects():
     assert f(FAKE, 1024, FAKE, 0, None) == tsl.CSA2_ERR_INVALID_ARG
     # nothing to read: nothing is enqueued
     assert f(FAKE, 0, FAKE, 16, None) == tsl.CSA2_OK
+    w = lib.csa2_diag_stream_write
+    assert w(None, 1024, 0.0, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert w(FAKE + 8, 1024, 0.0, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert w(FAKE, 1000, 0.0, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert w(FAKE, 0, 0.0, None) == tsl.CSA2_OK
 
 
 def test_topk_and_block_candidates_noalloc_rejects_sizes_past_the_scratch():

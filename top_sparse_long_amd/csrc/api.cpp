@@ -224,6 +224,16 @@ int csa2_diag_stream_read(const void* src, size_t bytes, float* sink, size_t sin
                     "csa2_diag_stream_read");
 }
 
+int csa2_diag_stream_write(void* dst, size_t bytes, float value, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(dst, CSA2_ERR_INVALID_ARG, "csa2_diag_stream_write: null pointer argument");
+  REQUIRE(aligned(dst, 16) && bytes % 16 == 0, CSA2_ERR_INVALID_ARG,
+          "csa2_diag_stream_write: dst must be 16-byte aligned and bytes a multiple of 16");
+  if (bytes == 0) return CSA2_OK;
+  return hip_status(csa2::launch_stream_write(dst, bytes, value, 4096, (hipStream_t)stream),
+                    "csa2_diag_stream_write");
+}
+
 size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k) {
   if (Q <= 0 || n_cols <= 0 || k <= 0) return 0;
   return csa2::select_workspace_bytes(Q, n_cols, k);

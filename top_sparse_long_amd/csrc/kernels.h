@@ -230,5 +230,7 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
 // Diagnostics ------------------------------------------------------------------
 // Streaming read of bytes (a multiple of 16) from src by n_blocks workgroups.
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, int n_blocks, hipStream_t s);
+// Fill of bytes (a multiple of 16) at dst with value by n_blocks workgroups.
+hipError_t launch_stream_write(void* dst, size_t bytes, float value, int n_blocks, hipStream_t s);
 
 }  // namespace csa2

@@ -68,6 +68,12 @@ def _parse():
     ap.add_argument("--summarize-mfma", nargs=3, metavar=("MFMA_DIR", "TRACE_DIR", "OUT_DIR"),
                     help="no GPU: summarize a rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
                          "SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU run of this benchmark")
+    ap.add_argument("--stage-only", default=None, metavar="STAGE",
+                    help="run one full step, then only the calls of STAGE (e.g. sparse_attn) "
+                         "--repeat times, and exit: a short target for counter runs")
+    ap.add_argument("--repeat", type=int, default=10)
+    ap.add_argument("--summarize-sq", nargs="+", metavar="PATH",
+                    help="no GPU: OUT_FILE then rocprofv3 --pmc output dirs of SQ counters")
     ap.add_argument("--profile-command", default="",
                     help="the benchmark command the profiles were taken on (recorded in the summaries)")
     return ap.parse_args()
@@ -303,6 +309,42 @@ def summarize_mfma(mfma_dir, trace_dir, out_dir, workload, command):
         lines.append(f"{len(d.get('GRBM_GUI_ACTIVE', [])):6d} {util:7.1f} {tf:9.1f} {tf / F16_PEAK_TFLOPS:7.3f} "
                      f"{mean.get('SQ_INSTS_VALU', 0.0):14.0f}  {name}")
     with open(os.path.join(out_dir, f"mfma_{workload}.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_sq(dirs, out_path, workload, stage, commands):
+    """Write a per-kernel table of SQ counters (averaged per dispatch) from
+    one or more rocprofv3 --pmc runs, with derived shares of the SIMD time."""
+    import csv
+    per = {}
+    for d in dirs:
+        for row in csv.DictReader(open(_find_csv(d, "counter_collection.csv"))):
+            if "csa2::" not in row["Kernel_Name"]:
+                continue
+            per.setdefault(row["Kernel_Name"], {}).setdefault(row["Counter_Name"], []).append(
+                float(row["Counter_Value"]))
+    lines = [f"# rocprofv3 SQ counters, workload {workload}, stage {stage} (values per dispatch)"]
+    lines += [f"# command: {c}" for c in commands]
+    lines += ["# derived: SIMD-cycles = GRBM_GUI_ACTIVE / 8 XCDs * 1024 SIMDs;",
+              "#   mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / SIMD-cycles;",
+              "#   valu_issue = 4 * SQ_ACTIVE_INST_VALU / SIMD-cycles (quad-cycles);",
+              "#   wave_wait = SQ_WAIT_ANY / SQ_WAVE_CYCLES", ""]
+    for name, d in sorted(per.items()):
+        mean = {k: sum(v) / len(v) for k, v in d.items()}
+        lines.append(name)
+        for k in sorted(mean):
+            lines.append(f"    {k:28s} {mean[k]:.4g}")
+        gui = mean.get("GRBM_GUI_ACTIVE")
+        if gui:
+            simd = gui / 8.0 * N_SIMD
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                lines.append(f"    mfma_busy                    {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / simd:.3f}")
+            if "SQ_ACTIVE_INST_VALU" in mean:
+                lines.append(f"    valu_issue                   {4 * mean['SQ_ACTIVE_INST_VALU'] / simd:.3f}")
+        if mean.get("SQ_WAVE_CYCLES") and "SQ_WAIT_ANY" in mean:
+            lines.append(f"    wave_wait                    {mean['SQ_WAIT_ANY'] / mean['SQ_WAVE_CYCLES']:.3f}")
+        lines.append("")
+    with open(out_path, "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -814,6 +856,11 @@ def main():
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma, args.workload, args.profile_command)
         return
+    if args.summarize_sq:
+        out_path, *dirs = args.summarize_sq
+        summarize_sq(dirs, out_path, args.workload, args.stage_only or "-",
+                     args.profile_command.split(" ;; "))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); sharding the path "
               "over several GPUs is designed, not built or measured.", file=sys.stderr)
@@ -825,6 +872,23 @@ def main():
 
     tsl.load()
     dev = "cuda"
+    if args.stage_only:
+        run = LayerRunner(synth.make_workload(args.workload, device=dev))
+        steps = run.steps()
+        for _, fn in steps:
+            fn()
+        calls = [fn for name, fn in steps if name == args.stage_only]
+        if not calls:
+            print(f"no stage {args.stage_only!r} in {args.workload}: "
+                  f"{sorted(set(n for n, _ in steps))}", file=sys.stderr)
+            sys.exit(2)
+        for _ in range(args.repeat):
+            for fn in calls:
+                fn()
+        torch.cuda.synchronize()
+        print(json.dumps({"workload": args.workload, "stage": args.stage_only,
+                          "calls": args.repeat * len(calls)}), flush=True)
+        return
     ceiling = read_ceiling(torch, tsl)
     timer = Timer(torch, 1 << 30)
 

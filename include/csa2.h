@@ -366,7 +366,8 @@ int csa2_diag_stream_write(void* dst, size_t bytes, float value, void* stream);
  * csa2_sparse_attn — core sparse attention ([CSA2] "per-layer attention
  * computation"; [3MODES] Q&A on Reuse layers).  For query t at position p of
  * sequence b and head i, the keys are the SWA rows of positions
- * [max(lo_b, p - window + 1), p] (oldest first) followed by the main rows
+ * [max(lo_b, swa_pos0[b], p - window + 1, 0), p] (oldest first) followed
+ * by the main rows
  * idx[t, j] >= 0; K = V (MQA, one 512-dim vector per key).  With
  * z_j = softmax_scale * q[t, i] . K_j:
  *   out[t, i] = sum_j exp(z_j) K_j / (sum_j exp(z_j) + exp(attn_sink[i]))
@@ -408,6 +409,13 @@ int csa2_diag_stream_write(void* dst, size_t bytes, float value, void* stream);
  *   Supported: D = 512; H a multiple of 16 up to 128; k <= 2048.
  *   Quantized path: q BF16, main FP4_E2M1, swa FP8_E4M3, out BF16 or F32.
  *   Float path: q, main, swa F32, out F32.
+ *   Precision of the quantized path: q is converted from bf16 to f16 for the
+ *   matrix cores, exactly for |q| in f16's normal range [2^-14, 65504];
+ *   smaller magnitudes keep f16's subnormal precision (2^-24 absolute), and
+ *   larger ones overflow to infinity, so q entries must stay below 65504 in
+ *   magnitude (scale q, not softmax_scale, to meet this).  Dequantized keys
+ *   are code x scale rounded once to f16 (exact for the 288-byte records);
+ *   probabilities are f16 below 2^8; all sums are fp32.
  */
 typedef struct {
     /* NULL, or fp32 [n_rope, 64]: row r holds cos of the 32 RoPE angles of

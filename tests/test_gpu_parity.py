@@ -359,6 +359,63 @@ def test_topk_from_block_max_exact(n_cols, k, ratio, levels, bs):
     assert np.array_equal(_np(idx), oracle.topk_rows_dense(sc.astype(np.float64), q_pos, ratio, k))
 
 
+def test_selections_many_rows():
+    """Grids of 1,100 rows take the 256-thread selection form for chunks of at
+    most 4,096 entries: the dense top-k, the pool top-k, block candidates and
+    the top-k through block maxima all equal the oracle bit for bit."""
+    _announce("selections over 1,100 rows")
+    rng = np.random.default_rng(1100)
+    Q, n, bs, k = 1100, 4099, 8, 512
+    sc = _tie_scores(rng, Q, n, 20)
+    q_pos = rng.integers(0, n + 300, size=Q).astype(np.int32)   # ragged, some rows all visible
+    q_pos[:5] = [0, 1, 510, 511, n - 1]
+    sc64 = sc.astype(np.float64)
+    dev = torch.full((Q, 4160), float("nan"), device=DEV)   # row stride a multiple of 4
+    dev[:, :n] = torch.from_numpy(sc).to(DEV)
+    qp = torch.from_numpy(q_pos).to(DEV)
+    ref = oracle.topk_rows_dense(sc64, q_pos, 1, k)
+    # the dense top-k of rows of 4,000 (one 4,096-entry chunk each)
+    nd = 4000
+    idx = torch.full((Q, k), -7, dtype=torch.int32, device=DEV)
+    ws = torch.empty((max(16, tsl.csa2_topk_workspace_size(Q, nd, k)),), dtype=torch.uint8, device=DEV)
+    tsl.csa2_topk(dev, nd, qp, 1, k, idx, ws, Q)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(idx), oracle.topk_rows_dense(sc64[:, :nd], q_pos, 1, k))
+    # block maxima of the visible prefixes, then the block route
+    nb = -(-n // bs)
+    nvis = oracle.visible_count(q_pos, 1)
+    host = np.full((Q, nb), -np.inf)
+    for t in range(Q):
+        m = oracle.block_maxima(sc64[t], int(min(nvis[t], n)), bs)
+        host[t, :len(m)] = m
+    bm = torch.from_numpy(host.astype(np.float32)).to(DEV)
+    idx2 = torch.full((Q, k), -7, dtype=torch.int32, device=DEV)
+    ws2 = torch.randint(0, 255, (max(16, tsl.csa2_topk_from_block_max_workspace_size(Q, n, k, bs)),),
+                        dtype=torch.uint8, device=DEV)
+    tsl.csa2_topk_from_block_max(dev, n, bm, qp, 1, bs, k, idx2, ws2, Q)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(idx2), ref)
+    # block candidates (256 of at most 513 blocks, latest forced)
+    cand = torch.empty((Q, 256), dtype=torch.int32, device=DEV)
+    wsb = torch.empty((max(16, tsl.csa2_block_candidates_workspace_size(Q, n, bs, 256)),),
+                      dtype=torch.uint8, device=DEV)
+    tsl.csa2_block_candidates(dev, n, qp, 1, bs, 256, cand, wsb, Q)
+    torch.cuda.synchronize()
+    cref = oracle.block_candidates(sc64, q_pos, 1, bs, 256)
+    assert np.array_equal(_np(cand), cref)
+    # pool top-k over 512 candidate blocks of 8 (4,096 pool entries per row)
+    pc = np.full((Q, 512), -1, dtype=np.int32)
+    for t in range(Q):
+        m = int(rng.integers(0, 513))
+        pc[t, :m] = np.sort(rng.choice(100000, m, replace=False))
+    psc = _tie_scores(rng, Q, 512 * bs, 20)
+    pidx = torch.empty((Q, k), dtype=torch.int32, device=DEV)
+    tsl.csa2_topk(torch.from_numpy(psc).to(DEV), 512 * bs, None, 1, k, pidx, None, Q,
+                  cand=torch.from_numpy(pc).to(DEV), block_size=bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(pidx), oracle.topk_rows_pool(psc.astype(np.float64), pc, bs, k))
+
+
 # ---------------------------------------------------------------------------
 # attention: the oracle runs on the same indices
 

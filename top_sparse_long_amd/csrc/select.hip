@@ -30,8 +30,16 @@
 
 namespace csa2 {
 
-constexpr int SEL_THREADS = 1024;
-constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_THREADS = 1024;   // threads of a workgroup
+// Stages over chunks of at most 4,096 entries with many workgroups run 256
+// threads (16 entries each, as a 16,384-entry chunk has with 1,024): four
+// waves per barrier instead of sixteen, and several workgroups per CU to hide
+// each one's latency chains (the m = 2 chunk's block-route top-k: 118 ->
+// 82 us).  Small grids keep 1,024 threads, whose shorter per-thread work
+// is what sets their latency (the 8-query decode selections were 1-2 us
+// slower with 256).
+constexpr int SEL_SMALL_THREADS = 256;
+constexpr int SEL_SMALL_MIN_WGS = 1024;   // grids at least this large use them
 constexpr int SEL_BATCH = 8;               // loads in flight per thread
 constexpr uint32_t KEY_NEG_INF = 0x007FFFFFu;  // key of -inf: selectable keys are larger
 constexpr uint32_t KEY_POS_INF = 0xFF800000u;  // key of +inf (the forced latest block)
@@ -98,7 +106,8 @@ __device__ __forceinline__ int lanes_below(uint64_t mask, int lane) {
   return __popcll(mask & ((1ull << lane) - 1ull));
 }
 
-// Block-wide exclusive scan of one value per thread (1024 threads).
+// Block-wide exclusive scan of one value per thread (NT threads).
+template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, int lane, int wave,
                                                     uint32_t* s_wsum, uint32_t* total) {
   uint32_t incl = wave_incl_scan(x, lane);
@@ -106,7 +115,7 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, int lane, int wa
   __syncthreads();
   uint32_t before = 0, all = 0;
 #pragma unroll
-  for (int w = 0; w < SEL_WAVES; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const uint32_t v = s_wsum[w];
     before += (w < wave) ? v : 0u;
     all += v;
@@ -118,18 +127,18 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, int lane, int wa
 // LDS bytes of one selection body of capacity CAP: the radix histogram
 // shares its bytes with the transpose buffer (the two are never live at the
 // same time), then the scan partials and the threshold words.
-template <int CAP>
+template <int CAP, int NT>
 struct SelSmem {
   static constexpr int HIST = (256 * 16 + 256) * 4;
-  static constexpr int TR = (CAP + 4 * SEL_THREADS) * 4;
+  static constexpr int TR = (CAP + 4 * NT) * 4;
   static constexpr int WSUM = 16 * 4;
   static constexpr int BODY = HIST > TR ? HIST : TR;
   static constexpr int BYTES = BODY + WSUM + 16;
 };
 
-template <int MODE, int CAP>
+template <int MODE, int CAP, int NT>
 __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, uint8_t* smem) {
-  constexpr int EMAX = CAP / SEL_THREADS;   // entries per thread at most
+  constexpr int EMAX = CAP / NT;   // entries per thread at most
   constexpr int NAUX = (MODE == SEL_POOL || MODE == SEL_LIST || MODE == SEL_GATHER) ? EMAX : 1;
   // first digit: 16 interleaved copies of the 256-bin histogram (bin b,
   // copy c at 16 b + c), so lanes that hit the same bin land on 16 different
@@ -138,8 +147,8 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
   // transpose buffer: entry p of the chunk at p + 4 (p / EMAX), so that each
   // thread's EMAX consecutive entries start on a different bank group
   uint32_t* s_tr = (uint32_t*)smem;   // same bytes as s_hist
-  uint32_t* s_wsum = (uint32_t*)(smem + SelSmem<CAP>::BODY);
-  uint32_t& s_bucket = *(uint32_t*)(smem + SelSmem<CAP>::BODY + SelSmem<CAP>::WSUM);
+  uint32_t* s_wsum = (uint32_t*)(smem + SelSmem<CAP, NT>::BODY);
+  uint32_t& s_bucket = *(uint32_t*)(smem + SelSmem<CAP, NT>::BODY + SelSmem<CAP, NT>::WSUM);
   uint32_t& s_above = (&s_bucket)[1];
   uint32_t& s_bcnt = (&s_bucket)[2];
 
@@ -153,7 +162,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
   const int count = (int)max((int64_t)0, min((int64_t)a.chunk, L - g0));
   const float* row = s.scores + (int64_t)t * s.score_stride;
 
-  // Striped ownership: entry j * SEL_THREADS + tid of the chunk is this
+  // Striped ownership: entry j * NT + tid of the chunk is this
   // thread's j-th key, so every load instruction reads consecutive addresses.
   // Loads are unconditional, from indices clamped into the chunk, and masked
   // afterwards, so they are all in flight together.
@@ -164,18 +173,18 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
     if (MODE == SEL_DENSE || MODE == SEL_POOL) {
       float v[EMAX];
 #pragma unroll
-      for (int j = 0; j < EMAX; ++j) v[j] = row[g0 + min(j * SEL_THREADS + tid, last)];
+      for (int j = 0; j < EMAX; ++j) v[j] = row[g0 + min(j * NT + tid, last)];
       if (MODE == SEL_POOL) {
 #pragma unroll
         for (int j = 0; j < EMAX; ++j) {
-          const int64_t g = g0 + min(j * SEL_THREADS + tid, last);
+          const int64_t g = g0 + min(j * NT + tid, last);
           aux[j % NAUX] =
               s.cand[(int64_t)t * s.n_cand_blocks + (int)(g >> s.block_shift)];
         }
       }
 #pragma unroll
       for (int j = 0; j < EMAX; ++j) {
-        const bool in = j * SEL_THREADS + tid < count;
+        const bool in = j * NT + tid < count;
         uint32_t kk = in ? float_key(v[j]) : KEY_PAD;
         if (MODE == SEL_POOL && in && aux[j % NAUX] < 0)
           kk = KEY_NEG_INF;
@@ -186,12 +195,12 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
       const int32_t* ip = a.in_pos + (int64_t)t * a.in_len + g0;
 #pragma unroll
       for (int j = 0; j < EMAX; ++j) {
-        key[j] = ik[min(j * SEL_THREADS + tid, last)];
-        aux[j % NAUX] = ip[min(j * SEL_THREADS + tid, last)];
+        key[j] = ik[min(j * NT + tid, last)];
+        aux[j % NAUX] = ip[min(j * NT + tid, last)];
       }
 #pragma unroll
       for (int j = 0; j < EMAX; ++j)
-        if (j * SEL_THREADS + tid >= count) key[j] = KEY_PAD;
+        if (j * NT + tid >= count) key[j] = KEY_PAD;
     } else if (MODE == SEL_GATHER) {
       // entry e is score (block << shift) + (e % block_size) of list block
       // e / block_size (block -1: nothing); positions past the row or the
@@ -201,18 +210,18 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
       const int nv = min(s.n_cols, sel_visible(s, t));
       int32_t blk[EMAX];
 #pragma unroll
-      for (int j = 0; j < EMAX; ++j) blk[j] = ib[(g0 + min(j * SEL_THREADS + tid, last)) >> s.block_shift];
+      for (int j = 0; j < EMAX; ++j) blk[j] = ib[(g0 + min(j * NT + tid, last)) >> s.block_shift];
       float v[EMAX];
 #pragma unroll
       for (int j = 0; j < EMAX; ++j) {
-        const int e = (int)(g0 + min(j * SEL_THREADS + tid, last));
+        const int e = (int)(g0 + min(j * NT + tid, last));
         const int p = blk[j] >= 0 ? (blk[j] << s.block_shift) + (e & (bs - 1)) : -1;
         aux[j] = (p >= 0 && p < nv) ? p : -1;
         v[j] = row[max(aux[j], 0)];
       }
 #pragma unroll
       for (int j = 0; j < EMAX; ++j) {
-        const bool in = j * SEL_THREADS + tid < count;
+        const bool in = j * NT + tid < count;
         key[j] = !in ? KEY_PAD : (aux[j] >= 0 ? float_key(v[j]) : KEY_NEG_INF);
       }
     } else {   // SEL_BLOCKMAX, SEL_BLOCKTOP
@@ -225,12 +234,12 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
       if (s.block_max) {
 #pragma unroll
         for (int j = 0; j < EMAX; ++j)
-          m[j] = s.block_max[(int64_t)t * s.block_max_stride + min(g0 + min(j * SEL_THREADS + tid, last), lim)];
+          m[j] = s.block_max[(int64_t)t * s.block_max_stride + min(g0 + min(j * NT + tid, last), lim)];
       } else if (L >= (FORCE ? 2 : 1)) {
         const int bs = 1 << s.block_shift;
 #pragma unroll
         for (int j = 0; j < EMAX; ++j) {
-          const float* src = row + (min(g0 + min(j * SEL_THREADS + tid, last), lim) << s.block_shift);
+          const float* src = row + (min(g0 + min(j * NT + tid, last), lim) << s.block_shift);
           float mm = -INFINITY;
           if (bs >= 4) {
             for (int p = 0; p < bs; p += 4) {
@@ -248,7 +257,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
       }
 #pragma unroll
       for (int j = 0; j < EMAX; ++j) {
-        const int i = j * SEL_THREADS + tid;
+        const int i = j * NT + tid;
         uint32_t kk = KEY_PAD;
         // the block of the latest visible position is always kept (unless
         // every block is ranked by its maximum)
@@ -267,7 +276,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
   {
 #pragma unroll
     for (int j = 0; j < EMAX; ++j) {
-      const int pe = j * SEL_THREADS + tid;
+      const int pe = j * NT + tid;
       s_tr[pe + 4 * (pe / EMAX)] = key[j];
     }
     __syncthreads();
@@ -284,7 +293,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
       __syncthreads();
 #pragma unroll
       for (int j = 0; j < EMAX; ++j) {
-        const int pe = j * SEL_THREADS + tid;
+        const int pe = j * NT + tid;
         s_tr[pe + 4 * (pe / EMAX)] = (uint32_t)aux[j % NAUX];
       }
       __syncthreads();
@@ -319,7 +328,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
     uint32_t& s_all = (&s_bucket)[3];
     __syncthreads();   // the transposed entries have been read: s_tr becomes the histogram
     uint32_t* s_hist1 = s_hist + 256 * 16;
-    for (int i = tid; i < 256 * 16 + 256; i += SEL_THREADS) s_hist[i] = 0;
+    for (int i = tid; i < 256 * 16 + 256; i += NT) s_hist[i] = 0;
     __syncthreads();
     uint32_t prefix = 0, mask = 0, krem = (uint32_t)k;
     for (int shift = 24; shift >= 0; shift -= 8) {
@@ -411,7 +420,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
     ce += (key[j] == T && my0 + j < count) ? 1u : 0u;
   }
   uint32_t tot_packed;
-  const uint32_t ex = block_excl_scan(cg | (ce << 16), lane, wave, s_wsum, &tot_packed);
+  const uint32_t ex = block_excl_scan<NT>(cg | (ce << 16), lane, wave, s_wsum, &tot_packed);
   const uint32_t total = (tot_packed & 0xFFFFu) + min(tot_packed >> 16, keq);
   uint32_t rg = ex & 0xFFFFu, re = ex >> 16;
 #pragma unroll
@@ -444,7 +453,7 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
     re += eq ? 1u : 0u;
   }
   // padding
-  for (int q = (int)total + tid; q < k; q += SEL_THREADS) {
+  for (int q = (int)total + tid; q < k; q += NT) {
     if (a.out_key) {
       const int64_t off = (int64_t)t * a.out_stride + (int64_t)c * k + q;
       a.out_key[off] = KEY_PAD;
@@ -459,15 +468,15 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
     // positions through the page table: every row's page lookups are
     // issued together, then the slots are written in order
     __syncthreads();
-    for (int q = tid; q < k; q += SEL_THREADS)
+    for (int q = tid; q < k; q += NT)
       s.out_idx[(int64_t)t * k + q] = out_slot(s, t, (int32_t)s_tr[q]);
   }
 }
 
-template <int MODE, int CAP>
-__global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SelSmem<CAP>::BYTES];
-  select_body<MODE, CAP>(a, blockIdx.x, blockIdx.y, smem);
+template <int MODE, int CAP, int NT>
+__global__ __launch_bounds__(NT) void select_kernel(StageArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SelSmem<CAP, NT>::BYTES];
+  select_body<MODE, CAP, NT>(a, blockIdx.x, blockIdx.y, smem);
 }
 
 // Two independent selections over the same queries in one launch (the
@@ -475,12 +484,13 @@ __global__ __launch_bounds__(SEL_THREADS) void select_kernel(StageArgs a) {
 // one LDS buffer sized for the larger of the two.
 template <int M1, int C1, int M2, int C2>
 __global__ __launch_bounds__(SEL_THREADS) void select_pair_kernel(StageArgs a1, StageArgs a2, int n1) {
-  constexpr int B1 = SelSmem<C1>::BYTES, B2 = SelSmem<C2>::BYTES;
+  constexpr int NT = SEL_THREADS;
+  constexpr int B1 = SelSmem<C1, NT>::BYTES, B2 = SelSmem<C2, NT>::BYTES;
   __shared__ __attribute__((aligned(16))) uint8_t smem[B1 > B2 ? B1 : B2];
   if ((int)blockIdx.x < n1)
-    select_body<M1, C1>(a1, blockIdx.x, blockIdx.y, smem);
+    select_body<M1, C1, NT>(a1, blockIdx.x, blockIdx.y, smem);
   else
-    select_body<M2, C2>(a2, blockIdx.x - n1, blockIdx.y, smem);
+    select_body<M2, C2, NT>(a2, blockIdx.x - n1, blockIdx.y, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -567,12 +577,15 @@ static int fit_cap(int64_t n) {
 template <int MODE>
 static hipError_t launch_stage(const StageArgs& a, int cap, int nchunks, int Q, hipStream_t s) {
   const dim3 grid(nchunks, Q), block(SEL_THREADS);
-  if (cap <= 4096)
-    hipLaunchKernelGGL((select_kernel<MODE, 4096>), grid, block, 0, s, a);
+  if (cap <= 4096 && (int64_t)nchunks * Q >= SEL_SMALL_MIN_WGS)
+    hipLaunchKernelGGL((select_kernel<MODE, 4096, SEL_SMALL_THREADS>), grid, dim3(SEL_SMALL_THREADS), 0, s, a);
+  else if (cap <= 4096)
+    hipLaunchKernelGGL((select_kernel<MODE, 4096, SEL_THREADS>), grid, block, 0, s, a);
   else if (MODE == SEL_LIST || cap <= 16384)   // list stages hold at most SEL_CAP_LIST
-    hipLaunchKernelGGL((select_kernel<MODE, 16384>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((select_kernel<MODE, 16384, SEL_THREADS>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((select_kernel<MODE, (MODE == SEL_LIST ? 16384 : SEL_CAP)>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((select_kernel<MODE, (MODE == SEL_LIST ? 16384 : SEL_CAP), SEL_THREADS>), grid, block, 0,
+                       s, a);
   return hipGetLastError();
 }
 

@@ -1132,23 +1132,25 @@ static_assert(ATTN_COMBINE_THREADS * ATTN_COMBINE_PARTS * 4 == AT_HEADS * AT_D &
               ATTN_COMBINE_THREADS % 64 == 0 && ATTN_COMBINE_THREADS <= 1024,
               "one 4-column group per thread");
 
+// NS = the number of splits (compiled per count, so a thread issues exactly
+// one record read per split).
+template <int NS>
 __global__ __launch_bounds__(ATTN_COMBINE_THREADS) void sparse_attn_combine_kernel(AttnArgs a) {
   const int n_hg = a.H / AT_HEADS;
   const int tg = blockIdx.x / ATTN_COMBINE_PARTS;
   const int e0 = (blockIdx.x % ATTN_COMBINE_PARTS) * (AT_HEADS * AT_D / ATTN_COMBINE_PARTS);
   const int t = tg / n_hg;
   const int h0 = (tg - t * n_hg) * AT_HEADS;
-  const float* rec0 = a.part + (int64_t)tg * a.n_split * ATTN_PART_FLOATS;
-  const int last = a.n_split - 1;
-  float4 x[1][ATTN_MAX_SPLIT];
-  float ms[1][ATTN_MAX_SPLIT], ls[1][ATTN_MAX_SPLIT];
+  const float* rec0 = a.part + (int64_t)tg * NS * ATTN_PART_FLOATS;
+  float4 x[1][NS];
+  float ms[1][NS], ls[1][NS];
 #pragma unroll
   for (int i = 0; i < 1; ++i) {
     const int e = e0 + threadIdx.x * 4;
     const int h = e / AT_D;
 #pragma unroll
-    for (int sp = 0; sp < ATTN_MAX_SPLIT; ++sp) {
-      const float* rec = rec0 + min(sp, last) * ATTN_PART_FLOATS;
+    for (int sp = 0; sp < NS; ++sp) {
+      const float* rec = rec0 + sp * ATTN_PART_FLOATS;
       x[i][sp] = *(const float4*)(rec + 32 + e);
       ms[i][sp] = rec[h];
       ls[i][sp] = rec[16 + h];
@@ -1165,19 +1167,18 @@ __global__ __launch_bounds__(ATTN_COMBINE_THREADS) void sparse_attn_combine_kern
     const float sink2 = a.sink[h0 + h] * LOG2E;
     float M = sink2;
 #pragma unroll
-    for (int sp = 0; sp < ATTN_MAX_SPLIT; ++sp)
-      if (sp <= last) M = fmaxf(M, ms[i][sp]);
+    for (int sp = 0; sp < NS; ++sp) M = fmaxf(M, ms[i][sp]);
     float den = (M == -INFINITY) ? 0.f : exp2f(sink2 - M);
-    float f[ATTN_MAX_SPLIT];
+    float f[NS];
 #pragma unroll
-    for (int sp = 0; sp < ATTN_MAX_SPLIT; ++sp) {
-      f[sp] = (sp > last || ms[i][sp] == -INFINITY) ? 0.f : exp2f(ms[i][sp] - M);
+    for (int sp = 0; sp < NS; ++sp) {
+      f[sp] = (ms[i][sp] == -INFINITY) ? 0.f : exp2f(ms[i][sp] - M);
       den += ls[i][sp] * f[sp];
     }
     const float inv = (den > 0.f) ? 1.f / den : 0.f;
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int sp = 0; sp < ATTN_MAX_SPLIT; ++sp) {
+    for (int sp = 0; sp < NS; ++sp) {
       const float fs = f[sp] * inv;
       v.x += x[i][sp].x * fs;
       v.y += x[i][sp].y * fs;
@@ -1200,6 +1201,24 @@ __global__ __launch_bounds__(ATTN_COMBINE_THREADS) void sparse_attn_combine_kern
       *(float4*)((float*)a.out + obase + e) = v;
     }
   }
+}
+
+template <int NS>
+static void launch_combine_n(const AttnArgs& a, int groups, hipStream_t s) {
+  hipLaunchKernelGGL((sparse_attn_combine_kernel<NS>), dim3(groups * ATTN_COMBINE_PARTS),
+                     dim3(ATTN_COMBINE_THREADS), 0, s, a);
+}
+
+template <int NS>
+static void launch_combine_upto(const AttnArgs& a, int groups, hipStream_t s) {
+  if constexpr (NS >= 2) {
+    if (a.n_split == NS) launch_combine_n<NS>(a, groups, s);
+    else launch_combine_upto<NS - 1>(a, groups, s);
+  }
+}
+
+static void launch_combine(const AttnArgs& a, int groups, hipStream_t s) {
+  launch_combine_upto<ATTN_MAX_SPLIT>(a, groups, s);
 }
 
 // Key splits per (query, 16 heads): only when the batch leaves most of the
@@ -1231,8 +1250,7 @@ hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s) {
     if (a.n_split > 1) {
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
-      hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3(groups * ATTN_COMBINE_PARTS),
-                         dim3(ATTN_COMBINE_THREADS), 0, s, a);
+      launch_combine(a, groups, s);
     }
     return hipGetLastError();
   }
@@ -1249,8 +1267,7 @@ hipError_t launch_sparse_attn_quant(const AttnArgs& a, hipStream_t s) {
   if (a.n_split > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sparse_attn_combine_kernel, dim3(groups * ATTN_COMBINE_PARTS),
-                       dim3(ATTN_COMBINE_THREADS), 0, s, a);
+    launch_combine(a, groups, s);
   }
   return hipGetLastError();
 }

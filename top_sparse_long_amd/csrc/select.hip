@@ -402,9 +402,11 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
     }
   }
 
-  // a final top-k through a page table stages its positions in the (now
-  // free) transpose buffer and translates them in one pass at the end
-  const bool stage_out = !a.out_key && s.page_table != nullptr;
+  // The output is staged in the (now free) transpose buffer -- positions at
+  // [0, k), and for a list output the keys at [0, k) and positions at
+  // [k, 2k) -- and written in order after one barrier: coalesced stores
+  // instead of one sparsely active store instruction per held entry, and a
+  // final top-k through a page table issues all of its lookups together.
 
   // order-preserving compaction ----------------------------------------------
   // Thread tid holds positions [EMAX tid, +EMAX) in order.  One block scan of
@@ -440,13 +442,10 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
         pos = aux[j % NAUX];
       }
       if (a.out_key) {
-        const int64_t off = (int64_t)t * a.out_stride + (int64_t)c * k + o;
-        a.out_key[off] = key[j];
-        a.out_pos[off] = pos;
-      } else if (stage_out) {
-        s_tr[o] = (uint32_t)pos;
+        s_tr[o] = key[j];
+        s_tr[k + o] = (uint32_t)pos;
       } else {
-        s.out_idx[(int64_t)t * k + o] = pos;
+        s_tr[o] = (uint32_t)pos;
       }
     }
     rg += gt ? 1u : 0u;
@@ -455,21 +454,24 @@ __device__ __forceinline__ void select_body(const StageArgs& a, int c, int t, ui
   // padding
   for (int q = (int)total + tid; q < k; q += NT) {
     if (a.out_key) {
-      const int64_t off = (int64_t)t * a.out_stride + (int64_t)c * k + q;
-      a.out_key[off] = KEY_PAD;
-      a.out_pos[off] = -1;
-    } else if (stage_out) {
-      s_tr[q] = 0xFFFFFFFFu;
+      s_tr[q] = KEY_PAD;
+      s_tr[k + q] = 0xFFFFFFFFu;
     } else {
-      s.out_idx[(int64_t)t * k + q] = -1;
+      s_tr[q] = 0xFFFFFFFFu;
     }
   }
-  if (stage_out) {
-    // positions through the page table: every row's page lookups are
-    // issued together, then the slots are written in order
-    __syncthreads();
+  __syncthreads();
+  if (a.out_key) {
+    const int64_t off = (int64_t)t * a.out_stride + (int64_t)c * k;
+    for (int q = tid; q < k; q += NT) {
+      a.out_key[off + q] = s_tr[q];
+      a.out_pos[off + q] = (int32_t)s_tr[k + q];
+    }
+  } else if (s.page_table) {
     for (int q = tid; q < k; q += NT)
       s.out_idx[(int64_t)t * k + q] = out_slot(s, t, (int32_t)s_tr[q]);
+  } else {
+    for (int q = tid; q < k; q += NT) s.out_idx[(int64_t)t * k + q] = (int32_t)s_tr[q];
   }
 }
 
@@ -576,6 +578,11 @@ static int fit_cap(int64_t n) {
 
 template <int MODE>
 static hipError_t launch_stage(const StageArgs& a, int cap, int nchunks, int Q, hipStream_t s) {
+  // the staged output (k positions, or k keys and k positions for a list)
+  // must fit the transpose buffer of the capacity that runs: at least
+  // CAP + 4 * threads entries (the planner keeps a list's chunk >= 4 k)
+  const int64_t staged = a.out_key ? 2 * (int64_t)a.s.k : (int64_t)a.s.k;
+  if (staged > (int64_t)(cap <= 4096 ? 4096 : cap) + 4 * SEL_SMALL_THREADS) return hipErrorInvalidValue;
   const dim3 grid(nchunks, Q), block(SEL_THREADS);
   if (cap <= 4096 && (int64_t)nchunks * Q >= SEL_SMALL_MIN_WGS)
     hipLaunchKernelGGL((select_kernel<MODE, 4096, SEL_SMALL_THREADS>), grid, dim3(SEL_SMALL_THREADS), 0, s, a);

@@ -1118,8 +1118,7 @@ __global__ __launch_bounds__(256) void sparse_attn_f32_kernel(AttnArgs a) {
 // 16 heads), one 4-column group per thread, so the partial records are read
 // by many CUs at once (measured: 8 x 256 threads is 0.7 us faster per call
 // than 4 x 256 with two groups per thread); every load (all splits' partial
-// O and their m, l) is issued before any is used, with split indices clamped
-// to the last split and zero factors past it, so one memory round trip
+// O and their m, l) is issued before any is used, so one memory round trip
 // covers the combine.
 constexpr int ATTN_MAX_SPLIT = 16;
 

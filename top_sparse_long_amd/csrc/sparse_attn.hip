@@ -461,7 +461,7 @@ __global__ __launch_bounds__(64 * AW_WAVES) void sparse_attn_quant_kernel(AttnAr
     const float inv = (den > 0.f) ? 1.f / den : 0.f;
 #pragma unroll
     for (int w = 0; w < AW_WAVES; ++w) fw[w][j] *= inv;
-    if (a.lse && wave == 0 && r == 0) a.lse[(int64_t)t * a.H + h_glob0 + h] = (Mx + log2f(den)) * LN2;
+    if (a.lse && wave == 0 && r == 0) a.lse[(int64_t)t * a.H + h_glob0 + h] = (Mx + __builtin_amdgcn_logf(den)) * LN2;
   }
   const int64_t obase = ((int64_t)t * a.H + h_glob0 + 4 * g) * AT_D + r;
   // inverse RoPE of dims 448..511 (column blocks 28..31): the pair (2i, 2i+1)
@@ -954,7 +954,7 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_wide_kernel(AttnArg
       const float e_keys = (Mh[hb][j] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(Mh[hb][j] - Mx);
       const float den = Lh[hb][j] * e_keys + ((Mx == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(sk - Mx));
       fo[hb][j] = (den > 0.f) ? e_keys * __builtin_amdgcn_rcpf(den) : 0.f;
-      if (write_lse) a.lse[(int64_t)t * WD_H + 16 * hb + 4 * g + j] = (Mx + log2f(den)) * LN2;
+      if (write_lse) a.lse[(int64_t)t * WD_H + 16 * hb + 4 * g + j] = (Mx + __builtin_amdgcn_logf(den)) * LN2;
     }
   // inverse RoPE of dims 448..511 (wave 7's columns): the pair (2i, 2i+1)
   // sits in lanes r, r ^ 1
@@ -1184,7 +1184,7 @@ __global__ __launch_bounds__(ATTN_COMBINE_THREADS) void sparse_attn_combine_kern
       v.z += x[i][sp].z * fs;
       v.w += x[i][sp].w * fs;
     }
-    if (a.lse && (e % AT_D) == 0) a.lse[(int64_t)t * a.H + h0 + h] = (M + log2f(den)) * LN2;
+    if (a.lse && (e % AT_D) == 0) a.lse[(int64_t)t * a.H + h0 + h] = (M + __builtin_amdgcn_logf(den)) * LN2;
     const int col = e % AT_D;
     if (turn && col >= 448) {
       const float* cs = a.rope + (int64_t)p * 64 + ((col - 448) >> 1);

@@ -675,17 +675,30 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_wide_kernel(AttnArg
       const float sc = R.s.x;
       const _Float16 mh = scale_mantissa(sc);
       const v2h m2 = {mh, mh};
+      // the q chunks of step c + 1 are read from LDS before the products of
+      // step c; the scheduling barrier keeps the compiler from sinking each
+      // read next to its product, which left one LDS round trip exposed per
+      // product (4,096-query chunk: 622 -> 602 us per call)
+      v8h qn[4];
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) qn[hb] = *(const v8h*)(qsrc + 16 * hb * V3_QS);
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
+        v8h qc[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) qc[hb] = qn[hb];
+        if (c + 1 < 16) {
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) qn[hb] = *(const v8h*)(qsrc + 16 * hb * V3_QS + 16 * (c + 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
         uint32_t kd[4];
         dequant_fp8x4(R.d[c >> 1][(c & 1) * 2], sc, m2, &kd[0]);
         dequant_fp8x4(R.d[c >> 1][(c & 1) * 2 + 1], sc, m2, &kd[2]);
         const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-          const v8h qv = *(const v8h*)(qsrc + 16 * hb * V3_QS + 16 * c);
-          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qv, acc[hb], 0, 0, 0);
-        }
+        for (int hb = 0; hb < 4; ++hb)
+          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qc[hb], acc[hb], 0, 0, 0);
       }
     } else {
       const float s4[4] = {R.s.x, R.s.y, R.s.z, R.s.w};
@@ -701,8 +714,19 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_wide_kernel(AttnArg
           s8[4 * w + 3] = hi2[1];
         }
       }
+      v8h qn[4];
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) qn[hb] = *(const v8h*)(qsrc + 16 * hb * V3_QS);
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
+        v8h qc[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) qc[hb] = qn[hb];
+        if (c + 1 < 16) {
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) qn[hb] = *(const v8h*)(qsrc + 16 * hb * V3_QS + 16 * (c + 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);
         uint32_t kd[4];
         if (S16) {
           dequant_fp4x8_h(R.d[c >> 2][c & 3], s8[c >> 1], kd);
@@ -712,10 +736,8 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_wide_kernel(AttnArg
         }
         const v4u kv = {kd[0], kd[1], kd[2], kd[3]};
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-          const v8h qv = *(const v8h*)(qsrc + 16 * hb * V3_QS + 16 * c);
-          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qv, acc[hb], 0, 0, 0);
-        }
+        for (int hb = 0; hb < 4; ++hb)
+          acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, kv), qc[hb], acc[hb], 0, 0, 0);
       }
     }
     // lane (r, g) of S^T holds keys 4 g + i of the tile for head 16 hb + r
@@ -847,15 +869,28 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_wide_kernel(AttnArg
         for (int half = 0; half < 2; ++half) {
           const int kt = 16 * (4 * half + g);
           const int rrow = v3_row(kt + r);
+          // every LDS read of the half (scales, transposing reads, the first
+          // head block's P) is issued before the conversions, and each head
+          // block's P is read during the previous block's products (602 ->
+          // 596 us per call on the same chunk)
           v8h B1[4], B2[4];
+          v8h S1s[4], S2s[4];
+          v2i_t tvs[4];
 #pragma unroll
           for (int cb = 0; cb < 4; ++cb) {
-            // scale group of columns c0 + 16 cb .. + 15
             const int grp = S16 ? (4 * wave + cb) : (2 * wave + (cb >> 1));
-            const v8h S1 = *(const v8h*)(&s_scl[grp][kt]);
-            const v8h S2 = *(const v8h*)(&s_scl[grp][kt + 8]);
-            const v2i_t tv = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
+            S1s[cb] = *(const v8h*)(&s_scl[grp][kt]);
+            S2s[cb] = *(const v8h*)(&s_scl[grp][kt + 8]);
+            tvs[cb] = __builtin_amdgcn_ds_read_tr4_b64_v2i32(
                 (__attribute__((address_space(3))) v2i_t*)(rawl + rrow + (c0 + 16 * cb) / 2));
+          }
+          v8h P1n = *(const v8h*)(s_p + r * WD_PS + 2 * kt);
+          v8h P2n = *(const v8h*)(s_p + r * WD_PS + 2 * (kt + 8));
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const v8h S1 = S1s[cb], S2 = S2s[cb];
+            const v2i_t tv = tvs[cb];
             uint32_t b1[4], b2[4];
             b1[0] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[0], 1.0f, 0));
             b1[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[0], 1.0f, 1));
@@ -871,8 +906,12 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_wide_kernel(AttnArg
           }
 #pragma unroll
           for (int hb = 0; hb < 4; ++hb) {
-            const v8h P1 = *(const v8h*)(s_p + (16 * hb + r) * WD_PS + 2 * kt);
-            const v8h P2 = *(const v8h*)(s_p + (16 * hb + r) * WD_PS + 2 * (kt + 8));
+            const v8h P1 = P1n, P2 = P2n;
+            if (hb + 1 < 4) {
+              P1n = *(const v8h*)(s_p + (16 * (hb + 1) + r) * WD_PS + 2 * kt);
+              P2n = *(const v8h*)(s_p + (16 * (hb + 1) + r) * WD_PS + 2 * (kt + 8));
+            }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
               O[hb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P1, B1[cb], O[hb][cb], 0, 0, 0);

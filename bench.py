@@ -171,7 +171,7 @@ STAGE_KERNELS = {
     "topk_blocks": ("select_kernel<5,", "select_kernel<4,"),
     "topk_and_blocks": ("select_pair_kernel", "select_kernel<0,", "select_kernel<2,", "select_kernel<3,",
                         "select_kernel<4,", "select_kernel<5,"),
-    "sparse_attn": ("sparse_attn_quant_kernel", "sparse_attn_wide_kernel", "sparse_attn_combine_kernel",
+    "sparse_attn": ("sparse_attn_pipe_kernel", "sparse_attn_wide_kernel", "sparse_attn_combine_kernel",
                     "sparse_attn_f32_kernel"),
     # the 65,536-token m = 2 chunk (the decode-batch calls use the prefetching
     # variant, cache_write_kernel<m, true>, and are not part of this record)

@@ -315,9 +315,11 @@ def test_sparse_attn_rejects(kw, status):
 def test_attention_workspace_sizes():
     lib = tsl.load()
     one = 16 + 16 + 16 * 512
-    # a small batch splits its 20 tiles five ways
-    assert lib.csa2_sparse_attn_workspace_size(8, 64, 512, 128) == 8 * 4 * 5 * one * 4
-    # a large batch fills the chip without splitting
+    # two queries of 64 heads: 8 groups of 16 heads x 4 column parts = 32
+    # workgroups, so the 5 rounds of 128 keys are split four ways
+    assert lib.csa2_sparse_attn_workspace_size(2, 64, 512, 128) == 2 * 4 * 4 * one * 4
+    # from 128 workgroups (8 queries of 64 heads) on, nothing is split
+    assert lib.csa2_sparse_attn_workspace_size(8, 64, 512, 128) == 0
     assert lib.csa2_sparse_attn_workspace_size(64, 64, 512, 128) == 0
     assert lib.csa2_sparse_attn_workspace_size(0, 64, 512, 128) == 0
     # a tiny key set needs no split either

@@ -846,8 +846,9 @@ def test_fused_block_max_sizes(bs, many):
 
 @pytest.mark.parametrize("concurrent", [False, True])
 def test_graph_replay_matches_eager(concurrent):
-    """A captured pass (optionally with block candidates on a second stream)
-    replays to the serial eager result, several times, with eager work and
+    """A captured pass (optionally with every attention call on a second
+    stream, overlapping the later layers' scoring and selection) replays to
+    the serial eager result, several times, with eager work and
     synchronisations between the replays."""
     _announce(f"graph replay concurrent={concurrent}")
     wl = synth.mini_workload(43, [70000, 20000], q_per_seq=2, modes=("full", "reuse", "reindex")).to(DEV)

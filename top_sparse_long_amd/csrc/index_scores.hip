@@ -141,6 +141,16 @@ __device__ __forceinline__ float relu(float x) {
   return __int_as_float(max(__float_as_int(x), 0));
 }
 
+// sum over a lane's 16 heads of gate * ReLU(score), in four independent
+// chains: one chain of 16 dependent FMAs left the VALU waiting on every
+// result
+__device__ __forceinline__ float gated_relu_sum(const float (&gate)[16], const v16f& acc) {
+  float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) p[j & 3] = fmaf(gate[j], relu(acc[j]), p[j & 3]);
+  return (p[0] + p[1]) + (p[2] + p[3]);
+}
+
 // v + (the value of the lane 32 away), in every lane (gfx950 permlane swap:
 // no LDS round trip).
 __device__ __forceinline__ float add_half_swap(float v) {
@@ -284,10 +294,7 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[2 * j], b0, acc, 0, 0, 0);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[2 * j + 1], b1, acc, 0, 0, 0);
         }
-        float v = 0.f;
-#pragma unroll
-        for (int j = 0; j < 16; ++j) v = fmaf(gate[j], relu(acc[j]), v);
-        v = add_half_swap(v);
+        const float v = add_half_swap(gated_relu_sum(gate, acc));
         // FP8 keys: the per-key scale multiplies the head sum; FP4 keys
         // carry their scales inside the operands
         sc = (S.pos[i] >= 0) ? (K4 ? v : v * S.ks[i]) : -INFINITY;
@@ -531,10 +538,7 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
         float sc[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          float v = 0.f;
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) v = fmaf(gate[i][jj], relu(acc[i][jj]), v);
-          v = add_half_swap(v);
+          const float v = add_half_swap(gated_relu_sum(gate[i], acc[i]));
           sc[i] = (act[i] && col < nv[i] && ks == ks) ? v * ks : -INFINITY;
         }
 #pragma unroll

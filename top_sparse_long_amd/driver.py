@@ -211,16 +211,21 @@ class LayerRunner:
         ranks blocks first (via_blocks) or a later layer needs the pool; the
         selections then read those maxima.  A Full layer that builds the pool
         makes both of its selections with one call
-        (csa2_topk_and_block_candidates) unless separate_select or concurrent
-        asks for two calls; a Full layer's own top-k alone is
-        csa2_topk_from_block_max (via_blocks) or csa2_topk.
+        (csa2_topk_and_block_candidates) unless separate_select asks for two
+        calls; a Full layer's own top-k alone is csa2_topk_from_block_max
+        (via_blocks) or csa2_topk.
 
-        concurrent=True runs the block-candidate selection on a second stream:
-        it needs only the Full layer's scores, so it overlaps that layer's
-        top-k and attention (and any Reuse layers after it); the pool scoring
-        of the Reindex layer waits for it.  Each callable launches on the
-        stream current when it is called, so the pass can be captured into
-        one graph."""
+        concurrent=True issues the attention calls that a later layer's
+        scoring and selection can overlap on a second stream, in layer
+        order: such a call waits only for the work issued before it on the
+        main stream (its own top-k); the attention calls after the last
+        scoring layer run on the main stream once the second stream's work
+        is done (nothing is left to overlap them).  Attention calls stay in
+        order among themselves (they share the split workspace), and every
+        buffer an attention call reads is written on the main stream before
+        it and not again within the pass (each layer has its own top-k
+        buffer).  Each callable launches on the stream current when it is
+        called, so the pass can be captured into one graph."""
         out = []
 
         def reset():
@@ -228,53 +233,55 @@ class LayerRunner:
             self.slots.candidates = None
         out.append(("reset", reset))
         has_pool = False
-        for li, lay in enumerate(self.wl.layers):
+        layers = self.wl.layers
+        last_scoring = max((i for i, l in enumerate(layers) if l.mode in ("full", "reindex")), default=-1)
+        joined = False
+        for li, lay in enumerate(layers):
             if lay.mode == "full":
                 fuse = self.fuses_block_max(li)
                 out.append(("index_scores_dense",
                             lambda li=li, fuse=fuse: self.index_scores(li, pool=False, block_max=fuse)))
-                if self.needs_pool[li] and not (concurrent or separate_select):
+                if self.needs_pool[li] and not separate_select:
                     out.append(("topk_and_blocks",
                                 lambda li=li, fuse=fuse: self.topk_and_blocks(li, fuse)))
-                    out.append(("sparse_attn", lambda li=li: self.attention(li)))
                     has_pool = True
-                    continue
-                if self.needs_pool[li]:
-                    if concurrent:
-                        out.append(("block_candidates",
-                                    lambda fuse=fuse: self._fork_block_candidates(fuse)))
-                    else:
+                else:
+                    if self.needs_pool[li]:
                         out.append(("block_candidates",
                                     lambda fuse=fuse: self.block_candidates(from_block_max=fuse)))
-                    has_pool = True
-                if self.via_blocks:
-                    out.append(("topk_blocks", lambda li=li: self.topk(li, pool=False, via_blocks=True)))
-                else:
-                    out.append(("topk_dense", lambda li=li: self.topk(li, pool=False)))
+                        has_pool = True
+                    if self.via_blocks:
+                        out.append(("topk_blocks", lambda li=li: self.topk(li, pool=False, via_blocks=True)))
+                    else:
+                        out.append(("topk_dense", lambda li=li: self.topk(li, pool=False)))
             elif lay.mode == "reindex":
                 pool = has_pool
-                if pool and concurrent:
-                    out.append(("index_scores_pool",
-                                lambda li=li: (self._join(), self.index_scores(li, pool=True))))
-                else:
-                    out.append(("index_scores_pool" if pool else "index_scores_dense",
-                                lambda li=li, pool=pool: self.index_scores(li, pool=pool)))
+                out.append(("index_scores_pool" if pool else "index_scores_dense",
+                            lambda li=li, pool=pool: self.index_scores(li, pool=pool)))
                 out.append(("topk_pool" if pool else "topk_dense",
                             lambda li=li, pool=pool: self.topk(li, pool=pool)))
-            out.append(("sparse_attn", lambda li=li: self.attention(li)))
-        if concurrent:
+            if concurrent and li < last_scoring:
+                out.append(("sparse_attn", lambda li=li: self._attention_side(li)))
+            else:
+                if concurrent and not joined:
+                    out.append(("join", self._join))
+                    joined = True
+                out.append(("sparse_attn", lambda li=li: self.attention(li)))
+        if concurrent and not joined:
             out.append(("join", self._join))
         return out
 
-    def _fork_block_candidates(self, fuse):
+    def _attention_side(self, li):
+        """Layer li's attention on the second stream, after everything issued
+        so far on the current stream."""
         main = torch.cuda.current_stream()
         if self._side is None:
             self._side = torch.cuda.Stream(device=main.device)   # default priority
-        fork = torch.cuda.Event()
-        fork.record(main)
-        self._side.wait_event(fork)
+        ready = torch.cuda.Event()
+        ready.record(main)
+        self._side.wait_event(ready)
         with torch.cuda.stream(self._side):
-            self.block_candidates(from_block_max=fuse)
+            self.attention(li)
         self._joined = torch.cuda.Event()
         self._joined.record(self._side)
 

@@ -828,6 +828,35 @@ def _roofline(stage, rec, workload):
     return r
 
 
+def mfma_valu_overlap(torch, tsl, iters=2048, reps=5):
+    """Whether matrix-core products and vector ALU work overlap on a SIMD
+    (csa2_diag_mfma_valu): the loop of eight independent 32x32x16 f16
+    products, of 64 independent fp32 FMAs, and of both, two waves per SIMD
+    on every CU; median of reps timed launches each.  overlap = the share
+    of the shorter loop's time hidden when both run: 1 if they overlap
+    fully, 0 if they serialize."""
+    sink = torch.empty(256 * 512, dtype=torch.float32, device="cuda")
+    res = {}
+    for mode, key in ((1, "mfma_us"), (2, "valu_us"), (3, "both_us")):
+        tsl.csa2_diag_mfma_valu(mode, iters, sink)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            tsl.csa2_diag_mfma_valu(mode, iters, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        res[key] = sorted(ts)[len(ts) // 2]
+    hidden = res["mfma_us"] + res["valu_us"] - res["both_us"]
+    res["overlap"] = hidden / min(res["mfma_us"], res["valu_us"])
+    res["what"] = ("per iteration and wave: 8 independent v_mfma_f32_32x32x16_f16, 64 independent fp32 FMAs, "
+                   "or both; 256 workgroups of 8 waves, %d iterations" % iters)
+    return res
+
+
 def targets(torch, synth, LayerRunner, timer, args):
     """The two stated targets, each on its own workload: prefill index
     scoring at >= 0.5 of the FP8 MFMA peak (the 4,096-query m = 2 chunk) and
@@ -906,6 +935,7 @@ def main():
                           "calls": args.repeat * len(calls)}), flush=True)
         return
     ceiling = read_ceiling(torch, tsl)
+    overlap = mfma_valu_overlap(torch, tsl)
     timer = Timer(torch, 1 << 30)
 
     m = measure_workload(torch, synth, LayerRunner, timer, args.workload, args, args.copies,
@@ -990,6 +1020,7 @@ def main():
         "sparse_attn_queries_per_s": attn_qps,
         "roofline": roofline,
         "hbm_read_ceiling": ceiling,
+        "mfma_valu_overlap": overlap,
         "cpu_baseline": cpu,
         "stages": stages,
         "targets": tgt,

@@ -363,6 +363,19 @@ int csa2_diag_stream_read(const void* src, size_t bytes, float* sink, size_t sin
 int csa2_diag_stream_write(void* dst, size_t bytes, float value, void* stream);
 
 /*
+ * csa2_diag_mfma_valu — a loop that measures whether matrix-core products
+ * and vector ALU work overlap on one SIMD: 256 workgroups of eight waves
+ * (two per SIMD) run iters iterations of eight independent
+ * v_mfma_f32_32x32x16_f16 products (mode 1), 64 independent fp32 FMAs
+ * (mode 2) or both (mode 3).  The caller times the launches; each thread
+ * writes one float of its results to sink.
+ *   sink   device memory of at least 256 * 512 floats (sink_floats).
+ *   Errors: CSA2_ERR_INVALID_ARG for a null sink, a short sink, mode not in
+ *   1..3 or iters < 1; CSA2_ERR_HIP if the launch fails.
+ */
+int csa2_diag_mfma_valu(int32_t mode, int32_t iters, float* sink, size_t sink_floats, void* stream);
+
+/*
  * csa2_sparse_attn — core sparse attention ([CSA2] "per-layer attention
  * computation"; [3MODES] Q&A on Reuse layers).  For query t at position p of
  * sequence b and head i, the keys are the SWA rows of positions

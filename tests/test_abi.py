@@ -212,6 +212,17 @@ def test_diag_stream_read_and_write_reject():
     assert w(FAKE, 0, 0.0, None) == tsl.CSA2_OK
 
 
+def test_diag_mfma_valu_rejects():
+    lib = tsl.load()
+    f = lib.csa2_diag_mfma_valu
+    n = 256 * 512
+    assert f(1, 10, None, n, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert f(0, 10, FAKE, n, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert f(4, 10, FAKE, n, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert f(3, 0, FAKE, n, None) == tsl.CSA2_ERR_INVALID_ARG
+    assert f(3, 10, FAKE, n - 1, None) == tsl.CSA2_ERR_INVALID_ARG
+
+
 def test_topk_and_block_candidates_noalloc_rejects_sizes_past_the_scratch():
     """The allocation-free variant refuses, before anything is enqueued, any
     shape whose selection lists exceed its static buffer; its other argument

@@ -21,6 +21,7 @@ EXPORTED = ("csa2_index_scores", "csa2_block_candidates", "csa2_block_candidates
             "csa2_topk_and_block_candidates_workspace_size",
             "csa2_topk_and_block_candidates_noalloc", "csa2_noalloc_scratch_bytes",
             "csa2_diag_index_scores_fp8_mfma", "csa2_diag_stream_read", "csa2_diag_stream_write",
+            "csa2_diag_mfma_valu",
             "csa2_topk_from_block_max", "csa2_topk_from_block_max_workspace_size", "csa2_sparse_attn",
             "csa2_sparse_attn_workspace_size", "csa2_cache_write",
             "csa2_status_string", "csa2_last_error", "csa2_version")
@@ -86,6 +87,7 @@ def load():
                                                            I32, P, I32, PP, P]
     lib.csa2_diag_stream_read.argtypes = [P, SZ, P, SZ, P]
     lib.csa2_diag_stream_write.argtypes = [P, SZ, ctypes.c_float, P]
+    lib.csa2_diag_mfma_valu.argtypes = [I32, I32, P, SZ, P]
     lib.csa2_topk_from_block_max.argtypes = [P, I64, I32, P, I64, P, I32, I32, I32, P, P, SZ, I32, PP, P]
     lib.csa2_topk_from_block_max_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.csa2_topk_from_block_max_workspace_size.restype = SZ
@@ -106,7 +108,7 @@ def load():
     for fn in ("csa2_index_scores", "csa2_block_candidates", "csa2_topk",
                "csa2_topk_and_block_candidates", "csa2_topk_and_block_candidates_noalloc",
                "csa2_diag_index_scores_fp8_mfma", "csa2_diag_stream_read", "csa2_diag_stream_write",
-               "csa2_topk_from_block_max", "csa2_sparse_attn", "csa2_cache_write",
+               "csa2_diag_mfma_valu", "csa2_topk_from_block_max", "csa2_sparse_attn", "csa2_cache_write",
                "csa2_version"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -249,6 +251,12 @@ def csa2_diag_stream_write(dst, value=0.0, stream=None):
     """Diagnostic: fill the whole of dst (a device tensor) at full speed."""
     _check(load().csa2_diag_stream_write(_ptr(dst), dst.numel() * dst.element_size(), value,
                                          _stream(stream)))
+
+
+def csa2_diag_mfma_valu(mode, iters, sink, stream=None):
+    """Diagnostic: the MFMA / VALU overlap loop (mode 1 products, 2 FMAs,
+    3 both) into sink, a device float tensor of at least 256 * 512 values."""
+    _check(load().csa2_diag_mfma_valu(mode, iters, _ptr(sink), sink.numel(), _stream(stream)))
 
 
 def csa2_topk_from_block_max_workspace_size(Q, n_cols, k, block_size):

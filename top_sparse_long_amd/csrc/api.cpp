@@ -234,6 +234,16 @@ int csa2_diag_stream_write(void* dst, size_t bytes, float value, void* stream) {
                     "csa2_diag_stream_write");
 }
 
+int csa2_diag_mfma_valu(int32_t mode, int32_t iters, float* sink, size_t sink_floats, void* stream) {
+  g_err[0] = 0;
+  REQUIRE(sink, CSA2_ERR_INVALID_ARG, "csa2_diag_mfma_valu: null sink");
+  REQUIRE(mode >= 1 && mode <= 3, CSA2_ERR_INVALID_ARG, "csa2_diag_mfma_valu: mode must be 1, 2 or 3");
+  REQUIRE(iters >= 1, CSA2_ERR_INVALID_ARG, "csa2_diag_mfma_valu: iters must be positive");
+  REQUIRE(sink_floats >= (size_t)csa2::MV_BLOCKS * 512, CSA2_ERR_INVALID_ARG,
+          "csa2_diag_mfma_valu: sink must hold 256 * 512 floats");
+  return hip_status(csa2::launch_mfma_valu(mode, iters, sink, (hipStream_t)stream), "csa2_diag_mfma_valu");
+}
+
 size_t csa2_topk_workspace_size(int32_t Q, int32_t n_cols, int32_t k) {
   if (Q <= 0 || n_cols <= 0 || k <= 0) return 0;
   return csa2::select_workspace_bytes(Q, n_cols, k);

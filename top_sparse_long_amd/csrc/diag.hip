@@ -11,6 +11,13 @@
 // stream_write: fills a buffer with one value through 16-byte non-temporal
 // stores in the same grid-stride form -- the write counterpart, and a write
 // of known size for calibrating memory-traffic counters.
+//
+// mfma_valu: whether matrix-core products and vector ALU work on the same
+// SIMD overlap.  256 workgroups of eight waves (two per SIMD, the occupancy
+// of the hot path's MFMA kernels) each run a loop of eight independent
+// v_mfma_f32_32x32x16_f16 products, 64 independent fp32 FMAs, or both; the
+// caller times the three launches.  If the two kinds of work overlapped,
+// both would take about as long as the longer one alone.
 #include "kernels.h"
 
 namespace csa2 {
@@ -58,6 +65,57 @@ __global__ __launch_bounds__(SR_THREADS) void stream_write_kernel(v4f_t* __restr
 
 hipError_t launch_stream_write(void* dst, size_t bytes, float value, int n_blocks, hipStream_t s) {
   hipLaunchKernelGGL(stream_write_kernel, dim3(n_blocks), dim3(SR_THREADS), 0, s, (v4f_t*)dst, bytes / 16, value);
+  return hipGetLastError();
+}
+
+typedef _Float16 v8h_t __attribute__((ext_vector_type(8)));
+typedef float v16f_t __attribute__((ext_vector_type(16)));
+constexpr int MV_THREADS = 512;
+
+template <bool MF, bool VA>
+__global__ __launch_bounds__(MV_THREADS) void mfma_valu_kernel(int iters, float* sink) {
+  const float seed = (float)(threadIdx.x & 31) * 0.001f;
+  v8h_t a[2], b[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      a[i][e] = (_Float16)(seed * (float)(e + i + 1));
+      b[i][e] = (_Float16)(seed * (float)(3 * e + i + 1));
+    }
+  v16f_t acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) acc[c] = (v16f_t){};
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = seed * (float)(i + 1);
+  const float gm = 1.0f - seed;
+  for (int it = 0; it < iters; ++it) {
+    if (MF) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[m & 1], b[m & 1], acc[m & 3], 0, 0, 0);
+    }
+    if (VA) {
+#pragma unroll
+      for (int v = 0; v < 64; ++v) x[v & 15] = fmaf(x[v & 15], gm, seed);
+    }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) s += acc[c][e];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += x[i];
+  sink[blockIdx.x * MV_THREADS + threadIdx.x] = s;
+}
+
+hipError_t launch_mfma_valu(int mode, int iters, float* sink, hipStream_t s) {
+  const dim3 grid(MV_BLOCKS), block(MV_THREADS);
+  if (mode == 1) hipLaunchKernelGGL((mfma_valu_kernel<true, false>), grid, block, 0, s, iters, sink);
+  else if (mode == 2) hipLaunchKernelGGL((mfma_valu_kernel<false, true>), grid, block, 0, s, iters, sink);
+  else hipLaunchKernelGGL((mfma_valu_kernel<true, true>), grid, block, 0, s, iters, sink);
   return hipGetLastError();
 }
 

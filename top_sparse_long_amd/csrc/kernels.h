@@ -232,5 +232,9 @@ hipError_t launch_cache_write(const CacheWriteArgs& a, hipStream_t s);
 hipError_t launch_stream_read(const void* src, size_t bytes, float* sink, int n_blocks, hipStream_t s);
 // Fill of bytes (a multiple of 16) at dst with value by n_blocks workgroups.
 hipError_t launch_stream_write(void* dst, size_t bytes, float value, int n_blocks, hipStream_t s);
+// MFMA / VALU overlap loop (mode 1: products, 2: FMAs, 3: both); sink holds
+// MV_BLOCKS * 512 floats.
+constexpr int MV_BLOCKS = 256;
+hipError_t launch_mfma_valu(int mode, int iters, float* sink, hipStream_t s);
 
 }  // namespace csa2

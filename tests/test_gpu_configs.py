@@ -18,8 +18,16 @@ from tests.parity import check_scores, check_index_table, check_topk_gap, check_
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
-SAMPLES = {"tiny_full_fp32": None, "decode_128k": [0, 5], "prefill_m2_chunk": [0, 1, 2047, 4095],
-           "reindex_1m": [0, 1], "decoder_group_256k": [0, 37], "decode_128k_pages_formats": [2, 7]}
+# Sampled queries: every query of the decode batches and of the 64-query
+# group; on the 4,096-query chunk, every 64th query plus both sides of the
+# boundaries where a kernel's query tiling or its workgroup-to-XCD mapping
+# changes (the scorer's 16-query tiles; the attention's workgroups, dealt to
+# the 8 XCDs in runs of 512), plus the ends.
+SAMPLES = {"tiny_full_fp32": None, "decode_128k": list(range(8)),
+           "prefill_m2_chunk": sorted(set(range(0, 4096, 64)) | {1, 15, 16, 17, 511, 512, 1023, 1024, 2047,
+                                                                 2048, 3071, 3072, 4094, 4095}),
+           "reindex_1m": [0, 1], "decoder_group_256k": list(range(64)),
+           "decode_128k_pages_formats": list(range(8))}
 
 
 @pytest.fixture(autouse=True)

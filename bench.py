@@ -108,12 +108,20 @@ def _stage_work(run, stage):
     nvis = wl.n_vis().clamp(max=run.n_cols)
     shared = wl.Q >= PREFILL_MIN_Q
     if stage == "index_scores_dense":
-        # plus the fused block maxima (4 B per block) when the step emits them
+        # plus the fused block maxima (4 B per block) when the step emits them;
+        # without the 4-B score when the Full layer re-scores its best blocks
         fused = any(run.fuses_block_max(li) for li, l in enumerate(wl.layers) if l.mode == "full")
         extra = 4.0 / wl.block_size if fused else 0.0
+        if run.rescore and any(run.needs_pool):
+            extra -= SCORE_BYTES
         pairs = int(nvis.sum().item())
         return (float(pairs) * (_index_bytes(wl) + extra), float(pairs) * INDEX_FLOPS_PER_PAIR, pairs,
                 "mfma" if shared else "hbm")
+    if stage == "index_scores_top":
+        pairs = wl.Q * run.top_cols
+        return float(pairs) * _index_bytes(wl), float(pairs) * INDEX_FLOPS_PER_PAIR, pairs, "hbm"
+    if stage == "topk_top":
+        return float(wl.Q * run.top_cols) * SCORE_BYTES, 0.0, wl.Q * run.top_cols, "hbm"
     if stage == "index_scores_pool":
         pairs = wl.Q * run.pool_cols
         return float(pairs) * _index_bytes(wl), float(pairs) * INDEX_FLOPS_PER_PAIR, pairs, "hbm"
@@ -121,6 +129,9 @@ def _stage_work(run, stage):
         nblk = (nvis + wl.block_size - 1) // wl.block_size
         return float(nblk.sum().item()) * SCORE_BYTES, 0.0, int(nvis.sum().item()), "hbm"
     nblk = (nvis + wl.block_size - 1) // wl.block_size
+    if stage == "top_blocks_and_blocks":
+        # one read of the block maxima (both rankings read the same)
+        return float(nblk.sum().item()) * SCORE_BYTES, 0.0, int(nvis.sum().item()), "hbm"
     # the top-k through block maxima reads the maxima, then the scores of the
     # k best blocks (the library takes this route when k * block_size <= 32,768)
     via = (run.via_blocks and run.fuse_block_max and wl.topk * wl.block_size <= 32768)
@@ -168,6 +179,10 @@ STAGE_KERNELS = {
     "block_candidates": ("select_kernel<2,",),
     "topk_dense": ("select_kernel<0,", "select_kernel<3,"),
     "topk_pool": ("select_kernel<1,",),
+    # the re-scoring route of a Full layer (its kernels are the pool stages')
+    "top_blocks_and_blocks": ("select_pair_kernel", "select_kernel<5,", "select_kernel<2,", "select_kernel<3,"),
+    "index_scores_top": ("index_scores_fp8_kernel<true",),
+    "topk_top": ("select_kernel<1,",),
     "topk_blocks": ("select_kernel<5,", "select_kernel<4,"),
     "topk_and_blocks": ("select_pair_kernel", "select_kernel<0,", "select_kernel<2,", "select_kernel<3,",
                         "select_kernel<4,", "select_kernel<5,"),
@@ -257,6 +272,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, workload, comma
         if stage == "topk_and_blocks":
             own = ["select_pair_kernel"]
         if not any(p in n for p in own for n in per_kernel_bytes):
+            continue
+        # the re-scoring route's stages run the pool stages' kernels: their
+        # dispatches cannot be told apart by name
+        if stage in ("index_scores_top", "topk_top"):
             continue
         # with the shared-launch call the separate-call stages do not occur
         if stage in ("topk_dense", "block_candidates", "topk_blocks") and any(

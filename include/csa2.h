@@ -139,7 +139,10 @@ typedef struct {
  *             cand[t, c] < 0 or that position is not visible.  n_cols must
  *             equal n_cand_blocks * block_size.
  *   scores    [Q, score_stride] fp32 output; score_stride >= n_cols,
- *             multiple of 4; 16-byte aligned.
+ *             multiple of 4; 16-byte aligned.  May be NULL in dense mode
+ *             when block_max is given: then only the block maxima are
+ *             written (csa2_top_blocks_and_block_candidates and a pool-mode
+ *             call over the best blocks give the top-k without the scores).
  *   block_max NULL, or (dense mode only) [Q, block_max_stride] fp32 output:
  *             entry b of row t is the largest score of columns
  *             [b*block_size, (b+1)*block_size) (-inf where none is visible),
@@ -289,6 +292,43 @@ int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, in
 
 size_t csa2_topk_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t k,
                                                      int32_t block_size, int32_t n_blocks);
+
+/*
+ * csa2_top_blocks_and_block_candidates — a Full layer's two rankings of its
+ * block maxima, without its scores ([CSA2] "hierarchical sparse indexer";
+ * [DSA] "Top-k: tokens, not blocks"), in shared launches:
+ *   top_blocks[t]  the k_blocks best blocks of row t by maximum (ties to the
+ *                  lower block; no block forced), ascending, -1 padded:
+ *                  csa2_block_candidates' selection without its forced
+ *                  latest block;
+ *   cand[t]        csa2_block_candidates(NULL, 0, n_cols, block_max, ...)
+ *                  bit for bit (the latest visible block forced).
+ * Every entry of row t among its k best under (score descending, position
+ * ascending) lies in one of its k best blocks (a block holding a kept entry
+ * has a maximum at least that entry's, and every block ranked above it is
+ * kept).  So with k_blocks = k, scoring only those blocks (csa2_index_scores
+ * in pool mode with cand = top_blocks) and taking the top-k of that pool
+ * (csa2_topk with cand = top_blocks) gives the dense top-k exactly, as long
+ * as the pool scores equal the dense ones (the same arithmetic per key,
+ * which the quantized scorer has).
+ *   block_max [Q, block_max_stride] from csa2_index_scores (scores may then
+ *             be NULL); block_max_stride >= ceil(n_cols / block_size).
+ *   top_blocks [Q, k_blocks] int32 output; cand [Q, n_blocks] int32 output.
+ *   workspace at least csa2_top_blocks_and_block_candidates_workspace_size(
+ *             Q, n_cols, block_size, k_blocks, n_blocks) bytes, 16-byte
+ *             aligned.
+ *   Supported: 1 <= k_blocks, n_blocks <= 4096; block_size a power of two
+ *   <= 64; ratio 1 or 2.
+ *   Errors: as csa2_block_candidates for either ranking.
+ */
+int csa2_top_blocks_and_block_candidates(const float* block_max, int64_t block_max_stride, int32_t n_cols,
+                                         const int32_t* q_pos, int32_t ratio, int32_t block_size,
+                                         int32_t k_blocks, int32_t* top_blocks, int32_t n_blocks,
+                                         int32_t* cand, void* workspace, size_t workspace_bytes, int32_t Q,
+                                         void* stream);
+
+size_t csa2_top_blocks_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t block_size,
+                                                           int32_t k_blocks, int32_t n_blocks);
 
 /*
  * csa2_topk_and_block_candidates_noalloc — csa2_topk_and_block_candidates

@@ -212,6 +212,36 @@ def test_diag_stream_read_and_write_reject():
     assert w(FAKE, 0, 0.0, None) == tsl.CSA2_OK
 
 
+def test_top_blocks_and_block_candidates_rejects():
+    lib = tsl.load()
+    f = lib.csa2_top_blocks_and_block_candidates
+    n = 1 << 23   # 1M blocks of 8: ranked in stages, through the workspace
+    ws = lib.csa2_top_blocks_and_block_candidates_workspace_size(2, n, 8, 64, 128)
+    assert ws > 0
+    ok = (FAKE, n // 8, n, FAKE, 1, 8, 64, FAKE, 128, FAKE, FAKE, ws, 2, None)
+    for i in (0, 3, 7, 9):   # block_max, q_pos, top_blocks, cand
+        args = list(ok)
+        args[i] = None
+        assert f(*args) == tsl.CSA2_ERR_INVALID_ARG, i
+    bad = list(ok)
+    bad[5] = 6   # block_size not a power of two
+    bad[1] = n
+    assert f(*bad) == tsl.CSA2_ERR_UNSUPPORTED
+    bad = list(ok)
+    bad[6] = 5000   # k_blocks above 4096
+    assert f(*bad) == tsl.CSA2_ERR_UNSUPPORTED
+    bad = list(ok)
+    bad[1] = n // 8 - 1   # block_max stride below the block count
+    assert f(*bad) == tsl.CSA2_ERR_INVALID_ARG
+    bad = list(ok)
+    bad[11] = ws - 16   # short workspace
+    assert f(*bad) == tsl.CSA2_ERR_WORKSPACE
+    # nothing to rank: nothing is enqueued
+    zero = list(ok)
+    zero[12] = 0
+    assert f(*zero) == tsl.CSA2_OK
+
+
 def test_diag_mfma_valu_rejects():
     lib = tsl.load()
     f = lib.csa2_diag_mfma_valu

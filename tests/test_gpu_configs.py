@@ -58,6 +58,38 @@ def _gathered_main(wl, b, idx_row, n_vis):
     return oracle_io.main_rows(wl, rows), compact
 
 
+def _check_rescore_route(run, wl, t, ref, idx_row, pos1, n):
+    """Query t of a Full layer that wrote only block maxima: the maxima meet
+    the score bound against the oracle's; the best blocks are the k best of
+    the GPU's maxima (exact); their re-scored keys meet the score bound; the
+    top-k is the exact top-k of those keys and, against the oracle's float64
+    scores, meets the gap rule; the pool is the candidate ranking of the
+    GPU's maxima (exact)."""
+    bs = wl.block_size
+    nb = -(-n // bs)
+    bm = _np(run.block_max[t, :nb]).astype(np.float64)
+    ref_bm = oracle.block_maxima(ref[0], n, bs)
+    tau = row_tau(ref[0])
+    fin = np.isfinite(ref_bm)
+    assert np.array_equal(np.isfinite(bm), fin)
+    assert np.all(np.abs(bm[fin] - ref_bm[fin]) <= 1e-3 * (np.abs(ref_bm[fin]) + tau))
+    order = sorted(range(nb), key=lambda b: (-bm[b], b))
+    want = sorted(b for b in order[:wl.topk] if bm[b] > -np.inf)
+    tb = _np(run.top_blocks[t])
+    assert [int(x) for x in tb if x >= 0] == want
+    ts = _np(run.top_scores[t:t + 1, :run.top_cols])
+    pos = oracle.pool_positions(tb[None], bs)[0]
+    ref_ts = np.where((pos >= 0) & (pos < n), ref[0][np.clip(pos, 0, ref.shape[1] - 1)], -np.inf)
+    check_scores(ts, ref_ts[None], "re-scored keys")
+    assert np.array_equal(idx_row, oracle.topk_rows_pool(ts.astype(np.float64), tb[None], bs, wl.topk)[0])
+    check_topk_gap(idx_row, ref[0, :n], np.arange(n), wl.topk, tau)
+    # the pool: a score row whose blocks hold the GPU maxima (first column)
+    row = np.full(ref.shape[1], -np.inf)
+    row[np.arange(nb) * bs] = bm
+    assert np.array_equal(_np(run.cand[t:t + 1]), oracle.block_candidates(row[None], pos1, wl.ratio, bs,
+                                                                          wl.n_blocks))
+
+
 @pytest.mark.parametrize("name", list(synth.CONFIG_NAMES) + list(synth.EXTRA_WORKLOADS))
 def test_config_parity(name):
     print(f"[case] config {name}", flush=True)
@@ -100,7 +132,13 @@ def test_config_parity(name):
         for j, t in enumerate(sample):
             kr, pos1, seq0 = sub(t)
             n = int(nvis[t])
-            if lay.mode == "full":
+            if lay.mode == "full" and run.rescore and run.needs_pool[li]:
+                # the re-scoring route: block maxima only, the best blocks'
+                # keys scored again
+                ref = oracle.index_scores_dense(qi[j:j + 1], wi[j:j + 1], kr, zero, seq0, pos1,
+                                                wl.ratio, run.n_cols)
+                _check_rescore_route(run, wl, t, ref, idx[j], pos1, n)
+            elif lay.mode == "full":
                 ref = oracle.index_scores_dense(qi[j:j + 1], wi[j:j + 1], kr, zero, seq0, pos1,
                                                 wl.ratio, run.n_cols)
                 g = _np(run.scores[t:t + 1, :run.n_cols])

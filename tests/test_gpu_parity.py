@@ -879,3 +879,51 @@ def test_graph_replay_matches_eager(concurrent):
             assert torch.equal(a, b), f"replay {rep} differs"
         run.run()              # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("k_fmt", ["fp8", "fp4s16"])
+def test_full_layer_rescore_route_equals_dense_route(k_fmt):
+    """A Full layer that writes only its block maxima, ranks its best blocks
+    (csa2_top_blocks_and_block_candidates) and takes its top-k among their
+    keys scored again gives exactly the dense route's top-k, pool and
+    attention: the re-scored keys carry the dense scores bit for bit, and the
+    k best entries lie in the k best blocks.  Ragged sequences, one shorter
+    than k keys, and ratio 2."""
+    _announce(f"Full-layer re-scoring route {k_fmt}")
+    for ratio in (1, 2):
+        wl = synth.mini_workload(91 + ratio, [9000, 3000, 300], q_per_seq=2, ratio=ratio,
+                                 modes=("full", "reindex"), k_fmt=k_fmt).to(DEV)
+        dense = LayerRunner(wl, rescore=False)
+        top = LayerRunner(wl, rescore=True)
+        assert top.rescore and not dense.rescore
+        dense.run()
+        top.run()
+        torch.cuda.synchronize()
+        assert "index_scores_top" in [n for n, _ in top.steps()]
+        for li in dense.idx:
+            assert torch.equal(dense.idx[li], top.idx[li]), (ratio, li)
+        assert torch.equal(dense.cand, top.cand)
+        for a, b in zip(dense.out, top.out):
+            assert torch.equal(a, b)
+        # the best blocks' re-scored keys equal the dense scores at their columns
+        bs = wl.block_size
+        tb = _np(top.top_blocks)
+        ts = _np(top.top_scores[:, :top.top_cols])
+        ds = _np(dense.scores[:, :dense.n_cols])
+        for t in range(wl.Q):
+            for i, blk in enumerate(tb[t]):
+                if blk < 0:
+                    assert np.all(ts[t, i * bs:(i + 1) * bs] == -np.inf)
+                    continue
+                cols = np.arange(blk * bs, min((blk + 1) * bs, dense.n_cols))
+                assert np.array_equal(ts[t, i * bs:i * bs + len(cols)], ds[t, cols]), (ratio, t, blk)
+        # the best blocks are the k best by maximum, ascending
+        bm = _np(dense.block_max)
+        nvis = oracle.visible_count(_np(wl.q_pos), wl.ratio)
+        for t in range(wl.Q):
+            nb = -(-int(nvis[t]) // bs)
+            m = bm[t, :nb].astype(np.float64)
+            order = sorted(range(nb), key=lambda j: (-m[j], j))
+            want = sorted(j for j in order[:wl.topk] if m[j] > -np.inf)
+            got = [int(x) for x in tb[t] if x >= 0]
+            assert got == want, (ratio, t)

@@ -21,7 +21,8 @@ EXPORTED = ("csa2_index_scores", "csa2_block_candidates", "csa2_block_candidates
             "csa2_topk_and_block_candidates_workspace_size",
             "csa2_topk_and_block_candidates_noalloc", "csa2_noalloc_scratch_bytes",
             "csa2_diag_index_scores_fp8_mfma", "csa2_diag_stream_read", "csa2_diag_stream_write",
-            "csa2_diag_mfma_valu",
+            "csa2_diag_mfma_valu", "csa2_top_blocks_and_block_candidates",
+            "csa2_top_blocks_and_block_candidates_workspace_size",
             "csa2_topk_from_block_max", "csa2_topk_from_block_max_workspace_size", "csa2_sparse_attn",
             "csa2_sparse_attn_workspace_size", "csa2_cache_write",
             "csa2_status_string", "csa2_last_error", "csa2_version")
@@ -88,6 +89,10 @@ def load():
     lib.csa2_diag_stream_read.argtypes = [P, SZ, P, SZ, P]
     lib.csa2_diag_stream_write.argtypes = [P, SZ, ctypes.c_float, P]
     lib.csa2_diag_mfma_valu.argtypes = [I32, I32, P, SZ, P]
+    lib.csa2_top_blocks_and_block_candidates.argtypes = [P, I64, I32, P, I32, I32, I32, P, I32, P, P, SZ,
+                                                         I32, P]
+    lib.csa2_top_blocks_and_block_candidates_workspace_size.argtypes = [I32, I32, I32, I32, I32]
+    lib.csa2_top_blocks_and_block_candidates_workspace_size.restype = SZ
     lib.csa2_topk_from_block_max.argtypes = [P, I64, I32, P, I64, P, I32, I32, I32, P, P, SZ, I32, PP, P]
     lib.csa2_topk_from_block_max_workspace_size.argtypes = [I32, I32, I32, I32]
     lib.csa2_topk_from_block_max_workspace_size.restype = SZ
@@ -109,6 +114,7 @@ def load():
                "csa2_topk_and_block_candidates", "csa2_topk_and_block_candidates_noalloc",
                "csa2_diag_index_scores_fp8_mfma", "csa2_diag_stream_read", "csa2_diag_stream_write",
                "csa2_diag_mfma_valu", "csa2_topk_from_block_max", "csa2_sparse_attn", "csa2_cache_write",
+               "csa2_top_blocks_and_block_candidates",
                "csa2_version"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
@@ -192,7 +198,7 @@ def csa2_index_scores(q_rows, w, w_dtype, k_rows, seq_base, q_seq, q_pos, ratio,
     bms = 0 if block_max is None else block_max.stride(0)
     _check(lib.csa2_index_scores(ctypes.byref(q_rows), _ptr(w), w_dtype, ctypes.byref(k_rows),
                                  _ptr(seq_base), _ptr(q_seq), _ptr(q_pos), ratio, _ptr(cand), ncb,
-                                 block_size, _ptr(scores), scores.stride(0), n_cols,
+                                 block_size, _ptr(scores), 0 if scores is None else scores.stride(0), n_cols,
                                  _ptr(block_max), bms, Q, H_I, d_I, _byref(pages),
                                  _stream(stream)))
 
@@ -298,6 +304,21 @@ def csa2_topk_and_block_candidates(scores, n_cols, q_pos, ratio, k, idx, block_s
                                               _ptr(idx), block_size, n_blocks, _ptr(cand),
                                               _ptr(workspace), wsb, Q, _byref(pages),
                                               _stream(stream)))
+
+
+def csa2_top_blocks_and_block_candidates_workspace_size(Q, n_cols, block_size, k_blocks, n_blocks):
+    return load().csa2_top_blocks_and_block_candidates_workspace_size(Q, n_cols, block_size, k_blocks,
+                                                                      n_blocks)
+
+
+def csa2_top_blocks_and_block_candidates(block_max, n_cols, q_pos, ratio, block_size, k_blocks,
+                                         top_blocks, n_blocks, cand, workspace, Q, stream=None):
+    lib = load()
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.csa2_top_blocks_and_block_candidates(_ptr(block_max), block_max.stride(0), n_cols,
+                                                    _ptr(q_pos), ratio, block_size, k_blocks,
+                                                    _ptr(top_blocks), n_blocks, _ptr(cand),
+                                                    _ptr(workspace), wsb, Q, _stream(stream)))
 
 
 def csa2_sparse_attn_workspace_size(Q, H, k, window):

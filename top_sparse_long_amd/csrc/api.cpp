@@ -71,8 +71,9 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
                       int64_t block_max_stride, int32_t Q, int32_t H_I, int32_t d_I,
                       const csa2_pages* pages, void* stream) {
   g_err[0] = 0;
-  REQUIRE(q_idx && k_idx && w && (seq_base || pages) && q_seq && q_pos && scores, CSA2_ERR_INVALID_ARG,
-          "csa2_index_scores: null pointer argument");
+  REQUIRE(q_idx && k_idx && w && (seq_base || pages) && q_seq && q_pos && (scores || block_max),
+          CSA2_ERR_INVALID_ARG, "csa2_index_scores: null pointer argument");
+  REQUIRE(scores || !cand, CSA2_ERR_INVALID_ARG, "csa2_index_scores: pool mode writes scores (null scores)");
   if (pages)
     REQUIRE(pages->table && pages->table_stride >= 1 && pages->n_pages >= 1 && pages->page_stride >= 0 &&
                 pages->page_stride % 16 == 0,
@@ -89,9 +90,11 @@ int csa2_index_scores(const csa2_rows* q_idx, const void* w, csa2_dtype w_dtype,
   REQUIRE(q_idx->dtype == k_idx->dtype || (q_idx->dtype == CSA2_FP8_E4M3 && k_fp4),
           CSA2_ERR_UNSUPPORTED,
           "csa2_index_scores: k_idx must share q_idx's dtype (or be FP4_E2M1_E4M3S16 with FP8 q_idx)");
-  REQUIRE(score_stride >= n_cols && score_stride % 4 == 0, CSA2_ERR_INVALID_ARG,
-          "csa2_index_scores: score_stride must be >= n_cols and a multiple of 4");
-  REQUIRE(aligned(scores, 16), CSA2_ERR_INVALID_ARG, "csa2_index_scores: scores must be 16-byte aligned");
+  if (scores) {
+    REQUIRE(score_stride >= n_cols && score_stride % 4 == 0, CSA2_ERR_INVALID_ARG,
+            "csa2_index_scores: score_stride must be >= n_cols and a multiple of 4");
+    REQUIRE(aligned(scores, 16), CSA2_ERR_INVALID_ARG, "csa2_index_scores: scores must be 16-byte aligned");
+  }
   REQUIRE(aligned(q_idx->data, 16) && aligned(k_idx->data, 16) && q_idx->row_stride % 16 == 0 &&
               k_idx->row_stride % 16 == 0 && q_idx->row_stride > 0 && k_idx->row_stride > 0,
           CSA2_ERR_INVALID_ARG, "csa2_index_scores: rows must be 16-byte aligned");
@@ -525,6 +528,37 @@ int csa2_topk_and_block_candidates(const float* scores, int64_t score_stride, in
   return topk_and_blocks(scores, score_stride, n_cols, block_max, block_max_stride, q_pos, ratio, k,
                          idx, block_size, n_blocks, cand, workspace, workspace_bytes, Q, pages,
                          stream, false);
+}
+
+size_t csa2_top_blocks_and_block_candidates_workspace_size(int32_t Q, int32_t n_cols, int32_t block_size,
+                                                           int32_t k_blocks, int32_t n_blocks) {
+  return align16(csa2_block_candidates_workspace_size(Q, n_cols, block_size, k_blocks)) +
+         csa2_block_candidates_workspace_size(Q, n_cols, block_size, n_blocks);
+}
+
+int csa2_top_blocks_and_block_candidates(const float* block_max, int64_t block_max_stride, int32_t n_cols,
+                                         const int32_t* q_pos, int32_t ratio, int32_t block_size,
+                                         int32_t k_blocks, int32_t* top_blocks, int32_t n_blocks,
+                                         int32_t* cand, void* workspace, size_t workspace_bytes, int32_t Q,
+                                         void* stream) {
+  g_err[0] = 0;
+  REQUIRE(block_max && top_blocks && cand, CSA2_ERR_INVALID_ARG,
+          "csa2_top_blocks_and_block_candidates: null pointer argument");
+  // the best blocks' workspace comes first, the candidates' follows at a
+  // 16-byte boundary
+  const size_t ws_t = align16(csa2_block_candidates_workspace_size(Q, n_cols, block_size, k_blocks));
+  const size_t ws_b = workspace_bytes > ws_t ? workspace_bytes - ws_t : 0;
+  csa2::SelectArgs at, ab;
+  int64_t n_rows = 0;
+  int st = prep_block_candidates(nullptr, 0, n_cols, block_max, block_max_stride, q_pos, ratio, block_size,
+                                 k_blocks, top_blocks, workspace, workspace_bytes < ws_t ? workspace_bytes : ws_t,
+                                 Q, &at, &n_rows);
+  if (st != CSA2_OK) return st;
+  st = prep_block_candidates(nullptr, 0, n_cols, block_max, block_max_stride, q_pos, ratio, block_size,
+                             n_blocks, cand, ws_b ? (uint8_t*)workspace + ws_t : nullptr, ws_b, Q, &ab, &n_rows);
+  if (st != CSA2_OK || Q == 0 || n_rows == 0) return st;
+  return hip_status(csa2::launch_top_blocks_and_blocks(at, ab, n_rows, (hipStream_t)stream),
+                    "csa2_top_blocks_and_block_candidates");
 }
 
 size_t csa2_noalloc_scratch_bytes(void) { return csa2::SELECT_SCRATCH_BYTES; }

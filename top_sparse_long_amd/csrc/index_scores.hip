@@ -172,7 +172,9 @@ __device__ __forceinline__ float group_max(float m, int bs) {
   return m;
 }
 
-template <bool POOL, bool W_BF16, bool K4, bool PAGED, int TILES>
+// SC: the scores are written (otherwise only the block maxima: a call that
+// re-scores the best blocks' keys instead of reading the scores back).
+template <bool POOL, bool W_BF16, bool K4, bool PAGED, int TILES, bool SC>
 __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexScoreArgs a) {
   constexpr int SUB = IS_WAVES * 32 * TILES;   // columns per sub-chunk
   const int t = blockIdx.y;
@@ -190,7 +192,7 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
   const int col_begin = blockIdx.x * SUB;
   const int col_end = a.n_cols;
   const int col_step = gridDim.x * SUB;
-  float* out = a.scores + (int64_t)t * a.score_stride;
+  float* out = SC ? a.scores + (int64_t)t * a.score_stride : nullptr;
   // Dense mode: columns past the visible prefix only need -inf.
   const int limit = (nvis <= 0) ? 0 : (POOL ? a.n_cols : min(a.n_cols, nvis));
 
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
         // carry their scales inside the operands
         sc = (S.pos[i] >= 0) ? (K4 ? v : v * S.ks[i]) : -INFINITY;
       }
-      if (half == 0 && col < a.n_cols) out[col] = sc;
+      if (SC && half == 0 && col < a.n_cols) out[col] = sc;
       if (!POOL && a.block_max) {
         // maximum over aligned groups of block_size lanes (block_size <= 32)
         const float m = group_max(sc, 1 << a.block_shift);
@@ -415,13 +417,15 @@ __global__ __launch_bounds__(64 * PF_WAVES) void index_scores_prefill_kernel(Ind
     for (int i = 0; i < 2; ++i) {
       if (!(i ? act1 : act0)) continue;
       const v4f v = *(const v4f*)&s_out[wave][i][c];
-      float* dst = a.scores + (int64_t)tq[i] * a.score_stride + colb + c;
-      if (vec_out && c + 4 <= ncols) {
-        *(v4f*)dst = v;
-      } else {
+      if (a.scores) {
+        float* dst = a.scores + (int64_t)tq[i] * a.score_stride + colb + c;
+        if (vec_out && c + 4 <= ncols) {
+          *(v4f*)dst = v;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (c + e < ncols) dst[e] = v[e];
+          for (int e = 0; e < 4; ++e)
+            if (c + e < ncols) dst[e] = v[e];
+        }
       }
       if (a.block_max) {
         const int bs = 1 << bshift;
@@ -657,7 +661,7 @@ __global__ __launch_bounds__(256) void index_scores_f32_kernel(IndexScoreArgs a)
       tot = fmaf(sw[h], fmaxf(dot, 0.f), tot);
     }
   }
-  if (col < a.n_cols) out[col] = tot;
+  if (a.scores && col < a.n_cols) out[col] = tot;
   if (!POOL && a.block_max) {
     // 256 consecutive columns per workgroup: wave-level groups of block_size
     float m = tot;
@@ -683,7 +687,7 @@ static void launch_prefill(const IndexScoreArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((index_scores_prefill_kernel<W_BF16, K4, PAGED>), grid, dim3(64 * PF_WAVES), 0, s, b);
 }
 
-template <bool POOL, bool W_BF16, bool K4, bool PAGED, int TILES>
+template <bool POOL, bool W_BF16, bool K4, bool PAGED, int TILES, bool SC>
 static void launch_decode_t(const IndexScoreArgs& a, hipStream_t s) {
   // sub-chunks per workgroup: enough workgroups for about one resident
   // round, each striding over the sub-chunks of one query's row
@@ -692,15 +696,21 @@ static void launch_decode_t(const IndexScoreArgs& a, hipStream_t s) {
   const int64_t subs = (a.n_cols + SUB - 1) / SUB;
   b.sub_per_wg = (int)std::max<int64_t>(1, (subs * a.Q + IS_RESIDENT_WGS - 1) / IS_RESIDENT_WGS);
   dim3 grid((unsigned)((subs + b.sub_per_wg - 1) / b.sub_per_wg), a.Q);
-  hipLaunchKernelGGL((index_scores_fp8_kernel<POOL, W_BF16, K4, PAGED, TILES>), grid, dim3(64 * IS_WAVES), 0, s, b);
+  hipLaunchKernelGGL((index_scores_fp8_kernel<POOL, W_BF16, K4, PAGED, TILES, SC>), grid, dim3(64 * IS_WAVES), 0, s, b);
+}
+
+template <bool POOL, bool W_BF16, bool K4, bool PAGED, bool SC>
+static void launch_decode_sc(const IndexScoreArgs& a, hipStream_t s) {
+  if (!POOL && (int64_t)a.n_cols * a.Q <= IS_ONE_TILE_MAX_KEYS)
+    launch_decode_t<POOL, W_BF16, K4, PAGED, 1, SC>(a, s);
+  else
+    launch_decode_t<POOL, W_BF16, K4, PAGED, IS_TILES, SC>(a, s);
 }
 
 template <bool POOL, bool W_BF16, bool K4, bool PAGED>
 static void launch_decode(const IndexScoreArgs& a, hipStream_t s) {
-  if (!POOL && (int64_t)a.n_cols * a.Q <= IS_ONE_TILE_MAX_KEYS)
-    launch_decode_t<POOL, W_BF16, K4, PAGED, 1>(a, s);
-  else
-    launch_decode_t<POOL, W_BF16, K4, PAGED, IS_TILES>(a, s);
+  if (POOL || a.scores) launch_decode_sc<POOL, W_BF16, K4, PAGED, true>(a, s);
+  else launch_decode_sc<POOL, W_BF16, K4, PAGED, false>(a, s);
 }
 
 template <bool K4, bool PAGED>

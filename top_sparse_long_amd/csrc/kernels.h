@@ -145,6 +145,11 @@ hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, bool
 bool top_via_blocks_supported(int k, int block_shift);
 size_t top_via_blocks_workspace_bytes(int Q, int64_t n_blocks, int k);
 hipError_t launch_topk_via_blocks(const SelectArgs& a, int64_t n_blocks, hipStream_t s);
+// The k best blocks by maximum (top.k of them, none forced, block indices
+// to top.out_idx) and the block candidates of the same n_rows maxima, in
+// shared launches; separate workspaces.
+hipError_t launch_top_blocks_and_blocks(const SelectArgs& top, const SelectArgs& blocks, int64_t n_rows,
+                                        hipStream_t s);
 
 // Sparse attention -----------------------------------------------------------
 struct AttnArgs {

@@ -808,4 +808,22 @@ hipError_t launch_topk_and_blocks(const SelectArgs& topk, int64_t topk_len, bool
   return hipSuccess;
 }
 
+// The best blocks (SEL_BLOCKTOP, no block forced) and the block candidates
+// (SEL_BLOCKMAX) of the same block maxima, in shared launches aligned at
+// their starts; both final stages write block indices.
+hipError_t launch_top_blocks_and_blocks(const SelectArgs& top, const SelectArgs& blocks, int64_t n_rows,
+                                        hipStream_t s) {
+  Stage t[SEL_MAX_STAGES], b[SEL_MAX_STAGES];
+  const int nt = make_stages(SEL_BLOCKTOP, top, n_rows, t);
+  const int nb = make_stages(SEL_BLOCKMAX, blocks, n_rows, b);
+  for (int j = 0; j < max(nt, nb); ++j) {
+    hipError_t e;
+    if (j < nt && j < nb) e = launch_pair(t[j], b[j], top.Q, s);
+    else if (j < nt) e = launch_one(t[j], top.Q, s);
+    else e = launch_one(b[j], top.Q, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace csa2

@@ -25,9 +25,18 @@ from . import (csa2_index_scores, csa2_block_candidates, csa2_topk, csa2_sparse_
                csa2_block_candidates_workspace_size, csa2_topk_workspace_size,
                csa2_sparse_attn_workspace_size, csa2_rows, csa2_pages,
                csa2_topk_from_block_max, csa2_topk_from_block_max_workspace_size,
+               csa2_top_blocks_and_block_candidates, csa2_top_blocks_and_block_candidates_workspace_size,
                rows_f32, rows_fp8, rows_fp4s16, rows_fp4_records, rows_fp4s16_records,
                rows_swa_records,
                CSA2_F32, CSA2_BF16, CSA2_FP8_E4M3, CSA2_FP4_E2M1_E4M3S16)
+
+
+# the re-scoring route for a Full layer's top-k (see LayerRunner): measured
+# per step, 64 x 262,144 keys 732.9 -> 680.8 us; 8 x 131,072 106.1 -> 108.6,
+# 2 x 1,048,576 148.6 -> 151.2 (the two extra launches cost more than the
+# score writes they save below some 8M keys per call)
+RESCORE_MAX_Q = 256
+RESCORE_MIN_KEYS = 8 << 20
 
 
 def _round_up(x, m):
@@ -51,7 +60,7 @@ class LayerRunner:
     slot; rope_cs: an optional [positions, 64] table — attention turns its
     output back by each query's position (the layout's table when paged)."""
 
-    def __init__(self, wl, device="cuda", paged=None, rope_cs=None, via_blocks=True):
+    def __init__(self, wl, device="cuda", paged=None, rope_cs=None, via_blocks=True, rescore=None):
         self.wl = wl
         self.dev = device
         self.paged = paged
@@ -98,6 +107,19 @@ class LayerRunner:
         self.block_max = torch.empty((Q, _round_up(max(nbm, 1), 64)), dtype=f32, device=device)
         self.pool_scores = torch.empty((Q, _round_up(self.pool_cols, 64)), dtype=f32, device=device)
         self.cand = torch.empty((Q, wl.n_blocks), dtype=torch.int32, device=device)
+        # A pool-building Full layer may skip writing its scores: the block
+        # maxima rank its best blocks, whose keys are scored again (pool
+        # mode, the same arithmetic, so the same values) and selected from.
+        # Worth it where the score writes cost more than the extra launches:
+        # decode batches (the query-tiled prefill scorer stages its writes)
+        # with many keys per call.
+        if rescore is None:
+            rescore = (self.quant and Q < RESCORE_MAX_Q and Q * self.n_cols >= RESCORE_MIN_KEYS)
+        self.rescore = bool(rescore) and self.quant and self.fuse_block_max and wl.topk <= 4096
+        self.top_cols = wl.topk * wl.block_size
+        self.top_blocks = torch.empty((Q, wl.topk), dtype=torch.int32, device=device)
+        self.top_scores = (torch.empty((Q, _round_up(self.top_cols, 64)), dtype=f32, device=device)
+                           if self.rescore else None)
         self.idx = {li: torch.empty((Q, wl.topk), dtype=torch.int32, device=device)
                     for li, l in enumerate(wl.layers) if l.mode in ("full", "reindex")}
         ws = max(csa2_topk_workspace_size(Q, self.n_cols, wl.topk),
@@ -105,7 +127,10 @@ class LayerRunner:
                  csa2_block_candidates_workspace_size(Q, self.n_cols, wl.block_size, wl.n_blocks),
                  csa2_topk_and_block_candidates_workspace_size(Q, self.n_cols, wl.topk,
                                                                wl.block_size, wl.n_blocks),
-                 csa2_topk_from_block_max_workspace_size(Q, self.n_cols, wl.topk, wl.block_size))
+                 csa2_topk_from_block_max_workspace_size(Q, self.n_cols, wl.topk, wl.block_size),
+                 csa2_top_blocks_and_block_candidates_workspace_size(Q, self.n_cols, wl.block_size, wl.topk,
+                                                                     wl.n_blocks) if self.rescore else 0,
+                 csa2_topk_workspace_size(Q, self.top_cols, wl.topk) if self.rescore else 0)
         self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=device)
         # block candidates may run beside the Full layer's top-k on a second
         # stream, so they get a workspace of their own
@@ -139,17 +164,24 @@ class LayerRunner:
         self.slots = SlotSet(self.main_rows, self.k_rows)
 
     # -- steps -----------------------------------------------------------------
-    def index_scores(self, li, pool, block_max=False):
+    def index_scores(self, li, pool, block_max=False, scores=True):
         wl, lay = self.wl, self.wl.layers[li]
         wdt = CSA2_BF16 if self.quant else CSA2_F32
-        if pool:
+        if pool == "top":
+            # the keys of the Full layer's best blocks, scored again
+            csa2_index_scores(self.layer_rows[li]["q_idx"], lay.w, wdt, self.slots.index_k,
+                              wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio, self.top_scores,
+                              self.top_cols, self.Q, cand=self.top_blocks,
+                              block_size=wl.block_size, pages=self.pages_scores)
+        elif pool:
             csa2_index_scores(self.layer_rows[li]["q_idx"], lay.w, wdt, self.slots.index_k,
                               wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio, self.pool_scores,
                               self.pool_cols, self.Q, cand=self.slots.candidates,
                               block_size=wl.block_size, pages=self.pages_scores)
         else:
             csa2_index_scores(self.layer_rows[li]["q_idx"], lay.w, wdt, self.slots.index_k,
-                              wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio, self.scores,
+                              wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio,
+                              self.scores if scores else None,
                               self.n_cols, self.Q, block_size=wl.block_size,
                               block_max=self.block_max if block_max else None,
                               pages=self.pages_scores)
@@ -175,6 +207,23 @@ class LayerRunner:
         else:
             csa2_topk(self.scores, self.n_cols, wl.q_pos, wl.ratio, wl.topk, idx, self.ws, self.Q,
                       pages=self.pages_topk)
+        self.slots.topk_idxs = idx
+
+    def top_blocks_and_blocks(self):
+        """The Full layer's best blocks and the candidate pool, from its block
+        maxima (no scores written)."""
+        wl = self.wl
+        csa2_top_blocks_and_block_candidates(self.block_max, self.n_cols, wl.q_pos, wl.ratio,
+                                             wl.block_size, wl.topk, self.top_blocks, wl.n_blocks,
+                                             self.cand, self.ws, self.Q)
+        self.slots.candidates = self.cand
+
+    def topk_top(self, li):
+        """The Full layer's top-k among its best blocks' re-scored keys."""
+        wl = self.wl
+        idx = self.idx[li]
+        csa2_topk(self.top_scores, self.top_cols, None, wl.ratio, wl.topk, idx, self.ws, self.Q,
+                  cand=self.top_blocks, block_size=wl.block_size, pages=self.pages_topk)
         self.slots.topk_idxs = idx
 
     def topk_and_blocks(self, li, from_block_max=False):
@@ -207,7 +256,11 @@ class LayerRunner:
         """The calls of one pass over every layer, in order, as (stage name,
         callable) pairs.
 
-        A Full layer's dense scoring writes the block maxima when its top-k
+        With rescore, a pool-building Full layer writes only its block
+        maxima; csa2_top_blocks_and_block_candidates ranks its best blocks and
+        the pool, and its top-k is taken among the best blocks' keys scored
+        again (the same values, so the same top-k).  Otherwise a Full layer's
+        dense scoring writes the block maxima when its top-k
         ranks blocks first (via_blocks) or a later layer needs the pool; the
         selections then read those maxima.  A Full layer that builds the pool
         makes both of its selections with one call
@@ -237,7 +290,14 @@ class LayerRunner:
         last_scoring = max((i for i, l in enumerate(layers) if l.mode in ("full", "reindex")), default=-1)
         joined = False
         for li, lay in enumerate(layers):
-            if lay.mode == "full":
+            if lay.mode == "full" and self.rescore and self.needs_pool[li] and not separate_select:
+                out.append(("index_scores_dense",
+                            lambda li=li: self.index_scores(li, pool=False, block_max=True, scores=False)))
+                out.append(("top_blocks_and_blocks", self.top_blocks_and_blocks))
+                out.append(("index_scores_top", lambda li=li: self.index_scores(li, pool="top")))
+                out.append(("topk_top", lambda li=li: self.topk_top(li)))
+                has_pool = True
+            elif lay.mode == "full":
                 fuse = self.fuses_block_max(li)
                 out.append(("index_scores_dense",
                             lambda li=li, fuse=fuse: self.index_scores(li, pool=False, block_max=fuse)))

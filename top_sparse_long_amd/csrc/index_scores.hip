@@ -262,10 +262,15 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
     }
   };
 
+  // The loads are unconditional: sub-chunks past the row's end read row 0
+  // (every column there has position -1) and are never used.  A load under
+  // a branch would make the wait before each contraction count for the
+  // worst path, which is to say for the next sub-chunk's rows as well.
+  // (start columns clamped to the row's end, so nothing overflows)
+  auto ahead = [&](int c, int n) { return (int)min((int64_t)c + (int64_t)n * col_step, (int64_t)col_end); };
   Sub buf[IS_NBUF];
 #pragma unroll
-  for (int k = 0; k + 1 < IS_NBUF; ++k)
-    if (col_begin + k * col_step < col_end) load_sub(col_begin + k * col_step, buf[k]);
+  for (int k = 0; k + 1 < IS_NBUF; ++k) load_sub(ahead(col_begin, k), buf[k]);
 
   // A operand widened to f16; gate of head r with the q scale folded in,
   // then the 16 heads this lane's accumulators hold.
@@ -320,8 +325,7 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
     for (int ph = 0; ph < IS_NBUF; ++ph) {
       const int cc = c0 + ph * col_step;
       if (cc >= col_end) break;
-      const int cn = cc + (IS_NBUF - 1) * col_step;
-      if (cn < col_end) load_sub(cn, buf[(ph + IS_NBUF - 1) % IS_NBUF]);
+      load_sub(ahead(cc, IS_NBUF - 1), buf[(ph + IS_NBUF - 1) % IS_NBUF]);
       compute_sub(cc, buf[ph]);
     }
   }

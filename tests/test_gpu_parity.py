@@ -844,6 +844,37 @@ def test_fused_block_max_sizes(bs, many):
         assert np.all(bm[t, len(ref):] == -np.inf), t
 
 
+@pytest.mark.parametrize("big", [False, True])
+@pytest.mark.parametrize("bs", [8, 32])
+def test_block_max_without_scores(bs, big):
+    """Dense scoring that writes only the block maxima (the decode kernel
+    with a storing wave) gives the maxima of the call that also writes the
+    scores, bit for bit: on the one-tile kernel and on the two-tile one
+    (above 1.5M keys), with ragged row ends and a query that sees nothing
+    (position 0 at m = 2), whose maxima are all -inf."""
+    _announce(f"block maxima without scores bs={bs} big={big}")
+    n = [900_003, 700_001] if big else [50_001, 9_001]
+    pos = [[2 * n[0] - 1, 0], [2 * n[1] - 1 - 999, 2 * 5_000 + 1]]
+    wl = synth.mini_workload(45, n, q_per_seq=2, ratio=2, block_size=bs, positions=pos).to(DEV)
+    run = LayerRunner(wl)
+    run.index_scores(0, pool=False, block_max=True)
+    torch.cuda.synchronize()
+    nb = -(-run.n_cols // bs)
+    ref = run.block_max[:, :nb].clone()
+    g = _np(run.scores[:, :run.n_cols]).astype(np.float64)
+    run.block_max.fill_(7.0)
+    run.index_scores(0, pool=False, block_max=True, scores=False)
+    torch.cuda.synchronize()
+    assert torch.equal(run.block_max[:, :nb], ref)
+    nvis = oracle.visible_count(_np(wl.q_pos), 2)
+    assert int(nvis.min()) == 0
+    refn = _np(ref).astype(np.float64)
+    for t in range(wl.Q):
+        r = oracle.block_maxima(g[t], int(nvis[t]), bs)
+        assert np.array_equal(refn[t, :len(r)], r), t
+        assert np.all(refn[t, len(r):] == -np.inf), t
+
+
 @pytest.mark.parametrize("concurrent", [False, True])
 def test_graph_replay_matches_eager(concurrent):
     """A captured pass (optionally with every attention call on a second

@@ -67,6 +67,12 @@ constexpr int IS_RESIDENT_WGS = CSA2_IS_RESIDENT;            // about one round 
 // sub-chunk buffers per wave (measured on 64 x 256K keys: 2 buffers 469 us,
 // 3 557 us, 4 555 us -- the extra registers cost occupancy)
 constexpr int IS_NBUF = CSA2_IS_NBUF;
+#ifndef CSA2_IS_UF
+#define CSA2_IS_UF 4
+#endif
+// Calls that write only block maxima: sub-chunks per batch handed to the
+// storing wave (measured on 64 x 256K keys: 2, 4 and 8 within 1 %)
+constexpr int IS_UF = CSA2_IS_UF;
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(((uint32_t)b) << 16);
@@ -174,12 +180,24 @@ __device__ __forceinline__ float group_max(float m, int bs) {
 
 // SC: the scores are written (otherwise only the block maxima: a call that
 // re-scores the best blocks' keys instead of reading the scores back).
+//
+// Calls without scores (dense, block maxima only) add a fifth, storing
+// wave: the four scoring waves hand each batch of IS_UF sub-chunks' scores
+// over in LDS (one barrier per batch), and the storing wave writes the
+// block maxima of whole sub-chunks, 16-32 consecutive values per store
+// instead of 4 per tile and wave.  Measured on 64 x 256K keys: 399 -> 372
+// us (stores removed altogether: 355 us).  With scores written (the
+// smaller decode calls) the same hand-over measured slower (128K x 8
+// queries 31.5 -> 33.7 us), so those waves store their own tiles.
 template <bool POOL, bool W_BF16, bool K4, bool PAGED, int TILES, bool SC>
-__global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexScoreArgs a) {
+__global__ __launch_bounds__(64 * (SC ? IS_WAVES : IS_WAVES + 1)) void index_scores_fp8_kernel(IndexScoreArgs a) {
   constexpr int SUB = IS_WAVES * 32 * TILES;   // columns per sub-chunk
+  constexpr bool SW = !SC;                     // a storing wave
+  static_assert(!(POOL && SW), "pool calls always write their scores");
+  __shared__ __attribute__((aligned(16))) float s_res[SW ? 2 : 1][SW ? IS_UF * SUB : 1];   // a batch's scores, by column
   const int t = blockIdx.y;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5;
   const int r = lane & 31;
 
@@ -193,6 +211,7 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
   const int col_end = a.n_cols;
   const int col_step = gridDim.x * SUB;
   float* out = SC ? a.scores + (int64_t)t * a.score_stride : nullptr;
+  float* bm_row = (!POOL && a.block_max) ? a.block_max + (int64_t)t * a.block_max_stride : nullptr;
   // Dense mode: columns past the visible prefix only need -inf.
   const int limit = (nvis <= 0) ? 0 : (POOL ? a.n_cols : min(a.n_cols, nvis));
 
@@ -215,11 +234,36 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
   if (limit == 0) {
     // nothing visible: every column of this workgroup is -inf
     for (int c0 = col_begin; c0 < col_end; c0 += col_step)
-      for (int c = c0 + threadIdx.x; c < min(col_end, c0 + SUB); c += 64 * IS_WAVES) {
-        out[c] = -INFINITY;
-        if (!POOL && a.block_max && (c & ((1 << a.block_shift) - 1)) == 0)
-          a.block_max[(int64_t)t * a.block_max_stride + (c >> a.block_shift)] = -INFINITY;
+      for (int c = c0 + threadIdx.x; c < min(col_end, c0 + SUB); c += blockDim.x) {
+        if (SC) out[c] = -INFINITY;
+        if (bm_row && (c & ((1 << a.block_shift) - 1)) == 0) bm_row[c >> a.block_shift] = -INFINITY;
       }
+    return;
+  }
+
+  // start column n sub-chunks on, clamped to the row's end (no overflow)
+  auto ahead = [&](int c, int n) { return (int)min((int64_t)c + (int64_t)n * col_step, (int64_t)col_end); };
+  if (SW && wave == IS_WAVES) {
+    // the storing wave: one barrier per batch, then the batch's block
+    // maxima from LDS (vector memory operations complete in order per wave,
+    // so no scoring wave's wait for key rows includes a store)
+    for (int c0 = col_begin, it = 0; c0 < col_end; c0 += IS_UF * col_step, ++it) {
+      __syncthreads();
+      if (!bm_row) continue;
+      const float* res = s_res[it & 1];
+      const int sh = a.block_shift;
+#pragma unroll
+      for (int ph = 0; ph < IS_UF; ++ph) {
+        const int sc0 = ahead(c0, ph);
+        if (sc0 >= col_end) break;
+        for (int j = lane; j < (SUB >> sh); j += 64) {
+          const float* v = res + ph * SUB + (j << sh);
+          float m = v[0];
+          for (int e = 1; e < (1 << sh); ++e) m = fmaxf(m, v[e]);
+          if (sc0 + (j << sh) < col_end) bm_row[(sc0 >> sh) + j] = m;
+        }
+      }
+    }
     return;
   }
 
@@ -266,8 +310,6 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
   // (every column there has position -1) and are never used.  A load under
   // a branch would make the wait before each contraction count for the
   // worst path, which is to say for the next sub-chunk's rows as well.
-  // (start columns clamped to the row's end, so nothing overflows)
-  auto ahead = [&](int c, int n) { return (int)min((int64_t)c + (int64_t)n * col_step, (int64_t)col_end); };
   Sub buf[IS_NBUF];
 #pragma unroll
   for (int k = 0; k + 1 < IS_NBUF; ++k) load_sub(ahead(col_begin, k), buf[k]);
@@ -285,7 +327,7 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
 #pragma unroll
   for (int j = 0; j < 16; ++j) gate[j] = __shfl(g_r, 8 * (j >> 2) + 4 * half + (j & 3));
 
-  auto compute_sub = [&](int sc0, const Sub& S) {
+  auto compute_sub = [&](int sc0, const Sub& S, float (&scs)[TILES]) {
 #pragma unroll
     for (int i = 0; i < TILES; ++i) {
       const int tcol = sc0 + (i * IS_WAVES + wave) * 32;
@@ -306,12 +348,13 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
         // carry their scales inside the operands
         sc = (S.pos[i] >= 0) ? (K4 ? v : v * S.ks[i]) : -INFINITY;
       }
+      scs[i] = sc;
+      if (SW) continue;
       if (SC && half == 0 && col < a.n_cols) out[col] = sc;
-      if (!POOL && a.block_max) {
+      if (bm_row) {
         // maximum over aligned groups of block_size lanes (block_size <= 32)
         const float m = group_max(sc, 1 << a.block_shift);
-        if (half == 0 && (r & ((1 << a.block_shift) - 1)) == 0 && col < a.n_cols)
-          a.block_max[(int64_t)t * a.block_max_stride + (col >> a.block_shift)] = m;
+        if (half == 0 && (r & ((1 << a.block_shift) - 1)) == 0 && col < a.n_cols) bm_row[col >> a.block_shift] = m;
       }
     }
   };
@@ -320,14 +363,43 @@ __global__ __launch_bounds__(64 * IS_WAVES) void index_scores_fp8_kernel(IndexSc
   // buffers: the next IS_NBUF - 1 sub-chunks' rows are in flight while the
   // current one is contracted, so HBM stays busy for the whole life of the
   // workgroup.
-  for (int c0 = col_begin; c0 < col_end; c0 += IS_NBUF * col_step) {
+  if (!SW) {
+    for (int c0 = col_begin; c0 < col_end; c0 += IS_NBUF * col_step) {
 #pragma unroll
-    for (int ph = 0; ph < IS_NBUF; ++ph) {
+      for (int ph = 0; ph < IS_NBUF; ++ph) {
+        const int cc = c0 + ph * col_step;
+        if (cc >= col_end) break;
+        load_sub(ahead(cc, IS_NBUF - 1), buf[(ph + IS_NBUF - 1) % IS_NBUF]);
+        float scs[TILES];
+        compute_sub(cc, buf[ph], scs);
+      }
+    }
+    return;
+  }
+  // with a storing wave: batches of IS_UF sub-chunks, their scores handed
+  // over in LDS (the storing wave reads a batch's buffer while the next
+  // batch fills the other)
+  static_assert(IS_UF % IS_NBUF == 0, "a batch is a whole number of rings");
+  for (int c0 = col_begin, it = 0; c0 < col_end; c0 += IS_UF * col_step, ++it) {
+    float scb[IS_UF][TILES];
+#pragma unroll
+    for (int ph = 0; ph < IS_UF; ++ph)
+#pragma unroll
+      for (int i = 0; i < TILES; ++i) scb[ph][i] = -INFINITY;
+#pragma unroll
+    for (int ph = 0; ph < IS_UF; ++ph) {
       const int cc = c0 + ph * col_step;
       if (cc >= col_end) break;
       load_sub(ahead(cc, IS_NBUF - 1), buf[(ph + IS_NBUF - 1) % IS_NBUF]);
-      compute_sub(cc, buf[ph]);
+      compute_sub(cc, buf[ph % IS_NBUF], scb[ph]);
     }
+    if (half == 0) {
+#pragma unroll
+      for (int ph = 0; ph < IS_UF; ++ph)
+#pragma unroll
+        for (int i = 0; i < TILES; ++i) s_res[it & 1][ph * SUB + (i * IS_WAVES + wave) * 32 + r] = scb[ph][i];
+    }
+    __syncthreads();
   }
 }
 
@@ -700,7 +772,8 @@ static void launch_decode_t(const IndexScoreArgs& a, hipStream_t s) {
   const int64_t subs = (a.n_cols + SUB - 1) / SUB;
   b.sub_per_wg = (int)std::max<int64_t>(1, (subs * a.Q + IS_RESIDENT_WGS - 1) / IS_RESIDENT_WGS);
   dim3 grid((unsigned)((subs + b.sub_per_wg - 1) / b.sub_per_wg), a.Q);
-  hipLaunchKernelGGL((index_scores_fp8_kernel<POOL, W_BF16, K4, PAGED, TILES, SC>), grid, dim3(64 * IS_WAVES), 0, s, b);
+  hipLaunchKernelGGL((index_scores_fp8_kernel<POOL, W_BF16, K4, PAGED, TILES, SC>), grid,
+                     dim3(64 * (SC ? IS_WAVES : IS_WAVES + 1)), 0, s, b);
 }
 
 template <bool POOL, bool W_BF16, bool K4, bool PAGED, bool SC>
@@ -713,7 +786,9 @@ static void launch_decode_sc(const IndexScoreArgs& a, hipStream_t s) {
 
 template <bool POOL, bool W_BF16, bool K4, bool PAGED>
 static void launch_decode(const IndexScoreArgs& a, hipStream_t s) {
-  if (POOL || a.scores) launch_decode_sc<POOL, W_BF16, K4, PAGED, true>(a, s);
+  // pool calls always write their scores
+  if constexpr (POOL) launch_decode_sc<POOL, W_BF16, K4, PAGED, true>(a, s);
+  else if (a.scores) launch_decode_sc<POOL, W_BF16, K4, PAGED, true>(a, s);
   else launch_decode_sc<POOL, W_BF16, K4, PAGED, false>(a, s);
 }
 

@@ -265,17 +265,24 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, out_dir, workload, comma
         f.write("\n".join(lines) + "\n")
 
     src = _source_hash()
+    # A Full layer on the re-score route runs the dense scorer without score
+    # stores (its last template argument false); its stages then share
+    # kernels with the pool stages, and the paired selection launch belongs
+    # to top_blocks_and_blocks instead of topk_and_blocks.
+    rescore = any("index_scores_fp8_kernel<false" in n and ", false>(csa2::IndexScoreArgs)" in n
+                  for n in per_kernel_bytes)
+    skip = ({"topk_and_blocks", "index_scores_pool", "topk_pool", "index_scores_top", "topk_top"} if rescore
+            else {"top_blocks_and_blocks", "index_scores_top", "topk_top"})
     for stage, pats in STAGE_KERNELS.items():
         # a stage is present when one of its own kernels is (the selection
         # list-stage kernels are shared between stages and do not count)
         own = [p for p in pats if p != "select_kernel<3,"]
-        if stage == "topk_and_blocks":
+        if stage in ("topk_and_blocks", "top_blocks_and_blocks"):
             own = ["select_pair_kernel"]
         if not any(p in n for p in own for n in per_kernel_bytes):
             continue
-        # the re-scoring route's stages run the pool stages' kernels: their
-        # dispatches cannot be told apart by name
-        if stage in ("index_scores_top", "topk_top"):
+        # stages whose dispatches cannot be told apart by kernel name
+        if stage in skip:
             continue
         # with the shared-launch call the separate-call stages do not occur
         if stage in ("topk_dense", "block_candidates", "topk_blocks") and any(

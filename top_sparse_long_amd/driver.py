@@ -32,11 +32,12 @@ from . import (csa2_index_scores, csa2_block_candidates, csa2_topk, csa2_sparse_
 
 
 # the re-scoring route for a Full layer's top-k (see LayerRunner): measured
-# per step, 64 x 262,144 keys 732.9 -> 680.8 us; 8 x 131,072 106.1 -> 108.6,
-# 2 x 1,048,576 148.6 -> 151.2 (the two extra launches cost more than the
-# score writes they save below some 8M keys per call)
+# per step, 64 x 262,144 keys 732.9 -> 680.8 us; with the scorer's storing
+# wave for maxima-only calls, 2 x 1,048,576 145.1 -> 143.2 us, while
+# 8 x 131,072 keys lose (105.5 -> 110.7: the two extra launches cost more
+# than the score writes they save)
 RESCORE_MAX_Q = 256
-RESCORE_MIN_KEYS = 8 << 20
+RESCORE_MIN_KEYS = 2 << 20
 
 
 def _round_up(x, m):

@@ -1009,6 +1009,8 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_pipe_kernel(AttnArg
           const int k0 = 32 * kb + 8 * g;
           const v8h S8 = *(const v8h*)(&s_scl[bf][c0 >> 7][k0]);
           const int rrow = v3_row(k0 + (r >> 1));
+          // the keys' scales (one 128-dim group for all the wave's
+          // columns) go into P, so V is the exact widened codes
           v8h B[CB];
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
@@ -1018,10 +1020,10 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_pipe_kernel(AttnArg
             const v2h x1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)tv[0], 1.0f, true);
             const v2h x2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)tv[1], 1.0f, false);
             const v2h x3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)tv[1], 1.0f, true);
-            B[cb] = (v8h){x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]} * S8;
+            B[cb] = (v8h){x0[0], x0[1], x1[0], x1[1], x2[0], x2[1], x3[0], x3[1]};
           }
           const _Float16 fT = (_Float16)((g >> 1) ? f[2 * kb + 1] : f[2 * kb]);
-          const v8h P = *(const v8h*)(pb + 2 * k0) * (v8h){fT, fT, fT, fT, fT, fT, fT, fT};
+          const v8h P = (*(const v8h*)(pb + 2 * k0) * (v8h){fT, fT, fT, fT, fT, fT, fT, fT}) * S8;
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P, B[cb], O[cb], 0, 0, 0);
         }
@@ -1051,6 +1053,18 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_pipe_kernel(AttnArg
           const _Float16 fT = (_Float16)fsel;
           const v8h f8 = {fT, fT, fT, fT, fT, fT, fT, fT};
           const v8h P1 = P1r * f8, P2 = P2r * f8;
+          // with one scale per 32 dims the wave's columns span NG scale
+          // groups (CB = 4: two); their scales go into P, once per group,
+          // instead of into every column block's V
+          constexpr int NG = S16 ? 1 : (CB == 4 ? 2 : 1);
+          v8h P1g[NG], P2g[NG];
+          if (!S16) {
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+              P1g[gi] = P1 * S1s[2 * gi];
+              P2g[gi] = P2 * S2s[2 * gi];
+            }
+          }
 #pragma unroll
           for (int cb = 0; cb < CB; ++cb) {
             const v2i_t tv = tvs[cb];
@@ -1064,10 +1078,16 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_pipe_kernel(AttnArg
             b2[2] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[1], 1.0f, 2));
             b2[3] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((uint32_t)tv[1], 1.0f, 3));
             const v4u u1 = {b1[0], b1[1], b1[2], b1[3]}, u2 = {b2[0], b2[1], b2[2], b2[3]};
-            const v8h B1 = __builtin_bit_cast(v8h, u1) * S1s[cb];
-            const v8h B2 = __builtin_bit_cast(v8h, u2) * S2s[cb];
-            O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P1, B1, O[cb], 0, 0, 0);
-            O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P2, B2, O[cb], 0, 0, 0);
+            if (S16) {
+              const v8h B1 = __builtin_bit_cast(v8h, u1) * S1s[cb];
+              const v8h B2 = __builtin_bit_cast(v8h, u2) * S2s[cb];
+              O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P1, B1, O[cb], 0, 0, 0);
+              O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P2, B2, O[cb], 0, 0, 0);
+            } else {
+              const int gi = (CB == 4) ? (cb >> 1) : 0;
+              O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P1g[gi], __builtin_bit_cast(v8h, u1), O[cb], 0, 0, 0);
+              O[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(P2g[gi], __builtin_bit_cast(v8h, u2), O[cb], 0, 0, 0);
+            }
           }
         }
       }

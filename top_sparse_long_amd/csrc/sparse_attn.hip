@@ -85,6 +85,26 @@ __device__ __forceinline__ void dequant_fp8x4(uint32_t x, float s, v2h m2, uint3
   out[1] = as_u32(__builtin_amdgcn_cvt_scalef32_pk_f16_fp8(x, s, true) * m2);
 }
 
+// x combined with the value of the lane 16 (32) away, in every lane: the
+// gfx950 permlane swaps leave {x, x[lane ^ 16]} ({x, x[lane ^ 32]}) in the
+// two results, with no LDS round trip
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float add_xor16(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+__device__ __forceinline__ float add_xor32(float x) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
 // Inverse RoPE of one output pair (x, y) = dims (2i, 2i+1) of the turned
 // range: x' = x cos + y sin, y' = y cos - x sin.
 __device__ __forceinline__ void unturn(float& x, float& y, float c, float s) {
@@ -364,8 +384,7 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_wide_kernel(AttnArg
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[hb][i] = ((vmask >> (4 * g + i)) & 1ull) ? acc[hb][i] * zscale : -INFINITY;
       float mt = fmaxf(fmaxf(z[hb][0], z[hb][1]), fmaxf(z[hb][2], z[hb][3]));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_xor32(max_xor16(mt));
       if (g == 0) s_m[wave][NHB * r + hb] = mt;
     }
     __syncthreads();
@@ -948,15 +967,13 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_pipe_kernel(AttnArg
 #pragma unroll
       for (int i = 0; i < 4; ++i) z[i] = ((vmask >> (4 * g + i)) & 1ull) ? acc[i] * zscale : -INFINITY;
       float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = max_xor32(max_xor16(mt));
       const float mref = (mt == -INFINITY) ? 0.f : mt;   // no key: every z is -inf, P is 0
       float pv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) pv[i] = __builtin_amdgcn_exp2f(z[i] - mref);
       float lt = (pv[0] + pv[1]) + (pv[2] + pv[3]);
-      lt += __shfl_xor(lt, 16);
-      lt += __shfl_xor(lt, 32);
+      lt = add_xor32(add_xor16(lt));
       const v4h P4 = {(_Float16)pv[0], (_Float16)pv[1], (_Float16)pv[2], (_Float16)pv[3]};
       *(v4h*)(s_p[bf] + r * WD_PS + 2 * (16 * wave + 4 * g)) = P4;
       if (g == 0) {

@@ -377,12 +377,12 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_wide_kernel(AttnArg
       }, acc);
     }
     // lane (r, g) of S^T holds keys 4 g + i of the tile for head 16 hb + r
-    const uint64_t vmask = __ballot(R.ok);
+    const uint32_t ok4 = (uint32_t)(__ballot(R.ok) >> (4 * g)) & 0xFu;
     float z[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[hb][i] = ((vmask >> (4 * g + i)) & 1ull) ? acc[hb][i] * zscale : -INFINITY;
+      for (int i = 0; i < 4; ++i) z[hb][i] = ((ok4 >> i) & 1u) ? acc[hb][i] * zscale : -INFINITY;
       float mt = fmaxf(fmaxf(z[hb][0], z[hb][1]), fmaxf(z[hb][2], z[hb][3]));
       mt = max_xor32(max_xor16(mt));
       if (g == 0) s_m[wave][NHB * r + hb] = mt;
@@ -962,10 +962,11 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_pipe_kernel(AttnArg
     }
     // tile statistics: lane (r, g) of S^T holds keys 4 g + i for head r
     {
-      const uint64_t vmask = __ballot(ok);
+      // validity of keys 4 g .. 4 g + 3 (lanes 4 g + i hold them)
+      const uint32_t ok4 = (uint32_t)(__ballot(ok) >> (4 * g)) & 0xFu;
       float z[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] = ((vmask >> (4 * g + i)) & 1ull) ? acc[i] * zscale : -INFINITY;
+      for (int i = 0; i < 4; ++i) z[i] = ((ok4 >> i) & 1u) ? acc[i] * zscale : -INFINITY;
       float mt = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
       mt = max_xor32(max_xor16(mt));
       const float mref = (mt == -INFINITY) ? 0.f : mt;   // no key: every z is -inf, P is 0
@@ -984,25 +985,50 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_pipe_kernel(AttnArg
     __syncthreads();
 
     // ---- phase C: running maximum, denominator, O[16 x 16 CB] += P V
-    float f[WD_WAVES];   // 2^(m_t - M) of every tile for head r
+    // SWA rounds: 2^(m_t - M) of every tile for head r; main rounds (whose
+    // products take tiles g and 4 + g in lane group g): only those two, the
+    // maximum and the denominator's sum combined across the lane groups
+    float f[WD_WAVES];
+    float f_g[2];
     {
-      const v4f ma = *(const v4f*)(&s_st[bf][0][r][0]), mb = *(const v4f*)(&s_st[bf][0][r][4]);
-      const v4f la = *(const v4f*)(&s_st[bf][1][r][0]), lb = *(const v4f*)(&s_st[bf][1][r][4]);
-      const float mt[WD_WAVES] = {ma[0], ma[1], ma[2], ma[3], mb[0], mb[1], mb[2], mb[3]};
-      const float lt[WD_WAVES] = {la[0], la[1], la[2], la[3], lb[0], lb[1], lb[2], lb[3]};
-      float mx = mt[0];
+      float mt[WD_WAVES], lt[WD_WAVES], mx;
+      if constexpr (swa_round) {
+        const v4f ma = *(const v4f*)(&s_st[bf][0][r][0]), mb = *(const v4f*)(&s_st[bf][0][r][4]);
+        const v4f la = *(const v4f*)(&s_st[bf][1][r][0]), lb = *(const v4f*)(&s_st[bf][1][r][4]);
 #pragma unroll
-      for (int w = 1; w < WD_WAVES; ++w) mx = fmaxf(mx, mt[w]);
+        for (int w = 0; w < 4; ++w) {
+          mt[w] = ma[w];
+          mt[4 + w] = mb[w];
+          lt[w] = la[w];
+          lt[4 + w] = lb[w];
+        }
+        mx = mt[0];
+#pragma unroll
+        for (int w = 1; w < WD_WAVES; ++w) mx = fmaxf(mx, mt[w]);
+      } else {
+        mt[0] = s_st[bf][0][r][g];
+        mt[1] = s_st[bf][0][r][4 + g];
+        lt[0] = s_st[bf][1][r][g];
+        lt[1] = s_st[bf][1][r][4 + g];
+        mx = max_xor32(max_xor16(fmaxf(mt[0], mt[1])));
+      }
       const bool up = mx > M + RESCALE_SLACK || (M == -INFINITY && mx > -INFINITY);
       const float m_new = up ? mx : M;
       const float alpha = (m_new == -INFINITY || !up) ? 1.f : __builtin_amdgcn_exp2f(M - m_new);
       M = m_new;
       const float mref = (M == -INFINITY) ? 0.f : M;
       float add = 0.f;
+      // m_t - M <= 8 here, and -inf gives 0
+      if constexpr (swa_round) {
 #pragma unroll
-      for (int w = 0; w < WD_WAVES; ++w) {
-        f[w] = __builtin_amdgcn_exp2f(mt[w] - mref);   // m_t - M <= 8 here, and -inf gives 0
-        add += f[w] * lt[w];
+        for (int w = 0; w < WD_WAVES; ++w) {
+          f[w] = __builtin_amdgcn_exp2f(mt[w] - mref);
+          add += f[w] * lt[w];
+        }
+      } else {
+        f_g[0] = __builtin_amdgcn_exp2f(mt[0] - mref);
+        f_g[1] = __builtin_amdgcn_exp2f(mt[1] - mref);
+        add = add_xor32(add_xor16(f_g[0] * lt[0] + f_g[1] * lt[1]));
       }
       L = L * alpha + add;
       // every wave takes the same decision (same maxima, same rule)
@@ -1066,8 +1092,7 @@ __global__ __launch_bounds__(64 * WD_WAVES) void sparse_attn_pipe_kernel(AttnArg
           const v8h P1r = *(const v8h*)(pb + 2 * kt);
           const v8h P2r = *(const v8h*)(pb + 2 * (kt + 8));
           __builtin_amdgcn_sched_barrier(0);
-          const float fsel = g == 0 ? f[4 * half] : g == 1 ? f[4 * half + 1] : g == 2 ? f[4 * half + 2] : f[4 * half + 3];
-          const _Float16 fT = (_Float16)fsel;
+          const _Float16 fT = (_Float16)f_g[half];
           const v8h f8 = {fT, fT, fT, fT, fT, fT, fT, fT};
           const v8h P1 = P1r * f8, P2 = P2r * f8;
           // with one scale per 32 dims the wave's columns span NG scale

@@ -875,6 +875,28 @@ def test_block_max_without_scores(bs, big):
         assert np.all(refn[t, len(r):] == -np.inf), t
 
 
+@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("k_fmt", ["fp8", "fp4s16"])
+def test_block_max_without_scores_formats(k_fmt, paged):
+    """The maxima-only call (the storing-wave form) with FP4 keys and their
+    E4M3 scales, and with index keys read through a page table: the same
+    block maxima as the score-writing call on the same runner, bit for bit."""
+    _announce(f"block maxima without scores keys={k_fmt} paged={paged}")
+    n = [300_001, 40_000]
+    pos = [[n[0] - 1, 123_457], [n[1] - 1, 0]]
+    wl = synth.mini_workload(46, n, q_per_seq=2, positions=pos, k_fmt=k_fmt).to(DEV)
+    run = LayerRunner(wl, paged=synth.paged_layout(wl, 76)) if paged else LayerRunner(wl)
+    run.index_scores(0, pool=False, block_max=True)
+    torch.cuda.synchronize()
+    nb = -(-run.n_cols // wl.block_size)
+    ref = run.block_max[:, :nb].clone()
+    run.block_max.fill_(7.0)
+    run.index_scores(0, pool=False, block_max=True, scores=False)
+    torch.cuda.synchronize()
+    assert torch.equal(run.block_max[:, :nb], ref)
+    assert bool(torch.isfinite(ref).any())
+
+
 @pytest.mark.parametrize("concurrent", [False, True])
 def test_graph_replay_matches_eager(concurrent):
     """A captured pass (optionally with every attention call on a second

@@ -276,11 +276,30 @@ __global__ __launch_bounds__(64 * (SC ? IS_WAVES : IS_WAVES + 1)) void index_sco
     float ks[TILES];
     int pos[TILES];
   };
+  // Pool calls: the candidate block of each lane's column is requested one
+  // sub-chunk ahead of its rows (cq), so a sub-chunk's row addresses never
+  // wait for a lookup issued in the same phase; the lookup is unconditional
+  // (columns past the row read its last entry and are masked below).
+  int cq[TILES];
+  auto cand_load = [&](int sc0) {
+    if (!POOL) return;
+#pragma unroll
+    for (int i = 0; i < TILES; ++i) {
+      const int col = min(sc0 + (i * IS_WAVES + wave) * 32 + r, a.n_cols - 1);
+      cq[i] = a.cand[(int64_t)t * a.n_cand_blocks + (col >> a.block_shift)];
+    }
+  };
   auto load_sub = [&](int sc0, Sub& S) {
 #pragma unroll
     for (int i = 0; i < TILES; ++i) {
       const int tcol = sc0 + (i * IS_WAVES + wave) * 32;
-      S.pos[i] = (tcol < limit) ? column_position<POOL>(a, t, tcol + r, nvis) : -1;
+      if (POOL) {
+        const int col = tcol + r;
+        const int p = (cq[i] << a.block_shift) | (col & ((1 << a.block_shift) - 1));
+        S.pos[i] = (tcol < limit && col < a.n_cols && cq[i] >= 0 && p < nvis) ? p : -1;
+      } else {
+        S.pos[i] = (tcol < limit) ? column_position<POOL>(a, t, tcol + r, nvis) : -1;
+      }
       int pg = 0;
       if (PAGED) {
         // dense: a 32-column tile lies in one 64-slot page (one scalar
@@ -311,8 +330,12 @@ __global__ __launch_bounds__(64 * (SC ? IS_WAVES : IS_WAVES + 1)) void index_sco
   // a branch would make the wait before each contraction count for the
   // worst path, which is to say for the next sub-chunk's rows as well.
   Sub buf[IS_NBUF];
+  cand_load(col_begin);
 #pragma unroll
-  for (int k = 0; k + 1 < IS_NBUF; ++k) load_sub(ahead(col_begin, k), buf[k]);
+  for (int k = 0; k + 1 < IS_NBUF; ++k) {
+    load_sub(ahead(col_begin, k), buf[k]);
+    cand_load(ahead(col_begin, k + 1));
+  }
 
   // A operand widened to f16; gate of head r with the q scale folded in,
   // then the 16 heads this lane's accumulators hold.
@@ -370,6 +393,7 @@ __global__ __launch_bounds__(64 * (SC ? IS_WAVES : IS_WAVES + 1)) void index_sco
         const int cc = c0 + ph * col_step;
         if (cc >= col_end) break;
         load_sub(ahead(cc, IS_NBUF - 1), buf[(ph + IS_NBUF - 1) % IS_NBUF]);
+        cand_load(ahead(cc, IS_NBUF));
         float scs[TILES];
         compute_sub(cc, buf[ph], scs);
       }

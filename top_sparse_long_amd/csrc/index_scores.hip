@@ -24,12 +24,13 @@
 // is summed exactly once.  The accumulator layout is the standard 32x32 one
 // (accumulator j of lane l: head 8 (j / 4) + 4 (l / 32) + j % 4, key l % 32),
 // so the ReLU-weighted head sum is 16 in-register FMAs plus one exchange with
-// the lane 32 away.  Each wave loads all of its tiles before computing, so
-// about 16 KB per wave are in flight.
+// the lane 32 away.  Each wave requests the rows of its next sub-chunk
+// before contracting the current one (a ring of IS_NBUF register buffers).
 //
 // Optional fused output: the block maximum of every block_size (<= 32)
 // consecutive columns (the first step of the CSA2 page's candidate pool:
-// "blocks are not compression"), taken over the scores in registers.
+// "blocks are not compression"), taken over the scores in registers, or in
+// LDS by a storing wave when only the maxima are written.
 #include "kernels.h"
 
 #include <algorithm>

@@ -112,7 +112,7 @@ def _stage_work(run, stage):
         # without the 4-B score when the Full layer re-scores its best blocks
         fused = any(run.fuses_block_max(li) for li, l in enumerate(wl.layers) if l.mode == "full")
         extra = 4.0 / wl.block_size if fused else 0.0
-        if run.rescore and any(run.needs_pool):
+        if any(run.rescored(li, overlap_route=True) for li in range(len(wl.layers))):
             extra -= SCORE_BYTES
         pairs = int(nvis.sum().item())
         return (float(pairs) * (_index_bytes(wl) + extra), float(pairs) * INDEX_FLOPS_PER_PAIR, pairs,
@@ -685,14 +685,15 @@ def stage_stats(timer, rs, n_samples, reps, protocols=("rotated", "cold", "warm"
     warm     one copy's calls right after the same calls ran.
     The medians of `rotated` are the stage times the roofline uses."""
     names = []
-    for name, _ in rs[0].steps():
+    for name, _ in rs[0].steps(overlap_route=True):
         if name != "reset" and name not in names:
             names.append(name)
     out = {}
     for name in names:
-        per_copy = [[f for n, f in r.steps() if n == name] for r in rs]
+        per_copy = [[f for n, f in r.steps(overlap_route=True) if n == name] for r in rs]
         calls = len(per_copy[0])
-        rot = timer.capture([f for _ in range(reps) for r in rs for n, f in r.steps() if n == name])
+        rot = timer.capture([f for _ in range(reps) for r in rs for n, f in r.steps(overlap_route=True)
+                             if n == name])
         rot.replay()
         for fns in per_copy:
             for f in fns:
@@ -755,7 +756,7 @@ def measure_workload(torch, synth, LayerRunner, timer, name, args, copies, steps
     t1 = time.perf_counter()
     del step_graphs
     # the same pass with every call on one stream, for reference
-    serial_graphs = [timer.capture([f for _, f in r.steps()]) for r in runs]
+    serial_graphs = [timer.capture([f for _, f in r.steps(overlap_route=True)]) for r in runs]
     for i in range(warmup):
         serial_graphs[i % len(serial_graphs)].replay()
     torch.cuda.synchronize()
@@ -945,7 +946,7 @@ def main():
     dev = "cuda"
     if args.stage_only:
         run = LayerRunner(synth.make_workload(args.workload, device=dev))
-        steps = run.steps()
+        steps = run.steps(overlap_route=True)
         for _, fn in steps:
             fn()
         calls = [fn for name, fn in steps if name == args.stage_only]

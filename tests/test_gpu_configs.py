@@ -90,9 +90,17 @@ def _check_rescore_route(run, wl, t, ref, idx_row, pos1, n):
                                                                           wl.n_blocks))
 
 
-@pytest.mark.parametrize("name", list(synth.CONFIG_NAMES) + list(synth.EXTRA_WORKLOADS))
-def test_config_parity(name):
-    print(f"[case] config {name}", flush=True)
+# Every workload on the route the benchmark times (overlap_route: a
+# pool-building Full layer of a decode batch re-scores its best blocks), and
+# the 128K decode step also on the single-stream default route (dense scores,
+# top-k and pool in shared launches).
+CONFIG_CASES = ([(n, True) for n in list(synth.CONFIG_NAMES) + list(synth.EXTRA_WORKLOADS)]
+                + [("decode_128k", False)])
+
+
+@pytest.mark.parametrize("name,overlap_route", CONFIG_CASES)
+def test_config_parity(name, overlap_route):
+    print(f"[case] config {name} overlap_route={overlap_route}", flush=True)
     gen_dev = "cpu" if name == "tiny_full_fp32" else DEV
     wl = synth.make_workload(name, device=gen_dev).to(DEV)
     run = LayerRunner(wl)
@@ -112,7 +120,7 @@ def test_config_parity(name):
         return keys[int(q_seq[t])], np.array([q_pos[t]]), np.array([0])
 
     # the benchmark's own call sequence, checked after each layer's attention
-    steps = iter(run.steps())
+    steps = iter(run.steps(overlap_route=overlap_route))
     for li, lay in enumerate(wl.layers):
         print(f"[case] config {name} layer {li} ({lay.mode})", flush=True)
         for step_name, fn in steps:
@@ -132,7 +140,7 @@ def test_config_parity(name):
         for j, t in enumerate(sample):
             kr, pos1, seq0 = sub(t)
             n = int(nvis[t])
-            if lay.mode == "full" and run.rescore and run.needs_pool[li]:
+            if run.rescored(li, overlap_route):
                 # the re-scoring route: block maxima only, the best blocks'
                 # keys scored again
                 ref = oracle.index_scores_dense(qi[j:j + 1], wi[j:j + 1], kr, zero, seq0, pos1,

@@ -902,10 +902,15 @@ def test_graph_replay_matches_eager(concurrent):
     """A captured pass (optionally with every attention call on a second
     stream, overlapping the later layers' scoring and selection) replays to
     the serial eager result, several times, with eager work and
-    synchronisations between the replays."""
+    synchronisations between the replays.  The overlapped pass takes the
+    Full layer's re-scoring route with its re-scoring, top-k and attention on
+    the second stream; the serial eager reference takes the dense route."""
     _announce(f"graph replay concurrent={concurrent}")
     wl = synth.mini_workload(43, [70000, 20000], q_per_seq=2, modes=("full", "reuse", "reindex")).to(DEV)
     run = LayerRunner(wl)
+    names = [n for n, _ in run.steps(concurrent=concurrent)]
+    assert ("topk_top_and_sparse_attn" in names) == concurrent
+    assert "topk_and_blocks" in [n for n, _ in run.steps()]
     run.run()
     torch.cuda.synchronize()
     ref = [o.clone() for o in run.out] + [run.cand.clone()] + [v.clone() for v in run.idx.values()]

@@ -117,10 +117,26 @@ class LayerRunner:
         if rescore is None:
             rescore = (self.quant and Q < RESCORE_MAX_Q and Q * self.n_cols >= RESCORE_MIN_KEYS)
         self.rescore = bool(rescore) and self.quant and self.fuse_block_max and wl.topk <= 4096
+        # The overlapped schedule (steps(concurrent=True)) takes that route
+        # for a pool-building Full layer whose attention runs on the second
+        # stream, whatever the layer's size: the re-scoring and its top-k go
+        # to that stream as well, so the main stream moves on to the next
+        # layers (pool scoring) right after the paired block ranking.
+        self.side_rescore = (self.quant and self.fuse_block_max and wl.topk <= 4096
+                             and Q < RESCORE_MAX_Q)
         self.top_cols = wl.topk * wl.block_size
-        self.top_blocks = torch.empty((Q, wl.topk), dtype=torch.int32, device=device)
-        self.top_scores = (torch.empty((Q, _round_up(self.top_cols, 64)), dtype=f32, device=device)
-                           if self.rescore else None)
+        # best blocks and their re-scored keys, per pool-building Full layer
+        # (a layer finishing on the second stream may still read its own
+        # while a later one ranks blocks on the main stream)
+        self.top_bufs = {}
+        if self.rescore or self.side_rescore:
+            for li, l in enumerate(wl.layers):
+                if l.mode == "full" and self.needs_pool[li]:
+                    self.top_bufs[li] = (
+                        torch.empty((Q, wl.topk), dtype=torch.int32, device=device),
+                        torch.empty((Q, _round_up(self.top_cols, 64)), dtype=f32, device=device))
+        first = self.top_bufs[min(self.top_bufs)] if self.top_bufs else (None, None)
+        self.top_blocks, self.top_scores = first
         self.idx = {li: torch.empty((Q, wl.topk), dtype=torch.int32, device=device)
                     for li, l in enumerate(wl.layers) if l.mode in ("full", "reindex")}
         ws = max(csa2_topk_workspace_size(Q, self.n_cols, wl.topk),
@@ -130,9 +146,13 @@ class LayerRunner:
                                                                wl.block_size, wl.n_blocks),
                  csa2_topk_from_block_max_workspace_size(Q, self.n_cols, wl.topk, wl.block_size),
                  csa2_top_blocks_and_block_candidates_workspace_size(Q, self.n_cols, wl.block_size, wl.topk,
-                                                                     wl.n_blocks) if self.rescore else 0,
-                 csa2_topk_workspace_size(Q, self.top_cols, wl.topk) if self.rescore else 0)
+                                                                     wl.n_blocks) if self.top_bufs else 0,
+                 csa2_topk_workspace_size(Q, self.top_cols, wl.topk) if self.top_bufs else 0)
         self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=device)
+        # the top-k among the best blocks' keys when it runs on the second
+        # stream, beside the main stream's selections
+        ws_t = csa2_topk_workspace_size(Q, self.top_cols, wl.topk) if self.top_bufs else 0
+        self.ws_side = torch.empty((max(ws_t, 16),), dtype=torch.uint8, device=device)
         # block candidates may run beside the Full layer's top-k on a second
         # stream, so they get a workspace of their own
         ws_b = csa2_block_candidates_workspace_size(Q, self.n_cols, wl.block_size, wl.n_blocks)
@@ -170,9 +190,10 @@ class LayerRunner:
         wdt = CSA2_BF16 if self.quant else CSA2_F32
         if pool == "top":
             # the keys of the Full layer's best blocks, scored again
+            top_blocks, top_scores = self.top_bufs[li]
             csa2_index_scores(self.layer_rows[li]["q_idx"], lay.w, wdt, self.slots.index_k,
-                              wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio, self.top_scores,
-                              self.top_cols, self.Q, cand=self.top_blocks,
+                              wl.seq_base, wl.q_seq, wl.q_pos, wl.ratio, top_scores,
+                              self.top_cols, self.Q, cand=top_blocks,
                               block_size=wl.block_size, pages=self.pages_scores)
         elif pool:
             csa2_index_scores(self.layer_rows[li]["q_idx"], lay.w, wdt, self.slots.index_k,
@@ -210,21 +231,23 @@ class LayerRunner:
                       pages=self.pages_topk)
         self.slots.topk_idxs = idx
 
-    def top_blocks_and_blocks(self):
-        """The Full layer's best blocks and the candidate pool, from its block
+    def top_blocks_and_blocks(self, li):
+        """Full layer li's best blocks and the candidate pool, from its block
         maxima (no scores written)."""
         wl = self.wl
         csa2_top_blocks_and_block_candidates(self.block_max, self.n_cols, wl.q_pos, wl.ratio,
-                                             wl.block_size, wl.topk, self.top_blocks, wl.n_blocks,
+                                             wl.block_size, wl.topk, self.top_bufs[li][0], wl.n_blocks,
                                              self.cand, self.ws, self.Q)
         self.slots.candidates = self.cand
 
-    def topk_top(self, li):
-        """The Full layer's top-k among its best blocks' re-scored keys."""
+    def topk_top(self, li, ws=None):
+        """Full layer li's top-k among its best blocks' re-scored keys."""
         wl = self.wl
         idx = self.idx[li]
-        csa2_topk(self.top_scores, self.top_cols, None, wl.ratio, wl.topk, idx, self.ws, self.Q,
-                  cand=self.top_blocks, block_size=wl.block_size, pages=self.pages_topk)
+        top_blocks, top_scores = self.top_bufs[li]
+        csa2_topk(top_scores, self.top_cols, None, wl.ratio, wl.topk, idx,
+                  self.ws if ws is None else ws, self.Q,
+                  cand=top_blocks, block_size=wl.block_size, pages=self.pages_topk)
         self.slots.topk_idxs = idx
 
     def topk_and_blocks(self, li, from_block_max=False):
@@ -253,7 +276,15 @@ class LayerRunner:
         """Whether layer li's dense scoring pass also writes block maxima."""
         return self.fuse_block_max and (self.needs_pool[li] or self.via_blocks)
 
-    def steps(self, concurrent=False, separate_select=False):
+    def rescored(self, li, overlap_route=False):
+        """Whether Full layer li takes the re-scoring route (writes only its
+        block maxima) in a pass on the given route."""
+        layers = self.wl.layers
+        last_scoring = max((i for i, l in enumerate(layers) if l.mode in ("full", "reindex")), default=-1)
+        return (layers[li].mode == "full" and self.needs_pool[li]
+                and (self.rescore or (overlap_route and li < last_scoring and self.side_rescore)))
+
+    def steps(self, concurrent=False, separate_select=False, overlap_route=None):
         """The calls of one pass over every layer, in order, as (stage name,
         callable) pairs.
 
@@ -274,10 +305,16 @@ class LayerRunner:
         order: such a call waits only for the work issued before it on the
         main stream (its own top-k); the attention calls after the last
         scoring layer run on the main stream once the second stream's work
-        is done (nothing is left to overlap them).  Attention calls stay in
+        is done (nothing is left to overlap them).  A pool-building Full
+        layer whose attention goes to the second stream takes the re-scoring
+        route when the layer allows it (side_rescore), with its re-scoring
+        and top-k on that stream before the attention, so the next layers
+        need only the block ranking; overlap_route=True (the default with
+        concurrent) takes the same route with every call on one stream.
+        Attention calls stay in
         order among themselves (they share the split workspace), and every
-        buffer an attention call reads is written on the main stream before
-        it and not again within the pass (each layer has its own top-k
+        buffer an attention call reads is written before it (on the main
+        stream, or ahead of it on the second) and not again within the pass (each layer has its own top-k
         buffer).  Each callable launches on the stream current when it is
         called, so the pass can be captured into one graph."""
         out = []
@@ -290,14 +327,23 @@ class LayerRunner:
         layers = self.wl.layers
         last_scoring = max((i for i, l in enumerate(layers) if l.mode in ("full", "reindex")), default=-1)
         joined = False
+        if overlap_route is None:
+            overlap_route = concurrent
         for li, lay in enumerate(layers):
-            if lay.mode == "full" and self.rescore and self.needs_pool[li] and not separate_select:
+            side = concurrent and li < last_scoring
+            if not separate_select and self.rescored(li, overlap_route):
                 out.append(("index_scores_dense",
                             lambda li=li: self.index_scores(li, pool=False, block_max=True, scores=False)))
-                out.append(("top_blocks_and_blocks", self.top_blocks_and_blocks))
+                out.append(("top_blocks_and_blocks", lambda li=li: self.top_blocks_and_blocks(li)))
+                has_pool = True
+                if side:
+                    # re-scoring, top-k and attention on the second stream
+                    out.append(("topk_top_and_sparse_attn", lambda li=li: self._attention_side(
+                        li, before=(lambda: self.index_scores(li, pool="top"),
+                                    lambda: self.topk_top(li, ws=self.ws_side)))))
+                    continue
                 out.append(("index_scores_top", lambda li=li: self.index_scores(li, pool="top")))
                 out.append(("topk_top", lambda li=li: self.topk_top(li)))
-                has_pool = True
             elif lay.mode == "full":
                 fuse = self.fuses_block_max(li)
                 out.append(("index_scores_dense",
@@ -321,7 +367,7 @@ class LayerRunner:
                             lambda li=li, pool=pool: self.index_scores(li, pool=pool)))
                 out.append(("topk_pool" if pool else "topk_dense",
                             lambda li=li, pool=pool: self.topk(li, pool=pool)))
-            if concurrent and li < last_scoring:
+            if side:
                 out.append(("sparse_attn", lambda li=li: self._attention_side(li)))
             else:
                 if concurrent and not joined:
@@ -332,9 +378,9 @@ class LayerRunner:
             out.append(("join", self._join))
         return out
 
-    def _attention_side(self, li):
-        """Layer li's attention on the second stream, after everything issued
-        so far on the current stream."""
+    def _attention_side(self, li, before=()):
+        """Layer li's attention (after the callables in before) on the second
+        stream, after everything issued so far on the current stream."""
         main = torch.cuda.current_stream()
         if self._side is None:
             self._side = torch.cuda.Stream(device=main.device)   # default priority
@@ -342,6 +388,8 @@ class LayerRunner:
         ready.record(main)
         self._side.wait_event(ready)
         with torch.cuda.stream(self._side):
+            for fn in before:
+                fn()
             self.attention(li)
         self._joined = torch.cuda.Event()
         self._joined.record(self._side)

@@ -897,19 +897,22 @@ def test_block_max_without_scores_formats(k_fmt, paged):
     assert bool(torch.isfinite(ref).any())
 
 
-@pytest.mark.parametrize("concurrent", [False, True])
-def test_graph_replay_matches_eager(concurrent):
+@pytest.mark.parametrize("concurrent,n_seq", [(False, 2), (True, 2), (True, 4)])
+def test_graph_replay_matches_eager(concurrent, n_seq):
     """A captured pass (optionally with every attention call on a second
     stream, overlapping the later layers' scoring and selection) replays to
     the serial eager result, several times, with eager work and
     synchronisations between the replays.  The overlapped pass takes the
     Full layer's re-scoring route with its re-scoring, top-k and attention on
-    the second stream; the serial eager reference takes the dense route."""
-    _announce(f"graph replay concurrent={concurrent}")
-    wl = synth.mini_workload(43, [70000, 20000], q_per_seq=2, modes=("full", "reuse", "reindex")).to(DEV)
+    the second stream; the serial eager reference takes the dense route.
+    With 8 queries attention splits no keys (no shared workspace)."""
+    _announce(f"graph replay concurrent={concurrent} sequences={n_seq}")
+    wl = synth.mini_workload(43, [70000, 20000, 30000, 5000][:n_seq], q_per_seq=2,
+                             modes=("full", "reuse", "reindex")).to(DEV)
     run = LayerRunner(wl)
     names = [n for n, _ in run.steps(concurrent=concurrent)]
     assert ("topk_top_and_sparse_attn" in names) == concurrent
+    assert (run.ws_attn is None) == (n_seq == 4)
     assert "topk_and_blocks" in [n for n, _ in run.steps()]
     run.run()
     torch.cuda.synchronize()

@@ -897,23 +897,26 @@ def test_block_max_without_scores_formats(k_fmt, paged):
     assert bool(torch.isfinite(ref).any())
 
 
-@pytest.mark.parametrize("concurrent,n_seq", [(False, 2), (True, 2), (True, 4)])
-def test_graph_replay_matches_eager(concurrent, n_seq):
+@pytest.mark.parametrize("concurrent,n_seq,rescore", [(False, 2, None), (True, 2, None), (True, 4, None),
+                                                     (True, 2, True)])
+def test_graph_replay_matches_eager(concurrent, n_seq, rescore):
     """A captured pass (optionally with every attention call on a second
     stream, overlapping the later layers' scoring and selection) replays to
     the serial eager result, several times, with eager work and
-    synchronisations between the replays.  The overlapped pass takes the
-    Full layer's re-scoring route with its re-scoring, top-k and attention on
-    the second stream; the serial eager reference takes the dense route.
-    With 8 queries attention splits no keys (no shared workspace)."""
-    _announce(f"graph replay concurrent={concurrent} sequences={n_seq}")
+    synchronisations between the replays.  Overlapped, the Full layer's
+    top-k (through its block maxima, or on the re-scoring route) and its
+    attention run on the second stream while the main stream ranks the pool
+    and scores it; the eager reference is the serial default pass.  With 8
+    queries attention splits no keys (no shared workspace)."""
+    _announce(f"graph replay concurrent={concurrent} sequences={n_seq} rescore={rescore}")
     wl = synth.mini_workload(43, [70000, 20000, 30000, 5000][:n_seq], q_per_seq=2,
                              modes=("full", "reuse", "reindex")).to(DEV)
-    run = LayerRunner(wl)
+    run = LayerRunner(wl, rescore=rescore)
     names = [n for n, _ in run.steps(concurrent=concurrent)]
-    assert ("topk_top_and_sparse_attn" in names) == concurrent
+    side = "topk_top_and_sparse_attn" if rescore else "topk_blocks_and_sparse_attn"
+    assert (side in names) == concurrent
     assert (run.ws_attn is None) == (n_seq == 4)
-    assert "topk_and_blocks" in [n for n, _ in run.steps()]
+    assert ("topk_and_blocks" in [n for n, _ in run.steps()]) == (not rescore)
     run.run()
     torch.cuda.synchronize()
     ref = [o.clone() for o in run.out] + [run.cand.clone()] + [v.clone() for v in run.idx.values()]

@@ -190,16 +190,23 @@ def test_paged_prefill_scores_equal_flat():
 # ---------------------------------------------------------------------------
 # a decoder group over the paged layout
 
-def test_paged_group_equals_flat():
-    _announce("group full/reuse/reindex/reuse, paged + slots + inverse RoPE")
+@pytest.mark.parametrize("concurrent,rescore", [(False, None), (True, None), (True, True)])
+def test_paged_group_equals_flat(concurrent, rescore):
+    """The paged group equals the flat one (default route, one stream), also
+    overlapped (the Full layer's top-k and attention on the second stream)
+    and on the re-scoring route (the best blocks' keys scored again through
+    the page table, their top-k writing slots)."""
+    _announce(f"group full/reuse/reindex/reuse, paged + slots + inverse RoPE, "
+              f"concurrent={concurrent} rescore={rescore}")
     wl = synth.mini_workload(78, [6000, 3333], q_per_seq=2,
                              modes=("full", "reuse", "reindex", "reuse"),
                              topk=128, n_blocks=60).to(DEV)
     pl = synth.paged_layout(wl, 79)
     flat = LayerRunner(wl, rope_cs=pl.rope_cs)
-    paged = LayerRunner(wl, paged=pl)
+    paged = LayerRunner(wl, paged=pl, rescore=rescore)
+    assert paged.rescored(0) == bool(rescore) and not flat.rescored(0)
     flat.run()
-    paged.run()
+    paged.run(concurrent=concurrent)
     torch.cuda.synchronize()
     table = _np(pl.page_table)
     q_seq = _np(wl.q_seq)

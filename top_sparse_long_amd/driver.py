@@ -117,19 +117,20 @@ class LayerRunner:
         if rescore is None:
             rescore = (self.quant and Q < RESCORE_MAX_Q and Q * self.n_cols >= RESCORE_MIN_KEYS)
         self.rescore = bool(rescore) and self.quant and self.fuse_block_max and wl.topk <= 4096
-        # The overlapped schedule (steps(concurrent=True)) takes that route
-        # for a pool-building Full layer whose attention runs on the second
-        # stream, whatever the layer's size: the re-scoring and its top-k go
-        # to that stream as well, so the main stream moves on to the next
-        # layers (pool scoring) right after the paired block ranking.
-        self.side_rescore = (self.quant and self.fuse_block_max and wl.topk <= 4096
-                             and Q < RESCORE_MAX_Q)
+        # In the overlapped schedule (steps(concurrent=True)) a pool-building
+        # Full layer whose attention runs on the second stream finishes its
+        # top-k on that stream too, so the main stream needs only the pool
+        # before the next layer's scoring: on this route the re-scoring and
+        # its top-k, else the top-k through the block maxima
+        # (side_topk_blocks), beside the pool's own ranking on the main
+        # stream.
+        self.side_topk_blocks = self.via_blocks and not self.rescore
         self.top_cols = wl.topk * wl.block_size
         # best blocks and their re-scored keys, per pool-building Full layer
         # (a layer finishing on the second stream may still read its own
         # while a later one ranks blocks on the main stream)
         self.top_bufs = {}
-        if self.rescore or self.side_rescore:
+        if self.rescore:
             for li, l in enumerate(wl.layers):
                 if l.mode == "full" and self.needs_pool[li]:
                     self.top_bufs[li] = (
@@ -149,9 +150,11 @@ class LayerRunner:
                                                                      wl.n_blocks) if self.top_bufs else 0,
                  csa2_topk_workspace_size(Q, self.top_cols, wl.topk) if self.top_bufs else 0)
         self.ws = torch.empty((max(ws, 16),), dtype=torch.uint8, device=device)
-        # the top-k among the best blocks' keys when it runs on the second
-        # stream, beside the main stream's selections
-        ws_t = csa2_topk_workspace_size(Q, self.top_cols, wl.topk) if self.top_bufs else 0
+        # a Full layer's top-k when it runs on the second stream, beside the
+        # main stream's selections
+        ws_t = max(csa2_topk_workspace_size(Q, self.top_cols, wl.topk) if self.top_bufs else 0,
+                   csa2_topk_from_block_max_workspace_size(Q, self.n_cols, wl.topk, wl.block_size)
+                   if self.side_topk_blocks else 0)
         self.ws_side = torch.empty((max(ws_t, 16),), dtype=torch.uint8, device=device)
         # block candidates may run beside the Full layer's top-k on a second
         # stream, so they get a workspace of their own
@@ -215,12 +218,12 @@ class LayerRunner:
                               block_max=self.block_max if from_block_max else None)
         self.slots.candidates = self.cand
 
-    def topk(self, li, pool, via_blocks=False):
+    def topk(self, li, pool, via_blocks=False, ws=None):
         wl = self.wl
         idx = self.idx[li]
         if via_blocks:
             csa2_topk_from_block_max(self.scores, self.n_cols, self.block_max, wl.q_pos, wl.ratio,
-                                     wl.block_size, wl.topk, idx, self.ws, self.Q,
+                                     wl.block_size, wl.topk, idx, self.ws if ws is None else ws, self.Q,
                                      pages=self.pages_topk)
         elif pool:
             csa2_topk(self.pool_scores, self.pool_cols, None, wl.ratio, wl.topk, idx, self.ws,
@@ -278,11 +281,8 @@ class LayerRunner:
 
     def rescored(self, li, overlap_route=False):
         """Whether Full layer li takes the re-scoring route (writes only its
-        block maxima) in a pass on the given route."""
-        layers = self.wl.layers
-        last_scoring = max((i for i, l in enumerate(layers) if l.mode in ("full", "reindex")), default=-1)
-        return (layers[li].mode == "full" and self.needs_pool[li]
-                and (self.rescore or (overlap_route and li < last_scoring and self.side_rescore)))
+        block maxima)."""
+        return self.wl.layers[li].mode == "full" and self.needs_pool[li] and self.rescore
 
     def steps(self, concurrent=False, separate_select=False, overlap_route=None):
         """The calls of one pass over every layer, in order, as (stage name,
@@ -306,11 +306,12 @@ class LayerRunner:
         main stream (its own top-k); the attention calls after the last
         scoring layer run on the main stream once the second stream's work
         is done (nothing is left to overlap them).  A pool-building Full
-        layer whose attention goes to the second stream takes the re-scoring
-        route when the layer allows it (side_rescore), with its re-scoring
-        and top-k on that stream before the attention, so the next layers
-        need only the block ranking; overlap_route=True (the default with
-        concurrent) takes the same route with every call on one stream.
+        layer whose attention goes to the second stream finishes its top-k
+        on that stream before the attention (the re-scoring and its top-k,
+        or the top-k through the block maxima with the pool ranked
+        separately on the main stream), so the next layers need only the
+        pool; overlap_route=True (the default with concurrent) takes the
+        same route with every call on one stream.
         Attention calls stay in
         order among themselves (they share the split workspace), and every
         buffer an attention call reads is written before it (on the main
@@ -331,7 +332,7 @@ class LayerRunner:
             overlap_route = concurrent
         for li, lay in enumerate(layers):
             side = concurrent and li < last_scoring
-            if not separate_select and self.rescored(li, overlap_route):
+            if not separate_select and self.rescored(li):
                 out.append(("index_scores_dense",
                             lambda li=li: self.index_scores(li, pool=False, block_max=True, scores=False)))
                 out.append(("top_blocks_and_blocks", lambda li=li: self.top_blocks_and_blocks(li)))
@@ -344,6 +345,21 @@ class LayerRunner:
                     continue
                 out.append(("index_scores_top", lambda li=li: self.index_scores(li, pool="top")))
                 out.append(("topk_top", lambda li=li: self.topk_top(li)))
+            elif (lay.mode == "full" and self.needs_pool[li] and not separate_select and overlap_route
+                  and self.side_topk_blocks and not any(l.mode == "full" for l in layers[li + 1:])):
+                # the pool's ranking on the main stream, the top-k through
+                # the block maxima beside it (it reads the layer's scores and
+                # maxima, so no later Full layer may rewrite them meanwhile)
+                out.append(("index_scores_dense",
+                            lambda li=li: self.index_scores(li, pool=False, block_max=True)))
+                has_pool = True
+                if side:
+                    out.append(("topk_blocks_and_sparse_attn", lambda li=li: self._attention_side(
+                        li, before=(lambda: self.topk(li, pool=False, via_blocks=True, ws=self.ws_side),))))
+                    out.append(("block_candidates", lambda: self.block_candidates(from_block_max=True)))
+                    continue
+                out.append(("topk_blocks", lambda li=li: self.topk(li, pool=False, via_blocks=True)))
+                out.append(("block_candidates", lambda: self.block_candidates(from_block_max=True)))
             elif lay.mode == "full":
                 fuse = self.fuses_block_max(li)
                 out.append(("index_scores_dense",

@@ -53,7 +53,9 @@ constexpr int IS_WAVES = CSA2_IS_WAVES;                      // waves per workgr
 constexpr int IS_TILES = CSA2_IS_TILES;                      // 32-key tiles per wave per sub-chunk
 // Dense calls of at most this many keys (queries x columns) use one tile per
 // wave per sub-chunk: twice the workgroups, each lighter (measured: 128K x 8
-// queries 33.4 against 34.4 us; neutral at 2M keys, slower at 16M).
+// queries 33.4 against 34.4 us; neutral at 2M keys, slower at 16M).  Pool
+// calls (candidate blocks, at most a decode batch x the pool) always do
+// (64 x 16,384 candidate keys 36.2 -> 35.2 us, 8 x 16,384 9.0 -> 8.9).
 #ifndef CSA2_IS_ONE_TILE
 #define CSA2_IS_ONE_TILE (3 << 19)
 #endif
@@ -803,7 +805,7 @@ static void launch_decode_t(const IndexScoreArgs& a, hipStream_t s) {
 
 template <bool POOL, bool W_BF16, bool K4, bool PAGED, bool SC>
 static void launch_decode_sc(const IndexScoreArgs& a, hipStream_t s) {
-  if (!POOL && (int64_t)a.n_cols * a.Q <= IS_ONE_TILE_MAX_KEYS)
+  if (POOL || (int64_t)a.n_cols * a.Q <= IS_ONE_TILE_MAX_KEYS)
     launch_decode_t<POOL, W_BF16, K4, PAGED, 1, SC>(a, s);
   else
     launch_decode_t<POOL, W_BF16, K4, PAGED, IS_TILES, SC>(a, s);
